@@ -1,0 +1,464 @@
+/*
+ * mmf_oracle.c -- plain, slow CPU oracle of the MatMul-free LM block forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load this
+ * file; only the tests, the package's smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (cited by page title and section):
+ *   [DC-ternary] DataCamp blog "MatMul-free language models" (zh), section
+ *                "Replacing MatMul with ternary operations" (用三值运算取代 MatMul):
+ *                BitLinear weights restricted to {-1,0,1}; absmean quantization scales the
+ *                matrix by the mean absolute value of its elements and rounds each element
+ *                to the nearest of -1, 0, 1; products by -1/0/1 become negate/drop/keep.
+ *   [DC-core]    same page, section "Core components: MLGRU and GLU" (核心组件：MLGRU 与 GLU):
+ *                RMSNorm normalises activations before they are quantized; MLGRU keeps a
+ *                hidden state updated token by token through element-wise gates in (0,1);
+ *                the MatMul-free GLU applies two BitLinears, SiLU on one branch, an
+ *                element-wise product and a third BitLinear.
+ *   [HL-fbl]     Hysen Labs project page "MatMul-Free LM: 用三元权重和门控循环把矩阵乘法请出语言模型",
+ *                section "FusedBitLinear": each projection RMS-normalises its input, then
+ *                quantizes and accumulates against the ternary weights.
+ *   [HL-hgrn]    same page, section "HGRN attention: gated recurrence replaces softmax":
+ *                block input -> RMSNorm -> i/f/g projections -> recurrence -> g_norm
+ *                (RMSNorm fused with a swish gate) -> o_proj.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   R1  activations: per-token symmetric absmax int8 in [-127,127]; the RMSNorm factor r
+ *       cancels in the absmax ratio, so q is computed from x*gamma and r enters only the
+ *       dequantization scale a = r*max|x*gamma|/127.
+ *   R2  both quantizers round half to even (rintf in the default rounding mode).
+ *   R3  guards: absmean scale and row absmax are floored at 1e-5.
+ *   R4  absmean sum: per row in double (k ascending), rows summed in double (n ascending).
+ *   R5  MLGRU: f = sigmoid(f_pre + b_f), c = SiLU(i_pre), h_t = f*h_{t-1} + (1-f)*c;
+ *       i_proj feeds the candidate, f_proj the forget gate, g_proj the output gate.
+ *   R6  output gate: o = RMSNorm_D(h)*gamma_g * g*sigmoid(g) (default) or sigmoid(g)*h.
+ *   R7  block: pre-norm residuals y1 = x + o_proj(...), y2 = y1 + GLU(y1); one RMSNorm per
+ *       BitLinear input; y1 and y2 rounded once to the residual dtype.
+ *   R8  stage inputs computed here in double are rounded to fp32 before quantization.
+ *
+ * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
+ * activation quant) are defined in fp32 so that both sides take each integer decision in
+ * the same precision.  Build with -ffp-contract=off and without -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#define ORC_ABI_VERSION 1
+
+int orc_abi_version(void) { return ORC_ABI_VERSION; }
+int orc_max_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+
+/* A ternary linear layer as the oracle sees it: q in {-1,0,1}, row n = output feature. */
+typedef struct orc_linear {
+    const int8_t *q;      /* [n, k] */
+    float scale;          /* absmean scale s (dequantized weight = q*s) */
+    const float *gamma;   /* [k] RMSNorm gain of the input, or NULL for ones */
+    const float *bias;    /* [n] or NULL */
+    int64_t n, k;
+} orc_linear;
+
+/* ---------------------------------------------------------------- helpers (fp64) */
+
+static double sigmoid_d(double z) { return 1.0 / (1.0 + exp(-z)); }
+static double silu_d(double z) { return z * sigmoid_d(z); }
+
+/* Round a double to the nearest bfloat16 value (ties to even), returned as a double.
+ * One rounding: the value is scaled by an exact power of two so that the bf16 unit in the
+ * last place becomes 1, rounded to an integer, and scaled back. */
+double orc_round_bf16(double d) {
+    if (d == 0.0 || !isfinite(d)) return d;
+    int e;
+    frexp(d, &e);                 /* d = m * 2^e, 0.5 <= |m| < 1 */
+    int ulp = e - 8;              /* bf16 keeps 8 significant bits */
+    if (ulp < -133) ulp = -133;   /* subnormal range: fixed ulp 2^-133 */
+    double r = ldexp(nearbyint(ldexp(d, -ulp)), ulp);
+    if (fabs(r) > 3.3895313892515355e38) r = copysign(INFINITY, d);
+    return r;
+}
+
+/* -------------------------------------------------------- O1 absmean ternarization
+ * [DC-ternary]: scale by the mean absolute value of the whole matrix, round each element
+ * to the nearest integer in {-1,0,1}.  Readings R2, R3, R4.
+ */
+int orc_ternarize(const float *w, int64_t n, int64_t k, int8_t *q, float *scale) {
+    if (!w || !q || !scale || n <= 0 || k <= 0) return -1;
+    double total = 0.0;
+    for (int64_t r = 0; r < n; ++r) {
+        double row = 0.0;
+        for (int64_t c = 0; c < k; ++c) row += fabs((double)w[r * k + c]);
+        total += row;
+    }
+    float mean_abs = (float)(total / ((double)n * (double)k));
+    float s = mean_abs > 1e-5f ? mean_abs : 1e-5f;
+    for (int64_t i = 0; i < n * k; ++i) {
+        float v = rintf(w[i] / s);
+        if (v > 1.0f) v = 1.0f;
+        if (v < -1.0f) v = -1.0f;
+        q[i] = (int8_t)v;
+    }
+    *scale = s;
+    return 0;
+}
+
+/* ------------------------------------------------------------- O2 2-bit packing
+ * Storage format for the ternary weights (the pages only say "trits"): code = q + 1 in
+ * {0,1,2}; a row of k values is stored as k/16 little-endian 32-bit words; element
+ * k = 16*j + 4*a + b lives in word j at bits [8*b + 2*a, 8*b + 2*a + 1].
+ */
+int orc_pack(const int8_t *q, int64_t n, int64_t k, uint32_t *packed) {
+    if (!q || !packed || n <= 0 || k <= 0 || k % 16) return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = 0; j < k / 16; ++j) {
+            uint32_t word = 0;
+            for (int a = 0; a < 4; ++a)
+                for (int b = 0; b < 4; ++b) {
+                    int v = q[r * k + 16 * j + 4 * a + b];
+                    if (v < -1 || v > 1) return -1;
+                    word |= (uint32_t)(v + 1) << (8 * b + 2 * a);
+                }
+            packed[r * (k / 16) + j] = word;
+        }
+    return 0;
+}
+
+int orc_unpack(const uint32_t *packed, int64_t n, int64_t k, int8_t *q) {
+    if (!q || !packed || n <= 0 || k <= 0 || k % 16) return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t kk = 0; kk < k; ++kk) {
+            int64_t j = kk / 16, a = (kk % 16) / 4, b = kk % 4;
+            uint32_t code = (packed[r * (k / 16) + j] >> (8 * b + 2 * a)) & 3u;
+            if (code == 3u) return -2;
+            q[r * k + kk] = (int8_t)((int)code - 1);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------- O3 activation quantization
+ * [DC-core] RMSNorm before quantization; [HL-fbl] norm -> quantize -> accumulate.
+ * Per row: p = fl32(x*gamma); m = max|p| floored at 1e-5; s = fl32(127/m);
+ * q = clamp(rne(fl32(p*s)), -127, 127); r = 1/sqrt(mean x^2 + eps) (fp64);
+ * a = r*m/127 (fp64).  Readings R1, R2, R3.
+ */
+void orc_act_quant(const float *x, int64_t m, int64_t k, const float *gamma, double eps,
+                   int8_t *q, double *a, int32_t *rowsum) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row) {
+        const float *xr = x + row * k;
+        float mx = 0.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            float p = gamma ? xr[c] * gamma[c] : xr[c];
+            float ap = fabsf(p);
+            if (ap > mx) mx = ap;
+        }
+        float me = mx > 1e-5f ? mx : 1e-5f;
+        float s = 127.0f / me;
+        int32_t sum = 0;
+        double ss = 0.0;
+        for (int64_t c = 0; c < k; ++c) {
+            float p = gamma ? xr[c] * gamma[c] : xr[c];
+            float v = rintf(p * s);
+            if (v > 127.0f) v = 127.0f;
+            if (v < -127.0f) v = -127.0f;
+            int8_t qi = (int8_t)v;
+            if (q) q[row * k + c] = qi;
+            sum += qi;
+            ss += (double)xr[c] * (double)xr[c];
+        }
+        double r = 1.0 / sqrt(ss / (double)k + eps);
+        if (a) a[row] = r * (double)me / 127.0;
+        if (rowsum) rowsum[row] = sum;
+    }
+}
+
+/* ------------------------------------------------------- O4 ternary accumulate
+ * [DC-ternary]: multiplying by -1/0/1 is negate/drop/keep, so the product with the
+ * weight matrix is a signed sum of int8 activations.  Exact in int32.
+ */
+void orc_accumulate(const int8_t *qx, const int8_t *qw, int64_t m, int64_t n, int64_t k,
+                    int32_t *acc) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row)
+        for (int64_t col = 0; col < n; ++col) {
+            const int8_t *xr = qx + row * k, *wr = qw + col * k;
+            int32_t s = 0;
+            for (int64_t c = 0; c < k; ++c) {
+                if (wr[c] > 0) s += xr[c];
+                else if (wr[c] < 0) s -= xr[c];
+            }
+            acc[row * n + col] = s;
+        }
+}
+
+/* ---------------------------------------------------------------- O5 BitLinear
+ * y[m, n] = acc[m, n] * s_w * a[m] + bias[n], fp64.  Optional outputs: q_x, a, acc.
+ */
+int orc_bitlinear(const float *x, int64_t m, const orc_linear *w, double eps, double *y,
+                  int8_t *q_out, double *a_out, int32_t *acc_out) {
+    if (!x || !w || !y || m < 0 || w->n <= 0 || w->k <= 0) return -1;
+    if (m == 0) return 0;
+    int64_t k = w->k, n = w->n;
+    int8_t *q = q_out ? q_out : (int8_t *)malloc((size_t)(m * k));
+    double *a = a_out ? a_out : (double *)malloc(sizeof(double) * (size_t)m);
+    int32_t *acc = acc_out ? acc_out : (int32_t *)malloc(sizeof(int32_t) * (size_t)(m * n));
+    if (!q || !a || !acc) return -3;
+    orc_act_quant(x, m, k, w->gamma, eps, q, a, NULL);
+    orc_accumulate(q, w->q, m, n, k, acc);
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row)
+        for (int64_t col = 0; col < n; ++col)
+            y[row * n + col] = (double)acc[row * n + col] * (double)w->scale * a[row] +
+                               (w->bias ? (double)w->bias[col] : 0.0);
+    if (!q_out) free(q);
+    if (!a_out) free(a);
+    if (!acc_out) free(acc);
+    return 0;
+}
+
+/* ------------------------------------------------------- O6 gated recurrence
+ * [DC-core]: the hidden state is the memory; gates in (0,1) decide what flows.
+ * h_t = f_t*h_{t-1} + (1-f_t)*c_t per (b, d), t ascending.  f, c given (post-activation).
+ * Layout [B, T, D]; h0 [B, D] or NULL (zeros); h_seq [B, T, D] and h_last [B, D] optional.
+ */
+void orc_gated_recurrence(const double *f, const double *c, int64_t B, int64_t T, int64_t D,
+                          const double *h0, double *h_seq, double *h_last) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            double h = h0 ? h0[b * D + d] : 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                int64_t i = (b * T + t) * D + d;
+                h = f[i] * h + (1.0 - f[i]) * c[i];
+                if (h_seq) h_seq[i] = h;
+            }
+            if (h_last) h_last[b * D + d] = h;
+        }
+}
+
+/* ----------------------------------------------------- O6 + O7 MLGRU with output gate
+ * ifg: [B, T, 3D] pre-activations, segments i | f | g along the last axis.
+ * [HL-hgrn] i/f/g projections, recurrence, g_norm = RMSNorm fused with a swish gate.
+ * Readings R5, R6.  gate_mode 0: out = h*rsqrt(mean_D h^2 + eps)*gnorm_w * g*sigmoid(g);
+ * gate_mode 1: out = sigmoid(g)*h.  h_last [B, D] receives h_T.
+ */
+int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f_bias,
+              const double *h0, const float *gnorm_w, double eps, int gate_mode,
+              double *out, double *h_last) {
+    if (!ifg || !out || B <= 0 || T < 0 || D <= 0 || (gate_mode != 0 && gate_mode != 1))
+        return -1;
+    int64_t M = B * T;
+    double *f = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *c = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *h = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    if (!f || !c || !h) return -3;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < M; ++row)
+        for (int64_t d = 0; d < D; ++d) {
+            const double *r = ifg + row * 3 * D;
+            f[row * D + d] = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
+            c[row * D + d] = silu_d(r[d]);
+        }
+    orc_gated_recurrence(f, c, B, T, D, h0, h, h_last);
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < M; ++row) {
+        const double *g = ifg + row * 3 * D + 2 * D;
+        const double *hr = h + row * D;
+        if (gate_mode == 0) {
+            double ss = 0.0;
+            for (int64_t d = 0; d < D; ++d) ss += hr[d] * hr[d];
+            double r = 1.0 / sqrt(ss / (double)D + eps);
+            for (int64_t d = 0; d < D; ++d)
+                out[row * D + d] =
+                    hr[d] * r * (gnorm_w ? (double)gnorm_w[d] : 1.0) * silu_d(g[d]);
+        } else {
+            for (int64_t d = 0; d < D; ++d) out[row * D + d] = sigmoid_d(g[d]) * hr[d];
+        }
+    }
+    free(f);
+    free(c);
+    free(h);
+    return 0;
+}
+
+/* Round a double stage input to fp32 (reading R8) or to the residual dtype. */
+static void to_f32(const double *src, float *dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = (float)src[i];
+}
+static void to_resid(const double *src, float *dst, int64_t n, int resid_bf16) {
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = resid_bf16 ? (float)orc_round_bf16(src[i]) : (float)src[i];
+}
+
+/* Per-BitLinear stage record of a block run (every pointer optional). */
+typedef struct orc_stage {
+    float *x_in;   /* [M, K] fp32 stage input as quantized */
+    int8_t *q;     /* [M, K] */
+    double *a;     /* [M] */
+    int32_t *acc;  /* [M, N]; for a group of projections sharing one input, N is the
+                      sum of their widths and the projections sit side by side */
+} orc_stage;
+
+/* Several BitLinears applied to one input x [M, K]: outs[p] = BitLinear_p(x) [M, n_p].
+ * The input is quantized once per projection (identically, as the gain is shared). */
+static int group_bitlinear(const float *x, int64_t M, int np, const orc_linear *const *w,
+                           double eps, double *const *outs, orc_stage *st) {
+    int64_t K = w[0]->k, ntot = 0;
+    for (int p = 0; p < np; ++p) ntot += w[p]->n;
+    int8_t *q = (int8_t *)malloc((size_t)(M * K));
+    double *a = (double *)malloc(sizeof(double) * (size_t)M);
+    if (!q || !a) return -3;
+    int64_t off = 0;
+    for (int p = 0; p < np; ++p) {
+        int64_t n = w[p]->n;
+        int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * n));
+        if (!acc) return -3;
+        int rc = orc_bitlinear(x, M, w[p], eps, outs[p], q, a, acc);
+        if (rc) return rc;
+        if (st && st->acc)
+            for (int64_t r = 0; r < M; ++r)
+                memcpy(st->acc + r * ntot + off, acc + r * n, sizeof(int32_t) * (size_t)n);
+        off += n;
+        free(acc);
+    }
+    if (st) {
+        if (st->x_in) memcpy(st->x_in, x, sizeof(float) * (size_t)(M * K));
+        if (st->q) memcpy(st->q, q, (size_t)(M * K));
+        if (st->a) memcpy(st->a, a, sizeof(double) * (size_t)M);
+    }
+    free(q);
+    free(a);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ O8 GLU
+ * [DC-core]: two BitLinears on the input, SiLU on one branch, element-wise product, a
+ * third BitLinear.  x [M, D] -> y [M, D] (fp64, no residual).  m_out [M, F] receives the
+ * fp32 stage input of the down projection (optional).
+ */
+static int glu_impl(const float *x, int64_t M, const orc_linear *gate, const orc_linear *up,
+                    const orc_linear *down, double eps, double *y, float *m_out,
+                    orc_stage *st_gu, orc_stage *st_down) {
+    if (gate->n != up->n || gate->k != up->k || down->k != gate->n || down->n != gate->k)
+        return -1;
+    int64_t F = gate->n;
+    double *yg = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *yu = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    float *mm = (float *)malloc(sizeof(float) * (size_t)(M * F));
+    if (!yg || !yu || !mm) return -3;
+    const orc_linear *gu[2] = {gate, up};
+    double *outs[2] = {yg, yu};
+    int rc = group_bitlinear(x, M, 2, gu, eps, outs, st_gu);
+    if (rc) return rc;
+    for (int64_t i = 0; i < M * F; ++i) yg[i] = silu_d(yg[i]) * yu[i];
+    to_f32(yg, mm, M * F);
+    if (m_out) memcpy(m_out, mm, sizeof(float) * (size_t)(M * F));
+    if (st_down && st_down->x_in) memcpy(st_down->x_in, mm, sizeof(float) * (size_t)(M * F));
+    rc = orc_bitlinear(mm, M, down, eps, y, st_down ? st_down->q : NULL,
+                       st_down ? st_down->a : NULL, st_down ? st_down->acc : NULL);
+    free(yg);
+    free(yu);
+    free(mm);
+    return rc;
+}
+
+int orc_glu(const float *x, int64_t M, const orc_linear *gate, const orc_linear *up,
+            const orc_linear *down, double eps, double *y, float *m_out) {
+    if (!x || !gate || !up || !down || !y || M < 0) return -1;
+    if (M == 0) return 0;
+    return glu_impl(x, M, gate, up, down, eps, y, m_out, NULL, NULL);
+}
+
+/* ---------------------------------------------------------------- O9 block
+ * [HL-hgrn] block: RMSNorm -> i/f/g BitLinears -> MLGRU -> g_norm -> o_proj; then the GLU
+ * of [DC-core].  Reading R7 (pre-norm residuals).
+ * x [B, T, D] fp32 holding values exact in the residual dtype; y [B, T, D] receives y2
+ * (rounded to the residual dtype); h0 [B, D] or NULL; h_last [B, D] optional;
+ * ifg_out [B, T, 3D] and y1_out [B, T, D] optional.  Stage records (optional): i|f|g
+ * (N = 3D), o, gate|up (N = 2F), down.
+ */
+int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
+              const orc_linear *wf, const orc_linear *wg, const orc_linear *wo,
+              const orc_linear *wgate, const orc_linear *wup, const orc_linear *wdown,
+              const float *f_bias, const float *gnorm_w, double eps, int gate_mode,
+              int resid_bf16, const double *h0, double *h_last, double *y,
+              double *ifg_out, float *y1_out, orc_stage *st_ifg, orc_stage *st_o,
+              orc_stage *st_gu, orc_stage *st_down) {
+    if (!x || !wi || !wf || !wg || !wo || !wgate || !wup || !wdown || !y) return -1;
+    int64_t D = wi->k, F = wgate->n, M = B * T;
+    if (wf->k != D || wg->k != D || wi->n != D || wf->n != D || wg->n != D) return -1;
+    if (wo->k != D || wo->n != D || wup->n != F || wgate->k != D || wup->k != D) return -1;
+    if (wdown->k != F || wdown->n != D) return -1;
+    if (M == 0) return 0;
+    double *yi = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *yf = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *yg = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *ifg = (double *)malloc(sizeof(double) * (size_t)(M * 3 * D));
+    double *o = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    float *o32 = (float *)malloc(sizeof(float) * (size_t)(M * D));
+    double *yo = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    float *y1 = (float *)malloc(sizeof(float) * (size_t)(M * D));
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *glu = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    if (!yi || !yf || !yg || !ifg || !o || !o32 || !yo || !y1 || !tmp || !glu) return -3;
+
+    /* i, f, g projections of x. */
+    const orc_linear *proj[3] = {wi, wf, wg};
+    double *outs[3] = {yi, yf, yg};
+    int rc = group_bitlinear(x, M, 3, proj, eps, outs, st_ifg);
+    if (rc) return rc;
+    for (int64_t r = 0; r < M; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            ifg[r * 3 * D + d] = yi[r * D + d];
+            ifg[r * 3 * D + D + d] = yf[r * D + d];
+            ifg[r * 3 * D + 2 * D + d] = yg[r * D + d];
+        }
+    if (ifg_out) memcpy(ifg_out, ifg, sizeof(double) * (size_t)(M * 3 * D));
+
+    /* MLGRU + output gate, then o_proj with the residual. */
+    rc = orc_mlgru(ifg, B, T, D, f_bias, h0, gnorm_w, eps, gate_mode, o, h_last);
+    if (rc) return rc;
+    to_f32(o, o32, M * D);
+    if (st_o && st_o->x_in) memcpy(st_o->x_in, o32, sizeof(float) * (size_t)(M * D));
+    rc = orc_bitlinear(o32, M, wo, eps, yo, st_o ? st_o->q : NULL, st_o ? st_o->a : NULL,
+                       st_o ? st_o->acc : NULL);
+    if (rc) return rc;
+    for (int64_t i = 0; i < M * D; ++i) tmp[i] = (double)x[i] + yo[i];
+    to_resid(tmp, y1, M * D, resid_bf16);
+    if (y1_out) memcpy(y1_out, y1, sizeof(float) * (size_t)(M * D));
+
+    /* GLU with the residual. */
+    rc = glu_impl(y1, M, wgate, wup, wdown, eps, glu, NULL, st_gu, st_down);
+    if (rc) return rc;
+    for (int64_t i = 0; i < M * D; ++i) tmp[i] = (double)y1[i] + glu[i];
+    for (int64_t i = 0; i < M * D; ++i)
+        y[i] = resid_bf16 ? orc_round_bf16(tmp[i]) : (double)(float)tmp[i];
+
+    free(yi); free(yf); free(yg); free(ifg); free(o); free(o32); free(yo); free(y1);
+    free(tmp); free(glu);
+    return 0;
+}
+
+/* ------------------------------------------------------ ternary embedding gather
+ * Embedding rows are ternary like every other weight matrix: x[t] = s_E * q_E[id[t]],
+ * rounded to the residual dtype.
+ */
+int orc_embedding(const int8_t *qe, float scale, int64_t vocab, int64_t D, const int32_t *ids,
+                  int64_t M, int resid_bf16, float *x) {
+    for (int64_t t = 0; t < M; ++t) {
+        if (ids[t] < 0 || ids[t] >= vocab) return -1;
+        for (int64_t d = 0; d < D; ++d) {
+            double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;
+            x[t * D + d] = resid_bf16 ? (float)orc_round_bf16(v) : (float)v;
+        }
+    }
+    return 0;
+}
+
+/* Vector form of orc_round_bf16 for the test harness. */
+void orc_round_bf16_array(const double *src, double *dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = orc_round_bf16(src[i]);
+}

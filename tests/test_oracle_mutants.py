@@ -1,0 +1,76 @@
+"""Mutation check of the oracle's pins: each plausible mistake, planted in a private copy
+of the oracle source and built on the CPU, must make at least one pin fail."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from oracle import oracle as O
+from tests.oracle_pins import PINS
+
+# (name, original text, planted mistake); the original must occur exactly once.
+MUTANTS = [
+    ("quant_round_half_away", "float v = rintf(p * s);", "float v = roundf(p * s);"),
+    ("ternary_round_half_away", "float v = rintf(w[i] / s);", "float v = roundf(w[i] / s);"),
+    ("quant_floor_dropped", "float me = mx > 1e-5f ? mx : 1e-5f;", "float me = mx;"),
+    ("rms_sum_not_mean", "double r = 1.0 / sqrt(ss / (double)k + eps);",
+     "double r = 1.0 / sqrt(ss + eps);"),
+    ("acc_wrong_sign", "else if (wr[c] < 0) s -= xr[c];", "else if (wr[c] < 0) s += xr[c];"),
+    ("acc_transposed", "const int8_t *xr = qx + row * k, *wr = qw + col * k;",
+     "const int8_t *xr = qx + row * k, *wr = qw + (col % m) * k;"),
+    ("rescale_drops_weight_scale",
+     "y[row * n + col] = (double)acc[row * n + col] * (double)w->scale * a[row] +",
+     "y[row * n + col] = (double)acc[row * n + col] * a[row] +"),
+    ("recurrence_drops_1_minus_f", "h = f[i] * h + (1.0 - f[i]) * c[i];",
+     "h = f[i] * h + c[i];"),
+    ("recurrence_ignores_h0", "double h = h0 ? h0[b * D + d] : 0.0;", "double h = 0.0;"),
+    ("mlgru_i_f_swapped",
+     "f[row * D + d] = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));",
+     "f[row * D + d] = sigmoid_d(r[d] + (f_bias ? (double)f_bias[d] : 0.0));"),
+    ("mlgru_bias_sign",
+     "sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0))",
+     "sigmoid_d(r[D + d] - (f_bias ? (double)f_bias[d] : 0.0))"),
+    ("gnorm_sum_not_mean", "double r = 1.0 / sqrt(ss / (double)D + eps);",
+     "double r = 1.0 / sqrt(ss + eps);"),
+    ("gnorm_sigmoid_not_swish",
+     "hr[d] * r * (gnorm_w ? (double)gnorm_w[d] : 1.0) * silu_d(g[d]);",
+     "hr[d] * r * (gnorm_w ? (double)gnorm_w[d] : 1.0) * sigmoid_d(g[d]);"),
+    ("gnorm_gain_dropped",
+     "hr[d] * r * (gnorm_w ? (double)gnorm_w[d] : 1.0) * silu_d(g[d]);",
+     "hr[d] * r * silu_d(g[d]);"),
+    ("glu_silu_on_up", "yg[i] = silu_d(yg[i]) * yu[i];", "yg[i] = yg[i] * silu_d(yu[i]);"),
+    ("block_no_attn_residual", "tmp[i] = (double)x[i] + yo[i];", "tmp[i] = yo[i];"),
+    ("block_no_mlp_residual", "tmp[i] = (double)y1[i] + glu[i];", "tmp[i] = glu[i];"),
+    ("pack_bit_position", "word |= (uint32_t)(v + 1) << (8 * b + 2 * a);",
+     "word |= (uint32_t)(v + 1) << (2 * b + 8 * a);"),
+    ("quant_gain_dropped", "float p = gamma ? xr[c] * gamma[c] : xr[c];\n            float ap",
+     "float p = xr[c];\n            float ap"),
+    ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
+     "double v = (double)qe[(int64_t)ids[t] * D + d];"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, bad):
+    src = open(O.SRC).read()
+    assert src.count(orig) == 1, f"mutation site for {name} not unique"
+    tmp = tempfile.mkdtemp(prefix="orc_mutant_")
+    try:
+        path = os.path.join(tmp, "mutant.c")
+        with open(path, "w") as fh:
+            fh.write(src.replace(orig, bad))
+        lib = os.path.join(tmp, "libmutant.so")
+        subprocess.run(["gcc", *O.CFLAGS, path, "-o", lib, "-lm"], check=True)
+        mutant = O.Oracle(lib)
+        failed = []
+        for pin in PINS:
+            try:
+                pin(mutant)
+            except (AssertionError, ValueError):
+                failed.append(pin.__name__)
+        assert failed, f"mutant {name} passed every pin"
+    finally:
+        shutil.rmtree(tmp)

@@ -35,7 +35,10 @@
  *   R6  output gate: o = RMSNorm_D(h)*gamma_g * g*sigmoid(g) (default) or sigmoid(g)*h.
  *   R7  block: pre-norm residuals y1 = x + o_proj(...), y2 = y1 + GLU(y1); one RMSNorm per
  *       BitLinear input; y1 and y2 rounded once to the residual dtype.
- *   R8  stage inputs computed here in double are rounded to fp32 before quantization.
+ *   R8  activations that leave a stage are stored in the activation dtype: with bf16
+ *       activations the i/f/g pre-activations, the gated MLGRU output and the GLU hidden
+ *       are rounded to bf16 (fp32 otherwise) before the next stage reads them; the
+ *       recurrent state is not rounded.
  *
  * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
  * activation quant) are defined in fp32 so that both sides take each integer decision in
@@ -284,13 +287,10 @@ int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f
     return 0;
 }
 
-/* Round a double stage input to fp32 (reading R8) or to the residual dtype. */
-static void to_f32(const double *src, float *dst, int64_t n) {
-    for (int64_t i = 0; i < n; ++i) dst[i] = (float)src[i];
-}
-static void to_resid(const double *src, float *dst, int64_t n, int resid_bf16) {
+/* Round a double activation to the activation dtype (reading R8): bf16 or fp32. */
+static void to_act(const double *src, float *dst, int64_t n, int act_bf16) {
     for (int64_t i = 0; i < n; ++i)
-        dst[i] = resid_bf16 ? (float)orc_round_bf16(src[i]) : (float)src[i];
+        dst[i] = act_bf16 ? (float)orc_round_bf16(src[i]) : (float)src[i];
 }
 
 /* Per-BitLinear stage record of a block run (every pointer optional). */
@@ -340,7 +340,7 @@ static int group_bitlinear(const float *x, int64_t M, int np, const orc_linear *
  * fp32 stage input of the down projection (optional).
  */
 static int glu_impl(const float *x, int64_t M, const orc_linear *gate, const orc_linear *up,
-                    const orc_linear *down, double eps, double *y, float *m_out,
+                    const orc_linear *down, double eps, int act_bf16, double *y, float *m_out,
                     orc_stage *st_gu, orc_stage *st_down) {
     if (gate->n != up->n || gate->k != up->k || down->k != gate->n || down->n != gate->k)
         return -1;
@@ -354,7 +354,7 @@ static int glu_impl(const float *x, int64_t M, const orc_linear *gate, const orc
     int rc = group_bitlinear(x, M, 2, gu, eps, outs, st_gu);
     if (rc) return rc;
     for (int64_t i = 0; i < M * F; ++i) yg[i] = silu_d(yg[i]) * yu[i];
-    to_f32(yg, mm, M * F);
+    to_act(yg, mm, M * F, act_bf16);
     if (m_out) memcpy(m_out, mm, sizeof(float) * (size_t)(M * F));
     if (st_down && st_down->x_in) memcpy(st_down->x_in, mm, sizeof(float) * (size_t)(M * F));
     rc = orc_bitlinear(mm, M, down, eps, y, st_down ? st_down->q : NULL,
@@ -366,10 +366,10 @@ static int glu_impl(const float *x, int64_t M, const orc_linear *gate, const orc
 }
 
 int orc_glu(const float *x, int64_t M, const orc_linear *gate, const orc_linear *up,
-            const orc_linear *down, double eps, double *y, float *m_out) {
+            const orc_linear *down, double eps, int act_bf16, double *y, float *m_out) {
     if (!x || !gate || !up || !down || !y || M < 0) return -1;
     if (M == 0) return 0;
-    return glu_impl(x, M, gate, up, down, eps, y, m_out, NULL, NULL);
+    return glu_impl(x, M, gate, up, down, eps, act_bf16, y, m_out, NULL, NULL);
 }
 
 /* ---------------------------------------------------------------- O9 block
@@ -416,22 +416,24 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
             ifg[r * 3 * D + D + d] = yf[r * D + d];
             ifg[r * 3 * D + 2 * D + d] = yg[r * D + d];
         }
+    if (resid_bf16)
+        for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = orc_round_bf16(ifg[i]);
     if (ifg_out) memcpy(ifg_out, ifg, sizeof(double) * (size_t)(M * 3 * D));
 
     /* MLGRU + output gate, then o_proj with the residual. */
     rc = orc_mlgru(ifg, B, T, D, f_bias, h0, gnorm_w, eps, gate_mode, o, h_last);
     if (rc) return rc;
-    to_f32(o, o32, M * D);
+    to_act(o, o32, M * D, resid_bf16);
     if (st_o && st_o->x_in) memcpy(st_o->x_in, o32, sizeof(float) * (size_t)(M * D));
     rc = orc_bitlinear(o32, M, wo, eps, yo, st_o ? st_o->q : NULL, st_o ? st_o->a : NULL,
                        st_o ? st_o->acc : NULL);
     if (rc) return rc;
     for (int64_t i = 0; i < M * D; ++i) tmp[i] = (double)x[i] + yo[i];
-    to_resid(tmp, y1, M * D, resid_bf16);
+    to_act(tmp, y1, M * D, resid_bf16);
     if (y1_out) memcpy(y1_out, y1, sizeof(float) * (size_t)(M * D));
 
     /* GLU with the residual. */
-    rc = glu_impl(y1, M, wgate, wup, wdown, eps, glu, NULL, st_gu, st_down);
+    rc = glu_impl(y1, M, wgate, wup, wdown, eps, resid_bf16, glu, NULL, st_gu, st_down);
     if (rc) return rc;
     for (int64_t i = 0; i < M * D; ++i) tmp[i] = (double)y1[i] + glu[i];
     for (int64_t i = 0; i < M * D; ++i)

@@ -57,7 +57,7 @@ class Oracle:
         L.orc_gated_recurrence.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.orc_mlgru.argtypes = [vp, i64, i64, i64, vp, vp, vp, f64, i32, vp, vp]
         L.orc_glu.argtypes = [vp, i64, C.POINTER(OrcLinear), C.POINTER(OrcLinear),
-                              C.POINTER(OrcLinear), f64, vp, vp]
+                              C.POINTER(OrcLinear), f64, i32, vp, vp]
         L.orc_block.argtypes = ([vp, i64, i64] + [C.POINTER(OrcLinear)] * 7 +
                                 [vp, vp, f64, i32, i32, vp, vp, vp, vp, vp] +
                                 [C.POINTER(OrcStage)] * 4)
@@ -176,8 +176,9 @@ class Oracle:
         return out, hl
 
     # -------------------------------------------------------------------- GLU
-    def glu(self, x, gate, up, down, eps: float = 1e-6):
-        """gate/up/down: (q, scale) pairs.  Returns (y fp64 [M, D], m fp32 [M, F])."""
+    def glu(self, x, gate, up, down, eps: float = 1e-6, act_bf16: bool = False):
+        """gate/up/down: (q, scale[, gamma]) tuples.  Returns (y fp64 [M, D], m [M, F]) with
+        m rounded to the activation dtype (bf16 when act_bf16)."""
         x = np.ascontiguousarray(x, dtype=np.float32)
         D = x.shape[-1]
         M = x.size // D
@@ -185,7 +186,7 @@ class Oracle:
         y = np.empty(x.shape, np.float64)
         m = np.empty(x.shape[:-1] + (lg.n,), np.float32)
         rc = self.lib.orc_glu(_p(x), M, C.byref(lg), C.byref(lu), C.byref(ld), eps,
-                              _p(y), _p(m))
+                              int(act_bf16), _p(y), _p(m))
         if rc:
             raise ValueError(f"orc_glu failed ({rc})")
         return y, m

@@ -358,6 +358,13 @@ def pin_block_stages(orc):
         assert np.array_equal(acc, st["acc"]), name
     assert np.array_equal(r["stages"]["ifg"]["x_in"], x.reshape(6, 64))
     assert np.array_equal(r["stages"]["gateup"]["x_in"], r["y1"].reshape(6, 64))
+    # bf16 activations: every activation handed between stages is a bf16 value
+    for v in (r["ifg"].astype(np.float32), r["stages"]["o"]["x_in"], r["stages"]["down"]["x_in"],
+              r["y1"]):
+        assert np.array_equal(_bf(v), v)
+    assert np.array_equal(r["ifg"], r["ifg"].astype(np.float32).astype(np.float64))
+    r32 = orc.block(x, W, record=True, resid_bf16=False)
+    assert not np.array_equal(_bf(r32["stages"]["o"]["x_in"]), r32["stages"]["o"]["x_in"])
 
 
 def pin_embedding(orc):

@@ -47,6 +47,10 @@ MUTANTS = [
      "word |= (uint32_t)(v + 1) << (2 * b + 8 * a);"),
     ("quant_gain_dropped", "float p = gamma ? xr[c] * gamma[c] : xr[c];\n            float ap",
      "float p = xr[c];\n            float ap"),
+    ("ifg_not_rounded_to_bf16",
+     "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = orc_round_bf16(ifg[i]);",
+     "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = ifg[i];"),
+    ("glu_hidden_not_rounded", "to_act(yg, mm, M * F, act_bf16);", "to_act(yg, mm, M * F, 0);"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

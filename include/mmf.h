@@ -1,0 +1,236 @@
+/*
+ * mmf.h -- C ABI of libmmf, a gfx950 (MI355X) implementation of the forward pass of one
+ * MatMul-free language-model block: ternary BitLinear -> MLGRU token mixer -> GLU.
+ *
+ * Sources (cited by page title and section):
+ *   [DC-ternary] DataCamp blog "MatMul-free language models", section "Replacing MatMul with
+ *                ternary operations": BitLinear with weights in {-1,0,1}; absmean
+ *                quantization of each weight matrix; products become add/subtract.
+ *   [DC-core]    same page, section "Core components: MLGRU and GLU": RMSNorm before
+ *                activation quantization; MLGRU hidden state updated token by token through
+ *                gates in (0,1); MatMul-free GLU = two BitLinears, SiLU on one branch,
+ *                element-wise product, a third BitLinear.
+ *   [HL-fbl]     Hysen Labs project page "MatMul-Free LM", section "FusedBitLinear": each
+ *                projection RMS-normalises its input, quantizes it and accumulates it against
+ *                the ternary weights inside one fused kernel.
+ *   [HL-hgrn]    same page, section "HGRN attention": block input -> RMSNorm -> i/f/g
+ *                projections -> gated recurrence -> g_norm (RMSNorm fused with a swish gate)
+ *                -> o_proj; default model: hidden 2048, vocabulary 32000, 24 layers.
+ *
+ * Arithmetic, shared by every entry point:
+ *   - activation quantization of a row x[0..K) with gain gamma: p = fl32(x*gamma),
+ *     m = max(max|p|, 1e-5), s = fl32(127/m), q = clamp(rint(fl32(p*s)), -127, 127)
+ *     (round half to even), a = m/127 * rsqrt(mean(x^2) + eps).  The RMSNorm factor cancels
+ *     in the absmax ratio, so it enters only the dequantization scale a;
+ *   - accumulation acc[m][n] = sum_k q_x[m][k] * q_w[n][k] in int32 (exact);
+ *   - rescale y = acc * s_w * a[m] (+ bias[n]) in fp32;
+ *   - MLGRU: f = sigmoid(f_pre + b_f), c = SiLU(i_pre), h_t = f*h_{t-1} + (1-f)*c (fp32
+ *     state); output gate o = RMSNorm_D(h)*gnorm_w * g*sigmoid(g) (MMF_GATE_SWISH_RMSNORM)
+ *     or sigmoid(g)*h (MMF_GATE_SIGMOID);
+ *   - GLU: SiLU(gate(x)) * up(x), then down;
+ *   - block: y1 = x + o_proj(MLGRU(x)); y = y1 + GLU(y1).  Activations that leave a
+ *     kernel are stored in the activation dtype (bf16 or fp32); the state h is fp32.
+ *
+ * Packed ternary weights: a matrix [N][K] (row n = output feature, K % 64 == 0) is stored
+ * as N*K/16 uint32 words, row-major; element k = 16*j + 4*a + b of a row sits in word j at
+ * bits 8*b + 2*a .. 8*b + 2*a + 1 as code = q + 1 (0 -> -1, 1 -> 0, 2 -> +1; 3 invalid).
+ * One fp32 scale per matrix (absmean is per matrix).
+ *
+ * Conventions for every entry point below:
+ *   - tensor pointers are DEVICE pointers owned by the caller (unless marked host) and must
+ *     stay valid until the work queued on the stream has finished;
+ *   - the library never allocates or frees device memory inside a forward call; all
+ *     scratch comes from the caller's workspace `ws` (size from the *_workspace_bytes call);
+ *   - nothing synchronises the stream; work is queued on `stream` (NULL = null stream);
+ *   - arguments are validated before anything is queued: on a non-zero return nothing was
+ *     queued and mmf_last_error() (thread-local) says why.  Device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI;
+ *   - x, y, packed weights and workspaces must be 16-byte aligned;
+ *   - every entry point is thread-safe; calls that share a workspace must be ordered.
+ */
+#ifndef MMF_H
+#define MMF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMF_ABI_VERSION 1
+
+/* Status codes. */
+#define MMF_OK 0
+#define MMF_EINVAL (-1)     /* NULL where required, bad enum, invalid packed code */
+#define MMF_ESHAPE (-2)     /* K % 64 != 0, mismatched dims, negative sizes */
+#define MMF_EALIGN (-3)     /* a pointer is not 16-byte aligned */
+#define MMF_EDTYPE (-4)     /* unsupported dtype */
+#define MMF_EWORKSPACE (-5) /* workspace NULL or smaller than required */
+#define MMF_EHIP (-6)       /* a HIP call failed (message carries hipGetErrorString) */
+#define MMF_EDEVICE (-7)    /* current device is not gfx950 */
+
+typedef enum mmf_dtype { MMF_F32 = 0, MMF_BF16 = 1 } mmf_dtype;
+
+typedef enum mmf_gate_mode {
+    MMF_GATE_SWISH_RMSNORM = 0, /* g_norm: RMSNorm_D(h) * gnorm_w * g * sigmoid(g) */
+    MMF_GATE_SIGMOID = 1        /* sigmoid(g) * h */
+} mmf_gate_mode;
+
+/* One BitLinear ([DC-ternary], [HL-fbl]). */
+typedef struct mmf_bitlinear {
+    const uint32_t *packed; /* device [N][K/16] packed ternary codes */
+    float scale;            /* absmean scale s_w of the matrix */
+    const float *norm_w;    /* device [K] RMSNorm gain of the input, or NULL (ones) */
+    const float *bias;      /* device [N] or NULL */
+    float eps;              /* RMSNorm epsilon of the input (1e-6 if unsure) */
+    int32_t K, N;
+} mmf_bitlinear;
+
+/* One block ([HL-hgrn], [DC-core]).  i, f, g, o: [D][D]; gate, up: [F][D]; down: [D][F].
+ * i, f, g must share norm_w (same pointer or all NULL) and eps, as must gate and up: each
+ * group quantizes its shared input once. */
+typedef struct mmf_block {
+    mmf_bitlinear i, f, g, o, gate, up, down;
+    const float *f_bias;  /* device [D] forget-gate bias, or NULL (zeros) */
+    const float *gnorm_w; /* device [D] g_norm gain, or NULL (ones) */
+    float eps;            /* g_norm epsilon */
+    int32_t gate_mode;    /* mmf_gate_mode */
+} mmf_block;
+
+/* Optional record of one BitLinear stage for token rows [row0, row1) (device buffers,
+ * any may be NULL): the fp32 input exactly as quantized, its int8 codes, its scale a, and
+ * the int32 accumulators acc = sum_k q_x * q_w.  For a group of projections sharing an
+ * input (i|f|g, gate|up) acc has the group's concatenated width (3D or 2F) in that order. */
+typedef struct mmf_stage_capture {
+    int64_t row0, row1;
+    float *x_in;   /* [rows][K] */
+    int8_t *q;     /* [rows][K] */
+    float *a;      /* [rows] */
+    int32_t *acc;  /* [rows][N] */
+} mmf_stage_capture;
+
+typedef struct mmf_capture {
+    mmf_stage_capture ifg, o, gateup, down;
+} mmf_capture;
+
+/* ------------------------------------------------------------------ library state */
+
+/* ABI version (MMF_ABI_VERSION). */
+int mmf_abi_version(void);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char *mmf_last_error(void);
+
+/* Test knob, process-wide: 0 = choose the BitLinear regime by token count (default),
+ * 1 = force the decode (weight-streaming) kernels, 2 = force the prefill (MFMA) kernels.
+ * Returns the previous value, or MMF_EINVAL for another value. */
+int mmf_set_regime(int regime);
+
+/* Per-kernel launch timing with HIP events recorded on the launch stream around every
+ * launch of the named kernel family.  enable: 1 on, 0 off (events are kept).  After the
+ * stream has been synchronised, mmf_timing_query returns the number of timed launches and
+ * their summed duration in ms for a family name (see mmf_timing_name); reset clears them. */
+int mmf_timing_enable(int enable);
+int mmf_timing_reset(void);
+int mmf_timing_query(const char *family, int64_t *launches, double *total_ms);
+/* Name of family i (0 <= i < mmf_timing_count()), or NULL. */
+const char *mmf_timing_name(int i);
+int mmf_timing_count(void);
+
+/* --------------------------------------------------------- host weight preparation */
+
+/* Absmean ternarization [DC-ternary], on HOST memory: s = max(mean|w|, 1e-5) with the mean
+ * summed in double per row (k ascending) and over rows (n ascending);
+ * q = clamp(rint(w / s), -1, 1) (fp32 division, ties to even).  w [n][k] host fp32,
+ * q_out [n][k] host int8, *scale_out host.  MMF_EINVAL on NULL, MMF_ESHAPE on n,k <= 0. */
+int mmf_ternary_quantize(const float *w, int64_t n, int64_t k, int8_t *q_out,
+                         float *scale_out);
+
+/* Pack q [n][k] in {-1,0,1} (host) into the 2-bit format (host, [n][k/16] words).
+ * MMF_ESHAPE unless k % 16 == 0; MMF_EINVAL on a value outside {-1,0,1}. */
+int mmf_ternary_pack(const int8_t *q, int64_t n, int64_t k, uint32_t *packed);
+
+/* Unpack (host -> host).  MMF_EINVAL on code 3 anywhere. */
+int mmf_ternary_unpack(const uint32_t *packed, int64_t n, int64_t k, int8_t *q);
+
+/* ------------------------------------------------------------------- forward calls */
+
+/* Scratch bytes bitlinear_forward needs for m token rows of w. */
+size_t bitlinear_workspace_bytes(const mmf_bitlinear *w, int64_t m);
+
+/* y[m][N] = BitLinear(x[m][K]) [HL-fbl]: RMSNorm + int8 quantization of each row of x,
+ * ternary accumulation, rescale (+ bias).  x dtype x_dt, y dtype y_dt.  m == 0 is a no-op.
+ * The regime (weight-streaming decode kernel vs int8-MFMA prefill kernel) is chosen from m.
+ * cap (nullable) records the stage for its row window. */
+int bitlinear_forward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
+                      void *y, mmf_dtype y_dt, void *ws, size_t ws_bytes,
+                      const mmf_stage_capture *cap, hipStream_t stream);
+
+/* MLGRU token mixer + output gate [DC-core], [HL-hgrn], without the o_proj. */
+typedef struct mmf_mlgru_args {
+    const void *ifg;       /* device [B][T][3D]: pre-activations i | f | g (ifg_dt) */
+    mmf_dtype ifg_dt;
+    const float *f_bias;   /* [D] or NULL */
+    const float *h0;       /* [B][D] fp32 initial state, or NULL (zeros) */
+    float *h_out;          /* [B][D] fp32 final state h_T, or NULL; may equal h0 */
+    const float *gnorm_w;  /* [D] or NULL */
+    float eps;
+    int32_t gate_mode;     /* mmf_gate_mode */
+    void *out;             /* [B][T][D] gated output (out_dt) */
+    mmf_dtype out_dt;
+    int64_t B, T, D;       /* D % 64 == 0, D <= 4096 */
+} mmf_mlgru_args;
+
+size_t mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);
+
+/* Chunked scan: parallel over (b, d), chunked over T with a carry pass between chunks. */
+int mlgru_scan(const mmf_mlgru_args *args, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* GLU channel mixer [DC-core]: y = down(SiLU(gate(x)) * up(x)) (+ residual if non-NULL).
+ * x, residual, y: [m][D] of dtype dt.  gate, up: [F][D]; down: [D][F]. */
+size_t glu_workspace_bytes(const mmf_bitlinear *gate, const mmf_bitlinear *down, int64_t m);
+int glu_forward(const mmf_bitlinear *gate, const mmf_bitlinear *up,
+                const mmf_bitlinear *down, const void *x, mmf_dtype dt, int64_t m,
+                const void *residual, void *y, void *ws, size_t ws_bytes,
+                const mmf_capture *cap, hipStream_t stream);
+
+/* One block [HL-hgrn]: x [B][T][D] (dt) -> y [B][T][D] (dt).  h_state: [B][D] fp32 state,
+ * read as h_0 and overwritten with h_T (NULL: h_0 = 0, h_T dropped).  T == 1 with h_state
+ * is one decode step.  cap (nullable) records each BitLinear stage. */
+size_t block_workspace_bytes(const mmf_block *w, int64_t B, int64_t T);
+int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
+                  float *h_state, void *y, void *ws, size_t ws_bytes,
+                  const mmf_capture *cap, hipStream_t stream);
+
+/* Ternary embedding gather: x[t][:] = s_E * q_E[ids[t]][:], rounded to dt.
+ * packed [vocab][D/16]; ids device int32 [m]; an id outside [0, vocab) yields a zero row. */
+int embedding_forward(const uint32_t *packed, float scale, int64_t vocab, int64_t D,
+                      const int32_t *ids, int64_t m, void *x, mmf_dtype dt,
+                      hipStream_t stream);
+
+/* A stack of blocks [HL-hgrn] with optional ternary embedding (ids -> x) and head
+ * (x_L -> logits, a BitLinear whose input RMSNorm is the final norm). */
+typedef struct mmf_stack {
+    const mmf_block *blocks;      /* HOST array of n_layers block descriptors */
+    int32_t n_layers;
+    const uint32_t *embed_packed; /* device [vocab][D/16] or NULL */
+    float embed_scale;
+    int64_t vocab;
+    const mmf_bitlinear *head;    /* HOST pointer to the head descriptor, or NULL */
+} mmf_stack;
+
+size_t stack_workspace_bytes(const mmf_stack *s, int64_t B, int64_t T);
+
+/* ids [B*T] (device int32) when the stack has an embedding, else x [B][T][D] (dt).
+ * h_state [n_layers][B][D] fp32 in/out or NULL.  y [B][T][D] (dt) receives x_L (nullable
+ * when logits are requested); logits [B*T][vocab] fp32 (nullable; needs a head). */
+int stack_forward(const mmf_stack *s, const int32_t *ids, const void *x, mmf_dtype dt,
+                  int64_t B, int64_t T, float *h_state, void *y, float *logits, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMF_H */

@@ -1,0 +1,356 @@
+"""Python binding of libmmf: argument marshalling around the C ABI of include/mmf.h.
+
+PyTorch provides device memory and the stream; every step of the forward pass runs in
+the HIP kernels of libmmf.  Names follow the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.MMF_F32, torch.bfloat16: L.MMF_BF16}
+
+
+def _dt(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+    return _DT[t]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _host(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+# ------------------------------------------------------------------ host weight prep
+
+def quantize_ternary(w: np.ndarray) -> tuple[np.ndarray, float]:
+    """Absmean ternarization on the host (mmf_ternary_quantize)."""
+    w, wp = _host(w, np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), np.int8)
+    s = np.zeros(1, np.float32)
+    L.check("mmf_ternary_quantize",
+            L.lib().mmf_ternary_quantize(wp, n, k, q.ctypes.data_as(C.c_void_p),
+                                         s.ctypes.data_as(C.c_void_p)))
+    return q, float(s[0])
+
+
+def pack_ternary(q: np.ndarray) -> np.ndarray:
+    q, qp = _host(q, np.int8)
+    n, k = q.shape
+    out = np.empty((n, k // 16), np.uint32)
+    L.check("mmf_ternary_pack", L.lib().mmf_ternary_pack(qp, n, k, out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+def unpack_ternary(packed: np.ndarray, k: int) -> np.ndarray:
+    packed, pp = _host(packed, np.uint32)
+    n = packed.shape[0]
+    q = np.empty((n, k), np.int8)
+    L.check("mmf_ternary_unpack", L.lib().mmf_ternary_unpack(pp, n, k, q.ctypes.data_as(C.c_void_p)))
+    return q
+
+
+@dataclass
+class TernaryLinear:
+    """A BitLinear on the device: packed ternary codes [N][K/16] + absmean scale."""
+    packed: torch.Tensor          # int32 view of the uint32 words, [N, K/16]
+    scale: float
+    K: int
+    N: int
+    norm_w: torch.Tensor | None = None
+    bias: torch.Tensor | None = None
+    eps: float = 1e-6
+
+    @classmethod
+    def from_latent(cls, w: np.ndarray, device="cuda", norm_w=None, bias=None, eps=1e-6):
+        q, s = quantize_ternary(w)
+        return cls.from_ternary(q, s, device, norm_w, bias, eps)
+
+    @classmethod
+    def from_ternary(cls, q: np.ndarray, scale: float, device="cuda", norm_w=None, bias=None,
+                     eps=1e-6):
+        packed = pack_ternary(q)
+        t = torch.from_numpy(packed.view(np.int32)).to(device)
+        nw = None if norm_w is None else torch.as_tensor(norm_w, dtype=torch.float32, device=device)
+        b = None if bias is None else torch.as_tensor(bias, dtype=torch.float32, device=device)
+        return cls(t, float(scale), q.shape[1], q.shape[0], nw, b, eps)
+
+    def desc(self) -> L.mmf_bitlinear:
+        return L.mmf_bitlinear(_ptr(self.packed), self.scale, _ptr(self.norm_w), _ptr(self.bias),
+                               self.eps, self.K, self.N)
+
+
+# ------------------------------------------------------------------ captures
+
+@dataclass
+class StageCapture:
+    """Device buffers recording one BitLinear stage for token rows [row0, row1)."""
+    row0: int
+    row1: int
+    x_in: torch.Tensor
+    q: torch.Tensor
+    a: torch.Tensor
+    acc: torch.Tensor
+
+    @classmethod
+    def alloc(cls, row0, row1, K, N, device="cuda"):
+        r = row1 - row0
+        return cls(row0, row1, torch.full((r, K), float("nan"), device=device),
+                   torch.full((r, K), -128, dtype=torch.int8, device=device),
+                   torch.full((r,), float("nan"), device=device),
+                   torch.full((r, N), -2**31, dtype=torch.int32, device=device))
+
+    def desc(self) -> L.mmf_stage_capture:
+        return L.mmf_stage_capture(self.row0, self.row1, _ptr(self.x_in), _ptr(self.q),
+                                   _ptr(self.a), _ptr(self.acc))
+
+    def host(self) -> dict:
+        return {k: getattr(self, k).cpu().numpy() for k in ("x_in", "q", "a", "acc")}
+
+
+@dataclass
+class BlockCapture:
+    ifg: StageCapture
+    o: StageCapture
+    gateup: StageCapture
+    down: StageCapture
+
+    @classmethod
+    def alloc(cls, row0, row1, D, F, device="cuda"):
+        return cls(StageCapture.alloc(row0, row1, D, 3 * D, device),
+                   StageCapture.alloc(row0, row1, D, D, device),
+                   StageCapture.alloc(row0, row1, D, 2 * F, device),
+                   StageCapture.alloc(row0, row1, F, D, device))
+
+    def desc(self) -> L.mmf_capture:
+        return L.mmf_capture(self.ifg.desc(), self.o.desc(), self.gateup.desc(), self.down.desc())
+
+
+def _empty_stage():
+    return L.mmf_stage_capture(0, 0, None, None, None, None)
+
+
+# ------------------------------------------------------------------ forward calls
+
+def set_regime(regime: int) -> int:
+    """0 auto, 1 force decode kernels, 2 force prefill kernels (test knob)."""
+    r = L.lib().mmf_set_regime(int(regime))
+    if r < 0:
+        L.check("mmf_set_regime", r)
+    return r
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def bitlinear_forward(w: TernaryLinear, x: torch.Tensor, out_dtype=None,
+                      capture: StageCapture | None = None, stream=None) -> torch.Tensor:
+    """y[m, N] = BitLinear(x[m, K]) (bitlinear_forward)."""
+    lib = L.lib()
+    x = x.contiguous()
+    m = x.numel() // w.K
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    y = torch.empty(x.shape[:-1] + (w.N,), dtype=out_dtype, device=x.device)
+    d = w.desc()
+    nb = lib.bitlinear_workspace_bytes(C.byref(d), m)
+    ws = _workspace(nb, x.device)
+    cap = C.byref(capture.desc()) if capture is not None else None
+    L.check("bitlinear_forward",
+            lib.bitlinear_forward(C.byref(d), _ptr(x), _dt(x.dtype), m, _ptr(y), _dt(out_dtype),
+                                  _ptr(ws), nb, cap, _stream(stream)))
+    return y
+
+
+def mlgru_scan(ifg: torch.Tensor, f_bias=None, h0=None, gnorm_w=None, eps: float = 1e-6,
+               gate_mode: int = 0, out_dtype=None, h_out: torch.Tensor | None = None,
+               stream=None):
+    """MLGRU + output gate over ifg [B, T, 3D] (mlgru_scan).  Returns (out, h_T)."""
+    lib = L.lib()
+    ifg = ifg.contiguous()
+    B, T, D3 = ifg.shape
+    D = D3 // 3
+    out_dtype = ifg.dtype if out_dtype is None else out_dtype
+    out = torch.empty((B, T, D), dtype=out_dtype, device=ifg.device)
+    if h_out is None:
+        h_out = torch.empty((B, D), dtype=torch.float32, device=ifg.device)
+    a = L.mmf_mlgru_args(_ptr(ifg), _dt(ifg.dtype), _ptr(f_bias), _ptr(h0), _ptr(h_out),
+                         _ptr(gnorm_w), eps, gate_mode, _ptr(out), _dt(out_dtype), B, T, D)
+    nb = lib.mlgru_workspace_bytes(B, T, D)
+    ws = _workspace(nb, ifg.device)
+    L.check("mlgru_scan", lib.mlgru_scan(C.byref(a), _ptr(ws), nb, _stream(stream)))
+    return out, h_out
+
+
+def glu_forward(gate: TernaryLinear, up: TernaryLinear, down: TernaryLinear, x: torch.Tensor,
+                residual: torch.Tensor | None = None, capture: BlockCapture | None = None,
+                stream=None) -> torch.Tensor:
+    """y = down(SiLU(gate(x)) * up(x)) (+ residual) (glu_forward)."""
+    lib = L.lib()
+    x = x.contiguous()
+    m = x.numel() // gate.K
+    y = torch.empty_like(x)
+    dg, du, dd = gate.desc(), up.desc(), down.desc()
+    nb = lib.glu_workspace_bytes(C.byref(dg), C.byref(dd), m)
+    ws = _workspace(nb, x.device)
+    cap = None
+    if capture is not None:
+        cap = L.mmf_capture(_empty_stage(), _empty_stage(), capture.gateup.desc(), capture.down.desc())
+    L.check("glu_forward",
+            lib.glu_forward(C.byref(dg), C.byref(du), C.byref(dd), _ptr(x), _dt(x.dtype), m,
+                            _ptr(residual.contiguous() if residual is not None else None), _ptr(y),
+                            _ptr(ws), nb, C.byref(cap) if cap is not None else None,
+                            _stream(stream)))
+    return y
+
+
+@dataclass
+class Block:
+    """One MatMul-free block: i, f, g, o [D, D]; gate, up [F, D]; down [D, F]."""
+    i: TernaryLinear
+    f: TernaryLinear
+    g: TernaryLinear
+    o: TernaryLinear
+    gate: TernaryLinear
+    up: TernaryLinear
+    down: TernaryLinear
+    f_bias: torch.Tensor | None = None
+    gnorm_w: torch.Tensor | None = None
+    eps: float = 1e-6
+    gate_mode: int = 0
+    _desc: L.mmf_block | None = field(default=None, repr=False)
+
+    @property
+    def D(self) -> int:
+        return self.i.K
+
+    @property
+    def F(self) -> int:
+        return self.gate.N
+
+    @classmethod
+    def from_latents(cls, lat: dict, device="cuda", f_bias=None, gnorm_w=None, eps=1e-6,
+                     gate_mode=0):
+        mats = {k: TernaryLinear.from_latent(lat[k], device, eps=eps)
+                for k in ("i", "f", "g", "o", "gate", "up", "down")}
+        fb = None if f_bias is None else torch.as_tensor(f_bias, dtype=torch.float32, device=device)
+        gw = None if gnorm_w is None else torch.as_tensor(gnorm_w, dtype=torch.float32, device=device)
+        return cls(**mats, f_bias=fb, gnorm_w=gw, eps=eps, gate_mode=gate_mode)
+
+    def desc(self) -> L.mmf_block:
+        if self._desc is None:
+            self._desc = L.mmf_block(self.i.desc(), self.f.desc(), self.g.desc(), self.o.desc(),
+                                     self.gate.desc(), self.up.desc(), self.down.desc(),
+                                     _ptr(self.f_bias), _ptr(self.gnorm_w), self.eps,
+                                     self.gate_mode)
+        return self._desc
+
+
+def block_workspace_bytes(block: Block, B: int, T: int) -> int:
+    d = block.desc()
+    return int(L.lib().block_workspace_bytes(C.byref(d), B, T))
+
+
+def block_forward(block: Block, x: torch.Tensor, h_state: torch.Tensor | None = None,
+                  y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  capture: BlockCapture | None = None, stream=None) -> torch.Tensor:
+    """One block forward on x [B, T, D] (block_forward); h_state [B, D] fp32 is updated."""
+    lib = L.lib()
+    B, T, D = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    d = block.desc()
+    nb = lib.block_workspace_bytes(C.byref(d), B, T)
+    if ws is None or ws.numel() < nb:
+        ws = _workspace(nb, x.device)
+    cap = C.byref(capture.desc()) if capture is not None else None
+    L.check("block_forward",
+            lib.block_forward(C.byref(d), _ptr(x), _dt(x.dtype), B, T, _ptr(h_state), _ptr(y),
+                              _ptr(ws), ws.numel(), cap, _stream(stream)))
+    return y
+
+
+def embedding_forward(packed: torch.Tensor, scale: float, vocab: int, D: int,
+                      ids: torch.Tensor, dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    x = torch.empty(ids.shape + (D,), dtype=dtype, device=ids.device)
+    L.check("embedding_forward",
+            L.lib().embedding_forward(_ptr(packed), scale, vocab, D, _ptr(ids), ids.numel(),
+                                      _ptr(x), _dt(dtype), _stream(stream)))
+    return x
+
+
+class Stack:
+    """L blocks with an optional ternary embedding and head."""
+
+    def __init__(self, blocks: list[Block], embed: TernaryLinear | None = None,
+                 head: TernaryLinear | None = None):
+        self.blocks = blocks
+        self.embed = embed
+        self.head = head
+        arr = (L.mmf_block * len(blocks))(*[b.desc() for b in blocks])
+        self._arr = arr
+        self._head = head.desc() if head is not None else None
+        self._desc = L.mmf_stack(arr, len(blocks),
+                                 _ptr(embed.packed) if embed is not None else None,
+                                 embed.scale if embed is not None else 0.0,
+                                 embed.N if embed is not None else 0,
+                                 C.pointer(self._head) if self._head is not None else None)
+
+    def workspace_bytes(self, B: int, T: int) -> int:
+        return int(L.lib().stack_workspace_bytes(C.byref(self._desc), B, T))
+
+
+def stack_forward(stack: Stack, B: int, T: int, ids: torch.Tensor | None = None,
+                  x: torch.Tensor | None = None, h_state: torch.Tensor | None = None,
+                  dtype=torch.bfloat16, want_y: bool = True, want_logits: bool = False,
+                  ws: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                  logits: torch.Tensor | None = None, stream=None):
+    """Run the stack (stack_forward).  Returns (y or None, logits or None)."""
+    lib = L.lib()
+    dev = (ids if ids is not None else x).device
+    D = stack.blocks[0].D
+    if want_y and y is None:
+        y = torch.empty((B, T, D), dtype=dtype, device=dev)
+    if want_logits and logits is None:
+        logits = torch.empty((B * T, stack.head.N), dtype=torch.float32, device=dev)
+    nb = stack.workspace_bytes(B, T)
+    if ws is None or ws.numel() < nb:
+        ws = _workspace(nb, dev)
+    L.check("stack_forward",
+            lib.stack_forward(C.byref(stack._desc), _ptr(ids), _ptr(x), _dt(dtype), B, T,
+                              _ptr(h_state), _ptr(y) if want_y else None,
+                              _ptr(logits) if want_logits else None, _ptr(ws), ws.numel(),
+                              _stream(stream)))
+    return (y if want_y else None), (logits if want_logits else None)
+
+
+def timing_enable(on: bool = True) -> None:
+    L.check("mmf_timing_enable", L.lib().mmf_timing_enable(int(on)))
+
+
+def timing_reset() -> None:
+    L.check("mmf_timing_reset", L.lib().mmf_timing_reset())
+
+
+def timing_query(family: str) -> tuple[int, float]:
+    n = C.c_int64(0)
+    ms = C.c_double(0.0)
+    L.check("mmf_timing_query",
+            L.lib().mmf_timing_query(family.encode(), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)

@@ -1,0 +1,227 @@
+// mmf_internal.h -- declarations shared by the host dispatch code and the HIP kernels of
+// libmmf (gfx950).  Not part of the public ABI (include/mmf.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "mmf.h"
+
+namespace mmf {
+
+// ------------------------------------------------------------------ device helpers
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float round_to_bf16(float f) {
+    return bf16_bits_to_f32(f32_to_bf16_bits(f));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_act(const void *p, int64_t i) {
+    if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else return static_cast<const float *>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_act(void *p, int64_t i, float v) {
+    if constexpr (BF16) static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
+    else static_cast<float *>(p)[i] = v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float siluf_(float z) { return z / (1.0f + expf(-z)); }
+
+// Wave-wide (64 lanes) reductions through cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Ternary unpack: word j of a packed row holds k = 16j + 4a + b at bits 8b + 2a; the
+// dword (w >> 2a) & 0x03030303 therefore holds the codes of k = 16j + 4a + 0..3 as four
+// int8 lanes.  The returned 128-bit vector holds the 16 codes of word j in k order.
+__device__ __forceinline__ v4i unpack_codes(uint32_t w) {
+    v4i r;
+    r.x = static_cast<int>(w & 0x03030303u);
+    r.y = static_cast<int>((w >> 2) & 0x03030303u);
+    r.z = static_cast<int>((w >> 4) & 0x03030303u);
+    r.w = static_cast<int>((w >> 6) & 0x03030303u);
+    return r;
+}
+
+// ------------------------------------------------------------ launch descriptors
+
+// Kernel families for per-launch timing (host side, mmf_api.cpp).
+enum Family : int {
+    FAM_QUANT = 0,
+    FAM_GEMM_IFG,
+    FAM_GEMM_O,
+    FAM_GEMM_GATEUP,
+    FAM_GEMM_DOWN,
+    FAM_GEMM_OTHER,
+    FAM_GEMV,
+    FAM_SCAN,
+    FAM_EMBED,
+    FAM_COUNT
+};
+
+void timing_begin(int family, hipStream_t s);
+void timing_end(int family, hipStream_t s);
+
+
+// Optional stage capture, in device pointers (see mmf_stage_capture).
+struct CapDev {
+    int64_t row0 = 0, row1 = 0;
+    float *x_in = nullptr;
+    int8_t *q = nullptr;
+    float *a = nullptr;
+    int32_t *acc = nullptr;
+    int32_t acc_ld = 0;   // row stride of acc (group width)
+    int32_t acc_col0 = 0; // column offset of this launch inside the group
+};
+
+// Row quantizer: x [M][K] -> q [M][K] int8, a [M], rowsum [M].
+struct QuantArgs {
+    const void *x;
+    int x_bf16;
+    const float *gamma;
+    float eps;
+    int64_t M;
+    int32_t K;
+    int8_t *q;
+    float *a;
+    int32_t *rowsum;
+    CapDev cap;
+};
+
+// One weight matrix inside a (possibly concatenated) BitLinear launch.
+struct Seg {
+    const uint32_t *packed = nullptr;
+    const float *bias = nullptr;
+    float scale = 0.f;
+    int32_t n = 0;        // rows of this matrix
+    int32_t out_col0 = 0; // first output column of this matrix
+    int32_t cap_col0 = 0; // first capture column of this matrix
+};
+
+enum Epi : int {
+    EPI_STORE = 0,  // y = acc*s*a (+bias)
+    EPI_RESID = 1,  // y = resid + acc*s*a (+bias)
+    EPI_GLU = 2     // segments 0,1 = gate,up: y = SiLU(gate) * up
+};
+
+// Prefill int8-MFMA GEMM with ternary weights.
+struct GemmArgs {
+    const int8_t *A;       // [M][K] int8 activations
+    const int32_t *rowsum; // [M]
+    const float *a;        // [M]
+    int64_t M;
+    int32_t K;
+    Seg seg[3];
+    int32_t nseg;
+    int32_t tiles_n[3];    // N tiles per segment (EPI_GLU: tiles of 64 gate/up pairs)
+    int32_t tiles_n_total;
+    int32_t epi;
+    void *out;
+    int32_t ldo;
+    int32_t out_bf16;
+    const void *resid;     // [M][ldr] (EPI_RESID), same dtype as out
+    int32_t ldr;
+    CapDev cap;            // acc capture only
+    int32_t family = FAM_GEMM_OTHER;
+};
+
+// Decode GEMV (weight streaming).  Input either raw activations (quantized in the
+// prologue) or pre-quantized rows.
+struct GemvArgs {
+    const void *x;         // [M][K] raw activations, or NULL when q is given
+    int32_t x_bf16;
+    const float *gamma;
+    float eps;
+    const int8_t *q;       // [M][K] pre-quantized (when x == NULL)
+    const float *a;
+    const int32_t *rowsum;
+    int64_t M;
+    int32_t K;
+    Seg seg[3];
+    int32_t nseg;
+    int32_t rows_total;    // sum of segment rows (EPI_GLU: F, the pair count)
+    int32_t epi;
+    void *out;
+    int32_t ldo;
+    int32_t out_bf16;
+    const void *resid;     // same dtype as out
+    int32_t ldr;
+    int32_t tokens_per_group;  // rows of q staged in LDS per workgroup (<= kGemvTokens)
+    CapDev cap;            // x_in/q/a written by column-block 0, acc by every block
+};
+
+// MLGRU scan.
+struct ScanArgs {
+    const void *ifg;       // [B][T][3D]
+    int32_t ifg_bf16;
+    const float *f_bias;
+    const float *h0;
+    float *h_out;
+    const float *gnorm_w;
+    float eps;
+    int32_t gate_mode;
+    int64_t B, T;
+    int32_t D;
+    int32_t chunk;         // tokens per chunk
+    int32_t n_chunks;
+    float *hloc;           // [B][n_chunks][D] local end state (phase 1)
+    float *pf;             // [B][n_chunks][D] product of f over the chunk (phase 1)
+    float *hin;            // [B][n_chunks][D] state entering each chunk (phase 2)
+    // output: either the gated activation or its int8 quantization for o_proj
+    void *out;             // [B*T][D] (out_bf16) when q == NULL
+    int32_t out_bf16;
+    int32_t round_bf16;    // round the gated output to bf16 before quantizing
+    int8_t *q;             // [B*T][D]
+    float *a;
+    int32_t *rowsum;
+    const float *q_gamma;  // o_proj input gain
+    float q_eps;           // o_proj input eps
+    CapDev cap;            // x_in/q/a of the o_proj stage
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
+                            const int32_t *ids, int64_t m, void *x, int bf16,
+                            hipStream_t s);
+hipError_t launch_copy_state(const float *h0, float *h_out, int64_t n, hipStream_t s);
+
+// Tokens per decode-kernel token group (rows of q staged in LDS).
+constexpr int kGemvTokens = 8;
+// Chunk length of the prefill scan.
+constexpr int kScanChunk = 32;
+
+}  // namespace mmf

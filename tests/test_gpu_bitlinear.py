@@ -1,0 +1,105 @@
+"""BitLinear parity on the GPU: int8 codes and int32 accumulators bit-exact against the
+oracle, rescaled outputs within tolerance, in both regimes (decode weight streaming and
+prefill MFMA) at shapes spanning several tiles, ragged tails and the real layer shapes."""
+import numpy as np
+import pytest
+import torch
+
+from ternary_weight_matmul_bitlinear_amd import api, synth
+from tests.gpu_helpers import TOL, dev, host, note, rel_check
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # M, K, N, dtype, gamma, bias
+    (1, 256, 256, torch.float32, False, False),
+    (64, 256, 256, torch.float32, True, True),
+    (3, 2048, 6144, torch.bfloat16, False, False),
+    (8, 1024, 200, torch.bfloat16, True, False),
+    (300, 512, 384, torch.bfloat16, False, True),
+    (129, 1024, 130, torch.float32, False, False),
+    (16, 5632, 2048, torch.bfloat16, False, False),
+    (1, 6912, 2560, torch.bfloat16, True, False),
+    (257, 2816, 1024, torch.bfloat16, False, False),
+]
+
+
+@pytest.fixture(autouse=True)
+def _restore_regime():
+    prev = api.set_regime(0)
+    yield
+    api.set_regime(prev)
+
+
+@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("M,K,N,dt,use_gamma,use_bias", CASES,
+                         ids=[f"M{c[0]}K{c[1]}N{c[2]}{'bf' if c[3] == torch.bfloat16 else 'f'}"
+                              for c in CASES])
+def test_bitlinear_parity(orc, regime, M, K, N, dt, use_gamma, use_bias):
+    note(f"bitlinear regime={regime} M={M} K={K} N={N} dt={dt}")
+    seed = M * 7919 + K * 31 + N
+    x = synth.gaussian(seed, (M, K))
+    if dt == torch.bfloat16:
+        x = synth.round_to_bf16(x)
+    lat = synth.gaussian(seed + 1, (N, K), 0.02)
+    gamma = (1.0 + 0.2 * synth.gaussian(seed + 2, (K,))).astype(np.float32) if use_gamma else None
+    bias = synth.gaussian(seed + 3, (N,)) if use_bias else None
+    q_l, s_l = api.quantize_ternary(lat)
+    q_o, s_o = orc.ternarize(lat)
+    assert s_l == s_o and np.array_equal(q_l, q_o)
+    w = api.TernaryLinear.from_ternary(q_l, s_l, norm_w=gamma, bias=bias)
+    api.set_regime(regime)
+    cap = api.StageCapture.alloc(0, M, K, N)
+    y = api.bitlinear_forward(w, dev(x, dt), out_dtype=torch.float32, capture=cap)
+    torch.cuda.synchronize()
+    c = cap.host()
+    y_o, qx_o, a_o, acc_o = orc.bitlinear(x, q_o, s_o, gamma=gamma, bias=bias)
+    assert np.array_equal(c["x_in"], x)
+    assert np.array_equal(c["q"], qx_o), "int8 activations differ"
+    assert np.array_equal(c["acc"], acc_o), "int32 accumulators differ"
+    np.testing.assert_allclose(c["a"], a_o, rtol=2e-5)
+    rel_check(host(y), y_o, TOL[torch.float32], "y")
+
+
+@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+def test_bitlinear_bf16_output_and_zero_rows(orc, regime):
+    """bf16 output; an all-zero input row gives exactly the bias (acc = 0)."""
+    M, K, N = 40, 512, 320
+    note(f"bitlinear zero rows regime={regime}")
+    x = synth.round_to_bf16(synth.gaussian(5, (M, K)))
+    x[7] = 0.0
+    lat = synth.gaussian(6, (N, K), 0.02)
+    bias = synth.gaussian(7, (N,))
+    q, s = api.quantize_ternary(lat)
+    w = api.TernaryLinear.from_ternary(q, s, bias=bias)
+    api.set_regime(regime)
+    y = api.bitlinear_forward(w, dev(x, torch.bfloat16), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y_o, _, _, acc_o = orc.bitlinear(x, q, s, bias=bias)
+    assert not acc_o[7].any()
+    rel_check(host(y), y_o, TOL[torch.bfloat16], "y bf16")
+    assert np.array_equal(host(y)[7], host(torch.from_numpy(bias).to(torch.bfloat16)))
+
+
+def test_bitlinear_empty_is_noop():
+    lat = synth.gaussian(8, (64, 256), 0.02)
+    w = api.TernaryLinear.from_latent(lat)
+    y = api.bitlinear_forward(w, torch.zeros((0, 256), device="cuda"))
+    assert y.shape == (0, 64)
+
+
+def test_regimes_agree_bit_exact_on_integers():
+    """Decode and prefill kernels produce identical int8 codes and accumulators."""
+    M, K, N = 24, 2048, 700
+    note("bitlinear regimes agree")
+    x = synth.round_to_bf16(synth.gaussian(9, (M, K)))
+    w = api.TernaryLinear.from_latent(synth.gaussian(10, (N, K), 0.02))
+    out = {}
+    for r in (1, 2):
+        api.set_regime(r)
+        cap = api.StageCapture.alloc(0, M, K, N)
+        api.bitlinear_forward(w, dev(x, torch.bfloat16), capture=cap)
+        torch.cuda.synchronize()
+        out[r] = cap.host()
+    assert np.array_equal(out[1]["q"], out[2]["q"])
+    assert np.array_equal(out[1]["acc"], out[2]["acc"])

@@ -1,0 +1,136 @@
+"""GLU and block parity on the GPU against the oracle.
+
+Stage-wise protocol: the first BitLinear of each group (i|f|g from x, gate|up from y1)
+must give bit-exact int8 codes and int32 accumulators against the oracle run on the same
+inputs; the downstream stages (o_proj, down) are rechecked bit-exactly from their captured
+fp32 inputs; end-to-end outputs and states meet the fp tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from ternary_weight_matmul_bitlinear_amd import api, synth
+from tests.gpu_helpers import (TOL, cat_weights, dev, host, make_block, note, rel_check,
+                               small_latents, stage_recheck)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _restore_regime():
+    prev = api.set_regime(0)
+    yield
+    api.set_regime(prev)
+
+
+@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("M,D,F,dt,resid", [(5, 256, 704, torch.float32, False),
+                                            (64, 256, 704, torch.bfloat16, True),
+                                            (300, 1024, 2816, torch.bfloat16, True)])
+def test_glu_parity(orc, regime, M, D, F, dt, resid):
+    note(f"glu regime={regime} M={M} D={D} F={F}")
+    lat = small_latents(M + D, D, F)
+    bf = dt == torch.bfloat16
+    x = synth.gaussian(M, (M, D))
+    if bf:
+        x = synth.round_to_bf16(x)
+    q = {k: orc.ternarize(lat[k]) for k in ("gate", "up", "down")}
+    g, u, d = (api.TernaryLinear.from_latent(lat[k]) for k in ("gate", "up", "down"))
+    api.set_regime(regime)
+    cap = api.BlockCapture.alloc(0, M, D, F)
+    y = api.glu_forward(g, u, d, dev(x, dt), residual=dev(x, dt) if resid else None, capture=cap)
+    torch.cuda.synchronize()
+    y_o, m_o = orc.glu(x, q["gate"], q["up"], q["down"], act_bf16=bf)
+    if resid:
+        y_o = y_o + x
+    W = {"gateup": np.concatenate([q["gate"][0], q["up"][0]]), "down": q["down"][0]}
+    gu = cap.gateup.host()
+    qx, _, _ = orc.act_quant(x)
+    assert np.array_equal(gu["q"], qx)
+    assert np.array_equal(gu["acc"], orc.accumulate(qx, W["gateup"]))
+    stage_recheck(orc, cap.down.host(), W["down"], what="down")
+    flips = np.mean(cap.down.host()["q"] != orc.act_quant(m_o)[0])
+    assert flips < 5e-3, flips
+    rel_check(host(y), y_o, TOL[dt], "y")
+
+
+def _block_case(orc, D, F, B, T, dt, seed, gate_mode=0, f_bias=None, use_gains=False):
+    lat = small_latents(seed, D, F)
+    gw = fb = None
+    if use_gains:
+        gw = (1 + 0.2 * synth.gaussian(seed + 5, (D,))).astype(np.float32)
+    if f_bias is not None:
+        fb = np.full(D, f_bias, np.float32)
+    blk, W = make_block(orc, lat, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode)
+    x = synth.gaussian(seed + 9, (B, T, D))
+    if dt == torch.bfloat16:
+        x = synth.round_to_bf16(x)
+    return blk, W, x, fb, gw
+
+
+@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("gate_mode", [0, 1])
+def test_block_tiny_parity(orc, regime, dt, gate_mode):
+    """The tiny workload (64 tokens, d = 256) end to end with every stage captured."""
+    D, F, B, T = 256, 704, 1, 64
+    note(f"block tiny regime={regime} dt={dt} gate={gate_mode}")
+    blk, W, x, fb, gw = _block_case(orc, D, F, B, T, dt, 21, gate_mode, f_bias=0.3, use_gains=True)
+    h = torch.zeros((B, D), device="cuda")
+    api.set_regime(regime)
+    cap = api.BlockCapture.alloc(0, B * T, D, F)
+    y = api.block_forward(blk, dev(x, dt), h_state=h, capture=cap)
+    torch.cuda.synchronize()
+    bf = dt == torch.bfloat16
+    r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf, record=True)
+    cw = cat_weights(W)
+    ifg = cap.ifg.host()
+    assert np.array_equal(ifg["q"], r["stages"]["ifg"]["q"])
+    assert np.array_equal(ifg["acc"], r["stages"]["ifg"]["acc"])
+    for name in ("o", "gateup", "down"):
+        stage_recheck(orc, getattr(cap, name).host(), cw[name], what=name)
+    for name in ("o", "down"):
+        flips = np.mean(getattr(cap, name).host()["q"] != r["stages"][name]["q"])
+        assert flips < 5e-3, (name, flips)
+    rel_check(host(y), r["y"], TOL[dt], "y")
+    rel_check(host(h), r["h_last"], 1e-3, "h_T")
+
+
+def test_block_decode_steps_match_prefill(orc):
+    """T one-token decode steps carrying h reproduce the prefill block on the same tokens."""
+    D, F, B, T = 256, 704, 3, 20
+    note("block decode steps vs prefill")
+    blk, W, x, fb, gw = _block_case(orc, D, F, B, T, torch.bfloat16, 31)
+    xd = dev(x, torch.bfloat16)
+    api.set_regime(2)
+    h_pf = torch.zeros((B, D), device="cuda")
+    y_pf = api.block_forward(blk, xd, h_state=h_pf)
+    api.set_regime(0)
+    h = torch.zeros((B, D), device="cuda")
+    ys = [api.block_forward(blk, xd[:, t:t + 1].contiguous(), h_state=h) for t in range(T)]
+    torch.cuda.synchronize()
+    y_dec = torch.cat(ys, dim=1)
+    rel_check(host(y_dec), host(y_pf), TOL[torch.bfloat16], "decode vs prefill")
+    rel_check(host(h), host(h_pf), 1e-3, "h")
+    r = orc.block(x, W, resid_bf16=True)
+    rel_check(host(y_dec), r["y"], TOL[torch.bfloat16], "decode vs oracle")
+
+
+def test_block_ragged_chunks_and_inplace(orc):
+    """T not a multiple of the scan chunk, several sequences, y written over x."""
+    D, F, B, T = 512, 1408, 3, 77
+    note("block ragged chunks in-place")
+    blk, W, x, fb, gw = _block_case(orc, D, F, B, T, torch.bfloat16, 41, f_bias=float(np.log(9)))
+    xd = dev(x, torch.bfloat16)
+    h = torch.zeros((B, D), device="cuda")
+    api.block_forward(blk, xd, h_state=h, y=xd)
+    torch.cuda.synchronize()
+    r = orc.block(x, W, f_bias=fb, resid_bf16=True)
+    rel_check(host(xd), r["y"], TOL[torch.bfloat16], "y")
+    rel_check(host(h), r["h_last"], 1e-3, "h_T")
+
+
+def test_block_zero_tokens_is_noop():
+    blk = api.Block.from_latents(small_latents(1, 256, 704))
+    x = torch.zeros((2, 0, 256), device="cuda")
+    y = api.block_forward(blk, x)
+    assert y.shape == (2, 0, 256)

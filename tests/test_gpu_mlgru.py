@@ -1,0 +1,94 @@
+"""MLGRU scan parity on the GPU against the oracle: gated outputs and final state within
+tolerance at chunk seams, ragged chunk tails and long T; the closed-form limits of the
+gates hold exactly."""
+import numpy as np
+import pytest
+import torch
+
+from ternary_weight_matmul_bitlinear_amd import api, synth
+from tests.gpu_helpers import TOL, dev, host, note, rel_check
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(1, 1, 64), (2, 31, 128), (2, 32, 256), (2, 33, 256), (3, 100, 1024), (1, 2048, 512),
+         (2, 70, 2560), (1, 5, 4096)]
+
+
+def _inputs(seed, B, T, D, dt):
+    ifg = synth.gaussian(seed, (B, T, 3 * D), 1.5)
+    if dt == torch.bfloat16:
+        ifg = synth.round_to_bf16(ifg)
+    fb = synth.gaussian(seed + 1, (D,), 0.5)
+    h0 = synth.gaussian(seed + 2, (B, D))
+    gw = (1.0 + 0.2 * synth.gaussian(seed + 3, (D,))).astype(np.float32)
+    return ifg, fb, h0, gw
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1], ids=["swish_rmsnorm", "sigmoid"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", CASES, ids=[f"B{b}T{t}D{d}" for b, t, d in CASES])
+def test_mlgru_parity(orc, B, T, D, dt, gate_mode):
+    note(f"mlgru B={B} T={T} D={D} dt={dt} gate={gate_mode}")
+    ifg, fb, h0, gw = _inputs(B * 1000 + T * 10 + D, B, T, D, dt)
+    out, hT = api.mlgru_scan(dev(ifg, dt), f_bias=dev(fb), h0=dev(h0), gnorm_w=dev(gw),
+                             gate_mode=gate_mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_o, hT_o = orc.mlgru(ifg.astype(np.float64), f_bias=fb, h0=h0, gnorm_w=gw,
+                            gate_mode=gate_mode)
+    rel_check(host(out), out_o, 1e-3, "out")
+    rel_check(host(hT), hT_o, 1e-3, "h_T")
+
+
+def test_mlgru_bf16_output_no_state_inputs(orc):
+    B, T, D = 2, 65, 256
+    note("mlgru bf16 out, no h0/bias/gain")
+    ifg = synth.gaussian(77, (B, T, 3 * D), 1.0)
+    out, hT = api.mlgru_scan(dev(ifg), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out_o, hT_o = orc.mlgru(ifg.astype(np.float64))
+    rel_check(host(out), out_o, TOL[torch.bfloat16], "out")
+    rel_check(host(hT), hT_o, 1e-3, "h_T")
+
+
+def test_mlgru_gate_limits_exact():
+    """f_pre = +40: sigmoid is 1 in fp32, the state never changes (h_T == h0 bit-exactly).
+    f_pre = -200: sigmoid underflows to 0, the state is the candidate after every step."""
+    B, T, D = 2, 77, 128
+    note("mlgru gate limits")
+    h0 = synth.gaussian(3, (B, D))
+    ifg = np.zeros((B, T, 3 * D), np.float32)
+    ifg[..., :D] = synth.gaussian(4, (B, T, D))
+    ifg[..., D:2 * D] = 40.0
+    _, hT = api.mlgru_scan(dev(ifg), h0=dev(h0), gate_mode=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(hT.cpu().numpy(), h0)
+    ifg[..., D:2 * D] = -200.0
+    _, hT = api.mlgru_scan(dev(ifg), h0=dev(h0), gate_mode=1)
+    torch.cuda.synchronize()
+    i_last = ifg[:, -1, :D].astype(np.float64)
+    np.testing.assert_allclose(hT.cpu().numpy(), i_last / (1 + np.exp(-i_last)), rtol=1e-6,
+                               atol=1e-7)
+
+
+def test_mlgru_state_carry_and_inplace(orc):
+    """scan(T1 + T2) == scan(T2 | h0 = scan(T1).h_T); h_out may alias h0."""
+    B, T1, T2, D = 2, 45, 70, 256
+    note("mlgru state carry")
+    ifg = synth.gaussian(11, (B, T1 + T2, 3 * D), 1.2)
+    full, hT = api.mlgru_scan(dev(ifg))
+    h = torch.zeros((B, D), device="cuda")
+    a, _ = api.mlgru_scan(dev(ifg[:, :T1]), h0=h, h_out=h)
+    b, _ = api.mlgru_scan(dev(ifg[:, T1:]), h0=h, h_out=h)
+    torch.cuda.synchronize()
+    got = np.concatenate([host(a), host(b)], axis=1)
+    rel_check(got, host(full), 1e-4, "carry out")
+    rel_check(host(h), host(hT), 1e-4, "carry h")
+
+
+def test_mlgru_empty_sequence_copies_state():
+    B, D = 3, 128
+    h0 = synth.gaussian(12, (B, D))
+    out, hT = api.mlgru_scan(torch.zeros((B, 0, 3 * D), device="cuda"), h0=dev(h0))
+    torch.cuda.synchronize()
+    assert out.shape == (B, 0, D)
+    assert np.array_equal(hT.cpu().numpy(), h0)

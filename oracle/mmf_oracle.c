@@ -35,10 +35,11 @@
  *   R6  output gate: o = RMSNorm_D(h)*gamma_g * g*sigmoid(g) (default) or sigmoid(g)*h.
  *   R7  block: pre-norm residuals y1 = x + o_proj(...), y2 = y1 + GLU(y1); one RMSNorm per
  *       BitLinear input; y1 and y2 rounded once to the residual dtype.
- *   R8  activations that leave a stage are stored in the activation dtype: with bf16
- *       activations the i/f/g pre-activations, the gated MLGRU output and the GLU hidden
- *       are rounded to bf16 (fp32 otherwise) before the next stage reads them; the
- *       recurrent state is not rounded.
+ *   R8  activations handed from one kernel to the next are stored in the activation
+ *       dtype: with bf16 activations the i/f/g pre-activations and the GLU hidden are
+ *       rounded to bf16 (fp32 otherwise); the gated MLGRU output is quantized for o_proj
+ *       inside the kernel that computes it, so it is rounded to fp32 only; the recurrent
+ *       state is not rounded.
  *
  * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
  * activation quant) are defined in fp32 so that both sides take each integer decision in
@@ -337,7 +338,7 @@ static int group_bitlinear(const float *x, int64_t M, int np, const orc_linear *
 /* ------------------------------------------------------------------ O8 GLU
  * [DC-core]: two BitLinears on the input, SiLU on one branch, element-wise product, a
  * third BitLinear.  x [M, D] -> y [M, D] (fp64, no residual).  m_out [M, F] receives the
- * fp32 stage input of the down projection (optional).
+ * stage input of the down projection, rounded to the activation dtype (optional; R8).
  */
 static int glu_impl(const float *x, int64_t M, const orc_linear *gate, const orc_linear *up,
                     const orc_linear *down, double eps, int act_bf16, double *y, float *m_out,
@@ -423,7 +424,7 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
     /* MLGRU + output gate, then o_proj with the residual. */
     rc = orc_mlgru(ifg, B, T, D, f_bias, h0, gnorm_w, eps, gate_mode, o, h_last);
     if (rc) return rc;
-    to_act(o, o32, M * D, resid_bf16);
+    to_act(o, o32, M * D, 0);
     if (st_o && st_o->x_in) memcpy(st_o->x_in, o32, sizeof(float) * (size_t)(M * D));
     rc = orc_bitlinear(o32, M, wo, eps, yo, st_o ? st_o->q : NULL, st_o ? st_o->a : NULL,
                        st_o ? st_o->acc : NULL);

@@ -177,8 +177,8 @@ class Oracle:
 
     # -------------------------------------------------------------------- GLU
     def glu(self, x, gate, up, down, eps: float = 1e-6, act_bf16: bool = False):
-        """gate/up/down: (q, scale[, gamma]) tuples.  Returns (y fp64 [M, D], m [M, F]) with
-        m rounded to the activation dtype (bf16 when act_bf16)."""
+        """gate/up/down: (q, scale[, gamma]) tuples.  Returns (y fp64 [M, D], m [M, F]), m
+        rounded to the activation dtype (bf16 when act_bf16)."""
         x = np.ascontiguousarray(x, dtype=np.float32)
         D = x.shape[-1]
         M = x.size // D

@@ -51,6 +51,7 @@ MUTANTS = [
      "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = orc_round_bf16(ifg[i]);",
      "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = ifg[i];"),
     ("glu_hidden_not_rounded", "to_act(yg, mm, M * F, act_bf16);", "to_act(yg, mm, M * F, 0);"),
+    ("gated_output_rounded_to_bf16", "to_act(o, o32, M * D, 0);", "to_act(o, o32, M * D, resid_bf16);"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

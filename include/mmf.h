@@ -100,15 +100,19 @@ typedef struct mmf_block {
 } mmf_block;
 
 /* Optional record of one BitLinear stage for token rows [row0, row1) (device buffers,
- * any may be NULL): the fp32 input exactly as quantized, its int8 codes, its scale a, and
- * the int32 accumulators acc = sum_k q_x * q_w.  For a group of projections sharing an
- * input (i|f|g, gate|up) acc has the group's concatenated width (3D or 2F) in that order. */
+ * any may be NULL): the fp32 input exactly as quantized, its int8 codes, its scale a, the
+ * int32 accumulators acc = sum_k q_x * q_w, and the stage output exactly as stored for
+ * the next kernel, widened to fp32 (i|f|g: the pre-activations; o: y1 = x + o_proj;
+ * gate|up: the GLU hidden SiLU(gate)*up; down: the block output).  For a group of
+ * projections sharing an input (i|f|g, gate|up) acc has the group's concatenated width
+ * (3D or 2F) in that order; y_out has the width of the stored output (3D, D, F, D). */
 typedef struct mmf_stage_capture {
     int64_t row0, row1;
     float *x_in;   /* [rows][K] */
     int8_t *q;     /* [rows][K] */
     float *a;      /* [rows] */
     int32_t *acc;  /* [rows][N] */
+    float *y_out;  /* [rows][N_out] */
 } mmf_stage_capture;
 
 typedef struct mmf_capture {

@@ -29,7 +29,8 @@ class mmf_block(C.Structure):
 
 
 class mmf_stage_capture(C.Structure):
-    _fields_ = [("row0", i64), ("row1", i64), ("x_in", vp), ("q", vp), ("a", vp), ("acc", vp)]
+    _fields_ = [("row0", i64), ("row1", i64), ("x_in", vp), ("q", vp), ("a", vp), ("acc", vp),
+                ("y_out", vp)]
 
 
 class mmf_capture(C.Structure):

@@ -107,21 +107,25 @@ class StageCapture:
     q: torch.Tensor
     a: torch.Tensor
     acc: torch.Tensor
+    y_out: torch.Tensor
 
     @classmethod
-    def alloc(cls, row0, row1, K, N, device="cuda"):
+    def alloc(cls, row0, row1, K, N, N_out=None, device="cuda"):
+        """Canary-filled buffers (NaN / -128 / INT_MIN) so unwritten entries show."""
         r = row1 - row0
+        N_out = N if N_out is None else N_out
         return cls(row0, row1, torch.full((r, K), float("nan"), device=device),
                    torch.full((r, K), -128, dtype=torch.int8, device=device),
                    torch.full((r,), float("nan"), device=device),
-                   torch.full((r, N), -2**31, dtype=torch.int32, device=device))
+                   torch.full((r, N), -2**31, dtype=torch.int32, device=device),
+                   torch.full((r, N_out), float("nan"), device=device))
 
     def desc(self) -> L.mmf_stage_capture:
         return L.mmf_stage_capture(self.row0, self.row1, _ptr(self.x_in), _ptr(self.q),
-                                   _ptr(self.a), _ptr(self.acc))
+                                   _ptr(self.a), _ptr(self.acc), _ptr(self.y_out))
 
     def host(self) -> dict:
-        return {k: getattr(self, k).cpu().numpy() for k in ("x_in", "q", "a", "acc")}
+        return {k: getattr(self, k).cpu().numpy() for k in ("x_in", "q", "a", "acc", "y_out")}
 
 
 @dataclass
@@ -133,17 +137,17 @@ class BlockCapture:
 
     @classmethod
     def alloc(cls, row0, row1, D, F, device="cuda"):
-        return cls(StageCapture.alloc(row0, row1, D, 3 * D, device),
-                   StageCapture.alloc(row0, row1, D, D, device),
-                   StageCapture.alloc(row0, row1, D, 2 * F, device),
-                   StageCapture.alloc(row0, row1, F, D, device))
+        return cls(StageCapture.alloc(row0, row1, D, 3 * D, 3 * D, device),
+                   StageCapture.alloc(row0, row1, D, D, D, device),
+                   StageCapture.alloc(row0, row1, D, 2 * F, F, device),
+                   StageCapture.alloc(row0, row1, F, D, D, device))
 
     def desc(self) -> L.mmf_capture:
         return L.mmf_capture(self.ifg.desc(), self.o.desc(), self.gateup.desc(), self.down.desc())
 
 
 def _empty_stage():
-    return L.mmf_stage_capture(0, 0, None, None, None, None)
+    return L.mmf_stage_capture(0, 0, None, None, None, None, None)
 
 
 # ------------------------------------------------------------------ forward calls

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(256) void gemm_ternary_kernel(GemmArgs p) {
             if (row >= p.M) continue;
             const int32_t rs = p.rowsum[row];
             const float arow_s = p.a[row];
-            const bool capr = p.cap.acc && p.cap.row0 <= row && row < p.cap.row1;
+            const bool capr = p.cap.row0 <= row && row < p.cap.row1;
+            const int64_t crow = row - p.cap.row0;
             if constexpr (EPI == EPI_GLU) {
                 const int f = nt * 64 + 32 * wn + r32;
                 if (f >= p.seg[0].n) continue;
@@ -142,11 +143,15 @@ __global__ __launch_bounds__(256) void gemm_ternary_kernel(GemmArgs p) {
                 float yu = static_cast<float>(au) * (p.seg[1].scale * arow_s);
                 if (p.seg[0].bias) yg += p.seg[0].bias[f];
                 if (p.seg[1].bias) yu += p.seg[1].bias[f];
-                store_act<OUT_BF16>(p.out, row * p.ldo + f, siluf_(yg) * yu);
+                const float mv = siluf_(yg) * yu;
+                store_act<OUT_BF16>(p.out, row * p.ldo + f, mv);
                 if (capr) {
-                    int32_t *c = p.cap.acc + (row - p.cap.row0) * p.cap.acc_ld;
-                    c[p.seg[0].cap_col0 + f] = ag_;
-                    c[p.seg[1].cap_col0 + f] = au;
+                    if (p.cap.acc) {
+                        int32_t *c = p.cap.acc + crow * p.cap.acc_ld;
+                        c[p.seg[0].cap_col0 + f] = ag_;
+                        c[p.seg[1].cap_col0 + f] = au;
+                    }
+                    if (p.cap.y_out) p.cap.y_out[crow * p.ldo + f] = OUT_BF16 ? round_to_bf16(mv) : mv;
                 }
             } else {
                 const Seg &S = p.seg[sg];
@@ -161,7 +166,10 @@ __global__ __launch_bounds__(256) void gemm_ternary_kernel(GemmArgs p) {
                     if constexpr (EPI == EPI_RESID)
                         y = load_act<OUT_BF16>(p.resid, row * p.ldr + S.out_col0 + n) + y;
                     store_act<OUT_BF16>(p.out, oi, y);
-                    if (capr) p.cap.acc[(row - p.cap.row0) * p.cap.acc_ld + S.cap_col0 + n] = av_;
+                    if (capr) {
+                        if (p.cap.acc) p.cap.acc[crow * p.cap.acc_ld + S.cap_col0 + n] = av_;
+                        if (p.cap.y_out) p.cap.y_out[crow * p.ldo + S.out_col0 + n] = OUT_BF16 ? round_to_bf16(y) : y;
+                    }
                 }
             }
         }

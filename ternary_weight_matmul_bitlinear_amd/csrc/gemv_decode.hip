@@ -219,18 +219,23 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
     const int64_t tok = t0 + j;
     const int32_t rs = s_rs[j];
     const float at = s_a[j];
-    const bool capr = p.cap.acc && p.cap.row0 <= tok && tok < p.cap.row1;
+    const bool capr = p.cap.row0 <= tok && tok < p.cap.row1;
+    const int64_t crow = tok - p.cap.row0;
     if constexpr (EPI == EPI_GLU) {
         const int32_t ag = my0 - rs, au = my1 - rs;
         float yg = static_cast<float>(ag) * (p.seg[0].scale * at);
         float yu = static_cast<float>(au) * (p.seg[1].scale * at);
         if (p.seg[0].bias) yg += p.seg[0].bias[n];
         if (p.seg[1].bias) yu += p.seg[1].bias[n];
-        store_act<OUT_BF16>(p.out, tok * p.ldo + n, siluf_(yg) * yu);
+        const float mv = siluf_(yg) * yu;
+        store_act<OUT_BF16>(p.out, tok * p.ldo + n, mv);
         if (capr) {
-            int32_t *cp = p.cap.acc + (tok - p.cap.row0) * p.cap.acc_ld;
-            cp[p.seg[0].cap_col0 + n] = ag;
-            cp[p.seg[1].cap_col0 + n] = au;
+            if (p.cap.acc) {
+                int32_t *cp = p.cap.acc + crow * p.cap.acc_ld;
+                cp[p.seg[0].cap_col0 + n] = ag;
+                cp[p.seg[1].cap_col0 + n] = au;
+            }
+            if (p.cap.y_out) p.cap.y_out[crow * p.ldo + n] = OUT_BF16 ? round_to_bf16(mv) : mv;
         }
     } else {
         const Seg &S = p.seg[sg];
@@ -239,7 +244,10 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
         if (S.bias) y += S.bias[n];
         if constexpr (EPI == EPI_RESID) y = load_act<OUT_BF16>(p.resid, tok * p.ldr + S.out_col0 + n) + y;
         store_act<OUT_BF16>(p.out, tok * p.ldo + S.out_col0 + n, y);
-        if (capr) p.cap.acc[(tok - p.cap.row0) * p.cap.acc_ld + S.cap_col0 + n] = av;
+        if (capr) {
+            if (p.cap.acc) p.cap.acc[crow * p.cap.acc_ld + S.cap_col0 + n] = av;
+            if (p.cap.y_out) p.cap.y_out[crow * p.ldo + S.out_col0 + n] = OUT_BF16 ? round_to_bf16(y) : y;
+        }
     }
 }
 

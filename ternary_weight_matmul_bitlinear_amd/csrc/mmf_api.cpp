@@ -151,6 +151,7 @@ static CapDev cap_of(const mmf_stage_capture *c, int32_t acc_ld) {
     d.q = c->q;
     d.a = c->a;
     d.acc = c->acc;
+    d.y_out = c->y_out;
     d.acc_ld = acc_ld;
     return d;
 }
@@ -194,6 +195,7 @@ static hipError_t quantize(const void *x, bool bf16, const float *gamma, float e
     qa.rowsum = qb.rs;
     qa.cap = cap_of(cap, 0);
     qa.cap.acc = nullptr;
+    qa.cap.y_out = nullptr;
     return launch_quant(qa, s);
 }
 
@@ -432,7 +434,6 @@ int mlgru_scan(const mmf_mlgru_args *a, void *ws, size_t ws_bytes, hipStream_t s
     }
     s.out = a->out;
     s.out_bf16 = a->out_dt == MMF_BF16;
-    s.round_bf16 = 0;
     e = launch_scan(s, stream);
     if (e != hipSuccess) return hip_error(e, "mlgru_scan launch");
     return MMF_OK;
@@ -481,6 +482,7 @@ int glu_forward(const mmf_bitlinear *gate, const mmf_bitlinear *up, const mmf_bi
     const int epi_dn = residual ? EPI_RESID : EPI_STORE;
     const mmf_stage_capture *cg = cap ? &cap->gateup : nullptr, *cd = cap ? &cap->down : nullptr;
     hipError_t e;
+    // the GLU hidden m is stored in the activation dtype between the two kernels
     if (use_decode(m)) {
         e = gemv(x, bf, gate->norm_w, gate->eps, nullptr, m, D, gu, 2, EPI_GLU, mact, F, bf, nullptr, 0, cg, 2 * F, stream);
         if (e == hipSuccess)
@@ -568,7 +570,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     }
     if (e != hipSuccess) return hip_error(e, "block_forward ifg launch");
 
-    // 3: MLGRU + g_norm, quantized for o_proj
+    // 3: MLGRU + g_norm, quantized from fp32 for o_proj
     ScanArgs s{};
     s.ifg = act;
     s.ifg_bf16 = bf;
@@ -589,7 +591,6 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
         s.pf = c.take<float>(n);
         s.hin = c.take<float>(n);
     }
-    s.round_bf16 = bf;
     s.q = qb.q;
     s.a = qb.a;
     s.rowsum = qb.rs;
@@ -597,6 +598,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     s.q_eps = w->o.eps;
     s.cap = cap_of(c_o, 0);
     s.cap.acc = nullptr;
+    s.cap.y_out = nullptr;
     e = launch_scan(s, stream);
     if (e != hipSuccess) return hip_error(e, "block_forward scan launch");
 
@@ -606,6 +608,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     if (e != hipSuccess) return hip_error(e, "block_forward o_proj launch");
 
     // 5-8: GLU with residual y1 -> y
+    // the GLU hidden m is stored in the activation dtype between the two kernels
     if (decode) {
         e = gemv(y1, bf, w->gate.norm_w, w->gate.eps, nullptr, M, D, gu, 2, EPI_GLU, act, F, bf, nullptr, 0, c_gu, 2 * F, stream);
         if (e == hipSuccess)

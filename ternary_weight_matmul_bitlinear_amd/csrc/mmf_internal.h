@@ -100,6 +100,7 @@ struct CapDev {
     int8_t *q = nullptr;
     float *a = nullptr;
     int32_t *acc = nullptr;
+    float *y_out = nullptr;  // stored output of the stage, widened to fp32 (row stride ldo)
     int32_t acc_ld = 0;   // row stride of acc (group width)
     int32_t acc_col0 = 0; // column offset of this launch inside the group
 };
@@ -200,7 +201,6 @@ struct ScanArgs {
     // output: either the gated activation or its int8 quantization for o_proj
     void *out;             // [B*T][D] (out_bf16) when q == NULL
     int32_t out_bf16;
-    int32_t round_bf16;    // round the gated output to bf16 before quantizing
     int8_t *q;             // [B*T][D]
     float *a;
     int32_t *rowsum;

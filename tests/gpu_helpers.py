@@ -71,3 +71,89 @@ def cat_weights(W: dict) -> dict:
 def small_latents(seed: int, D: int, F: int) -> dict:
     w = synth.Workload("t", D=D, F=F, B=1, T=1, seed=seed)
     return synth.layer_latents(w, 0)
+
+
+def round_act(orc, v, bf16: bool) -> np.ndarray:
+    """Round fp64 values to the activation dtype (the oracle's single rounding)."""
+    v = np.asarray(v, np.float64)
+    return orc.round_bf16(v) if bf16 else v.astype(np.float32).astype(np.float64)
+
+
+def block_stage_checks(orc, cap: dict, W: dict, x_rows: np.ndarray, bf16: bool, *,
+                       seq_rows: tuple | None = None, f_bias=None, gnorm_w=None,
+                       gate_mode: int = 0, h0=None, h_last=None, y_rows=None) -> dict:
+    """Stage-wise parity of one block run from its capture (host dicts per stage).
+
+    Integers: every stage's int8 codes and int32 accumulators must be bit-exact against the
+    oracle's quantizer and accumulator applied to the stage input the GPU captured.
+    Floating point: every stage's stored output must match the oracle applied to the GPU's
+    own stage inputs (tolerance of the stored dtype).  seq_rows = (B, T) when the capture
+    window holds whole sequences from t = 0, which enables the recurrence check."""
+    tol = 2e-2 if bf16 else 1e-3
+    stats = {}
+    cw = cat_weights(W)
+    D = x_rows.shape[-1]
+    F = W["gate"][0].shape[0]
+    x_rows = np.asarray(x_rows, np.float32).reshape(-1, D)
+    # i|f|g: input is x itself
+    st = cap["ifg"]
+    assert np.array_equal(st["x_in"], x_rows), "ifg x_in is not x"
+    stage_recheck(orc, st, cw["ifg"], what="ifg")
+    ifg_ref = np.concatenate([orc.bitlinear(x_rows, *W[k])[0] for k in ("i", "f", "g")], axis=1)
+    stats["ifg"] = rel_check(st["y_out"], round_act(orc, ifg_ref, bf16), tol, "ifg pre-activations")
+    # recurrence + g_norm from the GPU's stored pre-activations
+    o_in = cap["o"]["x_in"]
+    if seq_rows is not None:
+        B, T = seq_rows
+        o_ref, h_ref = orc.mlgru(st["y_out"].astype(np.float64).reshape(B, T, 3 * D),
+                                 f_bias=f_bias, h0=h0, gnorm_w=gnorm_w, gate_mode=gate_mode)
+        stats["mlgru"] = rel_check(o_in, o_ref.reshape(-1, D), 1e-3, "g_norm output")
+        if h_last is not None:
+            stats["h_T"] = rel_check(h_last, h_ref, 1e-3, "h_T")
+    # o_proj + residual
+    stage_recheck(orc, cap["o"], cw["o"], what="o")
+    y1_ref = round_act(orc, x_rows + orc.bitlinear(o_in, *W["o"])[0], bf16)
+    y1 = cap["o"]["y_out"]
+    stats["y1"] = rel_check(y1, y1_ref, tol, "y1")
+    # GLU
+    assert np.array_equal(cap["gateup"]["x_in"], y1), "GLU input is not the stored y1"
+    stage_recheck(orc, cap["gateup"], cw["gateup"], what="gateup")
+    _, m_ref = orc.glu(y1, W["gate"], W["up"], W["down"], act_bf16=bf16)
+    m = cap["gateup"]["y_out"]
+    stats["m"] = rel_check(m, m_ref, tol, "GLU hidden")
+    assert np.array_equal(cap["down"]["x_in"], m), "down input is not the stored GLU hidden"
+    stage_recheck(orc, cap["down"], cw["down"], what="down")
+    y_ref = round_act(orc, y1 + orc.bitlinear(m, *W["down"])[0], bf16)
+    stats["y"] = rel_check(cap["down"]["y_out"], y_ref, tol, "block output")
+    if y_rows is not None:
+        assert np.array_equal(np.asarray(y_rows, np.float32).reshape(-1, D),
+                              cap["down"]["y_out"]), "returned y differs from the captured output"
+    return stats
+
+
+def e2e_checks(got_y, ref_y, bf16: bool, cap: dict | None = None, rec: dict | None = None,
+               got_h=None, ref_h=None) -> dict:
+    """Independent end-to-end comparison (GPU vs oracle from the same x).  Downstream int8
+    codes may flip by one where fp32 and fp64 land on opposite sides of a rounding point,
+    and such a flip propagates; the bound is therefore statistical: p99.9 of the element
+    error and every row's norm-wise relative error within the tolerance, flips <= 1e-3."""
+    tol = 2e-2 if bf16 else 1e-3
+    g = np.asarray(got_y, np.float64).reshape(-1, got_y.shape[-1])
+    r = np.asarray(ref_y, np.float64).reshape(g.shape)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    el = np.abs(g - r) / (np.abs(r) + rms)
+    rowwise = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
+    out = {"max": float(el.max()), "p999": float(np.quantile(el, 0.999)),
+           "row_norm_max": float(rowwise.max())}
+    assert out["p999"] <= tol, out
+    assert out["row_norm_max"] <= tol, out
+    if cap is not None and rec is not None:
+        for name in ("o", "gateup", "down"):
+            f = float(np.mean(cap[name]["q"] != rec[name]["q"]))
+            d = np.abs(cap[name]["q"].astype(np.int32) - rec[name]["q"].astype(np.int32))
+            out[f"flips_{name}"] = f
+            assert f <= 1e-3, (name, f)
+            assert d.max() <= 1 or name != "o", (name, int(d.max()))
+    if got_h is not None:
+        out["h_T"] = rel_check(got_h, ref_h, tol, "h_T end to end")["max"]
+    return out

@@ -155,8 +155,8 @@ def test_block_validation_codes(lib):
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE, need - 1, None, None) == -5
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE + 8, need, None, None) == -3
     assert f(C.byref(_block()), None, 1, 0, 64, None, None, None, 0, None, None) == 0
-    cap = L.mmf_capture(L.mmf_stage_capture(5, 2, None, None, None, None),
-                        *[L.mmf_stage_capture(0, 0, None, None, None, None)] * 3)
+    cap = L.mmf_capture(L.mmf_stage_capture(5, 2, None, None, None, None, None),
+                        *[L.mmf_stage_capture(0, 0, None, None, None, None, None)] * 3)
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE, ws, C.byref(cap), None) == -1
 
 

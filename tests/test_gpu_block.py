@@ -9,8 +9,8 @@ import pytest
 import torch
 
 from ternary_weight_matmul_bitlinear_amd import api, synth
-from tests.gpu_helpers import (TOL, cat_weights, dev, host, make_block, note, rel_check,
-                               small_latents, stage_recheck)
+from tests.gpu_helpers import (TOL, block_stage_checks, dev, e2e_checks, host, make_block,
+                               note, rel_check, round_act, small_latents, stage_recheck)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,17 +40,22 @@ def test_glu_parity(orc, regime, M, D, F, dt, resid):
     y = api.glu_forward(g, u, d, dev(x, dt), residual=dev(x, dt) if resid else None, capture=cap)
     torch.cuda.synchronize()
     y_o, m_o = orc.glu(x, q["gate"], q["up"], q["down"], act_bf16=bf)
+    W = {"gateup": np.concatenate([q["gate"][0], q["up"][0]]), "down": q["down"][0]}
+    gu, dn = cap.gateup.host(), cap.down.host()
+    # gate|up from x: bit-exact codes and accumulators, hidden within tolerance
+    qx, _, _ = orc.act_quant(x)
+    assert np.array_equal(gu["x_in"], x) and np.array_equal(gu["q"], qx)
+    assert np.array_equal(gu["acc"], orc.accumulate(qx, W["gateup"]))
+    rel_check(gu["y_out"], m_o, TOL[dt], "GLU hidden")
+    # down from the GPU's own hidden: bit-exact, then the fp output
+    assert np.array_equal(dn["x_in"], gu["y_out"])
+    stage_recheck(orc, dn, W["down"], what="down")
+    y_ref = orc.bitlinear(dn["x_in"], *q["down"])[0] + (x if resid else 0.0)
+    rel_check(host(y), round_act(orc, y_ref, bf), TOL[dt], "y (stage)")
+    # independent end to end
     if resid:
         y_o = y_o + x
-    W = {"gateup": np.concatenate([q["gate"][0], q["up"][0]]), "down": q["down"][0]}
-    gu = cap.gateup.host()
-    qx, _, _ = orc.act_quant(x)
-    assert np.array_equal(gu["q"], qx)
-    assert np.array_equal(gu["acc"], orc.accumulate(qx, W["gateup"]))
-    stage_recheck(orc, cap.down.host(), W["down"], what="down")
-    flips = np.mean(cap.down.host()["q"] != orc.act_quant(m_o)[0])
-    assert flips < 5e-3, flips
-    rel_check(host(y), y_o, TOL[dt], "y")
+    e2e_checks(host(y), round_act(orc, y_o, bf), bf)
 
 
 def _block_case(orc, D, F, B, T, dt, seed, gate_mode=0, f_bias=None, use_gains=False):
@@ -81,18 +86,13 @@ def test_block_tiny_parity(orc, regime, dt, gate_mode):
     y = api.block_forward(blk, dev(x, dt), h_state=h, capture=cap)
     torch.cuda.synchronize()
     bf = dt == torch.bfloat16
+    ch = {k: getattr(cap, k).host() for k in ("ifg", "o", "gateup", "down")}
+    block_stage_checks(orc, ch, W, x, bf, seq_rows=(B, T), f_bias=fb, gnorm_w=gw,
+                       gate_mode=gate_mode, h_last=host(h), y_rows=host(y))
     r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf, record=True)
-    cw = cat_weights(W)
-    ifg = cap.ifg.host()
-    assert np.array_equal(ifg["q"], r["stages"]["ifg"]["q"])
-    assert np.array_equal(ifg["acc"], r["stages"]["ifg"]["acc"])
-    for name in ("o", "gateup", "down"):
-        stage_recheck(orc, getattr(cap, name).host(), cw[name], what=name)
-    for name in ("o", "down"):
-        flips = np.mean(getattr(cap, name).host()["q"] != r["stages"][name]["q"])
-        assert flips < 5e-3, (name, flips)
-    rel_check(host(y), r["y"], TOL[dt], "y")
-    rel_check(host(h), r["h_last"], 1e-3, "h_T")
+    assert np.array_equal(ch["ifg"]["q"], r["stages"]["ifg"]["q"])
+    assert np.array_equal(ch["ifg"]["acc"], r["stages"]["ifg"]["acc"])
+    e2e_checks(host(y), r["y"], bf, ch, r["stages"], host(h), r["h_last"])
 
 
 def test_block_decode_steps_match_prefill(orc):
@@ -109,10 +109,10 @@ def test_block_decode_steps_match_prefill(orc):
     ys = [api.block_forward(blk, xd[:, t:t + 1].contiguous(), h_state=h) for t in range(T)]
     torch.cuda.synchronize()
     y_dec = torch.cat(ys, dim=1)
-    rel_check(host(y_dec), host(y_pf), TOL[torch.bfloat16], "decode vs prefill")
+    e2e_checks(host(y_dec), host(y_pf), True)
     rel_check(host(h), host(h_pf), 1e-3, "h")
     r = orc.block(x, W, resid_bf16=True)
-    rel_check(host(y_dec), r["y"], TOL[torch.bfloat16], "decode vs oracle")
+    e2e_checks(host(y_dec), r["y"], True, got_h=host(h), ref_h=r["h_last"])
 
 
 def test_block_ragged_chunks_and_inplace(orc):
@@ -122,11 +122,14 @@ def test_block_ragged_chunks_and_inplace(orc):
     blk, W, x, fb, gw = _block_case(orc, D, F, B, T, torch.bfloat16, 41, f_bias=float(np.log(9)))
     xd = dev(x, torch.bfloat16)
     h = torch.zeros((B, D), device="cuda")
-    api.block_forward(blk, xd, h_state=h, y=xd)
+    cap = api.BlockCapture.alloc(0, B * T, D, F)
+    api.block_forward(blk, xd, h_state=h, y=xd, capture=cap)
     torch.cuda.synchronize()
+    ch = {k: getattr(cap, k).host() for k in ("ifg", "o", "gateup", "down")}
+    block_stage_checks(orc, ch, W, x, True, seq_rows=(B, T), f_bias=fb, h_last=host(h),
+                       y_rows=host(xd))
     r = orc.block(x, W, f_bias=fb, resid_bf16=True)
-    rel_check(host(xd), r["y"], TOL[torch.bfloat16], "y")
-    rel_check(host(h), r["h_last"], 1e-3, "h_T")
+    e2e_checks(host(xd), r["y"], True, got_h=host(h), ref_h=r["h_last"])
 
 
 def test_block_zero_tokens_is_noop():

@@ -41,8 +41,13 @@ __device__ __forceinline__ void store_act(void *p, int64_t i, float v) {
     else static_cast<float *>(p)[i] = v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
-__device__ __forceinline__ float siluf_(float z) { return z / (1.0f + expf(-z)); }
+// Logistic sigmoid and SiLU on the hardware transcendental units: 2^x (v_exp_f32) and
+// 1/x (v_rcp_f32), each accurate to about 1 ulp.  sigmoid(z) = 1 / (1 + 2^(-z*log2 e));
+// large positive z gives exactly 1, large negative z gives exactly 0.
+__device__ __forceinline__ float sigmoidf_(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+__device__ __forceinline__ float siluf_(float z) { return z * sigmoidf_(z); }
 
 // Wave-wide (64 lanes) reductions through cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -226,7 +226,7 @@ hipError_t launch_copy_state(const float *h0, float *h_out, int64_t n, hipStream
 
 // Tokens per decode-kernel token group (rows of q staged in LDS).
 constexpr int kGemvTokens = 8;
-// Chunk length of the prefill scan.
-constexpr int kScanChunk = 32;
+// Chunk length of the prefill scan (tokens per workgroup of the output pass).
+constexpr int kScanChunk = 16;
 
 }  // namespace mmf

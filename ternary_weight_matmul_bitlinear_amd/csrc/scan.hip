@@ -13,10 +13,10 @@
 // CUs at long T it is also chunked over time.  All phases are HBM-bound:
 //   phase 1 (per chunk, channel quad): local scan from 0 -> end state hloc and prod(f);
 //   phase 2 (per channel): carry across chunks, h_in[c+1] = prod_c*h_in[c] + hloc_c;
-//   phase 3 (workgroup per chunk): rerun the recurrence from h_in for a tile of tokens,
-//     parking h in LDS, then one wave per token does the RMSNorm over D, the gate and
-//     either a store of o or its int8 quantization for o_proj (q, a, row sum) with
-//     wave-only reductions: two barriers per token tile instead of two per token.
+//   phase 3 (workgroup per chunk, thread per channel quad): rerun the recurrence from h_in
+//     in registers for a tile of tokens, then the per-token RMSNorm over D, the gate and
+//     either a store of o or its int8 quantization for o_proj (q, a, row sum); the
+//     reductions over D of a whole tile share one LDS exchange each.
 // With one chunk (decode, short T) phases 1 and 2 are skipped.
 #include "mmf_internal.h"
 
@@ -37,6 +37,26 @@ __device__ __forceinline__ float4 load4(const void *p, int64_t i) {
 }
 
 __device__ __forceinline__ float4 ld4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// Raw (unconverted) quad of activations: 8 bytes of bf16 or 16 bytes of fp32.
+template <bool BF16> struct RawQuad;
+template <> struct RawQuad<true> { using T = uint2; };
+template <> struct RawQuad<false> { using T = float4; };
+
+template <bool BF16>
+__device__ __forceinline__ typename RawQuad<BF16>::T load_raw4(const void *p, int64_t i) {
+    if constexpr (BF16) return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+    else return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+}
+__device__ __forceinline__ void cvt4(uint2 u, float (&v)[4]) {
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void cvt4(float4 u, float (&v)[4]) {
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
 __device__ __forceinline__ void st4f(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
 __device__ __forceinline__ float gate_step(float h, float ip, float fp, float fb, float *f_out) {
@@ -105,171 +125,272 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs p) {
     }
 }
 
-// Phase 3: workgroup per (b, chunk), tokens in tiles of TS.  JQ = channel quads per
-// thread in the recurrence (D <= 1024*JQ); per token row a lane holds NV = 4*JQ float4.
-template <bool IN_BF16, int QUANT, bool OUT_BF16, int TS, int JQ>
+// Sum (or max) of N values per lane over the 64 lanes of a wave, N in {4, 8}: halving
+// exchanges (each lane keeps the half of the vector picked by its lane bit) followed by a
+// plain butterfly.  On return lane l holds the wave total of value index l >> (6 - log2 N).
+template <int N, bool MAX, typename T>
+__device__ __forceinline__ T wave_reduce_multi(T (&v)[N]) {
+    const int lane = threadIdx.x & 63;
+    T w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = v[i];
+    int n = N, bit = 32;
+#pragma unroll
+    for (int step = 0; step < 3; ++step) {
+        if (n > 1) {
+            const bool hi = lane & bit;
+            const int h = n / 2;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                if (i < h) {
+                    const T send = hi ? w[i] : w[i + h];
+                    const T keep = hi ? w[i + h] : w[i];
+                    const T recv = __shfl_xor(send, bit, 64);
+                    w[i] = MAX ? (keep > recv ? keep : recv) : keep + recv;
+                }
+            }
+            n = h;
+            bit >>= 1;
+        }
+    }
+    T r = w[0];
+    for (; bit > 0; bit >>= 1) {
+        const T o = __shfl_xor(r, bit, 64);
+        r = MAX ? (r > o ? r : o) : r + o;
+    }
+    return r;
+}
+
+// Workgroup-wide version: per-wave totals through LDS (red[4][N]); returns all N totals.
+template <int N, bool MAX, typename T>
+__device__ __forceinline__ void block_reduce_multi(T (&v)[N], T (*red)[N], T (&out)[N]) {
+    constexpr int SH = N == 8 ? 3 : 4;  // value index of lane l is l >> SH
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const T r = wave_reduce_multi<N, MAX>(v);
+    if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = r;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const T a = red[0][i], b = red[1][i], c = red[2][i], d = red[3][i];
+        out[i] = MAX ? ((a > b ? a : b) > (c > d ? c : d) ? (a > b ? a : b) : (c > d ? c : d))
+                     : (a + b) + (c + d);
+    }
+}
+
+// Phase 3: workgroup per (b, chunk); each thread owns JQ channel quads (D <= 1024*JQ) and
+// walks the chunk in tiles of TS tokens: the recurrence runs in registers, the per-token
+// reductions over D (sum h^2; max |p| and sum o^2; sum q) are multi-value wave butterflies
+// plus one LDS exchange each, and the next tile's pre-activations are loaded before the
+// current tile's reductions.
+template <bool IN_BF16, int QUANT, bool OUT_BF16, int JQ, int TS>
 __global__ __launch_bounds__(256) void scan_out_kernel(ScanArgs p) {
-    extern __shared__ __attribute__((aligned(16))) float hs[];  // [TS][D]
+    __shared__ float red_ss[4][TS], red_mx[4][TS], red_s2[4][TS];
+    __shared__ int red_q[4][TS];
     const int c = blockIdx.x;
     const int64_t b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int D = p.D;
     const int64_t t_beg = static_cast<int64_t>(c) * p.chunk;
     const int64_t t_end = t_beg + p.chunk < p.T ? t_beg + p.chunk : p.T;
     const float inv_d = 1.0f / static_cast<float>(D);
 
-    float h[JQ][4], fb[JQ][4];
+    float h[JQ][4], fb[JQ][4], gw[JQ][4], qg[JQ][4];
+    bool dv[JQ];
 #pragma unroll
     for (int j = 0; j < JQ; ++j) {
         const int d = 4 * (tid + 256 * j);
-        float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), fv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (d < D) {
+        dv[j] = d < D;
+        float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), fv = hv, g1 = make_float4(1.f, 1.f, 1.f, 1.f), q1 = g1;
+        if (dv[j]) {
             if (p.n_chunks > 1) hv = ld4f(p.hin + (b * p.n_chunks + c) * D + d);
             else if (p.h0) hv = ld4f(p.h0 + b * D + d);
             if (p.f_bias) fv = ld4f(p.f_bias + d);
+            if (p.gnorm_w) g1 = ld4f(p.gnorm_w + d);
+            if (QUANT && p.q_gamma) q1 = ld4f(p.q_gamma + d);
         }
         h[j][0] = hv.x; h[j][1] = hv.y; h[j][2] = hv.z; h[j][3] = hv.w;
         fb[j][0] = fv.x; fb[j][1] = fv.y; fb[j][2] = fv.z; fb[j][3] = fv.w;
+        gw[j][0] = g1.x; gw[j][1] = g1.y; gw[j][2] = g1.z; gw[j][3] = g1.w;
+        qg[j][0] = q1.x; qg[j][1] = q1.y; qg[j][2] = q1.z; qg[j][3] = q1.w;
     }
+
+    using Raw = typename RawQuad<IN_BF16>::T;
+    Raw ip[TS][JQ], fp[TS][JQ], gp[TS][JQ];
+    auto fetch = [&](int64_t tt) {
+        const int nt = static_cast<int>(t_end - tt < TS ? t_end - tt : TS);
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+            for (int j = 0; j < JQ; ++j) {
+                const int d = 4 * (tid + 256 * j);
+                if (t < nt && dv[j]) {
+                    const int64_t base = (b * p.T + tt + t) * 3 * D + d;
+                    ip[t][j] = load_raw4<IN_BF16>(p.ifg, base);
+                    fp[t][j] = load_raw4<IN_BF16>(p.ifg, base + D);
+                    gp[t][j] = load_raw4<IN_BF16>(p.ifg, base + 2 * D);
+                }
+            }
+    };
+    if (t_beg < t_end) fetch(t_beg);
 
     for (int64_t tt = t_beg; tt < t_end; tt += TS) {
         const int nt = static_cast<int>(t_end - tt < TS ? t_end - tt : TS);
-        // ---- recurrence for the tile (all loads of the tile issued before the chain)
-        float4 ip[TS][JQ], fp[TS][JQ];
+        // ---- recurrence (registers)
+        float o[TS][JQ][4], ss[TS];
+        Raw gs[TS][JQ];  // g of this tile, kept raw while the next tile is fetched
 #pragma unroll
-        for (int t = 0; t < TS; ++t)
-#pragma unroll
-            for (int j = 0; j < JQ; ++j) {
-                const int d = 4 * (tid + 256 * j);
-                if (t < nt && d < D) {
-                    const int64_t base = (b * p.T + tt + t) * 3 * D + d;
-                    ip[t][j] = load4<IN_BF16>(p.ifg, base);
-                    fp[t][j] = load4<IN_BF16>(p.ifg, base + D);
-                }
-            }
-#pragma unroll
-        for (int t = 0; t < TS; ++t)
+        for (int t = 0; t < TS; ++t) {
+            ss[t] = 0.f;
 #pragma unroll
             for (int j = 0; j < JQ; ++j) {
-                const int d = 4 * (tid + 256 * j);
-                if (t < nt && d < D) {
-                    const float iv[4] = {ip[t][j].x, ip[t][j].y, ip[t][j].z, ip[t][j].w};
-                    const float fv[4] = {fp[t][j].x, fp[t][j].y, fp[t][j].z, fp[t][j].w};
-                    float f;
+                float iv[4], fv[4];
+                cvt4(ip[t][j], iv);
+                cvt4(fp[t][j], fv);
+                gs[t][j] = gp[t][j];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[j][e] = gate_step(h[j][e], iv[e], fv[e], fb[j][e], &f);
-                    st4f(hs + t * D + d, make_float4(h[j][0], h[j][1], h[j][2], h[j][3]));
+                for (int e = 0; e < 4; ++e) {
+                    if (t < nt && dv[j]) {
+                        float f;
+                        h[j][e] = gate_step(h[j][e], iv[e], fv[e], fb[j][e], &f);
+                    }
+                    o[t][j][e] = h[j][e];
+                    ss[t] += (t < nt && dv[j]) ? h[j][e] * h[j][e] : 0.f;
                 }
             }
-        __syncthreads();
+        }
+        if (tt + TS < t_end) fetch(tt + TS);  // next tile in flight during the reductions
 
-        // ---- one wave per token: g_norm, gate, then store or quantize
-        constexpr int NV = JQ * 4;
-        for (int t = wave; t < nt; t += 4) {
-            const int64_t row = b * p.T + tt + t;
-            const float *hr = hs + t * D;
-            float4 hv[NV], gv[NV];
-            float ss = 0.f;
+        // ---- g_norm + gate
+        if (p.gate_mode == 0) {
+            float tot[TS];
+            block_reduce_multi<TS, false>(ss, red_ss, tot);
 #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int d = 4 * (lane + 64 * k);
-                if (d < D) {
-                    hv[k] = ld4f(hr + d);
-                    gv[k] = load4<IN_BF16>(p.ifg, row * 3 * D + 2 * D + d);
-                    ss += hv[k].x * hv[k].x + hv[k].y * hv[k].y + hv[k].z * hv[k].z + hv[k].w * hv[k].w;
+            for (int t = 0; t < TS; ++t) {
+                const float r = 1.0f / sqrtf(tot[t] * inv_d + p.eps);
+#pragma unroll
+                for (int j = 0; j < JQ; ++j) {
+                    float gv[4];
+                    cvt4(gs[t][j], gv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[t][j][e] = o[t][j][e] * r * gw[j][e] * siluf_(gv[e]);
                 }
             }
-            float r = 0.f;
-            if (p.gate_mode == 0) r = 1.0f / sqrtf(wave_sum(ss) * inv_d + p.eps);
-            float ov[NV][4];
+        } else {
 #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int d = 4 * (lane + 64 * k);
-                if (d < D) {
-                    const float hvv[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
-                    const float g[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w};
-                    const float4 gw = p.gnorm_w ? ld4f(p.gnorm_w + d) : make_float4(1.f, 1.f, 1.f, 1.f);
-                    const float gwa[4] = {gw.x, gw.y, gw.z, gw.w};
+            for (int t = 0; t < TS; ++t)
+#pragma unroll
+                for (int j = 0; j < JQ; ++j) {
+                    float gv[4];
+                    cvt4(gs[t][j], gv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[t][j][e] = sigmoidf_(gv[e]) * o[t][j][e];
+                }
+        }
+
+        if constexpr (QUANT == 0) {
+#pragma unroll
+            for (int t = 0; t < TS; ++t)
+#pragma unroll
+                for (int j = 0; j < JQ; ++j) {
+                    const int d = 4 * (tid + 256 * j);
+                    if (t < nt && dv[j]) {
+                        const int64_t oi = (b * p.T + tt + t) * D + d;
+                        if constexpr (OUT_BF16) {
+                            const uint32_t lo = f32_to_bf16_bits(o[t][j][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(o[t][j][1])) << 16);
+                            const uint32_t hi = f32_to_bf16_bits(o[t][j][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(o[t][j][3])) << 16);
+                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + oi) = make_uint2(lo, hi);
+                        } else {
+                            st4f(static_cast<float *>(p.out) + oi, make_float4(o[t][j][0], o[t][j][1], o[t][j][2], o[t][j][3]));
+                        }
+                    }
+                }
+        } else {
+            // ---- int8 quantization of o (with o_proj's gain) for o_proj
+            float mx[TS], s2[TS], mxt[TS], s2t[TS];
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                mx[t] = 0.f;
+                s2[t] = 0.f;
+#pragma unroll
+                for (int j = 0; j < JQ; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        ov[k][e] = p.gate_mode == 0 ? hvv[e] * r * gwa[e] * siluf_(g[e]) : sigmoidf_(g[e]) * hvv[e];
+                        if (t < nt && dv[j]) {
+                            const float pv = p.q_gamma ? o[t][j][e] * qg[j][e] : o[t][j][e];
+                            mx[t] = fmaxf(mx[t], fabsf(pv));
+                            s2[t] += o[t][j][e] * o[t][j][e];
+                        }
                     }
+            }
+            {
+                const float rm = wave_reduce_multi<TS, true>(mx);
+                const float rs = wave_reduce_multi<TS, false>(s2);
+                constexpr int SH = TS == 8 ? 3 : 4;
+                const int lane = tid & 63, wave = tid >> 6;
+                if ((lane & ((1 << SH) - 1)) == 0) {
+                    red_mx[wave][lane >> SH] = rm;
+                    red_s2[wave][lane >> SH] = rs;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int t = 0; t < TS; ++t) {
+                    mxt[t] = fmaxf(fmaxf(red_mx[0][t], red_mx[1][t]), fmaxf(red_mx[2][t], red_mx[3][t]));
+                    s2t[t] = (red_s2[0][t] + red_s2[1][t]) + (red_s2[2][t] + red_s2[3][t]);
                 }
             }
-            if constexpr (QUANT == 0) {
+            int qs[TS];
 #pragma unroll
-                for (int k = 0; k < NV; ++k) {
-                    const int d = 4 * (lane + 64 * k);
-                    if (d < D) {
-                        if constexpr (OUT_BF16) {
-                            const uint32_t lo = f32_to_bf16_bits(ov[k][0]) | (static_cast<uint32_t>(f32_to_bf16_bits(ov[k][1])) << 16);
-                            const uint32_t hi = f32_to_bf16_bits(ov[k][2]) | (static_cast<uint32_t>(f32_to_bf16_bits(ov[k][3])) << 16);
-                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + row * D + d) = make_uint2(lo, hi);
-                        } else {
-                            st4f(static_cast<float *>(p.out) + row * D + d, make_float4(ov[k][0], ov[k][1], ov[k][2], ov[k][3]));
-                        }
-                    }
-                }
-            } else {
-                float pv[NV][4];
-                float mx = 0.f, s2 = 0.f;
-#pragma unroll
-                for (int k = 0; k < NV; ++k) {
-                    const int d = 4 * (lane + 64 * k);
-                    if (d < D) {
-                        const float4 qg = p.q_gamma ? ld4f(p.q_gamma + d) : make_float4(1.f, 1.f, 1.f, 1.f);
-                        const float qga[4] = {qg.x, qg.y, qg.z, qg.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            pv[k][e] = p.q_gamma ? ov[k][e] * qga[e] : ov[k][e];
-                            mx = fmaxf(mx, fabsf(pv[k][e]));
-                            s2 += ov[k][e] * ov[k][e];
-                        }
-                    }
-                }
-                mx = wave_max(mx);
-                s2 = wave_sum(s2);
-                const float me = fmaxf(mx, 1e-5f);
+            for (int t = 0; t < TS; ++t) {
+                const float me = fmaxf(mxt[t], 1e-5f);
                 const float sc = 127.0f / me;
-                const bool capr = p.cap.row0 <= row && row < p.cap.row1;
+                const int64_t row = b * p.T + tt + t;
+                const bool capr = t < nt && p.cap.row0 <= row && row < p.cap.row1;
                 const int64_t cr = row - p.cap.row0;
-                int qsum = 0;
+                qs[t] = 0;
 #pragma unroll
-                for (int k = 0; k < NV; ++k) {
-                    const int d = 4 * (lane + 64 * k);
-                    if (d < D) {
+                for (int j = 0; j < JQ; ++j) {
+                    const int d = 4 * (tid + 256 * j);
+                    if (t < nt && dv[j]) {
                         uint32_t packed = 0;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            float rq = rintf(pv[k][e] * sc);
+                            const float pv = p.q_gamma ? o[t][j][e] * qg[j][e] : o[t][j][e];
+                            float rq = rintf(pv * sc);
                             rq = fminf(fmaxf(rq, -127.0f), 127.0f);
                             const int qi = static_cast<int>(rq);
-                            qsum += qi;
+                            qs[t] += qi;
                             packed |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * e);
                         }
                         *reinterpret_cast<uint32_t *>(p.q + row * D + d) = packed;
                         if (capr) {
-                            if (p.cap.x_in) st4f(p.cap.x_in + cr * D + d, make_float4(ov[k][0], ov[k][1], ov[k][2], ov[k][3]));
+                            if (p.cap.x_in) st4f(p.cap.x_in + cr * D + d, make_float4(o[t][j][0], o[t][j][1], o[t][j][2], o[t][j][3]));
                             if (p.cap.q) *reinterpret_cast<uint32_t *>(p.cap.q + cr * D + d) = packed;
                         }
                     }
                 }
-                qsum = wave_sum_i(qsum);
-                if (lane == 0) {
-                    const float a = me / 127.0f * (1.0f / sqrtf(s2 * inv_d + p.q_eps));
-                    p.a[row] = a;
-                    p.rowsum[row] = qsum;
-                    if (capr && p.cap.a) p.cap.a[cr] = a;
-                }
+            }
+            int qtot[TS];
+            block_reduce_multi<TS, false>(qs, red_q, qtot);
+            if (tid < nt) {
+                int qv = 0;
+                float me = 0.f, s2v = 0.f;
+#pragma unroll
+                for (int t = 0; t < TS; ++t)
+                    if (t == tid) { qv = qtot[t]; me = fmaxf(mxt[t], 1e-5f); s2v = s2t[t]; }
+                const int64_t row = b * p.T + tt + tid;
+                const float a = me / 127.0f * (1.0f / sqrtf(s2v * inv_d + p.q_eps));
+                p.a[row] = a;
+                p.rowsum[row] = qv;
+                if (p.cap.a && p.cap.row0 <= row && row < p.cap.row1) p.cap.a[row - p.cap.row0] = a;
             }
         }
-        __syncthreads();
+        __syncthreads();  // the reduction slots are reused by the next tile
     }
     if (c == p.n_chunks - 1 && p.h_out) {
 #pragma unroll
         for (int j = 0; j < JQ; ++j) {
             const int d = 4 * (tid + 256 * j);
-            if (d < D) st4f(p.h_out + b * D + d, make_float4(h[j][0], h[j][1], h[j][2], h[j][3]));
+            if (dv[j]) st4f(p.h_out + b * D + d, make_float4(h[j][0], h[j][1], h[j][2], h[j][3]));
         }
     }
 }
@@ -281,20 +402,18 @@ __global__ void copy_state_kernel(const float *h0, float *h_out, int64_t n) {
 
 template <bool IN_BF16, int QUANT, bool OUT_BF16, int TS>
 void launch_out_ts(const ScanArgs &a, dim3 grid, hipStream_t s) {
-    const size_t lds = static_cast<size_t>(TS) * a.D * 4;
     const int jq = (a.D + 1023) / 1024;
-    if (jq <= 1) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, TS, 1>), grid, dim3(256), lds, s, a);
-    else if (jq == 2) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, TS, 2>), grid, dim3(256), lds, s, a);
-    else if (jq == 3) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, TS, 3>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, TS, 4>), grid, dim3(256), lds, s, a);
+    if (jq <= 1) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, 1, TS>), grid, dim3(256), 0, s, a);
+    else if (jq == 2) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, 2, TS>), grid, dim3(256), 0, s, a);
+    else if (jq == 3) hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, 3, TS>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((scan_out_kernel<IN_BF16, QUANT, OUT_BF16, 4, TS>), grid, dim3(256), 0, s, a);
 }
 
-// Token tile: the LDS tile TS x D fp32 stays at or under 64 KB.
+// Token tile of 4: larger tiles amortize the reductions further but the replicated
+// per-token values push the kernel past 128 registers (measured slower at 8).
 template <bool IN_BF16, int QUANT, bool OUT_BF16>
 void launch_out_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
-    if (a.D <= 1024) launch_out_ts<IN_BF16, QUANT, OUT_BF16, 16>(a, grid, s);
-    else if (a.D <= 2048) launch_out_ts<IN_BF16, QUANT, OUT_BF16, 8>(a, grid, s);
-    else launch_out_ts<IN_BF16, QUANT, OUT_BF16, 4>(a, grid, s);
+    launch_out_ts<IN_BF16, QUANT, OUT_BF16, 4>(a, grid, s);
 }
 
 template <bool IN_BF16>

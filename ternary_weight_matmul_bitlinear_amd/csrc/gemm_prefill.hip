@@ -8,19 +8,24 @@
 // registers to int8 codes c = q + 1 in {0,1,2}, multiplied on the matrix cores, and the
 // offset is removed once per row: acc = sum_k q_x*c - sum_k q_x (exact in int32).
 //
-// Tiling (256 threads = 4 waves as 2 (M) x 2 (N); workgroup tile 128 x 256 x 64; two
-// workgroups per CU so one's epilogue overlaps the other's MFMA loop):
+// Tiling (256 threads = 4 waves as 2 (M) x 2 (N); workgroup tile 128 x 256, k-tiles of
+// 128; two workgroups per CU so one's epilogue overlaps the other's MFMA loop):
 //   - each wave owns 64 x 128 of the output = 2 x 4 MFMA blocks of 32 x 32 (128 int32
 //     accumulators per lane).  A (int8, 1 byte per k) costs 4x the LDS bytes of B (2 bits
-//     per k), so the wave tile is wide in N: 384 LDS bytes per 64K-op MFMA;
-//   - A tile 128 rows x 64 k in LDS with an 80-byte row pitch (16-byte reads of 8
-//     consecutive rows hit disjoint bank quads); B tile 256 rows x 4 packed words with a
-//     24-byte pitch (conflict-free 8-byte reads).  One packed word is exactly the 16-code
-//     B operand of a lane, so weights travel at 2 bits each all the way to the registers;
-//   - lane l (r = l % 32, g = l / 32) feeds, for MFMA half ks in {0,1}, activation bytes
-//     k = 32g + 16ks + [0,16) of row r and packed word 2g + ks of weight row r, so A and B
-//     agree on every (lane group, byte) -> k pairing;
-//   - double-buffered LDS, next k-tile prefetched into registers during the MFMAs;
+//     per k), so the wave tile is wide in N;
+//   - k-tiles stream from global memory straight into LDS (global_load_lds_dwordx4, no
+//     register staging) through a ring of 3 stages, so two tiles are in flight while the
+//     third is multiplied; one barrier per k-tile;
+//   - the direct loads write each wave's 1 KB in lane order, so bank spreading is done by
+//     choosing what each lane fetches: A row r keeps its eight 16-byte chunks in slots
+//     permuted by (r ^ r/8) & 7, B row r keeps its two 16-byte halves swapped when
+//     (r/4 ^ r/8) is odd; the 16-byte fragment reads of 8 (or 16) consecutive lanes then
+//     fall on distinct banks;
+//   - lane l (r = l % 32, g = l / 32) feeds MFMA step ks in {0..3} of a k-tile with
+//     packed word 4g + ks of weight row r (one word is exactly 16 codes, the B operand)
+//     and activation bytes k = 64g + 16ks + [0,16) of row r, so A and B agree on every
+//     (lane, byte) -> k pairing.  A ragged last k-tile (K % 128 == 64) zeroes the B
+//     operand of the upper lane half;
 //   - workgroups are dispatched round-robin over the 8 XCDs; tile ids are remapped so each
 //     XCD owns a contiguous run of tiles (N fastest), i.e. a few M-tiles of activations and
 //     all weight tiles, which stay in that XCD's L2.
@@ -28,25 +33,106 @@
 // a residual; or SiLU(gate)*up when the tile pairs 128 gate rows with the same 128 up rows.
 #include "mmf_internal.h"
 
+#include <type_traits>
+
+#ifndef MMF_UNPACK64
+#define MMF_UNPACK64 0
+#endif
+
 namespace mmf {
 
 namespace {
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int NT = 256;      // threads
-constexpr int A_PITCH = 80;  // bytes
-constexpr int B_PITCH = 24;  // bytes
+constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int NT = 256;                   // threads
+constexpr int STAGES = 3;
+constexpr int A_BYTES = BM * BK;          // 16 KB per stage
+constexpr int B_BYTES = BN * BK / 4;      // 8 KB per stage
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int A_LOADS = A_BYTES / (NT * 16);  // direct 16-byte loads per thread per stage
+constexpr int B_LOADS = B_BYTES / (NT * 16);
 constexpr int MI = 2, NI = 4;
 constexpr int EP_PITCH = 36;  // floats per staged epilogue row (32 + 4 pad)
-static_assert(NT / 64 * 32 * EP_PITCH * 4 <= 2 * BM * A_PITCH, "epilogue staging must fit in the A tiles");
+static_assert(A_LOADS == 4 && B_LOADS == 2, "load split");
+static_assert(NT / 64 * 32 * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue staging must fit");
+
+__device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_b(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt at maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Barrier without the memory fence of __syncthreads (whose release semantics would wait for
+// every outstanding direct-to-LDS load); ordering of the LDS ring is explicit via vmcnt.
+__device__ __forceinline__ void barrier_nofence() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane direct load from global memory into LDS: lane l reads 16 bytes at
+// base + off_l (base wave-uniform, in SGPRs; off_l a 32-bit lane offset) and they land at
+// LDS byte address lds + 16*l (lds wave-uniform, passed in M0).  Issued from inline
+// assembly so that the compiler does not order every later LDS read after it (the ring's
+// ordering is explicit: vmcnt waits and barriers); the instruction has no register result.
+// M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(const void *base_p, uint32_t off, uint32_t lds) {
+    const uint64_t b = reinterpret_cast<uintptr_t>(base_p);
+    // readfirstlane yields a signed int: take each half back to uint32_t before widening,
+    // or a low half with bit 31 set would be sign-extended into the high half
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+    lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds)
+        : "memory");
+}
+
+// Two packed words -> their 32 codes (two B operands).  The three shifted copies of the
+// pair come from 64-bit shifts; bits shifted in from the upper word land in bit positions
+// that the 0x03030303 mask clears.
+__device__ __forceinline__ void unpack_codes_x2(uint32_t w0, uint32_t w1, v4i &c0, v4i &c1) {
+#if MMF_UNPACK64
+    const uint64_t w = (static_cast<uint64_t>(w1) << 32) | w0;
+    const uint64_t s2 = w >> 2, s4 = w >> 4, s6 = w >> 6;
+    c0.x = static_cast<int>(w0 & 0x03030303u);
+    c1.x = static_cast<int>(w1 & 0x03030303u);
+    c0.y = static_cast<int>(static_cast<uint32_t>(s2) & 0x03030303u);
+    c1.y = static_cast<int>(static_cast<uint32_t>(s2 >> 32) & 0x03030303u);
+    c0.z = static_cast<int>(static_cast<uint32_t>(s4) & 0x03030303u);
+    c1.z = static_cast<int>(static_cast<uint32_t>(s4 >> 32) & 0x03030303u);
+    c0.w = static_cast<int>(static_cast<uint32_t>(s6) & 0x03030303u);
+    c1.w = static_cast<int>(static_cast<uint32_t>(s6 >> 32) & 0x03030303u);
+#else
+    c0 = unpack_codes(w0);
+    c1 = unpack_codes(w1);
+#endif
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
 
 template <int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) int8_t smA[2][BM * A_PITCH];
-    __shared__ __attribute__((aligned(16))) int8_t smB[2][BN * B_PITCH];
+    __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * STAGE_BYTES];
     __shared__ int32_t s_rs[BM];  // per-row activation code sum and scale of this tile
     __shared__ float s_a[BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int K = p.K, KW = K / 16;  // words per packed row
 
@@ -60,48 +146,71 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     while (sg + 1 < p.nseg && nt >= p.tiles_n[sg]) { nt -= p.tiles_n[sg]; ++sg; }
     const int64_t m0 = static_cast<int64_t>(mt) * BM;
 
-    // ---- global source pointers (clamped in-bounds; out-of-range rows are never stored)
-    const int arow = tid >> 1, ahalf = tid & 1;
-    const int64_t ag = m0 + arow < p.M ? m0 + arow : p.M - 1;
-    const int8_t *aptr = p.A + ag * K + ahalf * 32;
-    const uint32_t *bptr = nullptr;
-    if (tid < BN) {
+    // ---- direct-load sources.  Load i of this thread fills 16-byte LDS slot
+    //      s = (wave*L + i)*64 + lane of the stage from a wave-uniform base plus a 32-bit lane
+    //      offset fixed for the whole k loop.  Rows beyond M / N are clamped in-bounds (their
+    //      outputs are never stored); in a ragged last k-tile the upper half is re-read from
+    //      the lower half (in-bounds) and multiplied by zero codes.
+    const int8_t *a_base = p.A + m0 * K;
+    uint32_t a_off_g[A_LOADS];
+    bool a_hi[A_LOADS];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+        const int s = (wave * A_LOADS + i) * 64 + lane;
+        const int row = s >> 3, c = (s & 7) ^ swz_a(row);
+        const int64_t r = m0 + row < p.M ? row : p.M - 1 - m0;
+        a_off_g[i] = static_cast<uint32_t>(r * K + 16 * c);
+        a_hi[i] = c >= 4;
+    }
+    const uint32_t *b_base[B_LOADS];
+    uint32_t b_off_g[B_LOADS];
+    bool b_hi[B_LOADS];
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+        const int s = (wave * B_LOADS + i) * 64 + lane;
+        const int row = s >> 1, h = (s & 1) ^ swz_b(row);
+        int r;
         if constexpr (EPI == EPI_GLU) {
-            // tile column c: wave half wn = c / 128, block ni = (c % 128) / 32, lane j = c % 32
-            const int c = tid, cwn = c >> 7, cni = (c & 127) >> 5;
-            const int sub = cni >> 1;  // 0: gate, 1: up
-            const int f = nt * 128 + 64 * cwn + 32 * (cni & 1) + (c & 31);
-            const Seg &S = p.seg[sub];
-            bptr = S.packed + static_cast<int64_t>(f < S.n ? f : S.n - 1) * KW;
+            // tile column c: wave half wn = c / 128, block ni = (c % 128) / 32, lane j = c % 32;
+            // the 32 rows of one load share the block, hence the matrix (gate or up)
+            const int blk = wave * B_LOADS + i;
+            const int cwn = blk >> 2, cni = blk & 3;
+            const Seg &S = p.seg[cni >> 1];
+            const int f = nt * 128 + 64 * cwn + 32 * (cni & 1) + (row & 31);
+            r = f < S.n ? f : S.n - 1;
+            b_base[i] = S.packed;
         } else {
             const Seg &S = p.seg[sg];
-            const int n = nt * BN + tid;
-            bptr = S.packed + static_cast<int64_t>(n < S.n ? n : S.n - 1) * KW;
+            const int n = nt * BN + row;
+            r = n < S.n ? n : S.n - 1;
+            b_base[i] = S.packed;
         }
+        b_off_g[i] = static_cast<uint32_t>((r * KW + 4 * h) * 4);
+        b_hi[i] = h != 0;
     }
+    const int nk = (K + BK - 1) / BK;
+    const bool ragged = (K % BK) != 0;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    auto issue = [&](int kt, int st) {
+        const uint32_t dst = lds0 + st * STAGE_BYTES;
+        const bool cut = ragged && kt == nk - 1;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+            const uint32_t off = cut && a_hi[i] ? a_off_g[i] - 64 : a_off_g[i];
+            dma16(a_base + kt * BK, off, dst + (wave * A_LOADS + i) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+            const uint32_t off = cut && b_hi[i] ? b_off_g[i] - 16 : b_off_g[i];
+            dma16(b_base[i] + kt * (BK / 16), off, dst + A_BYTES + (wave * B_LOADS + i) * 1024);
+        }
+    };
 
     if (tid < BM) {
         const int64_t r = m0 + tid < p.M ? m0 + tid : p.M - 1;
         s_rs[tid] = p.rowsum[r];
         s_a[tid] = p.a[r];
     }
-
-    uint4 ra0, ra1, rb = make_uint4(0, 0, 0, 0);
-    auto gload = [&](int kt) {
-        ra0 = *reinterpret_cast<const uint4 *>(aptr + kt * BK);
-        ra1 = *reinterpret_cast<const uint4 *>(aptr + kt * BK + 16);
-        if (tid < BN) rb = *reinterpret_cast<const uint4 *>(bptr + kt * 4);
-    };
-    auto sstore = [&](int buf) {
-        int8_t *da = smA[buf] + arow * A_PITCH + ahalf * 32;
-        *reinterpret_cast<uint4 *>(da) = ra0;
-        *reinterpret_cast<uint4 *>(da + 16) = ra1;
-        if (tid < BN) {
-            uint2 *db = reinterpret_cast<uint2 *>(smB[buf] + tid * B_PITCH);
-            db[0] = make_uint2(rb.x, rb.y);
-            db[1] = make_uint2(rb.z, rb.w);
-        }
-    };
 
     v16i acc[MI][NI];
 #pragma unroll
@@ -112,45 +221,78 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
     const int g = lane >> 5, r32 = lane & 31;
-    const int nk = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        v4i av[MI][2];
+    // fragment offsets inside a stage: A row (wm*64 + mi*32 + r32), logical chunk 4g + ks;
+    // B row (wn*128 + ni*32 + r32), half g (its swizzle does not depend on ni)
+    int a_off[MI][4];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int8_t *pa = smA[cur] + (wm * 64 + mi * 32 + r32) * A_PITCH + g * 32;
-            av[mi][0] = *reinterpret_cast<const v4i *>(pa);
-            av[mi][1] = *reinterpret_cast<const v4i *>(pa + 16);
+    for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * 64 + mi * 32 + r32;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a_off[mi][ks] = row * BK + 16 * ((4 * g + ks) ^ swz_a(row));
+    }
+    const int brow = wn * 128 + r32;
+    const int b_off = A_BYTES + brow * 32 + 16 * (g ^ swz_b(brow));
+
+    // one k-tile: wait for it, free the oldest stage, refill it, multiply.  ST is static so
+    // every LDS address is a fixed register plus an immediate.
+    auto step = [&](int kt, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        // tile kt has landed once at most the next tile's loads are outstanding
+        if (kt + 1 < nk) wait_vmcnt<A_LOADS + B_LOADS>();
+        else wait_vmcnt<0>();
+        barrier_nofence();  // every wave's part of tile kt is in LDS; stage kt-1 is free
+        if (kt + 2 < nk) issue(kt + 2, (ST + 2) % STAGES);
+        const int8_t *sa = smem + ST * STAGE_BYTES;
+        v4i av[MI][4];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) av[mi][ks] = *reinterpret_cast<const v4i *>(sa + a_off[mi][ks]);
+        uint4 bw[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) bw[ni] = *reinterpret_cast<const uint4 *>(sa + b_off + ni * 1024);
+        if (ragged && kt == nk - 1 && g) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) bw[ni] = make_uint4(0, 0, 0, 0);
         }
-        uint2 bw[NI];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            bw[ni] = *reinterpret_cast<const uint2 *>(smB[cur] + (wn * 128 + ni * 32 + r32) * B_PITCH + g * 8);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int half = 0; half < 2; ++half) {
+            v4i bv[NI][2];
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-                const v4i bv = unpack_codes(ks ? bw[ni].y : bw[ni].x);
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][ks], bv, acc[mi][ni], 0, 0, 0);
+                const uint32_t w0 = half ? bw[ni].z : bw[ni].x, w1 = half ? bw[ni].w : bw[ni].y;
+                unpack_codes_x2(w0, w1, bv[ni][0], bv[ni][1]);
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][2 * half + kk], bv[ni][kk], acc[mi][ni], 0, 0, 0);
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    for (int kt = 0; kt < nk; kt += 3) {
+        step(kt, S0{});
+        if (kt + 1 < nk) step(kt + 1, S1{});
+        if (kt + 2 < nk) step(kt + 2, S2{});
     }
+    __syncthreads();  // all waves are done with the ring before it is reused for staging
 
     // ---- epilogue.  A lane holds C[row][col] for col = r32 of each 32-wide block and rows
     //      8*(e/4) + 4*g + (e%4) of each 32-tall block.  Final fp32 values are computed in
     //      that layout (rescale, bias, SiLU(gate)*up), staged one 32 x 32 block at a time in
     //      LDS (per-wave region, 36-float pitch), and read back as 8 consecutive columns of
     //      one row per lane, so the residual loads and the output stores are 16-byte
-    //      accesses covering whole row segments.
-    float *stg = reinterpret_cast<float *>(&smA[0][0]) + wave * (32 * EP_PITCH);
+    //      accesses covering whole row segments.  The staging region is private to the
+    //      wave, so only wave-level ordering is needed.
+    float *stg = reinterpret_cast<float *>(smem) + wave * (32 * EP_PITCH);
     constexpr int NOB = EPI == EPI_GLU ? 2 : NI;  // output blocks per 32-row slab
     // 16-byte accesses need 8-element-aligned row strides and column offsets
     const bool vec_ok = (p.ldo % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0) &&
@@ -168,29 +310,33 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob) {
             // global column of this lane's value and of the block's first column
-            int col_lane, col0;
+            int col0;
             if constexpr (EPI == EPI_GLU) {
                 col0 = nt * 128 + 64 * wn + 32 * ob;
             } else {
                 col0 = nt * BN + wn * 128 + ob * 32;
             }
-            col_lane = col0 + r32;
+            const int col_lane = col0 + r32;
             const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
             const int ncols = S.n;
             float v[16];
+            if constexpr (EPI == EPI_GLU) {
+                const float sg0 = p.seg[0].scale, su = p.seg[1].scale;
+                const float bg = p.seg[0].bias && col_lane < ncols ? p.seg[0].bias[col_lane] : 0.0f;
+                const float bu = p.seg[1].bias && col_lane < ncols ? p.seg[1].bias[col_lane] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                if constexpr (EPI == EPI_GLU) {
+                for (int e = 0; e < 16; ++e) {
                     const int32_t ag_ = acc[mi][ob][e] - rs_e[e], au = acc[mi][ob + 2][e] - rs_e[e];
-                    float yg = static_cast<float>(ag_) * (p.seg[0].scale * a_e[e]);
-                    float yu = static_cast<float>(au) * (p.seg[1].scale * a_e[e]);
-                    if (p.seg[0].bias && col_lane < ncols) yg += p.seg[0].bias[col_lane];
-                    if (p.seg[1].bias && col_lane < ncols) yu += p.seg[1].bias[col_lane];
+                    const float yg = static_cast<float>(ag_) * (sg0 * a_e[e]) + bg;
+                    const float yu = static_cast<float>(au) * (su * a_e[e]) + bu;
                     v[e] = siluf_(yg) * yu;
-                } else {
+                }
+            } else {
+                const float bb = S.bias && col_lane < ncols ? S.bias[col_lane] : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
                     const int32_t av_ = acc[mi][ob][e] - rs_e[e];
-                    v[e] = static_cast<float>(av_) * (S.scale * a_e[e]);
-                    if (S.bias && col_lane < ncols) v[e] += S.bias[col_lane];
+                    v[e] = static_cast<float>(av_) * (S.scale * a_e[e]) + bb;
                 }
             }
             if (p.cap.acc) {  // integer accumulators of captured rows (rare; test protocol)
@@ -210,7 +356,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) stg[(8 * (e >> 2) + 4 * g + (e & 3)) * EP_PITCH + r32] = v[e];
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
             // lane l: rows l/4 and l/4 + 16 of the block, columns 8*(l%4) .. +7
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -246,26 +393,33 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                             if (col + j < ncols) o[j] += load_act<OUT_BF16>(p.resid, ri + j);
                     }
                 }
-                if constexpr (OUT_BF16) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) o[j] = round_to_bf16(o[j]);
-                }
                 const int64_t oi = row * p.ldo + ocol;
-                if (full) {
-                    if constexpr (OUT_BF16) {
-                        uint32_t w[4];
+                if constexpr (OUT_BF16) {
+                    uint32_t w[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            w[j] = (__float_as_uint(o[2 * j]) >> 16) | (__float_as_uint(o[2 * j + 1]) & 0xFFFF0000u);
+                    for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
+                    if (full) {
                         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + oi) = make_uint4(w[0], w[1], w[2], w[3]);
                     } else {
-                        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi) = make_float4(o[0], o[1], o[2], o[3]);
-                        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi + 4) = make_float4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            if (col + j < ncols)
+                                static_cast<uint16_t *>(p.out)[oi + j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {  // the stored (rounded) values, for the capture
+                        o[2 * j] = __uint_as_float(w[j] << 16);
+                        o[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
                     }
                 } else {
+                    if (full) {
+                        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi) = make_float4(o[0], o[1], o[2], o[3]);
+                        *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi + 4) = make_float4(o[4], o[5], o[6], o[7]);
+                    } else {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (col + j < ncols) store_act<OUT_BF16>(p.out, oi + j, o[j]);
+                        for (int j = 0; j < 8; ++j)
+                            if (col + j < ncols) static_cast<float *>(p.out)[oi + j] = o[j];
+                    }
                 }
                 if (p.cap.y_out && p.cap.row0 <= row && row < p.cap.row1) {
                     float *cy = p.cap.y_out + (row - p.cap.row0) * p.ldo + ocol;
@@ -274,7 +428,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                         if (col + j < ncols) cy[j] = o[j];
                 }
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
         }
     }
 }

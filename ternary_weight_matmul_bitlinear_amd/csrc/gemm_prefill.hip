@@ -299,6 +299,31 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                         (EPI == EPI_GLU || p.seg[sg].out_col0 % 8 == 0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+        // residuals of this 32-row slab (bf16: all its blocks; fp32: loaded per block), issued
+        // before the values are computed so that their latency overlaps the rescale
+        constexpr int RB = EPI == EPI_RESID ? (OUT_BF16 ? NI : 1) : 1;
+        uint4 rvb[RB][2][OUT_BF16 ? 1 : 2];
+        auto load_resid = [&](int ob, uint4 (&dst)[2][OUT_BF16 ? 1 : 2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rr = (lane >> 2) + 16 * i, cc = 8 * (lane & 3);
+                const int64_t row = m0 + wm * 64 + mi * 32 + rr;
+                const int col = nt * BN + wn * 128 + ob * 32 + cc;
+                if (row < p.M && vec_ok && col + 8 <= p.seg[sg].n) {
+                    const int64_t ri = row * p.ldr + p.seg[sg].out_col0 + col;
+                    if constexpr (OUT_BF16) {
+                        dst[i][0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.resid) + ri);
+                    } else {
+                        dst[i][0] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.resid) + ri);
+                        dst[i][OUT_BF16 ? 0 : 1] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.resid) + ri + 4);
+                    }
+                }
+            }
+        };
+        if constexpr (EPI == EPI_RESID && OUT_BF16) {
+#pragma unroll
+            for (int ob = 0; ob < NI; ++ob) load_resid(ob, rvb[ob]);
+        }
         int32_t rs_e[16];
         float a_e[16];
 #pragma unroll
@@ -319,6 +344,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
             const int col_lane = col0 + r32;
             const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
             const int ncols = S.n;
+            if constexpr (EPI == EPI_RESID && !OUT_BF16) load_resid(ob, rvb[0]);
             float v[16];
             if constexpr (EPI == EPI_GLU) {
                 const float sg0 = p.seg[0].scale, su = p.seg[1].scale;
@@ -374,7 +400,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                     const int64_t ri = row * p.ldr + ocol;
                     if (full) {
                         if constexpr (OUT_BF16) {
-                            const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.resid) + ri);
+                            const uint4 u = rvb[ob][i][0];
                             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
@@ -382,8 +408,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                                 o[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
                             }
                         } else {
-                            const float4 r0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri);
-                            const float4 r1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri + 4);
+                            const float4 r0 = __builtin_bit_cast(float4, rvb[0][i][0]);
+                            const float4 r1 = __builtin_bit_cast(float4, rvb[0][i][OUT_BF16 ? 0 : 1]);
                             o[0] += r0.x; o[1] += r0.y; o[2] += r0.z; o[3] += r0.w;
                             o[4] += r1.x; o[5] += r1.y; o[6] += r1.z; o[7] += r1.w;
                         }

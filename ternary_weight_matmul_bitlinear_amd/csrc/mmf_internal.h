@@ -151,6 +151,7 @@ struct GemmArgs {
     int32_t nseg;
     int32_t tiles_n[3];    // N tiles per segment (EPI_GLU: tiles of 64 gate/up pairs)
     int32_t tiles_n_total;
+    int32_t tiles_total;   // M tiles x tiles_n_total (set by the launcher)
     int32_t epi;
     void *out;
     int32_t ldo;

@@ -137,6 +137,10 @@ int mmf_set_regime(int regime);
  * stream has been synchronised, mmf_timing_query returns the number of timed launches and
  * their summed duration in ms for a family name (see mmf_timing_name); reset clears them. */
 int mmf_timing_enable(int enable);
+/* Restrict timing to the families whose bit (1 << i, i as in mmf_timing_name) is set in
+ * mask; the default is every family.  Events cost a few microseconds of queue time each,
+ * so timing only the kernel of interest keeps the measured stream close to an untimed one. */
+int mmf_timing_families(uint32_t mask);
 int mmf_timing_reset(void);
 int mmf_timing_query(const char *family, int64_t *launches, double *total_ms);
 /* Name of family i (0 <= i < mmf_timing_count()), or NULL. */

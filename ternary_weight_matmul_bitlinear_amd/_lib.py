@@ -54,6 +54,7 @@ SIGNATURES = {
     "mmf_last_error": (C.c_char_p, []),
     "mmf_set_regime": (C.c_int, [C.c_int]),
     "mmf_timing_enable": (C.c_int, [C.c_int]),
+    "mmf_timing_families": (C.c_int, [C.c_uint32]),
     "mmf_timing_reset": (C.c_int, []),
     "mmf_timing_query": (C.c_int, [C.c_char_p, P(i64), P(C.c_double)]),
     "mmf_timing_name": (C.c_char_p, [C.c_int]),

@@ -348,6 +348,19 @@ def timing_enable(on: bool = True) -> None:
     L.check("mmf_timing_enable", L.lib().mmf_timing_enable(int(on)))
 
 
+def timing_families(names=None) -> None:
+    """Time only the named kernel families (None: all of them)."""
+    if names is None:
+        mask = 0xFFFFFFFF
+    else:
+        lib = L.lib()
+        idx = {lib.mmf_timing_name(i).decode(): i for i in range(lib.mmf_timing_count())}
+        mask = 0
+        for n in names:
+            mask |= 1 << idx[n]
+    L.check("mmf_timing_families", L.lib().mmf_timing_families(mask))
+
+
 def timing_reset() -> None:
     L.check("mmf_timing_reset", L.lib().mmf_timing_reset())
 

@@ -83,13 +83,14 @@ struct TimingFamily {
 };
 static std::mutex g_tmu;
 static bool g_timing = false;
+static uint32_t g_timing_mask = 0xFFFFFFFFu;  // families that record events while enabled
 static TimingFamily g_fam[FAM_COUNT];
 static const char *kFamNames[FAM_COUNT] = {"quant", "gemm_ifg", "gemm_o", "gemm_gateup",
                                            "gemm_down", "gemm", "gemv", "scan", "embed"};
 static thread_local hipEvent_t t_pending = nullptr;
 
 void timing_begin(int family, hipStream_t s) {
-    if (!g_timing) return;
+    if (!g_timing || !((g_timing_mask >> family) & 1u)) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     TimingFamily &f = g_fam[family];
     if (f.used + 2 > f.ev.size()) {
@@ -301,6 +302,12 @@ int mmf_set_regime(int regime) {
 int mmf_timing_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;
+    return MMF_OK;
+}
+
+int mmf_timing_families(uint32_t mask) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing_mask = mask;
     return MMF_OK;
 }
 

@@ -118,13 +118,6 @@ __device__ __forceinline__ void unpack_codes_x2(uint32_t w0, uint32_t w1, v4i &c
 #endif
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    const f2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
-}
-
 template <int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * STAGE_BYTES];

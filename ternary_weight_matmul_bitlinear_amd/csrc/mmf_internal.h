@@ -25,6 +25,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo in bits 0-15), round to nearest even, one instruction
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
 __device__ __forceinline__ float round_to_bf16(float f) {
     return bf16_bits_to_f32(f32_to_bf16_bits(f));
 }

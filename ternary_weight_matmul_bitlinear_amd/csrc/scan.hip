@@ -395,6 +395,269 @@ __global__ __launch_bounds__(256) void scan_out_kernel(ScanArgs p) {
     }
 }
 
+template <bool BF16, int CPL> struct RawVec {
+    static constexpr int NW = BF16 ? CPL / 2 : CPL;  // 32-bit words
+    uint32_t w[NW];
+};
+
+template <bool BF16, int CPL>
+__device__ __forceinline__ void load_vec(const void *base, int64_t elem, RawVec<BF16, CPL> &r) {
+    constexpr int NW = RawVec<BF16, CPL>::NW;
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const char *>(base) + elem * (BF16 ? 2 : 4));
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < NW; k += 4) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(p + k);
+            r.w[k] = u.x; r.w[k + 1] = u.y; r.w[k + 2] = u.z; r.w[k + 3] = u.w;
+        }
+    } else if constexpr (NW == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        r.w[0] = u.x; r.w[1] = u.y;
+    } else {
+        r.w[0] = p[0];
+    }
+}
+
+template <bool BF16, int CPL>
+__device__ __forceinline__ void cvt_vec(const RawVec<BF16, CPL> &r, float (&v)[CPL]) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int k = 0; k < CPL / 2; ++k) {
+            v[2 * k] = __uint_as_float(r.w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(r.w[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) v[k] = __uint_as_float(r.w[k]);
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void load_f32(const float *p, float (&v)[CPL], float dflt) {
+    if (!p) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) v[k] = dflt;
+        return;
+    }
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < CPL; k += 4) {
+            const float4 u = *reinterpret_cast<const float4 *>(p + k);
+            v[k] = u.x; v[k + 1] = u.y; v[k + 2] = u.z; v[k + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) v[k] = p[k];
+    }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_f32(float *p, const float (&v)[CPL]) {
+    if constexpr (CPL % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < CPL; k += 4) *reinterpret_cast<float4 *>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) p[k] = v[k];
+    }
+}
+
+// Row-wide reduction of TS per-token values: wave butterflies (lane l ends with value
+// index l >> SH), then with W > 1 an exchange through LDS slot buffer red[W][TS].
+template <int TS, int W, bool MAX, typename T>
+__device__ __forceinline__ void row_reduce(T (&v)[TS], T (*red)[TS], T (&out)[TS]) {
+    constexpr int SH = TS == 8 ? 3 : (TS == 4 ? 4 : 5);
+    const int lane = threadIdx.x & 63;
+    const T r = wave_reduce_multi<TS, MAX>(v);
+    if constexpr (W == 1) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) out[t] = __shfl(r, t << SH, 64);
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if ((lane & ((1 << SH) - 1)) == 0) red[wave][lane >> SH] = r;
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            T acc = red[0][t];
+#pragma unroll
+            for (int w = 1; w < W; ++w) acc = MAX ? (acc > red[w][t] ? acc : red[w][t]) : acc + red[w][t];
+            out[t] = acc;
+        }
+    }
+}
+
+template <bool IN_BF16, int QUANT, bool OUT_BF16, int CPL, int W, int TS>
+__global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
+    __shared__ float red_ss[2][W][TS], red_mx[2][W][TS], red_s2[2][W][TS];
+    __shared__ int red_q[2][W][TS];
+    const int c = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int D = p.D;
+    const int d0 = tid * CPL;
+    const int64_t t_beg = static_cast<int64_t>(c) * p.chunk;
+    const int64_t t_end = t_beg + p.chunk < p.T ? t_beg + p.chunk : p.T;
+    const float inv_d = 1.0f / static_cast<float>(D);
+
+    float h[CPL], fb[CPL], gw[CPL], qg[CPL];
+    if (p.n_chunks > 1) load_f32<CPL>(p.hin + (b * p.n_chunks + c) * D + d0, h, 0.0f);
+    else load_f32<CPL>(p.h0 ? p.h0 + b * D + d0 : nullptr, h, 0.0f);
+    load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    load_f32<CPL>(p.gnorm_w ? p.gnorm_w + d0 : nullptr, gw, 1.0f);
+    load_f32<CPL>(QUANT && p.q_gamma ? p.q_gamma + d0 : nullptr, qg, 1.0f);
+
+    using Raw = RawVec<IN_BF16, CPL>;
+    Raw ip[TS], fp[TS], gp[TS];
+    const int64_t D3 = 3 * static_cast<int64_t>(D);
+    auto fetch = [&](int64_t tt) __attribute__((always_inline)) {
+        const int nt = static_cast<int>(t_end - tt < TS ? t_end - tt : TS);
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            if (t < nt) {
+                const int64_t base = (b * p.T + tt + t) * D3 + d0;
+                load_vec<IN_BF16, CPL>(p.ifg, base, ip[t]);
+                load_vec<IN_BF16, CPL>(p.ifg, base + D, fp[t]);
+                load_vec<IN_BF16, CPL>(p.ifg, base + 2 * D, gp[t]);
+            }
+        }
+    };
+    if (t_beg < t_end) fetch(t_beg);
+
+    int par = 0;
+    for (int64_t tt = t_beg; tt < t_end; tt += TS, par ^= 1) {
+        const int nt = static_cast<int>(t_end - tt < TS ? t_end - tt : TS);
+        float o[TS][CPL], ss[TS];
+        Raw gs[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            float iv[CPL], fv[CPL];
+            cvt_vec<IN_BF16, CPL>(ip[t], iv);
+            cvt_vec<IN_BF16, CPL>(fp[t], fv);
+            gs[t] = gp[t];
+            ss[t] = 0.f;
+            if (t < nt) {
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    float f;
+                    h[k] = gate_step(h[k], iv[k], fv[k], fb[k], &f);
+                    ss[t] = fmaf(h[k], h[k], ss[t]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) o[t][k] = h[k];
+        }
+        if (tt + TS < t_end) fetch(tt + TS);  // next tile in flight during the reductions
+
+        if (p.gate_mode == 0) {
+            float tot[TS];
+            row_reduce<TS, W, false>(ss, red_ss[par], tot);
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                const float r = 1.0f / sqrtf(tot[t] * inv_d + p.eps);
+                float gv[CPL];
+                cvt_vec<IN_BF16, CPL>(gs[t], gv);
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) o[t][k] = o[t][k] * r * gw[k] * siluf_(gv[k]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                float gv[CPL];
+                cvt_vec<IN_BF16, CPL>(gs[t], gv);
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) o[t][k] = sigmoidf_(gv[k]) * o[t][k];
+            }
+        }
+
+        if constexpr (QUANT == 0) {
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                if (t >= nt) continue;
+                const int64_t oi = (b * p.T + tt + t) * D + d0;
+                if constexpr (OUT_BF16) {
+                    uint32_t w[CPL / 2 > 0 ? CPL / 2 : 1];
+#pragma unroll
+                    for (int k = 0; k < CPL / 2; ++k) w[k] = pack_bf16x2(o[t][2 * k], o[t][2 * k + 1]);
+                    uint32_t *dst = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p.out) + oi);
+                    if constexpr (CPL == 8) *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                    else if constexpr (CPL == 4) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+                    else {
+#pragma unroll
+                        for (int k = 0; k < CPL / 2; ++k) dst[k] = w[k];
+                    }
+                } else {
+                    store_f32<CPL>(static_cast<float *>(p.out) + oi, o[t]);
+                }
+            }
+        } else {
+            // ---- int8 quantization of o (with o_proj's gain) for o_proj
+            float mx[TS], s2[TS], mxt[TS], s2t[TS];
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                mx[t] = 0.f;
+                s2[t] = 0.f;
+                if (t < nt) {
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) {
+                        mx[t] = fmaxf(mx[t], fabsf(o[t][k] * qg[k]));
+                        s2[t] = fmaf(o[t][k], o[t][k], s2[t]);
+                    }
+                }
+            }
+            row_reduce<TS, W, true>(mx, red_mx[par], mxt);
+            row_reduce<TS, W, false>(s2, red_s2[par], s2t);
+            int qs[TS];
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                qs[t] = 0;
+                if (t >= nt) continue;
+                const float me = fmaxf(mxt[t], 1e-5f);
+                const float sc = 127.0f / me;
+                const int64_t row = b * p.T + tt + t;
+                uint32_t pk[CPL / 4 > 0 ? CPL / 4 : 1] = {};
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    float rq = rintf((o[t][k] * qg[k]) * sc);
+                    rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+                    const int qi = static_cast<int>(rq);
+                    qs[t] += qi;
+                    pk[k >> 2] |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * (k & 3));
+                }
+                int8_t *qd = p.q + row * D + d0;
+                if constexpr (CPL == 8) *reinterpret_cast<uint2 *>(qd) = make_uint2(pk[0], pk[1]);
+                else if constexpr (CPL == 4) *reinterpret_cast<uint32_t *>(qd) = pk[0];
+                else {
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) qd[k] = static_cast<int8_t>((pk[k >> 2] >> (8 * (k & 3))) & 0xFF);
+                }
+                if (p.cap.row0 <= row && row < p.cap.row1) {
+                    const int64_t cr = row - p.cap.row0;
+                    if (p.cap.x_in) store_f32<CPL>(p.cap.x_in + cr * D + d0, o[t]);
+                    if (p.cap.q) {
+#pragma unroll
+                        for (int k = 0; k < CPL; ++k) p.cap.q[cr * D + d0 + k] = static_cast<int8_t>((pk[k >> 2] >> (8 * (k & 3))) & 0xFF);
+                    }
+                }
+            }
+            int qtot[TS];
+            row_reduce<TS, W, false>(qs, red_q[par], qtot);
+            if (tid < nt) {
+                int qv = 0;
+                float me = 0.f, s2v = 0.f;
+#pragma unroll
+                for (int t = 0; t < TS; ++t)
+                    if (t == tid) { qv = qtot[t]; me = fmaxf(mxt[t], 1e-5f); s2v = s2t[t]; }
+                const int64_t row = b * p.T + tt + tid;
+                const float a = me / 127.0f * (1.0f / sqrtf(s2v * inv_d + p.q_eps));
+                p.a[row] = a;
+                p.rowsum[row] = qv;
+                if (p.cap.a && p.cap.row0 <= row && row < p.cap.row1) p.cap.a[row - p.cap.row0] = a;
+            }
+        }
+    }
+    if (c == p.n_chunks - 1 && p.h_out) store_f32<CPL>(p.h_out + b * D + d0, h);
+}
+
 __global__ void copy_state_kernel(const float *h0, float *h_out, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) h_out[i] = h0 ? h0[i] : 0.0f;
@@ -416,11 +679,52 @@ void launch_out_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
     launch_out_ts<IN_BF16, QUANT, OUT_BF16, 4>(a, grid, s);
 }
 
+// Row-layout output pass: W waves per token row, CPL channels per lane.
+// Tiles of 2 tokens at 8 channels per lane (4 at 4): larger tiles amortize the reductions
+// further but their registers halve the waves per SIMD (measured slower).
+template <bool IN_BF16, int QUANT, bool OUT_BF16, int CPL, int W>
+void launch_row(const ScanArgs &a, dim3 grid, hipStream_t s) {
+    constexpr int TS = CPL >= 8 ? 2 : 4;
+    hipLaunchKernelGGL((scan_row_kernel<IN_BF16, QUANT, OUT_BF16, CPL, W, TS>), grid, dim3(64 * W), 0, s, a);
+}
+
+template <bool IN_BF16, int QUANT, bool OUT_BF16>
+bool launch_row_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
+    const int D = a.D;
+    if (D % 512 == 0) {
+        switch (D / 512) {
+            case 1: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 1>(a, grid, s); return true;
+            case 2: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 2>(a, grid, s); return true;
+            case 3: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 3>(a, grid, s); return true;
+            case 4: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 4>(a, grid, s); return true;
+            case 5: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 5>(a, grid, s); return true;
+            case 6: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 6>(a, grid, s); return true;
+            case 7: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 7>(a, grid, s); return true;
+            case 8: launch_row<IN_BF16, QUANT, OUT_BF16, 8, 8>(a, grid, s); return true;
+            default: return false;
+        }
+    }
+    if (D % 256 == 0) {
+        switch (D / 256) {
+            case 1: launch_row<IN_BF16, QUANT, OUT_BF16, 4, 1>(a, grid, s); return true;
+            case 3: launch_row<IN_BF16, QUANT, OUT_BF16, 4, 3>(a, grid, s); return true;
+            case 4: launch_row<IN_BF16, QUANT, OUT_BF16, 4, 4>(a, grid, s); return true;
+            case 5: launch_row<IN_BF16, QUANT, OUT_BF16, 4, 5>(a, grid, s); return true;
+            default: return false;
+        }
+    }
+    return false;
+}
+
 template <bool IN_BF16>
 void launch_out(const ScanArgs &a, dim3 grid, hipStream_t s) {
-    if (a.q) launch_out_q<IN_BF16, 1, false>(a, grid, s);
-    else if (a.out_bf16) launch_out_q<IN_BF16, 0, true>(a, grid, s);
-    else launch_out_q<IN_BF16, 0, false>(a, grid, s);
+    if (a.q) {
+        if (!launch_row_q<IN_BF16, 1, false>(a, grid, s)) launch_out_q<IN_BF16, 1, false>(a, grid, s);
+    } else if (a.out_bf16) {
+        if (!launch_row_q<IN_BF16, 0, true>(a, grid, s)) launch_out_q<IN_BF16, 0, true>(a, grid, s);
+    } else {
+        if (!launch_row_q<IN_BF16, 0, false>(a, grid, s)) launch_out_q<IN_BF16, 0, false>(a, grid, s);
+    }
 }
 }  // namespace
 

@@ -658,6 +658,110 @@ __global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
     if (c == p.n_chunks - 1 && p.h_out) store_f32<CPL>(p.h_out + b * D + d0, h);
 }
 
+// Phase 1, row layout: thread per (b, chunk, group of CPL channels); the chunk's CH tokens
+// of i and f are all loaded before the local scan runs (one 16-byte load per token and
+// pre-activation), so the whole chunk is in flight at once.
+template <bool BF16, int CPL, int CH>
+__global__ __launch_bounds__(256) void scan_local_row_kernel(ScanArgs p) {
+    const int G = p.D / CPL;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= p.B * p.n_chunks * G) return;
+    const int gi = static_cast<int>(idx % G);
+    const int64_t bc = idx / G;
+    const int c = static_cast<int>(bc % p.n_chunks);
+    const int64_t b = bc / p.n_chunks;
+    const int D = p.D, d0 = gi * CPL;
+    const int64_t t_beg = static_cast<int64_t>(c) * CH;
+    const int nt = static_cast<int>(p.T - t_beg < CH ? p.T - t_beg : CH);
+    const int64_t D3 = 3 * static_cast<int64_t>(D);
+    using Raw = RawVec<BF16, CPL>;
+    Raw iv[CH], fv[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+        if (t < nt) {
+            const int64_t base = (b * p.T + t_beg + t) * D3 + d0;
+            load_vec<BF16, CPL>(p.ifg, base, iv[t]);
+            load_vec<BF16, CPL>(p.ifg, base + D, fv[t]);
+        }
+    }
+    float fb[CPL], h[CPL], pf[CPL];
+    load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) { h[k] = 0.f; pf[k] = 1.f; }
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+        if (t < nt) {
+            float i4[CPL], f4[CPL];
+            cvt_vec<BF16, CPL>(iv[t], i4);
+            cvt_vec<BF16, CPL>(fv[t], f4);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                float f;
+                h[k] = gate_step(h[k], i4[k], f4[k], fb[k], &f);
+                pf[k] *= f;
+            }
+        }
+    }
+    const int64_t o = (b * p.n_chunks + c) * D + d0;
+    store_f32<CPL>(p.hloc + o, h);
+    store_f32<CPL>(p.pf + o, pf);
+}
+
+// Phase 2, two-level: workgroup per (b, 64 channels), wave s owns the s-th of 8 runs of
+// consecutive chunks.  Each wave folds its run into one affine map h -> A*h + B (lane =
+// channel), the maps are composed through LDS to give the state entering every run, and
+// each wave walks its run again writing the state entering each chunk.  Loads are batched
+// U chunks ahead of the dependent multiply-add chain.
+__global__ __launch_bounds__(512) void scan_carry2_kernel(ScanArgs p) {
+    constexpr int RUNS = 8, U = 16;
+    __shared__ float sA[RUNS][64], sB[RUNS][64];
+    const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + lane;
+    const int64_t b = blockIdx.y;
+    const int D = p.D, nc = p.n_chunks;
+    const int L = (nc + RUNS - 1) / RUNS;
+    const int c0 = s * L, c1 = c0 + L < nc ? c0 + L : nc;
+    const int64_t row0 = b * nc;
+    float A = 1.f, Bv = 0.f;
+    for (int c = c0; c < c1; c += U) {
+        float pf[U], hl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u < c1 ? c + u : c1 - 1;
+            pf[u] = p.pf[(row0 + cc) * D + d];
+            hl[u] = p.hloc[(row0 + cc) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c + u < c1) {
+                Bv = pf[u] * Bv + hl[u];
+                A *= pf[u];
+            }
+        }
+    }
+    sA[s][lane] = A;
+    sB[s][lane] = Bv;
+    __syncthreads();
+    float h = p.h0 ? p.h0[b * D + d] : 0.0f;
+    for (int j = 0; j < s; ++j) h = sA[j][lane] * h + sB[j][lane];
+    for (int c = c0; c < c1; c += U) {
+        float pf[U], hl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u < c1 ? c + u : c1 - 1;
+            pf[u] = p.pf[(row0 + cc) * D + d];
+            hl[u] = p.hloc[(row0 + cc) * D + d];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c + u < c1) {
+                p.hin[(row0 + c + u) * D + d] = h;
+                h = pf[u] * h + hl[u];
+            }
+        }
+    }
+}
+
 __global__ void copy_state_kernel(const float *h0, float *h_out, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) h_out[i] = h0 ? h0[i] : 0.0f;
@@ -732,12 +836,23 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.T <= 0) return hipSuccess;
     timing_begin(FAM_SCAN, s);
     if (a.n_chunks > 1) {
-        const dim3 g1(static_cast<unsigned>((a.D / 4 + 255) / 256), static_cast<unsigned>(a.n_chunks),
-                      static_cast<unsigned>(a.B));
-        if (a.ifg_bf16) hipLaunchKernelGGL((scan_local_kernel<true>), g1, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((scan_local_kernel<false>), g1, dim3(256), 0, s, a);
-        const dim3 g2(static_cast<unsigned>((a.D + 255) / 256), static_cast<unsigned>(a.B));
-        hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, s, a);
+        if (a.chunk == kScanChunk && a.D % 64 == 0) {
+            // row layout: 8 (bf16) or 4 (fp32) channels per thread, runs of chunks for the carry
+            const int cpl = a.ifg_bf16 ? 8 : 4;
+            const int64_t n = a.B * a.n_chunks * (a.D / cpl);
+            const dim3 g1(static_cast<unsigned>((n + 255) / 256));
+            if (a.ifg_bf16) hipLaunchKernelGGL((scan_local_row_kernel<true, 8, kScanChunk>), g1, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((scan_local_row_kernel<false, 4, kScanChunk>), g1, dim3(256), 0, s, a);
+            const dim3 g2(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B));
+            hipLaunchKernelGGL(scan_carry2_kernel, g2, dim3(512), 0, s, a);
+        } else {
+            const dim3 g1(static_cast<unsigned>((a.D / 4 + 255) / 256), static_cast<unsigned>(a.n_chunks),
+                          static_cast<unsigned>(a.B));
+            if (a.ifg_bf16) hipLaunchKernelGGL((scan_local_kernel<true>), g1, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((scan_local_kernel<false>), g1, dim3(256), 0, s, a);
+            const dim3 g2(static_cast<unsigned>((a.D + 255) / 256), static_cast<unsigned>(a.B));
+            hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, s, a);
+        }
     }
     const dim3 g3(static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(a.B));
     if (a.ifg_bf16) launch_out<true>(a, g3, s);

@@ -69,6 +69,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=128,
                     help="tokens per sequence of the causal prefix timed on the CPU")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="decode stack: sequences per step (default: the workload's B)")
+    ap.add_argument("--regime", choices=("auto", "decode", "prefill"), default="auto",
+                    help="BitLinear kernel choice (auto: by token count)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -85,11 +89,10 @@ def main() -> int:
     from ternary_weight_matmul_bitlinear_amd import api, synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.layers != 1 or w.vocab:
-        print(f"workload {w.name} is a stack; bench.py times single-block workloads",
-              file=sys.stderr)
-        return 2
     torch.cuda.set_device(0)
+    api.set_regime({"auto": 0, "decode": 1, "prefill": 2}[args.regime])
+    if w.layers != 1 or w.vocab:
+        return bench_stack(args, w)
     dt = torch.bfloat16 if w.bf16 else torch.float32
     lat = synth.layer_latents(w, 0)
     fb = np.full(w.D, w.f_bias, np.float32) if w.f_bias else None
@@ -186,6 +189,130 @@ def main() -> int:
                        "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"},
             "roofline": roofline, "cpu_baseline": cpu,
             "kernels": fams, "kernels_note": f"separate {nb}-step pass, events around every launch"}
+    print(json.dumps(line))
+    return 0
+
+
+def bench_stack(args, w) -> int:
+    """Stack workloads.  1.3B-decode: one step = one token for each of B sequences through
+    the ternary embedding, 24 blocks (state carried) and the LM head; the weights (about
+    325 MB packed) exceed the 256 MB MALL, so every step streams them from HBM.
+    2.7B-longctx: one step = the 32-block prefill of 2 x 32768 tokens."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api, synth
+
+    D, F, L = w.D, w.F, w.layers
+    fb = np.full(D, w.f_bias, np.float32) if w.f_bias else None
+    t_build = time.perf_counter()
+    blocks = []
+    for l in range(L):
+        blocks.append(api.Block.from_latents(synth.layer_latents(w, l), "cuda", f_bias=fb))
+    emb = head = None
+    if w.vocab:
+        E, H = synth.embedding_latents(w)
+        emb = api.TernaryLinear.from_latent(E)
+        head = api.TernaryLinear.from_latent(H)
+        del E, H
+    stack = api.Stack(blocks, emb, head)
+    print(f"# workload {w.name}: {L} layers, D={D} F={F}; weights built in "
+          f"{time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+
+    decode = bool(w.vocab)
+    B = args.batch or w.B
+    T = 1 if decode else w.T
+    steps = args.steps
+    hs = torch.zeros((L, B, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(stack.workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
+    if decode:
+        ids_all = torch.from_numpy(synth.token_ids(w, args.warmup + steps, B)).to("cuda")
+        logits = torch.empty((B, w.vocab), dtype=torch.float32, device="cuda")
+
+        def step(i):
+            api.stack_forward(stack, B, 1, ids=ids_all[i], h_state=hs, want_y=False,
+                              want_logits=True, ws=ws, logits=logits)
+    else:
+        x = torch.from_numpy(synth.activations(w)).to("cuda").to(torch.bfloat16)
+        y = torch.empty_like(x)
+
+        def step(i):
+            hs.zero_()
+            api.stack_forward(stack, B, T, x=x, ws=ws, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # per-launch durations of the dominant kernel family: an eager pass with events
+    fam = "gemv" if decode else "gemm_gateup"
+    api.timing_reset()
+    api.timing_families([fam])
+    api.timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    api.timing_enable(False)
+    n, ms = api.timing_query(fam)
+    graph_ms = None
+    if decode:
+        # the timed loop replays one captured step (a HIP graph): a decode step is ~120 small
+        # launches, whose host-side launch cost would otherwise dominate
+        ids_static = ids_all[0].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            api.stack_forward(stack, B, 1, ids=ids_static, h_state=hs, want_y=False,
+                              want_logits=True, ws=ws, logits=logits)
+        for i in range(args.warmup):
+            ids_static.copy_(ids_all[i])
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ids_static.copy_(ids_all[args.warmup + i])
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        graph_ms = elapsed * 1e3 / steps
+    else:
+        elapsed = eager_ms * steps / 1e3
+    ms_step = elapsed * 1e3 / steps
+    value = B * T * steps / elapsed
+
+    if decode:
+        # algorithmic bytes of the decode BitLinear launches (N*K/4 packed weights + rows in
+        # + rows out, residual where added), and of the whole step (plus embedding rows and
+        # the fp32 state read and written per layer)
+        def bl(N, K, in_b, out_b, resid=0):
+            return N * K // 4 + B * K * in_b + B * N * out_b + B * N * resid
+        per_layer = (bl(3 * D, D, 2, 2) + bl(D, D, 1, 2, 2) + bl(2 * F, D, 2, 0) + B * F * 2
+                     + bl(D, F, 2, 2, 2))
+        gemv_bytes = L * per_layer + bl(w.vocab, D, 2, 4)
+        step_bytes = gemv_bytes + B * D // 4 + B * D * 2 + L * B * D * 4 * 2
+        achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
+        roofline = {"kernel": "decode BitLinear (weight-streaming dot4 GEMV), all launches of a step",
+                    "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": None,
+                    "algorithmic_bytes_per_step": gemv_bytes}
+        extra = {"step_hbm_fraction": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                 "step_algorithmic_bytes": step_bytes, "eager_ms_per_step": eager_ms,
+                 "graph_ms_per_step": graph_ms}
+    else:
+        ops = 2.0 * (B * T) * D * (2 * F)
+        achieved = ops * n / (ms * 1e-3) / 1e12 if n else None
+        roofline = {"kernel": "gemm_gateup (int8 MFMA, SiLU(gate)*up epilogue), all layers",
+                    "bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS if achieved else None,
+                    "traffic": None, "algorithmic_ops_per_launch": ops}
+        extra = {}
+    line = {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic (seeded ids / N(0,1) activations, ternary weights from N(0,0.02^2) latents)",
+            "config": {"workload": w.name, "B": B, "T": T, "D": D, "F": F, "layers": L,
+                       "vocab": w.vocab or None, "activations": "bf16", "state": "fp32"},
+            "roofline": roofline, "cpu_baseline": None, **extra}
     print(json.dumps(line))
     return 0
 

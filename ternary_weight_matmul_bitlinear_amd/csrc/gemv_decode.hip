@@ -6,27 +6,47 @@
 // custom FPGA" (token generation is limited by moving the weights); Hysen Labs
 // "MatMul-Free LM", section "FusedBitLinear" (norm + quantize + accumulate in one kernel).
 //
-// With one token per step the weights (0.25 byte each) are read once and used once, so
-// the kernel is HBM-bound.  Design:
-//   - prologue: the workgroup RMS/absmax-quantizes its token group (<= 8 rows) straight
-//     into LDS (the same arithmetic as the standalone quantizer, so the int8 codes are
-//     identical), or copies rows that are already quantized;
-//   - each wave owns 8 weight rows, 8 lanes per row; lane j of a row reads 16-byte chunks
-//     j, j+8, ... (64 k each), so one load instruction moves 8 rows x 128 contiguous bytes;
-//   - each packed word unpacks to four dwords of int8 codes (code = q+1) consumed by
-//     v_dot4_i32_i8 against the LDS-resident int8 activations; the code offset is removed
-//     with the row sum of the activations (acc = sum q_x*code - sum q_x, exact);
-//   - the 8 partial sums of a row are combined with 3 xor-shuffle steps, after which lane j
-//     of the row writes token j (fused rescale, bias, residual or SiLU(gate)*up).
-// LDS layout of a token row: chunk c (64 bytes) at byte 64c + 16*(c/2), which puts the
-// eight chunks read by one instruction on disjoint bank quads.
+// With a few tokens per step the weights (0.25 byte each) are read once and used once, and
+// one BitLinear moves only a few MB, about one memory latency's worth of HBM bandwidth, so
+// the kernel is built to have every weight byte in flight as early as possible:
+//   - 16 lanes per weight row, 4 rows per wave, 16 rows per workgroup; lane j of a row
+//     holds 16-byte chunks j, j+16, ... (64 k each) of the row in registers, and all of
+//     them are requested at kernel entry, before the activations are looked at;
+//   - meanwhile the workgroup RMS/absmax-quantizes its token group (<= TG rows) into LDS
+//     (the same arithmetic as the standalone quantizer, so the int8 codes are identical),
+//     or copies rows that are already quantized;
+//   - each packed word gives four dwords of 2-bit codes, which one v_perm_b32 each maps to
+//     signed int8 weights (code 0,1,2 -> -1,0,+1), consumed by v_dot4_i32_i8 against the
+//     LDS-resident activations: the int32 result is the exact ternary product;
+//   - the 16 partial sums of a row are reduced for all tokens at once (halving exchanges),
+//     after which one lane per token writes the output (fused rescale, bias, residual or
+//     SiLU(gate)*up).
+// LDS layout: chunk c (64 k) of all TG token rows together, token t at byte
+// c*(64*TG + 16) + 64*t: token offsets are immediates, and the 16-byte pad puts the sixteen
+// chunks read by one instruction on distinct bank quads.
 #include "mmf_internal.h"
 
 namespace mmf {
 
 namespace {
 
-__device__ __forceinline__ int chunk_off(int c) { return c * 64 + (c >> 1) * 16; }
+constexpr int LPR = 16;          // lanes per weight row
+constexpr int RPW = 64 / LPR;    // rows per wave
+constexpr int RPB = 4 * RPW;     // rows per workgroup (256 threads)
+constexpr int CB = 8;            // 64-k chunks held per lane per pass (K <= 8192 in one pass)
+
+__host__ __device__ __forceinline__ int chunk_stride(int tg) { return 64 * tg + 16; }
+
+// 2-bit codes (0,1,2) in each byte of (w >> 2a) & 0x03030303 -> signed ternary int8 x 4.
+__device__ __forceinline__ v4i signed_codes(uint32_t w) {
+    constexpr uint32_t kTab = 0x000100FFu;  // byte v of the table = value of code v
+    v4i r;
+    r.x = static_cast<int>(__builtin_amdgcn_perm(0u, kTab, w & 0x03030303u));
+    r.y = static_cast<int>(__builtin_amdgcn_perm(0u, kTab, (w >> 2) & 0x03030303u));
+    r.z = static_cast<int>(__builtin_amdgcn_perm(0u, kTab, (w >> 4) & 0x03030303u));
+    r.w = static_cast<int>(__builtin_amdgcn_perm(0u, kTab, (w >> 6) & 0x03030303u));
+    return r;
+}
 
 template <bool BF16>
 __device__ __forceinline__ void load8v(const void *x, int64_t idx, float v[8]) {
@@ -58,119 +78,23 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
 }
 
 // XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations.
-template <int EPI, int XIN, bool OUT_BF16>
+// TG: token rows per workgroup (1, 4, 8 or 16).
+template <int EPI, int XIN, bool OUT_BF16, int TG>
 __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
     extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-    __shared__ float red_a[4][kGemvTokens], red_b[4][kGemvTokens];
-    __shared__ float s_a[kGemvTokens];
-    __shared__ int s_rs[kGemvTokens];
+    __shared__ float red_m[4][TG], red_s[4][TG];
+    __shared__ float s_a[TG];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = p.K, NC = K / 64;
-    const int rowb = chunk_off(NC);  // bytes per token row in LDS (NC is even or padded)
-    const int TG = p.tokens_per_group;
+    constexpr int CS = 64 * TG + 16;      // bytes per chunk of all token rows in LDS
     const int64_t t0 = static_cast<int64_t>(blockIdx.y) * TG;
     const int mt = static_cast<int>(p.M - t0 < TG ? p.M - t0 : TG);
     const bool cap_blk = blockIdx.x == 0;
 
-    // ---------------------------------------------------------------- prologue
-    if constexpr (XIN != 0) {
-        constexpr bool BF = XIN == 2;
-        float pm[kGemvTokens], ps[kGemvTokens];
-#pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) { pm[t] = 0.f; ps[t] = 0.f; }
-#pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) {
-            if (t >= mt) break;
-            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
-                float v[8];
-                load8v<BF>(p.x, (t0 + t) * K + k0, v);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pj = p.gamma ? v[j] * p.gamma[k0 + j] : v[j];
-                    pm[t] = fmaxf(pm[t], fabsf(pj));
-                    ps[t] += v[j] * v[j];
-                }
-            }
-            pm[t] = wave_max(pm[t]);
-            ps[t] = wave_sum(ps[t]);
-            if (lane == 0) { red_a[wave][t] = pm[t]; red_b[wave][t] = ps[t]; }
-        }
-        __syncthreads();
-        float sc[kGemvTokens];
-        int qsum[kGemvTokens];
-#pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) {
-            const float mx = fmaxf(fmaxf(red_a[0][t], red_a[1][t]), fmaxf(red_a[2][t], red_a[3][t]));
-            const float me = fmaxf(mx, 1e-5f);
-            sc[t] = 127.0f / me;
-            qsum[t] = 0;
-            if (tid == 0 && t < mt) {
-                const float ss = (red_b[0][t] + red_b[1][t]) + (red_b[2][t] + red_b[3][t]);
-                s_a[t] = me / 127.0f * (1.0f / sqrtf(ss / static_cast<float>(K) + p.eps));
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) {
-            if (t >= mt) break;
-            const int64_t tok = t0 + t;
-            const bool capt = cap_blk && p.cap.row0 <= tok && tok < p.cap.row1;
-            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
-                float v[8];
-                load8v<BF>(p.x, tok * K + k0, v);
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pj = p.gamma ? v[j] * p.gamma[k0 + j] : v[j];
-                    float r = rintf(pj * sc[t]);
-                    r = fminf(fmaxf(r, -127.0f), 127.0f);
-                    const int qi = static_cast<int>(r);
-                    qsum[t] += qi;
-                    const uint32_t byte = static_cast<uint32_t>(qi) & 0xFFu;
-                    if (j < 4) lo |= byte << (8 * j);
-                    else hi |= byte << (8 * (j - 4));
-                }
-                const int c = k0 >> 6;
-                *reinterpret_cast<uint2 *>(qs + t * rowb + chunk_off(c) + (k0 & 63)) = make_uint2(lo, hi);
-                if (capt) {
-                    const int64_t cr = tok - p.cap.row0;
-                    if (p.cap.x_in)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) p.cap.x_in[cr * K + k0 + j] = v[j];
-                    if (p.cap.q) *reinterpret_cast<uint2 *>(p.cap.q + cr * K + k0) = make_uint2(lo, hi);
-                }
-            }
-            qsum[t] = wave_sum_i(qsum[t]);
-        }
-        __syncthreads();  // red_a reuse below
-        if (lane == 0) {
-#pragma unroll
-            for (int t = 0; t < kGemvTokens; ++t) red_a[wave][t] = __int_as_float(qsum[t]);
-        }
-        __syncthreads();
-        if (tid < mt) {
-            s_rs[tid] = (__float_as_int(red_a[0][tid]) + __float_as_int(red_a[1][tid])) +
-                        (__float_as_int(red_a[2][tid]) + __float_as_int(red_a[3][tid]));
-            const int64_t tok = t0 + tid;
-            if (cap_blk && p.cap.a && p.cap.row0 <= tok && tok < p.cap.row1)
-                p.cap.a[tok - p.cap.row0] = s_a[tid];
-        }
-    } else {
-        for (int t = 0; t < mt; ++t)
-            for (int k0 = tid * 16; k0 < K; k0 += 4096) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(p.q + (t0 + t) * K + k0);
-                *reinterpret_cast<uint4 *>(qs + t * rowb + chunk_off(k0 >> 6) + (k0 & 63)) = v;
-            }
-        if (tid < mt) {
-            s_a[tid] = p.a[t0 + tid];
-            s_rs[tid] = p.rowsum[t0 + tid];
-        }
-    }
-    __syncthreads();
-
-    // ---------------------------------------------------------------- main loop
-    const int slot = lane >> 3, j = lane & 7;
-    const int r = blockIdx.x * 32 + wave * 8 + slot;
+    // ---------------------------------------------------------------- weight rows
+    const int slot = lane / LPR, j = lane % LPR;
+    const int r = blockIdx.x * RPB + wave * RPW + slot;
     const bool rvalid = r < p.rows_total;
     int sg = 0, n = r;
     if constexpr (EPI != EPI_GLU) {
@@ -179,52 +103,205 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
     const int nn = rvalid ? n : 0;
     const uint32_t *w0 = p.seg[sg].packed + static_cast<int64_t>(nn) * (K / 16);
     const uint32_t *w1 = EPI == EPI_GLU ? p.seg[1].packed + static_cast<int64_t>(nn) * (K / 16) : nullptr;
-
-    int acc0[kGemvTokens], acc1[kGemvTokens];
+    uint4 wa[CB], wb[CB];
+    auto load_pass = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t) { acc0[t] = 0; acc1[t] = 0; }
-
-    for (int c = j; c < NC; c += 8) {
-        const uint4 wa = *reinterpret_cast<const uint4 *>(w0 + c * 4);
-        v4i ca[4] = {unpack_codes(wa.x), unpack_codes(wa.y), unpack_codes(wa.z), unpack_codes(wa.w)};
-        v4i cb[4];
-        if constexpr (EPI == EPI_GLU) {
-            const uint4 wb = *reinterpret_cast<const uint4 *>(w1 + c * 4);
-            cb[0] = unpack_codes(wb.x); cb[1] = unpack_codes(wb.y);
-            cb[2] = unpack_codes(wb.z); cb[3] = unpack_codes(wb.w);
+        for (int i = 0; i < CB; ++i) {
+            const int c = base + j + LPR * i;
+            if (c < NC && rvalid) {
+                wa[i] = *reinterpret_cast<const uint4 *>(w0 + c * 4);
+                if constexpr (EPI == EPI_GLU) wb[i] = *reinterpret_cast<const uint4 *>(w1 + c * 4);
+            }
         }
+    };
+    load_pass(0);  // the first pass of weights is in flight during the prologue
+    // residual of this lane's output (lane j of a row writes token j / (16 / TG)), requested
+    // now so that its latency overlaps the rest of the kernel
+    constexpr int STRIDE = LPR / TG;
+    const int tj = j / STRIDE;
+    float resid_v = 0.f;
+    if constexpr (EPI == EPI_RESID) {
+        if (rvalid && j % STRIDE == 0 && tj < mt)
+            resid_v = load_act<OUT_BF16>(p.resid, (t0 + tj) * p.ldr + p.seg[sg].out_col0 + n);
+    }
+
+    // ---------------------------------------------------------------- prologue
+    if constexpr (XIN != 0) {
+        // two straight-line passes over all TG token slots (slots past the group end read
+        // the group's last row and are never stored), so the loads of every token are in
+        // flight together
+        constexpr bool BF = XIN == 2;
+        float pm[TG], ps[TG];
+        // one token: its row (<= 3 x 8 values per thread for K <= 6144) stays in registers
+        // between the two passes
+        constexpr int KEEP = TG == 1 ? 3 : 0;
+        float xk[KEEP > 0 ? KEEP : 1][8];
+        const bool keep = KEEP > 0 && K <= 2048 * KEEP;
 #pragma unroll
-        for (int t = 0; t < kGemvTokens; ++t) {
-            if (t >= mt) break;
-            const v4i *qp = reinterpret_cast<const v4i *>(qs + t * rowb + chunk_off(c));
-            const v4i qv[4] = {qp[0], qp[1], qp[2], qp[3]};
-            acc0[t] = dot16(qv, ca, acc0[t]);
-            if constexpr (EPI == EPI_GLU) acc1[t] = dot16(qv, cb, acc1[t]);
+        for (int t = 0; t < TG; ++t) {
+            const int64_t tok = t0 + (t < mt ? t : mt - 1);
+            pm[t] = 0.f;
+            ps[t] = 0.f;
+            if (keep) {
+#pragma unroll
+                for (int it = 0; it < KEEP; ++it) {
+                    const int k0 = tid * 8 + 2048 * it;
+                    if (k0 < K) {
+                        load8v<BF>(p.x, tok * K + k0, xk[it]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float pj = p.gamma ? xk[it][e] * p.gamma[k0 + e] : xk[it][e];
+                            pm[t] = fmaxf(pm[t], fabsf(pj));
+                            ps[t] += xk[it][e] * xk[it][e];
+                        }
+                    }
+                }
+                continue;
+            }
+            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
+                float v[8];
+                load8v<BF>(p.x, tok * K + k0, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pj = p.gamma ? v[e] * p.gamma[k0 + e] : v[e];
+                    pm[t] = fmaxf(pm[t], fabsf(pj));
+                    ps[t] += v[e] * v[e];
+                }
+            }
+        }
+        {
+            constexpr int SH = 6 - (TG == 1 ? 0 : TG == 4 ? 2 : TG == 8 ? 3 : 4);
+            const float rm = wave_reduce_multi<TG, true>(pm);
+            const float rs = wave_reduce_multi<TG, false>(ps);
+            if ((lane & ((1 << SH) - 1)) == 0) {
+                red_m[wave][lane >> SH] = rm;
+                red_s[wave][lane >> SH] = rs;
+            }
+        }
+        __syncthreads();
+        float sc[TG];
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+            const float mx = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+            sc[t] = 127.0f / fmaxf(mx, 1e-5f);
+        }
+        const bool cap_any = cap_blk && (p.cap.x_in || p.cap.q) && p.cap.row0 < t0 + mt && t0 < p.cap.row1;
+        auto quant8 = [&](int t, int k0, const float (&v)[8]) __attribute__((always_inline)) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pj = p.gamma ? v[e] * p.gamma[k0 + e] : v[e];
+                float rq = rintf(pj * sc[t]);
+                rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+                const uint32_t byte = static_cast<uint32_t>(static_cast<int>(rq)) & 0xFFu;
+                if (e < 4) lo |= byte << (8 * e);
+                else hi |= byte << (8 * (e - 4));
+            }
+            *reinterpret_cast<uint2 *>(qs + (k0 >> 6) * CS + 64 * t + (k0 & 63)) = make_uint2(lo, hi);
+            const int64_t tok = t0 + t;
+            if (cap_any && t < mt && p.cap.row0 <= tok && tok < p.cap.row1) {  // test protocol
+                const int64_t cr = tok - p.cap.row0;
+                if (p.cap.x_in)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p.cap.x_in[cr * K + k0 + e] = v[e];
+                if (p.cap.q) *reinterpret_cast<uint2 *>(p.cap.q + cr * K + k0) = make_uint2(lo, hi);
+            }
+        };
+        if (keep) {
+#pragma unroll
+            for (int it = 0; it < KEEP; ++it) {
+                const int k0 = tid * 8 + 2048 * it;
+                if (k0 < K) quant8(0, k0, xk[it]);
+            }
+        } else {
+            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
+                float v[TG][8];
+#pragma unroll
+                for (int t = 0; t < TG; ++t) load8v<BF>(p.x, (t0 + (t < mt ? t : mt - 1)) * K + k0, v[t]);
+#pragma unroll
+                for (int t = 0; t < TG; ++t) quant8(t, k0, v[t]);
+            }
+        }
+        if (tid < mt) {
+            const int t = tid;
+            const float mx = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+            const float me = fmaxf(mx, 1e-5f);
+            const float ss = (red_s[0][t] + red_s[1][t]) + (red_s[2][t] + red_s[3][t]);
+            s_a[t] = me / 127.0f * (1.0f / sqrtf(ss / static_cast<float>(K) + p.eps));
+            const int64_t tok = t0 + t;
+            if (cap_blk && p.cap.a && p.cap.row0 <= tok && tok < p.cap.row1) p.cap.a[tok - p.cap.row0] = s_a[t];
+        }
+    } else {
+        for (int k0 = tid * 16; k0 < K; k0 += 4096) {
+            uint4 v[TG];  // every token's 16 bytes requested before any is stored
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+                v[t] = *reinterpret_cast<const uint4 *>(p.q + (t0 + (t < mt ? t : mt - 1)) * K + k0);
+#pragma unroll
+            for (int t = 0; t < TG; ++t) *reinterpret_cast<uint4 *>(qs + (k0 >> 6) * CS + 64 * t + (k0 & 63)) = v[t];
+        }
+        if (tid < mt) s_a[tid] = p.a[t0 + tid];
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- dot products
+    int acc0[TG], acc1[TG];
+#pragma unroll
+    for (int t = 0; t < TG; ++t) { acc0[t] = 0; acc1[t] = 0; }
+    for (int base = 0; base < NC; base += LPR * CB) {
+        if (base > 0) load_pass(base);
+        const int niter = (NC - base + LPR - 1) / LPR;  // chunk slots in use (uniform)
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            if (i >= niter) break;
+            // chunks past the row end (last slot of a ragged row) read as all-zero weights
+            // (code 1) against chunk 0
+            const int c = base + j + LPR * i;
+            const bool cv = c < NC && rvalid;
+            const uint32_t z = 0x55555555u;
+            const v4i ca[4] = {signed_codes(cv ? wa[i].x : z), signed_codes(cv ? wa[i].y : z),
+                               signed_codes(cv ? wa[i].z : z), signed_codes(cv ? wa[i].w : z)};
+            v4i cb[4];
+            if constexpr (EPI == EPI_GLU) {
+                cb[0] = signed_codes(cv ? wb[i].x : z); cb[1] = signed_codes(cv ? wb[i].y : z);
+                cb[2] = signed_codes(cv ? wb[i].z : z); cb[3] = signed_codes(cv ? wb[i].w : z);
+            }
+            const int8_t *qc = qs + (cv ? c : 0) * CS;
+            // every token slot is multiplied (slots past the group end hold stale values and
+            // their sums are never stored), so the loop has no token-dependent branches; the
+            // activations of up to 4 tokens are read before their dot products
+            constexpr int TB = TG < 4 ? TG : 4;
+#pragma unroll
+            for (int t0b = 0; t0b < TG; t0b += TB) {
+                v4i qv[TB][4];
+#pragma unroll
+                for (int u = 0; u < TB; ++u) {
+                    const v4i *qp = reinterpret_cast<const v4i *>(qc + 64 * (t0b + u));
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) qv[u][q4] = qp[q4];
+                }
+#pragma unroll
+                for (int u = 0; u < TB; ++u) {
+                    acc0[t0b + u] = dot16(qv[u], ca, acc0[t0b + u]);
+                    if constexpr (EPI == EPI_GLU) acc1[t0b + u] = dot16(qv[u], cb, acc1[t0b + u]);
+                }
+            }
         }
     }
-#pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t) {
-#pragma unroll
-        for (int o = 4; o > 0; o >>= 1) {
-            acc0[t] += __shfl_xor(acc0[t], o, 64);
-            if constexpr (EPI == EPI_GLU) acc1[t] += __shfl_xor(acc1[t], o, 64);
-        }
-    }
-    // lane j of the row writes token j
-    int my0 = 0, my1 = 0;
-#pragma unroll
-    for (int t = 0; t < kGemvTokens; ++t)
-        if (t == j) { my0 = acc0[t]; my1 = acc1[t]; }
-    if (!rvalid || j >= mt) return;
-    const int64_t tok = t0 + j;
-    const int32_t rs = s_rs[j];
-    const float at = s_a[j];
+    // the 16 partial sums of the row, for every token at once: lane j of the row ends with
+    // token j / (16 / TG)
+    const int my0 = wave_reduce_multi<TG, false, int, LPR>(acc0);
+    int my1 = 0;
+    if constexpr (EPI == EPI_GLU) my1 = wave_reduce_multi<TG, false, int, LPR>(acc1);
+    if (!rvalid || j % STRIDE != 0) return;
+    if (tj >= mt) return;
+    const int64_t tok = t0 + tj;
+    const float at = s_a[tj];
     const bool capr = p.cap.row0 <= tok && tok < p.cap.row1;
     const int64_t crow = tok - p.cap.row0;
     if constexpr (EPI == EPI_GLU) {
-        const int32_t ag = my0 - rs, au = my1 - rs;
-        float yg = static_cast<float>(ag) * (p.seg[0].scale * at);
-        float yu = static_cast<float>(au) * (p.seg[1].scale * at);
+        float yg = static_cast<float>(my0) * (p.seg[0].scale * at);
+        float yu = static_cast<float>(my1) * (p.seg[1].scale * at);
         if (p.seg[0].bias) yg += p.seg[0].bias[n];
         if (p.seg[1].bias) yu += p.seg[1].bias[n];
         const float mv = siluf_(yg) * yu;
@@ -232,29 +309,38 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
         if (capr) {
             if (p.cap.acc) {
                 int32_t *cp = p.cap.acc + crow * p.cap.acc_ld;
-                cp[p.seg[0].cap_col0 + n] = ag;
-                cp[p.seg[1].cap_col0 + n] = au;
+                cp[p.seg[0].cap_col0 + n] = my0;
+                cp[p.seg[1].cap_col0 + n] = my1;
             }
             if (p.cap.y_out) p.cap.y_out[crow * p.ldo + n] = OUT_BF16 ? round_to_bf16(mv) : mv;
         }
     } else {
         const Seg &S = p.seg[sg];
-        const int32_t av = my0 - rs;
-        float y = static_cast<float>(av) * (S.scale * at);
+        float y = static_cast<float>(my0) * (S.scale * at);
         if (S.bias) y += S.bias[n];
-        if constexpr (EPI == EPI_RESID) y = load_act<OUT_BF16>(p.resid, tok * p.ldr + S.out_col0 + n) + y;
+        if constexpr (EPI == EPI_RESID) y = resid_v + y;
         store_act<OUT_BF16>(p.out, tok * p.ldo + S.out_col0 + n, y);
         if (capr) {
-            if (p.cap.acc) p.cap.acc[crow * p.cap.acc_ld + S.cap_col0 + n] = av;
+            if (p.cap.acc) p.cap.acc[crow * p.cap.acc_ld + S.cap_col0 + n] = my0;
             if (p.cap.y_out) p.cap.y_out[crow * p.ldo + S.out_col0 + n] = OUT_BF16 ? round_to_bf16(y) : y;
         }
     }
 }
 
+template <int EPI, int XIN, int TG>
+void launch4(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true, TG>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false, TG>), grid, dim3(256), lds, s, a);
+}
+
 template <int EPI, int XIN>
 void launch3(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false>), grid, dim3(256), lds, s, a);
+    switch (a.tokens_per_group) {
+        case 1: launch4<EPI, XIN, 1>(a, grid, lds, s); break;
+        case 4: launch4<EPI, XIN, 4>(a, grid, lds, s); break;
+        case 8: launch4<EPI, XIN, 8>(a, grid, lds, s); break;
+        default: launch4<EPI, XIN, 16>(a, grid, lds, s); break;
+    }
 }
 
 template <int EPI>
@@ -266,23 +352,19 @@ void launch2(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
 
 }  // namespace
 
-// Bytes of LDS per token row for a given K.
-size_t gemv_lds_row_bytes(int K) {
-    const int nc = K / 64;
-    return static_cast<size_t>(nc * 64 + (nc >> 1) * 16 + 16);
-}
+// Bytes of LDS for tg token rows of length K.
+size_t gemv_lds_bytes(int K, int tg) { return static_cast<size_t>(K / 64) * chunk_stride(tg); }
 
 hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
     if (a_in.M <= 0) return hipSuccess;
     GemvArgs a = a_in;
-    const size_t rowb = gemv_lds_row_bytes(a.K);
-    int tg = static_cast<int>((64 * 1024) / rowb);
-    if (tg > kGemvTokens) tg = kGemvTokens;
-    if (tg < 1) tg = 1;
+    // token rows per workgroup: as many as the batch needs, up to 16, within 64 KB of LDS
+    int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
+    while (tg > 1 && gemv_lds_bytes(a.K, tg) > 64 * 1024) tg = tg == 16 ? 8 : tg == 8 ? 4 : 1;
     a.tokens_per_group = tg;
-    const dim3 grid(static_cast<unsigned>((a.rows_total + 31) / 32),
+    const dim3 grid(static_cast<unsigned>((a.rows_total + RPB - 1) / RPB),
                     static_cast<unsigned>((a.M + tg - 1) / tg));
-    const size_t lds = rowb * tg;
+    const size_t lds = gemv_lds_bytes(a.K, tg);
     timing_begin(FAM_GEMV, s);
     switch (a.epi) {
         case EPI_STORE: launch2<EPI_STORE>(a, grid, lds, s); break;

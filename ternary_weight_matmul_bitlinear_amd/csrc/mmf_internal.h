@@ -75,6 +75,46 @@ __device__ __forceinline__ int wave_sum_i(int v) {
     return v;
 }
 
+// Sum (or max) of N values per lane over groups of G lanes (G in {16, 32, 64}), N a power
+// of two <= G: halving exchanges (each lane keeps the half of the vector picked by its lane
+// bit) while more than one value is left, then a plain butterfly.  On return lane l holds
+// the group total of value index (l % G) >> (log2 G - log2 N).
+template <int N, bool MAX, typename T, int G = 64>
+__device__ __forceinline__ T wave_reduce_multi(T (&v)[N]) {
+    static_assert((N & (N - 1)) == 0 && N <= G, "N must be a power of two <= G");
+    const int lane = threadIdx.x & 63;
+    T w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = v[i];
+    int n = N;
+#pragma unroll
+    for (int bit = G / 2; bit > 0; bit >>= 1) {
+        if (n > 1) {
+            // keep/send picked with an xor blend (a select of w[i] vs w[i + h] on the lane bit
+            // is otherwise turned into a dynamically indexed register read)
+            const uint32_t m = (lane & bit) ? 0xFFFFFFFFu : 0u;
+            const int h = n / 2;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                if (i < h) {
+                    const uint32_t lo_b = __builtin_bit_cast(uint32_t, w[i]);
+                    const uint32_t hi_b = __builtin_bit_cast(uint32_t, w[i + h]);
+                    const uint32_t x = (lo_b ^ hi_b) & m;
+                    const T send = __builtin_bit_cast(T, hi_b ^ x);   // lane bit set: w[i]
+                    const T keep = __builtin_bit_cast(T, lo_b ^ x);   // lane bit set: w[i + h]
+                    const T recv = __shfl_xor(send, bit, 64);
+                    w[i] = MAX ? (keep > recv ? keep : recv) : keep + recv;
+                }
+            }
+            n = h;
+        } else {
+            const T o = __shfl_xor(w[0], bit, 64);
+            w[0] = MAX ? (w[0] > o ? w[0] : o) : w[0] + o;
+        }
+    }
+    return w[0];
+}
+
 // Ternary unpack: word j of a packed row holds k = 16j + 4a + b at bits 8b + 2a; the
 // dword (w >> 2a) & 0x03030303 therefore holds the codes of k = 16j + 4a + 0..3 as four
 // int8 lanes.  The returned 128-bit vector holds the 16 codes of word j in k order.

@@ -125,42 +125,6 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs p) {
     }
 }
 
-// Sum (or max) of N values per lane over the 64 lanes of a wave, N in {4, 8}: halving
-// exchanges (each lane keeps the half of the vector picked by its lane bit) followed by a
-// plain butterfly.  On return lane l holds the wave total of value index l >> (6 - log2 N).
-template <int N, bool MAX, typename T>
-__device__ __forceinline__ T wave_reduce_multi(T (&v)[N]) {
-    const int lane = threadIdx.x & 63;
-    T w[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) w[i] = v[i];
-    int n = N, bit = 32;
-#pragma unroll
-    for (int step = 0; step < 3; ++step) {
-        if (n > 1) {
-            const bool hi = lane & bit;
-            const int h = n / 2;
-#pragma unroll
-            for (int i = 0; i < N / 2; ++i) {
-                if (i < h) {
-                    const T send = hi ? w[i] : w[i + h];
-                    const T keep = hi ? w[i + h] : w[i];
-                    const T recv = __shfl_xor(send, bit, 64);
-                    w[i] = MAX ? (keep > recv ? keep : recv) : keep + recv;
-                }
-            }
-            n = h;
-            bit >>= 1;
-        }
-    }
-    T r = w[0];
-    for (; bit > 0; bit >>= 1) {
-        const T o = __shfl_xor(r, bit, 64);
-        r = MAX ? (r > o ? r : o) : r + o;
-    }
-    return r;
-}
-
 // Workgroup-wide version: per-wave totals through LDS (red[4][N]); returns all N totals.
 template <int N, bool MAX, typename T>
 __device__ __forceinline__ void block_reduce_multi(T (&v)[N], T (*red)[N], T (&out)[N]) {

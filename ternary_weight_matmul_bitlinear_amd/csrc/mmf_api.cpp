@@ -95,8 +95,10 @@ void timing_begin(int family, hipStream_t s) {
     TimingFamily &f = g_fam[family];
     if (f.used + 2 > f.ev.size()) {
         for (int i = 0; i < 64; ++i) {
+            // timing-only events: no system-scope fence (cache writeback and invalidate) when
+            // they are recorded, so they perturb the timed stream as little as possible
             hipEvent_t e;
-            if (hipEventCreate(&e) != hipSuccess) return;
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
             f.ev.push_back(e);
         }
     }

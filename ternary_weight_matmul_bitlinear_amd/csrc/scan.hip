@@ -10,14 +10,19 @@
 //   o_t = RMSNorm_D(h_t)*gnorm_w * g*sigmoid(g)   (or sigmoid(g)*h_t).
 //
 // The recurrence is elementwise in d, so it is parallel over B*D channels; to fill 256
-// CUs at long T it is also chunked over time.  All phases are HBM-bound:
-//   phase 1 (per chunk, channel quad): local scan from 0 -> end state hloc and prod(f);
-//   phase 2 (per channel): carry across chunks, h_in[c+1] = prod_c*h_in[c] + hloc_c;
-//   phase 3 (workgroup per chunk, thread per channel quad): rerun the recurrence from h_in
-//     in registers for a tile of tokens, then the per-token RMSNorm over D, the gate and
-//     either a store of o or its int8 quantization for o_proj (q, a, row sum); the
-//     reductions over D of a whole tile share one LDS exchange each.
-// With one chunk (decode, short T) phases 1 and 2 are skipped.
+// CUs at long T it is also chunked over time (16-token chunks):
+//   phase 1 (thread per chunk and 8 channels): local scan from 0 -> end state hloc and
+//     prod(f);
+//   phase 2 (per channel block, 8 runs of chunks composed through LDS): carry across
+//     chunks, h_in[c+1] = prod_c*h_in[c] + hloc_c;
+//   phase 3 (workgroup per chunk, W = D/512 waves per token row, 8 channels per lane):
+//     rerun the recurrence from h_in in registers tile by tile, then the per-token RMSNorm
+//     over D, the gate and either a store of o or its int8 quantization for o_proj (q, a,
+//     row sum); the reductions over D of a tile share one LDS exchange each.
+// Phases 1 and 3 read the pre-activations once each and evaluate three sigmoids per
+// element; at the 370M shape they are bound by vector ALU issue, not by HBM.  With one
+// chunk (decode, short T) phases 1 and 2 are skipped.  Shapes outside the row layout
+// (D not a multiple of 64, other chunk lengths) use the channel-quad kernels.
 #include "mmf_internal.h"
 
 namespace mmf {
@@ -622,6 +627,150 @@ __global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
     if (c == p.n_chunks - 1 && p.h_out) store_f32<CPL>(p.h_out + b * D + d0, h);
 }
 
+// Output pass over whole 16-token chunks of bf16 pre-activations, quantizing for o_proj (the
+// prefill block path).  Same arithmetic as scan_row_kernel with 4-token tiles, but the four
+// tiles of the chunk are unrolled and every global access is unconditional, so each wait
+// on a tile's loads counts exactly the accesses issued after them: the next tile's loads
+// stay in flight across this tile's stores instead of a wait that drains both.  The
+// per-token scale and code sum are stored by every lane (lane l writes token l % 4; equal
+// values to the same address).  CAP adds the stage-capture stores (tests only).
+template <int W, bool CAP>
+__global__ __launch_bounds__(64 * W) void scan_row16_kernel(ScanArgs p) {
+    constexpr int CPL = 8, TS = 4, NTILE = kScanChunk / TS;
+    __shared__ float red_ss[2][W][TS], red_mx[2][W][TS], red_s2[2][W][TS];
+    __shared__ int red_q[2][W][TS];
+    const int c = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int D = p.D;
+    const int d0 = tid * CPL;
+    const int64_t t_beg = static_cast<int64_t>(c) * kScanChunk;
+    const float inv_d = 1.0f / static_cast<float>(D);
+    const int64_t D3 = 3 * static_cast<int64_t>(D);
+
+    // per-channel parameters first: the waits for them then never cover tile loads
+    float h[CPL], fb[CPL], gw[CPL], qg[CPL];
+    if (p.n_chunks > 1) load_f32<CPL>(p.hin + (b * p.n_chunks + c) * D + d0, h, 0.0f);
+    else load_f32<CPL>(p.h0 ? p.h0 + b * D + d0 : nullptr, h, 0.0f);
+    load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    load_f32<CPL>(p.gnorm_w ? p.gnorm_w + d0 : nullptr, gw, 1.0f);
+    load_f32<CPL>(p.q_gamma ? p.q_gamma + d0 : nullptr, qg, 1.0f);
+
+    using Raw = RawVec<true, CPL>;
+    Raw ip[TS], fp[TS], gp[TS];
+    auto fetch = [&](int64_t tt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            const int64_t base = (b * p.T + tt + t) * D3 + d0;
+            load_vec<true, CPL>(p.ifg, base, ip[t]);
+            load_vec<true, CPL>(p.ifg, base + D, fp[t]);
+            load_vec<true, CPL>(p.ifg, base + 2 * D, gp[t]);
+        }
+    };
+    fetch(t_beg);
+
+#pragma unroll
+    for (int k = 0; k < NTILE; ++k) {
+        const int64_t tt = t_beg + k * TS;
+        const int par = k & 1;
+        float o[TS][CPL], ss[TS];
+        Raw gs[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            float iv[CPL], fv[CPL];
+            cvt_vec<true, CPL>(ip[t], iv);
+            cvt_vec<true, CPL>(fp[t], fv);
+            gs[t] = gp[t];
+            ss[t] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < CPL; ++kk) {
+                float f;
+                h[kk] = gate_step(h[kk], iv[kk], fv[kk], fb[kk], &f);
+                ss[t] = fmaf(h[kk], h[kk], ss[t]);
+                o[t][kk] = h[kk];
+            }
+        }
+        if (k + 1 < NTILE) fetch(tt + TS);  // next tile in flight during this tile's tail
+
+        if (p.gate_mode == 0) {
+            float tot[TS];
+            row_reduce<TS, W, false>(ss, red_ss[par], tot);
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                const float r = 1.0f / sqrtf(tot[t] * inv_d + p.eps);
+                float gv[CPL];
+                cvt_vec<true, CPL>(gs[t], gv);
+#pragma unroll
+                for (int kk = 0; kk < CPL; ++kk) o[t][kk] = o[t][kk] * r * gw[kk] * siluf_(gv[kk]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < TS; ++t) {
+                float gv[CPL];
+                cvt_vec<true, CPL>(gs[t], gv);
+#pragma unroll
+                for (int kk = 0; kk < CPL; ++kk) o[t][kk] = sigmoidf_(gv[kk]) * o[t][kk];
+            }
+        }
+
+        float mx[TS], s2[TS], mxt[TS], s2t[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            mx[t] = 0.f;
+            s2[t] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < CPL; ++kk) {
+                mx[t] = fmaxf(mx[t], fabsf(o[t][kk] * qg[kk]));
+                s2[t] = fmaf(o[t][kk], o[t][kk], s2[t]);
+            }
+        }
+        row_reduce<TS, W, true>(mx, red_mx[par], mxt);
+        row_reduce<TS, W, false>(s2, red_s2[par], s2t);
+        int qs[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            const float me = fmaxf(mxt[t], 1e-5f);
+            const float sc = 127.0f / me;
+            const int64_t row = b * p.T + tt + t;
+            uint32_t pk[2] = {0u, 0u};
+            qs[t] = 0;
+#pragma unroll
+            for (int kk = 0; kk < CPL; ++kk) {
+                float rq = rintf((o[t][kk] * qg[kk]) * sc);
+                rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+                const int qi = static_cast<int>(rq);
+                qs[t] += qi;
+                pk[kk >> 2] |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * (kk & 3));
+            }
+            *reinterpret_cast<uint2 *>(p.q + row * D + d0) = make_uint2(pk[0], pk[1]);
+            if constexpr (CAP) {
+                if (p.cap.row0 <= row && row < p.cap.row1) {
+                    const int64_t cr = row - p.cap.row0;
+                    if (p.cap.x_in) store_f32<CPL>(p.cap.x_in + cr * D + d0, o[t]);
+                    if (p.cap.q) *reinterpret_cast<uint2 *>(p.cap.q + cr * D + d0) = make_uint2(pk[0], pk[1]);
+                }
+            }
+        }
+        int qtot[TS];
+        row_reduce<TS, W, false>(qs, red_q[par], qtot);
+        const int tl = tid & (TS - 1);
+        int qv = qtot[0];
+        float me = mxt[0], s2v = s2t[0];
+#pragma unroll
+        for (int t = 1; t < TS; ++t)
+            if (t == tl) { qv = qtot[t]; me = mxt[t]; s2v = s2t[t]; }
+        me = fmaxf(me, 1e-5f);
+        const int64_t row = b * p.T + tt + tl;
+        const float a = me / 127.0f * (1.0f / sqrtf(s2v * inv_d + p.q_eps));
+        p.a[row] = a;
+        p.rowsum[row] = qv;
+        if constexpr (CAP) {
+            if (p.cap.a && p.cap.row0 <= row && row < p.cap.row1) p.cap.a[row - p.cap.row0] = a;
+        }
+    }
+    if (c == p.n_chunks - 1 && p.h_out) store_f32<CPL>(p.h_out + b * D + d0, h);
+}
+
 // Phase 1, row layout: thread per (b, chunk, group of CPL channels); the chunk's CH tokens
 // of i and f are all loaded before the local scan runs (one 16-byte load per token and
 // pre-activation), so the whole chunk is in flight at once.
@@ -638,18 +787,19 @@ __global__ __launch_bounds__(256) void scan_local_row_kernel(ScanArgs p) {
     const int64_t t_beg = static_cast<int64_t>(c) * CH;
     const int nt = static_cast<int>(p.T - t_beg < CH ? p.T - t_beg : CH);
     const int64_t D3 = 3 * static_cast<int64_t>(D);
+    float fb[CPL], h[CPL], pf[CPL];
+    load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    // every load is issued (a ragged last chunk re-reads its last token), so the wait before
+    // token t covers only the loads of tokens up to t
     using Raw = RawVec<BF16, CPL>;
     Raw iv[CH], fv[CH];
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-        if (t < nt) {
-            const int64_t base = (b * p.T + t_beg + t) * D3 + d0;
-            load_vec<BF16, CPL>(p.ifg, base, iv[t]);
-            load_vec<BF16, CPL>(p.ifg, base + D, fv[t]);
-        }
+        const int tc = t < nt ? t : nt - 1;
+        const int64_t base = (b * p.T + t_beg + tc) * D3 + d0;
+        load_vec<BF16, CPL>(p.ifg, base, iv[t]);
+        load_vec<BF16, CPL>(p.ifg, base + D, fv[t]);
     }
-    float fb[CPL], h[CPL], pf[CPL];
-    load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
 #pragma unroll
     for (int k = 0; k < CPL; ++k) { h[k] = 0.f; pf[k] = 1.f; }
 #pragma unroll
@@ -747,9 +897,10 @@ void launch_out_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
     launch_out_ts<IN_BF16, QUANT, OUT_BF16, 4>(a, grid, s);
 }
 
-// Row-layout output pass: W waves per token row, CPL channels per lane.
-// Tiles of 2 tokens at 8 channels per lane (4 at 4): larger tiles amortize the reductions
-// further but their registers halve the waves per SIMD (measured slower).
+// Row-layout output pass: W waves per token row, CPL channels per lane (ragged chunks,
+// fp32 pre-activations, unquantized output).  Tiles of 2 tokens at 8 channels per lane (4 at
+// 4): larger tiles amortize the reductions further but their registers halve the waves per
+// SIMD where more than two waves per SIMD are resident.
 template <bool IN_BF16, int QUANT, bool OUT_BF16, int CPL, int W>
 void launch_row(const ScanArgs &a, dim3 grid, hipStream_t s) {
     constexpr int TS = CPL >= 8 ? 2 : 4;
@@ -784,9 +935,31 @@ bool launch_row_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
     return false;
 }
 
+template <bool CAP>
+bool launch_row16(const ScanArgs &a, dim3 grid, hipStream_t s) {
+    switch (a.D / 512) {
+        case 1: hipLaunchKernelGGL((scan_row16_kernel<1, CAP>), grid, dim3(64), 0, s, a); return true;
+        case 2: hipLaunchKernelGGL((scan_row16_kernel<2, CAP>), grid, dim3(128), 0, s, a); return true;
+        case 3: hipLaunchKernelGGL((scan_row16_kernel<3, CAP>), grid, dim3(192), 0, s, a); return true;
+        case 4: hipLaunchKernelGGL((scan_row16_kernel<4, CAP>), grid, dim3(256), 0, s, a); return true;
+        case 5: hipLaunchKernelGGL((scan_row16_kernel<5, CAP>), grid, dim3(320), 0, s, a); return true;
+        case 6: hipLaunchKernelGGL((scan_row16_kernel<6, CAP>), grid, dim3(384), 0, s, a); return true;
+        case 7: hipLaunchKernelGGL((scan_row16_kernel<7, CAP>), grid, dim3(448), 0, s, a); return true;
+        case 8: hipLaunchKernelGGL((scan_row16_kernel<8, CAP>), grid, dim3(512), 0, s, a); return true;
+        default: return false;
+    }
+}
+
+// whole 16-token chunks of bf16 pre-activations quantized for o_proj
+bool launch_row16_q(const ScanArgs &a, dim3 grid, hipStream_t s) {
+    if (!a.ifg_bf16 || a.chunk != kScanChunk || a.T % kScanChunk != 0 || a.D % 512 != 0) return false;
+    return a.cap.row1 > a.cap.row0 ? launch_row16<true>(a, grid, s) : launch_row16<false>(a, grid, s);
+}
+
 template <bool IN_BF16>
 void launch_out(const ScanArgs &a, dim3 grid, hipStream_t s) {
     if (a.q) {
+        if (IN_BF16 && launch_row16_q(a, grid, s)) return;
         if (!launch_row_q<IN_BF16, 1, false>(a, grid, s)) launch_out_q<IN_BF16, 1, false>(a, grid, s);
     } else if (a.out_bf16) {
         if (!launch_row_q<IN_BF16, 0, true>(a, grid, s)) launch_out_q<IN_BF16, 0, true>(a, grid, s);

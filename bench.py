@@ -71,8 +71,9 @@ def main() -> int:
                     help="tokens per sequence of the causal prefix timed on the CPU")
     ap.add_argument("--batch", type=int, default=None,
                     help="decode stack: sequences per step (default: the workload's B)")
-    ap.add_argument("--regime", choices=("auto", "decode", "prefill"), default="auto",
-                    help="BitLinear kernel choice (auto: by token count)")
+    ap.add_argument("--regime", choices=("auto", "decode", "prefill", "tiles"), default="auto",
+                    help="BitLinear kernel choice (auto: by token count; decode: weight "
+                         "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -90,7 +91,7 @@ def main() -> int:
 
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    api.set_regime({"auto": 0, "decode": 1, "prefill": 2}[args.regime])
+    api.set_regime({"auto": 0, "decode": 1, "prefill": 2, "tiles": 3}[args.regime])
     if w.layers != 1 or w.vocab:
         return bench_stack(args, w)
     dt = torch.bfloat16 if w.bf16 else torch.float32
@@ -244,9 +245,12 @@ def bench_stack(args, w) -> int:
         step(i)
     torch.cuda.synchronize()
     # per-launch durations of the dominant kernel family: an eager pass with events
-    fam = "gemv" if decode else "gemm_gateup"
+    # decode: every BitLinear launch of the step (the dot4 kernel for a few rows, the k-split
+    # MFMA kernel for more, both under their own family names)
+    fams = (["gemv", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemm"] if decode
+            else ["gemm_gateup"])
     api.timing_reset()
-    api.timing_families([fam])
+    api.timing_families(fams)
     api.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
@@ -254,7 +258,10 @@ def bench_stack(args, w) -> int:
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     api.timing_enable(False)
-    n, ms = api.timing_query(fam)
+    n, ms = 0, 0.0
+    for f in fams:
+        nf, msf = api.timing_query(f)
+        n, ms = n + nf, ms + msf
     graph_ms = None
     if decode:
         # the timed loop replays one captured step (a HIP graph): a decode step is ~120 small
@@ -286,12 +293,16 @@ def bench_stack(args, w) -> int:
         # the fp32 state read and written per layer)
         def bl(N, K, in_b, out_b, resid=0):
             return N * K // 4 + B * K * in_b + B * N * out_b + B * N * resid
-        per_layer = (bl(3 * D, D, 2, 2) + bl(D, D, 1, 2, 2) + bl(2 * F, D, 2, 0) + B * F * 2
-                     + bl(D, F, 2, 2, 2))
-        gemv_bytes = L * per_layer + bl(w.vocab, D, 2, 4)
+        # the dot4 kernel (up to 4 rows) quantizes bf16 rows itself; the k-split kernel reads
+        # int8 rows written by the row quantizer
+        xin = 2 if B <= 4 else 1
+        per_layer = (bl(3 * D, D, xin, 2) + bl(D, D, 1, 2, 2) + bl(2 * F, D, xin, 0) + B * F * 2
+                     + bl(D, F, xin, 2, 2))
+        gemv_bytes = L * per_layer + bl(w.vocab, D, xin, 4)
         step_bytes = gemv_bytes + B * D // 4 + B * D * 2 + L * B * D * 4 * 2
         achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
-        roofline = {"kernel": "decode BitLinear (weight-streaming dot4 GEMV), all launches of a step",
+        roofline = {"kernel": "decode BitLinear (dot4 weight streaming up to 4 rows, k-split "
+                              "MFMA above), all launches of a step",
                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": None,
                     "algorithmic_bytes_per_step": gemv_bytes}

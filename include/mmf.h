@@ -127,8 +127,10 @@ int mmf_abi_version(void);
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char *mmf_last_error(void);
 
-/* Test knob, process-wide: 0 = choose the BitLinear regime by token count (default),
- * 1 = force the decode (weight-streaming) kernels, 2 = force the prefill (MFMA) kernels.
+/* Test knob, process-wide: 0 = choose the BitLinear kernel by token count (default: the
+ * weight-streaming dot4 kernel for few rows, the k-split MFMA kernel up to 64 rows, the
+ * 128-row MFMA tiles above), 1 = force the weight-streaming kernel, 2 = force the MFMA
+ * kernels (k-split up to 64 rows, tiles above), 3 = force the 128-row MFMA tiles.
  * Returns the previous value, or MMF_EINVAL for another value. */
 int mmf_set_regime(int regime);
 

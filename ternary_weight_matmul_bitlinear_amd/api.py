@@ -153,7 +153,8 @@ def _empty_stage():
 # ------------------------------------------------------------------ forward calls
 
 def set_regime(regime: int) -> int:
-    """0 auto, 1 force decode kernels, 2 force prefill kernels (test knob)."""
+    """0 auto, 1 force the weight-streaming kernel, 2 force the MFMA kernels (k-split up to
+    64 rows, 128-row tiles above), 3 force the 128-row tiles (test knob)."""
     r = L.lib().mmf_set_regime(int(regime))
     if r < 0:
         L.check("mmf_set_regime", r)

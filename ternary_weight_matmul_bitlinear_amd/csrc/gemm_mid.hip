@@ -1,0 +1,311 @@
+// gemm_mid.hip -- BitLinear for a few dozen token rows (up to 64): int8 MFMA against ternary
+// weights that are streamed from HBM exactly once, with the k range split over the waves of
+// a workgroup.
+//
+// DataCamp "MatMul-free language models", section "Replacing MatMul with ternary
+// operations": with weights in {-1,0,1} the layer output is an exact signed integer sum of
+// int8 activations; the packed codes c = q + 1 are multiplied on the matrix cores and the
+// offset is removed once per row, acc = sum_k q_x*c - sum_k q_x (exact in int32).
+//
+// Between one-token decode and thousands of prefill tokens: with tens of rows every weight
+// is still read once (the weights dominate the traffic), but the dot4 decode kernel spends
+// one VALU lane-op per 4 codes per token and becomes ALU-bound, while the prefill tiles
+// (128 rows) leave most workgroups idle.  Here:
+//   - one 256-thread workgroup owns 32 weight rows (for the GLU, 32 gate rows and the 32 up
+//     rows of the same features) and all M <= 64 token rows as two 32-row MFMA blocks;
+//   - its four waves take interleaved k-tiles of 128 (kt = wave, wave + 4, ...), so the
+//     four waves together read whole 128-byte lines of every weight row;
+//   - lane l (r = l % 32, g = l / 32) holds, per k-tile, the 16-byte packed piece (words
+//     4g..4g+3) of weight row r: word 4g + ks is exactly the 16-code B operand of MFMA step
+//     ks, paired with activation bytes 64g + 16ks + [0,16) of token row r.  All weight
+//     pieces of a wave are requested at kernel entry; activations (a few hundred KB, L2
+//     resident) are fetched up to four k-tiles ahead;
+//   - the four partial accumulators are summed through LDS and the fused epilogue (rescale,
+//     bias, residual, or SiLU(gate)*up) stores 8 consecutive outputs of one row per thread.
+// KTW (k-tiles per wave) is a template parameter so every load is unconditional: k-tiles
+// past the end re-read the last tile with zero weight codes.
+#include "mmf_internal.h"
+
+namespace mmf {
+
+namespace {
+
+constexpr int MID_NT = 256;
+constexpr int MID_KT = 128;  // k per tile
+
+template <int EPI, bool OUT_BF16, int KTW>
+__global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
+    constexpr int NB = EPI == EPI_GLU ? 2 : 1;  // 32-row weight blocks per workgroup
+    constexpr int MB = 2;                      // 32-row token blocks (M <= 64)
+    constexpr int PITCH = NB * 32 + 4;         // int32 per LDS row of a partial tile
+    __shared__ int32_t red[4][MB * 32][PITCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, g = lane >> 5;
+    const int K = p.K, KW = K / 16;
+    const int nk = (K + MID_KT - 1) / MID_KT;
+    const bool ragged = (K % MID_KT) != 0;
+
+    // ---- this workgroup's weight rows: block nb of segment sg starting at row n0
+    int blk = blockIdx.x, sg = 0;
+    if constexpr (EPI != EPI_GLU) {
+        while (sg + 1 < p.nseg && blk >= p.tiles_n[sg]) { blk -= p.tiles_n[sg]; ++sg; }
+    }
+    const int n0 = blk * 32;
+    const uint32_t *wrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const Seg &S = p.seg[EPI == EPI_GLU ? nb : sg];
+        const int n = n0 + r32 < S.n ? n0 + r32 : S.n - 1;  // clamped rows are never stored
+        wrow[nb] = S.packed + static_cast<int64_t>(n) * KW;
+    }
+    const int8_t *arow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int64_t m = mb * 32 + r32 < p.M ? mb * 32 + r32 : p.M - 1;
+        arow[mb] = p.A + m * K;
+    }
+
+    // ---- all weight pieces of this wave, requested up front (after the first activation
+    //      tile, so that the first k-tile waits only for its own two pieces of data)
+    uint4 bw[KTW][NB];
+    auto load_b = [&](int i) __attribute__((always_inline)) {
+        const int kt0 = wave + 4 * i;
+        const int kt = kt0 < nk ? kt0 : nk - 1;
+        // the upper lane half of a ragged last tile re-reads the lower half (in bounds)
+        const int word = kt * 8 + (ragged && kt == nk - 1 ? 0 : 4 * g);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bw[i][nb] = *reinterpret_cast<const uint4 *>(wrow[nb] + word);
+    };
+    auto a_off = [&](int i) __attribute__((always_inline)) {
+        const int kt0 = wave + 4 * i;
+        const int kt = kt0 < nk ? kt0 : nk - 1;
+        return kt * MID_KT + (ragged && kt == nk - 1 ? 0 : 64 * g);
+    };
+    // activations run PD k-tiles ahead of the MFMAs (their L2 latency would otherwise be
+    // paid once per k-tile of the wave)
+    constexpr int PD = KTW < 4 ? KTW : 4;
+    v4i av[PD][MB][4];
+    auto load_a = [&](int i, v4i (&dst)[MB][4]) __attribute__((always_inline)) {
+        const int off = a_off(i);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) dst[mb][ks] = *reinterpret_cast<const v4i *>(arow[mb] + off + 16 * ks);
+    };
+
+    v16i acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0;
+
+    load_a(0, av[0]);
+#pragma unroll
+    for (int i = 0; i < KTW; ++i) load_b(i);
+#pragma unroll
+    for (int i = 1; i < PD; ++i) load_a(i, av[i]);
+    // keep every load above issued here: the scheduler would otherwise sink them next to
+    // their first use and serialize the memory latency
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KTW; ++i) {
+        const int kt0 = wave + 4 * i;
+        // code mask: zero for tiles past the end and for the upper half of a ragged last tile
+        const bool live = kt0 < nk && !(ragged && kt0 == nk - 1 && g);
+        const uint32_t msk = live ? 0x03030303u : 0u;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t w[4] = {bw[i][nb].x, bw[i][nb].y, bw[i][nb].z, bw[i][nb].w};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const v4i b = v4i{static_cast<int>(w[ks] & msk), static_cast<int>((w[ks] >> 2) & msk),
+                                  static_cast<int>((w[ks] >> 4) & msk), static_cast<int>((w[ks] >> 6) & msk)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i % PD][mb][ks], b, acc[mb][nb], 0, 0, 0);
+            }
+        }
+        if (i + PD < KTW) load_a(i + PD, av[i % PD]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- sum the four waves' partial tiles.  Lane l holds C[row][col] for col = nb*32 + l%32
+    //      and rows mb*32 + 8*(e/4) + 4*g + (e%4).
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                red[wave][mb * 32 + 8 * (e >> 2) + 4 * g + (e & 3)][nb * 32 + r32] = acc[mb][nb][e];
+    __syncthreads();
+
+    // ---- epilogue: thread -> row tid/4, columns 8*(tid%4) .. +7 of the 32-column block
+    const int row_l = tid >> 2, c8 = 8 * (tid & 3);
+    const int64_t row = row_l;
+    if (row >= p.M) return;
+    int32_t v[NB][8];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[nb][j] = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int4 lo = *reinterpret_cast<const int4 *>(&red[w][row_l][nb * 32 + c8]);
+            const int4 hi = *reinterpret_cast<const int4 *>(&red[w][row_l][nb * 32 + c8 + 4]);
+            v[nb][0] += lo.x; v[nb][1] += lo.y; v[nb][2] += lo.z; v[nb][3] += lo.w;
+            v[nb][4] += hi.x; v[nb][5] += hi.y; v[nb][6] += hi.z; v[nb][7] += hi.w;
+        }
+    }
+    const int32_t rs = p.rowsum[row];
+    const float a = p.a[row];
+    const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
+    const int ncols = S.n;
+    const int col = n0 + c8;  // first column (feature) inside the segment
+    if (col >= ncols) return;
+    const bool full = col + 8 <= ncols;
+    float o[8];
+    if constexpr (EPI == EPI_GLU) {
+        const float sa_g = p.seg[0].scale * a, sa_u = p.seg[1].scale * a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cj = col + j < ncols ? col + j : ncols - 1;
+            const float bg = p.seg[0].bias ? p.seg[0].bias[cj] : 0.0f;
+            const float bu = p.seg[1].bias ? p.seg[1].bias[cj] : 0.0f;
+            const float yg = static_cast<float>(v[0][j] - rs) * sa_g + bg;
+            const float yu = static_cast<float>(v[1][j] - rs) * sa_u + bu;
+            o[j] = siluf_(yg) * yu;
+        }
+    } else {
+        const float sa = S.scale * a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int cj = col + j < ncols ? col + j : ncols - 1;
+            const float bb = S.bias ? S.bias[cj] : 0.0f;
+            o[j] = static_cast<float>(v[0][j] - rs) * sa + bb;
+        }
+    }
+    if (p.cap.acc && p.cap.row0 <= row && row < p.cap.row1) {  // test protocol (rare)
+        int32_t *c = p.cap.acc + (row - p.cap.row0) * p.cap.acc_ld;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (col + j >= ncols) continue;
+            if constexpr (EPI == EPI_GLU) {
+                c[p.seg[0].cap_col0 + col + j] = v[0][j] - rs;
+                c[p.seg[1].cap_col0 + col + j] = v[1][j] - rs;
+            } else {
+                c[S.cap_col0 + col + j] = v[0][j] - rs;
+            }
+        }
+    }
+    const int ocol = (EPI == EPI_GLU ? 0 : S.out_col0) + col;
+    const bool vec = full && (p.ldo % 8 == 0) && (ocol % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0);
+    if constexpr (EPI == EPI_RESID) {
+        const int64_t ri = row * p.ldr + ocol;
+        if (vec) {
+            if constexpr (OUT_BF16) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.resid) + ri);
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[2 * j] += __uint_as_float(w[j] << 16);
+                    o[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+                }
+            } else {
+                const float4 r0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri);
+                const float4 r1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri + 4);
+                o[0] += r0.x; o[1] += r0.y; o[2] += r0.z; o[3] += r0.w;
+                o[4] += r1.x; o[5] += r1.y; o[6] += r1.z; o[7] += r1.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (col + j < ncols) o[j] += load_act<OUT_BF16>(p.resid, ri + j);
+        }
+    }
+    const int64_t oi = row * p.ldo + ocol;
+    if constexpr (OUT_BF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
+        if (vec) {
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) + oi) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (col + j < ncols) static_cast<uint16_t *>(p.out)[oi + j] = static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // the stored (rounded) values, for the capture
+            o[2 * j] = __uint_as_float(w[j] << 16);
+            o[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+    } else {
+        if (vec) {
+            *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(static_cast<float *>(p.out) + oi + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (col + j < ncols) static_cast<float *>(p.out)[oi + j] = o[j];
+        }
+    }
+    if (p.cap.y_out && p.cap.row0 <= row && row < p.cap.row1) {
+        float *cy = p.cap.y_out + (row - p.cap.row0) * p.ldo + ocol;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (col + j < ncols) cy[j] = o[j];
+    }
+}
+
+template <int EPI, bool OUT_BF16>
+bool launch_ktw(const GemmArgs &a, dim3 grid, hipStream_t s) {
+    const int nk = (a.K + MID_KT - 1) / MID_KT;
+    const int ktw = (nk + 3) / 4;
+    if (ktw <= 2) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 2>), grid, dim3(MID_NT), 0, s, a);
+    else if (ktw <= 4) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 4>), grid, dim3(MID_NT), 0, s, a);
+    else if (ktw <= 8) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 8>), grid, dim3(MID_NT), 0, s, a);
+    else if (ktw <= 12 && EPI != EPI_GLU) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 12>), grid, dim3(MID_NT), 0, s, a);
+    else return false;
+    return true;
+}
+
+template <int EPI>
+bool launch_mid_epi(const GemmArgs &a, dim3 grid, hipStream_t s) {
+    return a.out_bf16 ? launch_ktw<EPI, true>(a, grid, s) : launch_ktw<EPI, false>(a, grid, s);
+}
+}  // namespace
+
+bool mid_gemm_supported(const GemmArgs &a) {
+    const int nk = (a.K + MID_KT - 1) / MID_KT;
+    const int ktw = (nk + 3) / 4;
+    return a.M >= 1 && a.M <= kMidMaxM && (ktw <= 8 || (ktw <= 12 && a.epi != EPI_GLU));
+}
+
+hipError_t launch_gemm_mid(const GemmArgs &a_in, hipStream_t s) {
+    if (a_in.M <= 0) return hipSuccess;
+    GemmArgs a = a_in;
+    a.tiles_n_total = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        a.tiles_n[i] = (a.seg[i].n + 31) / 32;
+        if (a.epi == EPI_GLU && i == 1) a.tiles_n[i] = 0;  // up rows ride with the gate block
+        a.tiles_n_total += a.tiles_n[i];
+    }
+    const dim3 grid(static_cast<unsigned>(a.tiles_n_total));
+    timing_begin(a.family, s);
+    bool ok;
+    switch (a.epi) {
+        case EPI_STORE: ok = launch_mid_epi<EPI_STORE>(a, grid, s); break;
+        case EPI_RESID: ok = launch_mid_epi<EPI_RESID>(a, grid, s); break;
+        default: ok = launch_mid_epi<EPI_GLU>(a, grid, s); break;
+    }
+    timing_end(a.family, s);
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace mmf

@@ -66,12 +66,12 @@ static int check_device() {
 // ------------------------------------------------------------------ regime knob
 static std::atomic<int> g_regime{0};
 // Token rows up to which the weight-streaming decode kernel is used.
-constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kDecodeMaxM = 4;
 
 static bool use_decode(int64_t m) {
     const int r = g_regime.load();
     if (r == 1) return true;
-    if (r == 2) return false;
+    if (r >= 2) return false;
     return m <= kDecodeMaxM;
 }
 
@@ -225,6 +225,9 @@ static hipError_t gemm(const QBuf &qb, int64_t M, int32_t K, const Seg *segs, in
     ga.cap.q = nullptr;
     ga.cap.a = nullptr;
     ga.family = family;
+    // up to kMidMaxM rows: the k-split kernel that reads the weights once (regime 3 forces
+    // the 128-row tiles at any M)
+    if (g_regime.load() != 3 && M <= kMidMaxM && mid_gemm_supported(ga)) return launch_gemm_mid(ga, s);
     return launch_gemm(ga, s);
 }
 
@@ -297,7 +300,7 @@ int mmf_abi_version(void) { return MMF_ABI_VERSION; }
 const char *mmf_last_error(void) { return g_err.c_str(); }
 
 int mmf_set_regime(int regime) {
-    if (regime < 0 || regime > 2) return set_error(MMF_EINVAL, "mmf_set_regime: %d", regime);
+    if (regime < 0 || regime > 3) return set_error(MMF_EINVAL, "mmf_set_regime: %d", regime);
     return g_regime.exchange(regime);
 }
 

@@ -274,6 +274,12 @@ hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, 
                             hipStream_t s);
 hipError_t launch_copy_state(const float *h0, float *h_out, int64_t n, hipStream_t s);
 
+// Token rows up to which the MFMA regime uses the mid-size kernel (gemm_mid.hip): weights
+// read once per launch, k split over the waves of a workgroup.
+constexpr int64_t kMidMaxM = 64;
+bool mid_gemm_supported(const GemmArgs &a);
+hipError_t launch_gemm_mid(const GemmArgs &a, hipStream_t s);
+
 // Tokens per decode-kernel token group (rows of q staged in LDS).
 constexpr int kGemvTokens = 8;
 // Chunk length of the prefill scan (tokens per workgroup of the output pass).

@@ -121,7 +121,7 @@ def test_workspace_too_small_is_reported(lib):
 
 
 def test_regime_knob(lib):
-    assert lib.mmf_set_regime(3) == -1
+    assert lib.mmf_set_regime(4) == -1
     prev = lib.mmf_set_regime(1)
     assert lib.mmf_set_regime(prev) == 1
 

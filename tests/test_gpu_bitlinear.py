@@ -1,6 +1,7 @@
 """BitLinear parity on the GPU: int8 codes and int32 accumulators bit-exact against the
-oracle, rescaled outputs within tolerance, in both regimes (decode weight streaming and
-prefill MFMA) at shapes spanning several tiles, ragged tails and the real layer shapes."""
+oracle, rescaled outputs within tolerance, for every kernel (decode weight streaming, the
+k-split MFMA kernel for up to 64 rows, the 128-row MFMA tiles) at shapes spanning several
+tiles, ragged tails and the real layer shapes."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +22,13 @@ CASES = [
     (16, 5632, 2048, torch.bfloat16, False, False),
     (1, 6912, 2560, torch.bfloat16, True, False),
     (257, 2816, 1024, torch.bfloat16, False, False),
+    # k-split MFMA kernel: ragged k-tiles (K % 128 == 64), k-tiles per wave 1..11, ragged N
+    (33, 192, 100, torch.bfloat16, True, True),
+    (64, 64, 40, torch.float32, False, False),
+    (50, 2048, 6144, torch.bfloat16, False, False),
+    (64, 5632, 2048, torch.bfloat16, False, True),
+    (17, 4096, 96, torch.float32, True, False),
+    (48, 2048, 32000, torch.bfloat16, False, False),
 ]
 
 
@@ -31,7 +39,7 @@ def _restore_regime():
     api.set_regime(prev)
 
 
-@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 @pytest.mark.parametrize("M,K,N,dt,use_gamma,use_bias", CASES,
                          ids=[f"M{c[0]}K{c[1]}N{c[2]}{'bf' if c[3] == torch.bfloat16 else 'f'}"
                               for c in CASES])
@@ -61,7 +69,7 @@ def test_bitlinear_parity(orc, regime, M, K, N, dt, use_gamma, use_bias):
     rel_check(host(y), y_o, TOL[torch.float32], "y")
 
 
-@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 def test_bitlinear_bf16_output_and_zero_rows(orc, regime):
     """bf16 output; an all-zero input row gives exactly the bias (acc = 0)."""
     M, K, N = 40, 512, 320
@@ -89,17 +97,18 @@ def test_bitlinear_empty_is_noop():
 
 
 def test_regimes_agree_bit_exact_on_integers():
-    """Decode and prefill kernels produce identical int8 codes and accumulators."""
+    """All three kernels produce identical int8 codes and accumulators."""
     M, K, N = 24, 2048, 700
     note("bitlinear regimes agree")
     x = synth.round_to_bf16(synth.gaussian(9, (M, K)))
     w = api.TernaryLinear.from_latent(synth.gaussian(10, (N, K), 0.02))
     out = {}
-    for r in (1, 2):
+    for r in (1, 2, 3):
         api.set_regime(r)
         cap = api.StageCapture.alloc(0, M, K, N)
         api.bitlinear_forward(w, dev(x, torch.bfloat16), capture=cap)
         torch.cuda.synchronize()
         out[r] = cap.host()
-    assert np.array_equal(out[1]["q"], out[2]["q"])
-    assert np.array_equal(out[1]["acc"], out[2]["acc"])
+    for r in (2, 3):
+        assert np.array_equal(out[1]["q"], out[r]["q"])
+        assert np.array_equal(out[1]["acc"], out[r]["acc"])

@@ -22,7 +22,7 @@ def _restore_regime():
     api.set_regime(prev)
 
 
-@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 @pytest.mark.parametrize("M,D,F,dt,resid", [(5, 256, 704, torch.float32, False),
                                             (64, 256, 704, torch.bfloat16, True),
                                             (300, 1024, 2816, torch.bfloat16, True)])
@@ -72,7 +72,7 @@ def _block_case(orc, D, F, B, T, dt, seed, gate_mode=0, f_bias=None, use_gains=F
     return blk, W, x, fb, gw
 
 
-@pytest.mark.parametrize("regime", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("gate_mode", [0, 1])
 def test_block_tiny_parity(orc, regime, dt, gate_mode):

@@ -74,6 +74,8 @@ def main() -> int:
     ap.add_argument("--regime", choices=("auto", "decode", "prefill", "tiles"), default="auto",
                     help="BitLinear kernel choice (auto: by token count; decode: weight "
                          "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
+    ap.add_argument("--no-kernel-sweep", dest="kernel_sweep", action="store_false",
+                    help="decode stacks: skip the per-kernel BitLinear streaming sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -139,11 +141,27 @@ def main() -> int:
         api.block_forward(blk, x, h_state=h, y=y, ws=ws)
     torch.cuda.synchronize()
     api.timing_enable(False)
+    # algorithmic work per step of each family: int8 ops of the GEMMs; bytes of the HBM-bound
+    # kernels (the scan reads the bf16 i|f|g pre-activations once and writes the int8 o_proj
+    # input with its scale and code sum; the row quantizers read x, y1 (D wide) and the GLU
+    # hidden (F wide) and write int8 codes + 8 bytes per row)
+    ab = 2 if w.bf16 else 4
+    work = {"gemm_ifg": ("mfma", 2.0 * M * D * 3 * D), "gemm_o": ("mfma", 2.0 * M * D * D),
+            "gemm_gateup": ("mfma", 2.0 * M * D * 2 * F), "gemm_down": ("mfma", 2.0 * M * F * D),
+            "scan": ("hbm", M * (3 * D * ab + D + 8.0)),
+            "quant": ("hbm", M * (2 * D * (ab + 1) + F * (ab + 1) + 24.0))}
     for fam in ("quant", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemv", "scan"):
         n, ms = api.timing_query(fam)
         if n:
             fams[fam] = {"launches_per_step": n / nb, "ms_per_launch": ms / n,
                          "ms_per_step": ms / nb}
+            if fam in work:
+                bound, amount = work[fam]
+                sec = ms / nb * 1e-3
+                if bound == "mfma":
+                    fams[fam].update(tops=amount / sec / 1e12, mfma_frac=amount / sec / 1e12 / PEAK_INT8_TOPS)
+                else:
+                    fams[fam].update(gbs=amount / sec / 1e9, hbm_frac=amount / sec / 1e9 / PEAK_HBM_GBS)
 
     # dominant kernel: gate|up GEMM, 2*M*K*N dense int8 ops per launch
     ops = 2.0 * M * D * (2 * F)
@@ -189,9 +207,58 @@ def main() -> int:
             "config": {"workload": w.name, "B": w.B, "T": w.T, "D": D, "F": F,
                        "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"},
             "roofline": roofline, "cpu_baseline": cpu,
-            "kernels": fams, "kernels_note": f"separate {nb}-step pass, events around every launch"}
+            "kernels": fams, "kernels_note": f"separate {nb}-step pass, events around every launch; "
+                                             "mfma_frac / hbm_frac: the family's algorithmic work per "
+                                             "step over its summed launch time"}
     print(json.dumps(line))
     return 0
+
+
+def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
+    """One BitLinear launch per (N, K) at B token rows, cycling through enough copies of random
+    packed weights (>= 512 MB) that none is in the 256 MB MALL when it is read again; durations
+    from the library's events.  Shapes: the 1.3B projections, the head, and one large matrix
+    whose streaming is not dominated by the per-launch latency."""
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api
+
+    out = []
+    fams = ["gemv", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemm"]
+    for N, K in ((3 * D, D), (2 * F, D), (D, F), (V, D), (65536, 8192)):
+        wbytes = N * K // 4
+        copies = max(2, -(-(512 << 20) // wbytes))
+        gen = torch.Generator(device="cuda").manual_seed(N * 131 + K)
+        ws = []
+        for _ in range(copies):
+            r0 = torch.randint(-2**31, 2**31 - 1, (N, K // 16), dtype=torch.int32, device="cuda", generator=gen)
+            r1 = torch.randint(-2**31, 2**31 - 1, (N, K // 16), dtype=torch.int32, device="cuda", generator=gen)
+            lo = r0 & 0x55555555                    # code bit 0
+            hi = (r1 & 0x55555555) & ~lo            # code bit 1 where bit 0 is clear: codes 0, 1, 2
+            ws.append(api.TernaryLinear(lo | (hi << 1), 0.016, K, N))
+        x = torch.randn((B, K), device="cuda").to(torch.bfloat16)
+        for i in range(copies):
+            api.bitlinear_forward(ws[i], x)
+        torch.cuda.synchronize()
+        api.timing_reset()
+        api.timing_families(fams)
+        api.timing_enable(True)
+        reps = max(copies, 40)
+        for i in range(reps):
+            api.bitlinear_forward(ws[i % copies], x)
+        torch.cuda.synchronize()
+        api.timing_enable(False)
+        n = ms = 0
+        for f in fams:
+            nf, msf = api.timing_query(f)
+            n, ms = n + nf, ms + msf
+        bytes_ = wbytes + B * K * 2 + B * N * 2
+        gbs = bytes_ * n / (ms * 1e-3) / 1e9
+        out.append({"N": N, "K": K, "rows": B, "weight_copies": copies,
+                    "us_per_launch": ms / n * 1e3, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
+        del ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_stack(args, w) -> int:
@@ -309,6 +376,8 @@ def bench_stack(args, w) -> int:
         extra = {"step_hbm_fraction": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                  "step_algorithmic_bytes": step_bytes, "eager_ms_per_step": eager_ms,
                  "graph_ms_per_step": graph_ms}
+        if args.kernel_sweep:
+            extra["decode_bitlinear_kernels"] = decode_kernel_sweep(B, D, F, w.vocab)
     else:
         ops = 2.0 * (B * T) * D * (2 * F)
         achieved = ops * n / (ms * 1e-3) / 1e12 if n else None

@@ -14,7 +14,9 @@
 // holds 8 consecutive elements per 512-element chunk of the row (one 16-byte bf16 load or
 // two 16-byte fp32 loads per chunk), NC chunks per row, kept in registers between the max
 // pass and the quantize pass, so the row is read from HBM once; the next row's loads are
-// issued before the current row is reduced.  HBM-bound: K*(bytes_in + 1) bytes per row.
+// issued before the current row is reduced.  Wide bf16 rows without a gain (the GLU hidden,
+// D = 2560) use quant_rows256_kernel instead, whose waits never drain earlier stores.
+// HBM-bound: K*(bytes_in + 1) bytes per row.
 #include "mmf_internal.h"
 
 namespace mmf {
@@ -143,6 +145,109 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
     }
 }
 
+// bf16 rows without a gain at the model widths (K = 256*NC): lane l holds elements 4l + 256c
+// of chunk c (one 8-byte load, one 4-byte store), R rows per wave with all of their loads
+// issued before the first row is reduced.  Every global access
+// after the row loads is unconditional (the rows of a partial last wave are clamped to the
+// last row and rewrite its identical results; the scale and code sum are stored by all
+// lanes), so each wait covers only the loads of the row it precedes and never the earlier
+// rows' stores.  CAP adds the stage-capture stores (tests only).
+template <int NC, int R, bool CAP>
+__global__ __launch_bounds__(256) void quant_rows256_kernel(QuantArgs p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int K = p.K;
+    int64_t rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = wave_id * R + r;
+        rows[r] = row < p.M ? row : p.M - 1;
+    }
+    uint2 raw[R][NC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            raw[r][c] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.x) + rows[r] * K + lane * 4 + 256 * c);
+    __builtin_amdgcn_sched_barrier(0);  // all row loads are issued here, not next to their use
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float v[NC][4];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            v[c][0] = __uint_as_float(raw[r][c].x << 16);
+            v[c][1] = __uint_as_float(raw[r][c].x & 0xFFFF0000u);
+            v[c][2] = __uint_as_float(raw[r][c].y << 16);
+            v[c][3] = __uint_as_float(raw[r][c].y & 0xFFFF0000u);
+        }
+        float mx = 0.0f, ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mx = fmaxf(mx, fabsf(v[c][j]));
+                ss += v[c][j] * v[c][j];
+            }
+        mx = wave_max(mx);
+        ss = wave_sum(ss);
+        const float me = fmaxf(mx, 1e-5f);
+        const float sc = 127.0f / me;
+        const int64_t row = rows[r];
+        int qsum = 0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            uint32_t pk = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float q = rintf(v[c][j] * sc);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+                const int qi = static_cast<int>(q);
+                qsum += qi;
+                pk |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * j);
+            }
+            const int64_t k0 = lane * 4 + 256 * c;
+            *reinterpret_cast<uint32_t *>(p.q + row * K + k0) = pk;
+            if constexpr (CAP) {
+                if (p.cap.row0 <= row && row < p.cap.row1) {
+                    const int64_t crow = row - p.cap.row0;
+                    if (p.cap.x_in) *reinterpret_cast<float4 *>(p.cap.x_in + crow * K + k0) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
+                    if (p.cap.q) *reinterpret_cast<uint32_t *>(p.cap.q + crow * K + k0) = pk;
+                }
+            }
+        }
+        qsum = wave_sum_i(qsum);
+        const float a = me / 127.0f * (1.0f / sqrtf(ss / static_cast<float>(K) + p.eps));
+        p.a[row] = a;
+        p.rowsum[row] = qsum;
+        if constexpr (CAP) {
+            if (lane == 0 && p.cap.a && p.cap.row0 <= row && row < p.cap.row1) p.cap.a[row - p.cap.row0] = a;
+        }
+    }
+}
+
+template <int NC, int R>
+void launch_rows256_r(const QuantArgs &a, hipStream_t s) {
+    const int64_t waves = (a.M + R - 1) / R;
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    if (a.cap.row1 > a.cap.row0) hipLaunchKernelGGL((quant_rows256_kernel<NC, R, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((quant_rows256_kernel<NC, R, false>), grid, dim3(256), 0, s, a);
+}
+
+// The wide model rows: D = 2560 and F = 2816, 5632, 6912 (two rows per wave up to 2816
+// elements when there are enough rows to fill the chip twice over, else one); at 1024 and
+// 2048 elements quant_rows_kernel measured as fast or faster.
+bool launch_rows256(const QuantArgs &a, hipStream_t s) {
+    if (!a.x_bf16 || a.gamma || a.K % 256 != 0) return false;
+    const bool two = a.M >= 4096;
+    switch (a.K / 256) {
+        case 10: if (two) launch_rows256_r<10, 2>(a, s); else launch_rows256_r<10, 1>(a, s); return true;
+        case 11: if (two) launch_rows256_r<11, 2>(a, s); else launch_rows256_r<11, 1>(a, s); return true;
+        case 22: launch_rows256_r<22, 1>(a, s); return true;
+        case 27: launch_rows256_r<27, 1>(a, s); return true;
+        default: return false;
+    }
+}
+
 template <bool BF16, bool GAMMA>
 void launch_nc(const QuantArgs &a, dim3 grid, hipStream_t s) {
     const int nc = (a.K + 511) / 512;
@@ -162,7 +267,8 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
     const int64_t wg_cap = 256 * 8;
     const dim3 grid(static_cast<unsigned>(wg_needed < wg_cap ? wg_needed : wg_cap));
     timing_begin(FAM_QUANT, s);
-    if (a.x_bf16) {
+    if (launch_rows256(a, s)) {
+    } else if (a.x_bf16) {
         if (a.gamma) launch_nc<true, true>(a, grid, s);
         else launch_nc<true, false>(a, grid, s);
     } else {

@@ -9,15 +9,20 @@
 // With a few tokens per step the weights (0.25 byte each) are read once and used once, and
 // one BitLinear moves only a few MB, about one memory latency's worth of HBM bandwidth, so
 // the kernel is built to have every weight byte in flight as early as possible:
-//   - 16 lanes per weight row, 4 rows per wave, 16 rows per workgroup; lane j of a row
+//   - 16 lanes per weight row, 4 rows per wave, 16 rows per workgroup (32 for one token and
+//     rows of 8192 or more, so the row is quantized half as often); lane j of a row
 //     holds 16-byte chunks j, j+16, ... (64 k each) of the row in registers, and all of
 //     them are requested at kernel entry, before the activations are looked at;
 //   - meanwhile the workgroup RMS/absmax-quantizes its token group (<= TG rows) into LDS
 //     (the same arithmetic as the standalone quantizer, so the int8 codes are identical),
 //     or copies rows that are already quantized;
-//   - each packed word gives four dwords of 2-bit codes, which one v_perm_b32 each maps to
-//     signed int8 weights (code 0,1,2 -> -1,0,+1), consumed by v_dot4_i32_i8 against the
-//     LDS-resident activations: the int32 result is the exact ternary product;
+//   - each packed word gives four dwords of 2-bit codes c = q + 1 ((w >> 2a) & 0x03030303),
+//     which one v_perm_b32 each maps to signed int8 weights (code 0,1,2 -> -1,0,+1),
+//     consumed by v_dot4_i32_i8 against the LDS-resident activations: the int32 result is
+//     the exact ternary product.  For one token and rows of 8192 or more the permute is
+//     skipped: the codes are multiplied as they are and the offset is removed once per
+//     token with the row's code sum (acc = sum q_x*c - sum q_x), which the prologue adds to
+//     its reductions;
 //   - the 16 partial sums of a row are reduced for all tokens at once (halving exchanges),
 //     after which one lane per token writes the output (fused rescale, bias, residual or
 //     SiLU(gate)*up).
@@ -32,7 +37,8 @@ namespace {
 
 constexpr int LPR = 16;          // lanes per weight row
 constexpr int RPW = 64 / LPR;    // rows per wave
-constexpr int RPB = 4 * RPW;     // rows per workgroup (256 threads)
+// rows per workgroup: NW waves of RPW rows (4 waves, or 8 for one token with K >= 8192:
+// the activation row is then quantized once per 32 rows instead of once per 16)
 constexpr int CB = 8;            // 64-k chunks held per lane per pass (K <= 8192 in one pass)
 
 __host__ __device__ __forceinline__ int chunk_stride(int tg) { return 64 * tg + 16; }
@@ -78,12 +84,19 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
 }
 
 // XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations.
-// TG: token rows per workgroup (1, 4, 8 or 16).
-template <int EPI, int XIN, bool OUT_BF16, int TG>
-__global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
+// TG: token rows per workgroup (1, 4, 8 or 16).  NW: waves per workgroup.
+template <int EPI, int XIN, bool OUT_BF16, int TG, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
+    constexpr int NT = 64 * NW;
+    // long rows (8 waves): codes multiplied as they are, offset removed per token with the
+    // row's code sum (fewer VALU per code); otherwise codes mapped to signed weights, which
+    // needs no code sum (no extra reduction before the dot products)
+    constexpr bool UNS = NW == 8;
     extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-    __shared__ float red_m[4][TG], red_s[4][TG];
+    __shared__ float red_m[NW][TG], red_s[NW][TG];
+    __shared__ int red_q[NW][TG];
     __shared__ float s_a[TG];
+    __shared__ int s_rs[TG];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = p.K, NC = K / 64;
@@ -94,7 +107,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
 
     // ---------------------------------------------------------------- weight rows
     const int slot = lane / LPR, j = lane % LPR;
-    const int r = blockIdx.x * RPB + wave * RPW + slot;
+    const int r = blockIdx.x * (NW * RPW) + wave * RPW + slot;
     const bool rvalid = r < p.rows_total;
     int sg = 0, n = r;
     if constexpr (EPI != EPI_GLU) {
@@ -134,9 +147,9 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
         float pm[TG], ps[TG];
         // one token: its row (<= 3 x 8 values per thread for K <= 6144) stays in registers
         // between the two passes
-        constexpr int KEEP = TG == 1 ? 3 : 0;
+        constexpr int KEEP = TG == 1 ? (NW == 8 ? 4 : 3) : 0;
         float xk[KEEP > 0 ? KEEP : 1][8];
-        const bool keep = KEEP > 0 && K <= 2048 * KEEP;
+        const bool keep = KEEP > 0 && K <= 8 * NT * KEEP;
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
             const int64_t tok = t0 + (t < mt ? t : mt - 1);
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
             if (keep) {
 #pragma unroll
                 for (int it = 0; it < KEEP; ++it) {
-                    const int k0 = tid * 8 + 2048 * it;
+                    const int k0 = tid * 8 + 8 * NT * it;
                     if (k0 < K) {
                         load8v<BF>(p.x, tok * K + k0, xk[it]);
 #pragma unroll
@@ -158,7 +171,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
                 }
                 continue;
             }
-            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
+            for (int k0 = tid * 8; k0 < K; k0 += 8 * NT) {
                 float v[8];
                 load8v<BF>(p.x, tok * K + k0, v);
 #pragma unroll
@@ -182,10 +195,15 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
         float sc[TG];
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
-            const float mx = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+            float mx = red_m[0][t];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red_m[w][t]);
             sc[t] = 127.0f / fmaxf(mx, 1e-5f);
         }
         const bool cap_any = cap_blk && (p.cap.x_in || p.cap.q) && p.cap.row0 < t0 + mt && t0 < p.cap.row1;
+        int qsum[TG];  // this thread's share of each token's code sum
+#pragma unroll
+        for (int t = 0; t < TG; ++t) qsum[t] = 0;
         auto quant8 = [&](int t, int k0, const float (&v)[8]) __attribute__((always_inline)) {
             uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -193,6 +211,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
                 const float pj = p.gamma ? v[e] * p.gamma[k0 + e] : v[e];
                 float rq = rintf(pj * sc[t]);
                 rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+                if constexpr (UNS) qsum[t] += static_cast<int>(rq);
                 const uint32_t byte = static_cast<uint32_t>(static_cast<int>(rq)) & 0xFFu;
                 if (e < 4) lo |= byte << (8 * e);
                 else hi |= byte << (8 * (e - 4));
@@ -210,11 +229,11 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
         if (keep) {
 #pragma unroll
             for (int it = 0; it < KEEP; ++it) {
-                const int k0 = tid * 8 + 2048 * it;
+                const int k0 = tid * 8 + 8 * NT * it;
                 if (k0 < K) quant8(0, k0, xk[it]);
             }
         } else {
-            for (int k0 = tid * 8; k0 < K; k0 += 2048) {
+            for (int k0 = tid * 8; k0 < K; k0 += 8 * NT) {
                 float v[TG][8];
 #pragma unroll
                 for (int t = 0; t < TG; ++t) load8v<BF>(p.x, (t0 + (t < mt ? t : mt - 1)) * K + k0, v[t]);
@@ -222,17 +241,24 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
                 for (int t = 0; t < TG; ++t) quant8(t, k0, v[t]);
             }
         }
+        if constexpr (UNS) {
+            // code sums: reduced here, summed over the waves after the barrier below
+            constexpr int SH = 6 - (TG == 1 ? 0 : TG == 4 ? 2 : TG == 8 ? 3 : 4);
+            const int rq = wave_reduce_multi<TG, false, int>(qsum);
+            if ((lane & ((1 << SH) - 1)) == 0) red_q[wave][lane >> SH] = rq;
+        }
         if (tid < mt) {
             const int t = tid;
-            const float mx = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+            float mx = red_m[0][t], ss = red_s[0][t];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, red_m[w][t]); ss += red_s[w][t]; }
             const float me = fmaxf(mx, 1e-5f);
-            const float ss = (red_s[0][t] + red_s[1][t]) + (red_s[2][t] + red_s[3][t]);
             s_a[t] = me / 127.0f * (1.0f / sqrtf(ss / static_cast<float>(K) + p.eps));
             const int64_t tok = t0 + t;
             if (cap_blk && p.cap.a && p.cap.row0 <= tok && tok < p.cap.row1) p.cap.a[tok - p.cap.row0] = s_a[t];
         }
     } else {
-        for (int k0 = tid * 16; k0 < K; k0 += 4096) {
+        for (int k0 = tid * 16; k0 < K; k0 += 16 * NT) {
             uint4 v[TG];  // every token's 16 bytes requested before any is stored
 #pragma unroll
             for (int t = 0; t < TG; ++t)
@@ -240,9 +266,21 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
 #pragma unroll
             for (int t = 0; t < TG; ++t) *reinterpret_cast<uint4 *>(qs + (k0 >> 6) * CS + 64 * t + (k0 & 63)) = v[t];
         }
-        if (tid < mt) s_a[tid] = p.a[t0 + tid];
+        if (tid < mt) {
+            s_a[tid] = p.a[t0 + tid];
+            s_rs[tid] = p.rowsum[t0 + tid];
+        }
     }
     __syncthreads();
+    if constexpr (XIN != 0 && UNS) {
+        if (tid < mt) {
+            int q = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) q += red_q[w][tid];
+            s_rs[tid] = q;
+        }
+        __syncthreads();
+    }
 
     // ---------------------------------------------------------------- dot products
     int acc0[TG], acc1[TG];
@@ -254,17 +292,19 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
 #pragma unroll
         for (int i = 0; i < CB; ++i) {
             if (i >= niter) break;
-            // chunks past the row end (last slot of a ragged row) read as all-zero weights
-            // (code 1) against chunk 0
+            // chunk slots past the row end read as weight 0 against chunk 0 and add nothing
             const int c = base + j + LPR * i;
             const bool cv = c < NC && rvalid;
-            const uint32_t z = 0x55555555u;
-            const v4i ca[4] = {signed_codes(cv ? wa[i].x : z), signed_codes(cv ? wa[i].y : z),
-                               signed_codes(cv ? wa[i].z : z), signed_codes(cv ? wa[i].w : z)};
+            const uint32_t z = UNS ? 0u : 0x55555555u;  // a zero contribution either way
+            auto codes = [&](uint32_t w) __attribute__((always_inline)) {
+                return UNS ? unpack_codes(w) : signed_codes(w);
+            };
+            const v4i ca[4] = {codes(cv ? wa[i].x : z), codes(cv ? wa[i].y : z),
+                               codes(cv ? wa[i].z : z), codes(cv ? wa[i].w : z)};
             v4i cb[4];
             if constexpr (EPI == EPI_GLU) {
-                cb[0] = signed_codes(cv ? wb[i].x : z); cb[1] = signed_codes(cv ? wb[i].y : z);
-                cb[2] = signed_codes(cv ? wb[i].z : z); cb[3] = signed_codes(cv ? wb[i].w : z);
+                cb[0] = codes(cv ? wb[i].x : z); cb[1] = codes(cv ? wb[i].y : z);
+                cb[2] = codes(cv ? wb[i].z : z); cb[3] = codes(cv ? wb[i].w : z);
             }
             const int8_t *qc = qs + (cv ? c : 0) * CS;
             // every token slot is multiplied (slots past the group end hold stale values and
@@ -290,11 +330,15 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
     }
     // the 16 partial sums of the row, for every token at once: lane j of the row ends with
     // token j / (16 / TG)
-    const int my0 = wave_reduce_multi<TG, false, int, LPR>(acc0);
+    int my0 = wave_reduce_multi<TG, false, int, LPR>(acc0);
     int my1 = 0;
     if constexpr (EPI == EPI_GLU) my1 = wave_reduce_multi<TG, false, int, LPR>(acc1);
     if (!rvalid || j % STRIDE != 0) return;
     if (tj >= mt) return;
+    if constexpr (UNS) {
+        my0 -= s_rs[tj];
+        if constexpr (EPI == EPI_GLU) my1 -= s_rs[tj];
+    }
     const int64_t tok = t0 + tj;
     const float at = s_a[tj];
     const bool capr = p.cap.row0 <= tok && tok < p.cap.row1;
@@ -327,27 +371,40 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs p) {
     }
 }
 
+template <int EPI, int XIN, int TG, int NW>
+void launch5(const GemvArgs &a, size_t lds, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>((a.rows_total + NW * RPW - 1) / (NW * RPW)),
+                    static_cast<unsigned>((a.M + TG - 1) / TG));
+    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true, TG, NW>), grid, dim3(64 * NW), lds, s, a);
+    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false, TG, NW>), grid, dim3(64 * NW), lds, s, a);
+}
+
 template <int EPI, int XIN, int TG>
-void launch4(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true, TG>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false, TG>), grid, dim3(256), lds, s, a);
+void launch4(const GemvArgs &a, size_t lds, hipStream_t s) {
+    if constexpr (TG == 1) {
+        if (a.K >= 8192) {
+            launch5<EPI, XIN, TG, 8>(a, lds, s);
+            return;
+        }
+    }
+    launch5<EPI, XIN, TG, 4>(a, lds, s);
 }
 
 template <int EPI, int XIN>
-void launch3(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
+void launch3(const GemvArgs &a, size_t lds, hipStream_t s) {
     switch (a.tokens_per_group) {
-        case 1: launch4<EPI, XIN, 1>(a, grid, lds, s); break;
-        case 4: launch4<EPI, XIN, 4>(a, grid, lds, s); break;
-        case 8: launch4<EPI, XIN, 8>(a, grid, lds, s); break;
-        default: launch4<EPI, XIN, 16>(a, grid, lds, s); break;
+        case 1: launch4<EPI, XIN, 1>(a, lds, s); break;
+        case 4: launch4<EPI, XIN, 4>(a, lds, s); break;
+        case 8: launch4<EPI, XIN, 8>(a, lds, s); break;
+        default: launch4<EPI, XIN, 16>(a, lds, s); break;
     }
 }
 
 template <int EPI>
-void launch2(const GemvArgs &a, dim3 grid, size_t lds, hipStream_t s) {
-    if (!a.x) launch3<EPI, 0>(a, grid, lds, s);
-    else if (a.x_bf16) launch3<EPI, 2>(a, grid, lds, s);
-    else launch3<EPI, 1>(a, grid, lds, s);
+void launch2(const GemvArgs &a, size_t lds, hipStream_t s) {
+    if (!a.x) launch3<EPI, 0>(a, lds, s);
+    else if (a.x_bf16) launch3<EPI, 2>(a, lds, s);
+    else launch3<EPI, 1>(a, lds, s);
 }
 
 }  // namespace
@@ -362,14 +419,12 @@ hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
     int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     while (tg > 1 && gemv_lds_bytes(a.K, tg) > 64 * 1024) tg = tg == 16 ? 8 : tg == 8 ? 4 : 1;
     a.tokens_per_group = tg;
-    const dim3 grid(static_cast<unsigned>((a.rows_total + RPB - 1) / RPB),
-                    static_cast<unsigned>((a.M + tg - 1) / tg));
     const size_t lds = gemv_lds_bytes(a.K, tg);
     timing_begin(FAM_GEMV, s);
     switch (a.epi) {
-        case EPI_STORE: launch2<EPI_STORE>(a, grid, lds, s); break;
-        case EPI_RESID: launch2<EPI_RESID>(a, grid, lds, s); break;
-        default: launch2<EPI_GLU>(a, grid, lds, s); break;
+        case EPI_STORE: launch2<EPI_STORE>(a, lds, s); break;
+        case EPI_RESID: launch2<EPI_RESID>(a, lds, s); break;
+        default: launch2<EPI_GLU>(a, lds, s); break;
     }
     timing_end(FAM_GEMV, s);
     return hipGetLastError();

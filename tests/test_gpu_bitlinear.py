@@ -29,6 +29,10 @@ CASES = [
     (64, 5632, 2048, torch.bfloat16, False, True),
     (17, 4096, 96, torch.float32, True, False),
     (48, 2048, 32000, torch.bfloat16, False, False),
+    # one token, rows of 8192 and more: the long-row weight-streaming variant (two passes of
+    # weight chunks at K = 16384)
+    (1, 8192, 300, torch.bfloat16, True, True),
+    (1, 16384, 130, torch.float32, False, False),
 ]
 
 

@@ -25,7 +25,9 @@ def _restore_regime():
 @pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 @pytest.mark.parametrize("M,D,F,dt,resid", [(5, 256, 704, torch.float32, False),
                                             (64, 256, 704, torch.bfloat16, True),
-                                            (300, 1024, 2816, torch.bfloat16, True)])
+                                            (300, 1024, 2816, torch.bfloat16, True),
+                                            # one token, down projection over K = F = 8192
+                                            (1, 256, 8192, torch.bfloat16, True)])
 def test_glu_parity(orc, regime, M, D, F, dt, resid):
     note(f"glu regime={regime} M={M} D={D} F={F}")
     lat = small_latents(M + D, D, F)

@@ -14,8 +14,8 @@
 // holds 8 consecutive elements per 512-element chunk of the row (one 16-byte bf16 load or
 // two 16-byte fp32 loads per chunk), NC chunks per row, kept in registers between the max
 // pass and the quantize pass, so the row is read from HBM once; the next row's loads are
-// issued before the current row is reduced.  Wide bf16 rows without a gain (the GLU hidden,
-// D = 2560) use quant_rows256_kernel instead, whose waits never drain earlier stores.
+// issued before the current row is reduced.  bf16 rows without a gain at the model widths
+// use quant_rows256_kernel instead, whose waits never drain earlier stores.
 // HBM-bound: K*(bytes_in + 1) bytes per row.
 #include "mmf_internal.h"
 
@@ -233,15 +233,15 @@ void launch_rows256_r(const QuantArgs &a, hipStream_t s) {
     else hipLaunchKernelGGL((quant_rows256_kernel<NC, R, false>), grid, dim3(256), 0, s, a);
 }
 
-// The wide model rows: D = 2560 and F = 2816, 5632, 6912 (two rows per wave up to 2816
-// elements when there are enough rows to fill the chip twice over, else one); at 1024 and
-// 2048 elements quant_rows_kernel measured as fast or faster.
+// The model widths: D = 1024, 2048, 2560 and F = 2816, 5632, 6912, one row per wave (more
+// rows per wave measured slower or equal).
 bool launch_rows256(const QuantArgs &a, hipStream_t s) {
     if (!a.x_bf16 || a.gamma || a.K % 256 != 0) return false;
-    const bool two = a.M >= 4096;
     switch (a.K / 256) {
-        case 10: if (two) launch_rows256_r<10, 2>(a, s); else launch_rows256_r<10, 1>(a, s); return true;
-        case 11: if (two) launch_rows256_r<11, 2>(a, s); else launch_rows256_r<11, 1>(a, s); return true;
+        case 4: launch_rows256_r<4, 1>(a, s); return true;
+        case 8: launch_rows256_r<8, 1>(a, s); return true;
+        case 10: launch_rows256_r<10, 1>(a, s); return true;
+        case 11: launch_rows256_r<11, 1>(a, s); return true;
         case 22: launch_rows256_r<22, 1>(a, s); return true;
         case 27: launch_rows256_r<27, 1>(a, s); return true;
         default: return false;

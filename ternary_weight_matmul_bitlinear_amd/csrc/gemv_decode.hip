@@ -85,7 +85,9 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
 
 // XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations.
 // TG: token rows per workgroup (1, 4, 8 or 16).  NW: waves per workgroup.
-template <int EPI, int XIN, bool OUT_BF16, int TG, int NW>
+// NI: 64-k chunks held per lane per pass (CB, or for one token the fewest of 1, 2, 4, 6, 8
+// that cover the row, so short rows neither hold nor request unused chunks).
+template <int EPI, int XIN, bool OUT_BF16, int TG, int NW, int NI>
 __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     constexpr int NT = 64 * NW;
     // long rows (8 waves): codes multiplied as they are, offset removed per token with the
@@ -112,18 +114,62 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     int sg = 0, n = r;
     if constexpr (EPI != EPI_GLU) {
         while (sg + 1 < p.nseg && n >= p.seg[sg].n) { n -= p.seg[sg].n; ++sg; }
+        // segment boundaries are multiples of the 4 rows of a wave (checked at launch), so the
+        // segment is wave-uniform and its fields come from scalar loads
+        sg = __builtin_amdgcn_readfirstlane(sg);
     }
     const int nn = rvalid ? n : 0;
     const uint32_t *w0 = p.seg[sg].packed + static_cast<int64_t>(nn) * (K / 16);
     const uint32_t *w1 = EPI == EPI_GLU ? p.seg[1].packed + static_cast<int64_t>(nn) * (K / 16) : nullptr;
-    uint4 wa[CB], wb[CB];
+    // One token: its activation row (bf16 to quantize, or pre-quantized codes) is requested
+    // before the weights.  Loads return in issue order, so a row fetched after the weights
+    // could only be quantized once every weight chunk had arrived; fetched first, the
+    // quantization overlaps the weight latency.  The weight and residual loads after it are
+    // unconditional (clamped addresses, unused values masked), which keeps the wait for the
+    // row exact.
+    constexpr bool EARLY = TG == 1 && XIN != 1;
+    constexpr int KEEP = TG == 1 ? (NW == 8 ? 4 : 3) : 0;
+    const bool keep = KEEP > 0 && K <= 8 * NT * KEEP;      // bf16 row held in registers
+    const bool qearly = EARLY && XIN == 0 && K <= 32 * NT;  // code row held in registers
+    uint4 xr[EARLY && XIN == 2 ? KEEP : 1];
+    uint4 qr[2];
+    // (requested whether or not the row fits the registers: clamped, in bounds, and unused
+    // when it does not; a conditional load here would make the compiler park it in scratch)
+    if constexpr (EARLY && XIN == 2) {
+#pragma unroll
+        for (int it = 0; it < KEEP; ++it) {
+            const int k0 = tid * 8 + 8 * NT * it;
+            xr[it] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + t0 * K + (k0 < K ? k0 : K - 8));
+        }
+    }
+    float a_early = 0.f;
+    int rs_early = 0;
+    if constexpr (EARLY && XIN == 0) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int k0 = tid * 16 + 16 * NT * it;
+            qr[it] = *reinterpret_cast<const uint4 *>(p.q + t0 * K + (k0 < K ? k0 : K - 16));
+        }
+        a_early = p.a[t0];
+        rs_early = p.rowsum[t0];
+    }
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
+    uint4 wa[NI], wb[NI];
     auto load_pass = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int c = base + j + LPR * i;
-            if (c < NC && rvalid) {
+        for (int i = 0; i < NI; ++i) {
+            if constexpr (EARLY) {
+                // every slot is requested (slots past the row end re-read its last chunk)
+                int c = base + j + LPR * i;
+                c = c < NC ? c : NC - 1;
                 wa[i] = *reinterpret_cast<const uint4 *>(w0 + c * 4);
                 if constexpr (EPI == EPI_GLU) wb[i] = *reinterpret_cast<const uint4 *>(w1 + c * 4);
+            } else {
+                const int c = base + j + LPR * i;
+                if (c < NC && rvalid) {
+                    wa[i] = *reinterpret_cast<const uint4 *>(w0 + c * 4);
+                    if constexpr (EPI == EPI_GLU) wb[i] = *reinterpret_cast<const uint4 *>(w1 + c * 4);
+                }
             }
         }
     };
@@ -134,9 +180,14 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     const int tj = j / STRIDE;
     float resid_v = 0.f;
     if constexpr (EPI == EPI_RESID) {
-        if (rvalid && j % STRIDE == 0 && tj < mt)
-            resid_v = load_act<OUT_BF16>(p.resid, (t0 + tj) * p.ldr + p.seg[sg].out_col0 + n);
+        if constexpr (EARLY) {
+            resid_v = load_act<OUT_BF16>(p.resid, t0 * p.ldr + p.seg[sg].out_col0 + nn);
+        } else {
+            if (rvalid && j % STRIDE == 0 && tj < mt)
+                resid_v = load_act<OUT_BF16>(p.resid, (t0 + tj) * p.ldr + p.seg[sg].out_col0 + n);
+        }
     }
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- prologue
     if constexpr (XIN != 0) {
@@ -145,11 +196,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
         // flight together
         constexpr bool BF = XIN == 2;
         float pm[TG], ps[TG];
-        // one token: its row (<= 3 x 8 values per thread for K <= 6144) stays in registers
-        // between the two passes
-        constexpr int KEEP = TG == 1 ? (NW == 8 ? 4 : 3) : 0;
+        // one token: its row (<= KEEP x 8 values per thread) stays in registers between the
+        // two passes
         float xk[KEEP > 0 ? KEEP : 1][8];
-        const bool keep = KEEP > 0 && K <= 8 * NT * KEEP;
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
             const int64_t tok = t0 + (t < mt ? t : mt - 1);
@@ -160,7 +209,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
                 for (int it = 0; it < KEEP; ++it) {
                     const int k0 = tid * 8 + 8 * NT * it;
                     if (k0 < K) {
-                        load8v<BF>(p.x, tok * K + k0, xk[it]);
+                        if constexpr (EARLY) {
+                            const uint32_t w[4] = {xr[it].x, xr[it].y, xr[it].z, xr[it].w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                xk[it][2 * e] = __uint_as_float(w[e] << 16);
+                                xk[it][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                            }
+                        } else {
+                            load8v<BF>(p.x, tok * K + k0, xk[it]);
+                        }
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float pj = p.gamma ? xk[it][e] * p.gamma[k0 + e] : xk[it][e];
@@ -258,7 +316,16 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
             if (cap_blk && p.cap.a && p.cap.row0 <= tok && tok < p.cap.row1) p.cap.a[tok - p.cap.row0] = s_a[t];
         }
     } else {
-        for (int k0 = tid * 16; k0 < K; k0 += 16 * NT) {
+        if (qearly) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int k0 = tid * 16 + 16 * NT * it;
+                // stored field by field: a whole-struct copy keeps qr in scratch memory
+                if (k0 < K)
+                    *reinterpret_cast<uint4 *>(qs + (k0 >> 6) * CS + (k0 & 63)) =
+                        make_uint4(qr[it].x, qr[it].y, qr[it].z, qr[it].w);
+            }
+        } else for (int k0 = tid * 16; k0 < K; k0 += 16 * NT) {
             uint4 v[TG];  // every token's 16 bytes requested before any is stored
 #pragma unroll
             for (int t = 0; t < TG; ++t)
@@ -267,8 +334,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
             for (int t = 0; t < TG; ++t) *reinterpret_cast<uint4 *>(qs + (k0 >> 6) * CS + 64 * t + (k0 & 63)) = v[t];
         }
         if (tid < mt) {
-            s_a[tid] = p.a[t0 + tid];
-            s_rs[tid] = p.rowsum[t0 + tid];
+            s_a[tid] = EARLY ? a_early : p.a[t0 + tid];
+            s_rs[tid] = EARLY ? rs_early : p.rowsum[t0 + tid];
         }
     }
     __syncthreads();
@@ -286,11 +353,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     int acc0[TG], acc1[TG];
 #pragma unroll
     for (int t = 0; t < TG; ++t) { acc0[t] = 0; acc1[t] = 0; }
-    for (int base = 0; base < NC; base += LPR * CB) {
+    for (int base = 0; base < NC; base += LPR * NI) {
         if (base > 0) load_pass(base);
         const int niter = (NC - base + LPR - 1) / LPR;  // chunk slots in use (uniform)
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
+        for (int i = 0; i < NI; ++i) {
             if (i >= niter) break;
             // chunk slots past the row end read as weight 0 against chunk 0 and add nothing
             const int c = base + j + LPR * i;
@@ -371,23 +438,31 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     }
 }
 
-template <int EPI, int XIN, int TG, int NW>
+template <int EPI, int XIN, int TG, int NW, int NI>
 void launch5(const GemvArgs &a, size_t lds, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>((a.rows_total + NW * RPW - 1) / (NW * RPW)),
                     static_cast<unsigned>((a.M + TG - 1) / TG));
-    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true, TG, NW>), grid, dim3(64 * NW), lds, s, a);
-    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false, TG, NW>), grid, dim3(64 * NW), lds, s, a);
+    if (a.out_bf16) hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, true, TG, NW, NI>), grid, dim3(64 * NW), lds, s, a);
+    else hipLaunchKernelGGL((gemv_dot4_kernel<EPI, XIN, false, TG, NW, NI>), grid, dim3(64 * NW), lds, s, a);
 }
 
 template <int EPI, int XIN, int TG>
 void launch4(const GemvArgs &a, size_t lds, hipStream_t s) {
     if constexpr (TG == 1) {
         if (a.K >= 8192) {
-            launch5<EPI, XIN, TG, 8>(a, lds, s);
+            launch5<EPI, XIN, TG, 8, CB>(a, lds, s);
             return;
         }
+        // one pass (K < 8192): chunks per lane = ceil(K / 64 / 16)
+        const int groups = (a.K / 64 + LPR - 1) / LPR;
+        if (groups <= 1) launch5<EPI, XIN, TG, 4, 1>(a, lds, s);
+        else if (groups <= 2) launch5<EPI, XIN, TG, 4, 2>(a, lds, s);
+        else if (groups <= 4) launch5<EPI, XIN, TG, 4, 4>(a, lds, s);
+        else if (groups <= 6) launch5<EPI, XIN, TG, 4, 6>(a, lds, s);
+        else launch5<EPI, XIN, TG, 4, CB>(a, lds, s);
+        return;
     }
-    launch5<EPI, XIN, TG, 4>(a, lds, s);
+    launch5<EPI, XIN, TG, 4, CB>(a, lds, s);
 }
 
 template <int EPI, int XIN>
@@ -414,6 +489,9 @@ size_t gemv_lds_bytes(int K, int tg) { return static_cast<size_t>(K / 64) * chun
 
 hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
     if (a_in.M <= 0) return hipSuccess;
+    if (a_in.epi != EPI_GLU)
+        for (int i = 0; i + 1 < a_in.nseg; ++i)
+            if (a_in.seg[i].n % RPW != 0) return hipErrorInvalidValue;  // segment not wave-aligned
     GemvArgs a = a_in;
     // token rows per workgroup: as many as the batch needs, up to 16, within 64 KB of LDS
     int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;

@@ -33,6 +33,12 @@ CASES = [
     # weight chunks at K = 16384)
     (1, 8192, 300, torch.bfloat16, True, True),
     (1, 16384, 130, torch.float32, False, False),
+    # one token, rows shorter than 8192: 1, 2, 4, 6 or 8 chunks per lane, ragged last group
+    (1, 1088, 96, torch.bfloat16, False, True),
+    (1, 2048, 6144, torch.bfloat16, False, False),
+    (1, 3136, 200, torch.float32, True, True),
+    (1, 5632, 2048, torch.bfloat16, False, False),
+    (1, 7232, 68, torch.bfloat16, True, False),
 ]
 
 

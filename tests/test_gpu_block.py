@@ -27,7 +27,8 @@ def _restore_regime():
                                             (64, 256, 704, torch.bfloat16, True),
                                             (300, 1024, 2816, torch.bfloat16, True),
                                             # one token, down projection over K = F = 8192
-                                            (1, 256, 8192, torch.bfloat16, True)])
+                                            (1, 256, 8192, torch.bfloat16, True),
+                                            (1, 1024, 2816, torch.bfloat16, True)])
 def test_glu_parity(orc, regime, M, D, F, dt, resid):
     note(f"glu regime={regime} M={M} D={D} F={F}")
     lat = small_latents(M + D, D, F)

@@ -38,6 +38,9 @@
 #ifndef MMF_UNPACK64
 #define MMF_UNPACK64 0
 #endif
+#ifndef MMF_GEMM_WN
+#define MMF_GEMM_WN 2
+#endif
 
 namespace mmf {
 
@@ -50,7 +53,8 @@ constexpr int B_BYTES = BN * BK / 4;      // 8 KB per stage
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int A_LOADS = A_BYTES / (NT * 16);  // direct 16-byte loads per thread per stage
 constexpr int B_LOADS = B_BYTES / (NT * 16);
-constexpr int MI = 2, NI = 4;
+constexpr int WN = MMF_GEMM_WN, WM = 4 / WN;  // waves along N and along M
+constexpr int MI = BM / 32 / WM, NI = BN / 32 / WN;  // 32 x 32 MFMA blocks per wave
 constexpr int EP_PITCH = 36;  // floats per staged epilogue row (32 + 4 pad)
 static_assert(A_LOADS == 4 && B_LOADS == 2, "load split");
 static_assert(NT / 64 * 32 * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue staging must fit");
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int K = p.K, KW = K / 16;  // words per packed row
 
     // ---- XCD-aware tile id: XCD x (= blockIdx % 8) owns a contiguous range of tiles
@@ -164,12 +168,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         const int row = s >> 1, h = (s & 1) ^ swz_b(row);
         int r;
         if constexpr (EPI == EPI_GLU) {
-            // tile column c: wave half wn = c / 128, block ni = (c % 128) / 32, lane j = c % 32;
+            // tile column c: wave wn = c / (32 NI), block ni = (c / 32) % NI, lane j = c % 32;
+            // the first NI/2 blocks of a wave are gate rows, the last NI/2 the same up rows;
             // the 32 rows of one load share the block, hence the matrix (gate or up)
             const int blk = wave * B_LOADS + i;
-            const int cwn = blk >> 2, cni = blk & 3;
-            const Seg &S = p.seg[cni >> 1];
-            const int f = nt * 128 + 64 * cwn + 32 * (cni & 1) + (row & 31);
+            const int cwn = blk / NI, cni = blk % NI;
+            const Seg &S = p.seg[cni / (NI / 2)];
+            const int f = nt * 128 + 16 * NI * cwn + 32 * (cni % (NI / 2)) + (row & 31);
             r = f < S.n ? f : S.n - 1;
             b_base[i] = S.packed;
         } else {
@@ -199,10 +204,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         }
     };
 
-    if (tid < BM) {
-        const int64_t r = m0 + tid < p.M ? m0 + tid : p.M - 1;
-        s_rs[tid] = p.rowsum[r];
-        s_a[tid] = p.a[r];
+    // per-row code sums and scales, needed only by the epilogue: requested before the first
+    // k-tiles so that the two latencies overlap, written to LDS after the k loop
+    // (every thread loads, threads past BM a duplicate row, so there is no branch)
+    int32_t rs_t;
+    float a_t;
+    {
+        const int64_t rr = m0 + (tid & (BM - 1));
+        const int64_t r = rr < p.M ? rr : p.M - 1;
+        rs_t = p.rowsum[r];
+        a_t = p.a[r];
     }
 
     v16i acc[MI][NI];
@@ -219,11 +230,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     int a_off[MI][4];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-        const int row = wm * 64 + mi * 32 + r32;
+        const int row = wm * (32 * MI) + mi * 32 + r32;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) a_off[mi][ks] = row * BK + 16 * ((4 * g + ks) ^ swz_a(row));
     }
-    const int brow = wn * 128 + r32;
+    const int brow = wn * (32 * NI) + r32;
     const int b_off = A_BYTES + brow * 32 + 16 * (g ^ swz_b(brow));
 
     // one k-tile: wait for it, free the oldest stage, refill it, multiply.  ST is static so
@@ -236,14 +247,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         barrier_nofence();  // every wave's part of tile kt is in LDS; stage kt-1 is free
         if (kt + 2 < nk) issue(kt + 2, (ST + 2) % STAGES);
         const int8_t *sa = smem + ST * STAGE_BYTES;
-        v4i av[MI][4];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) av[mi][ks] = *reinterpret_cast<const v4i *>(sa + a_off[mi][ks]);
+        // fragment reads in the order of first use (packed B words, then A for k-steps 0-1,
+        // then A for k-steps 2-3), so the first MFMAs wait only for the reads they consume
         uint4 bw[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) bw[ni] = *reinterpret_cast<const uint4 *>(sa + b_off + ni * 1024);
+        v4i av[MI][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) av[mi][ks] = *reinterpret_cast<const v4i *>(sa + a_off[mi][ks]);
         if (ragged && kt == nk - 1 && g) {
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) bw[ni] = make_uint4(0, 0, 0, 0);
@@ -276,6 +289,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         if (kt + 1 < nk) step(kt + 1, S1{});
         if (kt + 2 < nk) step(kt + 2, S2{});
     }
+    if (tid < BM) {
+        s_rs[tid] = rs_t;
+        s_a[tid] = a_t;
+    }
     __syncthreads();  // all waves are done with the ring before it is reused for staging
 
     // ---- epilogue.  A lane holds C[row][col] for col = r32 of each 32-wide block and rows
@@ -286,7 +303,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     //      accesses covering whole row segments.  The staging region is private to the
     //      wave, so only wave-level ordering is needed.
     float *stg = reinterpret_cast<float *>(smem) + wave * (32 * EP_PITCH);
-    constexpr int NOB = EPI == EPI_GLU ? 2 : NI;  // output blocks per 32-row slab
+    constexpr int NOB = EPI == EPI_GLU ? NI / 2 : NI;  // output blocks per 32-row slab
     // 16-byte accesses need 8-element-aligned row strides and column offsets
     const bool vec_ok = (p.ldo % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0) &&
                         (EPI == EPI_GLU || p.seg[sg].out_col0 % 8 == 0);
@@ -300,8 +317,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int rr = (lane >> 2) + 16 * i, cc = 8 * (lane & 3);
-                const int64_t row = m0 + wm * 64 + mi * 32 + rr;
-                const int col = nt * BN + wn * 128 + ob * 32 + cc;
+                const int64_t row = m0 + wm * (32 * MI) + mi * 32 + rr;
+                const int col = nt * BN + wn * (32 * NI) + ob * 32 + cc;
                 if (row < p.M && vec_ok && col + 8 <= p.seg[sg].n) {
                     const int64_t ri = row * p.ldr + p.seg[sg].out_col0 + col;
                     if constexpr (OUT_BF16) {
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         float a_e[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int lr = wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+            const int lr = wm * (32 * MI) + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
             rs_e[e] = s_rs[lr];
             a_e[e] = s_a[lr];
         }
@@ -330,9 +347,9 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
             // global column of this lane's value and of the block's first column
             int col0;
             if constexpr (EPI == EPI_GLU) {
-                col0 = nt * 128 + 64 * wn + 32 * ob;
+                col0 = nt * 128 + 16 * NI * wn + 32 * ob;
             } else {
-                col0 = nt * BN + wn * 128 + ob * 32;
+                col0 = nt * BN + wn * (32 * NI) + ob * 32;
             }
             const int col_lane = col0 + r32;
             const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
@@ -345,7 +362,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                 const float bu = p.seg[1].bias && col_lane < ncols ? p.seg[1].bias[col_lane] : 0.0f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int32_t ag_ = acc[mi][ob][e] - rs_e[e], au = acc[mi][ob + 2][e] - rs_e[e];
+                    const int32_t ag_ = acc[mi][ob][e] - rs_e[e], au = acc[mi][ob + NI / 2][e] - rs_e[e];
                     const float yg = static_cast<float>(ag_) * (sg0 * a_e[e]) + bg;
                     const float yu = static_cast<float>(au) * (su * a_e[e]) + bu;
                     v[e] = siluf_(yg) * yu;
@@ -361,12 +378,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
             if (p.cap.acc) {  // integer accumulators of captured rows (rare; test protocol)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int64_t row = m0 + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int64_t row = m0 + wm * (32 * MI) + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                     if (row < p.M && col_lane < ncols && p.cap.row0 <= row && row < p.cap.row1) {
                         int32_t *c = p.cap.acc + (row - p.cap.row0) * p.cap.acc_ld;
                         if constexpr (EPI == EPI_GLU) {
                             c[p.seg[0].cap_col0 + col_lane] = acc[mi][ob][e] - rs_e[e];
-                            c[p.seg[1].cap_col0 + col_lane] = acc[mi][ob + 2][e] - rs_e[e];
+                            c[p.seg[1].cap_col0 + col_lane] = acc[mi][ob + NI / 2][e] - rs_e[e];
                         } else {
                             c[S.cap_col0 + col_lane] = acc[mi][ob][e] - rs_e[e];
                         }
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int rr = (lane >> 2) + 16 * i, cc = 8 * (lane & 3);
-                const int64_t row = m0 + wm * 64 + mi * 32 + rr;
+                const int64_t row = m0 + wm * (32 * MI) + mi * 32 + rr;
                 const int col = col0 + cc;  // column inside the segment
                 const float4 lo = *reinterpret_cast<const float4 *>(stg + rr * EP_PITCH + cc);
                 const float4 hi = *reinterpret_cast<const float4 *>(stg + rr * EP_PITCH + cc + 4);

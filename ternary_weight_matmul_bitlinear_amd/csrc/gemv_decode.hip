@@ -31,6 +31,8 @@
 // chunks read by one instruction on distinct bank quads.
 #include "mmf_internal.h"
 
+#include <type_traits>
+
 namespace mmf {
 
 namespace {
@@ -83,7 +85,9 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
     return acc;
 }
 
-// XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations.
+// XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations, 3 = one MLGRU
+// step computed from the i|f|g pre-activations and the carried state (o_proj of one token;
+// activations in the output dtype).
 // TG: token rows per workgroup (1, 4, 8 or 16).  NW: waves per workgroup.
 // NI: 64-k chunks held per lane per pass (CB, or for one token the fewest of 1, 2, 4, 6, 8
 // that cover the row, so short rows neither hold nor request unused chunks).
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     // needs no code sum (no extra reduction before the dot products)
     constexpr bool UNS = NW == 8;
     extern __shared__ __attribute__((aligned(16))) int8_t qs[];
-    __shared__ float red_m[NW][TG], red_s[NW][TG];
+    __shared__ float red_m[NW][TG], red_s[NW][TG], red_h[NW];
     __shared__ int red_q[NW][TG];
     __shared__ float s_a[TG];
     __shared__ int s_rs[TG];
@@ -140,6 +144,42 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
         for (int it = 0; it < KEEP; ++it) {
             const int k0 = tid * 8 + 8 * NT * it;
             xr[it] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + t0 * K + (k0 < K ? k0 : K - 8));
+        }
+    }
+    // one MLGRU step (XIN 3): the token's i, f, g pre-activations, carried state, forget-gate
+    // bias and g_norm gain for this thread's KF groups of 8 channels
+    constexpr int KF = XIN == 3 ? (NI <= 2 ? 1 : 2) : 1;
+    using RawAct = typename std::conditional<OUT_BF16, uint4, float4[2]>::type;
+    RawAct ri[KF], rf[KF], rg[KF];
+    float4 rh[KF][2], rb[KF][2], rw[KF][2];
+    if constexpr (XIN == 3) {
+        auto ld_act = [&](int64_t e, RawAct &dst) __attribute__((always_inline)) {
+            if constexpr (OUT_BF16) {
+                dst = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + e);
+            } else {
+                dst[0] = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e);
+                dst[1] = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + e + 4);
+            }
+        };
+        auto ld_par = [&](const float *src, int k, float4 (&dst)[2], float dflt) __attribute__((always_inline)) {
+            if (src) {
+                dst[0] = *reinterpret_cast<const float4 *>(src + k);
+                dst[1] = *reinterpret_cast<const float4 *>(src + k + 4);
+            } else {
+                dst[0] = dst[1] = make_float4(dflt, dflt, dflt, dflt);
+            }
+        };
+#pragma unroll
+        for (int it = 0; it < KF; ++it) {
+            int k0 = tid * 8 + 8 * NT * it;
+            k0 = k0 < K ? k0 : K - 8;
+            const int64_t base = t0 * 3 * static_cast<int64_t>(K) + k0;
+            ld_act(base, ri[it]);
+            ld_act(base + K, rf[it]);
+            ld_act(base + 2 * K, rg[it]);
+            ld_par(p.h_prev ? p.h_prev + t0 * K : nullptr, k0, rh[it], 0.0f);
+            ld_par(p.f_bias, k0, rb[it], 0.0f);
+            ld_par(p.gnorm_w, k0, rw[it], 1.0f);
         }
     }
     float a_early = 0.f;
@@ -199,6 +239,77 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
         // one token: its row (<= KEEP x 8 values per thread) stays in registers between the
         // two passes
         float xk[KEEP > 0 ? KEEP : 1][8];
+        if constexpr (XIN == 3) {
+            // DataCamp "MatMul-free language models", "Core components: MLGRU and GLU";
+            // Hysen Labs "MatMul-Free LM", "HGRN attention" (g_norm):
+            //   f = sigmoid(f_pre + b_f), h_t = f*h_{t-1} + (1-f)*SiLU(i_pre),
+            //   o = RMSNorm_D(h_t)*gnorm_w * g*sigmoid(g)  (gate mode 1: sigmoid(g)*h_t);
+            // o is then quantized below as o_proj's input.  Workgroup 0 writes h_t.
+            auto cvt8 = [&](const RawAct &r, float (&v)[8]) __attribute__((always_inline)) {
+                if constexpr (OUT_BF16) {
+                    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] = __uint_as_float(w[e] << 16);
+                        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                    }
+                } else {
+                    v[0] = r[0].x; v[1] = r[0].y; v[2] = r[0].z; v[3] = r[0].w;
+                    v[4] = r[1].x; v[5] = r[1].y; v[6] = r[1].z; v[7] = r[1].w;
+                }
+            };
+            auto f8 = [](const float4 (&r)[2], float (&v)[8]) __attribute__((always_inline)) {
+                v[0] = r[0].x; v[1] = r[0].y; v[2] = r[0].z; v[3] = r[0].w;
+                v[4] = r[1].x; v[5] = r[1].y; v[6] = r[1].z; v[7] = r[1].w;
+            };
+            float hsum[1] = {0.f};
+#pragma unroll
+            for (int it = 0; it < KF; ++it) {
+                const int k0 = tid * 8 + 8 * NT * it;
+                float iv[8], fv[8], hv[8], bv[8];
+                cvt8(ri[it], iv);
+                cvt8(rf[it], fv);
+                f8(rh[it], hv);
+                f8(rb[it], bv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = sigmoidf_(fv[e] + bv[e]);
+                    hv[e] = f * hv[e] + (1.0f - f) * siluf_(iv[e]);
+                }
+                if (k0 < K) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        hsum[0] = fmaf(hv[e], hv[e], hsum[0]);
+                        xk[it][e] = hv[e];
+                    }
+                    if (blockIdx.x == 0 && p.h_new) {
+                        float *hd = p.h_new + t0 * K + k0;
+                        *reinterpret_cast<float4 *>(hd) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                        *reinterpret_cast<float4 *>(hd + 4) = make_float4(hv[4], hv[5], hv[6], hv[7]);
+                    }
+                }
+            }
+            const float hw = wave_reduce_multi<1, false>(hsum);
+            if (lane == 0) red_h[wave] = hw;
+            __syncthreads();
+            float htot = red_h[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) htot += red_h[w];
+            const float r = 1.0f / sqrtf(htot * (1.0f / static_cast<float>(K)) + p.g_eps);
+#pragma unroll
+            for (int it = 0; it < KF; ++it) {
+                const int k0 = tid * 8 + 8 * NT * it;
+                if (k0 < K) {
+                    float gv[8], gw[8];
+                    cvt8(rg[it], gv);
+                    f8(rw[it], gw);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        xk[it][e] = p.gate_mode == 0 ? xk[it][e] * r * gw[e] * siluf_(gv[e])
+                                                     : sigmoidf_(gv[e]) * xk[it][e];
+                }
+            }
+        }
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
             const int64_t tok = t0 + (t < mt ? t : mt - 1);
@@ -209,7 +320,9 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
                 for (int it = 0; it < KEEP; ++it) {
                     const int k0 = tid * 8 + 8 * NT * it;
                     if (k0 < K) {
-                        if constexpr (EARLY) {
+                        if constexpr (XIN == 3) {
+                            // xk holds the gated MLGRU output
+                        } else if constexpr (EARLY) {
                             const uint32_t w[4] = {xr[it].x, xr[it].y, xr[it].z, xr[it].w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -400,6 +513,11 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     int my0 = wave_reduce_multi<TG, false, int, LPR>(acc0);
     int my1 = 0;
     if constexpr (EPI == EPI_GLU) my1 = wave_reduce_multi<TG, false, int, LPR>(acc1);
+    if (p.copy_n > 0 && blockIdx.y == 0) {  // side copy (after the weights are consumed)
+        const int64_t i = (static_cast<int64_t>(blockIdx.x) * NT + tid) * 4;
+        if (i < p.copy_n)
+            *reinterpret_cast<float4 *>(p.copy_dst + i) = *reinterpret_cast<const float4 *>(p.copy_src + i);
+    }
     if (!rvalid || j % STRIDE != 0) return;
     if (tj >= mt) return;
     if constexpr (UNS) {
@@ -477,6 +595,15 @@ void launch3(const GemvArgs &a, size_t lds, hipStream_t s) {
 
 template <int EPI>
 void launch2(const GemvArgs &a, size_t lds, hipStream_t s) {
+    if constexpr (EPI == EPI_RESID) {
+        if (a.mlgru) {  // one token, K <= 4096 (checked by launch_gemv): 1, 2 or 4 chunks per lane
+            const int groups = (a.K / 64 + LPR - 1) / LPR;
+            if (groups <= 1) launch5<EPI, 3, 1, 4, 1>(a, lds, s);
+            else if (groups <= 2) launch5<EPI, 3, 1, 4, 2>(a, lds, s);
+            else launch5<EPI, 3, 1, 4, 4>(a, lds, s);
+            return;
+        }
+    }
     if (!a.x) launch3<EPI, 0>(a, lds, s);
     else if (a.x_bf16) launch3<EPI, 2>(a, lds, s);
     else launch3<EPI, 1>(a, lds, s);
@@ -492,6 +619,10 @@ hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
     if (a_in.epi != EPI_GLU)
         for (int i = 0; i + 1 < a_in.nseg; ++i)
             if (a_in.seg[i].n % RPW != 0) return hipErrorInvalidValue;  // segment not wave-aligned
+    if (a_in.mlgru && (a_in.epi != EPI_RESID || a_in.M != 1 || a_in.K > 4096 || !a_in.x ||
+                       a_in.x_bf16 != a_in.out_bf16))
+        return hipErrorInvalidValue;  // the fused MLGRU step covers one token, D <= 4096
+    if (a_in.copy_n % 4 != 0) return hipErrorInvalidValue;
     GemvArgs a = a_in;
     // token rows per workgroup: as many as the batch needs, up to 16, within 64 KB of LDS
     int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;

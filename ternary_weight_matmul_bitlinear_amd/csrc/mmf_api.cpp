@@ -231,12 +231,39 @@ static hipError_t gemm(const QBuf &qb, int64_t M, int32_t K, const Seg *segs, in
     return launch_gemm(ga, s);
 }
 
+// Extras of a decode GEMV: the fused MLGRU step of o_proj and a side copy of the state.
+struct GemvExtra {
+    const float *h_prev = nullptr;
+    float *h_new = nullptr;
+    const float *f_bias = nullptr;
+    const float *gnorm_w = nullptr;
+    float g_eps = 0.f;
+    int32_t gate_mode = 0;
+    bool mlgru = false;
+    const float *copy_src = nullptr;
+    float *copy_dst = nullptr;
+    int32_t copy_n = 0;
+};
+
 // Decode GEMV, from raw activations (x != NULL) or from quantized rows.
 static hipError_t gemv(const void *x, bool x_bf16, const float *gamma, float eps, const QBuf *qb,
                        int64_t M, int32_t K, const Seg *segs, int nseg, int epi, void *out,
                        int32_t ldo, bool out_bf16, const void *resid, int32_t ldr,
-                       const mmf_stage_capture *cap, int32_t cap_ld, hipStream_t s) {
+                       const mmf_stage_capture *cap, int32_t cap_ld, hipStream_t s,
+                       const GemvExtra *ex = nullptr) {
     GemvArgs ga{};
+    if (ex) {
+        ga.mlgru = ex->mlgru;
+        ga.h_prev = ex->h_prev;
+        ga.h_new = ex->h_new;
+        ga.f_bias = ex->f_bias;
+        ga.gnorm_w = ex->gnorm_w;
+        ga.g_eps = ex->g_eps;
+        ga.gate_mode = ex->gate_mode;
+        ga.copy_src = ex->copy_src;
+        ga.copy_dst = ex->copy_dst;
+        ga.copy_n = ex->copy_n;
+    }
     ga.x = x;
     ga.x_bf16 = x_bf16;
     ga.gamma = gamma;
@@ -536,7 +563,8 @@ size_t block_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) {
     if (!w || B <= 0 || T <= 0) return 0;
     const int64_t M = B * T, D = w->i.K, F = w->gate.N;
     return qbuf_bytes(M, std::max(D, F)) + align_up(static_cast<size_t>(M * std::max(3 * D, F)) * 4) +
-           align_up(static_cast<size_t>(M * D) * 4) + scan_bytes(B, T, D);
+           align_up(static_cast<size_t>(M * D) * 4) + scan_bytes(B, T, D) +
+           (M == 1 ? align_up(static_cast<size_t>(D) * 4) : 0);  // new state of a fused step
 }
 
 int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
@@ -581,6 +609,35 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
         if (e == hipSuccess) e = gemm(qb, M, D, ifg, 3, EPI_STORE, act, 3 * D, bf, nullptr, 0, c_ifg, 3 * D, FAM_GEMM_IFG, stream);
     }
     if (e != hipSuccess) return hip_error(e, "block_forward ifg launch");
+
+    if (decode && M == 1) {
+        // one token: the MLGRU step, g_norm and o_proj's quantization run in the o_proj
+        // kernel's prologue (every workgroup recomputes the D-wide step; workgroup 0 writes
+        // the new state to the workspace, and the gate|up kernel, which runs after every
+        // reader of the old state has finished, copies it into h_state)
+        float *h_tmp = h_state ? c.take<float>(static_cast<size_t>(D) * 4) : nullptr;
+        GemvExtra eo;
+        eo.mlgru = true;
+        eo.h_prev = h_state;
+        eo.h_new = h_tmp;
+        eo.f_bias = w->f_bias;
+        eo.gnorm_w = w->gnorm_w;
+        eo.g_eps = w->eps;
+        eo.gate_mode = w->gate_mode;
+        e = gemv(act, bf, w->o.norm_w, w->o.eps, nullptr, M, D, &so, 1, EPI_RESID, y1, D, bf, x, D, c_o, D, stream, &eo);
+        if (e != hipSuccess) return hip_error(e, "block_forward o_proj launch");
+        GemvExtra eg;
+        if (h_state) {
+            eg.copy_src = h_tmp;
+            eg.copy_dst = h_state;
+            eg.copy_n = D;
+        }
+        e = gemv(y1, bf, w->gate.norm_w, w->gate.eps, nullptr, M, D, gu, 2, EPI_GLU, act, F, bf, nullptr, 0, c_gu, 2 * F, stream, &eg);
+        if (e == hipSuccess)
+            e = gemv(act, bf, w->down.norm_w, w->down.eps, nullptr, M, F, &dn, 1, EPI_RESID, y, D, bf, y1, D, c_dn, D, stream);
+        if (e != hipSuccess) return hip_error(e, "block_forward glu launch");
+        return MMF_OK;
+    }
 
     // 3: MLGRU + g_norm, quantized from fp32 for o_proj
     ScanArgs s{};

@@ -234,6 +234,19 @@ struct GemvArgs {
     int32_t ldr;
     int32_t tokens_per_group;  // rows of q staged in LDS per workgroup (<= kGemvTokens)
     CapDev cap;            // x_in/q/a written by column-block 0, acc by every block
+    // one MLGRU step as the input (mlgru != 0, one token, K = D <= 4096): x is the token's
+    // i|f|g pre-activations [3D] in the output dtype; gamma/eps are o_proj's
+    int32_t mlgru;
+    const float *h_prev;   // [D] carried state (NULL: zeros)
+    float *h_new;          // [D] new state, written by column-block 0 (NULL: not kept)
+    const float *f_bias;   // [D] or NULL
+    const float *gnorm_w;  // [D] or NULL (ones)
+    float g_eps;
+    int32_t gate_mode;
+    // optional side copy of copy_n floats (a multiple of 4), done by the first workgroups
+    const float *copy_src;
+    float *copy_dst;
+    int32_t copy_n;
 };
 
 // MLGRU scan.

@@ -118,6 +118,37 @@ def test_block_decode_steps_match_prefill(orc):
     e2e_checks(host(y_dec), r["y"], True, got_h=host(h), ref_h=r["h_last"])
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("gate_mode", [0, 1])
+@pytest.mark.parametrize("D,F", [(256, 704), (4096, 256)])
+def test_block_one_token_steps(orc, dt, gate_mode, D, F):
+    """One-token decode steps, whose MLGRU step, g_norm and o_proj quantization run in the
+    o_proj kernel: each step is stage-checked from its capture against the oracle started
+    from the carried state, and the sequence of steps matches the oracle's block end to end.
+    D = 256 and 4096 give one and four 64-channel chunks per lane."""
+    B, T = 1, 6
+    note(f"block one-token steps dt={dt} gate={gate_mode} D={D}")
+    blk, W, x, fb, gw = _block_case(orc, D, F, B, T, dt, 41, gate_mode, f_bias=0.3, use_gains=True)
+    bf = dt == torch.bfloat16
+    xd = dev(x, dt)
+    api.set_regime(1)
+    h = torch.zeros((B, D), device="cuda")
+    ys = []
+    for t in range(T):
+        h_prev = host(h).copy()
+        cap = api.BlockCapture.alloc(0, 1, D, F)
+        y = api.block_forward(blk, xd[:, t:t + 1].contiguous(), h_state=h, capture=cap)
+        torch.cuda.synchronize()
+        ch = {k: getattr(cap, k).host() for k in ("ifg", "o", "gateup", "down")}
+        block_stage_checks(orc, ch, W, x[:, t:t + 1], bf, seq_rows=(1, 1), f_bias=fb,
+                           gnorm_w=gw, gate_mode=gate_mode, h0=h_prev, h_last=host(h),
+                           y_rows=host(y))
+        ys.append(y)
+    y_dec = torch.cat(ys, dim=1)
+    r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf)
+    e2e_checks(host(y_dec), r["y"], bf, got_h=host(h), ref_h=r["h_last"])
+
+
 def test_block_ragged_chunks_and_inplace(orc):
     """T not a multiple of the scan chunk, several sequences, y written over x."""
     D, F, B, T = 512, 1408, 3, 77

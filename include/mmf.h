@@ -90,7 +90,8 @@ typedef struct mmf_bitlinear {
 
 /* One block ([HL-hgrn], [DC-core]).  i, f, g, o: [D][D]; gate, up: [F][D]; down: [D][F].
  * i, f, g must share norm_w (same pointer or all NULL) and eps, as must gate and up: each
- * group quantizes its shared input once. */
+ * group quantizes its shared input once.  f_bias, gnorm_w and o.norm_w are read 16 bytes at
+ * a time and must be 16-byte aligned (MMF_EALIGN). */
 typedef struct mmf_block {
     mmf_bitlinear i, f, g, o, gate, up, down;
     const float *f_bias;  /* device [D] forget-gate bias, or NULL (zeros) */
@@ -185,7 +186,7 @@ typedef struct mmf_mlgru_args {
     const float *f_bias;   /* [D] or NULL */
     const float *h0;       /* [B][D] fp32 initial state, or NULL (zeros) */
     float *h_out;          /* [B][D] fp32 final state h_T, or NULL; may equal h0 */
-    const float *gnorm_w;  /* [D] or NULL */
+    const float *gnorm_w;  /* [D] or NULL; every pointer 16-byte aligned (MMF_EALIGN) */
     float eps;
     int32_t gate_mode;     /* mmf_gate_mode */
     void *out;             /* [B][T][D] gated output (out_dt) */

@@ -439,6 +439,9 @@ int mlgru_scan(const mmf_mlgru_args *a, void *ws, size_t ws_bytes, hipStream_t s
     const int64_t M = a->B * a->T;
     if (M > 0 && (!a->ifg || !a->out)) return set_error(MMF_EINVAL, "mlgru_scan: NULL ifg or out");
     if (M > 0 && (!aligned16(a->ifg) || !aligned16(a->out))) return set_error(MMF_EALIGN, "mlgru_scan: ifg/out not 16-byte aligned");
+    if ((a->h0 && !aligned16(a->h0)) || (a->h_out && !aligned16(a->h_out)) ||
+        (a->f_bias && !aligned16(a->f_bias)) || (a->gnorm_w && !aligned16(a->gnorm_w)))
+        return set_error(MMF_EALIGN, "mlgru_scan: h0/h_out/f_bias/gnorm_w not 16-byte aligned");
     const size_t need = mlgru_workspace_bytes(a->B, a->T, a->D);
     if (need && (!ws || ws_bytes < need)) return set_error(MMF_EWORKSPACE, "mlgru_scan: workspace %zu < %zu", ws ? ws_bytes : 0, need);
     if ((rc = check_device())) return rc;
@@ -556,6 +559,10 @@ static int check_block(const mmf_block *w, const char *who) {
         return set_error(MMF_EINVAL, "%s: i, f, g must share norm_w and eps", who);
     if (w->gate_mode != MMF_GATE_SWISH_RMSNORM && w->gate_mode != MMF_GATE_SIGMOID) return set_error(MMF_EINVAL, "%s: gate_mode %d", who, w->gate_mode);
     if (!(w->eps >= 0.0f)) return set_error(MMF_EINVAL, "%s: eps", who);
+    // per-channel vectors are read 16 bytes at a time
+    if ((w->f_bias && !aligned16(w->f_bias)) || (w->gnorm_w && !aligned16(w->gnorm_w)) ||
+        (w->o.norm_w && !aligned16(w->o.norm_w)))
+        return set_error(MMF_EALIGN, "%s: f_bias/gnorm_w/o.norm_w not 16-byte aligned", who);
     return MMF_OK;
 }
 
@@ -581,6 +588,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     if (M == 0) return MMF_OK;  // h_T = h_0 already in place
     if (!x || !y) return set_error(MMF_EINVAL, "block_forward: NULL x or y");
     if (!aligned16(x) || !aligned16(y)) return set_error(MMF_EALIGN, "block_forward: x/y not 16-byte aligned");
+    if (h_state && !aligned16(h_state)) return set_error(MMF_EALIGN, "block_forward: h_state not 16-byte aligned");
     const size_t need = block_workspace_bytes(w, B, T);
     if (!ws || ws_bytes < need) return set_error(MMF_EWORKSPACE, "block_forward: workspace %zu < %zu", ws ? ws_bytes : 0, need);
     if (!aligned16(ws)) return set_error(MMF_EALIGN, "block_forward: workspace not 16-byte aligned");
@@ -741,6 +749,7 @@ int stack_forward(const mmf_stack *s, const int32_t *ids, const void *x, mmf_dty
     const int64_t M = B * T;
     if (M == 0) return MMF_OK;
     if ((x && !aligned16(x)) || (y && !aligned16(y)) || (logits && !aligned16(logits))) return set_error(MMF_EALIGN, "stack_forward: x/y/logits not 16-byte aligned");
+    if (h_state && !aligned16(h_state)) return set_error(MMF_EALIGN, "stack_forward: h_state not 16-byte aligned");
     const size_t need = stack_workspace_bytes(s, B, T);
     if (!ws || ws_bytes < need) return set_error(MMF_EWORKSPACE, "stack_forward: workspace %zu < %zu", ws ? ws_bytes : 0, need);
     if (!aligned16(ws)) return set_error(MMF_EALIGN, "stack_forward: workspace not 16-byte aligned");

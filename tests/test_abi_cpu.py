@@ -155,6 +155,15 @@ def test_block_validation_codes(lib):
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE, need - 1, None, None) == -5
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE + 8, need, None, None) == -3
     assert f(C.byref(_block()), None, 1, 0, 64, None, None, None, 0, None, None) == 0
+    # state and per-channel vectors are read 16 bytes at a time
+    h_bad = FAKE + 4
+    assert f(C.byref(_block()), FAKE, 1, 1, 64, h_bad, FAKE, FAKE, ws, None, None) == -3
+    b = _block()
+    b.f_bias = h_bad
+    assert f(C.byref(b), FAKE, 1, 1, 64, None, FAKE, FAKE, ws, None, None) == -3
+    b = _block()
+    b.gnorm_w = h_bad
+    assert f(C.byref(b), FAKE, 1, 1, 64, None, FAKE, FAKE, ws, None, None) == -3
     cap = L.mmf_capture(L.mmf_stage_capture(5, 2, None, None, None, None, None),
                         *[L.mmf_stage_capture(0, 0, None, None, None, None, None)] * 3)
     assert f(C.byref(_block()), FAKE, 1, 1, 64, None, FAKE, FAKE, ws, C.byref(cap), None) == -1
@@ -173,6 +182,9 @@ def test_mlgru_and_glu_validation_codes(lib):
     need = lib.mlgru_workspace_bytes(2, 64, 256)
     assert need > 0
     assert lib.mlgru_scan(C.byref(a), FAKE, need - 1, None) == -5
+    a.h0 = FAKE + 4
+    assert lib.mlgru_scan(C.byref(a), FAKE, need, None) == -3
+    a.h0 = None
     g, u, d = _bl(256, 704), _bl(256, 704), _bl(704, 256)
     assert lib.glu_forward(C.byref(g), C.byref(u), C.byref(_bl(512, 256)), FAKE, 0, 4, None, FAKE,
                            FAKE, 1 << 20, None, None) == -2

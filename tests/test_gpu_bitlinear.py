@@ -39,6 +39,12 @@ CASES = [
     (1, 3136, 200, torch.float32, True, True),
     (1, 5632, 2048, torch.bfloat16, False, False),
     (1, 7232, 68, torch.bfloat16, True, False),
+    # two to four tokens, bf16: the group's rows held in registers (1, 4, 6 or 8 chunks per
+    # lane of weights, 1-4 slices of the row per thread), ragged rows and groups
+    (4, 320, 96, torch.bfloat16, False, True),
+    (2, 2048, 200, torch.bfloat16, True, False),
+    (4, 5632, 300, torch.bfloat16, True, True),
+    (3, 7232, 130, torch.bfloat16, False, False),
 ]
 
 

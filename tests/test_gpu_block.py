@@ -120,14 +120,15 @@ def test_block_decode_steps_match_prefill(orc):
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("gate_mode", [0, 1])
-@pytest.mark.parametrize("D,F", [(256, 704), (4096, 256)])
-def test_block_one_token_steps(orc, dt, gate_mode, D, F):
-    """One-token decode steps, whose MLGRU step, g_norm and o_proj quantization run in the
-    o_proj kernel: each step is stage-checked from its capture against the oracle started
+@pytest.mark.parametrize("B,D,F", [(1, 256, 704), (1, 4096, 256), (3, 256, 704), (4, 2048, 256)])
+def test_block_one_token_steps(orc, dt, gate_mode, B, D, F):
+    """Decode steps of B sequences (one sequence: the MLGRU step, g_norm and o_proj
+    quantization run in the o_proj kernel; 3-4 sequences: scan kernel and four-token
+    weight streaming): each step is stage-checked from its capture against the oracle started
     from the carried state, and the sequence of steps matches the oracle's block end to end.
-    D = 256 and 4096 give one and four 64-channel chunks per lane."""
-    B, T = 1, 6
-    note(f"block one-token steps dt={dt} gate={gate_mode} D={D}")
+    D = 256, 2048 and 4096 give one, two and four 64-channel chunks per lane."""
+    T = 6
+    note(f"block decode steps B={B} dt={dt} gate={gate_mode} D={D}")
     blk, W, x, fb, gw = _block_case(orc, D, F, B, T, dt, 41, gate_mode, f_bias=0.3, use_gains=True)
     bf = dt == torch.bfloat16
     xd = dev(x, dt)
@@ -136,17 +137,20 @@ def test_block_one_token_steps(orc, dt, gate_mode, D, F):
     ys = []
     for t in range(T):
         h_prev = host(h).copy()
-        cap = api.BlockCapture.alloc(0, 1, D, F)
+        cap = api.BlockCapture.alloc(0, B, D, F)
         y = api.block_forward(blk, xd[:, t:t + 1].contiguous(), h_state=h, capture=cap)
         torch.cuda.synchronize()
         ch = {k: getattr(cap, k).host() for k in ("ifg", "o", "gateup", "down")}
-        block_stage_checks(orc, ch, W, x[:, t:t + 1], bf, seq_rows=(1, 1), f_bias=fb,
+        block_stage_checks(orc, ch, W, x[:, t:t + 1], bf, seq_rows=(B, 1), f_bias=fb,
                            gnorm_w=gw, gate_mode=gate_mode, h0=h_prev, h_last=host(h),
                            y_rows=host(y))
         ys.append(y)
     y_dec = torch.cat(ys, dim=1)
     r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf)
-    e2e_checks(host(y_dec), r["y"], bf, got_h=host(h), ref_h=r["h_last"])
+    # run level: an int8 code that flips where fp32 and fp64 straddle a rounding point (rate
+    # ~1e-5 per code) feeds the carried state of every later step, so over 6 steps of several
+    # sequences the fp32 run is held to the bf16 bound; each step met the fp32 bar above
+    e2e_checks(host(y_dec), r["y"], bf or B > 1, got_h=host(h), ref_h=r["h_last"])
 
 
 def test_block_ragged_chunks_and_inplace(orc):

@@ -60,11 +60,32 @@ def cpu_baseline(w, x_np, W, B0: int, T0: int):
     return r, dt, orc.max_threads()
 
 
+def spin_up(fn, seconds: float) -> None:
+    """Untimed steps for `seconds` of wall time: the GPU reaches its steady clock only under
+    sustained load, which a handful of warm-up steps of a few hundred microseconds each does
+    not provide (the 370M block measured 0.37 ms/step after 5 steps, 0.33 after ~100)."""
+    if seconds <= 0:
+        return
+    import torch
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    per = max(time.perf_counter() - t0, 1e-6)
+    batch = max(1, min(50, int(0.02 / per)))  # ~20 ms of queued work between host checks
+    t_end = t0 + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spin-up", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", default="370M-block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=128,
@@ -109,6 +130,7 @@ def main() -> int:
     print(f"# workload {w.name}: B={w.B} T={w.T} D={D} F={F} dtype={dt}", file=sys.stderr,
           flush=True)
 
+    spin_up(lambda: api.block_forward(blk, x, h_state=h, y=y, ws=ws), args.spin_up)
     for _ in range(args.warmup):
         h.zero_()
         api.block_forward(blk, x, h_state=h, y=y, ws=ws)
@@ -308,6 +330,7 @@ def bench_stack(args, w) -> int:
             hs.zero_()
             api.stack_forward(stack, B, T, x=x, ws=ws, y=y)
 
+    spin_up(lambda: step(0), args.spin_up)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -12,10 +12,18 @@
 //   - 16 lanes per weight row, 4 rows per wave, 16 rows per workgroup (32 for one token and
 //     rows of 8192 or more, so the row is quantized half as often); lane j of a row
 //     holds 16-byte chunks j, j+16, ... (64 k each) of the row in registers, and all of
-//     them are requested at kernel entry, before the activations are looked at;
+//     them are requested at kernel entry;
+//   - loads return in issue order, so for one token and for groups of up to four bf16
+//     tokens the activation rows (or the pre-quantized codes with their scale and code
+//     sum) are requested first, held in registers, and the weight and residual requests
+//     that follow are unconditional (clamped addresses) so every wait is exact; the number
+//     of chunks per lane is a template parameter (1, 2, 4, 6 or 8), so a short row neither
+//     holds nor requests unused chunks;
 //   - meanwhile the workgroup RMS/absmax-quantizes its token group (<= TG rows) into LDS
 //     (the same arithmetic as the standalone quantizer, so the int8 codes are identical),
-//     or copies rows that are already quantized;
+//     or copies rows that are already quantized; for o_proj of one token the prologue
+//     first runs the MLGRU step and g_norm from the i|f|g pre-activations and the carried
+//     state (XIN 3);
 //   - each packed word gives four dwords of 2-bit codes c = q + 1 ((w >> 2a) & 0x03030303),
 //     which one v_perm_b32 each maps to signed int8 weights (code 0,1,2 -> -1,0,+1),
 //     consumed by v_dot4_i32_i8 against the LDS-resident activations: the int32 result is

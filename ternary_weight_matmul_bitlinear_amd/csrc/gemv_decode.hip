@@ -50,6 +50,7 @@ constexpr int RPW = 64 / LPR;    // rows per wave
 // rows per workgroup: NW waves of RPW rows (4 waves, or 8 for one token with K >= 8192:
 // the activation row is then quantized once per 32 rows instead of once per 16)
 constexpr int CB = 8;            // 64-k chunks held per lane per pass (K <= 8192 in one pass)
+constexpr int kStreamRows = 16384;  // one token and at least this many rows: streaming kernel
 
 __host__ __device__ __forceinline__ int chunk_stride(int tg) { return 64 * tg + 16; }
 
@@ -623,6 +624,184 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     }
 }
 
+// One token and many weight rows (the LM head, larger matrices): a grid of a few workgroups
+// per CU quantizes the activation row once into LDS and then streams blocks of 16 rows,
+// requesting the next block's weights before the current block's dot products, so the
+// prologue is paid once per workgroup instead of once per 16 rows and every workgroup keeps
+// two blocks of weights in flight.  Same arithmetic as the kernel above (one token, bf16
+// activations, plain store epilogue, one segment); the codes are multiplied unmapped and
+// the row's code sum is subtracted once per output.
+template <bool OUT_BF16, int NI>
+__global__ __launch_bounds__(256) void gemv_stream_kernel(GemvArgs p) {
+    constexpr int NW = 4, NT = 64 * NW, RB = NW * RPW;  // 16 rows per block
+    constexpr int NS = (NI + 1) / 2;                    // 8-value slices of the row per thread
+    constexpr int CS = 64 + 16;                         // LDS bytes per 64-k chunk
+    extern __shared__ __attribute__((aligned(16))) int8_t qs[];
+    __shared__ float red_m[NW], red_s[NW];
+    __shared__ int red_q[NW];
+    __shared__ float s_a;
+    __shared__ int s_rs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = lane / LPR, j = lane % LPR;
+    const int K = p.K, NC = K / 64;
+    const int nrb = (p.rows_total + RB - 1) / RB;
+    const Seg &S0 = p.seg[0];
+
+    // the activation row is requested first (loads return in issue order)
+    uint4 xr[NS];
+#pragma unroll
+    for (int s4 = 0; s4 < NS; ++s4) {
+        const int k0 = tid * 8 + 8 * NT * s4;
+        xr[s4] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + (k0 < K ? k0 : K - 8));
+    }
+    // a block's weights: every slot requested (rows and chunks past the end clamped)
+    auto wload = [&](int rb, uint4 (&w)[NI]) __attribute__((always_inline)) {
+        int r = rb * RB + wave * RPW + slot;
+        r = r < p.rows_total ? r : p.rows_total - 1;
+        const uint32_t *wr = S0.packed + static_cast<int64_t>(r) * (K / 16);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            int c = j + LPR * i;
+            c = c < NC ? c : NC - 1;
+            w[i] = *reinterpret_cast<const uint4 *>(wr + c * 4);
+        }
+    };
+    uint4 wa[NI], wb[NI];
+    int rb = blockIdx.x;
+    wload(rb, wa);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // prologue: RMS/absmax quantization of the row into LDS (the quantizer's arithmetic)
+    float xv[NS][8];
+    float pm[1] = {0.f}, ps[1] = {0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < NS; ++s4) {
+        const int k0 = tid * 8 + 8 * NT * s4;
+        bf16x8_to_f32(xr[s4], xv[s4]);
+        if (k0 < K) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pj = p.gamma ? xv[s4][e] * p.gamma[k0 + e] : xv[s4][e];
+                pm[0] = fmaxf(pm[0], fabsf(pj));
+                ps[0] += xv[s4][e] * xv[s4][e];
+            }
+        }
+    }
+    {
+        const float rm = wave_reduce_multi<1, true>(pm);
+        const float rs = wave_reduce_multi<1, false>(ps);
+        if (lane == 0) {
+            red_m[wave] = rm;
+            red_s[wave] = rs;
+        }
+    }
+    __syncthreads();
+    float mx = red_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red_m[w]);
+    const float sc = 127.0f / fmaxf(mx, 1e-5f);
+    const bool cap0 = blockIdx.x == 0 && p.cap.row0 <= 0 && 0 < p.cap.row1;
+    int qsum[1] = {0};  // the row's code sum: codes are multiplied unmapped (c = q_w + 1)
+#pragma unroll
+    for (int s4 = 0; s4 < NS; ++s4) {
+        const int k0 = tid * 8 + 8 * NT * s4;
+        if (k0 < K) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pj = p.gamma ? xv[s4][e] * p.gamma[k0 + e] : xv[s4][e];
+                float rq = rintf(pj * sc);
+                rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+                qsum[0] += static_cast<int>(rq);
+                const uint32_t byte = static_cast<uint32_t>(static_cast<int>(rq)) & 0xFFu;
+                if (e < 4) lo |= byte << (8 * e);
+                else hi |= byte << (8 * (e - 4));
+            }
+            *reinterpret_cast<uint2 *>(qs + (k0 >> 6) * CS + (k0 & 63)) = make_uint2(lo, hi);
+            if (cap0) {  // test protocol
+                const int64_t cr = -p.cap.row0;
+                if (p.cap.x_in)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p.cap.x_in[cr * K + k0 + e] = xv[s4][e];
+                if (p.cap.q) *reinterpret_cast<uint2 *>(p.cap.q + cr * K + k0) = make_uint2(lo, hi);
+            }
+        }
+    }
+    {
+        const int rq = wave_reduce_multi<1, false, int>(qsum);
+        if (lane == 0) red_q[wave] = rq;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float ss = red_s[0];
+        int qt = red_q[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            ss += red_s[w];
+            qt += red_q[w];
+        }
+        const float me = fmaxf(mx, 1e-5f);
+        s_a = me / 127.0f * (1.0f / sqrtf(ss / static_cast<float>(K) + p.eps));
+        s_rs = qt;
+        if (cap0 && p.cap.a) p.cap.a[-p.cap.row0] = s_a;
+    }
+    __syncthreads();
+    const float at = s_a;
+    const int row_sum = s_rs;
+
+    // dot products of one block against the LDS-resident codes, 16-lane reduction, store
+    auto block = [&](int rbk, const uint4 (&w)[NI]) __attribute__((always_inline)) {
+        const int r = rbk * RB + wave * RPW + slot;
+        int acc[1] = {0};
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = j + LPR * i;
+            const bool cv = c < NC;
+            // chunks past the row end (clamped re-reads) count as code 0
+            const v4i ca[4] = {unpack_codes(cv ? w[i].x : 0u), unpack_codes(cv ? w[i].y : 0u),
+                               unpack_codes(cv ? w[i].z : 0u), unpack_codes(cv ? w[i].w : 0u)};
+            const v4i *qp = reinterpret_cast<const v4i *>(qs + (cv ? c : 0) * CS);
+            const v4i qv[4] = {qp[0], qp[1], qp[2], qp[3]};
+            acc[0] = dot16(qv, ca, acc[0]);
+        }
+        const int tot = wave_reduce_multi<1, false, int, LPR>(acc) - row_sum;
+        if (r < p.rows_total && j == 0) {
+            float y = static_cast<float>(tot) * (S0.scale * at);
+            if (S0.bias) y += S0.bias[r];
+            store_act<OUT_BF16>(p.out, S0.out_col0 + r, y);
+            if (p.cap.row0 <= 0 && 0 < p.cap.row1) {
+                const int64_t cr = -p.cap.row0;
+                if (p.cap.acc) p.cap.acc[cr * p.cap.acc_ld + S0.cap_col0 + r] = tot;
+                if (p.cap.y_out) p.cap.y_out[cr * p.ldo + S0.out_col0 + r] = OUT_BF16 ? round_to_bf16(y) : y;
+            }
+        }
+    };
+    // two register sets of weights: the next block (or, past the end, the current one again)
+    // is requested unconditionally before the current block is multiplied
+    while (true) {
+        const int rn = rb + static_cast<int>(gridDim.x);
+        wload(rn < nrb ? rn : rb, wb);
+        block(rb, wa);
+        rb = rn;
+        if (rb >= nrb) break;
+        const int rn2 = rb + static_cast<int>(gridDim.x);
+        wload(rn2 < nrb ? rn2 : rb, wa);
+        block(rb, wb);
+        rb = rn2;
+        if (rb >= nrb) break;
+    }
+}
+
+template <bool OUT_BF16>
+void launch_stream(const GemvArgs &a, size_t lds, unsigned grid, hipStream_t s) {
+    const int groups = (a.K / 64 + LPR - 1) / LPR;
+    if (groups <= 1) hipLaunchKernelGGL((gemv_stream_kernel<OUT_BF16, 1>), dim3(grid), dim3(256), lds, s, a);
+    else if (groups <= 2) hipLaunchKernelGGL((gemv_stream_kernel<OUT_BF16, 2>), dim3(grid), dim3(256), lds, s, a);
+    else if (groups <= 4) hipLaunchKernelGGL((gemv_stream_kernel<OUT_BF16, 4>), dim3(grid), dim3(256), lds, s, a);
+    else if (groups <= 6) hipLaunchKernelGGL((gemv_stream_kernel<OUT_BF16, 6>), dim3(grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((gemv_stream_kernel<OUT_BF16, 8>), dim3(grid), dim3(256), lds, s, a);
+}
+
 template <int EPI, int XIN, int TG, int NW, int NI>
 void launch5(const GemvArgs &a, size_t lds, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>((a.rows_total + NW * RPW - 1) / (NW * RPW)),
@@ -702,6 +881,25 @@ hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
         return hipErrorInvalidValue;  // the fused MLGRU step covers one token, D <= 4096
     if (a_in.copy_n % 4 != 0) return hipErrorInvalidValue;
     GemvArgs a = a_in;
+    if (a.M == 1 && a.epi == EPI_STORE && a.nseg == 1 && a.x && a.x_bf16 && !a.mlgru &&
+        a.copy_n == 0 && a.K <= 8192 && a.rows_total >= kStreamRows) {
+        // one token, many rows: persistent streaming over 16-row blocks, 2 workgroups per CU
+        static const int cus = [] {
+            int dev = 0, n = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+                n = 256;
+            return n;
+        }();
+        const int nrb = (a.rows_total + 15) / 16;
+        const unsigned grid = static_cast<unsigned>(nrb < 2 * cus ? nrb : 2 * cus);
+        a.tokens_per_group = 1;
+        timing_begin(FAM_GEMV, s);
+        if (a.out_bf16) launch_stream<true>(a, gemv_lds_bytes(a.K, 1), grid, s);
+        else launch_stream<false>(a, gemv_lds_bytes(a.K, 1), grid, s);
+        timing_end(FAM_GEMV, s);
+        return hipGetLastError();
+    }
     // token rows per workgroup: as many as the batch needs, up to 16, within 64 KB of LDS
     int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
     while (tg > 1 && gemv_lds_bytes(a.K, tg) > 64 * 1024) tg = tg == 16 ? 8 : tg == 8 ? 4 : 1;

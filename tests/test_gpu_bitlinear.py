@@ -45,6 +45,12 @@ CASES = [
     (2, 2048, 200, torch.bfloat16, True, False),
     (4, 5632, 300, torch.bfloat16, True, True),
     (3, 7232, 130, torch.bfloat16, False, False),
+    # one token, 16384 rows and more (bf16): persistent streaming over 16-row blocks with the
+    # next block's weights in flight; ragged last block, 1/2/6/8 chunks per lane
+    (1, 320, 16390, torch.bfloat16, False, True),
+    (1, 2048, 20000, torch.bfloat16, False, False),
+    (1, 5632, 16384, torch.bfloat16, True, False),
+    (1, 8192, 16400, torch.bfloat16, True, True),
 ]
 
 

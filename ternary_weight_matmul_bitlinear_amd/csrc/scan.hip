@@ -11,7 +11,7 @@
 //
 // The recurrence is elementwise in d, so it is parallel over B*D channels; to fill 256
 // CUs at long T it is also chunked over time (16-token chunks):
-//   phase 1 (thread per chunk and 8 channels): local scan from 0 -> end state hloc and
+//   phase 1 (thread per chunk and 4 channels): local scan from 0 -> end state hloc and
 //     prod(f);
 //   phase 2 (per channel block, 8 runs of chunks composed through LDS): carry across
 //     chunks, h_in[c+1] = prod_c*h_in[c] + hloc_c;
@@ -974,11 +974,13 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
     timing_begin(FAM_SCAN, s);
     if (a.n_chunks > 1) {
         if (a.chunk == kScanChunk && a.D % 64 == 0) {
-            // row layout: 8 (bf16) or 4 (fp32) channels per thread, runs of chunks for the carry
-            const int cpl = a.ifg_bf16 ? 8 : 4;
+            // row layout: 4 channels per thread (8-byte bf16 or 16-byte fp32 loads; with 8 per
+            // thread the 370M block had half the waves in flight and phase 1 took 3 us longer),
+            // runs of chunks for the carry
+            const int cpl = 4;
             const int64_t n = a.B * a.n_chunks * (a.D / cpl);
             const dim3 g1(static_cast<unsigned>((n + 255) / 256));
-            if (a.ifg_bf16) hipLaunchKernelGGL((scan_local_row_kernel<true, 8, kScanChunk>), g1, dim3(256), 0, s, a);
+            if (a.ifg_bf16) hipLaunchKernelGGL((scan_local_row_kernel<true, 4, kScanChunk>), g1, dim3(256), 0, s, a);
             else hipLaunchKernelGGL((scan_local_row_kernel<false, 4, kScanChunk>), g1, dim3(256), 0, s, a);
             const dim3 g2(static_cast<unsigned>(a.D / 64), static_cast<unsigned>(a.B));
             hipLaunchKernelGGL(scan_carry2_kernel, g2, dim3(512), 0, s, a);

@@ -837,8 +837,11 @@ __global__ __launch_bounds__(512) void scan_carry2_kernel(ScanArgs p) {
     const int c0 = s * L, c1 = c0 + L < nc ? c0 + L : nc;
     const int64_t row0 = b * nc;
     float A = 1.f, Bv = 0.f;
+    // a run of at most U chunks (2048 tokens and fewer at 16 tokens per chunk) stays in
+    // registers for the second walk instead of being read again
+    float pf[U], hl[U];
+    const bool one_batch = c1 - c0 <= U;
     for (int c = c0; c < c1; c += U) {
-        float pf[U], hl[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int cc = c + u < c1 ? c + u : c1 - 1;
@@ -859,12 +862,13 @@ __global__ __launch_bounds__(512) void scan_carry2_kernel(ScanArgs p) {
     float h = p.h0 ? p.h0[b * D + d] : 0.0f;
     for (int j = 0; j < s; ++j) h = sA[j][lane] * h + sB[j][lane];
     for (int c = c0; c < c1; c += U) {
-        float pf[U], hl[U];
+        if (!one_batch) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int cc = c + u < c1 ? c + u : c1 - 1;
-            pf[u] = p.pf[(row0 + cc) * D + d];
-            hl[u] = p.hloc[(row0 + cc) * D + d];
+            for (int u = 0; u < U; ++u) {
+                const int cc = c + u < c1 ? c + u : c1 - 1;
+                pf[u] = p.pf[(row0 + cc) * D + d];
+                hl[u] = p.hloc[(row0 + cc) * D + d];
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

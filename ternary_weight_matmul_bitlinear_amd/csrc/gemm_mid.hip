@@ -12,14 +12,19 @@
 // one VALU lane-op per 4 codes per token and becomes ALU-bound, while the prefill tiles
 // (128 rows) leave most workgroups idle.  Here:
 //   - one 256-thread workgroup owns 32 weight rows (for the GLU, 32 gate rows and the 32 up
-//     rows of the same features) and all M <= 64 token rows as two 32-row MFMA blocks;
+//     rows of the same features) and all M <= 64 token rows as one or two 32-row MFMA
+//     blocks (MB = 1 up to 32 rows);
 //   - its four waves take interleaved k-tiles of 128 (kt = wave, wave + 4, ...), so the
 //     four waves together read whole 128-byte lines of every weight row;
 //   - lane l (r = l % 32, g = l / 32) holds, per k-tile, the 16-byte packed piece (words
 //     4g..4g+3) of weight row r: word 4g + ks is exactly the 16-code B operand of MFMA step
 //     ks, paired with activation bytes 64g + 16ks + [0,16) of token row r.  All weight
-//     pieces of a wave are requested at kernel entry; activations (a few hundred KB, L2
-//     resident) are fetched up to four k-tiles ahead;
+//     pieces of a wave are requested at kernel entry;
+//   - every workgroup reads all M x K activations (L2 resident), so their fetch sets the
+//     time: they are loaded as whole 128-byte row segments (8 lanes per row, up to four
+//     k-tiles ahead) and moved into the MFMA layout through a wave-private LDS buffer.  The
+//     MFMA layout fetched directly (32 rows per load, 16 bytes each) costs one cache-line
+//     access per lane and ran at about 30 GB/s per CU;
 //   - the four partial accumulators are summed through LDS and the fused epilogue (rescale,
 //     bias, residual, or SiLU(gate)*up) stores 8 consecutive outputs of one row per thread.
 // KTW (k-tiles per wave) is a template parameter so every load is unconditional: k-tiles
@@ -31,14 +36,26 @@ namespace mmf {
 namespace {
 
 constexpr int MID_NT = 256;
+
+// Keeps the compiler from moving LDS accesses of this wave across the point (the hardware
+// completes one wave's LDS instructions in issue order, so program order is enough).
+__device__ __forceinline__ void lds_order() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
 constexpr int MID_KT = 128;  // k per tile
 
-template <int EPI, bool OUT_BF16, int KTW>
+template <int EPI, bool OUT_BF16, int KTW, int MB>
 __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
     constexpr int NB = EPI == EPI_GLU ? 2 : 1;  // 32-row weight blocks per workgroup
-    constexpr int MB = 2;                      // 32-row token blocks (M <= 64)
+    // MB: 32-row token blocks (M <= 32 * MB)
     constexpr int PITCH = NB * 32 + 4;         // int32 per LDS row of a partial tile
-    __shared__ int32_t red[4][MB * 32][PITCH];
+    // the k loop stages activation tiles in LDS (two 8 KB buffers per wave); the partial
+    // tiles of the reduction reuse the same memory afterwards
+    constexpr int STG_BYTES = 4 * 2 * MB * 32 * MID_KT;
+    constexpr int RED_BYTES = 4 * MB * 32 * PITCH * 4;
+    __shared__ __attribute__((aligned(16))) int8_t lds[STG_BYTES > RED_BYTES ? STG_BYTES : RED_BYTES];
+    auto red = reinterpret_cast<int32_t (*)[MB * 32][PITCH]>(lds);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,39 +77,67 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
         const int n = n0 + r32 < S.n ? n0 + r32 : S.n - 1;  // clamped rows are never stored
         wrow[nb] = S.packed + static_cast<int64_t>(n) * KW;
     }
-    const int8_t *arow[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = mb * 32 + r32 < p.M ? mb * 32 + r32 : p.M - 1;
-        arow[mb] = p.A + m * K;
-    }
 
-    // ---- all weight pieces of this wave, requested up front (after the first activation
-    //      tile, so that the first k-tile waits only for its own two pieces of data)
+    // ---- activation tiles (MB*32 rows x 128 bytes) are fetched with whole 128-byte row
+    //      segments per 8 lanes: load j of lane l reads token row 8j + l/8, 16-byte chunk
+    //      (l%8) ^ (row%8), and stores it to LDS slot 16l of the wave's buffer, i.e. chunk c
+    //      of row r sits at r*128 + 16*(c ^ r%8), so the fragment reads of 8 consecutive rows
+    //      (same chunk) hit 8 different bank groups.  Rows past M re-read row M-1 (never
+    //      stored); the upper half of a ragged last tile re-reads the lower half (in bounds,
+    //      multiplied by zero codes).
+    constexpr int AL = MB * 32 / 8;  // 16-byte loads per lane per activation tile
+    uint32_t a_goff[AL];             // byte offset of this lane's chunk inside a k-tile
+    int a_chunk[AL];
+#pragma unroll
+    for (int j = 0; j < AL; ++j) {
+        const int row = 8 * j + (lane >> 3), c = (lane & 7) ^ (row & 7);
+        const int64_t m = row < p.M ? row : p.M - 1;
+        a_goff[j] = static_cast<uint32_t>(m * K + 16 * c);
+        a_chunk[j] = c;
+    }
+    auto tile_of = [&](int i) __attribute__((always_inline)) {
+        const int kt0 = wave + 4 * i;
+        return kt0 < nk ? kt0 : nk - 1;
+    };
+    // packed weights: all pieces of this wave requested up front
     uint4 bw[KTW][NB];
     auto load_b = [&](int i) __attribute__((always_inline)) {
-        const int kt0 = wave + 4 * i;
-        const int kt = kt0 < nk ? kt0 : nk - 1;
-        // the upper lane half of a ragged last tile re-reads the lower half (in bounds)
+        const int kt = tile_of(i);
         const int word = kt * 8 + (ragged && kt == nk - 1 ? 0 : 4 * g);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) bw[i][nb] = *reinterpret_cast<const uint4 *>(wrow[nb] + word);
     };
-    auto a_off = [&](int i) __attribute__((always_inline)) {
-        const int kt0 = wave + 4 * i;
-        const int kt = kt0 < nk ? kt0 : nk - 1;
-        return kt * MID_KT + (ragged && kt == nk - 1 ? 0 : 64 * g);
-    };
-    // activations run PD k-tiles ahead of the MFMAs (their L2 latency would otherwise be
-    // paid once per k-tile of the wave)
+    // raw activation tiles run PD k-tiles ahead of the MFMAs
     constexpr int PD = KTW < 4 ? KTW : 4;
-    v4i av[PD][MB][4];
-    auto load_a = [&](int i, v4i (&dst)[MB][4]) __attribute__((always_inline)) {
-        const int off = a_off(i);
+    v4i araw[PD][AL];  // vector type (a struct copy of uint4 would keep the array in scratch)
+    auto load_a = [&](int i, v4i (&dst)[AL]) __attribute__((always_inline)) {
+        const int kt = tile_of(i);
+        const bool cut = ragged && kt == nk - 1;
+        const int8_t *base = p.A + static_cast<int64_t>(kt) * MID_KT;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int j = 0; j < AL; ++j)
+            dst[j] = *reinterpret_cast<const v4i *>(base + (cut && a_chunk[j] >= 4 ? a_goff[j] - 64 : a_goff[j]));
+    };
+    int8_t *stg = lds + wave * (2 * MB * 32 * MID_KT);
+    auto put_a = [&](int buf, const v4i (&src)[AL]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) dst[mb][ks] = *reinterpret_cast<const v4i *>(arow[mb] + off + 16 * ks);
+        for (int j = 0; j < AL; ++j)
+            *reinterpret_cast<v4i *>(stg + buf * (MB * 32 * MID_KT) + j * 1024 + 16 * lane) = src[j];
+    };
+    // MFMA fragment of step ks: token row mb*32 + r32, bytes 64g + 16ks + [0,16) of the tile
+    int f_off[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int row = mb * 32 + r32;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) f_off[mb][ks] = row * MID_KT + 16 * ((4 * g + ks) ^ (row & 7));
+    }
+    auto get_a = [&](int buf, v4i (&dst)[MB][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                dst[mb][ks] = *reinterpret_cast<const v4i *>(stg + buf * (MB * 32 * MID_KT) + f_off[mb][ks]);
     };
 
     v16i acc[MB][NB];
@@ -103,16 +148,31 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0;
 
-    load_a(0, av[0]);
+    load_a(0, araw[0]);
 #pragma unroll
     for (int i = 0; i < KTW; ++i) load_b(i);
 #pragma unroll
-    for (int i = 1; i < PD; ++i) load_a(i, av[i]);
+    for (int i = 1; i < PD; ++i) load_a(i, araw[i]);
     // keep every load above issued here: the scheduler would otherwise sink them next to
     // their first use and serialize the memory latency
     __builtin_amdgcn_sched_barrier(0);
+    // LDS accesses of one wave complete in order, so its own buffers need no barrier
+    put_a(0, araw[0]);
+    if (PD < KTW) load_a(PD, araw[0]);
+    lds_order();
+    v4i av[2][MB][4];
+    get_a(0, av[0]);
 #pragma unroll
     for (int i = 0; i < KTW; ++i) {
+        // the next tile goes to the other buffer and its fragments are read before this
+        // tile's MFMAs, so the LDS latency hides behind them
+        if (i + 1 < KTW) {
+            lds_order();  // after the reads of the buffer's previous tile
+            put_a((i + 1) & 1, araw[(i + 1) % PD]);
+            if (i + 1 + PD < KTW) load_a(i + 1 + PD, araw[(i + 1) % PD]);
+            lds_order();
+            get_a((i + 1) & 1, av[(i + 1) & 1]);
+        }
         const int kt0 = wave + 4 * i;
         // code mask: zero for tiles past the end and for the upper half of a ragged last tile
         const bool live = kt0 < nk && !(ragged && kt0 == nk - 1 && g);
@@ -126,12 +186,12 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
                                   static_cast<int>((w[ks] >> 4) & msk), static_cast<int>((w[ks] >> 6) & msk)};
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i % PD][mb][ks], b, acc[mb][nb], 0, 0, 0);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[i & 1][mb][ks], b, acc[mb][nb], 0, 0, 0);
             }
         }
-        if (i + PD < KTW) load_a(i + PD, av[i % PD]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    __syncthreads();  // every wave is done with its staging buffers before they hold partials
 
     // ---- sum the four waves' partial tiles.  Lane l holds C[row][col] for col = nb*32 + l%32
     //      and rows mb*32 + 8*(e/4) + 4*g + (e%4).
@@ -147,7 +207,7 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
     // ---- epilogue: thread -> row tid/4, columns 8*(tid%4) .. +7 of the 32-column block
     const int row_l = tid >> 2, c8 = 8 * (tid & 3);
     const int64_t row = row_l;
-    if (row >= p.M) return;
+    if (row_l >= MB * 32 || row >= p.M) return;
     int32_t v[NB][8];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -262,21 +322,30 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
     }
 }
 
-template <int EPI, bool OUT_BF16>
+template <int EPI, bool OUT_BF16, int MB>
 bool launch_ktw(const GemmArgs &a, dim3 grid, hipStream_t s) {
     const int nk = (a.K + MID_KT - 1) / MID_KT;
     const int ktw = (nk + 3) / 4;
-    if (ktw <= 2) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 2>), grid, dim3(MID_NT), 0, s, a);
-    else if (ktw <= 4) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 4>), grid, dim3(MID_NT), 0, s, a);
-    else if (ktw <= 8) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 8>), grid, dim3(MID_NT), 0, s, a);
-    else if (ktw <= 12 && EPI != EPI_GLU) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 12>), grid, dim3(MID_NT), 0, s, a);
-    else return false;
+    if (ktw <= 2) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 2, MB>), grid, dim3(MID_NT), 0, s, a);
+    else if (ktw <= 4) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 4, MB>), grid, dim3(MID_NT), 0, s, a);
+    else if (ktw <= 8) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 8, MB>), grid, dim3(MID_NT), 0, s, a);
+    else if constexpr (EPI != EPI_GLU) {  // (the GLU's two weight blocks would not fit)
+        if (ktw <= 12) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 12, MB>), grid, dim3(MID_NT), 0, s, a);
+        else return false;
+    } else {
+        return false;
+    }
     return true;
+}
+
+template <int EPI, bool OUT_BF16>
+bool launch_mb(const GemmArgs &a, dim3 grid, hipStream_t s) {
+    return a.M <= 32 ? launch_ktw<EPI, OUT_BF16, 1>(a, grid, s) : launch_ktw<EPI, OUT_BF16, 2>(a, grid, s);
 }
 
 template <int EPI>
 bool launch_mid_epi(const GemmArgs &a, dim3 grid, hipStream_t s) {
-    return a.out_bf16 ? launch_ktw<EPI, true>(a, grid, s) : launch_ktw<EPI, false>(a, grid, s);
+    return a.out_bf16 ? launch_mb<EPI, true>(a, grid, s) : launch_mb<EPI, false>(a, grid, s);
 }
 }  // namespace
 

@@ -153,6 +153,27 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
     for (int i = 0; i < KTW; ++i) load_b(i);
 #pragma unroll
     for (int i = 1; i < PD; ++i) load_a(i, araw[i]);
+    // epilogue operands of this thread (token row tid/4, columns 8*(tid%4) .. +7 of the
+    // block), requested with the prologue so that their latency is not paid after the k loop
+    const int e_row = (tid >> 2) < p.M ? (tid >> 2) : static_cast<int>(p.M) - 1;
+    const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
+    const int col = n0 + 8 * (tid & 3);  // first column (feature) inside the segment
+    const int ocol = (EPI == EPI_GLU ? 0 : S.out_col0) + col;
+    const bool vec = col + 8 <= S.n && (p.ldo % 8 == 0) && (ocol % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0);
+    const int32_t rs = p.rowsum[e_row];
+    const float a = p.a[e_row];
+    v4i rv[OUT_BF16 ? 1 : 2] = {};
+    if constexpr (EPI == EPI_RESID) {
+        if (vec) {
+            const int64_t ri = static_cast<int64_t>(e_row) * p.ldr + ocol;
+            if constexpr (OUT_BF16) {
+                rv[0] = *reinterpret_cast<const v4i *>(static_cast<const uint16_t *>(p.resid) + ri);
+            } else {
+                rv[0] = *reinterpret_cast<const v4i *>(static_cast<const float *>(p.resid) + ri);
+                rv[OUT_BF16 ? 0 : 1] = *reinterpret_cast<const v4i *>(static_cast<const float *>(p.resid) + ri + 4);
+            }
+        }
+    }
     // keep every load above issued here: the scheduler would otherwise sink them next to
     // their first use and serialize the memory latency
     __builtin_amdgcn_sched_barrier(0);
@@ -206,7 +227,7 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
 
     // ---- epilogue: thread -> row tid/4, columns 8*(tid%4) .. +7 of the 32-column block
     const int row_l = tid >> 2, c8 = 8 * (tid & 3);
-    const int64_t row = row_l;
+    const int64_t row = row_l;  // equal to e_row from here on
     if (row_l >= MB * 32 || row >= p.M) return;
     int32_t v[NB][8];
 #pragma unroll
@@ -221,13 +242,8 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
             v[nb][4] += hi.x; v[nb][5] += hi.y; v[nb][6] += hi.z; v[nb][7] += hi.w;
         }
     }
-    const int32_t rs = p.rowsum[row];
-    const float a = p.a[row];
-    const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
     const int ncols = S.n;
-    const int col = n0 + c8;  // first column (feature) inside the segment
     if (col >= ncols) return;
-    const bool full = col + 8 <= ncols;
     float o[8];
     if constexpr (EPI == EPI_GLU) {
         const float sa_g = p.seg[0].scale * a, sa_u = p.seg[1].scale * a;
@@ -262,26 +278,24 @@ __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
             }
         }
     }
-    const int ocol = (EPI == EPI_GLU ? 0 : S.out_col0) + col;
-    const bool vec = full && (p.ldo % 8 == 0) && (ocol % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0);
     if constexpr (EPI == EPI_RESID) {
-        const int64_t ri = row * p.ldr + ocol;
         if (vec) {
             if constexpr (OUT_BF16) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.resid) + ri);
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    o[2 * j] += __uint_as_float(w[j] << 16);
-                    o[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+                    const uint32_t w = static_cast<uint32_t>(rv[0][j]);
+                    o[2 * j] += __uint_as_float(w << 16);
+                    o[2 * j + 1] += __uint_as_float(w & 0xFFFF0000u);
                 }
             } else {
-                const float4 r0 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri);
-                const float4 r1 = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.resid) + ri + 4);
-                o[0] += r0.x; o[1] += r0.y; o[2] += r0.z; o[3] += r0.w;
-                o[4] += r1.x; o[5] += r1.y; o[6] += r1.z; o[7] += r1.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[j] += __int_as_float(rv[0][j]);
+                    o[4 + j] += __int_as_float(rv[OUT_BF16 ? 0 : 1][j]);
+                }
             }
         } else {
+            const int64_t ri = row * p.ldr + ocol;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (col + j < ncols) o[j] += load_act<OUT_BF16>(p.resid, ri + j);
@@ -331,6 +345,7 @@ bool launch_ktw(const GemmArgs &a, dim3 grid, hipStream_t s) {
     else if (ktw <= 8) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 8, MB>), grid, dim3(MID_NT), 0, s, a);
     else if constexpr (EPI != EPI_GLU) {  // (the GLU's two weight blocks would not fit)
         if (ktw <= 12) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 12, MB>), grid, dim3(MID_NT), 0, s, a);
+        else if (ktw <= 16) hipLaunchKernelGGL((gemm_mid_kernel<EPI, OUT_BF16, 16, MB>), grid, dim3(MID_NT), 0, s, a);
         else return false;
     } else {
         return false;
@@ -352,7 +367,7 @@ bool launch_mid_epi(const GemmArgs &a, dim3 grid, hipStream_t s) {
 bool mid_gemm_supported(const GemmArgs &a) {
     const int nk = (a.K + MID_KT - 1) / MID_KT;
     const int ktw = (nk + 3) / 4;
-    return a.M >= 1 && a.M <= kMidMaxM && (ktw <= 8 || (ktw <= 12 && a.epi != EPI_GLU));
+    return a.M >= 1 && a.M <= kMidMaxM && (ktw <= 8 || (ktw <= 16 && a.epi != EPI_GLU));
 }
 
 hipError_t launch_gemm_mid(const GemmArgs &a_in, hipStream_t s) {

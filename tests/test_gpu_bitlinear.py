@@ -22,13 +22,16 @@ CASES = [
     (16, 5632, 2048, torch.bfloat16, False, False),
     (1, 6912, 2560, torch.bfloat16, True, False),
     (257, 2816, 1024, torch.bfloat16, False, False),
-    # k-split MFMA kernel: ragged k-tiles (K % 128 == 64), k-tiles per wave 1..11, ragged N
+    # k-split MFMA kernel: ragged k-tiles (K % 128 == 64), k-tiles per wave 1..16, one and two
+    # 32-row token blocks, ragged N
     (33, 192, 100, torch.bfloat16, True, True),
     (64, 64, 40, torch.float32, False, False),
     (50, 2048, 6144, torch.bfloat16, False, False),
     (64, 5632, 2048, torch.bfloat16, False, True),
     (17, 4096, 96, torch.float32, True, False),
     (48, 2048, 32000, torch.bfloat16, False, False),
+    (24, 6912, 320, torch.bfloat16, False, False),  # 14 k-tiles per wave (2.7B down width)
+    (40, 8192, 160, torch.float32, True, True),     # 16 k-tiles per wave
     # one token, rows of 8192 and more: the long-row weight-streaming variant (two passes of
     # weight chunks at K = 16384)
     (1, 8192, 300, torch.bfloat16, True, True),

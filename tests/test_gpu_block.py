@@ -25,6 +25,10 @@ def _restore_regime():
 @pytest.mark.parametrize("regime", [1, 2, 3], ids=["decode", "mfma", "tiles"])
 @pytest.mark.parametrize("M,D,F,dt,resid", [(5, 256, 704, torch.float32, False),
                                             (64, 256, 704, torch.bfloat16, True),
+                                            # up to 32 rows: one 32-row token block in the
+                                            # k-split kernel (ragged k-tiles at K = 1088)
+                                            (20, 256, 704, torch.bfloat16, True),
+                                            (32, 512, 1088, torch.float32, True),
                                             (300, 1024, 2816, torch.bfloat16, True),
                                             # one token, down projection over K = F = 8192
                                             (1, 256, 8192, torch.bfloat16, True),
@@ -120,19 +124,22 @@ def test_block_decode_steps_match_prefill(orc):
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("gate_mode", [0, 1])
-@pytest.mark.parametrize("B,D,F", [(1, 256, 704), (1, 4096, 256), (3, 256, 704), (4, 2048, 256)])
+@pytest.mark.parametrize("B,D,F", [(1, 256, 704), (1, 4096, 256), (3, 256, 704), (4, 2048, 256),
+                                   (16, 256, 704), (40, 512, 1088)])
 def test_block_one_token_steps(orc, dt, gate_mode, B, D, F):
     """Decode steps of B sequences (one sequence: the MLGRU step, g_norm and o_proj
     quantization run in the o_proj kernel; 3-4 sequences: scan kernel and four-token
-    weight streaming): each step is stage-checked from its capture against the oracle started
-    from the carried state, and the sequence of steps matches the oracle's block end to end.
-    D = 256, 2048 and 4096 give one, two and four 64-channel chunks per lane."""
+    weight streaming; 16 and 40 sequences: scan kernel and the k-split MFMA kernel with one
+    and two 32-row token blocks): each step is stage-checked from its capture against the
+    oracle started from the carried state, and the sequence of steps matches the oracle's
+    block end to end.  D = 256, 2048 and 4096 give one, two and four 64-channel chunks per
+    lane."""
     T = 6
     note(f"block decode steps B={B} dt={dt} gate={gate_mode} D={D}")
     blk, W, x, fb, gw = _block_case(orc, D, F, B, T, dt, 41, gate_mode, f_bias=0.3, use_gains=True)
     bf = dt == torch.bfloat16
     xd = dev(x, dt)
-    api.set_regime(1)
+    api.set_regime(1 if B <= 4 else 0)  # above 4 rows the automatic choice is the k-split kernel
     h = torch.zeros((B, D), device="cuda")
     ys = []
     for t in range(T):

@@ -84,7 +84,7 @@ def test_decode_stack_1p3b(orc):
     assert emb.scale == se and head.scale == sh
     stack = api.Stack(blocks, emb, head)
     steps = 3
-    for B in (1, 4):
+    for B in (1, 4, 16):
         note(f"1.3B decode B={B}")
         ids = synth.token_ids(w, steps, B)
         hs = torch.zeros((L, B, D), device="cuda")

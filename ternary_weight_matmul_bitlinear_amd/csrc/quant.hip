@@ -145,15 +145,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
     }
 }
 
-// bf16 rows without a gain at the model widths (K = 256*NC): lane l holds elements 4l + 256c
-// of chunk c (one 8-byte load, one 4-byte store), R rows per wave with all of their loads
-// issued before the first row is reduced.  Every global access
-// after the row loads is unconditional (the rows of a partial last wave are clamped to the
-// last row and rewrite its identical results; the scale and code sum are stored by all
-// lanes), so each wait covers only the loads of the row it precedes and never the earlier
-// rows' stores.  CAP adds the stage-capture stores (tests only).
-template <int NC, int R, bool CAP>
+// bf16 rows without a gain at the model widths: lane l holds EPL consecutive elements
+// EPL*l + 64*EPL*c of chunk c (EPL = 8: one 16-byte load and one 8-byte store per chunk, for
+// widths that are multiples of 512; EPL = 4: 8-byte loads and 4-byte stores otherwise), NC
+// chunks, R rows per wave with all of their loads issued before the first row is reduced.
+// Every global access after the row loads is unconditional (the rows of a partial last
+// wave are clamped to the last row and rewrite its identical results; the scale and code
+// sum are stored by all lanes), so each wait covers only the loads of the row it precedes
+// and never the earlier rows' stores.  CAP adds the stage-capture stores (tests only).
+template <int NC, int R, bool CAP, int EPL>
 __global__ __launch_bounds__(256) void quant_rows256_kernel(QuantArgs p) {
+    constexpr int NWD = EPL / 2;  // 32-bit words (bf16 pairs) per lane per chunk
+    typedef uint32_t raw_t __attribute__((ext_vector_type(NWD)));
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int K = p.K;
@@ -163,28 +166,28 @@ __global__ __launch_bounds__(256) void quant_rows256_kernel(QuantArgs p) {
         const int64_t row = wave_id * R + r;
         rows[r] = row < p.M ? row : p.M - 1;
     }
-    uint2 raw[R][NC];
+    raw_t raw[R][NC];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            raw[r][c] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.x) + rows[r] * K + lane * 4 + 256 * c);
+            raw[r][c] = *reinterpret_cast<const raw_t *>(static_cast<const uint16_t *>(p.x) + rows[r] * K + lane * EPL + 64 * EPL * c);
     __builtin_amdgcn_sched_barrier(0);  // all row loads are issued here, not next to their use
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        float v[NC][4];
+        float v[NC][EPL];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            v[c][0] = __uint_as_float(raw[r][c].x << 16);
-            v[c][1] = __uint_as_float(raw[r][c].x & 0xFFFF0000u);
-            v[c][2] = __uint_as_float(raw[r][c].y << 16);
-            v[c][3] = __uint_as_float(raw[r][c].y & 0xFFFF0000u);
-        }
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                v[c][2 * w] = __uint_as_float(raw[r][c][w] << 16);
+                v[c][2 * w + 1] = __uint_as_float(raw[r][c][w] & 0xFFFF0000u);
+            }
         float mx = 0.0f, ss = 0.0f;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < EPL; ++j) {
                 mx = fmaxf(mx, fabsf(v[c][j]));
                 ss += v[c][j] * v[c][j];
             }
@@ -196,22 +199,32 @@ __global__ __launch_bounds__(256) void quant_rows256_kernel(QuantArgs p) {
         int qsum = 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            uint32_t pk = 0;
+            uint32_t pk[EPL / 4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float q = rintf(v[c][j] * sc);
-                q = fminf(fmaxf(q, -127.0f), 127.0f);
-                const int qi = static_cast<int>(q);
-                qsum += qi;
-                pk |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * j);
+            for (int d = 0; d < EPL / 4; ++d) {
+                pk[d] = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float q = rintf(v[c][4 * d + j] * sc);
+                    q = fminf(fmaxf(q, -127.0f), 127.0f);
+                    const int qi = static_cast<int>(q);
+                    qsum += qi;
+                    pk[d] |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * j);
+                }
             }
-            const int64_t k0 = lane * 4 + 256 * c;
-            *reinterpret_cast<uint32_t *>(p.q + row * K + k0) = pk;
+            const int64_t k0 = lane * EPL + 64 * EPL * c;
+            if constexpr (EPL == 8) *reinterpret_cast<uint2 *>(p.q + row * K + k0) = make_uint2(pk[0], pk[1]);
+            else *reinterpret_cast<uint32_t *>(p.q + row * K + k0) = pk[0];
             if constexpr (CAP) {
                 if (p.cap.row0 <= row && row < p.cap.row1) {
                     const int64_t crow = row - p.cap.row0;
-                    if (p.cap.x_in) *reinterpret_cast<float4 *>(p.cap.x_in + crow * K + k0) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
-                    if (p.cap.q) *reinterpret_cast<uint32_t *>(p.cap.q + crow * K + k0) = pk;
+#pragma unroll
+                    for (int d = 0; d < EPL / 4; ++d) {
+                        if (p.cap.x_in)
+                            *reinterpret_cast<float4 *>(p.cap.x_in + crow * K + k0 + 4 * d) =
+                                make_float4(v[c][4 * d], v[c][4 * d + 1], v[c][4 * d + 2], v[c][4 * d + 3]);
+                        if (p.cap.q) *reinterpret_cast<uint32_t *>(p.cap.q + crow * K + k0 + 4 * d) = pk[d];
+                    }
                 }
             }
         }
@@ -225,25 +238,30 @@ __global__ __launch_bounds__(256) void quant_rows256_kernel(QuantArgs p) {
     }
 }
 
-template <int NC, int R>
+template <int NC, int R, int EPL>
 void launch_rows256_r(const QuantArgs &a, hipStream_t s) {
     const int64_t waves = (a.M + R - 1) / R;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-    if (a.cap.row1 > a.cap.row0) hipLaunchKernelGGL((quant_rows256_kernel<NC, R, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((quant_rows256_kernel<NC, R, false>), grid, dim3(256), 0, s, a);
+    if (a.cap.row1 > a.cap.row0) hipLaunchKernelGGL((quant_rows256_kernel<NC, R, true, EPL>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((quant_rows256_kernel<NC, R, false, EPL>), grid, dim3(256), 0, s, a);
 }
 
-// The model widths: D = 1024, 2048, 2560 and F = 2816, 5632, 6912, one row per wave (more
-// rows per wave measured slower or equal).
+// The model widths: D = 1024, 2048, 2560 and F = 5632 (16-byte loads), F = 2816, 6912 (8-byte
+// loads), one row per wave (more rows per wave measured slower or equal).
 bool launch_rows256(const QuantArgs &a, hipStream_t s) {
     if (!a.x_bf16 || a.gamma || a.K % 256 != 0) return false;
+    if (a.K % 512 == 0) {
+        switch (a.K / 512) {
+            case 2: launch_rows256_r<2, 1, 8>(a, s); return true;
+            case 4: launch_rows256_r<4, 1, 8>(a, s); return true;
+            case 5: launch_rows256_r<5, 1, 8>(a, s); return true;
+            case 11: launch_rows256_r<11, 1, 8>(a, s); return true;
+            default: return false;
+        }
+    }
     switch (a.K / 256) {
-        case 4: launch_rows256_r<4, 1>(a, s); return true;
-        case 8: launch_rows256_r<8, 1>(a, s); return true;
-        case 10: launch_rows256_r<10, 1>(a, s); return true;
-        case 11: launch_rows256_r<11, 1>(a, s); return true;
-        case 22: launch_rows256_r<22, 1>(a, s); return true;
-        case 27: launch_rows256_r<27, 1>(a, s); return true;
+        case 11: launch_rows256_r<11, 1, 4>(a, s); return true;
+        case 27: launch_rows256_r<27, 1, 4>(a, s); return true;
         default: return false;
     }
 }

@@ -36,6 +36,7 @@ namespace mmf {
 namespace {
 
 constexpr int MID_NT = 256;
+constexpr int MID_KT = 128;  // k per tile
 
 // Keeps the compiler from moving LDS accesses of this wave across the point (the hardware
 // completes one wave's LDS instructions in issue order, so program order is enough).
@@ -43,15 +44,14 @@ __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 }
-constexpr int MID_KT = 128;  // k per tile
 
 template <int EPI, bool OUT_BF16, int KTW, int MB>
 __global__ __launch_bounds__(MID_NT) void gemm_mid_kernel(GemmArgs p) {
     constexpr int NB = EPI == EPI_GLU ? 2 : 1;  // 32-row weight blocks per workgroup
     // MB: 32-row token blocks (M <= 32 * MB)
     constexpr int PITCH = NB * 32 + 4;         // int32 per LDS row of a partial tile
-    // the k loop stages activation tiles in LDS (two 8 KB buffers per wave); the partial
-    // tiles of the reduction reuse the same memory afterwards
+    // the k loop stages activation tiles in LDS (two buffers of MB * 4 KB per wave); the
+    // partial tiles of the reduction reuse the same memory afterwards
     constexpr int STG_BYTES = 4 * 2 * MB * 32 * MID_KT;
     constexpr int RED_BYTES = 4 * MB * 32 * PITCH * 4;
     __shared__ __attribute__((aligned(16))) int8_t lds[STG_BYTES > RED_BYTES ? STG_BYTES : RED_BYTES];

@@ -35,11 +35,15 @@
  *   R6  output gate: o = RMSNorm_D(h)*gamma_g * g*sigmoid(g) (default) or sigmoid(g)*h.
  *   R7  block: pre-norm residuals y1 = x + o_proj(...), y2 = y1 + GLU(y1); one RMSNorm per
  *       BitLinear input; y1 and y2 rounded once to the residual dtype.
- *   R8  activations handed from one kernel to the next are stored in the activation
- *       dtype: with bf16 activations the i/f/g pre-activations and the GLU hidden are
- *       rounded to bf16 (fp32 otherwise); the gated MLGRU output is quantized for o_proj
- *       inside the kernel that computes it, so it is rounded to fp32 only; the recurrent
- *       state is not rounded.
+ *   R8  every tensor that one of the pages' modules hands to the next is materialised in
+ *       the activation dtype (bf16 for bf16 workloads, fp32 otherwise), as the pages' model
+ *       runs in half precision (Hysen Labs, section on the official generation example:
+ *       the model is moved to the GPU in half precision).  The modules are the ones the
+ *       pages name: the i, f and g projections (their outputs feed the recurrence), g_norm
+ *       (Hysen Labs, "HGRN attention": a module of its own whose output feeds o_proj),
+ *       the MatMul-free GLU's gated product (DataCamp, "Core components": formed from the
+ *       two branches, then passed to the third BitLinear), and the residual stream y1, y2.
+ *       The recurrent state h is carried in fp32 and is not rounded.
  *
  * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
  * activation quant) are defined in fp32 so that both sides take each integer decision in
@@ -424,7 +428,7 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
     /* MLGRU + output gate, then o_proj with the residual. */
     rc = orc_mlgru(ifg, B, T, D, f_bias, h0, gnorm_w, eps, gate_mode, o, h_last);
     if (rc) return rc;
-    to_act(o, o32, M * D, 0);
+    to_act(o, o32, M * D, resid_bf16);
     if (st_o && st_o->x_in) memcpy(st_o->x_in, o32, sizeof(float) * (size_t)(M * D));
     rc = orc_bitlinear(o32, M, wo, eps, yo, st_o ? st_o->q : NULL, st_o ? st_o->a : NULL,
                        st_o ? st_o->acc : NULL);

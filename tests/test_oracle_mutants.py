@@ -51,7 +51,12 @@ MUTANTS = [
      "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = orc_round_bf16(ifg[i]);",
      "for (int64_t i = 0; i < M * 3 * D; ++i) ifg[i] = ifg[i];"),
     ("glu_hidden_not_rounded", "to_act(yg, mm, M * F, act_bf16);", "to_act(yg, mm, M * F, 0);"),
-    ("gated_output_rounded_to_bf16", "to_act(o, o32, M * D, 0);", "to_act(o, o32, M * D, resid_bf16);"),
+    ("gated_output_not_rounded", "to_act(o, o32, M * D, resid_bf16);", "to_act(o, o32, M * D, 0);"),
+    ("ternarize_floor_dropped", "float s = mean_abs > 1e-5f ? mean_abs : 1e-5f;",
+     "float s = mean_abs;"),
+    ("quant_divides_by_max", "float v = rintf(p * s);", "float v = rintf((p * 127.0f) / me);"),
+    ("quant_exact_quotient", "float v = rintf(p * s);",
+     "float v = (float)rint((double)p * 127.0 / (double)me);"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

@@ -44,6 +44,13 @@
  *       the MatMul-free GLU's gated product (DataCamp, "Core components": formed from the
  *       two branches, then passed to the third BitLinear), and the residual stream y1, y2.
  *       The recurrent state h is carried in fp32 and is not rounded.
+ *   R9  HGRN's hierarchical forget-gate lower bound (Hysen Labs, "HGRN attention", names
+ *       the Hierarchical Gated Recurrent Network but not its formula; the formula is read
+ *       from HGRN's published design and its parity is unpinned by the pages): layer l has
+ *       a per-channel bound lb_l in [0,1) that grows with depth, made from per-layer logits
+ *       G[L][D] as an exclusive cumulative softmax over the layers, lb_l[d] =
+ *       sum_{j<l} exp(G[j][d]) / sum_j exp(G[j][d]) (layer 0 is unbounded); the forget gate
+ *       becomes f = lb + (1 - lb)*sigmoid(f_pre + b_f).
  *
  * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
  * activation quant) are defined in fp32 so that both sides take each integer decision in
@@ -250,12 +257,12 @@ void orc_gated_recurrence(const double *f, const double *c, int64_t B, int64_t T
 /* ----------------------------------------------------- O6 + O7 MLGRU with output gate
  * ifg: [B, T, 3D] pre-activations, segments i | f | g along the last axis.
  * [HL-hgrn] i/f/g projections, recurrence, g_norm = RMSNorm fused with a swish gate.
- * Readings R5, R6.  gate_mode 0: out = h*rsqrt(mean_D h^2 + eps)*gnorm_w * g*sigmoid(g);
+ * Readings R5, R6, R9 (f_lower [D] or NULL).  gate_mode 0: out = h*rsqrt(mean_D h^2 + eps)*gnorm_w * g*sigmoid(g);
  * gate_mode 1: out = sigmoid(g)*h.  h_last [B, D] receives h_T.
  */
 int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f_bias,
-              const double *h0, const float *gnorm_w, double eps, int gate_mode,
-              double *out, double *h_last) {
+              const float *f_lower, const double *h0, const float *gnorm_w, double eps,
+              int gate_mode, double *out, double *h_last) {
     if (!ifg || !out || B <= 0 || T < 0 || D <= 0 || (gate_mode != 0 && gate_mode != 1))
         return -1;
     int64_t M = B * T;
@@ -267,7 +274,9 @@ int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f
     for (int64_t row = 0; row < M; ++row)
         for (int64_t d = 0; d < D; ++d) {
             const double *r = ifg + row * 3 * D;
-            f[row * D + d] = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
+            double sg = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
+            double lb = f_lower ? (double)f_lower[d] : 0.0;   /* reading R9 */
+            f[row * D + d] = lb + (1.0 - lb) * sg;
             c[row * D + d] = silu_d(r[d]);
         }
     orc_gated_recurrence(f, c, B, T, D, h0, h, h_last);
@@ -388,8 +397,8 @@ int orc_glu(const float *x, int64_t M, const orc_linear *gate, const orc_linear 
 int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
               const orc_linear *wf, const orc_linear *wg, const orc_linear *wo,
               const orc_linear *wgate, const orc_linear *wup, const orc_linear *wdown,
-              const float *f_bias, const float *gnorm_w, double eps, int gate_mode,
-              int resid_bf16, const double *h0, double *h_last, double *y,
+              const float *f_bias, const float *f_lower, const float *gnorm_w, double eps,
+              int gate_mode, int resid_bf16, const double *h0, double *h_last, double *y,
               double *ifg_out, float *y1_out, orc_stage *st_ifg, orc_stage *st_o,
               orc_stage *st_gu, orc_stage *st_down) {
     if (!x || !wi || !wf || !wg || !wo || !wgate || !wup || !wdown || !y) return -1;
@@ -426,7 +435,7 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
     if (ifg_out) memcpy(ifg_out, ifg, sizeof(double) * (size_t)(M * 3 * D));
 
     /* MLGRU + output gate, then o_proj with the residual. */
-    rc = orc_mlgru(ifg, B, T, D, f_bias, h0, gnorm_w, eps, gate_mode, o, h_last);
+    rc = orc_mlgru(ifg, B, T, D, f_bias, f_lower, h0, gnorm_w, eps, gate_mode, o, h_last);
     if (rc) return rc;
     to_act(o, o32, M * D, resid_bf16);
     if (st_o && st_o->x_in) memcpy(st_o->x_in, o32, sizeof(float) * (size_t)(M * D));
@@ -446,6 +455,28 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
 
     free(yi); free(yf); free(yg); free(ifg); free(o); free(o32); free(yo); free(y1);
     free(tmp); free(glu);
+    return 0;
+}
+
+/* ----------------------------------------- HGRN forget-gate lower bounds (R9)
+ * G [L, D] per-layer logits -> lb [L, D]: for each channel, a softmax over the L layers
+ * (fp64; the largest logit is subtracted first so exp cannot overflow), accumulated over
+ * the layers before l.  lb_0 = 0 and lb grows with l, staying below 1.
+ */
+int orc_hgrn_lower_bounds(const float *G, int64_t L, int64_t D, float *lb) {
+    if (!G || !lb || L <= 0 || D <= 0) return -1;
+    for (int64_t d = 0; d < D; ++d) {
+        double mx = (double)G[d];
+        for (int64_t l = 1; l < L; ++l)
+            if ((double)G[l * D + d] > mx) mx = (double)G[l * D + d];
+        double tot = 0.0;
+        for (int64_t l = 0; l < L; ++l) tot += exp((double)G[l * D + d] - mx);
+        double acc = 0.0;
+        for (int64_t l = 0; l < L; ++l) {
+            lb[l * D + d] = (float)(acc / tot);
+            acc += exp((double)G[l * D + d] - mx);
+        }
+    }
     return 0;
 }
 

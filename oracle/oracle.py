@@ -55,11 +55,12 @@ class Oracle:
         L.orc_accumulate.argtypes = [vp, vp, i64, i64, i64, vp]
         L.orc_bitlinear.argtypes = [vp, i64, C.POINTER(OrcLinear), f64, vp, vp, vp, vp]
         L.orc_gated_recurrence.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
-        L.orc_mlgru.argtypes = [vp, i64, i64, i64, vp, vp, vp, f64, i32, vp, vp]
+        L.orc_mlgru.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, f64, i32, vp, vp]
+        L.orc_hgrn_lower_bounds.argtypes = [vp, i64, i64, vp]
         L.orc_glu.argtypes = [vp, i64, C.POINTER(OrcLinear), C.POINTER(OrcLinear),
                               C.POINTER(OrcLinear), f64, i32, vp, vp]
         L.orc_block.argtypes = ([vp, i64, i64] + [C.POINTER(OrcLinear)] * 7 +
-                                [vp, vp, f64, i32, i32, vp, vp, vp, vp, vp] +
+                                [vp, vp, vp, f64, i32, i32, vp, vp, vp, vp, vp] +
                                 [C.POINTER(OrcStage)] * 4)
         L.orc_embedding.argtypes = [vp, f32, i64, i64, vp, i64, i32, vp]
         L.orc_round_bf16_array.argtypes = [vp, vp, i64]
@@ -160,7 +161,7 @@ class Oracle:
         return h, hl
 
     def mlgru(self, ifg, f_bias=None, h0=None, gnorm_w=None, eps: float = 1e-6,
-              gate_mode: int = 0):
+              gate_mode: int = 0, f_lower=None):
         ifg = np.ascontiguousarray(ifg, dtype=np.float64)
         B, T, D3 = ifg.shape
         D = D3 // 3
@@ -169,8 +170,9 @@ class Oracle:
         fb = None if f_bias is None else np.ascontiguousarray(f_bias, dtype=np.float32)
         gw = None if gnorm_w is None else np.ascontiguousarray(gnorm_w, dtype=np.float32)
         h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
-        rc = self.lib.orc_mlgru(_p(ifg), B, T, D, _p(fb), _p(h0), _p(gw), eps, gate_mode,
-                                _p(out), _p(hl))
+        lb = None if f_lower is None else np.ascontiguousarray(f_lower, dtype=np.float32)
+        rc = self.lib.orc_mlgru(_p(ifg), B, T, D, _p(fb), _p(lb), _p(h0), _p(gw), eps,
+                                gate_mode, _p(out), _p(hl))
         if rc:
             raise ValueError(f"orc_mlgru failed ({rc})")
         return out, hl
@@ -193,7 +195,8 @@ class Oracle:
 
     # ------------------------------------------------------------------ block
     def block(self, x, W: dict, f_bias=None, gnorm_w=None, eps: float = 1e-6,
-              gate_mode: int = 0, resid_bf16: bool = True, h0=None, record=False):
+              gate_mode: int = 0, resid_bf16: bool = True, h0=None, record=False,
+              f_lower=None):
         """One block forward.  W maps i, f, g, o, gate, up, down -> (q, scale[, gamma]).
 
         Returns a dict with y (fp64 [B, T, D]), h_last, ifg, y1 and, when record is set,
@@ -209,6 +212,7 @@ class Oracle:
         ifg = np.empty((B, T, 3 * D), np.float64)
         y1 = np.empty((B, T, D), np.float32)
         fb = None if f_bias is None else np.ascontiguousarray(f_bias, dtype=np.float32)
+        lb = None if f_lower is None else np.ascontiguousarray(f_lower, dtype=np.float32)
         gw = None if gnorm_w is None else np.ascontiguousarray(gnorm_w, dtype=np.float32)
         h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
         stages = {}
@@ -224,11 +228,21 @@ class Oracle:
                 recs.append(None)
         rc = self.lib.orc_block(
             _p(x), B, T, *(C.byref(lins[k]) for k in ("i", "f", "g", "o", "gate", "up", "down")),
-            _p(fb), _p(gw), eps, gate_mode, int(resid_bf16), _p(h0), _p(hl), _p(y), _p(ifg),
+            _p(fb), _p(lb), _p(gw), eps, gate_mode, int(resid_bf16), _p(h0), _p(hl), _p(y), _p(ifg),
             _p(y1), *(C.byref(r) if r is not None else None for r in recs))
         if rc:
             raise ValueError(f"orc_block failed ({rc})")
         return dict(y=y, h_last=hl, ifg=ifg, y1=y1, stages=stages)
+
+    def hgrn_lower_bounds(self, G):
+        """Per-layer forget-gate lower bounds [L, D] from logits G [L, D] (fp32)."""
+        G = np.ascontiguousarray(G, dtype=np.float32)
+        L, D = G.shape
+        lb = np.empty((L, D), np.float32)
+        rc = self.lib.orc_hgrn_lower_bounds(_p(G), L, D, _p(lb))
+        if rc:
+            raise ValueError(f"orc_hgrn_lower_bounds failed ({rc})")
+        return lb
 
     # -------------------------------------------------------------- embedding
     def embedding(self, qe, scale, ids, resid_bf16: bool = True):

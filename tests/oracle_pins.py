@@ -267,6 +267,53 @@ def pin_output_gate(orc):
     assert np.allclose(out1[0, 0], h / (1.0 + np.exp(-g)), rtol=1e-15, atol=0)
 
 
+def pin_hgrn_lower_bound_gate(orc):
+    """Reading R9: f = lb + (1 - lb)*sigmoid(f_pre + b_f).  lb = 0 is the plain MLGRU bit
+    for bit; lb = 1 keeps the state exactly (also through a whole block); lb = 0.5 with
+    f_pre = 0 gives f = 0.75, so with SiLU(40) = 40 (fp64) and h0 = 0 the state runs
+    10, 17.5, 23.125 (dyadic, exact)."""
+    D = 2
+    rng = np.random.default_rng(19)
+    ifg = rng.standard_normal((2, 9, 3 * D))
+    fb = np.array([0.3, -0.2], np.float32)
+    a, ha = orc.mlgru(ifg, f_bias=fb, gate_mode=0)
+    b, hb = orc.mlgru(ifg, f_bias=fb, gate_mode=0, f_lower=np.zeros(D, np.float32))
+    assert np.array_equal(a, b) and np.array_equal(ha, hb)
+    h0 = rng.standard_normal((2, D))
+    _, hl = orc.mlgru(ifg, h0=h0, gate_mode=1, f_lower=np.ones(D, np.float32))
+    assert np.array_equal(hl, h0)
+    ifg3 = np.zeros((1, 3, 3 * D))
+    ifg3[..., :D] = 40.0
+    lb = np.full(D, 0.5, np.float32)
+    hs = [orc.mlgru(ifg3[:, :T], gate_mode=1, f_lower=lb)[1][0, 0] for T in (1, 2, 3)]
+    assert hs == [10.0, 17.5, 23.125], hs
+    x = _bf(rng.standard_normal((2, 5, 64)))
+    hb0 = rng.standard_normal((2, 64))
+    r = orc.block(x, _small_block(orc, 7), h0=hb0, f_lower=np.ones(64, np.float32))
+    assert np.array_equal(r["h_last"], hb0)
+
+
+def pin_hgrn_lower_bounds(orc):
+    """Reading R9's bounds: an exclusive cumulative softmax over the layers.  Equal logits
+    over 4 layers give 0, 1/4, 1/2, 3/4 exactly; for any logits layer 0 is 0, the bound
+    grows with depth and stays below 1, and the last layer's bound is 1 minus the softmax
+    weight of the last layer."""
+    lb = orc.hgrn_lower_bounds(np.zeros((4, 3), np.float32))
+    assert lb.tolist() == [[0.0] * 3, [0.25] * 3, [0.5] * 3, [0.75] * 3], lb.tolist()
+    rng = np.random.default_rng(20)
+    G = (rng.standard_normal((24, 64)) * 2).astype(np.float32)
+    lb = orc.hgrn_lower_bounds(G)
+    assert np.all(lb[0] == 0) and np.all(np.diff(lb, axis=0) >= 0) and np.all(lb < 1)
+    p = np.exp(G.astype(np.float64))
+    p /= p.sum(axis=0)
+    assert np.allclose(lb[-1], 1.0 - p[-1], rtol=0, atol=2e-7)
+    # a layer whose logit dominates takes nearly all the remaining mass at its successor
+    G2 = np.zeros((3, 1), np.float32)
+    G2[1, 0] = 30.0
+    lb2 = orc.hgrn_lower_bounds(G2)[:, 0]
+    assert lb2[0] == 0.0 and float(lb2[1]) < 1e-12 and float(lb2[2]) > 1 - 1e-12
+
+
 # --------------------------------------------------------------------- GLU / block
 
 def _latent_identity(n, scale):
@@ -398,5 +445,5 @@ def pin_round_bf16(orc):
 PINS = [pin_act_quant_hand, pin_ternarize_hand, pin_pack_format, pin_quant_invariants,
         pin_quant_literal_rmsnorm, pin_ternary_invariants, pin_bitlinear_hand,
         pin_bitlinear_brute, pin_recurrence_hand, pin_recurrence_unrolled, pin_mlgru_roles,
-        pin_mlgru_limits, pin_output_gate, pin_glu_identity, pin_block_residuals,
+        pin_mlgru_limits, pin_output_gate, pin_hgrn_lower_bound_gate, pin_hgrn_lower_bounds, pin_glu_identity, pin_block_residuals,
         pin_block_causal_and_carry, pin_block_stages, pin_embedding, pin_round_bf16]

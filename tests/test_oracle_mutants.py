@@ -27,8 +27,8 @@ MUTANTS = [
      "h = f[i] * h + c[i];"),
     ("recurrence_ignores_h0", "double h = h0 ? h0[b * D + d] : 0.0;", "double h = 0.0;"),
     ("mlgru_i_f_swapped",
-     "f[row * D + d] = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));",
-     "f[row * D + d] = sigmoid_d(r[d] + (f_bias ? (double)f_bias[d] : 0.0));"),
+     "double sg = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));",
+     "double sg = sigmoid_d(r[d] + (f_bias ? (double)f_bias[d] : 0.0));"),
     ("mlgru_bias_sign",
      "sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0))",
      "sigmoid_d(r[D + d] - (f_bias ? (double)f_bias[d] : 0.0))"),
@@ -57,6 +57,13 @@ MUTANTS = [
     ("quant_divides_by_max", "float v = rintf(p * s);", "float v = rintf((p * 127.0f) / me);"),
     ("quant_exact_quotient", "float v = rintf(p * s);",
      "float v = (float)rint((double)p * 127.0 / (double)me);"),
+    ("hgrn_bound_ignored", "f[row * D + d] = lb + (1.0 - lb) * sg;", "f[row * D + d] = sg;"),
+    ("hgrn_bound_as_scale", "f[row * D + d] = lb + (1.0 - lb) * sg;",
+     "f[row * D + d] = lb * sg;"),
+    ("hgrn_bound_inclusive_cumsum",
+     "            lb[l * D + d] = (float)(acc / tot);\n            acc += exp((double)G[l * D + d] - mx);",
+     "            acc += exp((double)G[l * D + d] - mx);\n            lb[l * D + d] = (float)(acc / tot);"),
+    ("hgrn_bound_unnormalised", "lb[l * D + d] = (float)(acc / tot);", "lb[l * D + d] = (float)acc;"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

@@ -153,6 +153,63 @@ int orc_unpack(const uint32_t *packed, int64_t n, int64_t k, int8_t *q) {
     return 0;
 }
 
+/* ------------------------------------------- base-3 "trit" packing (1.6 bits)
+ * HackerPapers page on arXiv 2406.02528 (HN discussion list): the weights are ternary digits,
+ * "trits", with values in {-1, 0, 1}.  Five trits fit in a byte (3^5 = 243 <= 256).
+ * Format (a reading; the pages give none): codes c = q + 1 in {0,1,2}; a row is cut into
+ * words of 4 bytes = 20 trits; byte j (0..3) of word w holds the codes of
+ * k = 20w + 4i + j for i = 0..4 as the base-3 number v = sum_i c_i * 3^(4-i) (i = 0 most
+ * significant), stored as b = ceil(256*v/243); a row is padded with code 1 (q = 0) to whole
+ * 16-byte chunks of 80 trits.  The oracle decodes by the definition: v = floor(243*b/256)
+ * (exact inverse, as 243/256 < 1) and base-3 digits by repeated division.
+ */
+int64_t orc_trit_row_bytes(int64_t k) { return 16 * ((k + 79) / 80); }
+
+static int64_t trit_pos(int64_t byte_in_row, int i) {   /* k of digit i of a row byte */
+    int64_t w = byte_in_row / 4, j = byte_in_row % 4;
+    return 20 * w + 4 * i + j;
+}
+
+int orc_pack_trits(const int8_t *q, int64_t n, int64_t k, uint8_t *packed) {
+    if (!q || !packed || n <= 0 || k <= 0) return -1;
+    int64_t rb = orc_trit_row_bytes(k);
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t by = 0; by < rb; ++by) {
+            int v = 0;
+            for (int i = 0; i < 5; ++i) {
+                int64_t kk = trit_pos(by, i);
+                int c = 1;                               /* padding: q = 0 */
+                if (kk < k) {
+                    int qq = q[r * k + kk];
+                    if (qq < -1 || qq > 1) return -1;
+                    c = qq + 1;
+                }
+                v = 3 * v + c;
+            }
+            packed[r * rb + by] = (uint8_t)((256 * v + 242) / 243);   /* ceil(256 v / 243) */
+        }
+    return 0;
+}
+
+int orc_unpack_trits(const uint8_t *packed, int64_t n, int64_t k, int8_t *q) {
+    if (!q || !packed || n <= 0 || k <= 0) return -1;
+    int64_t rb = orc_trit_row_bytes(k);
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t by = 0; by < rb; ++by) {
+            int b = packed[r * rb + by];
+            int v = (243 * b) / 256;
+            if ((256 * v + 242) / 243 != b) return -2;   /* not the encoding of any v */
+            int c[5];
+            for (int i = 4; i >= 0; --i) { c[i] = v % 3; v /= 3; }
+            for (int i = 0; i < 5; ++i) {
+                int64_t kk = trit_pos(by, i);
+                if (kk < k) q[r * k + kk] = (int8_t)(c[i] - 1);
+                else if (c[i] != 1) return -2;           /* padding must be q = 0 */
+            }
+        }
+    return 0;
+}
+
 /* ------------------------------------------------- O3 activation quantization
  * [DC-core] RMSNorm before quantization; [HL-fbl] norm -> quantize -> accumulate.
  * Per row: p = fl32(x*gamma); m = max|p| floored at 1e-5; s = fl32(127/m);

@@ -57,6 +57,10 @@ class Oracle:
         L.orc_gated_recurrence.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.orc_mlgru.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, f64, i32, vp, vp]
         L.orc_hgrn_lower_bounds.argtypes = [vp, i64, i64, vp]
+        L.orc_trit_row_bytes.argtypes = [i64]
+        L.orc_trit_row_bytes.restype = i64
+        L.orc_pack_trits.argtypes = [vp, i64, i64, vp]
+        L.orc_unpack_trits.argtypes = [vp, i64, i64, vp]
         L.orc_glu.argtypes = [vp, i64, C.POINTER(OrcLinear), C.POINTER(OrcLinear),
                               C.POINTER(OrcLinear), f64, i32, vp, vp]
         L.orc_block.argtypes = ([vp, i64, i64] + [C.POINTER(OrcLinear)] * 7 +
@@ -102,6 +106,28 @@ class Oracle:
         rc = self.lib.orc_unpack(_p(packed), n, k, _p(q))
         if rc:
             raise ValueError(f"orc_unpack failed ({rc})")
+        return q
+
+    def trit_row_bytes(self, k: int) -> int:
+        return int(self.lib.orc_trit_row_bytes(k))
+
+    def pack_trits(self, q: np.ndarray) -> np.ndarray:
+        """Base-3 packing, 5 trits per byte: [n, k] int8 -> [n, trit_row_bytes(k)] uint8."""
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        n, k = q.shape
+        out = np.empty((n, self.trit_row_bytes(k)), np.uint8)
+        rc = self.lib.orc_pack_trits(_p(q), n, k, _p(out))
+        if rc:
+            raise ValueError(f"orc_pack_trits failed ({rc})")
+        return out
+
+    def unpack_trits(self, packed: np.ndarray, k: int) -> np.ndarray:
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        n = packed.shape[0]
+        q = np.empty((n, k), np.int8)
+        rc = self.lib.orc_unpack_trits(_p(packed), n, k, _p(q))
+        if rc:
+            raise ValueError(f"orc_unpack_trits failed ({rc})")
         return q
 
     # -------------------------------------------------------------- activations

@@ -78,6 +78,70 @@ def pin_pack_format(orc):
         raise AssertionError("code 3 accepted")
 
 
+def pin_trit_pack_hand(orc):
+    """Base-3 packing, five trits per byte: hand-worked bytes from the definition
+    b = ceil(256 v / 243), v = sum_i c_i 3^(4-i); the strided byte layout of a 20-trit word;
+    padding with code 1; the inverse v = floor(243 b / 256); a byte no group packs to."""
+    g = _golden("trit_pack_hand.json")
+    for case in g["bytes"]:
+        c = case["codes"]
+        # a 20-trit row whose byte 0 holds these codes and whose other bytes are all zeros (q = 0)
+        q = np.zeros((1, 20), np.int8)
+        for i, ci in enumerate(c):
+            q[0, 4 * i] = ci - 1
+        p = orc.pack_trits(q)
+        assert int(p[0, 0]) == case["b"], (c, int(p[0, 0]))
+        assert np.all(p[0, 1:] == 128)
+        assert np.array_equal(orc.unpack_trits(p, 20), q)
+    r = g["row20"]
+    q = np.array([r["q"]], np.int8)
+    p = orc.pack_trits(q)
+    assert p[0].tolist() == r["packed"], p[0].tolist()
+    assert np.array_equal(orc.unpack_trits(p, 20), q)
+    r = g["row64_plus_one"]
+    p = orc.pack_trits(np.full((1, r["k"]), r["q_value"], np.int8))
+    assert p[0].tolist() == r["packed"], p[0].tolist()
+    inv = g["inverse"]
+    row = np.full((1, 16), 128, np.uint8)
+    row[0, 0] = inv["b"]
+    qq = orc.unpack_trits(row, 20)
+    assert [int(qq[0, 4 * i]) + 1 for i in range(5)] == inv["codes"]
+    for bad in (g["invalid_byte"]["b"],):
+        row[0, 0] = bad
+        try:
+            orc.unpack_trits(row, 20)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"byte {bad} accepted")
+    row[0, 0] = 128
+    row64 = np.array([r["packed"]], np.uint8)
+    row64[0, 12] = 255                       # padding digits 1..4 of word 3 set to code 2
+    try:
+        orc.unpack_trits(row64, 64)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("non-zero padding accepted")
+
+
+def pin_trit_invariants(orc):
+    """Round trip on random ternary rows of several lengths; the trit and 2-bit formats
+    decode to the same weights; only 243 byte values ever occur; a row costs 16 bytes per
+    80 weights (1.6 bits each)."""
+    rng = np.random.default_rng(21)
+    seen = set()
+    for k in (64, 80, 1024, 2048, 2816):
+        q = rng.integers(-1, 2, (33, k)).astype(np.int8)
+        p = orc.pack_trits(q)
+        assert p.shape == (33, 16 * ((k + 79) // 80))
+        assert np.array_equal(orc.unpack_trits(p, k), q)
+        assert np.array_equal(orc.unpack_trits(p, k), orc.unpack(orc.pack(q), k))
+        seen |= set(np.unique(p).tolist())
+    assert len(seen) <= 243 and 1 not in seen
+    assert orc.trit_row_bytes(2048) == 416 and orc.trit_row_bytes(80) == 16
+
+
 def pin_quant_invariants(orc):
     """q in [-127,127]; every non-zero row reaches +-127 at its max; sign kept; monotone;
     scaling the row by 2^k leaves q unchanged; rowsum is the sum of q."""
@@ -442,7 +506,8 @@ def pin_round_bf16(orc):
     assert got[5] == round(1e-40 / 2.0**-133) * 2.0**-133
 
 
-PINS = [pin_act_quant_hand, pin_ternarize_hand, pin_pack_format, pin_quant_invariants,
+PINS = [pin_act_quant_hand, pin_ternarize_hand, pin_pack_format, pin_trit_pack_hand,
+        pin_trit_invariants, pin_quant_invariants,
         pin_quant_literal_rmsnorm, pin_ternary_invariants, pin_bitlinear_hand,
         pin_bitlinear_brute, pin_recurrence_hand, pin_recurrence_unrolled, pin_mlgru_roles,
         pin_mlgru_limits, pin_output_gate, pin_hgrn_lower_bound_gate, pin_hgrn_lower_bounds, pin_glu_identity, pin_block_residuals,

@@ -64,6 +64,13 @@ MUTANTS = [
      "            lb[l * D + d] = (float)(acc / tot);\n            acc += exp((double)G[l * D + d] - mx);",
      "            acc += exp((double)G[l * D + d] - mx);\n            lb[l * D + d] = (float)(acc / tot);"),
     ("hgrn_bound_unnormalised", "lb[l * D + d] = (float)(acc / tot);", "lb[l * D + d] = (float)acc;"),
+    ("trit_contiguous_layout", "return 20 * w + 4 * i + j;", "return 20 * w + 5 * j + i;"),
+    ("trit_floor_not_ceil", "packed[r * rb + by] = (uint8_t)((256 * v + 242) / 243);",
+     "packed[r * rb + by] = (uint8_t)((256 * v) / 243);"),
+    ("trit_pad_code_zero", "int c = 1;                               /* padding: q = 0 */",
+     "int c = 0;"),
+    ("trit_digits_reversed", "for (int i = 4; i >= 0; --i) { c[i] = v % 3; v /= 3; }",
+     "for (int i = 0; i < 5; ++i) { c[i] = v % 3; v /= 3; }"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

@@ -1,14 +1,17 @@
 """Benchmark: MatMul-free LM block forward on one MI355X.
 
-A step is one pass of the whole block (RMSNorm + int8 quantization, i|f|g ternary
-BitLinear, chunked MLGRU scan with RMSNorm-swish gate, o_proj + residual, GLU with
-SiLU(gate)*up, down + residual) over one batch of synthetic input already resident in
-HBM.  Default workload: the 370M-shaped block, 8 sequences x 2048 tokens, hidden 1024,
-GLU 2816, bf16 activations, ternary weights from N(0, 0.02^2) latents.
+Default (the largest single-GPU workload, `2.7B-longctx`): a step is one prefill of the
+32-layer 2.7B-shaped stack over 2 sequences x 32768 tokens -- in every layer RMSNorm + int8
+quantization, the i|f|g ternary BitLinear, the chunked MLGRU scan with the RMSNorm-swish
+gate, o_proj + residual, the GLU with SiLU(gate)*up and down + residual -- on synthetic
+bf16 activations already resident in HBM and ternary weights from N(0, 0.02^2) latents.
 
-Prints one JSON line.  `roofline` describes the dominant kernel (the gate|up int8-MFMA
-GEMM), timed with HIP events on the launch stream during the timed steps;
-`cpu_baseline` is the CPU oracle timed on a causal prefix of the same workload.
+Prints one JSON line.  `roofline` describes the dominant kernel (the gate|up int8-MFMA GEMM)
+with its launch durations from HIP events recorded on the launch stream during the timed
+steps; `cpu_baseline` is the CPU oracle timed on a bounded causal sample of the same
+workload.  `extra_workloads` carries the other shapes measured the same way: the 2.7B block
+(16 x 2048 tokens), the 370M block (8 x 2048 tokens) and the 24-layer 1.3B decode stack at
+batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches).
 """
 from __future__ import annotations
 
@@ -25,39 +28,52 @@ sys.path.insert(0, ROOT)
 METRIC = "block tokens/s; % peak HBM GB/s (decode), % int8 MFMA util (prefill)"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, tera-ops/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gateup_370M-block_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "ternary_weight_matmul_bitlinear_amd", "csrc", "gemm_prefill.hip")
+CSRC = os.path.join(ROOT, "ternary_weight_matmul_bitlinear_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+DEFAULT_EXTRAS = "2.7B-block,370M-block,1.3B-decode@1,1.3B-decode@64"
+DATA = "synthetic (seeded N(0,1) activations / uniform token ids, ternary weights from N(0,0.02^2) latents)"
 
 
-def _src_hash(path: str) -> str:
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+# ------------------------------------------------------------------------ helpers
+
+def _src_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic(per_launch_key: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, or
-    None when the summary is missing or the kernel source changed since it was taken."""
+def traffic(kernel_id: str, workload: str, srcs: tuple, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per step) of a kernel from its committed counter summary
+    (profiles/<kernel_id>_<workload>_traffic.json), or None when the summary is missing or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel_id}_{workload}_traffic.json")
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha256_16") != _src_hash(KERNEL_SRC):
+    if t.get("kernel_src_sha256_16") != _src_hash(*srcs):
         return None
-    return t.get(per_launch_key)
+    return t.get(key)
 
 
-def cpu_baseline(w, x_np, W, B0: int, T0: int):
-    """Oracle block forward on the causal prefix x[:B0, :T0] (bounded CPU sample)."""
-    import numpy as np
-    from oracle import oracle as O
-    orc = O.get()
-    xs = np.ascontiguousarray(x_np[:B0, :T0])
-    orc.block(np.ascontiguousarray(xs[:1, :8]), W, resid_bf16=w.bf16)  # warm-up
-    t = time.perf_counter()
-    r = orc.block(xs, W, resid_bf16=w.bf16)
-    dt = time.perf_counter() - t
-    return r, dt, orc.max_threads()
+def cpu_info(orc) -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cores": orc.max_threads(), "nproc": nproc, "cpu_model": model}
 
 
 def spin_up(fn, seconds: float) -> None:
@@ -79,44 +95,90 @@ def spin_up(fn, seconds: float) -> None:
         torch.cuda.synchronize()
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--spin-up", type=float, default=0.5,
-                    help="seconds of untimed steps before the warm-up steps (clock ramp)")
-    ap.add_argument("--workload", default="370M-block")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=128,
-                    help="tokens per sequence of the causal prefix timed on the CPU")
-    ap.add_argument("--batch", type=int, default=None,
-                    help="decode stack: sequences per step (default: the workload's B)")
-    ap.add_argument("--regime", choices=("auto", "decode", "prefill", "tiles"), default="auto",
-                    help="BitLinear kernel choice (auto: by token count; decode: weight "
-                         "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
-    ap.add_argument("--no-kernel-sweep", dest="kernel_sweep", action="store_false",
-                    help="decode stacks: skip the per-kernel BitLinear streaming sweep")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one plain 256 MiB device copy (counter calibration)")
-    args = ap.parse_args()
+def log(msg: str) -> None:
+    print(f"# {msg}", file=sys.stderr, flush=True)
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
-              f"asked for --gpus {args.gpus} / WORLD_SIZE={world}", file=sys.stderr)
-        return 2
 
+def rel_err(got, ref) -> float:
+    """max |got - ref| / (|ref| + rms of ref's row)."""
+    import numpy as np
+    got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(got.shape)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    return float(np.max(np.abs(got - ref) / (np.abs(ref) + rms)))
+
+
+def timed_events(fams, fn, steps: int):
+    """Run fn(i) for `steps` steps with the library's HIP events around every launch of the
+    given kernel families; returns (wall ms per step, {family: (launches, total ms)})."""
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api
+    api.timing_reset()
+    api.timing_families(fams)
+    api.timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    api.timing_enable(False)
+    return wall, {f: api.timing_query(f) for f in fams}
+
+
+def gemm_families(M: int, D: int, F: int, ab: int, per_step_layers: int = 1):
+    """Algorithmic work per step of each kernel family of a prefill block: int8 ops of the
+    GEMMs; bytes of the HBM-bound kernels (the scan reads the i|f|g pre-activations once
+    and writes the int8 o_proj input with its scale and code sum; the row quantizers read x,
+    y1 (D wide) and the GLU hidden (F wide) and write int8 codes + 8 bytes per row)."""
+    L = per_step_layers
+    return {"gemm_ifg": ("mfma", L * 2.0 * M * D * 3 * D), "gemm_o": ("mfma", L * 2.0 * M * D * D),
+            "gemm_gateup": ("mfma", L * 2.0 * M * D * 2 * F),
+            "gemm_down": ("mfma", L * 2.0 * M * F * D),
+            "scan": ("hbm", L * M * (3 * D * ab + D + 8.0)),
+            "quant": ("hbm", L * M * (2 * D * (ab + 1) + F * (ab + 1) + 24.0))}
+
+
+def family_breakdown(fn, nb: int, work: dict) -> dict:
+    """A separate pass with events around every launch: per-family launch counts, durations
+    and fractions of their roofline."""
+    _, q = timed_events(["quant", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "scan"], fn, nb)
+    fams = {}
+    for fam, (n, ms) in q.items():
+        if not n:
+            continue
+        d = {"launches_per_step": n / nb, "ms_per_launch": ms / n, "ms_per_step": ms / nb}
+        if fam in work:
+            bound, amount = work[fam]
+            sec = ms / nb * 1e-3
+            if bound == "mfma":
+                d.update(tops=amount / sec / 1e12, mfma_frac=amount / sec / 1e12 / PEAK_INT8_TOPS)
+            else:
+                d.update(gbs=amount / sec / 1e9, hbm_frac=amount / sec / 1e9 / PEAK_HBM_GBS)
+        fams[fam] = d
+    return fams
+
+
+def gateup_roofline(w, M: int, n: int, ms: float, note: str) -> dict:
+    ops = 2.0 * M * w.D * (2 * w.F)
+    achieved = ops / (ms / n * 1e-3) / 1e12 if n else None
+    return {"kernel": f"gemm_gateup (int8 MFMA, SiLU(gate)*up epilogue){note}", "bound": "mfma",
+            "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_INT8_TOPS if achieved else None,
+            "traffic": traffic("gemm_gateup", w.name, ("gemm_prefill.hip",)),
+            "algorithmic_ops_per_launch": ops, "launches_timed": n,
+            "us_per_launch": ms / n * 1e3 if n else None}
+
+
+# ------------------------------------------------------------------ prefill block
+
+def bench_block(w, args, orc) -> dict:
+    """One block over B x T tokens (the 370M and 2.7B blocks)."""
     import numpy as np
     import torch
 
     from ternary_weight_matmul_bitlinear_amd import api, synth
 
-    w = synth.WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    api.set_regime({"auto": 0, "decode": 1, "prefill": 2, "tiles": 3}[args.regime])
-    if w.layers != 1 or w.vocab:
-        return bench_stack(args, w)
     dt = torch.bfloat16 if w.bf16 else torch.float32
     lat = synth.layer_latents(w, 0)
     fb = np.full(w.D, w.f_bias, np.float32) if w.f_bias else None
@@ -126,114 +188,232 @@ def main() -> int:
     y = torch.empty_like(x)
     h = torch.zeros((w.B, w.D), dtype=torch.float32, device="cuda")
     ws = torch.empty(api.block_workspace_bytes(blk, w.B, w.T), dtype=torch.uint8, device="cuda")
-    M, D, F = w.M, w.D, w.F
-    print(f"# workload {w.name}: B={w.B} T={w.T} D={D} F={F} dtype={dt}", file=sys.stderr,
-          flush=True)
+    M = w.M
+    log(f"workload {w.name}: B={w.B} T={w.T} D={w.D} F={w.F}")
 
-    spin_up(lambda: api.block_forward(blk, x, h_state=h, y=y, ws=ws), args.spin_up)
-    for _ in range(args.warmup):
-        h.zero_()
+    def step(i):
         api.block_forward(blk, x, h_state=h, y=y, ws=ws)
-    torch.cuda.synchronize()
 
-    # timed region: HIP events only around the dominant kernel (gate|up GEMM), on the
-    # stream it is launched on, so the measured stream stays close to an untimed one
-    api.timing_reset()
-    api.timing_families(["gemm_gateup"])
-    api.timing_enable(True)
+    spin_up(lambda: step(0), args.spin_up)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: HIP events only around the dominant kernel (gate|up GEMM), on the stream
+    # it is launched on, so the measured stream stays close to an untimed one
+    ms_step, q = timed_events(["gemm_gateup"], step, args.steps)
+    n, ms = q["gemm_gateup"]
+    log(f"{w.name}: timed {args.steps} steps: {ms_step:.3f} ms/step")
+    fams = family_breakdown(step, min(args.steps, 10), gemm_families(M, w.D, w.F, 2 if w.bf16 else 4))
+    out = {"workload": w.name, "value": M / (ms_step * 1e-3), "unit": "tokens/s",
+           "ms_per_step": ms_step, "steps": args.steps,
+           "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "F": w.F, "layers": 1,
+                      "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"},
+           "roofline": gateup_roofline(w, M, n, ms, ""), "kernels": fams}
+    if orc is not None:
+        # the timed steps chained the state; the sample is checked on a fresh prefill
+        h.zero_()
+        step(0)
+        torch.cuda.synchronize()
+        ct = args.cpu_tokens or (128 if w.D <= 1024 else 16)
+        B0, T0 = min(w.B, args.cpu_seqs), min(ct, w.T)
+        W = {k: orc.ternarize(lat[k]) for k in ("i", "f", "g", "o", "gate", "up", "down")}
+        xs = np.ascontiguousarray(x_np[:B0, :T0])
+        orc.block(np.ascontiguousarray(xs[:1, :2]), W, f_bias=fb, resid_bf16=w.bf16)  # warm-up
+        t = time.perf_counter()
+        r = orc.block(xs, W, f_bias=fb, resid_bf16=w.bf16)
+        cdt = time.perf_counter() - t
+        got = y.float().cpu().numpy()[:B0, :T0]
+        out["cpu_baseline"] = {
+            "value": B0 * T0 / cdt, "unit": "tokens/s", **cpu_info(orc), "kind": "oracle",
+            "sample": f"causal prefix: first {T0} tokens of {B0} of the {w.B} sequences "
+                      f"({B0 * T0} tokens), one block, {cdt:.1f} s",
+            "sample_max_rel_err_vs_gpu": rel_err(got, r["y"])}
+    return out
+
+
+# ------------------------------------------------------------- long-context stack
+
+def build_stack(w, with_oracle: bool, orc):
+    import numpy as np
+
+    from ternary_weight_matmul_bitlinear_amd import api, synth
+
+    fb = np.full(w.D, w.f_bias, np.float32) if w.f_bias else None
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        api.block_forward(blk, x, h_state=h, y=y, ws=ws)
+    blocks, Ws = [], []
+    for l in range(w.layers):
+        lat = synth.layer_latents(w, l)
+        blocks.append(api.Block.from_latents(lat, "cuda", f_bias=fb))
+        if with_oracle:
+            Ws.append({k: orc.ternarize(lat[k]) for k in ("i", "f", "g", "o", "gate", "up", "down")})
+        del lat
+        if (l + 1) % 8 == 0:
+            log(f"{w.name}: {l + 1} of {w.layers} layers built")
+    emb = head = None
+    qe = qh = None
+    if w.vocab:
+        E, H = synth.embedding_latents(w)
+        emb = api.TernaryLinear.from_latent(E)
+        head = api.TernaryLinear.from_latent(H)
+        if with_oracle:
+            qe, qh = orc.ternarize(E), orc.ternarize(H)
+        del E, H
+    log(f"{w.name}: {w.layers} layers built in {time.perf_counter() - t0:.1f} s")
+    return api.Stack(blocks, emb, head), Ws, qe, qh, fb
+
+
+def bench_longctx(w, args, orc) -> dict:
+    """The 32-layer 2.7B stack prefill over 2 x 32768 tokens."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api, synth
+
+    stack, Ws, _, _, fb = build_stack(w, orc is not None, orc)
+    B, T, D, F, L = w.B, w.T, w.D, w.F, w.layers
+    x_np = synth.activations(w)
+    x = torch.from_numpy(x_np).to("cuda").to(torch.bfloat16)
+    y = torch.empty_like(x)
+    ws = torch.empty(stack.workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        api.stack_forward(stack, B, T, x=x, ws=ws, y=y)
+
+    spin_up(lambda: step(0), args.spin_up)
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    api.timing_enable(False)
-    elapsed = t1 - t0
-    ms_step = elapsed * 1e3 / args.steps
-    value = M * args.steps / elapsed
-    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-    gn, gms = api.timing_query("gemm_gateup")
+    ms_step, q = timed_events(["gemm_gateup"], step, args.steps)
+    n, ms = q["gemm_gateup"]
+    log(f"{w.name}: timed {args.steps} steps: {ms_step:.3f} ms/step")
+    M = B * T
+    fams = family_breakdown(step, min(args.steps, 3), gemm_families(M, D, F, 2, L))
+    out = {"workload": w.name, "value": M / (ms_step * 1e-3), "unit": "tokens/s",
+           "ms_per_step": ms_step, "steps": args.steps,
+           "layer_tokens_per_s": M * L / (ms_step * 1e-3),
+           "config": {"workload": w.name, "B": B, "T": T, "D": D, "F": F, "layers": L,
+                      "forget_bias": w.f_bias, "activations": "bf16", "state": "fp32"},
+           "roofline": gateup_roofline(w, M, n, ms, f", one launch per layer"), "kernels": fams}
+    if orc is not None:
+        P = min(args.cpu_tokens_stack, T)
+        xo = np.ascontiguousarray(x_np[:, :P])
+        orc.block(np.ascontiguousarray(xo[:1, :1]), Ws[0], f_bias=fb, resid_bf16=True)  # warm-up
+        t = time.perf_counter()
+        for l in range(L):
+            xo = orc.block(xo, Ws[l], f_bias=fb, resid_bf16=True)["y"].astype(np.float32)
+        cdt = time.perf_counter() - t
+        got = y.float().cpu().numpy()[:, :P]
+        out["cpu_baseline"] = {
+            "value": B * P / cdt, "unit": "tokens/s", **cpu_info(orc), "kind": "oracle",
+            "sample": f"causal prefix: first {P} tokens of each of the {B} sequences through all "
+                      f"{L} layers ({B * P} tokens), {cdt:.1f} s",
+            "sample_max_rel_err_vs_gpu": rel_err(got, xo),
+            "sample_err_note": "independent 32-layer runs: near-tie int8 flips compound layer by layer"}
+    return out
 
-    # per-family breakdown: a separate, shorter pass with events around every launch
-    fams = {}
-    nb = min(args.steps, 10)
-    api.timing_reset()
-    api.timing_families(None)
-    api.timing_enable(True)
-    for _ in range(nb):
-        api.block_forward(blk, x, h_state=h, y=y, ws=ws)
-    torch.cuda.synchronize()
-    api.timing_enable(False)
-    # algorithmic work per step of each family: int8 ops of the GEMMs; bytes of the HBM-bound
-    # kernels (the scan reads the bf16 i|f|g pre-activations once and writes the int8 o_proj
-    # input with its scale and code sum; the row quantizers read x, y1 (D wide) and the GLU
-    # hidden (F wide) and write int8 codes + 8 bytes per row)
-    ab = 2 if w.bf16 else 4
-    work = {"gemm_ifg": ("mfma", 2.0 * M * D * 3 * D), "gemm_o": ("mfma", 2.0 * M * D * D),
-            "gemm_gateup": ("mfma", 2.0 * M * D * 2 * F), "gemm_down": ("mfma", 2.0 * M * F * D),
-            "scan": ("hbm", M * (3 * D * ab + D + 8.0)),
-            "quant": ("hbm", M * (2 * D * (ab + 1) + F * (ab + 1) + 24.0))}
-    for fam in ("quant", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemv", "scan"):
-        n, ms = api.timing_query(fam)
-        if n:
-            fams[fam] = {"launches_per_step": n / nb, "ms_per_launch": ms / n,
-                         "ms_per_step": ms / nb}
-            if fam in work:
-                bound, amount = work[fam]
-                sec = ms / nb * 1e-3
-                if bound == "mfma":
-                    fams[fam].update(tops=amount / sec / 1e12, mfma_frac=amount / sec / 1e12 / PEAK_INT8_TOPS)
-                else:
-                    fams[fam].update(gbs=amount / sec / 1e9, hbm_frac=amount / sec / 1e9 / PEAK_HBM_GBS)
 
-    # dominant kernel: gate|up GEMM, 2*M*K*N dense int8 ops per launch
-    ops = 2.0 * M * D * (2 * F)
-    achieved = ops / (gms / gn * 1e-3) / 1e12 if gn else None
-    traffic = _traffic("hbm_bytes_per_launch")
-    roofline = {"kernel": "gemm_gateup (int8 MFMA, SiLU(gate)*up epilogue)", "bound": "mfma",
-                "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                "frac": (achieved / PEAK_INT8_TOPS) if achieved else None, "traffic": traffic,
-                "algorithmic_ops_per_launch": ops}
+# ------------------------------------------------------------------- decode stack
 
-    if args.calibrate_copy:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
+def decode_bytes(B: int, D: int, F: int, V: int, L: int):
+    """Algorithmic bytes of a decode step's BitLinear launches (N*K/4 packed weights + rows
+    in + rows out, residual where added) and of the whole step (plus embedding rows and the
+    fp32 state read and written per layer).  Up to 4 rows the weight-streaming kernel
+    quantizes the bf16 rows itself; above, the k-split kernel reads int8 rows written by the
+    row quantizer."""
+    def bl(N, K, in_b, out_b, resid=0):
+        return N * K // 4 + B * K * in_b + B * N * out_b + B * N * resid
+    xin = 2 if B <= 4 else 1
+    per_layer = (bl(3 * D, D, xin, 2) + bl(D, D, 1, 2, 2) + bl(2 * F, D, xin, 0) + B * F * 2
+                 + bl(D, F, xin, 2, 2))
+    gemv = L * per_layer + bl(V, D, xin, 4)
+    return gemv, gemv + B * D // 4 + B * D * 2 + L * B * D * 4 * 2
+
+
+def bench_decode(w, args, batches, orc) -> list:
+    """The 24-layer 1.3B stack + ternary embedding and head, one token per sequence per
+    step, state carried; steps replayed from a captured HIP graph (a step is ~100-200
+    small launches whose host-side launch cost would otherwise dominate)."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api, synth
+
+    stack, Ws, qe, qh, _ = build_stack(w, orc is not None, orc)
+    D, F, L, V = w.D, w.F, w.layers, w.vocab
+    outs = []
+    fams = ["gemv", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemm"]
+    for B in batches:
+        steps = args.steps
+        hs = torch.zeros((L, B, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(stack.workspace_bytes(B, 1), dtype=torch.uint8, device="cuda")
+        ids_all = torch.from_numpy(synth.token_ids(w, args.warmup + steps, B)).to("cuda")
+        logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
+
+        def eager(i):
+            api.stack_forward(stack, B, 1, ids=ids_all[i], h_state=hs, want_y=False,
+                              want_logits=True, ws=ws, logits=logits)
+
+        for i in range(2):
+            eager(i)
         torch.cuda.synchronize()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        # the timed steps chained the state; parity is checked on a fresh prefill (h0 = 0)
-        h.zero_()
-        api.block_forward(blk, x, h_state=h, y=y, ws=ws)
+        # per-launch durations of the decode BitLinear launches: an eager pass with events
+        eager_ms, q = timed_events(fams, lambda i: eager(args.warmup + i), steps)
+        n = sum(v[0] for v in q.values())
+        ms = sum(v[1] for v in q.values())
+        # timed loop: graph replay of one captured step
+        ids_static = ids_all[0].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            api.stack_forward(stack, B, 1, ids=ids_static, h_state=hs, want_y=False,
+                              want_logits=True, ws=ws, logits=logits)
+        spin_up(lambda: g.replay(), args.spin_up)
+        for i in range(args.warmup):
+            ids_static.copy_(ids_all[i])
+            g.replay()
         torch.cuda.synchronize()
-        B0, T0 = w.B, min(args.cpu_sample_tokens, w.T)
-        W = {}
-        from oracle import oracle as O
-        orc = O.get()
-        for k in ("i", "f", "g", "o", "gate", "up", "down"):
-            W[k] = orc.ternarize(lat[k])
-        r, cdt, threads = cpu_baseline(w, x_np, W, B0, T0)
-        ref = r["y"]
-        got = y.float().cpu().numpy()[:B0, :T0].astype(np.float64)
-        rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-        err = float(np.max(np.abs(got - ref) / (np.abs(ref) + rms)))
-        cpu = {"value": B0 * T0 / cdt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"causal prefix: first {T0} tokens of each of the {B0} sequences "
-                         f"({B0 * T0} tokens), one block, {cdt:.1f} s",
-               "sample_max_rel_err_vs_gpu": err}
-
-    line = {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-            "data": "synthetic (seeded N(0,1) activations, ternary weights from N(0,0.02^2) latents)",
-            "config": {"workload": w.name, "B": w.B, "T": w.T, "D": D, "F": F,
-                       "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"},
-            "roofline": roofline, "cpu_baseline": cpu,
-            "kernels": fams, "kernels_note": f"separate {nb}-step pass, events around every launch; "
-                                             "mfma_frac / hbm_frac: the family's algorithmic work per "
-                                             "step over its summed launch time"}
-    print(json.dumps(line))
-    return 0
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ids_static.copy_(ids_all[args.warmup + i])
+            g.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+        del g
+        gemv_bytes, step_bytes = decode_bytes(B, D, F, V, L)
+        achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
+        name = f"{w.name}@{B}"
+        log(f"{name}: graph-replayed step {ms_step:.4f} ms, eager {eager_ms:.4f} ms")
+        res = {"workload": name, "value": B / (ms_step * 1e-3), "unit": "tokens/s",
+               "ms_per_step": ms_step, "steps": steps,
+               "config": {"workload": w.name, "B": B, "T": 1, "D": D, "F": F, "layers": L,
+                          "vocab": V, "activations": "bf16", "state": "fp32"},
+               "roofline": {"kernel": "decode BitLinear (dot4 weight streaming up to 4 rows, "
+                                      "k-split MFMA above), all launches of a step",
+                            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS if achieved else None,
+                            "traffic": traffic("decode_bitlinear", name,
+                                               ("gemv_decode.hip", "gemm_mid.hip"),
+                                               "hbm_bytes_per_step"),
+                            "algorithmic_bytes_per_step": gemv_bytes,
+                            "launches_per_step": n / steps},
+               "step_hbm_fraction": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "step_algorithmic_bytes": step_bytes, "eager_ms_per_step": eager_ms}
+        if orc is not None:
+            Bs = min(B, args.cpu_seqs_decode)
+            ids_np = synth.token_ids(w, 1, B)[0][:Bs]
+            t = time.perf_counter()
+            xo = orc.embedding(qe[0], qe[1], ids_np, resid_bf16=True).reshape(Bs, 1, D)
+            for l in range(L):
+                xo = orc.block(xo, Ws[l], resid_bf16=True)["y"].astype(np.float32)
+            orc.bitlinear(xo.reshape(Bs, D), *qh)
+            cdt = time.perf_counter() - t
+            res["cpu_baseline"] = {
+                "value": Bs / cdt, "unit": "tokens/s", **cpu_info(orc), "kind": "oracle",
+                "sample": f"one decode step (embedding, {L} layers, head) of {Bs} of the {B} "
+                          f"sequences, {cdt:.1f} s"}
+        outs.append(res)
+        del hs, ws, logits
+        torch.cuda.empty_cache()
+    return outs
 
 
 def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
@@ -262,18 +442,10 @@ def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
         for i in range(copies):
             api.bitlinear_forward(ws[i], x)
         torch.cuda.synchronize()
-        api.timing_reset()
-        api.timing_families(fams)
-        api.timing_enable(True)
         reps = max(copies, 40)
-        for i in range(reps):
-            api.bitlinear_forward(ws[i % copies], x)
-        torch.cuda.synchronize()
-        api.timing_enable(False)
-        n = ms = 0
-        for f in fams:
-            nf, msf = api.timing_query(f)
-            n, ms = n + nf, ms + msf
+        _, q = timed_events(fams, lambda i: api.bitlinear_forward(ws[i % copies], x), reps)
+        n = sum(v[0] for v in q.values())
+        ms = sum(v[1] for v in q.values())
         bytes_ = wbytes + B * K * 2 + B * N * 2
         gbs = bytes_ * n / (ms * 1e-3) / 1e9
         out.append({"N": N, "K": K, "rows": B, "weight_copies": copies,
@@ -283,139 +455,97 @@ def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
     return out
 
 
-def bench_stack(args, w) -> int:
-    """Stack workloads.  1.3B-decode: one step = one token for each of B sequences through
-    the ternary embedding, 24 blocks (state carried) and the LM head; the weights (about
-    325 MB packed) exceed the 256 MB MALL, so every step streams them from HBM.
-    2.7B-longctx: one step = the 32-block prefill of 2 x 32768 tokens."""
-    import numpy as np
+# ---------------------------------------------------------------------------- main
+
+def run_workload(spec: str, args, orc):
+    from ternary_weight_matmul_bitlinear_amd import synth
+    name, _, b = spec.partition("@")
+    w = synth.WORKLOADS[name]
+    if w.vocab:
+        batches = [int(b)] if b else ([args.batch] if args.batch else [1, 64])
+        return bench_decode(w, args, batches, orc)
+    if w.layers > 1:
+        return [bench_longctx(w, args, orc)]
+    return [bench_block(w, args, orc)]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spin-up", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up steps (clock ramp)")
+    ap.add_argument("--workload", default="2.7B-longctx",
+                    help="headline workload (a name of synth.WORKLOADS, decode stacks as "
+                         "NAME@BATCH)")
+    ap.add_argument("--extras", default=DEFAULT_EXTRAS,
+                    help="comma-separated workloads measured after the headline ('' for none)")
+    ap.add_argument("--no-extras", dest="extras", action="store_const", const="")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="block workloads: tokens per sequence of the causal CPU sample "
+                         "(default: 128 at hidden size <= 1024, else 16)")
+    ap.add_argument("--cpu-seqs", type=int, default=16,
+                    help="block workloads: sequences of the causal CPU sample")
+    ap.add_argument("--cpu-tokens-stack", type=int, default=8,
+                    help="long-context stack: tokens per sequence of the causal CPU sample")
+    ap.add_argument("--cpu-seqs-decode", type=int, default=16,
+                    help="decode stack: sequences of the one-step CPU sample")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="decode stack without @BATCH: sequences per step")
+    ap.add_argument("--regime", choices=("auto", "decode", "prefill", "tiles"), default="auto",
+                    help="BitLinear kernel choice (auto: by token count; decode: weight "
+                         "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
+    ap.add_argument("--kernel-sweep", action="store_true",
+                    help="decode stacks: also time single BitLinear launches on rotated weights")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"asked for --gpus {args.gpus} / WORLD_SIZE={world}", file=sys.stderr)
+        return 2
+
     import torch
 
-    from ternary_weight_matmul_bitlinear_amd import api, synth
+    from ternary_weight_matmul_bitlinear_amd import api
 
-    D, F, L = w.D, w.F, w.layers
-    fb = np.full(D, w.f_bias, np.float32) if w.f_bias else None
-    t_build = time.perf_counter()
-    blocks = []
-    for l in range(L):
-        blocks.append(api.Block.from_latents(synth.layer_latents(w, l), "cuda", f_bias=fb))
-    emb = head = None
-    if w.vocab:
-        E, H = synth.embedding_latents(w)
-        emb = api.TernaryLinear.from_latent(E)
-        head = api.TernaryLinear.from_latent(H)
-        del E, H
-    stack = api.Stack(blocks, emb, head)
-    print(f"# workload {w.name}: {L} layers, D={D} F={F}; weights built in "
-          f"{time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+    torch.cuda.set_device(0)
+    api.set_regime({"auto": 0, "decode": 1, "prefill": 2, "tiles": 3}[args.regime])
+    orc = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        orc = O.get()
 
-    decode = bool(w.vocab)
-    B = args.batch or w.B
-    T = 1 if decode else w.T
-    steps = args.steps
-    hs = torch.zeros((L, B, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(stack.workspace_bytes(B, T), dtype=torch.uint8, device="cuda")
-    if decode:
-        ids_all = torch.from_numpy(synth.token_ids(w, args.warmup + steps, B)).to("cuda")
-        logits = torch.empty((B, w.vocab), dtype=torch.float32, device="cuda")
-
-        def step(i):
-            api.stack_forward(stack, B, 1, ids=ids_all[i], h_state=hs, want_y=False,
-                              want_logits=True, ws=ws, logits=logits)
-    else:
-        x = torch.from_numpy(synth.activations(w)).to("cuda").to(torch.bfloat16)
-        y = torch.empty_like(x)
-
-        def step(i):
-            hs.zero_()
-            api.stack_forward(stack, B, T, x=x, ws=ws, y=y)
-
-    spin_up(lambda: step(0), args.spin_up)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # per-launch durations of the dominant kernel family: an eager pass with events
-    # decode: every BitLinear launch of the step (the dot4 kernel for a few rows, the k-split
-    # MFMA kernel for more, both under their own family names)
-    fams = (["gemv", "gemm_ifg", "gemm_o", "gemm_gateup", "gemm_down", "gemm"] if decode
-            else ["gemm_gateup"])
-    api.timing_reset()
-    api.timing_families(fams)
-    api.timing_enable(True)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-    api.timing_enable(False)
-    n, ms = 0, 0.0
-    for f in fams:
-        nf, msf = api.timing_query(f)
-        n, ms = n + nf, ms + msf
-    graph_ms = None
-    if decode:
-        # the timed loop replays one captured step (a HIP graph): a decode step is ~120 small
-        # launches, whose host-side launch cost would otherwise dominate
-        ids_static = ids_all[0].clone()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            api.stack_forward(stack, B, 1, ids=ids_static, h_state=hs, want_y=False,
-                              want_logits=True, ws=ws, logits=logits)
-        for i in range(args.warmup):
-            ids_static.copy_(ids_all[i])
-            g.replay()
+    res = run_workload(args.workload, args, orc)
+    head, rest = res[0], res[1:]
+    extras = list(rest)
+    for spec in [s for s in args.extras.split(",") if s and s != args.workload]:
+        extras.extend(run_workload(spec, args, orc))
+        torch.cuda.empty_cache()
+    if args.kernel_sweep:
+        from ternary_weight_matmul_bitlinear_amd import synth
+        w3 = synth.WORKLOADS["1.3B-decode"]
+        head["decode_bitlinear_kernels"] = {
+            f"rows={b}": decode_kernel_sweep(b, w3.D, w3.F, w3.vocab) for b in (1, 64)}
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            ids_static.copy_(ids_all[args.warmup + i])
-            g.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        graph_ms = elapsed * 1e3 / steps
-    else:
-        elapsed = eager_ms * steps / 1e3
-    ms_step = elapsed * 1e3 / steps
-    value = B * T * steps / elapsed
 
-    if decode:
-        # algorithmic bytes of the decode BitLinear launches (N*K/4 packed weights + rows in
-        # + rows out, residual where added), and of the whole step (plus embedding rows and
-        # the fp32 state read and written per layer)
-        def bl(N, K, in_b, out_b, resid=0):
-            return N * K // 4 + B * K * in_b + B * N * out_b + B * N * resid
-        # the dot4 kernel (up to 4 rows) quantizes bf16 rows itself; the k-split kernel reads
-        # int8 rows written by the row quantizer
-        xin = 2 if B <= 4 else 1
-        per_layer = (bl(3 * D, D, xin, 2) + bl(D, D, 1, 2, 2) + bl(2 * F, D, xin, 0) + B * F * 2
-                     + bl(D, F, xin, 2, 2))
-        gemv_bytes = L * per_layer + bl(w.vocab, D, xin, 4)
-        step_bytes = gemv_bytes + B * D // 4 + B * D * 2 + L * B * D * 4 * 2
-        achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
-        roofline = {"kernel": "decode BitLinear (dot4 weight streaming up to 4 rows, k-split "
-                              "MFMA above), all launches of a step",
-                    "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": None,
-                    "algorithmic_bytes_per_step": gemv_bytes}
-        extra = {"step_hbm_fraction": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                 "step_algorithmic_bytes": step_bytes, "eager_ms_per_step": eager_ms,
-                 "graph_ms_per_step": graph_ms}
-        if args.kernel_sweep:
-            extra["decode_bitlinear_kernels"] = decode_kernel_sweep(B, D, F, w.vocab)
-    else:
-        ops = 2.0 * (B * T) * D * (2 * F)
-        achieved = ops * n / (ms * 1e-3) / 1e12 if n else None
-        roofline = {"kernel": "gemm_gateup (int8 MFMA, SiLU(gate)*up epilogue), all layers",
-                    "bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS,
-                    "unit": "TFLOP/s", "frac": achieved / PEAK_INT8_TOPS if achieved else None,
-                    "traffic": None, "algorithmic_ops_per_launch": ops}
-        extra = {}
-    line = {"metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-            "data": "synthetic (seeded ids / N(0,1) activations, ternary weights from N(0,0.02^2) latents)",
-            "config": {"workload": w.name, "B": B, "T": T, "D": D, "F": F, "layers": L,
-                       "vocab": w.vocab or None, "activations": "bf16", "state": "fp32"},
-            "roofline": roofline, "cpu_baseline": None, **extra}
+    line = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": DATA, "config": head["config"], "roofline": head["roofline"],
+            "cpu_baseline": head.get("cpu_baseline")}
+    for k, v in head.items():
+        if k not in line and k not in ("workload", "unit", "steps"):
+            line[k] = v
+    line["extra_workloads"] = extras
     print(json.dumps(line))
     return 0
 

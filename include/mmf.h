@@ -15,7 +15,9 @@
  *                the ternary weights inside one fused kernel.
  *   [HL-hgrn]    same page, section "HGRN attention": block input -> RMSNorm -> i/f/g
  *                projections -> gated recurrence -> g_norm (RMSNorm fused with a swish gate)
- *                -> o_proj; default model: hidden 2048, vocabulary 32000, 24 layers.
+ *                -> o_proj.
+ *   [HL-init]    same page, section "Installation and model initialization": the default
+ *                configuration has hidden size 2048, a 32000-entry embedding and 24 layers.
  *
  * Arithmetic, shared by every entry point:
  *   - activation quantization of a row x[0..K) with gain gamma: p = fl32(x*gamma),
@@ -28,8 +30,9 @@
  *     state); output gate o = RMSNorm_D(h)*gnorm_w * g*sigmoid(g) (MMF_GATE_SWISH_RMSNORM)
  *     or sigmoid(g)*h (MMF_GATE_SIGMOID);
  *   - GLU: SiLU(gate(x)) * up(x), then down;
- *   - block: y1 = x + o_proj(MLGRU(x)); y = y1 + GLU(y1).  Activations that leave a
- *     kernel are stored in the activation dtype (bf16 or fp32); the state h is fp32.
+ *   - block: y1 = x + o_proj(MLGRU(x)); y = y1 + GLU(y1).  Every tensor one module hands
+ *     to the next -- the i/f/g projections, the g_norm output, the GLU's gated product, y1
+ *     and y -- is materialised in the activation dtype (bf16 or fp32); the state h is fp32.
  *
  * Packed ternary weights: a matrix [N][K] (row n = output feature, K % 64 == 0) is stored
  * as N*K/16 uint32 words, row-major; element k = 16*j + 4*a + b of a row sits in word j at
@@ -219,7 +222,9 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
                   float *h_state, void *y, void *ws, size_t ws_bytes,
                   const mmf_capture *cap, hipStream_t stream);
 
-/* Ternary embedding gather: x[t][:] = s_E * q_E[ids[t]][:], rounded to dt.
+/* Ternary embedding gather of the 32000-entry embedding [HL-init], read as a ternary
+ * matrix like every other weight matrix [DC-ternary] (a reading: the pages do not say how
+ * the embedding is stored): x[t][:] = s_E * q_E[ids[t]][:], rounded to dt.
  * packed [vocab][D/16]; ids device int32 [m]; an id outside [0, vocab) yields a zero row. */
 int embedding_forward(const uint32_t *packed, float scale, int64_t vocab, int64_t D,
                       const int32_t *ids, int64_t m, void *x, mmf_dtype dt,

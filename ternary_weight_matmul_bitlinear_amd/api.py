@@ -5,6 +5,7 @@ the HIP kernels of libmmf.  Names follow the C entry points.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 from dataclasses import dataclass, field
 
@@ -26,9 +27,15 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream=None) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _on(stream):
+    """Make `stream` current for the call, so that outputs, workspaces and temporaries come
+    from the caching allocator's pool of the stream the kernels run on (a block handed back
+    at the end of the call is then reused only by work ordered after these kernels)."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _host(a, dtype):
@@ -168,61 +175,64 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
 def bitlinear_forward(w: TernaryLinear, x: torch.Tensor, out_dtype=None,
                       capture: StageCapture | None = None, stream=None) -> torch.Tensor:
     """y[m, N] = BitLinear(x[m, K]) (bitlinear_forward)."""
-    lib = L.lib()
-    x = x.contiguous()
-    m = x.numel() // w.K
-    out_dtype = x.dtype if out_dtype is None else out_dtype
-    y = torch.empty(x.shape[:-1] + (w.N,), dtype=out_dtype, device=x.device)
-    d = w.desc()
-    nb = lib.bitlinear_workspace_bytes(C.byref(d), m)
-    ws = _workspace(nb, x.device)
-    cap = C.byref(capture.desc()) if capture is not None else None
-    L.check("bitlinear_forward",
-            lib.bitlinear_forward(C.byref(d), _ptr(x), _dt(x.dtype), m, _ptr(y), _dt(out_dtype),
-                                  _ptr(ws), nb, cap, _stream(stream)))
-    return y
+    with _on(stream):
+        lib = L.lib()
+        x = x.contiguous()
+        m = x.numel() // w.K
+        out_dtype = x.dtype if out_dtype is None else out_dtype
+        y = torch.empty(x.shape[:-1] + (w.N,), dtype=out_dtype, device=x.device)
+        d = w.desc()
+        nb = lib.bitlinear_workspace_bytes(C.byref(d), m)
+        ws = _workspace(nb, x.device)
+        cap = C.byref(capture.desc()) if capture is not None else None
+        L.check("bitlinear_forward",
+                lib.bitlinear_forward(C.byref(d), _ptr(x), _dt(x.dtype), m, _ptr(y), _dt(out_dtype),
+                                      _ptr(ws), nb, cap, _stream()))
+        return y
 
 
 def mlgru_scan(ifg: torch.Tensor, f_bias=None, h0=None, gnorm_w=None, eps: float = 1e-6,
                gate_mode: int = 0, out_dtype=None, h_out: torch.Tensor | None = None,
                stream=None):
     """MLGRU + output gate over ifg [B, T, 3D] (mlgru_scan).  Returns (out, h_T)."""
-    lib = L.lib()
-    ifg = ifg.contiguous()
-    B, T, D3 = ifg.shape
-    D = D3 // 3
-    out_dtype = ifg.dtype if out_dtype is None else out_dtype
-    out = torch.empty((B, T, D), dtype=out_dtype, device=ifg.device)
-    if h_out is None:
-        h_out = torch.empty((B, D), dtype=torch.float32, device=ifg.device)
-    a = L.mmf_mlgru_args(_ptr(ifg), _dt(ifg.dtype), _ptr(f_bias), _ptr(h0), _ptr(h_out),
-                         _ptr(gnorm_w), eps, gate_mode, _ptr(out), _dt(out_dtype), B, T, D)
-    nb = lib.mlgru_workspace_bytes(B, T, D)
-    ws = _workspace(nb, ifg.device)
-    L.check("mlgru_scan", lib.mlgru_scan(C.byref(a), _ptr(ws), nb, _stream(stream)))
-    return out, h_out
+    with _on(stream):
+        lib = L.lib()
+        ifg = ifg.contiguous()
+        B, T, D3 = ifg.shape
+        D = D3 // 3
+        out_dtype = ifg.dtype if out_dtype is None else out_dtype
+        out = torch.empty((B, T, D), dtype=out_dtype, device=ifg.device)
+        if h_out is None:
+            h_out = torch.empty((B, D), dtype=torch.float32, device=ifg.device)
+        a = L.mmf_mlgru_args(_ptr(ifg), _dt(ifg.dtype), _ptr(f_bias), _ptr(h0), _ptr(h_out),
+                             _ptr(gnorm_w), eps, gate_mode, _ptr(out), _dt(out_dtype), B, T, D)
+        nb = lib.mlgru_workspace_bytes(B, T, D)
+        ws = _workspace(nb, ifg.device)
+        L.check("mlgru_scan", lib.mlgru_scan(C.byref(a), _ptr(ws), nb, _stream()))
+        return out, h_out
 
 
 def glu_forward(gate: TernaryLinear, up: TernaryLinear, down: TernaryLinear, x: torch.Tensor,
                 residual: torch.Tensor | None = None, capture: BlockCapture | None = None,
                 stream=None) -> torch.Tensor:
     """y = down(SiLU(gate(x)) * up(x)) (+ residual) (glu_forward)."""
-    lib = L.lib()
-    x = x.contiguous()
-    m = x.numel() // gate.K
-    y = torch.empty_like(x)
-    dg, du, dd = gate.desc(), up.desc(), down.desc()
-    nb = lib.glu_workspace_bytes(C.byref(dg), C.byref(dd), m)
-    ws = _workspace(nb, x.device)
-    cap = None
-    if capture is not None:
-        cap = L.mmf_capture(_empty_stage(), _empty_stage(), capture.gateup.desc(), capture.down.desc())
-    L.check("glu_forward",
-            lib.glu_forward(C.byref(dg), C.byref(du), C.byref(dd), _ptr(x), _dt(x.dtype), m,
-                            _ptr(residual.contiguous() if residual is not None else None), _ptr(y),
-                            _ptr(ws), nb, C.byref(cap) if cap is not None else None,
-                            _stream(stream)))
-    return y
+    with _on(stream):
+        lib = L.lib()
+        x = x.contiguous()
+        m = x.numel() // gate.K
+        y = torch.empty_like(x)
+        dg, du, dd = gate.desc(), up.desc(), down.desc()
+        nb = lib.glu_workspace_bytes(C.byref(dg), C.byref(dd), m)
+        ws = _workspace(nb, x.device)
+        cap = None
+        if capture is not None:
+            cap = L.mmf_capture(_empty_stage(), _empty_stage(), capture.gateup.desc(), capture.down.desc())
+        L.check("glu_forward",
+                lib.glu_forward(C.byref(dg), C.byref(du), C.byref(dd), _ptr(x), _dt(x.dtype), m,
+                                _ptr(residual.contiguous() if residual is not None else None), _ptr(y),
+                                _ptr(ws), nb, C.byref(cap) if cap is not None else None,
+                                _stream()))
+        return y
 
 
 @dataclass
@@ -276,28 +286,30 @@ def block_forward(block: Block, x: torch.Tensor, h_state: torch.Tensor | None = 
                   y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
                   capture: BlockCapture | None = None, stream=None) -> torch.Tensor:
     """One block forward on x [B, T, D] (block_forward); h_state [B, D] fp32 is updated."""
-    lib = L.lib()
-    B, T, D = x.shape
-    if y is None:
-        y = torch.empty_like(x)
-    d = block.desc()
-    nb = lib.block_workspace_bytes(C.byref(d), B, T)
-    if ws is None or ws.numel() < nb:
-        ws = _workspace(nb, x.device)
-    cap = C.byref(capture.desc()) if capture is not None else None
-    L.check("block_forward",
-            lib.block_forward(C.byref(d), _ptr(x), _dt(x.dtype), B, T, _ptr(h_state), _ptr(y),
-                              _ptr(ws), ws.numel(), cap, _stream(stream)))
-    return y
+    with _on(stream):
+        lib = L.lib()
+        B, T, D = x.shape
+        if y is None:
+            y = torch.empty_like(x)
+        d = block.desc()
+        nb = lib.block_workspace_bytes(C.byref(d), B, T)
+        if ws is None or ws.numel() < nb:
+            ws = _workspace(nb, x.device)
+        cap = C.byref(capture.desc()) if capture is not None else None
+        L.check("block_forward",
+                lib.block_forward(C.byref(d), _ptr(x), _dt(x.dtype), B, T, _ptr(h_state), _ptr(y),
+                                  _ptr(ws), ws.numel(), cap, _stream()))
+        return y
 
 
 def embedding_forward(packed: torch.Tensor, scale: float, vocab: int, D: int,
                       ids: torch.Tensor, dtype=torch.bfloat16, stream=None) -> torch.Tensor:
-    x = torch.empty(ids.shape + (D,), dtype=dtype, device=ids.device)
-    L.check("embedding_forward",
-            L.lib().embedding_forward(_ptr(packed), scale, vocab, D, _ptr(ids), ids.numel(),
-                                      _ptr(x), _dt(dtype), _stream(stream)))
-    return x
+    with _on(stream):
+        x = torch.empty(ids.shape + (D,), dtype=dtype, device=ids.device)
+        L.check("embedding_forward",
+                L.lib().embedding_forward(_ptr(packed), scale, vocab, D, _ptr(ids), ids.numel(),
+                                          _ptr(x), _dt(dtype), _stream()))
+        return x
 
 
 class Stack:
@@ -327,22 +339,23 @@ def stack_forward(stack: Stack, B: int, T: int, ids: torch.Tensor | None = None,
                   ws: torch.Tensor | None = None, y: torch.Tensor | None = None,
                   logits: torch.Tensor | None = None, stream=None):
     """Run the stack (stack_forward).  Returns (y or None, logits or None)."""
-    lib = L.lib()
-    dev = (ids if ids is not None else x).device
-    D = stack.blocks[0].D
-    if want_y and y is None:
-        y = torch.empty((B, T, D), dtype=dtype, device=dev)
-    if want_logits and logits is None:
-        logits = torch.empty((B * T, stack.head.N), dtype=torch.float32, device=dev)
-    nb = stack.workspace_bytes(B, T)
-    if ws is None or ws.numel() < nb:
-        ws = _workspace(nb, dev)
-    L.check("stack_forward",
-            lib.stack_forward(C.byref(stack._desc), _ptr(ids), _ptr(x), _dt(dtype), B, T,
-                              _ptr(h_state), _ptr(y) if want_y else None,
-                              _ptr(logits) if want_logits else None, _ptr(ws), ws.numel(),
-                              _stream(stream)))
-    return (y if want_y else None), (logits if want_logits else None)
+    with _on(stream):
+        lib = L.lib()
+        dev = (ids if ids is not None else x).device
+        D = stack.blocks[0].D
+        if want_y and y is None:
+            y = torch.empty((B, T, D), dtype=dtype, device=dev)
+        if want_logits and logits is None:
+            logits = torch.empty((B * T, stack.head.N), dtype=torch.float32, device=dev)
+        nb = stack.workspace_bytes(B, T)
+        if ws is None or ws.numel() < nb:
+            ws = _workspace(nb, dev)
+        L.check("stack_forward",
+                lib.stack_forward(C.byref(stack._desc), _ptr(ids), _ptr(x), _dt(dtype), B, T,
+                                  _ptr(h_state), _ptr(y) if want_y else None,
+                                  _ptr(logits) if want_logits else None, _ptr(ws), ws.numel(),
+                                  _stream()))
+        return (y if want_y else None), (logits if want_logits else None)
 
 
 def timing_enable(on: bool = True) -> None:

@@ -35,12 +35,6 @@
 
 #include <type_traits>
 
-#ifndef MMF_UNPACK64
-#define MMF_UNPACK64 0
-#endif
-#ifndef MMF_GEMM_WN
-#define MMF_GEMM_WN 2
-#endif
 
 namespace mmf {
 
@@ -53,7 +47,7 @@ constexpr int B_BYTES = BN * BK / 4;      // 8 KB per stage
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int A_LOADS = A_BYTES / (NT * 16);  // direct 16-byte loads per thread per stage
 constexpr int B_LOADS = B_BYTES / (NT * 16);
-constexpr int WN = MMF_GEMM_WN, WM = 4 / WN;  // waves along N and along M
+constexpr int WN = 2, WM = 4 / WN;  // waves along N and along M
 constexpr int MI = BM / 32 / WM, NI = BN / 32 / WN;  // 32 x 32 MFMA blocks per wave
 constexpr int EP_PITCH = 36;  // floats per staged epilogue row (32 + 4 pad)
 static_assert(A_LOADS == 4 && B_LOADS == 2, "load split");
@@ -101,25 +95,10 @@ __device__ __forceinline__ void dma16(const void *base_p, uint32_t off, uint32_t
         : "memory");
 }
 
-// Two packed words -> their 32 codes (two B operands).  The three shifted copies of the
-// pair come from 64-bit shifts; bits shifted in from the upper word land in bit positions
-// that the 0x03030303 mask clears.
+// Two packed words -> their 32 codes (two B operands).
 __device__ __forceinline__ void unpack_codes_x2(uint32_t w0, uint32_t w1, v4i &c0, v4i &c1) {
-#if MMF_UNPACK64
-    const uint64_t w = (static_cast<uint64_t>(w1) << 32) | w0;
-    const uint64_t s2 = w >> 2, s4 = w >> 4, s6 = w >> 6;
-    c0.x = static_cast<int>(w0 & 0x03030303u);
-    c1.x = static_cast<int>(w1 & 0x03030303u);
-    c0.y = static_cast<int>(static_cast<uint32_t>(s2) & 0x03030303u);
-    c1.y = static_cast<int>(static_cast<uint32_t>(s2 >> 32) & 0x03030303u);
-    c0.z = static_cast<int>(static_cast<uint32_t>(s4) & 0x03030303u);
-    c1.z = static_cast<int>(static_cast<uint32_t>(s4 >> 32) & 0x03030303u);
-    c0.w = static_cast<int>(static_cast<uint32_t>(s6) & 0x03030303u);
-    c1.w = static_cast<int>(static_cast<uint32_t>(s6 >> 32) & 0x03030303u);
-#else
     c0 = unpack_codes(w0);
     c1 = unpack_codes(w1);
-#endif
 }
 
 template <int EPI, bool OUT_BF16>

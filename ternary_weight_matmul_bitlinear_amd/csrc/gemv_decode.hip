@@ -345,6 +345,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
                     for (int e = 0; e < 8; ++e)
                         xk[it][e] = p.gate_mode == 0 ? xk[it][e] * r * gw[e] * siluf_(gv[e])
                                                      : sigmoidf_(gv[e]) * xk[it][e];
+                    // g_norm's output is materialised in the activation dtype before it is
+                    // quantized as o_proj's input
+                    if constexpr (OUT_BF16) {
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) round_bf16_pair(xk[it][e], xk[it][e + 1]);
+                    }
                 }
             }
         }

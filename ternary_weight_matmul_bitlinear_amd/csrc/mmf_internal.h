@@ -38,6 +38,14 @@ __device__ __forceinline__ float round_to_bf16(float f) {
     return bf16_bits_to_f32(f32_to_bf16_bits(f));
 }
 
+// Round two fp32 values to bf16 (nearest even) in place, widened back to fp32: one
+// v_cvt_pk_bf16_f32 and two bit operations.
+__device__ __forceinline__ void round_bf16_pair(float &lo, float &hi) {
+    const uint32_t w = pack_bf16x2(lo, hi);
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xFFFF0000u);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load_act(const void *p, int64_t i) {
     if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);

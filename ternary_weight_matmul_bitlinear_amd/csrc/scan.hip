@@ -274,7 +274,17 @@ __global__ __launch_bounds__(256) void scan_out_kernel(ScanArgs p) {
                     }
                 }
         } else {
-            // ---- int8 quantization of o (with o_proj's gain) for o_proj
+            // ---- int8 quantization of o (with o_proj's gain) for o_proj; o is first
+            // materialised in the activation dtype, as g_norm's output
+            if constexpr (IN_BF16) {
+#pragma unroll
+                for (int t = 0; t < TS; ++t)
+#pragma unroll
+                    for (int j = 0; j < JQ; ++j) {
+                        round_bf16_pair(o[t][j][0], o[t][j][1]);
+                        round_bf16_pair(o[t][j][2], o[t][j][3]);
+                    }
+            }
             float mx[TS], s2[TS], mxt[TS], s2t[TS];
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
@@ -559,7 +569,15 @@ __global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
                 }
             }
         } else {
-            // ---- int8 quantization of o (with o_proj's gain) for o_proj
+            // ---- int8 quantization of o (with o_proj's gain) for o_proj; o is first
+            // materialised in the activation dtype, as g_norm's output
+            if constexpr (IN_BF16) {
+                static_assert(CPL % 2 == 0, "channels per lane come in pairs");
+#pragma unroll
+                for (int t = 0; t < TS; ++t)
+#pragma unroll
+                    for (int k = 0; k < CPL; k += 2) round_bf16_pair(o[t][k], o[t][k + 1]);
+            }
             float mx[TS], s2[TS], mxt[TS], s2t[TS];
 #pragma unroll
             for (int t = 0; t < TS; ++t) {
@@ -712,6 +730,12 @@ __global__ __launch_bounds__(64 * W) void scan_row16_kernel(ScanArgs p) {
                 for (int kk = 0; kk < CPL; ++kk) o[t][kk] = sigmoidf_(gv[kk]) * o[t][kk];
             }
         }
+        // g_norm's output is materialised in the activation dtype (bf16) before o_proj
+        // quantizes it
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+            for (int kk = 0; kk < CPL; kk += 2) round_bf16_pair(o[t][kk], o[t][kk + 1]);
 
         float mx[TS], s2[TS], mxt[TS], s2t[TS];
 #pragma unroll

@@ -103,11 +103,15 @@ def block_stage_checks(orc, cap: dict, W: dict, x_rows: np.ndarray, bf16: bool, 
     stats["ifg"] = rel_check(st["y_out"], round_act(orc, ifg_ref, bf16), tol, "ifg pre-activations")
     # recurrence + g_norm from the GPU's stored pre-activations
     o_in = cap["o"]["x_in"]
+    assert np.array_equal(round_act(orc, o_in, bf16).astype(np.float32), o_in), \
+        "g_norm output is not a value of the activation dtype"
     if seq_rows is not None:
         B, T = seq_rows
         o_ref, h_ref = orc.mlgru(st["y_out"].astype(np.float64).reshape(B, T, 3 * D),
                                  f_bias=f_bias, h0=h0, gnorm_w=gnorm_w, gate_mode=gate_mode)
-        stats["mlgru"] = rel_check(o_in, o_ref.reshape(-1, D), 1e-3, "g_norm output")
+        # g_norm's output is materialised in the activation dtype before o_proj
+        stats["mlgru"] = rel_check(o_in, round_act(orc, o_ref.reshape(-1, D), bf16), tol,
+                                   "g_norm output")
         if h_last is not None:
             stats["h_T"] = rel_check(h_last, h_ref, 1e-3, "h_T")
     # o_proj + residual
@@ -132,11 +136,14 @@ def block_stage_checks(orc, cap: dict, W: dict, x_rows: np.ndarray, bf16: bool, 
 
 
 def e2e_checks(got_y, ref_y, bf16: bool, cap: dict | None = None, rec: dict | None = None,
-               got_h=None, ref_h=None) -> dict:
+               got_h=None, ref_h=None, decisions_agree: bool = False) -> dict:
     """Independent end-to-end comparison (GPU vs oracle from the same x).  Downstream int8
     codes may flip by one where fp32 and fp64 land on opposite sides of a rounding point,
-    and such a flip propagates; the bound is therefore statistical: p99.9 of the element
-    error and every row's norm-wise relative error within the tolerance, flips <= 1e-3."""
+    and such a flip propagates.  While every downstream int8 decision agrees (the captured
+    codes equal the oracle's, or the caller established it: decisions_agree) every element
+    is held to the tolerance; after a flip the bound is statistical: p99.9 of the element
+    error and every row's norm-wise relative error within the tolerance, flips <= 1e-3,
+    and the maximum is reported."""
     tol = 2e-2 if bf16 else 1e-3
     g = np.asarray(got_y, np.float64).reshape(-1, got_y.shape[-1])
     r = np.asarray(ref_y, np.float64).reshape(g.shape)
@@ -148,12 +155,19 @@ def e2e_checks(got_y, ref_y, bf16: bool, cap: dict | None = None, rec: dict | No
     assert out["p999"] <= tol, out
     assert out["row_norm_max"] <= tol, out
     if cap is not None and rec is not None:
+        n_flips = 0
         for name in ("o", "gateup", "down"):
-            f = float(np.mean(cap[name]["q"] != rec[name]["q"]))
+            ne = cap[name]["q"] != rec[name]["q"]
+            f = float(np.mean(ne))
+            n_flips += int(np.count_nonzero(ne))
             d = np.abs(cap[name]["q"].astype(np.int32) - rec[name]["q"].astype(np.int32))
             out[f"flips_{name}"] = f
             assert f <= 1e-3, (name, f)
             assert d.max() <= 1 or name != "o", (name, int(d.max()))
+        decisions_agree = decisions_agree or n_flips == 0
+    if decisions_agree:
+        assert out["max"] <= tol, out
     if got_h is not None:
         out["h_T"] = rel_check(got_h, ref_h, tol, "h_T end to end")["max"]
+    note(f"  end to end: {out}")
     return out

@@ -141,7 +141,7 @@ def test_block_one_token_steps(orc, dt, gate_mode, B, D, F):
     xd = dev(x, dt)
     api.set_regime(1 if B <= 4 else 0)  # above 4 rows the automatic choice is the k-split kernel
     h = torch.zeros((B, D), device="cuda")
-    ys = []
+    ys, qs = [], {k: [] for k in ("o", "gateup", "down")}
     for t in range(T):
         h_prev = host(h).copy()
         cap = api.BlockCapture.alloc(0, B, D, F)
@@ -151,13 +151,38 @@ def test_block_one_token_steps(orc, dt, gate_mode, B, D, F):
         block_stage_checks(orc, ch, W, x[:, t:t + 1], bf, seq_rows=(B, 1), f_bias=fb,
                            gnorm_w=gw, gate_mode=gate_mode, h0=h_prev, h_last=host(h),
                            y_rows=host(y))
+        for k in qs:
+            qs[k].append(ch[k]["q"])
         ys.append(y)
     y_dec = torch.cat(ys, dim=1)
-    r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf)
-    # run level: an int8 code that flips where fp32 and fp64 straddle a rounding point (rate
-    # ~1e-5 per code) feeds the carried state of every later step, so over 6 steps of several
-    # sequences the fp32 run is held to the bf16 bound; each step met the fp32 bar above
-    e2e_checks(host(y_dec), r["y"], bf or B > 1, got_h=host(h), ref_h=r["h_last"])
+    r = orc.block(x, W, f_bias=fb, gnorm_w=gw, gate_mode=gate_mode, resid_bf16=bf, record=True)
+    # run level: the independent oracle run takes its own downstream int8 decisions.  Where
+    # fp32 and fp64 land on opposite sides of a rounding point a code flips by one, and the
+    # flip feeds the carried state of every later step.  So every step before the first
+    # flip is held to its dtype's tolerance element by element; the first flip must be a
+    # single +-1 decision; from that step on the run is held to the bf16 bound (p99.9 and
+    # row norms) and the flip counts are reported.
+    first, flips = T, {}
+    for k in qs:
+        got = np.stack(qs[k], axis=1)                      # [B, T, K]: GPU step t, row b
+        ref = r["stages"][k]["q"].reshape(got.shape)       # oracle rows b*T + t
+        ne = got != ref
+        flips[k] = int(np.count_nonzero(ne))
+        steps_with = np.nonzero(ne.any(axis=(0, 2)))[0]
+        if steps_with.size:
+            t0 = int(steps_with[0])
+            first = min(first, t0)
+            d = np.abs(got[:, t0].astype(np.int32) - ref[:, t0].astype(np.int32))
+            assert d.max() <= 1, (k, t0, int(d.max()))
+    note(f"  downstream int8 flips over the run: {flips}, first at step {first}")
+    yg, yr = host(y_dec), r["y"]
+    if first > 0:
+        e2e_checks(yg[:, :first], yr[:, :first], bf, decisions_agree=True)
+    if first < T:
+        e2e_checks(yg[:, first:], yr[:, first:], True)
+        rel_check(host(h), r["h_last"], 2e-2, "h_T after a flip")
+    else:
+        rel_check(host(h), r["h_last"], 2e-2 if bf else 1e-3, "h_T")
 
 
 def test_block_ragged_chunks_and_inplace(orc):
@@ -182,3 +207,31 @@ def test_block_zero_tokens_is_noop():
     x = torch.zeros((2, 0, 256), device="cuda")
     y = api.block_forward(blk, x)
     assert y.shape == (2, 0, 256)
+
+
+def test_side_stream_calls(orc):
+    """Calls given stream= run on that stream and give the results of the current stream;
+    their outputs, workspaces and temporaries come from the side stream's allocator pool, so
+    blocks the current stream allocates meanwhile never alias memory the kernels still use."""
+    D, F, B, T = 256, 704, 2, 40
+    note("side stream: block_forward, bitlinear_forward, glu_forward")
+    blk, W, x, fb, gw = _block_case(orc, D, F, B, T, torch.bfloat16, 51)
+    xd = dev(x, torch.bfloat16)
+    rows = xd.reshape(-1, D)[::2]          # a strided view: the call makes a contiguous copy
+    y0 = api.block_forward(blk, xd)
+    b0 = api.bitlinear_forward(blk.gate, rows)
+    g0 = api.glu_forward(blk.gate, blk.up, blk.down, xd.reshape(-1, D), residual=xd.reshape(-1, D))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    y1 = api.block_forward(blk, xd, stream=s)
+    b1 = api.bitlinear_forward(blk.gate, rows, stream=s)
+    g1 = api.glu_forward(blk.gate, blk.up, blk.down, xd.reshape(-1, D), residual=xd.reshape(-1, D),
+                         stream=s)
+    # allocations and writes on the current stream while the side stream may still run
+    junk = [torch.full((1 << 20,), 7, dtype=torch.uint8, device="cuda") for _ in range(16)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(y0, y1) and torch.equal(b0, b1) and torch.equal(g0, g1)
+

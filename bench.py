@@ -360,24 +360,27 @@ def bench_decode(w, args, batches, orc) -> list:
         eager_ms, q = timed_events(fams, lambda i: eager(args.warmup + i), steps)
         n = sum(v[0] for v in q.values())
         ms = sum(v[1] for v in q.values())
-        # timed loop: graph replay of one captured step
-        ids_static = ids_all[0].clone()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            api.stack_forward(stack, B, 1, ids=ids_static, h_state=hs, want_y=False,
-                              want_logits=True, ws=ws, logits=logits)
-        spin_up(lambda: g.replay(), args.spin_up)
-        for i in range(args.warmup):
-            ids_static.copy_(ids_all[i])
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            ids_static.copy_(ids_all[args.warmup + i])
-            g.replay()
-        torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1e3 / steps
-        del g
+        if args.no_graph:   # profiler runs: eager steps only
+            ms_step = eager_ms
+        else:
+            # timed loop: graph replay of one captured step
+            ids_static = ids_all[0].clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                api.stack_forward(stack, B, 1, ids=ids_static, h_state=hs, want_y=False,
+                                  want_logits=True, ws=ws, logits=logits)
+            spin_up(lambda: g.replay(), args.spin_up)
+            for i in range(args.warmup):
+                ids_static.copy_(ids_all[i])
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                ids_static.copy_(ids_all[args.warmup + i])
+                g.replay()
+            torch.cuda.synchronize()
+            ms_step = (time.perf_counter() - t0) * 1e3 / steps
+            del g
         gemv_bytes, step_bytes = decode_bytes(B, D, F, V, L)
         achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
         name = f"{w.name}@{B}"
@@ -448,10 +451,36 @@ def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
         ms = sum(v[1] for v in q.values())
         bytes_ = wbytes + B * K * 2 + B * N * 2
         gbs = bytes_ * n / (ms * 1e-3) / 1e9
-        out.append({"N": N, "K": K, "rows": B, "weight_copies": copies,
-                    "us_per_launch": ms / n * 1e3, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS})
+        res = {"N": N, "K": K, "rows": B, "weight_copies": copies,
+               "us_per_launch": ms / n * 1e3, "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
         del ws
         torch.cuda.empty_cache()
+        if B <= 16 and K <= 10240:
+            # the same shape with base-3 packed weights (five per byte): random valid bytes
+            # b = ceil(256 v / 243), v uniform in [0, 243)
+            rb = api.trit_row_bytes(K)
+            tbytes = N * rb
+            tcopies = max(2, -(-(512 << 20) // tbytes))
+            wt = []
+            for _ in range(tcopies):
+                v = torch.randint(0, 243, (N, rb), dtype=torch.int32, device="cuda", generator=gen)
+                b = ((v * 256 + 242) // 243).to(torch.uint8)
+                wt.append(api.TernaryLinearTrits(b, 0.016, K, N))
+            for i in range(tcopies):
+                api.bitlinear_forward_trits(wt[i], x)
+            torch.cuda.synchronize()
+            reps = max(tcopies, 40)
+            _, q = timed_events(["gemv"], lambda i: api.bitlinear_forward_trits(wt[i % tcopies], x), reps)
+            n3, ms3 = q["gemv"]
+            tb = tbytes + B * K * 2 + B * N * 2
+            res["trits"] = {"weight_bytes": tbytes, "weight_copies": tcopies,
+                            "us_per_launch": ms3 / n3 * 1e3,
+                            "gbs": tb * n3 / (ms3 * 1e-3) / 1e9,
+                            "hbm_frac": tb * n3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "weights_per_s_vs_2bit": (ms / n) / (ms3 / n3)}
+            del wt
+            torch.cuda.empty_cache()
+        out.append(res)
     return out
 
 
@@ -499,6 +528,8 @@ def main() -> int:
                          "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
     ap.add_argument("--kernel-sweep", action="store_true",
                     help="decode stacks: also time single BitLinear launches on rotated weights")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="decode stacks: time eager steps only (no HIP graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()

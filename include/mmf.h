@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MMF_ABI_VERSION 1
+#define MMF_ABI_VERSION 2
 
 /* Status codes. */
 #define MMF_OK 0
@@ -93,14 +93,19 @@ typedef struct mmf_bitlinear {
 
 /* One block ([HL-hgrn], [DC-core]).  i, f, g, o: [D][D]; gate, up: [F][D]; down: [D][F].
  * i, f, g must share norm_w (same pointer or all NULL) and eps, as must gate and up: each
- * group quantizes its shared input once.  f_bias, gnorm_w and o.norm_w are read 16 bytes at
- * a time and must be 16-byte aligned (MMF_EALIGN). */
+ * group quantizes its shared input once.  f_bias, f_lower, gnorm_w and o.norm_w are read 16
+ * bytes at a time and must be 16-byte aligned (MMF_EALIGN).
+ * f_lower is HGRN's per-layer lower bound on the forget gate: [HL-hgrn] names the
+ * Hierarchical Gated Recurrent Network, and, following HGRN's published design (a reading:
+ * the pages give no formula), the gate becomes f = lb + (1 - lb)*sigmoid(f_pre + b_f), with
+ * lb in [0, 1] growing with depth (mmf_hgrn_lower_bounds builds it); NULL = no bound. */
 typedef struct mmf_block {
     mmf_bitlinear i, f, g, o, gate, up, down;
     const float *f_bias;  /* device [D] forget-gate bias, or NULL (zeros) */
     const float *gnorm_w; /* device [D] g_norm gain, or NULL (ones) */
     float eps;            /* g_norm epsilon */
     int32_t gate_mode;    /* mmf_gate_mode */
+    const float *f_lower; /* device [D] forget-gate lower bound, or NULL (none) */
 } mmf_block;
 
 /* Optional record of one BitLinear stage for token rows [row0, row1) (device buffers,
@@ -169,6 +174,25 @@ int mmf_ternary_pack(const int8_t *q, int64_t n, int64_t k, uint32_t *packed);
 /* Unpack (host -> host).  MMF_EINVAL on code 3 anywhere. */
 int mmf_ternary_unpack(const uint32_t *packed, int64_t n, int64_t k, int8_t *q);
 
+/* HGRN forget-gate lower bounds of an L-layer stack, on HOST memory (reading of [HL-hgrn],
+ * see mmf_block.f_lower): per channel d a softmax of the per-layer logits g[0..L)[d] over
+ * the layers, summed over the layers before l: lb[l][d] = sum_{j<l} e^g[j][d] / sum_j
+ * e^g[j][d] (sums in double, largest logit subtracted first), so lb[0] = 0 and lb grows
+ * with depth.  g, lb: [L][D] fp32.  MMF_EINVAL on NULL, MMF_ESHAPE on L, D <= 0. */
+int mmf_hgrn_lower_bounds(const float *g, int64_t L, int64_t D, float *lb);
+
+/* Base-3 packing ("trits", five ternary weights per byte, 1.6 bits each): the HackerPapers
+ * page on arXiv 2406.02528 (HN discussion list) calls the weights ternary digits, trits;
+ * 3^5 = 243 <= 256.  Format (a reading): codes c = q + 1; byte j of 4-byte word w of a row
+ * holds k = 20w + 4i + j (i = 0..4, i = 0 most significant) as v = sum_i c_i 3^(4-i),
+ * stored as b = ceil(256 v / 243); rows are padded with q = 0 to 16-byte chunks of 80
+ * weights, mmf_trit_row_bytes(k) = 16 * ceil(k / 80) bytes.  Host memory.  Pack: MMF_EINVAL
+ * on a value outside {-1,0,1}; unpack: MMF_EINVAL on a byte no group packs to or non-zero
+ * padding. */
+int64_t mmf_trit_row_bytes(int64_t k);
+int mmf_ternary_pack_trits(const int8_t *q, int64_t n, int64_t k, uint8_t *packed);
+int mmf_ternary_unpack_trits(const uint8_t *packed, int64_t n, int64_t k, int8_t *q);
+
 /* ------------------------------------------------------------------- forward calls */
 
 /* Scratch bytes bitlinear_forward needs for m token rows of w. */
@@ -181,6 +205,24 @@ size_t bitlinear_workspace_bytes(const mmf_bitlinear *w, int64_t m);
 int bitlinear_forward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
                       void *y, mmf_dtype y_dt, void *ws, size_t ws_bytes,
                       const mmf_stage_capture *cap, hipStream_t stream);
+
+/* A BitLinear with base-3 packed weights (see mmf_ternary_pack_trits). */
+typedef struct mmf_bitlinear_trits {
+    const uint8_t *packed;  /* device [N][mmf_trit_row_bytes(K)], 16-byte aligned */
+    float scale;            /* absmean scale s_w of the matrix */
+    const float *norm_w;    /* device [K] RMSNorm gain of the input, or NULL (ones) */
+    const float *bias;      /* device [N] or NULL */
+    float eps;
+    int32_t K, N;           /* K % 64 == 0, K <= 10240 */
+} mmf_bitlinear_trits;
+
+/* y[m][N] = BitLinear(x[m][K]) [HL-fbl] in the decode regime (0 <= m <= 16 token rows)
+ * over base-3 packed weights: the same quantization, exact int32 accumulation and rescale
+ * as bitlinear_forward, with 20 % fewer weight bytes streamed.  No workspace.  cap as for
+ * bitlinear_forward (acc and y_out rows have stride N). */
+int bitlinear_forward_trits(const mmf_bitlinear_trits *w, const void *x, mmf_dtype x_dt,
+                            int64_t m, void *y, mmf_dtype y_dt, const mmf_stage_capture *cap,
+                            hipStream_t stream);
 
 /* MLGRU token mixer + output gate [DC-core], [HL-hgrn], without the o_proj. */
 typedef struct mmf_mlgru_args {
@@ -195,6 +237,7 @@ typedef struct mmf_mlgru_args {
     void *out;             /* [B][T][D] gated output (out_dt) */
     mmf_dtype out_dt;
     int64_t B, T, D;       /* D % 64 == 0, D <= 4096 */
+    const float *f_lower;  /* [D] forget-gate lower bound (see mmf_block), or NULL */
 } mmf_mlgru_args;
 
 size_t mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D);

@@ -44,7 +44,7 @@
  *       the MatMul-free GLU's gated product (DataCamp, "Core components": formed from the
  *       two branches, then passed to the third BitLinear), and the residual stream y1, y2.
  *       The recurrent state h is carried in fp32 and is not rounded.
- *   R9  HGRN's hierarchical forget-gate lower bound (Hysen Labs, "HGRN attention", names
+ *   R12 HGRN's hierarchical forget-gate lower bound (Hysen Labs, "HGRN attention", names
  *       the Hierarchical Gated Recurrent Network but not its formula; the formula is read
  *       from HGRN's published design and its parity is unpinned by the pages): layer l has
  *       a per-channel bound lb_l in [0,1) that grows with depth, made from per-layer logits
@@ -314,7 +314,7 @@ void orc_gated_recurrence(const double *f, const double *c, int64_t B, int64_t T
 /* ----------------------------------------------------- O6 + O7 MLGRU with output gate
  * ifg: [B, T, 3D] pre-activations, segments i | f | g along the last axis.
  * [HL-hgrn] i/f/g projections, recurrence, g_norm = RMSNorm fused with a swish gate.
- * Readings R5, R6, R9 (f_lower [D] or NULL).  gate_mode 0: out = h*rsqrt(mean_D h^2 + eps)*gnorm_w * g*sigmoid(g);
+ * Readings R5, R6, R12 (f_lower [D] or NULL).  gate_mode 0: out = h*rsqrt(mean_D h^2 + eps)*gnorm_w * g*sigmoid(g);
  * gate_mode 1: out = sigmoid(g)*h.  h_last [B, D] receives h_T.
  */
 int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f_bias,
@@ -332,7 +332,7 @@ int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f
         for (int64_t d = 0; d < D; ++d) {
             const double *r = ifg + row * 3 * D;
             double sg = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
-            double lb = f_lower ? (double)f_lower[d] : 0.0;   /* reading R9 */
+            double lb = f_lower ? (double)f_lower[d] : 0.0;   /* reading R12 */
             f[row * D + d] = lb + (1.0 - lb) * sg;
             c[row * D + d] = silu_d(r[d]);
         }
@@ -515,7 +515,7 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
     return 0;
 }
 
-/* ----------------------------------------- HGRN forget-gate lower bounds (R9)
+/* ----------------------------------------- HGRN forget-gate lower bounds (R12)
  * G [L, D] per-layer logits -> lb [L, D]: for each channel, a softmax over the L layers
  * (fp64; the largest logit is subtracted first so exp cannot overflow), accumulated over
  * the layers before l.  lb_0 = 0 and lb grows with l, staying below 1.

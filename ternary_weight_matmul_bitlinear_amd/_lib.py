@@ -25,7 +25,12 @@ class mmf_bitlinear(C.Structure):
 
 class mmf_block(C.Structure):
     _fields_ = [(n, mmf_bitlinear) for n in ("i", "f", "g", "o", "gate", "up", "down")] + [
-        ("f_bias", vp), ("gnorm_w", vp), ("eps", f32), ("gate_mode", i32)]
+        ("f_bias", vp), ("gnorm_w", vp), ("eps", f32), ("gate_mode", i32), ("f_lower", vp)]
+
+
+class mmf_bitlinear_trits(C.Structure):
+    _fields_ = [("packed", vp), ("scale", f32), ("norm_w", vp), ("bias", vp), ("eps", f32),
+                ("K", i32), ("N", i32)]
 
 
 class mmf_stage_capture(C.Structure):
@@ -40,7 +45,7 @@ class mmf_capture(C.Structure):
 class mmf_mlgru_args(C.Structure):
     _fields_ = [("ifg", vp), ("ifg_dt", i32), ("f_bias", vp), ("h0", vp), ("h_out", vp),
                 ("gnorm_w", vp), ("eps", f32), ("gate_mode", i32), ("out", vp), ("out_dt", i32),
-                ("B", i64), ("T", i64), ("D", i64)]
+                ("B", i64), ("T", i64), ("D", i64), ("f_lower", vp)]
 
 
 class mmf_stack(C.Structure):
@@ -62,6 +67,12 @@ SIGNATURES = {
     "mmf_ternary_quantize": (C.c_int, [vp, i64, i64, vp, vp]),
     "mmf_ternary_pack": (C.c_int, [vp, i64, i64, vp]),
     "mmf_ternary_unpack": (C.c_int, [vp, i64, i64, vp]),
+    "mmf_hgrn_lower_bounds": (C.c_int, [vp, i64, i64, vp]),
+    "mmf_trit_row_bytes": (i64, [i64]),
+    "mmf_ternary_pack_trits": (C.c_int, [vp, i64, i64, vp]),
+    "mmf_ternary_unpack_trits": (C.c_int, [vp, i64, i64, vp]),
+    "bitlinear_forward_trits": (C.c_int, [P(mmf_bitlinear_trits), vp, C.c_int, i64, vp, C.c_int,
+                                          P(mmf_stage_capture), vp]),
     "bitlinear_workspace_bytes": (sz, [P(mmf_bitlinear), i64]),
     "bitlinear_forward": (C.c_int, [P(mmf_bitlinear), vp, C.c_int, i64, vp, C.c_int, vp, sz,
                                     P(mmf_stage_capture), vp]),

@@ -65,11 +65,45 @@ def pack_ternary(q: np.ndarray) -> np.ndarray:
     return out
 
 
+def hgrn_lower_bounds(g: np.ndarray) -> np.ndarray:
+    """HGRN forget-gate lower bounds [L, D] from per-layer logits [L, D] (mmf_hgrn_lower_bounds)."""
+    g, gp = _host(g, np.float32)
+    L_, D = g.shape
+    lb = np.empty((L_, D), np.float32)
+    L.check("mmf_hgrn_lower_bounds",
+            L.lib().mmf_hgrn_lower_bounds(gp, L_, D, lb.ctypes.data_as(C.c_void_p)))
+    return lb
+
+
 def unpack_ternary(packed: np.ndarray, k: int) -> np.ndarray:
     packed, pp = _host(packed, np.uint32)
     n = packed.shape[0]
     q = np.empty((n, k), np.int8)
     L.check("mmf_ternary_unpack", L.lib().mmf_ternary_unpack(pp, n, k, q.ctypes.data_as(C.c_void_p)))
+    return q
+
+
+def trit_row_bytes(k: int) -> int:
+    return int(L.lib().mmf_trit_row_bytes(k))
+
+
+def pack_trits(q: np.ndarray) -> np.ndarray:
+    """Base-3 packing, five weights per byte (mmf_ternary_pack_trits): [n, k] int8 ->
+    [n, trit_row_bytes(k)] uint8."""
+    q, qp = _host(q, np.int8)
+    n, k = q.shape
+    out = np.empty((n, trit_row_bytes(k)), np.uint8)
+    L.check("mmf_ternary_pack_trits",
+            L.lib().mmf_ternary_pack_trits(qp, n, k, out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+def unpack_trits(packed: np.ndarray, k: int) -> np.ndarray:
+    packed, pp = _host(packed, np.uint8)
+    n = packed.shape[0]
+    q = np.empty((n, k), np.int8)
+    L.check("mmf_ternary_unpack_trits",
+            L.lib().mmf_ternary_unpack_trits(pp, n, k, q.ctypes.data_as(C.c_void_p)))
     return q
 
 
@@ -101,6 +135,30 @@ class TernaryLinear:
     def desc(self) -> L.mmf_bitlinear:
         return L.mmf_bitlinear(_ptr(self.packed), self.scale, _ptr(self.norm_w), _ptr(self.bias),
                                self.eps, self.K, self.N)
+
+
+@dataclass
+class TernaryLinearTrits:
+    """A BitLinear with base-3 packed weights on the device: [N, trit_row_bytes(K)] uint8."""
+    packed: torch.Tensor
+    scale: float
+    K: int
+    N: int
+    norm_w: torch.Tensor | None = None
+    bias: torch.Tensor | None = None
+    eps: float = 1e-6
+
+    @classmethod
+    def from_ternary(cls, q: np.ndarray, scale: float, device="cuda", norm_w=None, bias=None,
+                     eps=1e-6):
+        t = torch.from_numpy(pack_trits(q)).to(device)
+        nw = None if norm_w is None else torch.as_tensor(norm_w, dtype=torch.float32, device=device)
+        b = None if bias is None else torch.as_tensor(bias, dtype=torch.float32, device=device)
+        return cls(t, float(scale), q.shape[1], q.shape[0], nw, b, eps)
+
+    def desc(self) -> L.mmf_bitlinear_trits:
+        return L.mmf_bitlinear_trits(_ptr(self.packed), self.scale, _ptr(self.norm_w),
+                                     _ptr(self.bias), self.eps, self.K, self.N)
 
 
 # ------------------------------------------------------------------ captures
@@ -191,9 +249,25 @@ def bitlinear_forward(w: TernaryLinear, x: torch.Tensor, out_dtype=None,
         return y
 
 
+def bitlinear_forward_trits(w: TernaryLinearTrits, x: torch.Tensor, out_dtype=None,
+                            capture: StageCapture | None = None, stream=None) -> torch.Tensor:
+    """y[m, N] = BitLinear(x[m, K]) over base-3 packed weights, m <= 16 (bitlinear_forward_trits)."""
+    with _on(stream):
+        x = x.contiguous()
+        m = x.numel() // w.K
+        out_dtype = x.dtype if out_dtype is None else out_dtype
+        y = torch.empty(x.shape[:-1] + (w.N,), dtype=out_dtype, device=x.device)
+        d = w.desc()
+        cap = C.byref(capture.desc()) if capture is not None else None
+        L.check("bitlinear_forward_trits",
+                L.lib().bitlinear_forward_trits(C.byref(d), _ptr(x), _dt(x.dtype), m, _ptr(y),
+                                                _dt(out_dtype), cap, _stream()))
+        return y
+
+
 def mlgru_scan(ifg: torch.Tensor, f_bias=None, h0=None, gnorm_w=None, eps: float = 1e-6,
                gate_mode: int = 0, out_dtype=None, h_out: torch.Tensor | None = None,
-               stream=None):
+               stream=None, f_lower=None):
     """MLGRU + output gate over ifg [B, T, 3D] (mlgru_scan).  Returns (out, h_T)."""
     with _on(stream):
         lib = L.lib()
@@ -205,7 +279,8 @@ def mlgru_scan(ifg: torch.Tensor, f_bias=None, h0=None, gnorm_w=None, eps: float
         if h_out is None:
             h_out = torch.empty((B, D), dtype=torch.float32, device=ifg.device)
         a = L.mmf_mlgru_args(_ptr(ifg), _dt(ifg.dtype), _ptr(f_bias), _ptr(h0), _ptr(h_out),
-                             _ptr(gnorm_w), eps, gate_mode, _ptr(out), _dt(out_dtype), B, T, D)
+                             _ptr(gnorm_w), eps, gate_mode, _ptr(out), _dt(out_dtype), B, T, D,
+                             _ptr(f_lower))
         nb = lib.mlgru_workspace_bytes(B, T, D)
         ws = _workspace(nb, ifg.device)
         L.check("mlgru_scan", lib.mlgru_scan(C.byref(a), _ptr(ws), nb, _stream()))
@@ -249,6 +324,7 @@ class Block:
     gnorm_w: torch.Tensor | None = None
     eps: float = 1e-6
     gate_mode: int = 0
+    f_lower: torch.Tensor | None = None
     _desc: L.mmf_block | None = field(default=None, repr=False)
 
     @property
@@ -261,19 +337,20 @@ class Block:
 
     @classmethod
     def from_latents(cls, lat: dict, device="cuda", f_bias=None, gnorm_w=None, eps=1e-6,
-                     gate_mode=0):
+                     gate_mode=0, f_lower=None):
         mats = {k: TernaryLinear.from_latent(lat[k], device, eps=eps)
                 for k in ("i", "f", "g", "o", "gate", "up", "down")}
         fb = None if f_bias is None else torch.as_tensor(f_bias, dtype=torch.float32, device=device)
         gw = None if gnorm_w is None else torch.as_tensor(gnorm_w, dtype=torch.float32, device=device)
-        return cls(**mats, f_bias=fb, gnorm_w=gw, eps=eps, gate_mode=gate_mode)
+        lb = None if f_lower is None else torch.as_tensor(f_lower, dtype=torch.float32, device=device)
+        return cls(**mats, f_bias=fb, gnorm_w=gw, eps=eps, gate_mode=gate_mode, f_lower=lb)
 
     def desc(self) -> L.mmf_block:
         if self._desc is None:
             self._desc = L.mmf_block(self.i.desc(), self.f.desc(), self.g.desc(), self.o.desc(),
                                      self.gate.desc(), self.up.desc(), self.down.desc(),
                                      _ptr(self.f_bias), _ptr(self.gnorm_w), self.eps,
-                                     self.gate_mode)
+                                     self.gate_mode, _ptr(self.f_lower))
         return self._desc
 
 

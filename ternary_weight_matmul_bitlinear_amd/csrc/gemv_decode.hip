@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     constexpr int KF = XIN == 3 ? (NI <= 2 ? 1 : 2) : 1;
     using RawAct = typename std::conditional<OUT_BF16, uint4, float4[2]>::type;
     RawAct ri[KF], rf[KF], rg[KF];
-    float4 rh[KF][2], rb[KF][2], rw[KF][2];
+    float4 rh[KF][2], rb[KF][2], rl[KF][2], rw[KF][2];
     if constexpr (XIN == 3) {
         auto ld_act = [&](int64_t e, RawAct &dst) __attribute__((always_inline)) {
             if constexpr (OUT_BF16) {
@@ -215,6 +215,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
             ld_act(base + 2 * K, rg[it]);
             ld_par(p.h_prev ? p.h_prev + t0 * K : nullptr, k0, rh[it], 0.0f);
             ld_par(p.f_bias, k0, rb[it], 0.0f);
+            ld_par(p.f_lower, k0, rl[it], 0.0f);
             ld_par(p.gnorm_w, k0, rw[it], 1.0f);
         }
     }
@@ -304,14 +305,15 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
 #pragma unroll
             for (int it = 0; it < KF; ++it) {
                 const int k0 = tid * 8 + 8 * NT * it;
-                float iv[8], fv[8], hv[8], bv[8];
+                float iv[8], fv[8], hv[8], bv[8], lv[8];
                 cvt8(ri[it], iv);
                 cvt8(rf[it], fv);
                 f8(rh[it], hv);
                 f8(rb[it], bv);
+                f8(rl[it], lv);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float f = sigmoidf_(fv[e] + bv[e]);
+                    const float f = fmaf(1.0f - lv[e], sigmoidf_(fv[e] + bv[e]), lv[e]);
                     hv[e] = f * hv[e] + (1.0f - f) * siluf_(iv[e]);
                 }
                 if (k0 < K) {

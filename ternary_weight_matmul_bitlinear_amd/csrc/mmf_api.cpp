@@ -236,6 +236,7 @@ struct GemvExtra {
     const float *h_prev = nullptr;
     float *h_new = nullptr;
     const float *f_bias = nullptr;
+    const float *f_lower = nullptr;
     const float *gnorm_w = nullptr;
     float g_eps = 0.f;
     int32_t gate_mode = 0;
@@ -257,6 +258,7 @@ static hipError_t gemv(const void *x, bool x_bf16, const float *gamma, float eps
         ga.h_prev = ex->h_prev;
         ga.h_new = ex->h_new;
         ga.f_bias = ex->f_bias;
+        ga.f_lower = ex->f_lower;
         ga.gnorm_w = ex->gnorm_w;
         ga.g_eps = ex->g_eps;
         ga.gate_mode = ex->gate_mode;
@@ -417,6 +419,44 @@ int bitlinear_forward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int
     return MMF_OK;
 }
 
+// --------------------------------------------------- BitLinear, base-3 packed weights
+int bitlinear_forward_trits(const mmf_bitlinear_trits *w, const void *x, mmf_dtype x_dt,
+                            int64_t m, void *y, mmf_dtype y_dt, const mmf_stage_capture *cap,
+                            hipStream_t stream) {
+    if (!w) return set_error(MMF_EINVAL, "bitlinear_forward_trits: NULL descriptor");
+    if (!w->packed) return set_error(MMF_EINVAL, "bitlinear_forward_trits: NULL packed weights");
+    if (w->K <= 0 || w->N <= 0 || w->K % 64 || w->K > 10240)
+        return set_error(MMF_ESHAPE, "bitlinear_forward_trits: K=%d N=%d (K must be a positive multiple of 64, at most 10240)", w->K, w->N);
+    if (!valid_dt(x_dt) || !valid_dt(y_dt)) return set_error(MMF_EDTYPE, "bitlinear_forward_trits: dtype %d/%d", x_dt, y_dt);
+    if (m < 0 || m > 16) return set_error(MMF_ESHAPE, "bitlinear_forward_trits: m=%lld (decode regime: 0..16 token rows)", (long long)m);
+    if (!(w->eps >= 0.0f)) return set_error(MMF_EINVAL, "bitlinear_forward_trits: eps must be >= 0");
+    int rc;
+    if ((rc = check_cap(cap, "bitlinear_forward_trits"))) return rc;
+    if (m == 0) return MMF_OK;
+    if (!x || !y) return set_error(MMF_EINVAL, "bitlinear_forward_trits: NULL x or y");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(w->packed))
+        return set_error(MMF_EALIGN, "bitlinear_forward_trits: x, y or packed not 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    TritArgs a{};
+    a.x = x;
+    a.x_bf16 = x_dt == MMF_BF16;
+    a.gamma = w->norm_w;
+    a.eps = w->eps;
+    a.M = m;
+    a.K = w->K;
+    a.row_bytes = static_cast<int32_t>(mmf_trit_row_bytes(w->K));
+    a.packed = w->packed;
+    a.scale = w->scale;
+    a.bias = w->bias;
+    a.N = w->N;
+    a.out = y;
+    a.out_bf16 = y_dt == MMF_BF16;
+    a.cap = cap_of(cap, w->N);
+    const hipError_t e = launch_gemv_trits(a, stream);
+    if (e != hipSuccess) return hip_error(e, "bitlinear_forward_trits launch");
+    return MMF_OK;
+}
+
 // ------------------------------------------------------------------ MLGRU
 size_t mlgru_workspace_bytes(int64_t B, int64_t T, int64_t D) {
     if (B <= 0 || T <= 0 || D <= 0) return 0;
@@ -440,8 +480,9 @@ int mlgru_scan(const mmf_mlgru_args *a, void *ws, size_t ws_bytes, hipStream_t s
     if (M > 0 && (!a->ifg || !a->out)) return set_error(MMF_EINVAL, "mlgru_scan: NULL ifg or out");
     if (M > 0 && (!aligned16(a->ifg) || !aligned16(a->out))) return set_error(MMF_EALIGN, "mlgru_scan: ifg/out not 16-byte aligned");
     if ((a->h0 && !aligned16(a->h0)) || (a->h_out && !aligned16(a->h_out)) ||
-        (a->f_bias && !aligned16(a->f_bias)) || (a->gnorm_w && !aligned16(a->gnorm_w)))
-        return set_error(MMF_EALIGN, "mlgru_scan: h0/h_out/f_bias/gnorm_w not 16-byte aligned");
+        (a->f_bias && !aligned16(a->f_bias)) || (a->gnorm_w && !aligned16(a->gnorm_w)) ||
+        (a->f_lower && !aligned16(a->f_lower)))
+        return set_error(MMF_EALIGN, "mlgru_scan: h0/h_out/f_bias/f_lower/gnorm_w not 16-byte aligned");
     const size_t need = mlgru_workspace_bytes(a->B, a->T, a->D);
     if (need && (!ws || ws_bytes < need)) return set_error(MMF_EWORKSPACE, "mlgru_scan: workspace %zu < %zu", ws ? ws_bytes : 0, need);
     if ((rc = check_device())) return rc;
@@ -457,6 +498,7 @@ int mlgru_scan(const mmf_mlgru_args *a, void *ws, size_t ws_bytes, hipStream_t s
     s.ifg = a->ifg;
     s.ifg_bf16 = a->ifg_dt == MMF_BF16;
     s.f_bias = a->f_bias;
+    s.f_lower = a->f_lower;
     s.h0 = a->h0;
     s.h_out = a->h_out;
     s.gnorm_w = a->gnorm_w;
@@ -561,8 +603,8 @@ static int check_block(const mmf_block *w, const char *who) {
     if (!(w->eps >= 0.0f)) return set_error(MMF_EINVAL, "%s: eps", who);
     // per-channel vectors are read 16 bytes at a time
     if ((w->f_bias && !aligned16(w->f_bias)) || (w->gnorm_w && !aligned16(w->gnorm_w)) ||
-        (w->o.norm_w && !aligned16(w->o.norm_w)))
-        return set_error(MMF_EALIGN, "%s: f_bias/gnorm_w/o.norm_w not 16-byte aligned", who);
+        (w->o.norm_w && !aligned16(w->o.norm_w)) || (w->f_lower && !aligned16(w->f_lower)))
+        return set_error(MMF_EALIGN, "%s: f_bias/f_lower/gnorm_w/o.norm_w not 16-byte aligned", who);
     return MMF_OK;
 }
 
@@ -629,6 +671,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
         eo.h_prev = h_state;
         eo.h_new = h_tmp;
         eo.f_bias = w->f_bias;
+        eo.f_lower = w->f_lower;
         eo.gnorm_w = w->gnorm_w;
         eo.g_eps = w->eps;
         eo.gate_mode = w->gate_mode;
@@ -652,6 +695,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     s.ifg = act;
     s.ifg_bf16 = bf;
     s.f_bias = w->f_bias;
+    s.f_lower = w->f_lower;
     s.h0 = h_state;
     s.h_out = h_state;
     s.gnorm_w = w->gnorm_w;

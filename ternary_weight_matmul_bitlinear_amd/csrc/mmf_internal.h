@@ -248,6 +248,7 @@ struct GemvArgs {
     const float *h_prev;   // [D] carried state (NULL: zeros)
     float *h_new;          // [D] new state, written by column-block 0 (NULL: not kept)
     const float *f_bias;   // [D] or NULL
+    const float *f_lower;  // [D] forget-gate lower bound or NULL (zeros)
     const float *gnorm_w;  // [D] or NULL (ones)
     float g_eps;
     int32_t gate_mode;
@@ -262,6 +263,7 @@ struct ScanArgs {
     const void *ifg;       // [B][T][3D]
     int32_t ifg_bf16;
     const float *f_bias;
+    const float *f_lower;  // [D] forget-gate lower bound or NULL (zeros)
     const float *h0;
     float *h_out;
     const float *gnorm_w;
@@ -285,6 +287,24 @@ struct ScanArgs {
     CapDev cap;            // x_in/q/a of the o_proj stage
 };
 
+// Decode BitLinear over base-3 packed weights (five per byte, rows of row_bytes bytes).
+struct TritArgs {
+    const void *x;         // [M][K] activations (quantized in the prologue)
+    int32_t x_bf16;
+    const float *gamma;
+    float eps;
+    int64_t M;
+    int32_t K;
+    int32_t row_bytes;     // 16 * ceil(K / 80)
+    const uint8_t *packed; // [N][row_bytes]
+    float scale;
+    const float *bias;
+    int32_t N;
+    void *out;             // [M][N]
+    int32_t out_bf16;
+    CapDev cap;            // x_in/q/a by column-block 0, acc/y_out by every block (stride N)
+};
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
@@ -294,6 +314,7 @@ hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, 
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);
 hipError_t launch_copy_state(const float *h0, float *h_out, int64_t n, hipStream_t s);
+hipError_t launch_gemv_trits(const TritArgs &a, hipStream_t s);
 
 // Token rows up to which the MFMA regime uses the mid-size kernel (gemm_mid.hip): weights
 // read once per launch, k split over the waves of a workgroup.

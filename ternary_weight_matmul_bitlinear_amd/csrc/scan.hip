@@ -6,8 +6,10 @@
 // Hysen Labs "MatMul-Free LM", section "HGRN attention": the recurrence needs only the
 // current token and the previous state (linear in T); its output passes g_norm, an RMSNorm
 // fused with a swish gate, before o_proj.  Per (b, d):
-//   f = sigmoid(f_pre + b_f), c = SiLU(i_pre), h_t = f*h_{t-1} + (1-f)*c,
+//   f = lb + (1 - lb)*sigmoid(f_pre + b_f), c = SiLU(i_pre), h_t = f*h_{t-1} + (1-f)*c,
 //   o_t = RMSNorm_D(h_t)*gnorm_w * g*sigmoid(g)   (or sigmoid(g)*h_t).
+// lb is the optional per-layer lower bound of HGRN's forget gate (0 without one): the same
+// page names the Hierarchical Gated Recurrent Network; the bound follows HGRN's design.
 //
 // The recurrence is elementwise in d, so it is parallel over B*D channels; to fill 256
 // CUs at long T it is also chunked over time (16-token chunks):
@@ -64,8 +66,11 @@ __device__ __forceinline__ void cvt4(float4 u, float (&v)[4]) {
 }
 __device__ __forceinline__ void st4f(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
 
-__device__ __forceinline__ float gate_step(float h, float ip, float fp, float fb, float *f_out) {
-    const float f = sigmoidf_(fp + fb);
+// Forget gate with HGRN's per-layer lower bound lb (0 without one; fma(1, s, 0) = s, so the
+// unbounded gate is unchanged): f = lb + (1 - lb)*sigmoid(f_pre + b_f).
+__device__ __forceinline__ float gate_step(float h, float ip, float fp, float fb, float lb,
+                                           float *f_out) {
+    const float f = fmaf(1.0f - lb, sigmoidf_(fp + fb), lb);
     *f_out = f;
     return f * h + (1.0f - f) * siluf_(ip);
 }
@@ -82,8 +87,9 @@ __global__ __launch_bounds__(256) void scan_local_kernel(ScanArgs p) {
     const int64_t t_beg = static_cast<int64_t>(c) * p.chunk;
     const int nt = static_cast<int>((t_beg + p.chunk < p.T ? t_beg + p.chunk : p.T) - t_beg);
     const float4 fb = p.f_bias ? ld4f(p.f_bias + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 lb = p.f_lower ? ld4f(p.f_lower + d) : make_float4(0.f, 0.f, 0.f, 0.f);
     float h[4] = {0.f, 0.f, 0.f, 0.f}, pf[4] = {1.f, 1.f, 1.f, 1.f};
-    const float fbv[4] = {fb.x, fb.y, fb.z, fb.w};
+    const float fbv[4] = {fb.x, fb.y, fb.z, fb.w}, lbv[4] = {lb.x, lb.y, lb.z, lb.w};
     const int64_t base = (b * p.T + t_beg) * 3 * D + d;
 #pragma unroll 8
     for (int t = 0; t < nt; ++t) {
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(256) void scan_local_kernel(ScanArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float f;
-            h[e] = gate_step(h[e], iv[e], fv[e], fbv[e], &f);
+            h[e] = gate_step(h[e], iv[e], fv[e], fbv[e], lbv[e], &f);
             pf[e] *= f;
         }
     }
@@ -163,22 +169,24 @@ __global__ __launch_bounds__(256) void scan_out_kernel(ScanArgs p) {
     const int64_t t_end = t_beg + p.chunk < p.T ? t_beg + p.chunk : p.T;
     const float inv_d = 1.0f / static_cast<float>(D);
 
-    float h[JQ][4], fb[JQ][4], gw[JQ][4], qg[JQ][4];
+    float h[JQ][4], fb[JQ][4], lb[JQ][4], gw[JQ][4], qg[JQ][4];
     bool dv[JQ];
 #pragma unroll
     for (int j = 0; j < JQ; ++j) {
         const int d = 4 * (tid + 256 * j);
         dv[j] = d < D;
-        float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), fv = hv, g1 = make_float4(1.f, 1.f, 1.f, 1.f), q1 = g1;
+        float4 hv = make_float4(0.f, 0.f, 0.f, 0.f), fv = hv, lv = hv, g1 = make_float4(1.f, 1.f, 1.f, 1.f), q1 = g1;
         if (dv[j]) {
             if (p.n_chunks > 1) hv = ld4f(p.hin + (b * p.n_chunks + c) * D + d);
             else if (p.h0) hv = ld4f(p.h0 + b * D + d);
             if (p.f_bias) fv = ld4f(p.f_bias + d);
+            if (p.f_lower) lv = ld4f(p.f_lower + d);
             if (p.gnorm_w) g1 = ld4f(p.gnorm_w + d);
             if (QUANT && p.q_gamma) q1 = ld4f(p.q_gamma + d);
         }
         h[j][0] = hv.x; h[j][1] = hv.y; h[j][2] = hv.z; h[j][3] = hv.w;
         fb[j][0] = fv.x; fb[j][1] = fv.y; fb[j][2] = fv.z; fb[j][3] = fv.w;
+        lb[j][0] = lv.x; lb[j][1] = lv.y; lb[j][2] = lv.z; lb[j][3] = lv.w;
         gw[j][0] = g1.x; gw[j][1] = g1.y; gw[j][2] = g1.z; gw[j][3] = g1.w;
         qg[j][0] = q1.x; qg[j][1] = q1.y; qg[j][2] = q1.z; qg[j][3] = q1.w;
     }
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(256) void scan_out_kernel(ScanArgs p) {
                 for (int e = 0; e < 4; ++e) {
                     if (t < nt && dv[j]) {
                         float f;
-                        h[j][e] = gate_step(h[j][e], iv[e], fv[e], fb[j][e], &f);
+                        h[j][e] = gate_step(h[j][e], iv[e], fv[e], fb[j][e], lb[j][e], &f);
                     }
                     o[t][j][e] = h[j][e];
                     ss[t] += (t < nt && dv[j]) ? h[j][e] * h[j][e] : 0.f;
@@ -478,10 +486,11 @@ __global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
     const int64_t t_end = t_beg + p.chunk < p.T ? t_beg + p.chunk : p.T;
     const float inv_d = 1.0f / static_cast<float>(D);
 
-    float h[CPL], fb[CPL], gw[CPL], qg[CPL];
+    float h[CPL], fb[CPL], lb[CPL], gw[CPL], qg[CPL];
     if (p.n_chunks > 1) load_f32<CPL>(p.hin + (b * p.n_chunks + c) * D + d0, h, 0.0f);
     else load_f32<CPL>(p.h0 ? p.h0 + b * D + d0 : nullptr, h, 0.0f);
     load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    load_f32<CPL>(p.f_lower ? p.f_lower + d0 : nullptr, lb, 0.0f);
     load_f32<CPL>(p.gnorm_w ? p.gnorm_w + d0 : nullptr, gw, 1.0f);
     load_f32<CPL>(QUANT && p.q_gamma ? p.q_gamma + d0 : nullptr, qg, 1.0f);
 
@@ -518,7 +527,7 @@ __global__ __launch_bounds__(64 * W) void scan_row_kernel(ScanArgs p) {
 #pragma unroll
                 for (int k = 0; k < CPL; ++k) {
                     float f;
-                    h[k] = gate_step(h[k], iv[k], fv[k], fb[k], &f);
+                    h[k] = gate_step(h[k], iv[k], fv[k], fb[k], lb[k], &f);
                     ss[t] = fmaf(h[k], h[k], ss[t]);
                 }
             }
@@ -667,10 +676,11 @@ __global__ __launch_bounds__(64 * W) void scan_row16_kernel(ScanArgs p) {
     const int64_t D3 = 3 * static_cast<int64_t>(D);
 
     // per-channel parameters first: the waits for them then never cover tile loads
-    float h[CPL], fb[CPL], gw[CPL], qg[CPL];
+    float h[CPL], fb[CPL], lb[CPL], gw[CPL], qg[CPL];
     if (p.n_chunks > 1) load_f32<CPL>(p.hin + (b * p.n_chunks + c) * D + d0, h, 0.0f);
     else load_f32<CPL>(p.h0 ? p.h0 + b * D + d0 : nullptr, h, 0.0f);
     load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    load_f32<CPL>(p.f_lower ? p.f_lower + d0 : nullptr, lb, 0.0f);
     load_f32<CPL>(p.gnorm_w ? p.gnorm_w + d0 : nullptr, gw, 1.0f);
     load_f32<CPL>(p.q_gamma ? p.q_gamma + d0 : nullptr, qg, 1.0f);
 
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(64 * W) void scan_row16_kernel(ScanArgs p) {
 #pragma unroll
             for (int kk = 0; kk < CPL; ++kk) {
                 float f;
-                h[kk] = gate_step(h[kk], iv[kk], fv[kk], fb[kk], &f);
+                h[kk] = gate_step(h[kk], iv[kk], fv[kk], fb[kk], lb[kk], &f);
                 ss[t] = fmaf(h[kk], h[kk], ss[t]);
                 o[t][kk] = h[kk];
             }
@@ -811,8 +821,9 @@ __global__ __launch_bounds__(256) void scan_local_row_kernel(ScanArgs p) {
     const int64_t t_beg = static_cast<int64_t>(c) * CH;
     const int nt = static_cast<int>(p.T - t_beg < CH ? p.T - t_beg : CH);
     const int64_t D3 = 3 * static_cast<int64_t>(D);
-    float fb[CPL], h[CPL], pf[CPL];
+    float fb[CPL], lb[CPL], h[CPL], pf[CPL];
     load_f32<CPL>(p.f_bias ? p.f_bias + d0 : nullptr, fb, 0.0f);
+    load_f32<CPL>(p.f_lower ? p.f_lower + d0 : nullptr, lb, 0.0f);
     // every load is issued (a ragged last chunk re-reads its last token), so the wait before
     // token t covers only the loads of tokens up to t
     using Raw = RawVec<BF16, CPL>;
@@ -835,7 +846,7 @@ __global__ __launch_bounds__(256) void scan_local_row_kernel(ScanArgs p) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
                 float f;
-                h[k] = gate_step(h[k], i4[k], f4[k], fb[k], &f);
+                h[k] = gate_step(h[k], i4[k], f4[k], fb[k], lb[k], &f);
                 pf[k] *= f;
             }
         }

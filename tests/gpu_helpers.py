@@ -51,11 +51,11 @@ def stage_recheck(orc, st: dict, w_cat: np.ndarray, gamma=None, eps: float = 1e-
 
 
 def make_block(orc, lat: dict, device="cuda", f_bias=None, gnorm_w=None, gate_mode=0,
-               eps=1e-6):
+               eps=1e-6, f_lower=None):
     """Device block from latent weights (library host quantizer) and the oracle's own
     ternarization of the same latents (asserted identical)."""
     blk = api.Block.from_latents(lat, device, f_bias=f_bias, gnorm_w=gnorm_w, eps=eps,
-                                 gate_mode=gate_mode)
+                                 gate_mode=gate_mode, f_lower=f_lower)
     W = {}
     for k in ("i", "f", "g", "o", "gate", "up", "down"):
         q, s = orc.ternarize(lat[k])
@@ -81,7 +81,8 @@ def round_act(orc, v, bf16: bool) -> np.ndarray:
 
 def block_stage_checks(orc, cap: dict, W: dict, x_rows: np.ndarray, bf16: bool, *,
                        seq_rows: tuple | None = None, f_bias=None, gnorm_w=None,
-                       gate_mode: int = 0, h0=None, h_last=None, y_rows=None) -> dict:
+                       gate_mode: int = 0, h0=None, h_last=None, y_rows=None,
+                       f_lower=None) -> dict:
     """Stage-wise parity of one block run from its capture (host dicts per stage).
 
     Integers: every stage's int8 codes and int32 accumulators must be bit-exact against the
@@ -108,7 +109,8 @@ def block_stage_checks(orc, cap: dict, W: dict, x_rows: np.ndarray, bf16: bool, 
     if seq_rows is not None:
         B, T = seq_rows
         o_ref, h_ref = orc.mlgru(st["y_out"].astype(np.float64).reshape(B, T, 3 * D),
-                                 f_bias=f_bias, h0=h0, gnorm_w=gnorm_w, gate_mode=gate_mode)
+                                 f_bias=f_bias, h0=h0, gnorm_w=gnorm_w, gate_mode=gate_mode,
+                                 f_lower=f_lower)
         # g_norm's output is materialised in the activation dtype before o_proj
         stats["mlgru"] = rel_check(o_in, round_act(orc, o_ref.reshape(-1, D), bf16), tol,
                                    "g_norm output")

@@ -332,7 +332,7 @@ def pin_output_gate(orc):
 
 
 def pin_hgrn_lower_bound_gate(orc):
-    """Reading R9: f = lb + (1 - lb)*sigmoid(f_pre + b_f).  lb = 0 is the plain MLGRU bit
+    """Reading R12: f = lb + (1 - lb)*sigmoid(f_pre + b_f).  lb = 0 is the plain MLGRU bit
     for bit; lb = 1 keeps the state exactly (also through a whole block); lb = 0.5 with
     f_pre = 0 gives f = 0.75, so with SiLU(40) = 40 (fp64) and h0 = 0 the state runs
     10, 17.5, 23.125 (dyadic, exact)."""
@@ -358,7 +358,7 @@ def pin_hgrn_lower_bound_gate(orc):
 
 
 def pin_hgrn_lower_bounds(orc):
-    """Reading R9's bounds: an exclusive cumulative softmax over the layers.  Equal logits
+    """Reading R12's bounds: an exclusive cumulative softmax over the layers.  Equal logits
     over 4 layers give 0, 1/4, 1/2, 3/4 exactly; for any logits layer 0 is 0, the bound
     grows with depth and stays below 1, and the last layer's bound is 1 minus the softmax
     weight of the last layer."""

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.mmf_abi_version() == 1
+    assert lib.mmf_abi_version() == 2
 
 
 def test_timing_names(lib):
@@ -201,3 +201,58 @@ def test_no_device_is_an_error_not_a_crash(lib):
         pytest.skip("GPU present")
     rc = lib.bitlinear_forward(C.byref(_bl()), FAKE, 0, 4, FAKE, 0, FAKE, 1 << 20, None, None)
     assert rc in (-6, -7)
+
+
+@pytest.mark.parametrize("L_,D,scale", [(4, 3, 0.0), (24, 64, 2.0), (32, 2560, 1.0)])
+def test_host_hgrn_lower_bounds_match_oracle(orc, L_, D, scale):
+    """The library's host bound builder and the oracle's agree bit for bit (both sum in
+    double in the same order); equal logits give l / L."""
+    g = (np.random.default_rng(L_ + D).standard_normal((L_, D)) * scale).astype(np.float32)
+    lb = api.hgrn_lower_bounds(g)
+    assert np.array_equal(lb, orc.hgrn_lower_bounds(g))
+    if scale == 0.0:
+        assert np.array_equal(lb, np.repeat((np.arange(L_) / L_)[:, None], D, 1).astype(np.float32))
+
+
+def test_hgrn_lower_bounds_validation(lib):
+    g = np.zeros((2, 4), np.float32)
+    out = np.zeros((2, 4), np.float32)
+    vp = C.c_void_p
+    assert lib.mmf_hgrn_lower_bounds(None, 2, 4, out.ctypes.data_as(vp)) == -1
+    assert lib.mmf_hgrn_lower_bounds(g.ctypes.data_as(vp), 0, 4, out.ctypes.data_as(vp)) == -2
+
+
+@pytest.mark.parametrize("k", [16, 64, 80, 2048, 5632])
+def test_host_trit_pack_matches_oracle(orc, k):
+    """The library's base-3 packing equals the oracle's byte for byte; the library's unpack
+    (fixed-point digit extraction) inverts it; invalid bytes and padding are rejected."""
+    q = np.random.default_rng(k).integers(-1, 2, (19, k)).astype(np.int8)
+    p = api.pack_trits(q)
+    assert api.trit_row_bytes(k) == orc.trit_row_bytes(k)
+    assert np.array_equal(p, orc.pack_trits(q))
+    assert np.array_equal(api.unpack_trits(p, k), q)
+    bad = p.copy()
+    bad[3, 0] = 1                     # no group of five trits packs to 1
+    with pytest.raises(L.MMFError):
+        api.unpack_trits(bad, k)
+    with pytest.raises(L.MMFError):
+        api.pack_trits(np.full((1, k), 2, np.int8))
+
+
+def test_lower_bound_and_trit_validation_codes(lib):
+    """f_lower is read 16 bytes at a time; the trit BitLinear takes 0..16 rows and K a
+    multiple of 64 up to 10240."""
+    b = _block()
+    b.f_lower = FAKE + 4
+    assert lib.block_forward(C.byref(b), FAKE, 1, 1, 64, None, FAKE, FAKE, 1 << 30, None, None) == -3
+    a = L.mmf_mlgru_args(FAKE, 0, None, None, None, None, 1e-6, 0, FAKE, 0, 2, 64, 256, FAKE + 4)
+    assert lib.mlgru_scan(C.byref(a), FAKE, 1 << 30, None) == -3
+    t = L.mmf_bitlinear_trits(FAKE, 0.5, None, None, 1e-6, 256, 64)
+    f = lib.bitlinear_forward_trits
+    assert f(C.byref(t), FAKE, 0, 17, FAKE, 0, None, None) == -2
+    assert f(C.byref(t), FAKE, 0, 0, FAKE, 0, None, None) == 0
+    assert f(C.byref(t), FAKE + 8, 0, 2, FAKE, 0, None, None) == -3
+    assert f(C.byref(t), FAKE, 7, 2, FAKE, 0, None, None) == -4
+    for K in (100, 10304):
+        t.K = K
+        assert f(C.byref(t), FAKE, 0, 2, FAKE, 0, None, None) == -2

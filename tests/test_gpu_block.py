@@ -235,3 +235,34 @@ def test_side_stream_calls(orc):
     del junk
     assert torch.equal(y0, y1) and torch.equal(b0, b1) and torch.equal(g0, g1)
 
+
+@pytest.mark.parametrize("B,T", [(2, 40), (1, 1), (3, 1)], ids=["prefill", "decode1", "decode3"])
+def test_block_hgrn_lower_bound(orc, B, T):
+    """A block whose forget gate has HGRN's lower bound (the bounds of layer 5 of a 12-layer
+    stack): prefill through the scan kernels, one-token steps through the o_proj kernel's
+    fused MLGRU step (B = 1) and through the scan kernel (B = 3), stage-checked from captures
+    and end to end over the steps."""
+    D, F = 256, 704
+    note(f"block lower bound B={B} T={T}")
+    lbs = orc.hgrn_lower_bounds(synth.gaussian(5, (12, D), 1.0))
+    lb = lbs[5]
+    assert np.array_equal(api.hgrn_lower_bounds(synth.gaussian(5, (12, D), 1.0))[5], lb)
+    lat = small_latents(61, D, F)
+    fb = np.full(D, 0.3, np.float32)
+    blk, W = make_block(orc, lat, f_bias=fb, f_lower=lb)
+    steps = 6 if T == 1 else 1
+    x = synth.round_to_bf16(synth.gaussian(62, (B, T * steps, D)))
+    xd = dev(x, torch.bfloat16)
+    h = torch.zeros((B, D), device="cuda")
+    ys = []
+    for s in range(steps):
+        h_prev = host(h).copy()
+        cap = api.BlockCapture.alloc(0, B * T, D, F)
+        y = api.block_forward(blk, xd[:, s * T:(s + 1) * T].contiguous(), h_state=h, capture=cap)
+        torch.cuda.synchronize()
+        ch = {k: getattr(cap, k).host() for k in ("ifg", "o", "gateup", "down")}
+        block_stage_checks(orc, ch, W, x[:, s * T:(s + 1) * T], True, seq_rows=(B, T),
+                           f_bias=fb, h0=h_prev, h_last=host(h), y_rows=host(y), f_lower=lb)
+        ys.append(y)
+    r = orc.block(x, W, f_bias=fb, resid_bf16=True, f_lower=lb)
+    e2e_checks(host(torch.cat(ys, dim=1)), r["y"], True, got_h=host(h), ref_h=r["h_last"])

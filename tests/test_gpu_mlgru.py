@@ -92,3 +92,25 @@ def test_mlgru_empty_sequence_copies_state():
     torch.cuda.synchronize()
     assert out.shape == (B, 0, D)
     assert np.array_equal(hT.cpu().numpy(), h0)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(1, 1, 256), (2, 33, 256), (3, 100, 1024), (2, 70, 2560),
+                                   (1, 2048, 512), (2, 64, 192)])
+def test_mlgru_hgrn_lower_bound(orc, B, T, D, dt):
+    """HGRN's forget-gate lower bound f = lb + (1 - lb)*sigmoid(f_pre + b_f) in every scan
+    path (one chunk, chunk seams, ragged tails, channel-quad layout at D = 192)."""
+    note(f"mlgru lower bound B={B} T={T} D={D} dt={dt}")
+    ifg, fb, h0, gw = _inputs(B * 77 + T + D, B, T, D, dt)
+    lb = np.clip(synth.gaussian(B + T + D, (D,), 0.3) + 0.5, 0.0, 0.97).astype(np.float32)
+    out, hT = api.mlgru_scan(dev(ifg, dt), f_bias=dev(fb), h0=dev(h0), gnorm_w=dev(gw),
+                             out_dtype=torch.float32, f_lower=dev(lb))
+    torch.cuda.synchronize()
+    out_o, hT_o = orc.mlgru(ifg.astype(np.float64), f_bias=fb, h0=h0, gnorm_w=gw, f_lower=lb)
+    rel_check(host(out), out_o, 1e-3, "out")
+    rel_check(host(hT), hT_o, 1e-3, "h_T")
+    # lb = 1: the state never changes, bit for bit
+    _, hT1 = api.mlgru_scan(dev(ifg, dt), f_bias=dev(fb), h0=dev(h0), out_dtype=torch.float32,
+                            f_lower=torch.ones(D, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(hT1.cpu().numpy(), h0)

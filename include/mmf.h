@@ -265,6 +265,19 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
                   float *h_state, void *y, void *ws, size_t ws_bytes,
                   const mmf_capture *cap, hipStream_t stream);
 
+/* block_forward without a caller workspace and without any device allocation, for callers
+ * that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The scratch is a static device array of block_scratch_bytes() bytes
+ * (32 MiB), one per GPU, reserved when the library is loaded onto it and held until the
+ * process ends; the call fails with MMF_EWORKSPACE, queueing nothing, when
+ * block_workspace_bytes(w, B, T) exceeds it (for example above 850 token rows at hidden
+ * 2048 / GLU 5632).  Same arguments and results as block_forward without capture.  Every
+ * call on one GPU uses that GPU's scratch: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller. */
+size_t block_scratch_bytes(void);
+int block_forward_noalloc(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
+                          float *h_state, void *y, hipStream_t stream);
+
 /* Ternary embedding gather of the 32000-entry embedding [HL-init], read as a ternary
  * matrix like every other weight matrix [DC-ternary] (a reading: the pages do not say how
  * the embedding is stored): x[t][:] = s_E * q_E[ids[t]][:], rounded to dt.

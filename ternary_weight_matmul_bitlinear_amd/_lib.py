@@ -84,6 +84,8 @@ SIGNATURES = {
     "block_workspace_bytes": (sz, [P(mmf_block), i64, i64]),
     "block_forward": (C.c_int, [P(mmf_block), vp, C.c_int, i64, i64, vp, vp, vp, sz,
                                 P(mmf_capture), vp]),
+    "block_scratch_bytes": (sz, []),
+    "block_forward_noalloc": (C.c_int, [P(mmf_block), vp, C.c_int, i64, i64, vp, vp, vp]),
     "embedding_forward": (C.c_int, [vp, f32, i64, i64, vp, i64, vp, C.c_int, vp]),
     "stack_workspace_bytes": (sz, [P(mmf_stack), i64, i64]),
     "stack_forward": (C.c_int, [P(mmf_stack), vp, vp, C.c_int, i64, i64, vp, vp, vp, vp, sz, vp]),

@@ -379,6 +379,21 @@ def block_forward(block: Block, x: torch.Tensor, h_state: torch.Tensor | None = 
         return y
 
 
+def block_forward_noalloc(block: Block, x: torch.Tensor, h_state: torch.Tensor | None = None,
+                          y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """block_forward on the library's static per-GPU scratch (block_forward_noalloc): the
+    library allocates nothing; y is allocated here only when the caller passes none."""
+    with _on(stream):
+        B, T, D = x.shape
+        if y is None:
+            y = torch.empty_like(x)
+        d = block.desc()
+        L.check("block_forward_noalloc",
+                L.lib().block_forward_noalloc(C.byref(d), _ptr(x), _dt(x.dtype), B, T,
+                                              _ptr(h_state), _ptr(y), _stream()))
+        return y
+
+
 def embedding_forward(packed: torch.Tensor, scale: float, vocab: int, D: int,
                       ids: torch.Tensor, dtype=torch.bfloat16, stream=None) -> torch.Tensor:
     with _on(stream):

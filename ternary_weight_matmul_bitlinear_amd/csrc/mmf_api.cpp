@@ -317,6 +317,33 @@ static size_t scan_bytes(int64_t B, int64_t T, int64_t D) {
     return 3 * align_up(static_cast<size_t>(B * nc * D) * 4);
 }
 
+// ------------------------------------------------------------ static scratch
+// Device scratch of the no-allocation entry point: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::mutex g_scr_mu;
+static std::vector<void *> g_scr_ptr;  // per device; nullptr until looked up
+
+static int scratch_for_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_error(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if (dev >= static_cast<int>(g_scr_ptr.size())) g_scr_ptr.resize(dev + 1, nullptr);
+    if (!g_scr_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_error(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return set_error(MMF_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scr_ptr[dev] = p;
+    }
+    *out = g_scr_ptr[dev];
+    return MMF_OK;
+}
+
 }  // namespace mmf
 
 using namespace mmf;
@@ -742,6 +769,25 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     }
     if (e != hipSuccess) return hip_error(e, "block_forward glu launch");
     return MMF_OK;
+}
+
+size_t block_scratch_bytes(void) { return kScratchBytes; }
+
+int block_forward_noalloc(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
+                          float *h_state, void *y, hipStream_t stream) {
+    int rc = check_block(w, "block_forward_noalloc");
+    if (rc) return rc;
+    if (B < 0 || T < 0) return set_error(MMF_ESHAPE, "block_forward_noalloc: B=%lld T=%lld", (long long)B, (long long)T);
+    if (B * T == 0) return MMF_OK;
+    const size_t need = block_workspace_bytes(w, B, T);
+    if (need > kScratchBytes)
+        return set_error(MMF_EWORKSPACE, "block_forward_noalloc: B*T=%lld needs %zu bytes of scratch, more than the %zu-byte static scratch",
+                         (long long)(B * T), need, kScratchBytes);
+    void *ws = nullptr;
+    if ((rc = check_device()) || (rc = scratch_for_current_device(&ws))) return rc;
+    // every byte of the workspace a block_forward call reads was written earlier in the same
+    // call, so the scratch needs no clearing between calls
+    return block_forward(w, x, dt, B, T, h_state, y, ws, kScratchBytes, nullptr, stream);
 }
 
 // ------------------------------------------------------------------ embedding

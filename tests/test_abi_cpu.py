@@ -239,9 +239,10 @@ def test_host_trit_pack_matches_oracle(orc, k):
         api.pack_trits(np.full((1, k), 2, np.int8))
 
 
-def test_lower_bound_and_trit_validation_codes(lib):
+def test_lower_bound_trit_and_noalloc_validation_codes(lib):
     """f_lower is read 16 bytes at a time; the trit BitLinear takes 0..16 rows and K a
-    multiple of 64 up to 10240."""
+    multiple of 64 up to 10240; block_forward_noalloc rejects work beyond its static scratch
+    before touching the device."""
     b = _block()
     b.f_lower = FAKE + 4
     assert lib.block_forward(C.byref(b), FAKE, 1, 1, 64, None, FAKE, FAKE, 1 << 30, None, None) == -3
@@ -256,3 +257,7 @@ def test_lower_bound_and_trit_validation_codes(lib):
     for K in (100, 10304):
         t.K = K
         assert f(C.byref(t), FAKE, 0, 2, FAKE, 0, None, None) == -2
+    big = _block(D=2048, F=5632)
+    assert lib.block_workspace_bytes(C.byref(big), 1, 4096) > lib.block_scratch_bytes()
+    assert lib.block_forward_noalloc(C.byref(big), FAKE, 1, 1, 4096, None, FAKE, None) == -5
+    assert lib.block_forward_noalloc(C.byref(big), FAKE, 1, 0, 4096, None, FAKE, None) == 0

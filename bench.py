@@ -384,6 +384,28 @@ def bench_decode(w, args, batches, orc) -> list:
         gemv_bytes, step_bytes = decode_bytes(B, D, F, V, L)
         achieved = gemv_bytes * steps / (ms * 1e-3) / 1e9 if n else None
         name = f"{w.name}@{B}"
+        one = None
+        if B == 1 and args.one_launch:
+            # the whole step in one cooperative launch (stack_decode_step): its kernel
+            # duration from HIP events on the launch stream is the step's BitLinear time
+            ds = api.DecodeStep(stack)
+            h1 = torch.zeros((L, 1, D), dtype=torch.float32, device="cuda")
+            lg1 = torch.empty((1, V), dtype=torch.float32, device="cuda")
+            run1 = lambda i: ds.step(ids_all[i % (args.warmup + steps)], h1, logits=lg1)
+            spin_up(lambda: run1(0), args.spin_up)
+            for i in range(args.warmup):
+                run1(i)
+            torch.cuda.synchronize()
+            wall1, q1 = timed_events(["gemv"], lambda i: run1(args.warmup + i), steps)
+            ds.status()
+            n1, ms1 = q1["gemv"]
+            k1 = ms1 / n1 if n1 else None
+            one = {"kernel": "one cooperative launch per step (embedding, 24 blocks, head)",
+                   "ms_per_step": wall1, "kernel_ms": k1,
+                   "achieved_gbs": gemv_bytes / (k1 * 1e-3) / 1e9 if k1 else None}
+            one["hbm_frac"] = one["achieved_gbs"] / PEAK_HBM_GBS if k1 else None
+            log(f"{name}: one-launch step {wall1:.4f} ms (kernel {k1:.4f} ms)")
+            del ds, h1, lg1
         log(f"{name}: graph-replayed step {ms_step:.4f} ms, eager {eager_ms:.4f} ms")
         res = {"workload": name, "value": B / (ms_step * 1e-3), "unit": "tokens/s",
                "ms_per_step": ms_step, "steps": steps,
@@ -400,6 +422,17 @@ def bench_decode(w, args, batches, orc) -> list:
                             "launches_per_step": n / steps},
                "step_hbm_fraction": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                "step_algorithmic_bytes": step_bytes, "eager_ms_per_step": eager_ms}
+        if one is not None:
+            # the one-launch step is the batch-1 path: it becomes the line's value and roofline,
+            # the graph-replayed launch-per-stage step is kept beside it
+            res["launch_per_stage"] = {"ms_per_step": ms_step, "roofline": res["roofline"]}
+            res["value"] = B / (one["ms_per_step"] * 1e-3)
+            res["ms_per_step"] = one["ms_per_step"]
+            res["roofline"] = {"kernel": one["kernel"], "bound": "hbm", "achieved": one["achieved_gbs"],
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": one["hbm_frac"],
+                               "traffic": None, "algorithmic_bytes_per_step": gemv_bytes,
+                               "kernel_ms": one["kernel_ms"]}
+            res["step_hbm_fraction"] = step_bytes / (one["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS
         if orc is not None:
             Bs = min(B, args.cpu_seqs_decode)
             ids_np = synth.token_ids(w, 1, B)[0][:Bs]
@@ -528,6 +561,8 @@ def main() -> int:
                          "streaming; prefill: MFMA kernels; tiles: 128-row MFMA tiles only)")
     ap.add_argument("--kernel-sweep", action="store_true",
                     help="decode stacks: also time single BitLinear launches on rotated weights")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="decode stack at batch 1: also time the one-launch step (stack_decode_step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="decode stacks: time eager steps only (no HIP graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -10,6 +10,8 @@
  *                activation quantization; MLGRU hidden state updated token by token through
  *                gates in (0,1); MatMul-free GLU = two BitLinears, SiLU on one branch,
  *                element-wise product, a third BitLinear.
+ *   [DC-gpu]     same page, section "From optimised GPU to custom FPGA": fused kernels
+ *                avoid memory round trips; token generation is limited by moving weights.
  *   [HL-fbl]     Hysen Labs project page "MatMul-Free LM", section "FusedBitLinear": each
  *                projection RMS-normalises its input, quantizes it and accumulates it against
  *                the ternary weights inside one fused kernel.
@@ -305,6 +307,35 @@ size_t stack_workspace_bytes(const mmf_stack *s, int64_t B, int64_t T);
 int stack_forward(const mmf_stack *s, const int32_t *ids, const void *x, mmf_dtype dt,
                   int64_t B, int64_t T, float *h_state, void *y, float *logits, void *ws,
                   size_t ws_bytes, hipStream_t stream);
+
+/* One decode step of a stack for ONE sequence in a single cooperative launch: embedding of
+ * ids[0], every block (state h_state [n_layers][D] fp32, read and written), the head
+ * (logits [vocab] fp32, nullable) and the last hidden row y [D] (bf16, nullable), with the
+ * arithmetic of stack_forward (bf16 activations).  Generating a token is limited by moving
+ * the weights ([DC-gpu], section "From optimised GPU to custom FPGA"), and with one token
+ * every BitLinear is a short dependent stage: here each workgroup of a co-resident grid
+ * streams a slice of every stage's weights and the stages hand their outputs over through
+ * the workspace instead of through kernel launches.
+ * The workspace (stack_decode_workspace_bytes) belongs to one stack: stack_decode_init
+ * writes its layer table and clears it (synchronising the stream; call it once, and again
+ * after a timeout); consecutive steps on one workspace must be ordered.  Needs an
+ * embedding and a head; limits: D <= 4096, F <= 8192, at most 128 rows of a stage per
+ * workgroup (one workgroup per CU), else MMF_ESHAPE (use stack_forward).  Every wait of
+ * the kernel is bounded (0.2 s); a timeout ends the kernel and is reported by
+ * stack_decode_status, which synchronises the stream.  Workspace layout (for inspection):
+ * bytes [0, 12) hold the epoch, a counter and the timeout flag (uint32 each); bytes
+ * [256, 256 + 16 * (4 * n_layers + 2)) hold 100 MHz stamps (uint64 pairs) taken by workgroup
+ * 0 in the last step: the kernel's start (twice), then for every layer the start and end
+ * of its waits for the layer input (zero for layer 0), i|f|g, y1 and the GLU hidden, then
+ * the head's wait, then the end of its work (and a zero); the last
+ * align_up((n_layers + 1) * S * 8, 256) bytes, S = 5*D/2 + F/2, are the exchange words of
+ * the last step: word l*S + j (1 <= l <= n_layers, j < D/2) holds layer l's input elements
+ * 2j, 2j+1 as bf16 in its low 32 bits (layer n_layers: the head's input). */
+size_t stack_decode_workspace_bytes(const mmf_stack *s);
+int stack_decode_init(const mmf_stack *s, void *ws, size_t ws_bytes, hipStream_t stream);
+int stack_decode_step(const mmf_stack *s, const int32_t *ids, float *h_state, float *logits,
+                      void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+int stack_decode_status(const void *ws, hipStream_t stream);
 
 #ifdef __cplusplus
 }

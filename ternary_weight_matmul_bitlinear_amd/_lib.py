@@ -89,6 +89,10 @@ SIGNATURES = {
     "embedding_forward": (C.c_int, [vp, f32, i64, i64, vp, i64, vp, C.c_int, vp]),
     "stack_workspace_bytes": (sz, [P(mmf_stack), i64, i64]),
     "stack_forward": (C.c_int, [P(mmf_stack), vp, vp, C.c_int, i64, i64, vp, vp, vp, vp, sz, vp]),
+    "stack_decode_workspace_bytes": (sz, [P(mmf_stack)]),
+    "stack_decode_init": (C.c_int, [P(mmf_stack), vp, sz, vp]),
+    "stack_decode_step": (C.c_int, [P(mmf_stack), vp, vp, vp, vp, vp, sz, vp]),
+    "stack_decode_status": (C.c_int, [vp, vp]),
 }
 
 

@@ -450,6 +450,46 @@ def stack_forward(stack: Stack, B: int, T: int, ids: torch.Tensor | None = None,
         return (y if want_y else None), (logits if want_logits else None)
 
 
+class DecodeStep:
+    """One-launch decode step of a stack for one sequence (stack_decode_*): owns the
+    workspace (exchange area and layer table), initialised once for the stack."""
+
+    def __init__(self, stack: Stack, device="cuda", stream=None):
+        self.stack = stack
+        with _on(stream):
+            nb = int(L.lib().stack_decode_workspace_bytes(C.byref(stack._desc)))
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+            self.init(stream)
+
+    def init(self, stream=None) -> None:
+        with _on(stream):
+            L.check("stack_decode_init",
+                    L.lib().stack_decode_init(C.byref(self.stack._desc), _ptr(self.ws),
+                                              self.ws.numel(), _stream()))
+
+    def step(self, ids: torch.Tensor, h_state: torch.Tensor, logits: torch.Tensor | None = None,
+             y: torch.Tensor | None = None, stream=None):
+        """ids [1] int32, h_state [L, 1, D] fp32 (updated); returns (logits [1, V] fp32, y)."""
+        with _on(stream):
+            L.check("stack_decode_step",
+                    L.lib().stack_decode_step(C.byref(self.stack._desc), _ptr(ids), _ptr(h_state),
+                                              _ptr(logits), _ptr(y), _ptr(self.ws),
+                                              self.ws.numel(), _stream()))
+            return logits, y
+
+    def status(self, stream=None) -> None:
+        with _on(stream):
+            L.check("stack_decode_status", L.lib().stack_decode_status(_ptr(self.ws), _stream()))
+
+    def stage_stamps(self) -> torch.Tensor:
+        """Workgroup 0's 100 MHz stamps of the last step, [4 * n_layers + 2, 2] int64 (the
+        workspace bytes 256 onwards): row 0 the kernel's start, row 4l + k the start and end of
+        layer l's wait k (layer input, i|f|g, y1, GLU hidden), row 4 n_layers the head's wait,
+        the last row's first entry the end of the work."""
+        n = 4 * len(self.stack.blocks) + 2
+        return self.ws[256:256 + 16 * n].view(torch.int64).view(n, 2).cpu()
+
+
 def timing_enable(on: bool = True) -> None:
     L.check("mmf_timing_enable", L.lib().mmf_timing_enable(int(on)))
 

@@ -27,8 +27,9 @@
 //     (lane, byte) -> k pairing.  A ragged last k-tile (K % 128 == 64) zeroes the B
 //     operand of the upper lane half;
 //   - workgroups are dispatched round-robin over the 8 XCDs; tile ids are remapped so each
-//     XCD owns a contiguous run of tiles (N fastest), i.e. a few M-tiles of activations and
-//     all weight tiles, which stay in that XCD's L2.
+//     XCD owns a contiguous run of tiles, walked in groups of 8 M-tiles (N-tile by N-tile,
+//     the group's M-tiles side by side): the activation tiles of a group stay in that XCD's
+//     L2 while each weight tile is read once per group.
 // Epilogues (fused, in registers): y = acc*s_w*a (+bias) stored in fp32/bf16; the same plus
 // a residual; or SiLU(gate)*up when the tile pairs 128 gate rows with the same 128 up rows.
 #include "mmf_internal.h"
@@ -112,12 +113,20 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     const int wm = wave % WM, wn = wave / WM;
     const int K = p.K, KW = K / 16;  // words per packed row
 
-    // ---- XCD-aware tile id: XCD x (= blockIdx % 8) owns a contiguous range of tiles
+    // ---- XCD-aware tile id: XCD x (= blockIdx % 8) owns a contiguous range of tiles, and
+    //      tiles run in groups of GM M-tiles: N-tile by N-tile, the GM M-tiles of a group
+    //      side by side.  The ~64 tiles an XCD runs at once then share GM activation tiles
+    //      (GM x 128 rows, kept in its L2 while the group walks N) and a few weight tiles, so
+    //      every weight tile is fetched once per group instead of once per M-tile.
     const int nwg = gridDim.x, bid = blockIdx.x;
     const int qx = nwg >> 3, rx = nwg & 7, xcd = bid & 7, idx = bid >> 3;
     const int tile = (xcd < rx ? xcd * (qx + 1) : rx * (qx + 1) + (xcd - rx) * qx) + idx;
-    const int mt = tile / p.tiles_n_total;
-    int nt = tile % p.tiles_n_total;
+    constexpr int GM = 8;
+    const int ntn = p.tiles_n_total, n_mt = static_cast<int>((p.M + BM - 1) / BM);
+    const int grp = tile / (GM * ntn), in_g = tile % (GM * ntn);
+    const int gm = n_mt - grp * GM < GM ? n_mt - grp * GM : GM;   // M-tiles in this group
+    const int mt = grp * GM + in_g % gm;
+    int nt = in_g / gm;
     int sg = 0;
     while (sg + 1 < p.nseg && nt >= p.tiles_n[sg]) { nt -= p.tiles_n[sg]; ++sg; }
     const int64_t m0 = static_cast<int64_t>(mt) * BM;

@@ -871,3 +871,159 @@ int stack_forward(const mmf_stack *s, const int32_t *ids, const void *x, mmf_dty
 }
 
 }  // extern "C"
+
+// --------------------------------------------- one-launch decode step (one sequence)
+namespace {
+struct DecodeLayout {
+    size_t trace, table, xch, total;   // byte offsets of the stamps, layer table, exchange area
+};
+DecodeLayout decode_layout(const mmf_stack *s) {
+    const int64_t D = s->blocks[0].i.K, F = s->blocks[0].gate.N, L = s->n_layers;
+    DecodeLayout d;
+    d.trace = 256;
+    d.table = d.trace + align_up(static_cast<size_t>(4 * L + 2) * 16);
+    d.xch = d.table + align_up(static_cast<size_t>(L) * sizeof(PLayer));
+    d.total = d.xch + align_up(static_cast<size_t>(L + 1) * static_cast<size_t>(D / 2 * 5 + F / 2) * 8);
+    return d;
+}
+int decode_grid() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    int per_cu = 0;
+    if (persist_occupancy(&per_cu) != 0 || per_cu < 1) return 0;
+    return prop.multiProcessorCount;   // one workgroup per CU
+}
+int check_decode_stack(const mmf_stack *s, int grid, const char *who) {
+    if (!s || !s->blocks || s->n_layers <= 0) return set_error(MMF_EINVAL, "%s: empty stack", who);
+    if (!s->embed_packed || !s->head) return set_error(MMF_EINVAL, "%s: the stack needs an embedding and a head", who);
+    int rc;
+    const int32_t D = s->blocks[0].i.K, F = s->blocks[0].gate.N;
+    for (int l = 0; l < s->n_layers; ++l) {
+        if ((rc = check_block(&s->blocks[l], who))) return rc;
+        if (s->blocks[l].i.K != D || s->blocks[l].gate.N != F)
+            return set_error(MMF_ESHAPE, "%s: layer %d has D=%d F=%d, not %d/%d", who, l, s->blocks[l].i.K, s->blocks[l].gate.N, D, F);
+    }
+    if ((rc = check_linear(s->head, "head"))) return rc;
+    if (s->head->K != D) return set_error(MMF_ESHAPE, "%s: head K=%d != D=%d", who, s->head->K, D);
+    int mu, mw, mk, md, mr;
+    persist_limits(&mu, &mw, &mk, &md, &mr);
+    const int G = grid > 0 ? grid : 1;
+    auto per_wg = [&](int n, int unit) { return ((n / unit + G - 1) / G) * unit; };
+    const int V = s->head->N;
+    if (D > md || F > mk || D % 4 || F % 4)
+        return set_error(MMF_ESHAPE, "%s: D=%d F=%d outside the one-launch limits (D <= %d, F <= %d)", who, D, F, md, mk);
+    if (per_wg(V, 1) > mr || 2 * per_wg(F, 2) > mr || per_wg(3 * D, 2) > mr)
+        return set_error(MMF_ESHAPE, "%s: more than %d rows per workgroup at %d workgroups", who, mr, G);
+    const int need[5] = {persist_max_units(per_wg(3 * D, 2), D), persist_max_units(per_wg(D, 2), D),
+                         persist_max_units(2 * per_wg(F, 2), D), persist_max_units(per_wg(D, 2), F),
+                         persist_max_units(per_wg(V, 1), D)};
+    int have[5];
+    persist_stage_units(have);
+    for (int k = 0; k < 5; ++k)
+        if (need[k] > have[k])
+            return set_error(MMF_ESHAPE, "%s: stage %d needs %d weight units per thread, more than %d, at %d workgroups", who, k, need[k], have[k], G);
+    (void)mu;
+    return MMF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t stack_decode_workspace_bytes(const mmf_stack *s) {
+    if (!s || !s->blocks || s->n_layers <= 0) return 0;
+    return decode_layout(s).total;
+}
+
+int stack_decode_init(const mmf_stack *s, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if ((rc = check_device())) return rc;
+    const int G = decode_grid();
+    if (G <= 0) return set_error(MMF_EHIP, "stack_decode_init: no occupancy for the one-launch decode kernel");
+    if ((rc = check_decode_stack(s, G, "stack_decode_init"))) return rc;
+    const DecodeLayout lay = decode_layout(s);
+    if (!ws || ws_bytes < lay.total) return set_error(MMF_EWORKSPACE, "stack_decode_init: workspace %zu < %zu", ws ? ws_bytes : 0, lay.total);
+    if (!aligned16(ws)) return set_error(MMF_EALIGN, "stack_decode_init: workspace not 16-byte aligned");
+    std::vector<PLayer> tab(s->n_layers);
+    for (int l = 0; l < s->n_layers; ++l) {
+        const mmf_block &b = s->blocks[l];
+        const mmf_bitlinear *m[7] = {&b.i, &b.f, &b.g, &b.o, &b.gate, &b.up, &b.down};
+        PLayer &t = tab[l];
+        for (int k = 0; k < 7; ++k) {
+            t.w[k] = m[k]->packed;
+            t.s[k] = m[k]->scale;
+            t.b[k] = m[k]->bias;
+        }
+        t.g_x = b.i.norm_w; t.e_x = b.i.eps;
+        t.g_o = b.o.norm_w; t.e_o = b.o.eps;
+        t.g_gu = b.gate.norm_w; t.e_gu = b.gate.eps;
+        t.g_down = b.down.norm_w; t.e_down = b.down.eps;
+        t.f_bias = b.f_bias;
+        t.f_lower = b.f_lower;
+        t.gnorm_w = b.gnorm_w;
+        t.g_eps = b.eps;
+        t.gate_mode = b.gate_mode;
+    }
+    char *base = static_cast<char *>(ws);
+    hipError_t e = hipMemsetAsync(base, 0, lay.total, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(base + lay.table, tab.data(), tab.size() * sizeof(PLayer), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);   // the host table is a local
+    if (e != hipSuccess) return hip_error(e, "stack_decode_init");
+    return MMF_OK;
+}
+
+int stack_decode_step(const mmf_stack *s, const int32_t *ids, float *h_state, float *logits,
+                      void *y, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc;
+    if (!s || !s->blocks || s->n_layers <= 0) return set_error(MMF_EINVAL, "stack_decode_step: empty stack");
+    if (!ids || !h_state) return set_error(MMF_EINVAL, "stack_decode_step: NULL ids or h_state");
+    if (!logits && !y) return set_error(MMF_EINVAL, "stack_decode_step: neither logits nor y");
+    if ((y && !aligned16(y)) || (logits && !aligned16(logits)) || !aligned16(h_state))
+        return set_error(MMF_EALIGN, "stack_decode_step: y/logits/h_state not 16-byte aligned");
+    const DecodeLayout lay = decode_layout(s);
+    if (!ws || ws_bytes < lay.total) return set_error(MMF_EWORKSPACE, "stack_decode_step: workspace %zu < %zu", ws ? ws_bytes : 0, lay.total);
+    if (!aligned16(ws)) return set_error(MMF_EALIGN, "stack_decode_step: workspace not 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    const int G = decode_grid();
+    if (G <= 0) return set_error(MMF_EHIP, "stack_decode_step: no occupancy for the one-launch decode kernel");
+    if ((rc = check_decode_stack(s, G, "stack_decode_step"))) return rc;
+    char *base = static_cast<char *>(ws);
+    PersistArgs a{};
+    a.layers = reinterpret_cast<const PLayer *>(base + lay.table);
+    a.L = s->n_layers;
+    a.D = s->blocks[0].i.K;
+    a.F = s->blocks[0].gate.N;
+    a.V = s->head->N;
+    a.emb = s->embed_packed;
+    a.emb_scale = s->embed_scale;
+    a.vocab = s->vocab;
+    a.head = s->head->packed;
+    a.head_scale = s->head->scale;
+    a.head_bias = s->head->bias;
+    a.head_gamma = s->head->norm_w;
+    a.head_eps = s->head->eps;
+    a.ids = ids;
+    a.h_state = h_state;
+    a.logits = logits;
+    a.y = y;
+    a.xch = reinterpret_cast<uint64_t *>(base + lay.xch);
+    a.ctl = reinterpret_cast<uint32_t *>(base);
+    a.trace = reinterpret_cast<uint64_t *>(base + lay.trace);
+    a.spin_ticks = 20000000;   // 0.2 s per wait (100 MHz counter)
+    const hipError_t e = launch_decode_persistent(a, G, stream);
+    if (e != hipSuccess) return hip_error(e, "stack_decode_step launch");
+    return MMF_OK;
+}
+
+int stack_decode_status(const void *ws, hipStream_t stream) {
+    if (!ws) return set_error(MMF_EINVAL, "stack_decode_status: NULL workspace");
+    uint32_t ctl[3] = {0, 0, 0};
+    hipError_t e = hipMemcpyAsync(ctl, ws, sizeof ctl, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_error(e, "stack_decode_status");
+    if (ctl[2]) return set_error(MMF_EHIP, "stack_decode_step: a stage wait timed out (re-initialise the workspace)");
+    return MMF_OK;
+}
+
+}  // extern "C"

@@ -305,6 +305,46 @@ struct TritArgs {
     CapDev cap;            // x_in/q/a by column-block 0, acc/y_out by every block (stride N)
 };
 
+// One decode step of a whole stack for one sequence in one cooperative launch
+// (decode_persistent.hip).  The layer table lives in device memory (the caller's workspace).
+struct PLayer {
+    const uint32_t *w[7];        // packed i, f, g, o, gate, up, down
+    float s[7];                  // their absmean scales
+    const float *b[7];           // their biases (nullable)
+    const float *g_x, *g_o, *g_gu, *g_down;   // input RMSNorm gains (nullable)
+    float e_x, e_o, e_gu, e_down;
+    const float *f_bias, *f_lower, *gnorm_w;
+    float g_eps;
+    int32_t gate_mode;
+};
+struct PersistArgs {
+    const PLayer *layers;
+    int32_t L, D, F, V;
+    const uint32_t *emb;
+    float emb_scale;
+    int64_t vocab;
+    const uint32_t *head;
+    float head_scale;
+    const float *head_bias, *head_gamma;
+    float head_eps;
+    const int32_t *ids;          // [1]
+    float *h_state;              // [L][D]
+    float *logits;               // [V] or NULL
+    void *y;                     // [D] bf16 or NULL
+    uint64_t *xch;               // exchange words
+    uint32_t *ctl;               // [0] epoch, [1] finished workgroups, [2] timeout flag
+    int64_t spin_ticks;          // bound of every wait, in 100 MHz ticks
+    uint64_t *trace;             // NULL, or [2 * (4 * L + 2)] 100 MHz stamps of workgroup 0:
+                                 // the kernel's start, the (start, end) of each layer's waits
+                                 // for x (l > 0), i|f|g, y1 and the GLU hidden, the head's
+                                 // wait, the end of the work
+};
+int persist_limits(int *max_units, int *max_words, int *max_k, int *max_d, int *max_rows);
+int persist_max_units(int rows, int K);
+void persist_stage_units(int (&u)[5]);   // per-stage unit bounds: i|f|g, o, gate|up, down, head
+int persist_occupancy(int *blocks_per_cu);
+hipError_t launch_decode_persistent(const PersistArgs &a, int grid, hipStream_t s);
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);

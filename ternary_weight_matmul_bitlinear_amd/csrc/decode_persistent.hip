@@ -12,7 +12,11 @@
 // then the head).  Here every workgroup of one co-resident grid owns a slice of every
 // stage's weight rows and keeps the chain inside the kernel:
 //   - the slice of the next stage is requested into registers as soon as the current stage's
-//     outputs are stored, so its HBM latency overlaps the wait for the other workgroups;
+//     outputs are stored, and the small vectors the next stage reads (its quantizer's gain,
+//     for the MLGRU step the state, forget bias and bound and the g_norm weight) are copied
+//     into LDS by direct loads at the same point, with that stage's bias values; so the HBM
+//     latency of all of them overlaps the wait for the other workgroups, and no dependent
+//     global load is left between a wait and the stage's outputs;
 //   - a stage's outputs go to an exchange area as 64-bit words holding two bf16 values and
 //     the launch's tag in the upper half; a word is written with one 64-bit store and read
 //     with one 64-bit load, both relaxed device-scope atomics, so a reader that sees the
@@ -45,6 +49,7 @@ constexpr int kPMaxWD = 8;     // the same for hidden-size vectors (D <= 4096)
 constexpr int kPMaxK = 8192;   // widest BitLinear input
 constexpr int kPMaxD = 4096;   // widest hidden size
 constexpr int kPMaxRows = 128; // rows of one stage slice
+static_assert(kPMaxRows <= 2 * kPT, "an epilogue handles its rows in one pass");
 
 __device__ __forceinline__ uint64_t xch_load(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -103,29 +108,38 @@ struct Slice {
     int K, N;        // K of the input, rows per matrix
     int r0, nr;      // first concatenated row (or pair p0) and virtual rows
     int pairs;       // 1: gate|up pairs (nr = 2 * pairs count)
+    // The matrix is chosen by adding address differences, not by selecting among the fields:
+    // a select of two field loads is folded into one load at a lane-dependent offset, which
+    // sends the whole struct to scratch memory, and every scratch reload then waits for the
+    // weight loads issued before it.
     __device__ __forceinline__ const uint32_t *row(int v) const {
+        const intptr_t a0 = reinterpret_cast<intptr_t>(m0);
+        const intptr_t d1 = reinterpret_cast<intptr_t>(m1) - a0, d2 = reinterpret_cast<intptr_t>(m2) - a0;
+        int r;
+        intptr_t a;
         if (pairs) {
             const int np = nr / 2;
-            return v < np ? m0 + static_cast<int64_t>(r0 + v) * (K / 16)
-                          : m1 + static_cast<int64_t>(r0 + v - np) * (K / 16);
+            a = a0 + (v < np ? 0 : d1);
+            r = r0 + (v < np ? v : v - np);
+        } else {
+            const int c = r0 + v;
+            a = a0 + (c < N ? 0 : (c < 2 * N ? d1 : d2));
+            r = c < N ? c : (c < 2 * N ? c - N : c - 2 * N);
         }
-        const int r = r0 + v;
-        const uint32_t *m = r < N ? m0 : (r < 2 * N ? m1 : m2);
-        return m + static_cast<int64_t>(r % N) * (K / 16);
+        return reinterpret_cast<const uint32_t *>(a) + static_cast<int64_t>(r) * (K / 16);
     }
 };
 
 template <int NU>
 __device__ __forceinline__ void prefetch(const Slice &s, uint4 (&wv)[NU]) {
-    // every register of the array is written (units past the slice repeat its last unit), so
-    // no earlier contents stay live across the waits
+    // every register of the array is written (zero past the slice), so no earlier contents
+    // stay live across the waits; units past the slice issue no load
     const int upr = s.K / 64, U = s.nr * upr;
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-        int u = threadIdx.x + kPT * i;
-        u = u < U ? u : U - 1;
+        const int u = threadIdx.x + kPT * i;
         wv[i] = make_uint4(0u, 0u, 0u, 0u);
-        if (u >= 0) wv[i] = *reinterpret_cast<const uint4 *>(s.row(u / upr) + 4 * (u % upr));
+        if (u < U) wv[i] = *reinterpret_cast<const uint4 *>(s.row(u / upr) + 4 * (u % upr));
     }
 }
 
@@ -164,6 +178,8 @@ struct PState {   // per-workgroup LDS
     uint16_t xs[kPMaxD];    // the layer's input x (bf16 bits), for the o_proj residual
     uint16_t y1s[kPMaxD];   // the layer's y1 (bf16 bits), for the down residual
     int racc[kPMaxRows];
+    alignas(16) float gain[kPMaxK + 256];      // the next quantizer's gain (+ 1 KB of slack)
+    alignas(16) float vb[4][kPMaxD + 256];     // MLGRU step: h, forget bias, lower bound, g_norm weight
     Red red;
     float a;
     int rs;
@@ -171,29 +187,55 @@ struct PState {   // per-workgroup LDS
 
 namespace {
 
-// Bounded wait until every listed exchange word carries the tag; the words' value halves are
-// returned in vals.  false (for the whole workgroup) on a timeout or a reported error.
-template <int NW>
+// Copy n floats (n % 4 == 0, src 16-byte aligned; nothing when src is NULL) into LDS at dst
+// with direct 16-byte loads, 1 KB per wave instruction.  The copy lands asynchronously;
+// wait_words (or an explicit vmcnt wait and barrier) orders it before the reads.  Lanes past
+// the end re-read the last 16 bytes into dst's 1 KB of slack.
+__device__ __forceinline__ void stage_vec(const float *src, int n, float *dst) {
+    if (!src) return;
+    const int bytes = 4 * n, chunks = (bytes + 1023) >> 10;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+    for (int c = wave; c < chunks; c += kPT / 64) {
+        uint32_t off = static_cast<uint32_t>(c * 1024 + 16 * lane);
+        off = off < static_cast<uint32_t>(bytes) ? off : static_cast<uint32_t>(bytes - 16);
+        dma16(src, off, lds + static_cast<uint32_t>(c) * 1024u);
+    }
+}
+
+// Bounded wait until every word of NB lists of n_words exchange words (list b at base + b *
+// stride) carries the tag; word tid + 256 j of list b returns its value half in
+// vals[b * NW + j].  The lists are polled together, so one memory round trip serves all.
+// false (for the whole workgroup) on a timeout or a reported error.  Every direct-to-LDS copy
+// issued before it has landed when it returns.
+template <int NW, int NB = 1>
 __device__ __forceinline__ bool wait_words(const uint64_t *base, int n_words, uint32_t tag,
-                                           uint32_t (&vals)[NW], const PersistArgs &p,
-                                           int trace_slot = -1) {
+                                           uint32_t *vals, const PersistArgs &p,
+                                           int trace_slot = -1, int64_t stride = 0) {
+    static_assert(NW * NB <= 32, "pending mask");
     const uint64_t t_in = __builtin_amdgcn_s_memrealtime();
     uint32_t pending = 0;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-        vals[j] = 0u;
-        if (static_cast<int>(threadIdx.x) + kPT * j < n_words) pending |= 1u << j;
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            vals[b * NW + j] = 0u;
+            if (static_cast<int>(threadIdx.x) + kPT * j < n_words) pending |= 1u << (b * NW + j);
+        }
     }
     const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.spin_ticks;
     bool ok = true;
     while (pending) {
 #pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            if (pending & (1u << j)) {
-                const uint64_t w = xch_load(base + threadIdx.x + kPT * j);
-                if (static_cast<uint32_t>(w >> 32) == tag) {
-                    vals[j] = static_cast<uint32_t>(w);
-                    pending &= ~(1u << j);
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                if (pending & (1u << (b * NW + j))) {
+                    const uint64_t w = xch_load(base + b * stride + threadIdx.x + kPT * j);
+                    if (static_cast<uint32_t>(w >> 32) == tag) {
+                        vals[b * NW + j] = static_cast<uint32_t>(w);
+                        pending &= ~(1u << (b * NW + j));
+                    }
                 }
             }
         }
@@ -205,6 +247,7 @@ __device__ __forceinline__ bool wait_words(const uint64_t *base, int n_words, ui
         __builtin_amdgcn_s_sleep(1);
     }
     if (!ok) __hip_atomic_store(p.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmcnt<0>();   // this thread's direct-to-LDS copies have landed
     const bool all_ok = !__syncthreads_or(!ok);
     if (p.trace && trace_slot >= 0 && blockIdx.x == 0 && threadIdx.x == 0) {
         p.trace[2 * trace_slot] = t_in;
@@ -265,6 +308,9 @@ __device__ __forceinline__ void split(int n, int unit, int &lo, int &hi) {
     hi = static_cast<int>(static_cast<int64_t>(g + 1) * nu / G) * unit;
 }
 
+// NWD / NWF: exchange words per thread of a hidden-size / GLU-size vector (two values each);
+// the launch picks the smallest instance that covers D and F
+template <int NWD, int NWF>
 __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
     __shared__ PState st;
     const int tid = threadIdx.x;
@@ -279,8 +325,8 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
     auto M = [&](int l) { return p.xch + l * lstride + (5 * D) / 2; }; // [F/2]
 
     uint4 w_ifg[kUIfg], w_o[kUO], w_gu[kUGu], w_dn[kUDn], w_hd[kUHd];
-    uint32_t vals[kPMaxWD], mvals[kPMaxW];
-    float hnew[kPMaxWD][2];
+    uint32_t vals[NWD], mvals[NWF];
+    float hnew[NWD][2];
 
     // slices of this workgroup (the same for every layer)
     int ifg0, ifg1, o0, o1, gu0, gu1, dn0, dn1, hd0, hd1;
@@ -302,15 +348,54 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
     auto clear_acc = [&](int nr) {
         for (int v = tid; v < nr; v += kPT) st.racc[v] = 0;
     };
+    // bias values of this thread's epilogue rows (v = 2 tid + e), read before the stage's wait
+    float bp[4];
+    auto bias_ifg = [&](const PLayer &ly) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = 0.0f;
+        if (2 * tid < ifg1 - ifg0) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = ifg0 + 2 * tid + e, seg = r / D;
+                if (ly.b[seg]) bp[e] = ly.b[seg][r % D];
+            }
+        }
+    };
+    auto bias_rows = [&](const float *b, int r0, int nr) {   // o, down
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = 0.0f;
+        if (b && 2 * tid < nr) {
+            bp[0] = b[r0 + 2 * tid];
+            bp[1] = b[r0 + 2 * tid + 1];
+        }
+    };
+    auto bias_gu = [&](const PLayer &ly) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = 0.0f;
+        if (2 * tid < gu1 - gu0) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if (ly.b[4]) bp[e] = ly.b[4][gu0 + 2 * tid + e];
+                if (ly.b[5]) bp[2 + e] = ly.b[5][gu0 + 2 * tid + e];
+            }
+        }
+    };
+    auto bias_head = [&]() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = 0.0f;
+        if (p.head_bias && tid < hd1 - hd0) bp[0] = p.head_bias[hd0 + tid];
+    };
 
     prefetch(slice_ifg(p.layers[0]), w_ifg);
+    stage_vec(p.layers[0].g_x, D, st.gain);
+    bias_ifg(p.layers[0]);
     // ---- embedding: x0 = s_E * q_E[id], rounded to bf16 (every workgroup builds it)
     {
         const int id = p.ids[0];
         const bool idv = id >= 0 && id < p.vocab;
         const uint32_t *er = p.emb + static_cast<int64_t>(idv ? id : 0) * (D / 16);
 #pragma unroll
-        for (int j = 0; j < kPMaxWD; ++j) {
+        for (int j = 0; j < NWD; ++j) {
             const int w = tid + kPT * j;
             if (2 * w < D) {
                 uint32_t pr = 0;
@@ -325,50 +410,57 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
             }
         }
     }
+    wait_vmcnt<0>();   // layer 0 has no wait: land its gain copy here
+    __syncthreads();
 
     for (int l = 0; l < L; ++l) {
         const PLayer &ly = p.layers[l];
         // ================= stage A: i|f|g = BitLinear(x)
-        if (l > 0 && !wait_words(X(l), D / 2, tag, vals, p, 4 * l)) return;
+        if (l > 0 && !wait_words<NWD>(X(l), D / 2, tag, vals, p, 4 * l)) return;
 #pragma unroll
-        for (int j = 0; j < kPMaxWD; ++j) {
+        for (int j = 0; j < NWD; ++j) {
             const int w = tid + kPT * j;
             if (2 * w < D) *reinterpret_cast<uint32_t *>(st.xs + 2 * w) = vals[j];
         }
         clear_acc(ifg1 - ifg0);
-        quantize_words(vals, D, ly.g_x, ly.e_x, st);
+        quantize_words(vals, D, ly.g_x ? st.gain : nullptr, ly.e_x, st);
         {
             const Slice s = slice_ifg(ly);
             dot_slice(s, w_ifg, st.xq, st.racc);
             __syncthreads();
             const float a = st.a;
             const int rs = st.rs;
-            for (int v = 2 * tid; v < s.nr; v += 2 * kPT) {
+            const int v = 2 * tid;
+            if (v < s.nr) {
                 uint32_t pr = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int r = ifg0 + v + e, seg = r / D, n = r % D;
-                    float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[seg] * a);
-                    if (ly.b[seg]) y += ly.b[seg][n];
+                    const int seg = (ifg0 + v + e) / D;
+                    const float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[seg] * a) + bp[e];
                     pr |= static_cast<uint32_t>(f32_to_bf16_bits(y)) << (16 * e);
                 }
                 xch_store(IFG(l) + (ifg0 + v) / 2, pr, tag);
             }
         }
+        // next: o_proj's slice, its gain, the MLGRU step's vectors, o's bias values
         prefetch(slice_o(ly), w_o);
+        stage_vec(ly.g_o, D, st.gain);
+        stage_vec(p.h_state + static_cast<int64_t>(l) * D, D, st.vb[0]);
+        stage_vec(ly.f_bias, D, st.vb[1]);
+        stage_vec(ly.f_lower, D, st.vb[2]);
+        stage_vec(ly.gnorm_w, D, st.vb[3]);
+        bias_rows(ly.b[3], o0, o1 - o0);
 
         // ================= stage B: MLGRU step, g_norm, o_proj + residual
         {
             // thread word w covers channels 2w, 2w+1: i at IFG[w], f at IFG[D/2 + w], g at
-            // IFG[D + w]; the three are waited for as one list of words
-            uint32_t vi[kPMaxWD], vf[kPMaxWD], vg[kPMaxWD];
-            if (!wait_words(IFG(l), D / 2, tag, vi, p, 4 * l + 1)) return;
-            if (!wait_words(IFG(l) + D / 2, D / 2, tag, vf, p)) return;
-            if (!wait_words(IFG(l) + D, D / 2, tag, vg, p)) return;
-            const float *hp = p.h_state + static_cast<int64_t>(l) * D;
+            // IFG[D + w]; the three lists are polled together
+            uint32_t vifg[3 * NWD];
+            if (!wait_words<NWD, 3>(IFG(l), D / 2, tag, vifg, p, 4 * l + 1, D / 2)) return;
+            const uint32_t *vi = vifg, *vf = vifg + NWD, *vg = vifg + 2 * NWD;
             float hsum = 0.f;
 #pragma unroll
-            for (int j = 0; j < kPMaxWD; ++j) {
+            for (int j = 0; j < NWD; ++j) {
                 const int w = tid + kPT * j;
                 hnew[j][0] = hnew[j][1] = 0.f;
                 if (2 * w < D) {
@@ -377,10 +469,10 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
                         const int d = 2 * w + e;
                         const float iv = __uint_as_float(e ? vi[j] & 0xFFFF0000u : vi[j] << 16);
                         const float fv = __uint_as_float(e ? vf[j] & 0xFFFF0000u : vf[j] << 16);
-                        const float fb = ly.f_bias ? ly.f_bias[d] : 0.0f;
-                        const float lb = ly.f_lower ? ly.f_lower[d] : 0.0f;
+                        const float fb = ly.f_bias ? st.vb[1][d] : 0.0f;
+                        const float lb = ly.f_lower ? st.vb[2][d] : 0.0f;
                         const float f = fmaf(1.0f - lb, sigmoidf_(fv + fb), lb);
-                        const float h = f * hp[d] + (1.0f - f) * siluf_(iv);
+                        const float h = f * st.vb[0][d] + (1.0f - f) * siluf_(iv);
                         hnew[j][e] = h;
                         hsum = fmaf(h, h, hsum);
                     }
@@ -390,7 +482,7 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
             const float r = 1.0f / sqrtf(htot * (1.0f / static_cast<float>(D)) + ly.g_eps);
             // g_norm output, materialised in bf16, held as pairs in vals for the quantizer
 #pragma unroll
-            for (int j = 0; j < kPMaxWD; ++j) {
+            for (int j = 0; j < NWD; ++j) {
                 const int w = tid + kPT * j;
                 if (2 * w < D) {
                     float o[2];
@@ -398,7 +490,7 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
                     for (int e = 0; e < 2; ++e) {
                         const int d = 2 * w + e;
                         const float gv = __uint_as_float(e ? vg[j] & 0xFFFF0000u : vg[j] << 16);
-                        const float gw = ly.gnorm_w ? ly.gnorm_w[d] : 1.0f;
+                        const float gw = ly.gnorm_w ? st.vb[3][d] : 1.0f;
                         o[e] = ly.gate_mode == 0 ? hnew[j][e] * r * gw * siluf_(gv) : sigmoidf_(gv) * hnew[j][e];
                     }
                     vals[j] = pack_bf16x2(o[0], o[1]);
@@ -406,20 +498,20 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
             }
         }
         clear_acc(o1 - o0);
-        quantize_words(vals, D, ly.g_o, ly.e_o, st);
+        quantize_words(vals, D, ly.g_o ? st.gain : nullptr, ly.e_o, st);
         {
             const Slice s = slice_o(ly);
             dot_slice(s, w_o, st.xq, st.racc);
             __syncthreads();
             const float a = st.a;
             const int rs = st.rs;
-            for (int v = 2 * tid; v < s.nr; v += 2 * kPT) {
+            const int v = 2 * tid;
+            if (v < s.nr) {
                 uint32_t pr = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int n = o0 + v + e;
-                    float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[3] * a);
-                    if (ly.b[3]) y += ly.b[3][n];
+                    float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[3] * a) + bp[e];
                     y = __uint_as_float(static_cast<uint32_t>(st.xs[n]) << 16) + y;
                     pr |= static_cast<uint32_t>(f32_to_bf16_bits(y)) << (16 * e);
                 }
@@ -427,63 +519,65 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
             }
         }
         prefetch(slice_gu(ly), w_gu);
+        stage_vec(ly.g_gu, D, st.gain);
+        bias_gu(ly);
 
         // ================= stage C: gate|up, SiLU(gate) * up
-        if (!wait_words(Y1(l), D / 2, tag, vals, p, 4 * l + 2)) return;
+        if (!wait_words<NWD>(Y1(l), D / 2, tag, vals, p, 4 * l + 2)) return;
         if (blockIdx.x == 0) {   // every workgroup has read the old state: store the new one
             float *hd = p.h_state + static_cast<int64_t>(l) * D;
 #pragma unroll
-            for (int j = 0; j < kPMaxWD; ++j) {
+            for (int j = 0; j < NWD; ++j) {
                 const int w = tid + kPT * j;
                 if (2 * w < D) *reinterpret_cast<float2 *>(hd + 2 * w) = make_float2(hnew[j][0], hnew[j][1]);
             }
         }
 #pragma unroll
-        for (int j = 0; j < kPMaxWD; ++j) {
+        for (int j = 0; j < NWD; ++j) {
             const int w = tid + kPT * j;
             if (2 * w < D) *reinterpret_cast<uint32_t *>(st.y1s + 2 * w) = vals[j];
         }
         clear_acc(2 * (gu1 - gu0));
-        quantize_words(vals, D, ly.g_gu, ly.e_gu, st);
+        quantize_words(vals, D, ly.g_gu ? st.gain : nullptr, ly.e_gu, st);
         {
             const Slice s = slice_gu(ly);
             dot_slice(s, w_gu, st.xq, st.racc);
             __syncthreads();
             const float a = st.a;
             const int rs = st.rs, np = s.nr / 2;
-            for (int v = 2 * tid; v < np; v += 2 * kPT) {
+            const int v = 2 * tid;
+            if (v < np) {
                 uint32_t pr = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int n = gu0 + v + e;
-                    float yg = static_cast<float>(st.racc[v + e] - rs) * (ly.s[4] * a);
-                    float yu = static_cast<float>(st.racc[np + v + e] - rs) * (ly.s[5] * a);
-                    if (ly.b[4]) yg += ly.b[4][n];
-                    if (ly.b[5]) yu += ly.b[5][n];
+                    const float yg = static_cast<float>(st.racc[v + e] - rs) * (ly.s[4] * a) + bp[e];
+                    const float yu = static_cast<float>(st.racc[np + v + e] - rs) * (ly.s[5] * a) + bp[2 + e];
                     pr |= static_cast<uint32_t>(f32_to_bf16_bits(siluf_(yg) * yu)) << (16 * e);
                 }
                 xch_store(M(l) + (gu0 + v) / 2, pr, tag);
             }
         }
         prefetch(slice_dn(ly), w_dn);
+        stage_vec(ly.g_down, F, st.gain);
+        bias_rows(ly.b[6], dn0, dn1 - dn0);
 
         // ================= stage D: down + residual -> next layer's input
-        if (!wait_words(M(l), F / 2, tag, mvals, p, 4 * l + 3)) return;
+        if (!wait_words<NWF>(M(l), F / 2, tag, mvals, p, 4 * l + 3)) return;
         clear_acc(dn1 - dn0);
-        quantize_words(mvals, F, ly.g_down, ly.e_down, st);
+        quantize_words(mvals, F, ly.g_down ? st.gain : nullptr, ly.e_down, st);
         {
             const Slice s = slice_dn(ly);
             dot_slice(s, w_dn, st.xq, st.racc);
             __syncthreads();
             const float a = st.a;
             const int rs = st.rs;
-            for (int v = 2 * tid; v < s.nr; v += 2 * kPT) {
+            const int v = 2 * tid;
+            if (v < s.nr) {
                 uint32_t pr = 0;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int n = dn0 + v + e;
-                    float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[6] * a);
-                    if (ly.b[6]) y += ly.b[6][n];
+                    float y = static_cast<float>(st.racc[v + e] - rs) * (ly.s[6] * a) + bp[e];
                     y = __uint_as_float(static_cast<uint32_t>(st.y1s[n]) << 16) + y;
                     pr |= static_cast<uint32_t>(f32_to_bf16_bits(y)) << (16 * e);
                 }
@@ -491,24 +585,27 @@ __global__ __launch_bounds__(kPT) void decode_persistent_kernel(PersistArgs p) {
                 if (l == L - 1 && p.y) *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p.y) + dn0 + v) = pr;
             }
         }
-        if (l + 1 < L) prefetch(slice_ifg(p.layers[l + 1]), w_ifg);
-        else prefetch(slice_hd, w_hd);
+        if (l + 1 < L) {
+            prefetch(slice_ifg(p.layers[l + 1]), w_ifg);
+            stage_vec(p.layers[l + 1].g_x, D, st.gain);
+            bias_ifg(p.layers[l + 1]);
+        } else {
+            prefetch(slice_hd, w_hd);
+            stage_vec(p.head_gamma, D, st.gain);
+            bias_head();
+        }
     }
 
     // ================= head: logits = BitLinear(x_L)
     if (p.logits) {
-        if (!wait_words(X(L), D / 2, tag, vals, p, 4 * L)) return;
+        if (!wait_words<NWD>(X(L), D / 2, tag, vals, p, 4 * L)) return;
         clear_acc(hd1 - hd0);
-        quantize_words(vals, D, p.head_gamma, p.head_eps, st);
+        quantize_words(vals, D, p.head_gamma ? st.gain : nullptr, p.head_eps, st);
         dot_slice(slice_hd, w_hd, st.xq, st.racc);
         __syncthreads();
         const float a = st.a;
         const int rs = st.rs;
-        for (int v = tid; v < hd1 - hd0; v += kPT) {
-            float y = static_cast<float>(st.racc[v] - rs) * (p.head_scale * a);
-            if (p.head_bias) y += p.head_bias[hd0 + v];
-            p.logits[hd0 + v] = y;
-        }
+        if (tid < hd1 - hd0) p.logits[hd0 + tid] = static_cast<float>(st.racc[tid] - rs) * (p.head_scale * a) + bp[0];
     }
     if (p.trace && blockIdx.x == 0 && tid == 0) {   // end of this workgroup's work
         p.trace[2 * (4 * L + 1)] = __builtin_amdgcn_s_memrealtime();
@@ -540,18 +637,27 @@ int persist_limits(int *max_units, int *max_words, int *max_k, int *max_d, int *
     return kPT;
 }
 
+namespace {
+using PersistKernel = void (*)(PersistArgs);
+// the instance for hidden size D and GLU size F
+PersistKernel persist_kernel(int D, int F) {
+    if (D <= 2 * kPT * 4 && F <= 2 * kPT * 12) return decode_persistent_kernel<4, 12>;
+    return decode_persistent_kernel<kPMaxWD, kPMaxW>;
+}
+}  // namespace
+
 hipError_t launch_decode_persistent(const PersistArgs &a, int grid, hipStream_t s) {
     timing_begin(FAM_GEMV, s);
     void *args[] = {const_cast<PersistArgs *>(&a)};
-    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(decode_persistent_kernel),
+    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(persist_kernel(a.D, a.F)),
                                                     dim3(grid), dim3(kPT), args, 0, s);
     timing_end(FAM_GEMV, s);
     return e;
 }
 
-int persist_occupancy(int *blocks_per_cu) {
+int persist_occupancy(int D, int F, int *blocks_per_cu) {
     return static_cast<int>(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, reinterpret_cast<const void *>(decode_persistent_kernel), kPT, 0));
+        blocks_per_cu, reinterpret_cast<const void *>(persist_kernel(D, F)), kPT, 0));
 }
 
 }  // namespace mmf

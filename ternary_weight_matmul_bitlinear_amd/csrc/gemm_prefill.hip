@@ -57,43 +57,11 @@ static_assert(NT / 64 * 32 * EP_PITCH * 4 <= STAGES * STAGE_BYTES, "epilogue sta
 __device__ __forceinline__ int swz_a(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz_b(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
-// s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt at maximum)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Barrier without the memory fence of __syncthreads (whose release semantics would wait for
 // every outstanding direct-to-LDS load); ordering of the LDS ring is explicit via vmcnt.
 __device__ __forceinline__ void barrier_nofence() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// One 16-byte-per-lane direct load from global memory into LDS: lane l reads 16 bytes at
-// base + off_l (base wave-uniform, in SGPRs; off_l a 32-bit lane offset) and they land at
-// LDS byte address lds + 16*l (lds wave-uniform, passed in M0).  Issued from inline
-// assembly so that the compiler does not order every later LDS read after it (the ring's
-// ordering is explicit: vmcnt waits and barriers); the instruction has no register result.
-// M0 is saved and restored around it.
-__device__ __forceinline__ void dma16(const void *base_p, uint32_t off, uint32_t lds) {
-    const uint64_t b = reinterpret_cast<uintptr_t>(base_p);
-    // readfirstlane yields a signed int: take each half back to uint32_t before widening,
-    // or a low half with bit 31 set would be sign-extended into the high half
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
-    lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(lds)
-        : "memory");
 }
 
 // Two packed words -> their 32 codes (two B operands).

@@ -886,13 +886,13 @@ DecodeLayout decode_layout(const mmf_stack *s) {
     d.total = d.xch + align_up(static_cast<size_t>(L + 1) * static_cast<size_t>(D / 2 * 5 + F / 2) * 8);
     return d;
 }
-int decode_grid() {
+int decode_grid(const mmf_stack *s) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
     int per_cu = 0;
-    if (persist_occupancy(&per_cu) != 0 || per_cu < 1) return 0;
+    if (persist_occupancy(s->blocks[0].i.K, s->blocks[0].gate.N, &per_cu) != 0 || per_cu < 1) return 0;
     return prop.multiProcessorCount;   // one workgroup per CU
 }
 int check_decode_stack(const mmf_stack *s, int grid, const char *who) {
@@ -907,6 +907,14 @@ int check_decode_stack(const mmf_stack *s, int grid, const char *who) {
     }
     if ((rc = check_linear(s->head, "head"))) return rc;
     if (s->head->K != D) return set_error(MMF_ESHAPE, "%s: head K=%d != D=%d", who, s->head->K, D);
+    // the kernel copies these vectors into LDS with 16-byte direct loads
+    for (int l = 0; l < s->n_layers; ++l) {
+        const mmf_block &b = s->blocks[l];
+        const void *v[7] = {b.i.norm_w, b.o.norm_w, b.gate.norm_w, b.down.norm_w, b.f_bias, b.f_lower, b.gnorm_w};
+        for (const void *q : v)
+            if (q && !aligned16(q)) return set_error(MMF_EALIGN, "%s: layer %d: a gain, forget bias/bound or g_norm weight is not 16-byte aligned", who, l);
+    }
+    if (s->head->norm_w && !aligned16(s->head->norm_w)) return set_error(MMF_EALIGN, "%s: head gain not 16-byte aligned", who);
     int mu, mw, mk, md, mr;
     persist_limits(&mu, &mw, &mk, &md, &mr);
     const int G = grid > 0 ? grid : 1;
@@ -938,8 +946,9 @@ size_t stack_decode_workspace_bytes(const mmf_stack *s) {
 
 int stack_decode_init(const mmf_stack *s, void *ws, size_t ws_bytes, hipStream_t stream) {
     int rc;
+    if (!s || !s->blocks || s->n_layers <= 0) return set_error(MMF_EINVAL, "stack_decode_init: empty stack");
     if ((rc = check_device())) return rc;
-    const int G = decode_grid();
+    const int G = decode_grid(s);
     if (G <= 0) return set_error(MMF_EHIP, "stack_decode_init: no occupancy for the one-launch decode kernel");
     if ((rc = check_decode_stack(s, G, "stack_decode_init"))) return rc;
     const DecodeLayout lay = decode_layout(s);
@@ -985,7 +994,7 @@ int stack_decode_step(const mmf_stack *s, const int32_t *ids, float *h_state, fl
     if (!ws || ws_bytes < lay.total) return set_error(MMF_EWORKSPACE, "stack_decode_step: workspace %zu < %zu", ws ? ws_bytes : 0, lay.total);
     if (!aligned16(ws)) return set_error(MMF_EALIGN, "stack_decode_step: workspace not 16-byte aligned");
     if ((rc = check_device())) return rc;
-    const int G = decode_grid();
+    const int G = decode_grid(s);
     if (G <= 0) return set_error(MMF_EHIP, "stack_decode_step: no occupancy for the one-launch decode kernel");
     if ((rc = check_decode_stack(s, G, "stack_decode_step"))) return rc;
     char *base = static_cast<char *>(ws);

@@ -66,6 +66,38 @@ __device__ __forceinline__ float sigmoidf_(float z) {
 }
 __device__ __forceinline__ float siluf_(float z) { return z * sigmoidf_(z); }
 
+// s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt at maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte-per-lane direct load from global memory into LDS: lane l reads 16 bytes at
+// base + off_l (base wave-uniform, in SGPRs; off_l a 32-bit lane offset) and they land at
+// LDS byte address lds + 16*l (lds wave-uniform, passed in M0).  Issued from inline
+// assembly so that the compiler does not order every later LDS read after it (the caller
+// orders them: vmcnt waits and barriers); the instruction has no register result.
+// M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(const void *base_p, uint32_t off, uint32_t lds) {
+    const uint64_t b = reinterpret_cast<uintptr_t>(base_p);
+    // readfirstlane yields a signed int: take each half back to uint32_t before widening,
+    // or a low half with bit 31 set would be sign-extended into the high half
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+    lds = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(lds)
+        : "memory");
+}
+
 // Wave-wide (64 lanes) reductions through cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -342,7 +374,7 @@ struct PersistArgs {
 int persist_limits(int *max_units, int *max_words, int *max_k, int *max_d, int *max_rows);
 int persist_max_units(int rows, int K);
 void persist_stage_units(int (&u)[5]);   // per-stage unit bounds: i|f|g, o, gate|up, down, head
-int persist_occupancy(int *blocks_per_cu);
+int persist_occupancy(int D, int F, int *blocks_per_cu);
 hipError_t launch_decode_persistent(const PersistArgs &a, int grid, hipStream_t s);
 
 // ---------------------------------------------------------------- launchers

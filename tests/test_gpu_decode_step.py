@@ -44,6 +44,9 @@ CASES = {
     "tiny": dict(w=synth.Workload("tiny-stack", D=256, F=704, B=1, T=1, layers=3, vocab=1000, seed=11),
                  extras=True, steps=4),
     "1.3B": dict(w=synth.WORKLOADS["1.3B-decode"], extras=False, steps=3),
+    # the 2.7B widths: D > 2048 and F > 6144 take the kernel instance sized for D <= 4096
+    "wide": dict(w=synth.Workload("wide-stack", D=2560, F=6912, B=1, T=1, layers=2, vocab=2000, seed=12),
+                 extras=True, steps=2),
 }
 
 

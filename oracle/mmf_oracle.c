@@ -22,6 +22,9 @@
  *   [HL-hgrn]    same page, section "HGRN attention: gated recurrence replaces softmax":
  *                block input -> RMSNorm -> i/f/g projections -> recurrence -> g_norm
  *                (RMSNorm fused with a swish gate) -> o_proj.
+ *   [DC-train]   DataCamp page, section "Replacing MatMul with ternary operations": the
+ *                weights are trained in full precision and ternarized during training;
+ *                section "From optimised GPU to custom FPGA": fused training kernels.
  *
  * Readings where the pages are silent (each is listed with its reason in the design notes):
  *   R1  activations: per-token symmetric absmax int8 in [-127,127]; the RMSNorm factor r
@@ -51,6 +54,12 @@
  *       G[L][D] as an exclusive cumulative softmax over the layers, lb_l[d] =
  *       sum_{j<l} exp(G[j][d]) / sum_j exp(G[j][d]) (layer 0 is unbounded); the forget gate
  *       becomes f = lb + (1 - lb)*sigmoid(f_pre + b_f).
+ *   R14 backward ([DC-train]; the pages do not say how a gradient crosses the quantizers):
+ *       the straight-through estimator -- the activation quantizer passes the gradient of
+ *       its dequantized output x_hat = q*a unchanged to x*gamma*r (the RMS-normalised input
+ *       it approximates), and the ternarizer passes the gradient of W_hat = s_w*T unchanged
+ *       to the latent weights.  Everything else (RMSNorm, the gates, the recurrence,
+ *       g_norm) is differentiated exactly.
  *
  * Floating point: every non-quantizer computation is fp64.  The quantizers (ternarize,
  * activation quant) are defined in fp32 so that both sides take each integer decision in
@@ -355,6 +364,187 @@ int orc_mlgru(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f
     free(f);
     free(c);
     free(h);
+    return 0;
+}
+
+/* ------------------------------------------- B1 BitLinear backward (reading R14)
+ * Forward (O3-O5): y = x_hat W_hat^T + b, x_hat[m,c] = q[m,c]*a[m], W_hat = s_w*T.  With
+ * the straight-through estimator, x_hat stands for u = x*gamma*r (r = (mean_c x^2 +
+ * eps)^(-1/2) per row) and W_hat for the latent weights.  Given dy [m, n]:
+ *   g[m,c]     = sum_n dy[m,n] W_hat[n,c]            gradient at u
+ *   dw[n,c]    = sum_m dy[m,n] x_hat[m,c]            gradient of the latent weights
+ *   db[n]      = sum_m dy[m,n]
+ *   dgamma[c]  = sum_m g[m,c] x[m,c] r[m]
+ *   dx[m,c]    = r gamma_c g[m,c] - x[m,c] r^3 / k * sum_j g[m,j] gamma_j x[m,j]
+ * (u_j = gamma_j x_j r and dr/dx_c = -x_c r^3 / k).  gamma NULL means gamma = 1.  Every
+ * output may be NULL.  fp64.
+ */
+int orc_bitlinear_backward(const float *x, int64_t m, const orc_linear *w, double eps,
+                           const double *dy, double *dx, double *dgamma, double *dw,
+                           double *db) {
+    if (!x || !w || !dy || m < 0 || w->n <= 0 || w->k <= 0) return -1;
+    const int64_t k = w->k, n = w->n;
+    int8_t *q = (int8_t *)malloc((size_t)(m * k + 1));
+    double *a = (double *)malloc(sizeof(double) * (size_t)(m + 1));
+    double *g = (double *)malloc(sizeof(double) * (size_t)(m * k + 1));
+    double *r = (double *)malloc(sizeof(double) * (size_t)(m + 1));
+    if (!q || !a || !g || !r) return -3;
+    orc_act_quant(x, m, k, w->gamma, eps, q, a, NULL);
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < k; ++c) ss += (double)x[row * k + c] * (double)x[row * k + c];
+        r[row] = 1.0 / sqrt(ss / (double)k + eps);
+        for (int64_t c = 0; c < k; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < n; ++j) acc += dy[row * n + j] * (double)w->q[j * k + c];
+            g[row * k + c] = acc * (double)w->scale;
+        }
+    }
+    if (dw) {
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j)
+            for (int64_t c = 0; c < k; ++c) {
+                double acc = 0.0;
+                for (int64_t row = 0; row < m; ++row)
+                    acc += dy[row * n + j] * (double)q[row * k + c] * a[row];
+                dw[j * k + c] = acc;
+            }
+    }
+    if (db)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int64_t row = 0; row < m; ++row) acc += dy[row * n + j];
+            db[j] = acc;
+        }
+    if (dgamma)
+        for (int64_t c = 0; c < k; ++c) {
+            double acc = 0.0;
+            for (int64_t row = 0; row < m; ++row) acc += g[row * k + c] * (double)x[row * k + c] * r[row];
+            dgamma[c] = acc;
+        }
+    if (dx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t row = 0; row < m; ++row) {
+            const float *xr = x + row * k;
+            double dot = 0.0;
+            for (int64_t c = 0; c < k; ++c)
+                dot += g[row * k + c] * (w->gamma ? (double)w->gamma[c] : 1.0) * (double)xr[c];
+            const double r1 = r[row], r3 = r1 * r1 * r1;
+            for (int64_t c = 0; c < k; ++c)
+                dx[row * k + c] = r1 * (w->gamma ? (double)w->gamma[c] : 1.0) * g[row * k + c] -
+                                  (double)xr[c] * r3 / (double)k * dot;
+        }
+    }
+    free(q);
+    free(a);
+    free(g);
+    free(r);
+    return 0;
+}
+
+/* ------------------------------------ B2 MLGRU + output gate backward (reading R14)
+ * Forward: orc_mlgru.  Given dout [B,T,D] (gradient at the gated output) and dh_last [B,D]
+ * (gradient at the final state, or NULL), returns d_ifg [B,T,3D] (gradients of the i | f | g
+ * pre-activations), and, each optional, dh0 [B,D], dgnorm_w [D], df_bias [D].
+ *   gate_mode 0: n = h*rho, rho = (mean_D h^2 + eps)^(-1/2), out = n*w*silu(g):
+ *     dg = dout*n*w*silu'(g);  dn = dout*w*silu(g);  dgnorm_w += dout*n*silu(g);
+ *     dh_out = rho*dn - h*rho^3/D * sum_D(dn*h)
+ *   gate_mode 1: out = sigmoid(g)*h: dg = dout*h*sigmoid'(g);  dh_out = dout*sigmoid(g)
+ *   reverse recurrence, t descending: G_t = dh_out_t + f_{t+1}*G_{t+1} (dh_last joins at the
+ *     last step); dc = (1-f_t)*G_t;  df = (h_{t-1} - c_t)*G_t;  di = dc*silu'(i);
+ *     dz = df*(1-lb)*sigmoid(z)*(1-sigmoid(z)), z = f_pre + b_f (= the f_pre gradient, and
+ *     summed over tokens, df_bias);  dh0 = f_0*G_0.
+ * silu'(z) = sigmoid(z)*(1 + z*(1 - sigmoid(z))).  fp64.
+ */
+int orc_mlgru_backward(const double *ifg, int64_t B, int64_t T, int64_t D, const float *f_bias,
+                       const float *f_lower, const double *h0, const float *gnorm_w, double eps,
+                       int gate_mode, const double *dout, const double *dh_last, double *d_ifg,
+                       double *dh0, double *dgnorm_w, double *df_bias) {
+    if (!ifg || !dout || !d_ifg || B <= 0 || T < 0 || D <= 0 || (gate_mode != 0 && gate_mode != 1))
+        return -1;
+    const int64_t M = B * T;
+    double *f = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *c = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *h = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *dho = (double *)malloc(sizeof(double) * (size_t)(M * D + 1));
+    double *gw_part = (double *)calloc((size_t)(M * D + 1), sizeof(double));
+    if (!f || !c || !h || !dho || !gw_part) return -3;
+    for (int64_t row = 0; row < M; ++row)
+        for (int64_t d = 0; d < D; ++d) {
+            const double *r = ifg + row * 3 * D;
+            double sg = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
+            double lb = f_lower ? (double)f_lower[d] : 0.0;
+            f[row * D + d] = lb + (1.0 - lb) * sg;
+            c[row * D + d] = silu_d(r[d]);
+        }
+    orc_gated_recurrence(f, c, B, T, D, h0, h, NULL);
+    /* output gate backward, token by token */
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < M; ++row) {
+        const double *g = ifg + row * 3 * D + 2 * D, *hr = h + row * D, *dor = dout + row * D;
+        double *dg = d_ifg + row * 3 * D + 2 * D;
+        if (gate_mode == 0) {
+            double ss = 0.0;
+            for (int64_t d = 0; d < D; ++d) ss += hr[d] * hr[d];
+            const double rho = 1.0 / sqrt(ss / (double)D + eps);
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                const double w = gnorm_w ? (double)gnorm_w[d] : 1.0;
+                const double sgm = sigmoid_d(g[d]);
+                const double n = hr[d] * rho;
+                dg[d] = dor[d] * n * w * sgm * (1.0 + g[d] * (1.0 - sgm));
+                gw_part[row * D + d] = dor[d] * n * silu_d(g[d]);
+                const double dn = dor[d] * w * silu_d(g[d]);
+                dho[row * D + d] = dn;   /* finished below */
+                dot += dn * hr[d];
+            }
+            for (int64_t d = 0; d < D; ++d)
+                dho[row * D + d] = rho * dho[row * D + d] - hr[d] * rho * rho * rho / (double)D * dot;
+        } else {
+            for (int64_t d = 0; d < D; ++d) {
+                const double sgm = sigmoid_d(g[d]);
+                dg[d] = dor[d] * hr[d] * sgm * (1.0 - sgm);
+                dho[row * D + d] = dor[d] * sgm;
+            }
+        }
+    }
+    /* reverse recurrence, per (b, d) */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t d = 0; d < D; ++d) {
+            double G = 0.0;
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const int64_t i = (b * T + t) * D + d;
+                G = dho[i] + (t == T - 1 ? (dh_last ? dh_last[b * D + d] : 0.0)
+                                         : f[(b * T + t + 1) * D + d] * G);
+                const double hp = t > 0 ? h[i - D] : (h0 ? h0[b * D + d] : 0.0);
+                const double *r = ifg + (b * T + t) * 3 * D;
+                const double si = sigmoid_d(r[d]);
+                d_ifg[(b * T + t) * 3 * D + d] = (1.0 - f[i]) * G * si * (1.0 + r[d] * (1.0 - si));
+                const double z = r[D + d] + (f_bias ? (double)f_bias[d] : 0.0), sz = sigmoid_d(z);
+                const double lb = f_lower ? (double)f_lower[d] : 0.0;
+                d_ifg[(b * T + t) * 3 * D + D + d] = (hp - c[i]) * G * (1.0 - lb) * sz * (1.0 - sz);
+            }
+            if (dh0) dh0[b * D + d] = T > 0 ? f[(b * T) * D + d] * G : (dh_last ? dh_last[b * D + d] : 0.0);
+        }
+    if (dgnorm_w)
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t row = 0; row < M; ++row) acc += gw_part[row * D + d];
+            dgnorm_w[d] = gate_mode == 0 ? acc : 0.0;
+        }
+    if (df_bias)
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (int64_t row = 0; row < M; ++row) acc += d_ifg[row * 3 * D + D + d];
+            df_bias[d] = acc;
+        }
+    free(f);
+    free(c);
+    free(h);
+    free(dho);
+    free(gw_part);
     return 0;
 }
 

@@ -57,6 +57,9 @@ class Oracle:
         L.orc_gated_recurrence.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.orc_mlgru.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, f64, i32, vp, vp]
         L.orc_hgrn_lower_bounds.argtypes = [vp, i64, i64, vp]
+        L.orc_bitlinear_backward.argtypes = [vp, i64, C.POINTER(OrcLinear), f64, vp, vp, vp, vp, vp]
+        L.orc_mlgru_backward.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, f64, i32, vp, vp, vp,
+                                         vp, vp, vp]
         L.orc_trit_row_bytes.argtypes = [i64]
         L.orc_trit_row_bytes.restype = i64
         L.orc_pack_trits.argtypes = [vp, i64, i64, vp]
@@ -202,6 +205,45 @@ class Oracle:
         if rc:
             raise ValueError(f"orc_mlgru failed ({rc})")
         return out, hl
+
+    # --------------------------------------------------------------- backward
+    def bitlinear_backward(self, x, q, scale, dy, gamma=None, eps: float = 1e-6):
+        """Straight-through BitLinear backward (reading R14).  x [M, K] fp32, q [N, K] int8
+        ternary, dy [M, N].  Returns dict dx [M, K], dgamma [K], dw [N, K], db [N] (fp64)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        dy = np.ascontiguousarray(dy, dtype=np.float64)
+        M, K = x.shape
+        lin = self.linear(q, scale, gamma)
+        N = lin.n
+        out = {"dx": np.empty((M, K)), "dgamma": np.empty(K), "dw": np.empty((N, K)),
+               "db": np.empty(N)}
+        rc = self.lib.orc_bitlinear_backward(_p(x), M, C.byref(lin), eps, _p(dy), _p(out["dx"]),
+                                             _p(out["dgamma"]), _p(out["dw"]), _p(out["db"]))
+        if rc:
+            raise ValueError(f"orc_bitlinear_backward failed ({rc})")
+        return out
+
+    def mlgru_backward(self, ifg, dout, f_bias=None, h0=None, gnorm_w=None, eps: float = 1e-6,
+                       gate_mode: int = 0, f_lower=None, dh_last=None):
+        """MLGRU + output gate backward (reading R14).  ifg [B, T, 3D], dout [B, T, D].
+        Returns dict d_ifg [B, T, 3D], dh0 [B, D], dgnorm_w [D], df_bias [D] (fp64)."""
+        ifg = np.ascontiguousarray(ifg, dtype=np.float64)
+        dout = np.ascontiguousarray(dout, dtype=np.float64)
+        B, T, D3 = ifg.shape
+        D = D3 // 3
+        fb = None if f_bias is None else np.ascontiguousarray(f_bias, dtype=np.float32)
+        gw = None if gnorm_w is None else np.ascontiguousarray(gnorm_w, dtype=np.float32)
+        h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+        lb = None if f_lower is None else np.ascontiguousarray(f_lower, dtype=np.float32)
+        dl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float64)
+        out = {"d_ifg": np.empty((B, T, 3 * D)), "dh0": np.empty((B, D)),
+               "dgnorm_w": np.empty(D), "df_bias": np.empty(D)}
+        rc = self.lib.orc_mlgru_backward(_p(ifg), B, T, D, _p(fb), _p(lb), _p(h0), _p(gw), eps,
+                                         gate_mode, _p(dout), _p(dl), _p(out["d_ifg"]),
+                                         _p(out["dh0"]), _p(out["dgnorm_w"]), _p(out["df_bias"]))
+        if rc:
+            raise ValueError(f"orc_mlgru_backward failed ({rc})")
+        return out
 
     # -------------------------------------------------------------------- GLU
     def glu(self, x, gate, up, down, eps: float = 1e-6, act_bf16: bool = False):

@@ -506,9 +506,114 @@ def pin_round_bf16(orc):
     assert got[5] == round(1e-40 / 2.0**-133) * 2.0**-133
 
 
+# ------------------------------------------------------------------- backward
+# Reading R14 (straight-through estimator): the gradients are those of a smooth surrogate
+# forward in which the quantizers are the identity.  The pins differentiate that surrogate
+# numerically (central differences in fp64), so a mistake in the chain rule (a dropped
+# term, a wrong sign or index, a transposed operand) shows up against the forward alone.
+
+def _fd(fun, v, idx, h=1e-6):
+    """Central difference of scalar fun() with respect to v[idx] (v modified in place)."""
+    old = v[idx]
+    v[idx] = old + h
+    up = fun()
+    v[idx] = old - h
+    dn = fun()
+    v[idx] = old
+    return (up - dn) / (2 * h)
+
+
+def pin_bitlinear_backward_fd(orc):
+    """dx, dgamma, db against central differences of the surrogate y = (x*gamma*r) W_hat^T + b,
+    r = (mean x^2 + eps)^-1/2, written here in numpy; dw against differences of
+    sum dy * (x_hat W^T) in W, x_hat = q_x * a from the (pinned) activation quantizer."""
+    rng = np.random.default_rng(7)
+    M, K, N, eps = 3, 8, 5, 1e-6
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    gamma = (1 + 0.3 * rng.standard_normal(K)).astype(np.float32)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    s = 0.37
+    dy = rng.standard_normal((M, N))
+    got = orc.bitlinear_backward(x, T, s, dy, gamma=gamma, eps=eps)
+    xs, gs, bs = x.astype(np.float64), gamma.astype(np.float64), np.zeros(N)
+    What = s * T.astype(np.float64)
+
+    def loss():
+        r = 1.0 / np.sqrt((xs**2).mean(axis=1, keepdims=True) + eps)
+        return float(np.sum(dy * ((xs * gs * r) @ What.T + bs)))
+
+    for idx in [(0, 0), (1, 3), (2, 7), (0, 5)]:
+        fd = _fd(loss, xs, idx)
+        assert abs(got["dx"][idx] - fd) <= 1e-6 * (1 + abs(fd)), ("dx", idx, got["dx"][idx], fd)
+    for c in [0, 4, 7]:
+        fd = _fd(loss, gs, c)
+        assert abs(got["dgamma"][c] - fd) <= 1e-6 * (1 + abs(fd)), ("dgamma", c, got["dgamma"][c], fd)
+    for j in [0, 4]:
+        fd = _fd(loss, bs, j)
+        assert abs(got["db"][j] - fd) <= 1e-6 * (1 + abs(fd)), ("db", j)
+    q, a, _ = orc.act_quant(x, gamma, eps)
+    xh = q.astype(np.float64) * a[:, None]
+    Wv = What.copy()
+    lw = lambda: float(np.sum(dy * (xh @ Wv.T)))
+    for idx in [(0, 0), (4, 7), (2, 3)]:
+        fd = _fd(lw, Wv, idx)
+        assert abs(got["dw"][idx] - fd) <= 1e-6 * (1 + abs(fd)), ("dw", idx, got["dw"][idx], fd)
+
+
+def pin_mlgru_backward_fd(orc):
+    """d_ifg (i, f, g parts), dh0, dgnorm_w and df_bias against central differences of the
+    (pinned) forward: L = sum dout*out + sum dh_last*h_last, both gate modes, with forget
+    bias, lower bound, g_norm weight, initial and final state gradients."""
+    rng = np.random.default_rng(11)
+    B, T, D, eps = 2, 5, 4, 1e-6
+    for gate_mode in (0, 1):
+        ifg = rng.standard_normal((B, T, 3 * D))
+        fb = (0.5 * rng.standard_normal(D)).astype(np.float32)
+        lb = (0.3 * rng.random(D)).astype(np.float32)
+        gw = (1 + 0.3 * rng.standard_normal(D)).astype(np.float32)
+        h0 = rng.standard_normal((B, D))
+        dout = rng.standard_normal((B, T, D))
+        dl = rng.standard_normal((B, D))
+        got = orc.mlgru_backward(ifg, dout, f_bias=fb, h0=h0, gnorm_w=gw, eps=eps,
+                                 gate_mode=gate_mode, f_lower=lb, dh_last=dl)
+
+        def loss():
+            out, hl = orc.mlgru(ifg, f_bias=fb, h0=h0, gnorm_w=gw, eps=eps,
+                                gate_mode=gate_mode, f_lower=lb)
+            return float(np.sum(dout * out) + np.sum(dl * hl))
+
+        # f_bias and gnorm_w are fp32 inputs of the oracle, so they are differentiated through
+        # exact identities instead (a shift of every f pre-activation of the channel; out is
+        # linear in gnorm_w)
+        for idx in [(0, 0, 1), (1, 4, 2), (0, 2, D + 1), (1, 0, D + 3), (0, 4, 2 * D), (1, 3, 2 * D + 2),
+                    (0, 1, D), (1, 2, 3)]:
+            fd = _fd(loss, ifg, idx)
+            assert abs(got["d_ifg"][idx] - fd) <= 1e-6 * (1 + abs(fd)), (gate_mode, "d_ifg", idx, got["d_ifg"][idx], fd)
+        for idx in [(0, 0), (1, 3)]:
+            fd = _fd(loss, h0, idx)
+            assert abs(got["dh0"][idx] - fd) <= 1e-6 * (1 + abs(fd)), (gate_mode, "dh0", idx)
+        # df_bias: shifting b_f[d] equals shifting every f pre-activation of channel d
+        for d in [0, 2]:
+            def lb_shift(hh, d=d):
+                old = ifg[:, :, D + d].copy()
+                ifg[:, :, D + d] += hh
+                v = loss()
+                ifg[:, :, D + d] = old
+                return v
+            fd = (lb_shift(1e-6) - lb_shift(-1e-6)) / 2e-6
+            assert abs(got["df_bias"][d] - fd) <= 1e-6 * (1 + abs(fd)), (gate_mode, "df_bias", d)
+        if gate_mode == 0:
+            # dgnorm_w: out is linear in gnorm_w[d], so the derivative is sum dout*out/w
+            out, _ = orc.mlgru(ifg, f_bias=fb, h0=h0, gnorm_w=gw, eps=eps, gate_mode=0, f_lower=lb)
+            for d in [1, 3]:
+                ref = float(np.sum(dout[:, :, d] * out[:, :, d]) / float(gw[d]))
+                assert abs(got["dgnorm_w"][d] - ref) <= 1e-9 * (1 + abs(ref)), ("dgnorm_w", d)
+
+
 PINS = [pin_act_quant_hand, pin_ternarize_hand, pin_pack_format, pin_trit_pack_hand,
         pin_trit_invariants, pin_quant_invariants,
         pin_quant_literal_rmsnorm, pin_ternary_invariants, pin_bitlinear_hand,
         pin_bitlinear_brute, pin_recurrence_hand, pin_recurrence_unrolled, pin_mlgru_roles,
         pin_mlgru_limits, pin_output_gate, pin_hgrn_lower_bound_gate, pin_hgrn_lower_bounds, pin_glu_identity, pin_block_residuals,
-        pin_block_causal_and_carry, pin_block_stages, pin_embedding, pin_round_bf16]
+        pin_block_causal_and_carry, pin_block_stages, pin_embedding, pin_round_bf16,
+        pin_bitlinear_backward_fd, pin_mlgru_backward_fd]

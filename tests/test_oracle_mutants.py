@@ -71,6 +71,29 @@ MUTANTS = [
      "int c = 0;"),
     ("trit_digits_reversed", "for (int i = 4; i >= 0; --i) { c[i] = v % 3; v /= 3; }",
      "for (int i = 0; i < 5; ++i) { c[i] = v % 3; v /= 3; }"),
+    ("bwd_dx_drops_norm_term", "(double)xr[c] * r3 / (double)k * dot;", "0.0 * dot;"),
+    ("bwd_dx_r_not_cubed", "const double r1 = r[row], r3 = r1 * r1 * r1;",
+     "const double r1 = r[row], r3 = r1;"),
+    ("bwd_g_transposed", "acc += dy[row * n + j] * (double)w->q[j * k + c];",
+     "acc += dy[row * n + j] * (double)w->q[(c % n) * k + (j % k)];"),
+    ("bwd_dw_without_scale_a", "acc += dy[row * n + j] * (double)q[row * k + c] * a[row];",
+     "acc += dy[row * n + j] * (double)q[row * k + c];"),
+    ("bwd_dgamma_without_r", "acc += g[row * k + c] * (double)x[row * k + c] * r[row];",
+     "acc += g[row * k + c] * (double)x[row * k + c];"),
+    ("bwd_recurrence_same_step_f", ": f[(b * T + t + 1) * D + d] * G);", ": f[(b * T + t) * D + d] * G);"),
+    ("bwd_df_sign", "(hp - c[i]) * G * (1.0 - lb) * sz * (1.0 - sz);",
+     "(c[i] - hp) * G * (1.0 - lb) * sz * (1.0 - sz);"),
+    ("bwd_df_ignores_bound", "(hp - c[i]) * G * (1.0 - lb) * sz * (1.0 - sz);",
+     "(hp - c[i]) * G * sz * (1.0 - sz);"),
+    ("bwd_silu_prime_is_sigmoid", "(1.0 - f[i]) * G * si * (1.0 + r[d] * (1.0 - si));",
+     "(1.0 - f[i]) * G * si;"),
+    ("bwd_gnorm_drops_mean_term",
+     "dho[row * D + d] = rho * dho[row * D + d] - hr[d] * rho * rho * rho / (double)D * dot;",
+     "dho[row * D + d] = rho * dho[row * D + d];"),
+    ("bwd_dh0_without_f", "if (dh0) dh0[b * D + d] = T > 0 ? f[(b * T) * D + d] * G :",
+     "if (dh0) dh0[b * D + d] = T > 0 ? G :"),
+    ("bwd_dh_last_dropped", "G = dho[i] + (t == T - 1 ? (dh_last ? dh_last[b * D + d] : 0.0)",
+     "G = dho[i] + (t == T - 1 ? 0.0"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

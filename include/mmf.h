@@ -337,6 +337,44 @@ int stack_decode_step(const mmf_stack *s, const int32_t *ids, float *h_state, fl
                       void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 int stack_decode_status(const void *ws, hipStream_t stream);
 
+/* ------------------------------------------------------------------ backward
+ * Gradients for training the latent weights.  DataCamp "MatMul-free language models",
+ * section "Replacing MatMul with ternary operations": the weights are trained in full
+ * precision and ternarized during training; section "From optimised GPU to custom FPGA":
+ * fused training kernels.  The pages do not say how a gradient crosses the quantizers; here
+ * it passes straight through both: the activation quantizer's dequantized output q*a stands
+ * for u = x*gamma*r (r = (mean x^2 + eps)^(-1/2)) and W_hat = s_w*T for the latent weights.
+ *
+ * bitlinear_backward: x [m][K] (x_dt, the forward input), dy [m][N] (dy_dt, gradient at the
+ * BitLinear output).  Outputs (fp32, each may be NULL):
+ *   dx [m][K]     = r*gamma*g - x*r^3/K * sum_K(g*gamma*x),  g = s_w * dy T
+ *   dgamma [K]    = sum_m g*x*r       (gradient of w->norm_w; ones when it is NULL)
+ *   dw [N][K]     = sum_m dy[m][n] * q[m][k] * a[m]   (latent weights)
+ *   db [N]        = sum_m dy
+ * g and dw run on bf16 matrix cores with fp32 accumulation: dy is rounded to bf16 (exact
+ * for bf16 dy) and, for dw, the product dy*a is.  dgamma, dw and db are summed with fp32
+ * atomics (the order of the sum varies between runs).  Needs N % 8 == 0, K <= 8192, every
+ * pointer 16-byte aligned.  Workspace: bitlinear_backward_workspace_bytes (q, a, g). */
+size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m);
+int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
+                       const void *dy, mmf_dtype dy_dt, float *dx, float *dgamma, float *dw,
+                       float *db, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* mlgru_backward: the forward's arguments (args->out, h_out, out_dt unused), dout [B][T][D]
+ * (dout_dt, gradient at the gated output), dh_last [B][D] fp32 (gradient at h_T) or NULL.
+ * Outputs (fp32): d_ifg [B][T][3D] gradients of the i | f | g pre-activations; dh0 [B][D],
+ * dgnorm_w [D] (zero in gate mode MMF_GATE_SIGMOID), df_bias [D], each may be NULL:
+ *   gate 0: dg = dout*n*w*silu'(g), dh = rho*dn - h*rho^3/D*sum_D(dn*h), dn = dout*w*silu(g),
+ *           n = h*rho; gate 1: dg = dout*h*sigmoid'(g), dh = dout*sigmoid(g);
+ *   G_t = dh_t + f_{t+1} G_{t+1} (+ dh_last at the last token), di = (1-f_t) G_t silu'(i),
+ *   df_pre = (h_{t-1} - c_t) G_t (1-lb) sigmoid'(f_pre + b_f), dh0 = f_0 G_0.
+ * fp32 throughout; dgnorm_w and df_bias are summed over 16-token chunks with fp32 atomics.
+ * Same shape limits as mlgru_scan.  Workspace: mlgru_backward_workspace_bytes. */
+size_t mlgru_backward_workspace_bytes(int64_t B, int64_t T, int64_t D);
+int mlgru_backward(const mmf_mlgru_args *args, const void *dout, mmf_dtype dout_dt,
+                   const float *dh_last, float *d_ifg, float *dh0, float *dgnorm_w,
+                   float *df_bias, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

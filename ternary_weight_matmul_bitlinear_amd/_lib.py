@@ -93,6 +93,11 @@ SIGNATURES = {
     "stack_decode_init": (C.c_int, [P(mmf_stack), vp, sz, vp]),
     "stack_decode_step": (C.c_int, [P(mmf_stack), vp, vp, vp, vp, vp, sz, vp]),
     "stack_decode_status": (C.c_int, [vp, vp]),
+    "bitlinear_backward_workspace_bytes": (sz, [P(mmf_bitlinear), i64]),
+    "bitlinear_backward": (C.c_int, [P(mmf_bitlinear), vp, C.c_int, i64, vp, C.c_int, vp, vp, vp,
+                                     vp, vp, sz, vp]),
+    "mlgru_backward_workspace_bytes": (sz, [i64, i64, i64]),
+    "mlgru_backward": (C.c_int, [P(mmf_mlgru_args), vp, C.c_int, vp, vp, vp, vp, vp, vp, sz, vp]),
 }
 
 

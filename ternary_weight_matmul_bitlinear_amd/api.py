@@ -287,6 +287,65 @@ def mlgru_scan(ifg: torch.Tensor, f_bias=None, h0=None, gnorm_w=None, eps: float
         return out, h_out
 
 
+def bitlinear_backward(w: TernaryLinear, x: torch.Tensor, dy: torch.Tensor, want_dx: bool = True,
+                       want_dgamma: bool = True, want_dw: bool = True, want_db: bool = True,
+                       stream=None) -> dict:
+    """Straight-through BitLinear backward (bitlinear_backward).  x [m, K] forward input,
+    dy [m, N].  Returns dict of fp32 tensors dx [m, K], dgamma [K], dw [N, K], db [N] (the
+    ones asked for)."""
+    with _on(stream):
+        lib = L.lib()
+        x = x.contiguous()
+        dy = dy.contiguous()
+        m = x.numel() // w.K
+        dev = x.device
+        out = {}
+        if want_dx:
+            out["dx"] = torch.empty((m, w.K), dtype=torch.float32, device=dev)
+        if want_dgamma:
+            out["dgamma"] = torch.empty(w.K, dtype=torch.float32, device=dev)
+        if want_dw:
+            out["dw"] = torch.empty((w.N, w.K), dtype=torch.float32, device=dev)
+        if want_db:
+            out["db"] = torch.empty(w.N, dtype=torch.float32, device=dev)
+        d = w.desc()
+        nb = lib.bitlinear_backward_workspace_bytes(C.byref(d), m)
+        ws = _workspace(nb, dev)
+        L.check("bitlinear_backward",
+                lib.bitlinear_backward(C.byref(d), _ptr(x), _dt(x.dtype), m, _ptr(dy), _dt(dy.dtype),
+                                       _ptr(out.get("dx")), _ptr(out.get("dgamma")), _ptr(out.get("dw")),
+                                       _ptr(out.get("db")), _ptr(ws), nb, _stream()))
+        return out
+
+
+def mlgru_backward(ifg: torch.Tensor, dout: torch.Tensor, f_bias=None, h0=None, gnorm_w=None,
+                   eps: float = 1e-6, gate_mode: int = 0, f_lower=None, dh_last=None,
+                   stream=None) -> dict:
+    """MLGRU + output gate backward (mlgru_backward).  ifg [B, T, 3D], dout [B, T, D].
+    Returns dict of fp32 tensors d_ifg [B, T, 3D], dh0 [B, D], dgnorm_w [D], df_bias [D]."""
+    with _on(stream):
+        lib = L.lib()
+        ifg = ifg.contiguous()
+        dout = dout.contiguous()
+        B, T, D3 = ifg.shape
+        D = D3 // 3
+        dev = ifg.device
+        out = {"d_ifg": torch.empty((B, T, D3), dtype=torch.float32, device=dev),
+               "dh0": torch.empty((B, D), dtype=torch.float32, device=dev),
+               "dgnorm_w": torch.empty(D, dtype=torch.float32, device=dev),
+               "df_bias": torch.empty(D, dtype=torch.float32, device=dev)}
+        a = L.mmf_mlgru_args(_ptr(ifg), _dt(ifg.dtype), _ptr(f_bias), _ptr(h0), None,
+                             _ptr(gnorm_w), eps, gate_mode, None, _dt(ifg.dtype), B, T, D,
+                             _ptr(f_lower))
+        nb = lib.mlgru_backward_workspace_bytes(B, T, D)
+        ws = _workspace(nb, dev)
+        L.check("mlgru_backward",
+                lib.mlgru_backward(C.byref(a), _ptr(dout), _dt(dout.dtype), _ptr(dh_last),
+                                   _ptr(out["d_ifg"]), _ptr(out["dh0"]), _ptr(out["dgnorm_w"]),
+                                   _ptr(out["df_bias"]), _ptr(ws), nb, _stream()))
+        return out
+
+
 def glu_forward(gate: TernaryLinear, up: TernaryLinear, down: TernaryLinear, x: torch.Tensor,
                 residual: torch.Tensor | None = None, capture: BlockCapture | None = None,
                 stream=None) -> torch.Tensor:

@@ -86,7 +86,7 @@ static bool g_timing = false;
 static uint32_t g_timing_mask = 0xFFFFFFFFu;  // families that record events while enabled
 static TimingFamily g_fam[FAM_COUNT];
 static const char *kFamNames[FAM_COUNT] = {"quant", "gemm_ifg", "gemm_o", "gemm_gateup",
-                                           "gemm_down", "gemm", "gemv", "scan", "embed"};
+                                           "gemm_down", "gemm", "gemv", "scan", "embed", "bwd_g", "bwd_dw", "bwd_scan"};
 static thread_local hipEvent_t t_pending = nullptr;
 
 void timing_begin(int family, hipStream_t s) {
@@ -1032,6 +1032,157 @@ int stack_decode_status(const void *ws, hipStream_t stream) {
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_error(e, "stack_decode_status");
     if (ctl[2]) return set_error(MMF_EHIP, "stack_decode_step: a stage wait timed out (re-initialise the workspace)");
+    return MMF_OK;
+}
+
+// ------------------------------------------------------------------ backward
+size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m) {
+    if (!w || w->K <= 0 || m <= 0) return 0;
+    const size_t K = static_cast<size_t>(w->K), M = static_cast<size_t>(m);
+    return align_up(M * K) + align_up(M * 4) + align_up(M * 4) + align_up(M * K * 4);
+}
+
+int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
+                       const void *dy, mmf_dtype dy_dt, float *dx, float *dgamma, float *dw,
+                       float *db, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_linear(w, "bitlinear_backward");
+    if (rc) return rc;
+    if (!valid_dt(x_dt) || !valid_dt(dy_dt)) return set_error(MMF_EDTYPE, "bitlinear_backward: dtype %d/%d", x_dt, dy_dt);
+    if (m < 0) return set_error(MMF_ESHAPE, "bitlinear_backward: m=%lld", (long long)m);
+    if (w->N % 8) return set_error(MMF_ESHAPE, "bitlinear_backward: N=%d is not a multiple of 8", w->N);
+    if (w->K > 8192) return set_error(MMF_ESHAPE, "bitlinear_backward: K=%d exceeds 8192", w->K);
+    if (m == 0) {   // every gradient is an empty sum
+        hipError_t e = hipSuccess;
+        if (dgamma) e = launch_fill_zero(dgamma, w->K, stream);
+        if (e == hipSuccess && dw) e = launch_fill_zero(dw, static_cast<int64_t>(w->N) * w->K, stream);
+        if (e == hipSuccess && db) e = launch_fill_zero(db, w->N, stream);
+        return e == hipSuccess ? MMF_OK : hip_error(e, "bitlinear_backward fill");
+    }
+    if (!x || !dy) return set_error(MMF_EINVAL, "bitlinear_backward: NULL x or dy");
+    if (!aligned16(x) || !aligned16(dy) || (dx && !aligned16(dx)) || (dw && !aligned16(dw)) ||
+        (w->norm_w && !aligned16(w->norm_w)))
+        return set_error(MMF_EALIGN, "bitlinear_backward: x/dy/dx/dw/norm_w not 16-byte aligned");
+    const size_t need = bitlinear_backward_workspace_bytes(w, m);
+    if (!ws || ws_bytes < need) return set_error(MMF_EWORKSPACE, "bitlinear_backward: workspace %zu < %zu", ws ? ws_bytes : 0, need);
+    if (!aligned16(ws)) return set_error(MMF_EALIGN, "bitlinear_backward: workspace not 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    Carver c(ws);
+    QBuf qb;
+    qb.q = c.take<int8_t>(static_cast<size_t>(m) * w->K);
+    qb.a = c.take<float>(static_cast<size_t>(m) * 4);
+    qb.rs = c.take<int32_t>(static_cast<size_t>(m) * 4);
+    float *g = c.take<float>(static_cast<size_t>(m) * w->K * 4);
+    hipError_t e = quantize(x, x_dt == MMF_BF16, w->norm_w, w->eps, m, w->K, qb, nullptr, stream);
+    if (e != hipSuccess) return hip_error(e, "bitlinear_backward quant launch");
+    BitlinearBwdArgs a{};
+    a.x = x;
+    a.x_bf16 = x_dt == MMF_BF16;
+    a.gamma = w->norm_w;
+    a.eps = w->eps;
+    a.M = m;
+    a.K = w->K;
+    a.N = w->N;
+    a.packed = w->packed;
+    a.scale = w->scale;
+    a.dy = dy;
+    a.dy_bf16 = dy_dt == MMF_BF16;
+    a.q = qb.q;
+    a.a = qb.a;
+    a.g = g;
+    a.dx = dx;
+    a.dgamma = dgamma;
+    a.dw = dw;
+    a.db = db;
+    e = launch_bitlinear_bwd(a, stream);
+    if (e != hipSuccess) return hip_error(e, "bitlinear_backward launch");
+    return MMF_OK;
+}
+
+size_t mlgru_backward_workspace_bytes(int64_t B, int64_t T, int64_t D) {
+    if (B <= 0 || T <= 0 || D <= 0) return 0;
+    const size_t cn = static_cast<size_t>(B * scan_chunks(T) * D) * 4;
+    return scan_bytes(B, T, D) + align_up(static_cast<size_t>(B * T * D) * 4) + 6 * align_up(cn);
+}
+
+int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt, const float *dh_last,
+                   float *d_ifg, float *dh0, float *dgnorm_w, float *df_bias, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+    if (!a) return set_error(MMF_EINVAL, "mlgru_backward: NULL args");
+    int rc = check_scan_shape(a->B, a->T, a->D, "mlgru_backward");
+    if (rc) return rc;
+    if (!valid_dt(a->ifg_dt) || !valid_dt(dout_dt)) return set_error(MMF_EDTYPE, "mlgru_backward: dtype");
+    if (a->gate_mode != MMF_GATE_SWISH_RMSNORM && a->gate_mode != MMF_GATE_SIGMOID) return set_error(MMF_EINVAL, "mlgru_backward: gate_mode %d", a->gate_mode);
+    if (!(a->eps >= 0.0f)) return set_error(MMF_EINVAL, "mlgru_backward: eps");
+    const int64_t M = a->B * a->T;
+    if (M > 0 && (!a->ifg || !dout || !d_ifg)) return set_error(MMF_EINVAL, "mlgru_backward: NULL ifg, dout or d_ifg");
+    if ((a->h0 && !aligned16(a->h0)) || (a->f_bias && !aligned16(a->f_bias)) ||
+        (a->gnorm_w && !aligned16(a->gnorm_w)) || (a->f_lower && !aligned16(a->f_lower)) ||
+        (M > 0 && (!aligned16(a->ifg) || !aligned16(dout) || !aligned16(d_ifg))))
+        return set_error(MMF_EALIGN, "mlgru_backward: a pointer is not 16-byte aligned");
+    if ((rc = check_device())) return rc;
+    hipError_t e = hipSuccess;
+    if (M == 0) {   // dh0 = dh_last; the parameter gradients are empty sums
+        if (dh0 && a->B > 0) e = launch_copy_state(dh_last, dh0, a->B * a->D, stream);
+        if (e == hipSuccess && dgnorm_w) e = launch_fill_zero(dgnorm_w, a->D, stream);
+        if (e == hipSuccess && df_bias) e = launch_fill_zero(df_bias, a->D, stream);
+        return e == hipSuccess ? MMF_OK : hip_error(e, "mlgru_backward fill");
+    }
+    const size_t need = mlgru_backward_workspace_bytes(a->B, a->T, a->D);
+    if (!ws || ws_bytes < need) return set_error(MMF_EWORKSPACE, "mlgru_backward: workspace %zu < %zu", ws ? ws_bytes : 0, need);
+    if (!aligned16(ws)) return set_error(MMF_EALIGN, "mlgru_backward: workspace not 16-byte aligned");
+    const int32_t nc = static_cast<int32_t>(scan_chunks(a->T));
+    const size_t cn = static_cast<size_t>(a->B * nc * a->D) * 4;
+    Carver c(ws);
+    ScanArgs s{};
+    s.ifg = a->ifg;
+    s.ifg_bf16 = a->ifg_dt == MMF_BF16;
+    s.f_bias = a->f_bias;
+    s.f_lower = a->f_lower;
+    s.h0 = a->h0;
+    s.B = a->B;
+    s.T = a->T;
+    s.D = static_cast<int32_t>(a->D);
+    s.chunk = kScanChunk;
+    s.n_chunks = nc;
+    {
+        Carver sc(c.take<char>(scan_bytes(a->B, a->T, a->D)));
+        if (nc > 1) {
+            s.hloc = sc.take<float>(cn);
+            s.pf = sc.take<float>(cn);
+            s.hin = sc.take<float>(cn);
+        }
+    }
+    MlgruBwdArgs b{};
+    b.ifg = a->ifg;
+    b.ifg_bf16 = s.ifg_bf16;
+    b.f_bias = a->f_bias;
+    b.f_lower = a->f_lower;
+    b.h0 = a->h0;
+    b.gnorm_w = a->gnorm_w;
+    b.eps = a->eps;
+    b.gate_mode = a->gate_mode;
+    b.B = a->B;
+    b.T = a->T;
+    b.D = static_cast<int32_t>(a->D);
+    b.n_chunks = nc;
+    b.hin = s.hin;
+    b.dout = dout;
+    b.dout_bf16 = dout_dt == MMF_BF16;
+    b.dh_last = dh_last;
+    b.d_ifg = d_ifg;
+    b.dh0 = dh0;
+    b.dgnorm_w = dgnorm_w;
+    b.df_bias = df_bias;
+    b.dho = c.take<float>(static_cast<size_t>(M * a->D) * 4);
+    b.cb = c.take<float>(cn);
+    b.cp = c.take<float>(cn);
+    b.cf0 = c.take<float>(cn);
+    b.cg = c.take<float>(cn);
+    b.gw_part = c.take<float>(cn);
+    b.fb_part = c.take<float>(cn);
+    e = launch_scan_carries(s, stream);
+    if (e == hipSuccess) e = launch_mlgru_bwd(b, stream);
+    if (e != hipSuccess) return hip_error(e, "mlgru_backward launch");
     return MMF_OK;
 }
 

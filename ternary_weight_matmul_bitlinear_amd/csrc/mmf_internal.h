@@ -180,6 +180,9 @@ enum Family : int {
     FAM_GEMV,
     FAM_SCAN,
     FAM_EMBED,
+    FAM_BWD_G,      // backward: g = s_w dy T
+    FAM_BWD_DW,     // backward: dW = (dy a)^T q
+    FAM_BWD_SCAN,   // backward: MLGRU + output gate
     FAM_COUNT
 };
 
@@ -377,11 +380,61 @@ void persist_stage_units(int (&u)[5]);   // per-stage unit bounds: i|f|g, o, gat
 int persist_occupancy(int D, int F, int *blocks_per_cu);
 hipError_t launch_decode_persistent(const PersistArgs &a, int grid, hipStream_t s);
 
+// Straight-through BitLinear backward (backward.hip).
+struct BitlinearBwdArgs {
+    const void *x;         // [M][K] forward input
+    int32_t x_bf16;
+    const float *gamma;    // [K] or NULL
+    float eps;
+    int64_t M;
+    int32_t K, N;
+    const uint32_t *packed;  // [N][K/16]
+    float scale;
+    const void *dy;        // [M][N]
+    int32_t dy_bf16;
+    const int8_t *q;       // [M][K] codes of the forward quantizer (workspace)
+    const float *a;        // [M] its dequantization scales (workspace)
+    float *g;              // [M][K] fp32 gradient at the normalised input (workspace)
+    float *dx;             // [M][K] or NULL
+    float *dgamma;         // [K] or NULL
+    float *dw;             // [N][K] or NULL
+    float *db;             // [N] or NULL
+};
+
+// MLGRU + output gate backward (backward.hip).
+struct MlgruBwdArgs {
+    const void *ifg;       // [B][T][3D]
+    int32_t ifg_bf16;
+    const float *f_bias, *f_lower, *h0, *gnorm_w;
+    float eps;
+    int32_t gate_mode;
+    int64_t B, T;
+    int32_t D;
+    int32_t n_chunks;      // chunks of 16 tokens
+    const float *hin;      // [B][n_chunks][D] state entering each chunk (chunk 0: h0)
+    const void *dout;      // [B][T][D]
+    int32_t dout_bf16;
+    const float *dh_last;  // [B][D] or NULL
+    float *d_ifg;          // [B][T][3D]
+    float *dh0;            // [B][D] or NULL
+    float *dgnorm_w;       // [D] or NULL
+    float *df_bias;        // [D] or NULL
+    // workspace
+    float *dho;            // [B][T][D] gradient at h from the output gate
+    float *cb, *cp, *cf0, *cg;  // [B][n_chunks][D] per-chunk scan values
+    float *gw_part, *fb_part;   // [B][n_chunks][D] per-chunk partial sums
+};
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// phases 1 and 2 of the scan only: the state entering every chunk into a.hin (n_chunks > 1)
+hipError_t launch_scan_carries(const ScanArgs &a, hipStream_t s);
+hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s);
+hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);

@@ -1008,9 +1008,8 @@ void launch_out(const ScanArgs &a, dim3 grid, hipStream_t s) {
 }
 }  // namespace
 
-hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+hipError_t launch_scan_carries(const ScanArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.T <= 0) return hipSuccess;
-    timing_begin(FAM_SCAN, s);
     if (a.n_chunks > 1) {
         if (a.chunk == kScanChunk && a.D % 64 == 0) {
             // row layout: 4 channels per thread (8-byte bf16 or 16-byte fp32 loads; with 8 per
@@ -1032,6 +1031,13 @@ hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
             hipLaunchKernelGGL(scan_carry_kernel, g2, dim3(256), 0, s, a);
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s) {
+    if (a.B <= 0 || a.T <= 0) return hipSuccess;
+    timing_begin(FAM_SCAN, s);
+    launch_scan_carries(a, s);
     const dim3 g3(static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(a.B));
     if (a.ifg_bf16) launch_out<true>(a, g3, s);
     else launch_out<false>(a, g3, s);

@@ -261,3 +261,35 @@ def test_lower_bound_trit_and_noalloc_validation_codes(lib):
     assert lib.block_workspace_bytes(C.byref(big), 1, 4096) > lib.block_scratch_bytes()
     assert lib.block_forward_noalloc(C.byref(big), FAKE, 1, 1, 4096, None, FAKE, None) == -5
     assert lib.block_forward_noalloc(C.byref(big), FAKE, 1, 0, 4096, None, FAKE, None) == 0
+
+
+def test_backward_validation_codes(lib):
+    f = lib.bitlinear_backward
+    args = lambda w, x=FAKE, xdt=0, m=4, dy=FAKE, dydt=0, ws=FAKE, nb=1 << 24: (
+        C.byref(w) if w is not None else None, x, xdt, m, dy, dydt, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    assert f(*args(None)) == -1
+    assert f(*args(_bl(K=100))) == -2
+    assert f(*args(_bl(256, 100))) == -2                 # N % 8
+    assert f(*args(_bl(8256, 64))) == -2                 # K > 8192
+    assert f(*args(_bl(), xdt=7)) == -4
+    assert f(*args(_bl(), x=FAKE + 8)) == -3
+    assert f(*args(_bl(), dy=None)) == -1
+    assert f(*args(_bl(), m=-1)) == -2
+    need = lib.bitlinear_backward_workspace_bytes(C.byref(_bl()), 4)
+    assert need >= 4 * 256 * 5
+    assert f(*args(_bl(), nb=need - 1)) == -5
+    # m == 0 with no outputs asked for needs no device
+    assert f(C.byref(_bl()), None, 0, 0, None, 0, None, None, None, None, None, 0, None) == 0
+    g = lib.mlgru_backward
+    a = L.mmf_mlgru_args(FAKE, 0, None, None, None, None, 1e-6, 0, None, 0, 2, 64, 100)
+    assert g(C.byref(a), FAKE, 0, None, FAKE, None, None, None, FAKE, 1 << 24, None) == -2
+    a.D = 256
+    a.gate_mode = 4
+    assert g(C.byref(a), FAKE, 0, None, FAKE, None, None, None, FAKE, 1 << 24, None) == -1
+    a.gate_mode = 0
+    assert g(C.byref(a), FAKE, 9, None, FAKE, None, None, None, FAKE, 1 << 24, None) == -4
+    assert g(C.byref(a), None, 0, None, FAKE, None, None, None, FAKE, 1 << 24, None) == -1
+    a.h0 = FAKE + 4
+    assert g(C.byref(a), FAKE, 0, None, FAKE, None, None, None, FAKE, 1 << 24, None) == -3
+    a.h0 = None
+    assert lib.mlgru_backward_workspace_bytes(2, 64, 256) > lib.mlgru_workspace_bytes(2, 64, 256)

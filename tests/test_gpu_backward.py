@@ -1,0 +1,188 @@
+"""Straight-through BitLinear backward and MLGRU + output-gate backward on the GPU against the
+oracle (reading R14).
+
+BitLinear: every output is compared element by element with a bound derived from the
+kernel's arithmetic: the contractions run on bf16 matrix cores with fp32 accumulation, so
+an output is a sum of n terms each rounded once to bf16 (relative 2^-9: dy when it is fp32,
+dy*a for dW; bf16 dy and the codes are exact) plus n fp32 additions (n*2^-24 relative), all
+relative to the sum of the terms' absolute values (computed here in fp64 from the same
+inputs); dx inherits g's bound through its formula.  The MLGRU backward is fp32 throughout
+and is held to the fp32 tolerance 1e-3 (relative to |ref| + the row's rms)."""
+import numpy as np
+import pytest
+import torch
+
+from ternary_weight_matmul_bitlinear_amd import api, synth
+from tests.gpu_helpers import dev, host, note, rel_check
+
+pytestmark = pytest.mark.gpu
+
+U_BF16 = 2.0**-9
+U_F32 = 2.0**-24
+
+
+def _bl_inputs(seed, M, K, N, x_bf, dy_bf, with_gamma):
+    x = synth.gaussian(seed, (M, K))
+    if x_bf:
+        x = synth.round_to_bf16(x)
+    lat = synth.gaussian(seed + 1, (N, K), 0.02)
+    dy = synth.gaussian(seed + 2, (M, N))
+    if dy_bf:
+        dy = synth.round_to_bf16(dy)
+    gamma = (1.0 + 0.2 * synth.gaussian(seed + 3, (K,))).astype(np.float32) if with_gamma else None
+    return x, lat, dy, gamma
+
+
+def _bounds(orc, x, q, s, dy, gamma, dy_bf, eps=1e-6):
+    """Per-element error bounds of the GPU's g, dx, dgamma, dw, db (fp64)."""
+    M, K = x.shape
+    N = q.shape[0]
+    xs = x.astype(np.float64)
+    ady = np.abs(dy.astype(np.float64))
+    aq = np.abs(q.astype(np.float64))
+    gm = np.ones(K) if gamma is None else gamma.astype(np.float64)
+    eg = (0.0 if dy_bf else U_BF16) + N * U_F32
+    gb = eg * s * (ady @ aq)                         # bound of g
+    r = 1.0 / np.sqrt((xs * xs).mean(axis=1) + eps)
+    g_ref = s * (dy.astype(np.float64) @ q.astype(np.float64))
+    mag = r[:, None] * np.abs(gm) * np.abs(g_ref) + np.abs(xs) * (r**3 / K)[:, None] * np.abs(
+        (g_ref * gm * xs).sum(axis=1))[:, None]
+    dxb = (r[:, None] * np.abs(gm) * gb
+           + np.abs(xs) * (r**3 / K)[:, None] * (gb * np.abs(gm * xs)).sum(axis=1)[:, None]
+           + 1e-5 * mag)
+    dgb = (gb * np.abs(xs) * r[:, None]).sum(axis=0) + M * U_F32 * (np.abs(g_ref * xs) * r[:, None]).sum(axis=0)
+    qx, a, _ = orc.act_quant(x, gamma, eps)
+    dwb = (U_BF16 + 2 * U_F32 + M * U_F32) * ((ady * a[:, None]).T @ np.abs(qx.astype(np.float64)))
+    dbb = M * U_F32 * ady.sum(axis=0) + (0.0 if dy_bf else U_BF16) * ady.sum(axis=0)
+    return {"dx": dxb, "dgamma": dgb, "dw": dwb, "db": dbb}
+
+
+def _bound_check(got, ref, bound, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = np.abs(got - ref)
+    # factor 2 over the bound; the floor covers exact zeros of the reference
+    lim = 2.0 * bound + 1e-30
+    ratio = err / lim
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (f"{what}: err {err[worst]:.3e} > 2 x bound {bound[worst]:.3e} at {worst} "
+                                f"(got {got[worst]:.6e}, ref {ref[worst]:.6e})")
+    return float(ratio.max())
+
+
+BL_CASES = [(1, 64, 8), (37, 128, 40), (300, 704, 256), (257, 1024, 2816), (64, 2816, 1024)]
+
+
+@pytest.mark.parametrize("with_gamma", [True, False], ids=["gamma", "nogamma"])
+@pytest.mark.parametrize("x_bf,dy_bf", [(False, False), (True, True), (True, False)],
+                         ids=["x32-dy32", "x16-dy16", "x16-dy32"])
+@pytest.mark.parametrize("M,K,N", BL_CASES, ids=[f"M{m}K{k}N{n}" for m, k, n in BL_CASES])
+def test_bitlinear_backward_parity(orc, M, K, N, x_bf, dy_bf, with_gamma):
+    note(f"bitlinear_backward M={M} K={K} N={N} x_bf16={x_bf} dy_bf16={dy_bf} gamma={with_gamma}")
+    x, lat, dy, gamma = _bl_inputs(M * 7 + K + N, M, K, N, x_bf, dy_bf, with_gamma)
+    q, s = orc.ternarize(lat)
+    w = api.TernaryLinear.from_ternary(q, s, "cuda", norm_w=gamma)
+    xdt = torch.bfloat16 if x_bf else torch.float32
+    ydt = torch.bfloat16 if dy_bf else torch.float32
+    got = api.bitlinear_backward(w, dev(x, xdt), dev(dy, ydt))
+    torch.cuda.synchronize()
+    ref = orc.bitlinear_backward(x, q, s, dy.astype(np.float64), gamma=gamma)
+    b = _bounds(orc, x, q, s, dy, gamma, dy_bf)
+    for k in ("dx", "dgamma", "dw", "db"):
+        _bound_check(host(got[k]), ref[k], b[k], k)
+
+
+def test_bitlinear_backward_full_size_sampled(orc):
+    """The 370M gate projection at the benchmark's size (16384 tokens, K 1024, N 2816, bf16):
+    dx on sampled rows (rows are independent), dW on sampled entries, db whole."""
+    M, K, N = 16384, 1024, 2816
+    note(f"bitlinear_backward full size M={M} K={K} N={N}")
+    x, lat, dy, gamma = _bl_inputs(4242, M, K, N, True, True, True)
+    q, s = orc.ternarize(lat)
+    w = api.TernaryLinear.from_ternary(q, s, "cuda", norm_w=gamma)
+    got = api.bitlinear_backward(w, dev(x, torch.bfloat16), dev(dy, torch.bfloat16), want_dgamma=False)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 9000, 16382, 16383])
+    ref = orc.bitlinear_backward(x[rows], q, s, dy[rows].astype(np.float64), gamma=gamma)
+    b = _bounds(orc, x[rows], q, s, dy[rows], gamma, True)
+    _bound_check(host(got["dx"])[rows], ref["dx"], b["dx"], "dx rows")
+    qx, a, _ = orc.act_quant(x, gamma)
+    rng = np.random.default_rng(5)
+    ns, ks = rng.integers(0, N, 64), rng.integers(0, K, 64)
+    dws = host(got["dw"])[ns, ks]
+    dyd = dy.astype(np.float64)
+    ref_dw = np.array([np.dot(dyd[:, n] * a, qx[:, k].astype(np.float64)) for n, k in zip(ns, ks)])
+    bnd = np.array([(U_BF16 + (M + 2) * U_F32) * np.dot(np.abs(dyd[:, n]) * a, np.abs(qx[:, k].astype(np.float64)))
+                    for n, k in zip(ns, ks)])
+    _bound_check(dws, ref_dw, bnd, "dw sampled")
+    db_ref = dyd.sum(axis=0)
+    _bound_check(host(got["db"]), db_ref, M * U_F32 * np.abs(dyd).sum(axis=0), "db")
+
+
+def test_bitlinear_backward_empty(orc):
+    """m = 0: the parameter gradients are empty sums (zero)."""
+    q, s = orc.ternarize(synth.gaussian(1, (16, 64), 0.02))
+    w = api.TernaryLinear.from_ternary(q, s, "cuda")
+    got = api.bitlinear_backward(w, torch.empty((0, 64), device="cuda"), torch.empty((0, 16), device="cuda"))
+    torch.cuda.synchronize()
+    for k in ("dgamma", "dw", "db"):
+        assert float(got[k].abs().max()) == 0.0, k
+
+
+MG_CASES = [(1, 1, 64), (1, 16, 128), (2, 37, 256), (2, 200, 1024), (1, 33, 2560), (1, 20, 4096),
+            (8, 2048, 1024)]
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1], ids=["swish_rmsnorm", "sigmoid"])
+@pytest.mark.parametrize("bf", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", MG_CASES, ids=[f"B{b}T{t}D{d}" for b, t, d in MG_CASES])
+def test_mlgru_backward_parity(orc, B, T, D, bf, gate_mode):
+    note(f"mlgru_backward B={B} T={T} D={D} bf16={bf} gate={gate_mode}")
+    seed = B * 1000 + T * 10 + D
+    ifg = synth.gaussian(seed, (B, T, 3 * D), 1.5)
+    dout = synth.gaussian(seed + 1, (B, T, D))
+    if bf:
+        ifg, dout = synth.round_to_bf16(ifg), synth.round_to_bf16(dout)
+    fb = synth.gaussian(seed + 2, (D,), 0.5)
+    h0 = synth.gaussian(seed + 3, (B, D))
+    gw = (1.0 + 0.2 * synth.gaussian(seed + 4, (D,))).astype(np.float32)
+    lb = orc.hgrn_lower_bounds(synth.gaussian(seed + 5, (3, D)))[1].astype(np.float32)
+    dl = synth.gaussian(seed + 6, (B, D))
+    dt = torch.bfloat16 if bf else torch.float32
+    got = api.mlgru_backward(dev(ifg, dt), dev(dout, dt), f_bias=dev(fb), h0=dev(h0), gnorm_w=dev(gw),
+                             gate_mode=gate_mode, f_lower=dev(lb), dh_last=dev(dl))
+    torch.cuda.synchronize()
+    ref = orc.mlgru_backward(ifg.astype(np.float64), dout.astype(np.float64), f_bias=fb, h0=h0,
+                             gnorm_w=gw, gate_mode=gate_mode, f_lower=lb, dh_last=dl)
+    rel_check(host(got["d_ifg"]), ref["d_ifg"], 1e-3, "d_ifg")
+    rel_check(host(got["dh0"]), ref["dh0"], 1e-3, "dh0")
+    rel_check(host(got["df_bias"]), ref["df_bias"], 1e-3, "df_bias")
+    if gate_mode == 0:
+        rel_check(host(got["dgnorm_w"]), ref["dgnorm_w"], 1e-3, "dgnorm_w")
+    else:
+        assert float(got["dgnorm_w"].abs().max()) == 0.0
+
+
+def test_mlgru_backward_no_options(orc):
+    """No forget bias, bound, gain, initial state or final-state gradient (all NULL)."""
+    B, T, D = 2, 50, 256
+    ifg = synth.gaussian(77, (B, T, 3 * D), 1.5)
+    dout = synth.gaussian(78, (B, T, D))
+    got = api.mlgru_backward(dev(ifg), dev(dout))
+    torch.cuda.synchronize()
+    ref = orc.mlgru_backward(ifg.astype(np.float64), dout)
+    rel_check(host(got["d_ifg"]), ref["d_ifg"], 1e-3, "d_ifg")
+    rel_check(host(got["dh0"]), ref["dh0"], 1e-3, "dh0")
+
+
+def test_mlgru_backward_empty(orc):
+    """T = 0: dh0 = dh_last, the parameter gradients are zero."""
+    D = 128
+    dl = synth.gaussian(3, (2, D))
+    got = api.mlgru_backward(torch.empty((2, 0, 3 * D), device="cuda"), torch.empty((2, 0, D), device="cuda"),
+                             dh_last=dev(dl))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got["dh0"]), dl.astype(np.float32).astype(np.float64))
+    assert float(got["df_bias"].abs().max()) == 0.0

@@ -11,7 +11,9 @@ with its launch durations from HIP events recorded on the launch stream during t
 steps; `cpu_baseline` is the CPU oracle timed on a bounded causal sample of the same
 workload.  `extra_workloads` carries the other shapes measured the same way: the 2.7B block
 (16 x 2048 tokens), the 370M block (8 x 2048 tokens) and the 24-layer 1.3B decode stack at
-batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches).
+batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches), then the
+backward kernels (straight-through BitLinear backward on bf16 MFMA, MLGRU backward) at the
+370M and 2.7B block sizes.
 """
 from __future__ import annotations
 
@@ -28,9 +30,11 @@ sys.path.insert(0, ROOT)
 METRIC = "block tokens/s; % peak HBM GB/s (decode), % int8 MFMA util (prefill)"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, tera-ops/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 CSRC = os.path.join(ROOT, "ternary_weight_matmul_bitlinear_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_EXTRAS = "2.7B-block,370M-block,1.3B-decode@1,1.3B-decode@64"
+DEFAULT_BACKWARD = "370M-block,2.7B-block"
 DATA = "synthetic (seeded N(0,1) activations / uniform token ids, ternary weights from N(0,0.02^2) latents)"
 
 
@@ -519,6 +523,89 @@ def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
 
 # ---------------------------------------------------------------------------- main
 
+# ------------------------------------------------------------------ backward
+
+def bench_backward(w, args, orc) -> dict:
+    """Backward of one block-sized training step's two fused kernels at the block workload's
+    size: the straight-through BitLinear backward of the gate projection (K = D, N = F:
+    g = s_w dy T and dW = (dy a)^T q_x on bf16 MFMA, dx with the RMSNorm backward, dgamma,
+    db) and the MLGRU + output-gate backward (B x T x D).  bf16 inputs, fp32 gradients."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api, synth
+
+    M, D, F = w.B * w.T, w.D, w.F
+    lat = synth.layer_latents(w, 0)
+    lin = api.TernaryLinear.from_latent(lat["gate"], "cuda")
+    x = torch.from_numpy(synth.activations(w).reshape(M, D)).to("cuda").to(torch.bfloat16)
+    dy = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 101, (M, F)))).to("cuda").to(torch.bfloat16)
+    ifg = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 102, (w.B, w.T, 3 * D), 1.5))).to("cuda").to(torch.bfloat16)
+    dout = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 103, (w.B, w.T, D)))).to("cuda").to(torch.bfloat16)
+    fb = torch.full((D,), float(w.f_bias or 0.0), device="cuda")
+    gw = torch.ones(D, device="cuda")
+    h0 = torch.zeros((w.B, D), device="cuda")
+
+    def step(_i):
+        api.bitlinear_backward(lin, x, dy)
+        api.mlgru_backward(ifg, dout, f_bias=fb, h0=h0, gnorm_w=gw)
+
+    spin_up(lambda: step(0), args.spin_up)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = args.steps
+    wall, q = timed_events(["bwd_g", "bwd_dw", "bwd_scan"], step, steps)
+    ops = 2.0 * M * F * D
+    scan_bytes = M * D * (4 * 2 + 12.0)   # read i|f|g and dout (bf16), write d_ifg (fp32)
+    kern = {}
+    for fam, (n, ms) in q.items():
+        if not n:
+            continue
+        d = {"launches_per_step": n / steps, "us_per_launch": ms / n * 1e3}
+        sec = ms / n * 1e-3
+        if fam == "bwd_scan":
+            d.update(bound="hbm", algorithmic_bytes=scan_bytes, gbs=scan_bytes / sec / 1e9,
+                     hbm_frac=scan_bytes / sec / 1e9 / PEAK_HBM_GBS)
+        else:
+            d.update(bound="mfma", algorithmic_flops=ops, tflops=ops / sec / 1e12,
+                     mfma_frac=ops / sec / 1e12 / PEAK_BF16_TFLOPS)
+        kern[fam] = d
+    n_g, ms_g = q["bwd_g"]
+    tf = ops / (ms_g / n_g * 1e-3) / 1e12 if n_g else None
+    res = {"workload": f"{w.name} backward", "value": M / (wall * 1e-3), "unit": "tokens/s",
+           "ms_per_step": wall, "steps": steps,
+           "config": {"workload": f"{w.name} backward", "B": w.B, "T": w.T, "D": D, "F": F,
+                      "bitlinear": f"gate projection K={D} N={F}", "inputs": "bf16", "gradients": "fp32"},
+           "roofline": {"kernel": "bwd_g: g = s_w dy T (bf16 MFMA, ternary codes unpacked to bf16)",
+                        "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / PEAK_BF16_TFLOPS if tf else None, "traffic": None,
+                        "algorithmic_flops_per_launch": ops},
+           "kernels": kern}
+    if orc is not None:
+        # oracle on a bounded sample: the BitLinear backward of 32 tokens (every gradient of
+        # that slice) and the MLGRU backward of one 256-token sequence
+        Ms, Ts = 32, min(256, w.T)
+        qg, sg = orc.ternarize(lat["gate"])
+        xs = x[:Ms].float().cpu().numpy()
+        dys = dy[:Ms].float().cpu().numpy().astype(np.float64)
+        t = time.perf_counter()
+        orc.bitlinear_backward(xs, qg, sg, dys)
+        t_bl = time.perf_counter() - t
+        ifs = ifg[:1, :Ts].float().cpu().numpy().astype(np.float64)
+        dos = dout[:1, :Ts].float().cpu().numpy().astype(np.float64)
+        t = time.perf_counter()
+        orc.mlgru_backward(ifs, dos, f_bias=fb.cpu().numpy(), gnorm_w=gw.cpu().numpy())
+        t_mg = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": 1.0 / (t_bl / Ms + t_mg / Ts), "unit": "tokens/s",
+                               **cpu_info(orc), "kind": "oracle",
+                               "sample": f"BitLinear backward of {Ms} tokens ({t_bl:.2f} s) + "
+                                         f"MLGRU backward of 1 x {Ts} tokens ({t_mg:.3f} s), fp64"}
+    log(f"{w.name} backward: {wall:.3f} ms/step; bwd_g {kern.get('bwd_g', {}).get('mfma_frac', 0):.3f} of bf16 peak")
+    del x, dy, ifg, dout
+    return res
+
+
 def run_workload(spec: str, args, orc):
     from ternary_weight_matmul_bitlinear_amd import synth
     name, _, b = spec.partition("@")
@@ -544,6 +631,9 @@ def main() -> int:
     ap.add_argument("--extras", default=DEFAULT_EXTRAS,
                     help="comma-separated workloads measured after the headline ('' for none)")
     ap.add_argument("--no-extras", dest="extras", action="store_const", const="")
+    ap.add_argument("--backward", default=DEFAULT_BACKWARD,
+                    help="block workloads whose backward kernels are measured after the extras "
+                         "('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="block workloads: tokens per sequence of the causal CPU sample "
@@ -591,6 +681,10 @@ def main() -> int:
     extras = list(rest)
     for spec in [s for s in args.extras.split(",") if s and s != args.workload]:
         extras.extend(run_workload(spec, args, orc))
+        torch.cuda.empty_cache()
+    from ternary_weight_matmul_bitlinear_amd import synth as _synth
+    for spec in [s for s in args.backward.split(",") if s]:
+        extras.append(bench_backward(_synth.WORKLOADS[spec], args, orc))
         torch.cuda.empty_cache()
     if args.kernel_sweep:
         from ternary_weight_matmul_bitlinear_amd import synth

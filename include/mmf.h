@@ -354,7 +354,9 @@ int stack_decode_status(const void *ws, hipStream_t stream);
  * g and dw run on bf16 matrix cores with fp32 accumulation: dy is rounded to bf16 (exact
  * for bf16 dy) and, for dw, the product dy*a is.  dgamma, dw and db are summed with fp32
  * atomics (the order of the sum varies between runs).  Needs N % 8 == 0, K <= 8192, every
- * pointer 16-byte aligned.  Workspace: bitlinear_backward_workspace_bytes (q, a, g). */
+ * pointer 16-byte aligned.  Workspace: bitlinear_backward_workspace_bytes (q, a, g, a bf16
+ * copy of the ternary matrix transposed, and bf16 transposes of dy*a and q; about
+ * m*(7K + 2N) + 2KN bytes). */
 size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m);
 int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
                        const void *dy, mmf_dtype dy_dt, float *dx, float *dgamma, float *dw,

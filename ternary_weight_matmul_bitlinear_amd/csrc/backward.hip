@@ -9,12 +9,16 @@
 // approximates), the ternarizer's W_hat = s_w*T to the latent weights.
 //
 // BitLinear (y = x_hat W_hat^T + b), given dy [M][N]:
-//   g  = s_w * dy T          [M][K]   bf16 matrix cores, T's codes unpacked exactly to bf16
-//   dW = (dy*a)^T q_x        [N][K]   bf16 matrix cores, contraction over tokens split
-//                                     over workgroups (fp32 atomics)
+//   g  = s_w * dy T          [M][K]   bf16 matrix cores over n; T is expanded once to a
+//                                     bf16 [K][N] copy (values -1/0/1, exact)
+//   dW = (dy*a)^T q_x        [N][K]   bf16 matrix cores over tokens; (dy*a) and q_x are
+//                                     first transposed to bf16 [.][m] copies, and the
+//                                     token range is split over workgroups (fp32 atomics)
 //   dx = r*gamma*g - x*r^3/K * sum_K(g*gamma*x),  dgamma = sum_M g*x*r,  db = sum_M dy
-// q_x and a are recomputed by the forward quantizer; dy enters the matrix cores rounded to
-// bf16 (exact when dy is bf16), (dy*a) rounded to bf16 for dW; accumulation is fp32.
+// Both contractions are one kernel with the contraction index contiguous in both operands,
+// so its k loop moves only 16-byte vectors.  q_x and a are recomputed by the forward
+// quantizer; dy enters the matrix cores rounded to bf16 (exact when dy is bf16), (dy*a)
+// rounded to bf16 for dW; accumulation is fp32.
 //
 // MLGRU + output gate, given dout [B][T][D] (and dh_T): the forward's chunk carries give
 // the state entering every 16-token chunk, then
@@ -38,8 +42,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int GT = 256;          // threads of a GEMM workgroup (2 x 2 waves)
 constexpr int BR = 128, BS = 128;  // output tile rows x columns
-constexpr int BT = 32;           // contraction step (two 16-deep MFMA steps)
-constexpr int LP = 40;           // LDS pitch of a tile row in bf16 (32 + 8: 80 bytes)
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return f32_to_bf16_bits(v); }
 
@@ -85,109 +87,88 @@ __device__ __forceinline__ void load16(const void *base, int64_t idx, int valid,
     }
 }
 
-// C[r][s] = scale * sum_t A(r, t) B(t, s) on v_mfma_f32_32x32x16_bf16.
-//   MODE 0: g = s_w * dy T: r = token m, s = input column k, t = output row n;
-//           A(m, n) = dy[m][n], B(n, k) = code of T[n][k] - 1 (exact in bf16).
-//   MODE 1: dW = (dy*a)^T q: r = output row n, s = input column k, t = token m;
-//           A(n, m) = bf16(dy[m][n] * a[m]), B(m, k) = q[m][k] (exact in bf16); the token
-//           range is split over blockIdx.z and the partial tiles are added with fp32 atomics
-//           into a zeroed output.
+// C[r][s] = scale * sum_t A[r][t] B[s][t] on v_mfma_f32_32x32x16_bf16, both operands with
+// the contraction index t contiguous: A [R][lda] bf16 (or fp32, rounded to bf16 as it is
+// loaded), B [S][ldb] bf16, rows 16-byte aligned.  When the t range is split over blockIdx.z
+// the partial tiles are added with fp32 atomics into a zeroed C.
 // Tiles of 128 x 128 per workgroup (4 waves, 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks),
-// contraction steps of 32 double-buffered in LDS: the next step's global loads are issued
-// before the current step's MFMAs and written to the other buffer after them.  Operands are
-// stored [row][t] with t contiguous (A) and [column][t] (B), so every MFMA operand is one
-// 16-byte LDS read; transposed loads write 2-byte values along a column of the buffer.
-struct BwdGemmArgs {
-    const void *dy;
-    int32_t dy_bf16;
-    const uint32_t *packed;  // MODE 0: [N][K/16]
-    const int8_t *q;         // MODE 1: [M][K]
-    const float *a;          // MODE 1: [M]
-    int64_t M;
-    int32_t N, K;
+// contraction steps of 64 double-buffered in LDS: the next step's global loads (16-byte
+// vectors, 32 elements of A and of B per thread) are issued before the current step's 8
+// MFMAs per wave and written to the other buffer after them; one barrier per step.  Rows
+// are padded to 72 elements (144 bytes), so every MFMA operand is one 16-byte LDS read.
+struct NtGemmArgs {
+    const void *A;
+    int32_t a_bf16;
+    const uint16_t *B;
+    int64_t R;
+    int32_t S;
+    int64_t T;              // contraction length
+    int64_t lda, ldb;       // row strides in elements
     float scale;
-    float *out;              // MODE 0: [M][K]; MODE 1: [N][K]
-    int32_t t_per_split;     // MODE 1: tokens per blockIdx.z (multiple of BT)
+    float *C;               // [R][S]
+    int64_t t_per_split;    // multiple of BT (T when not split)
+    int32_t atomic;
 };
 
-template <int MODE, bool DYBF16>
-__global__ __launch_bounds__(GT) void bwd_gemm_kernel(BwdGemmArgs p) {
+constexpr int BT = 64;           // contraction step (four 16-deep MFMA steps)
+constexpr int LP = BT + 8;       // LDS pitch of a tile row in bf16 (144 bytes)
+
+// 16 bf16 values of B's row from t on (valid of them; the rest zero)
+__device__ __forceinline__ void load16_bf16(const uint16_t *p, int valid, uint16_t (&o)[16]) {
+    if (valid >= 16) {
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(p), v1 = *reinterpret_cast<const uint4 *>(p + 8);
+        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o[2 * e] = static_cast<uint16_t>(w[e] & 0xFFFFu);
+            o[2 * e + 1] = static_cast<uint16_t>(w[e] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[e] = e < valid ? p[e] : static_cast<uint16_t>(0);
+    }
+}
+
+__device__ __forceinline__ void store16(uint16_t *d, const uint16_t (&v)[16]) {
+    uint4 *q = reinterpret_cast<uint4 *>(d);
+    q[0] = make_uint4(v[0] | (uint32_t(v[1]) << 16), v[2] | (uint32_t(v[3]) << 16),
+                      v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
+    q[1] = make_uint4(v[8] | (uint32_t(v[9]) << 16), v[10] | (uint32_t(v[11]) << 16),
+                      v[12] | (uint32_t(v[13]) << 16), v[14] | (uint32_t(v[15]) << 16));
+}
+
+template <bool ABF16>
+__global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t sa[2][BR * LP];
     __shared__ __attribute__((aligned(16))) uint16_t sb[2][BS * LP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int r32 = lane & 31, g = lane >> 5;
-    const int64_t R = MODE == 0 ? p.M : p.N;
-    const int S = p.K;
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * BR;
     const int s0 = blockIdx.x * BS;
-    int64_t t_begin = 0, t_end = MODE == 0 ? p.N : p.M;
-    if constexpr (MODE == 1) {
-        t_begin = static_cast<int64_t>(blockIdx.z) * p.t_per_split;
-        t_end = t_begin + p.t_per_split < p.M ? t_begin + p.t_per_split : p.M;
-    }
-    const int KW = p.K / 16;
-
-    // staged operands of one contraction step (bf16 bits)
-    uint16_t va[16];
-    uint32_t wb = 0;       // MODE 0: one packed word
-    uint16_t vb[16];       // MODE 1: 16 codes of q
+    const int64_t t_begin = static_cast<int64_t>(blockIdx.z) * p.t_per_split;
+    const int64_t t_end = t_begin + p.t_per_split < p.T ? t_begin + p.t_per_split : p.T;
+    // this thread's rows of the A and B tiles and its 32 t-values of a step
+    const int lr = tid >> 1, lt = 32 * (tid & 1);
+    const int64_t ar = r0 + lr;
+    const int bs = s0 + lr;
+    uint16_t va[2][16], vb[2][16];
     auto load_step = [&](int64_t t0) {
-        if constexpr (MODE == 0) {
-            // A: row m = r0 + tid/2, n = t0 + 16*(tid&1) .. +15
-            const int64_t m = r0 + (tid >> 1);
-            const int64_t n = t0 + 16 * (tid & 1);
-            const int valid = m < p.M ? static_cast<int>(t_end - n < 16 ? (t_end - n > 0 ? t_end - n : 0) : 16) : 0;
-            load16<DYBF16>(p.dy, (m < p.M ? m : 0) * p.N + (valid > 0 ? n : 0), valid, 1.0f, va);
-            // B: row n = t0 + tid/8, word (s0/16 + tid%8): 16 codes along k
-            const int64_t nb = t0 + (tid >> 3);
-            const int kw = s0 / 16 + (tid & 7);
-            wb = nb < t_end && kw < KW ? p.packed[nb * KW + kw] : 0x55555555u;
-        } else {
-            // A: token m = t0 + tid/8, outputs n = r0 + 16*(tid%8) .. +15, times a[m]
-            const int64_t m = t0 + (tid >> 3);
-            const int64_t n = r0 + 16 * (tid & 7);
-            const bool mv = m < t_end;
-            const int valid = mv ? static_cast<int>(p.N - n < 16 ? (p.N - n > 0 ? p.N - n : 0) : 16) : 0;
-            const float am = mv ? p.a[m] : 0.0f;
-            load16<DYBF16>(p.dy, (mv ? m : 0) * p.N + (valid > 0 ? n : 0), valid, am, va);
-            // B: token m, columns k = s0 + 16*(tid%8) .. +15 of q
-            const int k = s0 + 16 * (tid & 7);
-            if (mv && k + 16 <= p.K) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(p.q + m * p.K + k);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    vb[e] = bf16_bits(static_cast<float>(static_cast<int8_t>((w[e / 4] >> (8 * (e % 4))) & 0xFFu)));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) vb[e] = 0;
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int64_t t = t0 + lt + 16 * h;
+            const int64_t rem = t_end - t;
+            const int valid = rem <= 0 ? 0 : (rem < 16 ? static_cast<int>(rem) : 16);
+            load16<ABF16>(p.A, (ar < p.R && valid ? ar * p.lda + t : 0), ar < p.R ? valid : 0, 1.0f, va[h]);
+            load16_bf16(p.B + (bs < p.S && valid ? static_cast<int64_t>(bs) * p.ldb + t : 0),
+                        bs < p.S ? valid : 0, vb[h]);
         }
     };
     auto store_step = [&](int buf) {
-        if constexpr (MODE == 0) {
-            // A row-major: row tid/2, t = 16*(tid&1)
-            uint4 *d = reinterpret_cast<uint4 *>(&sa[buf][(tid >> 1) * LP + 16 * (tid & 1)]);
-            d[0] = make_uint4(va[0] | (uint32_t(va[1]) << 16), va[2] | (uint32_t(va[3]) << 16),
-                              va[4] | (uint32_t(va[5]) << 16), va[6] | (uint32_t(va[7]) << 16));
-            d[1] = make_uint4(va[8] | (uint32_t(va[9]) << 16), va[10] | (uint32_t(va[11]) << 16),
-                              va[12] | (uint32_t(va[13]) << 16), va[14] | (uint32_t(va[15]) << 16));
-            // B transposed: column k = 16*(tid%8) + e, t = tid/8
-            const int t = tid >> 3, kc = 16 * (tid & 7);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int code = static_cast<int>((wb >> (8 * (e % 4) + 2 * (e / 4))) & 3u);
-                sb[buf][(kc + e) * LP + t] = bf16_bits(static_cast<float>(code - 1));
-            }
-        } else {
-            // A transposed: row n = 16*(tid%8) + e, t = tid/8
-            const int t = tid >> 3, nc = 16 * (tid & 7);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sa[buf][(nc + e) * LP + t] = va[e];
-            // B transposed: column k = 16*(tid%8) + e, t = tid/8
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sb[buf][(nc + e) * LP + t] = vb[e];
+        for (int h = 0; h < 2; ++h) {
+            store16(&sa[buf][lr * LP + lt + 16 * h], va[h]);
+            store16(&sb[buf][lr * LP + lt + 16 * h], vb[h]);
         }
     };
 
@@ -209,14 +190,12 @@ __global__ __launch_bounds__(GT) void bwd_gemm_kernel(BwdGemmArgs p) {
         const int buf = st & 1;
         if (st + 1 < nsteps) load_step(t_begin + static_cast<int64_t>(st + 1) * BT);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < BT / 16; ++ks) {
             bf16x8 av[2], bv[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int row = wr * 64 + i * 32 + r32;
-                av[i] = *reinterpret_cast<const bf16x8 *>(&sa[buf][row * LP + 16 * ks + 8 * g]);
-                const int col = wc * 64 + i * 32 + r32;
-                bv[i] = *reinterpret_cast<const bf16x8 *>(&sb[buf][col * LP + 16 * ks + 8 * g]);
+                av[i] = *reinterpret_cast<const bf16x8 *>(&sa[buf][(wr * 64 + i * 32 + r32) * LP + 16 * ks + 8 * g]);
+                bv[i] = *reinterpret_cast<const bf16x8 *>(&sb[buf][(wc * 64 + i * 32 + r32) * LP + 16 * ks + 8 * g]);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -233,17 +212,76 @@ __global__ __launch_bounds__(GT) void bwd_gemm_kernel(BwdGemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = s0 + wc * 64 + j * 32 + r32;
-            if (col >= S) continue;
+            if (col >= p.S) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = r0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (row < R) {
-                    float *o = p.out + row * S + col;
-                    if constexpr (MODE == 0) *o = acc[i][j][e] * p.scale;
-                    else atomicAdd(o, acc[i][j][e] * p.scale);
+                if (row < p.R) {
+                    float *o = p.C + row * p.S + col;
+                    if (p.atomic) atomicAdd(o, acc[i][j][e] * p.scale);
+                    else *o = acc[i][j][e] * p.scale;
                 }
             }
         }
+}
+
+// W^T as bf16 values -1/0/1: out[k][n] for the packed [N][K/16] matrix; thread per (k, 8
+// consecutive n), one 16-byte store (N % 8 == 0).
+__global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, int32_t N, int32_t K,
+                                                        uint16_t *out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int ng = N / 8;
+    if (i >= static_cast<int64_t>(K) * ng) return;
+    const int k = static_cast<int>(i / ng), n0 = static_cast<int>(i % ng) * 8;
+    const int KW = K / 16, sh = 8 * (k % 4) + 2 * ((k % 16) / 4);
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int code = static_cast<int>((packed[static_cast<int64_t>(n0 + e) * KW + k / 16] >> sh) & 3u);
+        v[e] = code == 2 ? 0x3F80u : (code == 0 ? 0xBF80u : 0u);
+    }
+    *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(k) * N + n0) =
+        make_uint4(v[0] | (uint32_t(v[1]) << 16), v[2] | (uint32_t(v[3]) << 16),
+                   v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
+}
+
+// dst[c][m] = bf16(src[m][c] * (scale ? scale[m] : 1)) for m < M, 0 for M <= m < ldm (the
+// padding of every destination row); src bf16, fp32 (SRC 0/1) or int8 codes (SRC 2).
+// 64 x 64 tiles through LDS: rows read and columns written as contiguous runs.
+template <int SRC>
+__global__ __launch_bounds__(256) void transpose_kernel(const void *src, const float *scale, int64_t M,
+                                                        int32_t C, int64_t ldm, uint16_t *dst) {
+    __shared__ float tile[64][65];
+    const int tid = threadIdx.x;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 64;
+    const int c0 = blockIdx.x * 64;
+    {
+        const int r = tid >> 2, cc = 16 * (tid & 3);
+        const int64_t m = m0 + r;
+        const float sc = m < M ? (scale ? scale[m] : 1.0f) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int c = c0 + cc + e;
+            float v = 0.0f;
+            if (m < M && c < C) {
+                const int64_t idx = m * C + c;
+                if constexpr (SRC == 0) v = bf16_bits_to_f32(static_cast<const uint16_t *>(src)[idx]);
+                else if constexpr (SRC == 1) v = static_cast<const float *>(src)[idx];
+                else v = static_cast<float>(static_cast<const int8_t *>(src)[idx]);
+            }
+            tile[r][cc + e] = v * sc;
+        }
+    }
+    __syncthreads();
+    {
+        const int c = c0 + (tid >> 2), mm = 16 * (tid & 3);
+        if (c < C && m0 + mm < ldm) {
+            uint16_t v[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = bf16_bits(tile[mm + e][tid >> 2]);
+            store16(dst + static_cast<int64_t>(c) * ldm + m0 + mm, v);
+        }
+    }
 }
 
 // dx and dgamma from g: workgroup per RPW rows, thread per columns c = tid + 256 j.
@@ -536,23 +574,30 @@ hipError_t launch_col_sum(const void *src, int bf16, int64_t R, int32_t C, float
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    // g = s_w * dy T
-    timing_begin(FAM_BWD_G, s);
+    // g = s_w * dy (W^T)^T: W^T expanded to bf16 once, then the NT GEMM over n
     {
-        BwdGemmArgs g{};
-        g.dy = a.dy;
-        g.dy_bf16 = a.dy_bf16;
-        g.packed = a.packed;
-        g.M = a.M;
-        g.N = a.N;
-        g.K = a.K;
+        const int64_t n = static_cast<int64_t>(a.K) * (a.N / 8);
+        hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                           a.packed, a.N, a.K, a.wt);
+        NtGemmArgs g{};
+        g.A = a.dy;
+        g.a_bf16 = a.dy_bf16;
+        g.B = a.wt;
+        g.R = a.M;
+        g.S = a.K;
+        g.T = a.N;
+        g.lda = a.N;
+        g.ldb = a.N;
         g.scale = a.scale;
-        g.out = a.g;
-        const dim3 grid(static_cast<unsigned>((a.K + BS - 1) / BS), static_cast<unsigned>((a.M + BR - 1) / BR));
-        if (a.dy_bf16) hipLaunchKernelGGL((bwd_gemm_kernel<0, true>), grid, dim3(GT), 0, s, g);
-        else hipLaunchKernelGGL((bwd_gemm_kernel<0, false>), grid, dim3(GT), 0, s, g);
+        g.C = a.g;
+        g.t_per_split = a.N;
+        g.atomic = 0;
+        const dim3 grid(static_cast<unsigned>((a.K + BS - 1) / BS), static_cast<unsigned>((a.M + BR - 1) / BR), 1);
+        timing_begin(FAM_BWD_G, s);
+        if (a.dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
+        else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, g);
+        timing_end(FAM_BWD_G, s);
     }
-    timing_end(FAM_BWD_G, s);
     if (a.dgamma && (e = launch_fill_zero(a.dgamma, a.K, s)) != hipSuccess) return e;
     {
         const dim3 grid(static_cast<unsigned>((a.M + RPW - 1) / RPW));
@@ -560,32 +605,40 @@ hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
         else hipLaunchKernelGGL((bwd_rows_kernel<false>), grid, dim3(256), 0, s, a.x, a.g, a.gamma, a.eps, a.M, a.K, a.dx, a.dgamma);
     }
     if (a.dw) {
+        // dW = (dy a)^T q: both operands transposed to [.][m] bf16 (m padded to ldm with
+        // zeros), then the NT GEMM over m, split over workgroups
+        const dim3 gt1(static_cast<unsigned>((a.N + 63) / 64), static_cast<unsigned>(a.ldm / 64));
+        if (a.dy_bf16) hipLaunchKernelGGL((transpose_kernel<0>), gt1, dim3(256), 0, s, a.dy, a.a, a.M, a.N, a.ldm, a.dyaT);
+        else hipLaunchKernelGGL((transpose_kernel<1>), gt1, dim3(256), 0, s, a.dy, a.a, a.M, a.N, a.ldm, a.dyaT);
+        const dim3 gt2(static_cast<unsigned>((a.K + 63) / 64), static_cast<unsigned>(a.ldm / 64));
+        hipLaunchKernelGGL((transpose_kernel<2>), gt2, dim3(256), 0, s, a.q, nullptr, a.M, a.K, a.ldm, a.qT);
         if ((e = launch_fill_zero(a.dw, static_cast<int64_t>(a.N) * a.K, s)) != hipSuccess) return e;
-        BwdGemmArgs g{};
-        g.dy = a.dy;
-        g.dy_bf16 = a.dy_bf16;
-        g.q = a.q;
-        g.a = a.a;
-        g.M = a.M;
-        g.N = a.N;
-        g.K = a.K;
+        NtGemmArgs g{};
+        g.A = a.dyaT;
+        g.a_bf16 = 1;
+        g.B = a.qT;
+        g.R = a.N;
+        g.S = a.K;
+        g.T = a.ldm;
+        g.lda = a.ldm;
+        g.ldb = a.ldm;
         g.scale = 1.0f;
-        g.out = a.dw;
+        g.C = a.dw;
+        g.atomic = 1;
         const int64_t tiles = static_cast<int64_t>((a.K + BS - 1) / BS) * ((a.N + BR - 1) / BR);
         // split the tokens so that about 1024 workgroups run, each over >= 8 steps
         int64_t splits = (1024 + tiles - 1) / tiles;
-        const int64_t max_splits = (a.M + 8 * BT - 1) / (8 * BT);
+        const int64_t max_splits = (a.ldm + 8 * BT - 1) / (8 * BT);
         if (splits > max_splits) splits = max_splits;
         if (splits < 1) splits = 1;
-        int64_t per = (a.M + splits - 1) / splits;
+        int64_t per = (a.ldm + splits - 1) / splits;
         per = (per + BT - 1) / BT * BT;
-        splits = (a.M + per - 1) / per;
-        g.t_per_split = static_cast<int32_t>(per);
+        splits = (a.ldm + per - 1) / per;
+        g.t_per_split = per;
         const dim3 grid(static_cast<unsigned>((a.K + BS - 1) / BS), static_cast<unsigned>((a.N + BR - 1) / BR),
                         static_cast<unsigned>(splits));
         timing_begin(FAM_BWD_DW, s);
-        if (a.dy_bf16) hipLaunchKernelGGL((bwd_gemm_kernel<1, true>), grid, dim3(GT), 0, s, g);
-        else hipLaunchKernelGGL((bwd_gemm_kernel<1, false>), grid, dim3(GT), 0, s, g);
+        hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
         timing_end(FAM_BWD_DW, s);
     }
     if (a.db) {

@@ -1037,9 +1037,11 @@ int stack_decode_status(const void *ws, hipStream_t stream) {
 
 // ------------------------------------------------------------------ backward
 size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m) {
-    if (!w || w->K <= 0 || m <= 0) return 0;
-    const size_t K = static_cast<size_t>(w->K), M = static_cast<size_t>(m);
-    return align_up(M * K) + align_up(M * 4) + align_up(M * 4) + align_up(M * K * 4);
+    if (!w || w->K <= 0 || w->N <= 0 || m <= 0) return 0;
+    const size_t K = static_cast<size_t>(w->K), N = static_cast<size_t>(w->N), M = static_cast<size_t>(m);
+    const size_t ldm = (M + 63) / 64 * 64;
+    return align_up(M * K) + align_up(M * 4) + align_up(M * 4) + align_up(M * K * 4) +
+           align_up(K * N * 2) + align_up(N * ldm * 2) + align_up(K * ldm * 2);
 }
 
 int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
@@ -1072,6 +1074,10 @@ int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, in
     qb.a = c.take<float>(static_cast<size_t>(m) * 4);
     qb.rs = c.take<int32_t>(static_cast<size_t>(m) * 4);
     float *g = c.take<float>(static_cast<size_t>(m) * w->K * 4);
+    const int64_t ldm = (m + 63) / 64 * 64;
+    uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(w->K) * w->N * 2);
+    uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(w->N) * ldm * 2);
+    uint16_t *qT = c.take<uint16_t>(static_cast<size_t>(w->K) * ldm * 2);
     hipError_t e = quantize(x, x_dt == MMF_BF16, w->norm_w, w->eps, m, w->K, qb, nullptr, stream);
     if (e != hipSuccess) return hip_error(e, "bitlinear_backward quant launch");
     BitlinearBwdArgs a{};
@@ -1089,6 +1095,10 @@ int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, in
     a.q = qb.q;
     a.a = qb.a;
     a.g = g;
+    a.wt = wt;
+    a.ldm = ldm;
+    a.dyaT = dyaT;
+    a.qT = qT;
     a.dx = dx;
     a.dgamma = dgamma;
     a.dw = dw;

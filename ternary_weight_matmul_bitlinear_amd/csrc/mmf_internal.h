@@ -395,6 +395,10 @@ struct BitlinearBwdArgs {
     const int8_t *q;       // [M][K] codes of the forward quantizer (workspace)
     const float *a;        // [M] its dequantization scales (workspace)
     float *g;              // [M][K] fp32 gradient at the normalised input (workspace)
+    uint16_t *wt;          // [K][N] bf16 copy of the ternary matrix, transposed (workspace)
+    int64_t ldm;           // M rounded up to 64: row length of the two copies below
+    uint16_t *dyaT;        // [N][ldm] bf16 (dy * a) transposed (workspace)
+    uint16_t *qT;          // [K][ldm] bf16 q transposed (workspace)
     float *dx;             // [M][K] or NULL
     float *dgamma;         // [K] or NULL
     float *dw;             // [N][K] or NULL

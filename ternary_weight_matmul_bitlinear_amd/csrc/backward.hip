@@ -22,14 +22,17 @@
 //
 // MLGRU + output gate, given dout [B][T][D] (and dh_T): the forward's chunk carries give
 // the state entering every 16-token chunk, then
-//   phase 1 (workgroup per chunk, whole rows of D): rerun the recurrence, the output gate's
-//     backward per token (two row reductions: sum h^2, sum dn*h), dh_out and dg; then the
-//     chunk's reverse scan of G_t = dh_out_t + f_{t+1} G_{t+1} from zero, keeping its value
-//     at the first token, the product of f over the chunk after the first token, and f at
-//     the first token;
-//   phase 2 (thread per channel): carry G backwards across chunks; dh0 = f_0 G_0;
-//   phase 3 (thread per chunk and channel): rerun the chunk forward, then walk it backwards
-//     with the carried G: di = (1-f) G silu'(i), df_pre = (h_{t-1} - c) G (1-lb) sigma'(z).
+//   phase 1 (gate mode 0; workgroup per chunk, whole rows of D): rerun the recurrence and
+//     reduce per token sum h^2 and sum dn*h (dn = dout*w*silu(g)), all 32 sums of a chunk
+//     in one LDS reduction; store rho and rho^3/D * sum dn*h per token;
+//   phase 2 (thread per chunk and channel): rerun the chunk forward, form the gradient at
+//     h from the output gate (dh = rho*dn - h*k3, or dout*sigmoid(g)) and dg, then the
+//     chunk's reverse scan of G_t = dh_t + f_{t+1} G_{t+1} from zero, keeping its value at
+//     the first token, the product of f over the chunk after the first token, and f at the
+//     first token;
+//   phase 3 (thread per channel): carry G backwards across chunks; dh0 = f_0 G_0;
+//   phase 4 (as phase 2): walk the chunk backwards with the carried G:
+//     di = (1-f) G silu'(i), df_pre = (h_{t-1} - c) G (1-lb) sigma'(z).
 // Per-chunk partial sums of dgnorm_w and df_bias are reduced by a column-sum kernel.
 #include "mmf_internal.h"
 
@@ -367,120 +370,101 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
 
 // ------------------------------------------------------------------ MLGRU backward
 constexpr int kBC = 16;           // tokens per chunk (the forward's chunk)
-constexpr int kJD = 16;           // channels per thread in phase 1 (D <= 4096)
 
 __device__ __forceinline__ float silu_grad(float z) {
     const float s = sigmoidf_(z);
     return s * (1.0f + z * (1.0f - s));
 }
 
-// Phase 1: workgroup per (chunk, b), thread per channels d = tid + 256 j.
-template <bool IFGBF16, bool DOBF16>
-__global__ __launch_bounds__(256) void mlgru_bwd_rows_kernel(MlgruBwdArgs p) {
-    __shared__ float red[2][4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Phase 1 (gate mode 0 only): workgroup per (chunk, b); thread per channel quads
+// q = tid + 256 j (channels 4q..4q+3).  Reruns the recurrence over the chunk, keeps per token
+// the thread's partial sums of h^2 and dn*h (dn = dout*w*silu(g)), reduces all 2x16 of them
+// at once through LDS and stores per token rho = (mean h^2 + eps)^(-1/2) and
+// k3 = rho^3/D * sum(dn*h).
+template <bool IFGBF16, bool DOBF16, int JQ>
+__global__ __launch_bounds__(256) void mlgru_bwd_stats_kernel(MlgruBwdArgs p) {
+    __shared__ float red[2 * kBC][257];
+    __shared__ float tot[2 * kBC];
+    const int tid = threadIdx.x;
     const int c = blockIdx.x, b = blockIdx.y;
     const int D = p.D;
     const int64_t t0 = static_cast<int64_t>(c) * kBC;
-    const int64_t t1 = t0 + kBC < p.T ? t0 + kBC : p.T;
-    const int nj = D / 256 + (D % 256 ? 1 : 0);
-    float h[kJD], gw_part[kJD];
+    const int n = static_cast<int>(t0 + kBC < p.T ? kBC : p.T - t0);
     const int64_t crow = static_cast<int64_t>(b) * p.n_chunks + c;
+    float h[JQ][4], fbv[JQ][4], lbv[JQ][4], gwv[JQ][4];
+    float hs[kBC], sd[kBC];
 #pragma unroll
-    for (int j = 0; j < kJD; ++j) {
-        const int d = tid + 256 * j;
-        gw_part[j] = 0.0f;
-        h[j] = 0.0f;
-        if (j < nj && d < D)
-            h[j] = c == 0 ? (p.h0 ? p.h0[static_cast<int64_t>(b) * D + d] : 0.0f) : p.hin[crow * D + d];
-    }
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t row = static_cast<int64_t>(b) * p.T + t;
-        float hs = 0.0f, sd = 0.0f;
-        float dn[kJD];
+    for (int k = 0; k < kBC; ++k) hs[k] = sd[k] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kJD; ++j) {
-            const int d = tid + 256 * j;
-            dn[j] = 0.0f;
-            if (j < nj && d < D) {
-                const float iv = load_act<IFGBF16>(p.ifg, row * 3 * D + d);
-                const float fv = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d);
-                const float lb = p.f_lower ? p.f_lower[d] : 0.0f;
-                const float f = fmaf(1.0f - lb, sigmoidf_(fv + (p.f_bias ? p.f_bias[d] : 0.0f)), lb);
-                h[j] = f * h[j] + (1.0f - f) * siluf_(iv);
-                if (p.gate_mode == 0) {
-                    const float gv = load_act<IFGBF16>(p.ifg, row * 3 * D + 2 * D + d);
-                    const float dov = load_act<DOBF16>(p.dout, row * D + d);
-                    dn[j] = dov * (p.gnorm_w ? p.gnorm_w[d] : 1.0f) * siluf_(gv);
-                    hs = fmaf(h[j], h[j], hs);
-                    sd = fmaf(dn[j], h[j], sd);
-                }
-            }
+    for (int j = 0; j < JQ; ++j) {
+        const int d0 = 4 * (tid + 256 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[j][e] = fbv[j][e] = lbv[j][e] = 0.0f;
+            gwv[j][e] = 1.0f;
         }
-        float rho = 0.0f, k3 = 0.0f;
-        if (p.gate_mode == 0) {
-            hs = wave_sum(hs);
-            sd = wave_sum(sd);
-            if (lane == 0) {
-                red[0][wave] = hs;
-                red[1][wave] = sd;
-            }
-            __syncthreads();
-            hs = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-            sd = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-            __syncthreads();
-            rho = 1.0f / sqrtf(hs / static_cast<float>(D) + p.eps);
-            k3 = rho * rho * rho / static_cast<float>(D) * sd;
-        }
+        if (d0 < D) {
 #pragma unroll
-        for (int j = 0; j < kJD; ++j) {
-            const int d = tid + 256 * j;
-            if (j < nj && d < D) {
-                const float gv = load_act<IFGBF16>(p.ifg, row * 3 * D + 2 * D + d);
-                const float dov = load_act<DOBF16>(p.dout, row * D + d);
-                float dho, dg;
-                if (p.gate_mode == 0) {
-                    const float w = p.gnorm_w ? p.gnorm_w[d] : 1.0f;
-                    const float nrm = h[j] * rho;
-                    dg = dov * nrm * w * silu_grad(gv);
-                    gw_part[j] = fmaf(dov * nrm, siluf_(gv), gw_part[j]);
-                    dho = rho * dn[j] - h[j] * k3;
-                } else {
-                    const float s = sigmoidf_(gv);
-                    dg = dov * h[j] * s * (1.0f - s);
-                    dho = dov * s;
-                }
-                if (t == p.T - 1 && p.dh_last) dho += p.dh_last[static_cast<int64_t>(b) * D + d];
-                p.d_ifg[row * 3 * D + 2 * D + d] = dg;
-                p.dho[row * D + d] = dho;
+            for (int e = 0; e < 4; ++e) {
+                const int d = d0 + e;
+                h[j][e] = c == 0 ? (p.h0 ? p.h0[static_cast<int64_t>(b) * D + d] : 0.0f) : p.hin[crow * D + d];
+                fbv[j][e] = p.f_bias ? p.f_bias[d] : 0.0f;
+                lbv[j][e] = p.f_lower ? p.f_lower[d] : 0.0f;
+                gwv[j][e] = p.gnorm_w ? p.gnorm_w[d] : 1.0f;
             }
         }
     }
-    // the chunk's reverse scan from zero (this thread re-reads its own dh_out values)
 #pragma unroll
-    for (int j = 0; j < kJD; ++j) {
-        const int d = tid + 256 * j;
-        if (j < nj && d < D) {
-            const float lb = p.f_lower ? p.f_lower[d] : 0.0f;
-            const float fb = p.f_bias ? p.f_bias[d] : 0.0f;
-            float G = 0.0f, fnext = 0.0f, prod = 1.0f, f = 0.0f;
-            for (int64_t t = t1 - 1; t >= t0; --t) {
-                const int64_t row = static_cast<int64_t>(b) * p.T + t;
-                G = p.dho[row * D + d] + fnext * G;
-                const float fv = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d);
-                f = fmaf(1.0f - lb, sigmoidf_(fv + fb), lb);
-                if (t > t0) prod *= f;
-                fnext = f;
+    for (int k = 0; k < kBC; ++k) {
+        if (k < n) {
+            const int64_t row = static_cast<int64_t>(b) * p.T + t0 + k;
+#pragma unroll
+            for (int j = 0; j < JQ; ++j) {
+                const int d0 = 4 * (tid + 256 * j);
+                if (d0 < D) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int d = d0 + e;
+                        const float iv = load_act<IFGBF16>(p.ifg, row * 3 * D + d);
+                        const float fv = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d);
+                        const float gv = load_act<IFGBF16>(p.ifg, row * 3 * D + 2 * D + d);
+                        const float dov = load_act<DOBF16>(p.dout, row * D + d);
+                        const float f = fmaf(1.0f - lbv[j][e], sigmoidf_(fv + fbv[j][e]), lbv[j][e]);
+                        h[j][e] = f * h[j][e] + (1.0f - f) * siluf_(iv);
+                        const float dn = dov * gwv[j][e] * siluf_(gv);
+                        hs[k] = fmaf(h[j][e], h[j][e], hs[k]);
+                        sd[k] = fmaf(dn, h[j][e], sd[k]);
+                    }
+                }
             }
-            p.cb[crow * D + d] = G;       // local G at the chunk's first token
-            p.cp[crow * D + d] = prod;    // prod of f over the chunk after its first token
-            p.cf0[crow * D + d] = f;      // f at the chunk's first token
-            p.gw_part[crow * D + d] = gw_part[j];
         }
+    }
+#pragma unroll
+    for (int k = 0; k < kBC; ++k) {
+        red[k][tid] = hs[k];
+        red[kBC + k][tid] = sd[k];
+    }
+    __syncthreads();
+    {   // value v = tid / 8 summed by 8 lanes over 32 partials each, then across the 8 lanes
+        const int v = tid >> 3, part = tid & 7;
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int i = 0; i < 32; ++i) acc += red[v][part * 32 + i];
+        acc += __shfl_xor(acc, 4, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 1, 64);
+        if (part == 0) tot[v] = acc;
+    }
+    __syncthreads();
+    if (tid < n) {
+        const float rho = 1.0f / sqrtf(tot[tid] / static_cast<float>(D) + p.eps);
+        const int64_t row = static_cast<int64_t>(b) * p.T + t0 + tid;
+        p.stats[2 * row] = rho;
+        p.stats[2 * row + 1] = rho * rho * rho / static_cast<float>(D) * tot[kBC + tid];
     }
 }
 
-// Phase 2: thread per (b, d): G entering chunk c from the right (true G at chunk c+1's first
+// Phase 3: thread per (b, d): G entering chunk c from the right (true G at chunk c+1's first
 // token) into cg[c]; dh0 = f_0 * G_0.
 __global__ __launch_bounds__(256) void mlgru_bwd_carry_kernel(MlgruBwdArgs p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -497,10 +481,15 @@ __global__ __launch_bounds__(256) void mlgru_bwd_carry_kernel(MlgruBwdArgs p) {
     if (p.dh0) p.dh0[i] = p.cf0[b * p.n_chunks * D + d] * Gn;
 }
 
-// Phase 3: thread per (b, chunk, d): rerun the chunk forward (state, f, c per token in
-// registers), then walk it backwards with the carried G.
-template <bool IFGBF16>
-__global__ __launch_bounds__(256) void mlgru_bwd_out_kernel(MlgruBwdArgs p) {
+// Phases 2 and 4: thread per (b, chunk, d).  Rerun the chunk forward (state before each
+// token, f, c, i in registers), form the gradient at h from the output gate (gate mode 0
+// with the per-token rho and k3 of phase 1), then walk the chunk backwards:
+//   PASS 0: from zero (G_t = dh_t + f_{t+1} G_{t+1}) -> the chunk's first-token G, the
+//           product of f after the first token, f at the first token; dg and the chunk's
+//           partial sum of the g_norm weight gradient;
+//   PASS 1: from the carried G (phase 3) -> di, df_pre and the chunk's partial sum of df.
+template <bool IFGBF16, bool DOBF16, int PASS>
+__global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int D = p.D;
     if (i >= p.B * p.n_chunks * D) return;
@@ -510,44 +499,75 @@ __global__ __launch_bounds__(256) void mlgru_bwd_out_kernel(MlgruBwdArgs p) {
     const int n = static_cast<int>(t0 + kBC < p.T ? kBC : p.T - t0);
     const float lb = p.f_lower ? p.f_lower[d] : 0.0f;
     const float fb = p.f_bias ? p.f_bias[d] : 0.0f;
-    float hprev[kBC], fz[kBC], cv[kBC], iv[kBC];
+    const float gw = p.gnorm_w ? p.gnorm_w[d] : 1.0f;
+    float hprev[kBC], fz[kBC], iv[kBC], dh[kBC];
     float h = c == 0 ? (p.h0 ? p.h0[b * D + d] : 0.0f) : p.hin[crow * D + d];
+    float gwp = 0.0f;
 #pragma unroll
     for (int k = 0; k < kBC; ++k) {
-        hprev[k] = fz[k] = cv[k] = iv[k] = 0.0f;
+        hprev[k] = fz[k] = iv[k] = dh[k] = 0.0f;
         if (k < n) {
             const int64_t row = b * p.T + t0 + k;
             iv[k] = load_act<IFGBF16>(p.ifg, row * 3 * D + d);
             fz[k] = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d) + fb;
-        }
-    }
-    float fnext = c + 1 < p.n_chunks ? p.cf0[(crow + 1) * D + d] : 0.0f;
-    float G = p.cg[crow * D + d];
-    float dfb = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kBC; ++k) {
-        if (k < n) {
+            const float gv = load_act<IFGBF16>(p.ifg, row * 3 * D + 2 * D + d);
+            const float dov = load_act<DOBF16>(p.dout, row * D + d);
             const float f = fmaf(1.0f - lb, sigmoidf_(fz[k]), lb);
             hprev[k] = h;
-            cv[k] = siluf_(iv[k]);
-            h = f * h + (1.0f - f) * cv[k];
+            h = f * h + (1.0f - f) * siluf_(iv[k]);
+            float dho, dg;
+            if (p.gate_mode == 0) {
+                const float rho = p.stats[2 * row], k3 = p.stats[2 * row + 1];
+                const float nrm = h * rho, sg = siluf_(gv);
+                dho = rho * (dov * gw * sg) - h * k3;
+                dg = dov * nrm * gw * silu_grad(gv);
+                gwp = fmaf(dov * nrm, sg, gwp);
+            } else {
+                const float s = sigmoidf_(gv);
+                dg = dov * h * s * (1.0f - s);
+                dho = dov * s;
+            }
+            if (t0 + k == p.T - 1 && p.dh_last) dho += p.dh_last[b * D + d];
+            dh[k] = dho;
+            if constexpr (PASS == 0) p.d_ifg[row * 3 * D + 2 * D + d] = dg;
         }
     }
+    if constexpr (PASS == 0) {
+        float G = 0.0f, fnext = 0.0f, prod = 1.0f, f = 0.0f;
 #pragma unroll
-    for (int k = kBC - 1; k >= 0; --k) {
-        if (k < n) {
-            const int64_t row = b * p.T + t0 + k;
-            const float sz = sigmoidf_(fz[k]);
-            const float f = fmaf(1.0f - lb, sz, lb);
-            G = p.dho[row * D + d] + fnext * G;
-            p.d_ifg[row * 3 * D + d] = (1.0f - f) * G * silu_grad(iv[k]);
-            const float dz = (hprev[k] - cv[k]) * G * (1.0f - lb) * sz * (1.0f - sz);
-            p.d_ifg[row * 3 * D + D + d] = dz;
-            dfb += dz;
-            fnext = f;
+        for (int k = kBC - 1; k >= 0; --k) {
+            if (k < n) {
+                G = dh[k] + fnext * G;
+                f = fmaf(1.0f - lb, sigmoidf_(fz[k]), lb);
+                if (k > 0) prod *= f;
+                fnext = f;
+            }
         }
+        p.cb[crow * D + d] = G;
+        p.cp[crow * D + d] = prod;
+        p.cf0[crow * D + d] = f;
+        p.gw_part[crow * D + d] = gwp;
+    } else {
+        float fnext = c + 1 < p.n_chunks ? p.cf0[(crow + 1) * D + d] : 0.0f;
+        float G = p.cg[crow * D + d];
+        float dfb = 0.0f;
+#pragma unroll
+        for (int k = kBC - 1; k >= 0; --k) {
+            if (k < n) {
+                const int64_t row = b * p.T + t0 + k;
+                const float sz = sigmoidf_(fz[k]);
+                const float f = fmaf(1.0f - lb, sz, lb);
+                const float cv = siluf_(iv[k]);
+                G = dh[k] + fnext * G;
+                p.d_ifg[row * 3 * D + d] = (1.0f - f) * G * silu_grad(iv[k]);
+                const float dz = (hprev[k] - cv) * G * (1.0f - lb) * sz * (1.0f - sz);
+                p.d_ifg[row * 3 * D + D + d] = dz;
+                dfb += dz;
+                fnext = f;
+            }
+        }
+        p.fb_part[crow * D + d] = dfb;
     }
-    p.fb_part[crow * D + d] = dfb;
 }
 
 }  // namespace
@@ -652,20 +672,32 @@ hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
     hipError_t e;
     timing_begin(FAM_BWD_SCAN, s);
-    const dim3 g1(static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(a.B));
-    if (a.ifg_bf16) {
-        if (a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_rows_kernel<true, true>), g1, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((mlgru_bwd_rows_kernel<true, false>), g1, dim3(256), 0, s, a);
-    } else {
-        if (a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_rows_kernel<false, true>), g1, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((mlgru_bwd_rows_kernel<false, false>), g1, dim3(256), 0, s, a);
+    if (a.gate_mode == 0) {
+        const dim3 g1(static_cast<unsigned>(a.n_chunks), static_cast<unsigned>(a.B));
+        const int jq = (a.D + 1023) / 1024;
+#define MMF_STATS(JQ)                                                                                    \
+        if (a.ifg_bf16 && a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_stats_kernel<true, true, JQ>), g1, dim3(256), 0, s, a); \
+        else if (a.ifg_bf16) hipLaunchKernelGGL((mlgru_bwd_stats_kernel<true, false, JQ>), g1, dim3(256), 0, s, a);         \
+        else if (a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_stats_kernel<false, true, JQ>), g1, dim3(256), 0, s, a);        \
+        else hipLaunchKernelGGL((mlgru_bwd_stats_kernel<false, false, JQ>), g1, dim3(256), 0, s, a);
+        if (jq <= 1) { MMF_STATS(1) }
+        else if (jq == 2) { MMF_STATS(2) }
+        else if (jq == 3) { MMF_STATS(3) }
+        else { MMF_STATS(4) }
+#undef MMF_STATS
     }
-    const int64_t nc = a.B * a.D;
-    hipLaunchKernelGGL(mlgru_bwd_carry_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a);
     const int64_t n3 = a.B * a.n_chunks * a.D;
     const dim3 g3(static_cast<unsigned>((n3 + 255) / 256));
-    if (a.ifg_bf16) hipLaunchKernelGGL((mlgru_bwd_out_kernel<true>), g3, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((mlgru_bwd_out_kernel<false>), g3, dim3(256), 0, s, a);
+#define MMF_CHAN(PASS)                                                                                   \
+    if (a.ifg_bf16 && a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_chan_kernel<true, true, PASS>), g3, dim3(256), 0, s, a); \
+    else if (a.ifg_bf16) hipLaunchKernelGGL((mlgru_bwd_chan_kernel<true, false, PASS>), g3, dim3(256), 0, s, a);         \
+    else if (a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_chan_kernel<false, true, PASS>), g3, dim3(256), 0, s, a);        \
+    else hipLaunchKernelGGL((mlgru_bwd_chan_kernel<false, false, PASS>), g3, dim3(256), 0, s, a);
+    MMF_CHAN(0)
+    const int64_t nc = a.B * a.D;
+    hipLaunchKernelGGL(mlgru_bwd_carry_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a);
+    MMF_CHAN(1)
+#undef MMF_CHAN
     const int64_t R = a.B * a.n_chunks;
     if (a.dgnorm_w) {
         if ((e = launch_fill_zero(a.dgnorm_w, a.D, s)) != hipSuccess) return e;

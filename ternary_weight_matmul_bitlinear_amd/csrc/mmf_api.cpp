@@ -1111,7 +1111,7 @@ int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, in
 size_t mlgru_backward_workspace_bytes(int64_t B, int64_t T, int64_t D) {
     if (B <= 0 || T <= 0 || D <= 0) return 0;
     const size_t cn = static_cast<size_t>(B * scan_chunks(T) * D) * 4;
-    return scan_bytes(B, T, D) + align_up(static_cast<size_t>(B * T * D) * 4) + 6 * align_up(cn);
+    return scan_bytes(B, T, D) + align_up(static_cast<size_t>(B * T) * 8) + 6 * align_up(cn);
 }
 
 int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt, const float *dh_last,
@@ -1183,7 +1183,7 @@ int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt,
     b.dh0 = dh0;
     b.dgnorm_w = dgnorm_w;
     b.df_bias = df_bias;
-    b.dho = c.take<float>(static_cast<size_t>(M * a->D) * 4);
+    b.stats = c.take<float>(static_cast<size_t>(M) * 8);
     b.cb = c.take<float>(cn);
     b.cp = c.take<float>(cn);
     b.cf0 = c.take<float>(cn);

@@ -424,7 +424,7 @@ struct MlgruBwdArgs {
     float *dgnorm_w;       // [D] or NULL
     float *df_bias;        // [D] or NULL
     // workspace
-    float *dho;            // [B][T][D] gradient at h from the output gate
+    float *stats;          // [B][T][2] per token rho and rho^3/D * sum(dn*h) (gate mode 0)
     float *cb, *cp, *cf0, *cg;  // [B][n_chunks][D] per-chunk scan values
     float *gw_part, *fb_part;   // [B][n_chunks][D] per-chunk partial sums
 };

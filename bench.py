@@ -579,7 +579,8 @@ def bench_backward(w, args, orc) -> dict:
                       "bitlinear": f"gate projection K={D} N={F}", "inputs": "bf16", "gradients": "fp32"},
            "roofline": {"kernel": "bwd_g: g = s_w dy T (bf16 MFMA, ternary codes unpacked to bf16)",
                         "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / PEAK_BF16_TFLOPS if tf else None, "traffic": None,
+                        "frac": tf / PEAK_BF16_TFLOPS if tf else None,
+                        "traffic": traffic("bwd_g", f"{w.name}-backward", ("backward.hip",)),
                         "algorithmic_flops_per_launch": ops},
            "kernels": kern}
     if orc is not None:

@@ -94,8 +94,9 @@ __device__ __forceinline__ void load16(const void *base, int64_t idx, int valid,
 // the contraction index t contiguous: A [R][lda] bf16 (or fp32, rounded to bf16 as it is
 // loaded), B [S][ldb] bf16, rows 16-byte aligned.  When the t range is split over blockIdx.z
 // the partial tiles are added with fp32 atomics into a zeroed C.
-// Tiles of 128 x 128 per workgroup (4 waves, 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks),
-// contraction steps of 64 double-buffered in LDS: the next step's global loads (16-byte
+// Tiles of 128 x 128 per workgroup (4 waves, 2 x 2, each 64 x 64 = 2 x 2 MFMA blocks), one
+// workgroup per tile along blockIdx.x (grouped, XCD-aware order below), contraction steps
+// of 64 double-buffered in LDS: the next step's global loads (16-byte
 // vectors, 32 elements of A and of B per thread) are issued before the current step's 8
 // MFMAs per wave and written to the other buffer after them; one barrier per step.  Rows
 // are padded to 72 elements (144 bytes), so every MFMA operand is one 16-byte LDS read.
@@ -147,8 +148,25 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int r32 = lane & 31, g = lane >> 5;
-    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * BR;
-    const int s0 = blockIdx.x * BS;
+    // Tile order: workgroups are dispatched round-robin over the 8 XCDs, so tile ids are
+    // remapped to give each XCD a contiguous run, walked in groups of GM row tiles (column
+    // tile by column tile, the group's row tiles side by side): a column tile's B rows are
+    // read once per group and a row tile's A rows once per column sweep of its group,
+    // instead of B once per row tile.
+    int rt, st;
+    {
+        const int n_rt = static_cast<int>((p.R + BR - 1) / BR), n_st = (p.S + BS - 1) / BS;
+        const int nwg = gridDim.x, bid = blockIdx.x;
+        const int qx = nwg >> 3, rx = nwg & 7, xcd = bid & 7, idx = bid >> 3;
+        const int tile = (xcd < rx ? xcd * (qx + 1) : rx * (qx + 1) + (xcd - rx) * qx) + idx;
+        constexpr int GM = 8;
+        const int grp = tile / (GM * n_st), in_g = tile % (GM * n_st);
+        const int gm = n_rt - grp * GM < GM ? n_rt - grp * GM : GM;
+        rt = grp * GM + in_g % gm;
+        st = in_g / gm;
+    }
+    const int64_t r0 = static_cast<int64_t>(rt) * BR;
+    const int s0 = st * BS;
     const int64_t t_begin = static_cast<int64_t>(blockIdx.z) * p.t_per_split;
     const int64_t t_end = t_begin + p.t_per_split < p.T ? t_begin + p.t_per_split : p.T;
     // this thread's rows of the A and B tiles and its 32 t-values of a step
@@ -612,7 +630,7 @@ hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
         g.C = a.g;
         g.t_per_split = a.N;
         g.atomic = 0;
-        const dim3 grid(static_cast<unsigned>((a.K + BS - 1) / BS), static_cast<unsigned>((a.M + BR - 1) / BR), 1);
+        const dim3 grid(static_cast<unsigned>(((a.K + BS - 1) / BS) * ((a.M + BR - 1) / BR)), 1, 1);
         timing_begin(FAM_BWD_G, s);
         if (a.dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
         else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, g);
@@ -655,8 +673,7 @@ hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
         per = (per + BT - 1) / BT * BT;
         splits = (a.ldm + per - 1) / per;
         g.t_per_split = per;
-        const dim3 grid(static_cast<unsigned>((a.K + BS - 1) / BS), static_cast<unsigned>((a.N + BR - 1) / BR),
-                        static_cast<unsigned>(splits));
+        const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
         timing_begin(FAM_BWD_DW, s);
         hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
         timing_end(FAM_BWD_DW, s);

@@ -146,7 +146,8 @@ def test_decode_stack_1p3b(orc):
                                         np.linalg.norm(xo.reshape(nb, D), axis=1))))
             print(f"B={B} step {s}: independent stack divergence by layer",
                   " ".join(f"{d:.1e}" for d in div), flush=True)
-            assert div[0] <= 2e-2 and max(div) <= 0.5, div
+            # measured: at most 0.12 after 24 layers (batch 1-64, 3 steps); bound at ~2x
+            assert div[0] <= 2e-2 and max(div) <= 0.25, div
 
 
 def test_longctx_stack_2p7b(orc):
@@ -204,4 +205,5 @@ def test_longctx_stack_2p7b(orc):
         g, o = pre_gpu[l + 1].reshape(-1, D), xo.reshape(-1, D)
         div.append(float(np.max(np.linalg.norm(g - o, axis=1) / np.linalg.norm(o, axis=1))))
     print("independent 32-layer divergence by layer", " ".join(f"{d:.1e}" for d in div), flush=True)
-    assert div[0] <= 2e-2 and max(div) <= 0.5, div
+    # measured: 0.095 after 32 layers; bound at ~2x the largest stack divergence measured
+    assert div[0] <= 2e-2 and max(div) <= 0.25, div

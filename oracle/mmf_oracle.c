@@ -471,11 +471,11 @@ int orc_mlgru_backward(const double *ifg, int64_t B, int64_t T, int64_t D, const
     double *gw_part = (double *)calloc((size_t)(M * D + 1), sizeof(double));
     if (!f || !c || !h || !dho || !gw_part) return -3;
     for (int64_t row = 0; row < M; ++row)
-        for (int64_t d = 0; d < D; ++d) {
+        for (int64_t d = 0; d < D; ++d) {   /* the forward's gates (O6), recomputed */
             const double *r = ifg + row * 3 * D;
-            double sg = sigmoid_d(r[D + d] + (f_bias ? (double)f_bias[d] : 0.0));
-            double lb = f_lower ? (double)f_lower[d] : 0.0;
-            f[row * D + d] = lb + (1.0 - lb) * sg;
+            const double zf = r[D + d] + (f_bias ? (double)f_bias[d] : 0.0);
+            const double lbd = f_lower ? (double)f_lower[d] : 0.0;
+            f[row * D + d] = lbd + (1.0 - lbd) * sigmoid_d(zf);
             c[row * D + d] = silu_d(r[d]);
         }
     orc_gated_recurrence(f, c, B, T, D, h0, h, NULL);

@@ -169,27 +169,61 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
     const int s0 = st * BS;
     const int64_t t_begin = static_cast<int64_t>(blockIdx.z) * p.t_per_split;
     const int64_t t_end = t_begin + p.t_per_split < p.T ? t_begin + p.t_per_split : p.T;
-    // this thread's rows of the A and B tiles and its 32 t-values of a step
+    // this thread's rows of the A and B tiles and its 32 t-values of a step, staged as four
+    // 16-byte words (8 bf16 each) per operand
     const int lr = tid >> 1, lt = 32 * (tid & 1);
     const int64_t ar = r0 + lr;
     const int bs = s0 + lr;
-    uint16_t va[2][16], vb[2][16];
+    const bool rows_in = r0 + BR <= p.R && s0 + BS <= p.S;   // uniform over the workgroup
+    uint4 ra[4], rb[4];
+    auto pack8 = [](const uint16_t (&v)[16], int h, uint4 &o) {
+        o = make_uint4(v[8 * h] | (uint32_t(v[8 * h + 1]) << 16), v[8 * h + 2] | (uint32_t(v[8 * h + 3]) << 16),
+                       v[8 * h + 4] | (uint32_t(v[8 * h + 5]) << 16), v[8 * h + 6] | (uint32_t(v[8 * h + 7]) << 16));
+    };
     auto load_step = [&](int64_t t0) {
+        if (rows_in && t0 + BT <= t_end) {
+            // every row and every t of the step in range: unconditional 16-byte loads
+            const uint16_t *pb = p.B + static_cast<int64_t>(bs) * p.ldb + t0 + lt;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rb[q] = *reinterpret_cast<const uint4 *>(pb + 8 * q);
+            if constexpr (ABF16) {
+                const uint16_t *pa = static_cast<const uint16_t *>(p.A) + ar * p.lda + t0 + lt;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const uint4 *>(pa + 8 * q);
+            } else {
+                const float *pa = static_cast<const float *>(p.A) + ar * p.lda + t0 + lt;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 u = *reinterpret_cast<const float4 *>(pa + 8 * q);
+                    const float4 v = *reinterpret_cast<const float4 *>(pa + 8 * q + 4);
+                    ra[q] = make_uint4(pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                                       pack_bf16x2(v.z, v.w));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t t = t0 + lt + 16 * h;
             const int64_t rem = t_end - t;
             const int valid = rem <= 0 ? 0 : (rem < 16 ? static_cast<int>(rem) : 16);
-            load16<ABF16>(p.A, (ar < p.R && valid ? ar * p.lda + t : 0), ar < p.R ? valid : 0, 1.0f, va[h]);
+            uint16_t va[16], vb[16];
+            load16<ABF16>(p.A, (ar < p.R && valid ? ar * p.lda + t : 0), ar < p.R ? valid : 0, 1.0f, va);
             load16_bf16(p.B + (bs < p.S && valid ? static_cast<int64_t>(bs) * p.ldb + t : 0),
-                        bs < p.S ? valid : 0, vb[h]);
+                        bs < p.S ? valid : 0, vb);
+            pack8(va, 0, ra[2 * h]);
+            pack8(va, 1, ra[2 * h + 1]);
+            pack8(vb, 0, rb[2 * h]);
+            pack8(vb, 1, rb[2 * h + 1]);
         }
     };
     auto store_step = [&](int buf) {
+        uint4 *da = reinterpret_cast<uint4 *>(&sa[buf][lr * LP + lt]);
+        uint4 *db = reinterpret_cast<uint4 *>(&sb[buf][lr * LP + lt]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            store16(&sa[buf][lr * LP + lt + 16 * h], va[h]);
-            store16(&sb[buf][lr * LP + lt + 16 * h], vb[h]);
+        for (int q = 0; q < 4; ++q) {
+            da[q] = ra[q];
+            db[q] = rb[q];
         }
     };
 

@@ -175,12 +175,12 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
     const int64_t ar = r0 + lr;
     const int bs = s0 + lr;
     const bool rows_in = r0 + BR <= p.R && s0 + BS <= p.S;   // uniform over the workgroup
-    uint4 ra[4], rb[4];
+    uint4 ra0[4], rb0[4], ra1[4], rb1[4];   // two staging sets (even / odd steps)
     auto pack8 = [](const uint16_t (&v)[16], int h, uint4 &o) {
         o = make_uint4(v[8 * h] | (uint32_t(v[8 * h + 1]) << 16), v[8 * h + 2] | (uint32_t(v[8 * h + 3]) << 16),
                        v[8 * h + 4] | (uint32_t(v[8 * h + 5]) << 16), v[8 * h + 6] | (uint32_t(v[8 * h + 7]) << 16));
     };
-    auto load_step = [&](int64_t t0) {
+    auto load_step = [&](int64_t t0, uint4 (&ra)[4], uint4 (&rb)[4]) {
         if (rows_in && t0 + BT <= t_end) {
             // every row and every t of the step in range: unconditional 16-byte loads
             const uint16_t *pb = p.B + static_cast<int64_t>(bs) * p.ldb + t0 + lt;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
             pack8(vb, 1, rb[2 * h + 1]);
         }
     };
-    auto store_step = [&](int buf) {
+    auto store_step = [&](int buf, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
         uint4 *da = reinterpret_cast<uint4 *>(&sa[buf][lr * LP + lt]);
         uint4 *db = reinterpret_cast<uint4 *>(&sb[buf][lr * LP + lt]);
 #pragma unroll
@@ -235,15 +235,14 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nsteps = t_end > t_begin ? static_cast<int>((t_end - t_begin + BT - 1) / BT) : 0;
-    if (nsteps > 0) {
-        load_step(t_begin);
-        store_step(0);
-    }
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nsteps) load_step(t_begin + static_cast<int64_t>(st + 1) * BT);
+    // Barrier without the memory fence of __syncthreads (which would also wait for the loads
+    // issued two steps ahead): each wave waits for its own LDS stores, then s_barrier.
+    auto lds_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BT / 16; ++ks) {
             bf16x8 av[2], bv[2];
@@ -258,8 +257,28 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (st + 1 < nsteps) store_step(buf ^ 1);
-        __syncthreads();
+    };
+    // steps in pairs: LDS buffer 0 and staging set 0 for even steps, 1 for odd ones; a
+    // step's loads are issued two steps before its MFMAs
+    const int nsteps = t_end > t_begin ? static_cast<int>((t_end - t_begin + BT - 1) / BT) : 0;
+    auto tstep = [&](int st) { return t_begin + static_cast<int64_t>(st) * BT; };
+    if (nsteps > 0) {
+        load_step(tstep(0), ra0, rb0);
+        if (nsteps > 1) load_step(tstep(1), ra1, rb1);
+        store_step(0, ra0, rb0);
+    }
+    lds_barrier();
+    for (int st = 0; st < nsteps; st += 2) {
+        if (st + 2 < nsteps) load_step(tstep(st + 2), ra0, rb0);
+        compute(0);
+        if (st + 1 < nsteps) store_step(1, ra1, rb1);
+        lds_barrier();
+        if (st + 1 < nsteps) {
+            if (st + 3 < nsteps) load_step(tstep(st + 3), ra1, rb1);
+            compute(1);
+            if (st + 2 < nsteps) store_step(0, ra0, rb0);
+            lds_barrier();
+        }
     }
     // C block (i, j): lane holds rows 8*(e/4) + 4*g + e%4, column r32
 #pragma unroll

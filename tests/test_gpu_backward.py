@@ -94,17 +94,18 @@ def test_bitlinear_backward_parity(orc, M, K, N, x_bf, dy_bf, with_gamma):
         _bound_check(host(got[k]), ref[k], b[k], k)
 
 
-def test_bitlinear_backward_full_size_sampled(orc):
-    """The 370M gate projection at the benchmark's size (16384 tokens, K 1024, N 2816, bf16):
-    dx on sampled rows (rows are independent), dW on sampled entries, db whole."""
-    M, K, N = 16384, 1024, 2816
+@pytest.mark.parametrize("M,K,N", [(16384, 1024, 2816), (32768, 2560, 6912)], ids=["370M", "2.7B"])
+def test_bitlinear_backward_full_size_sampled(orc, M, K, N):
+    """The gate projection at the benchmark's block sizes (370M: 16384 tokens, K 1024,
+    N 2816; 2.7B: 32768 tokens, K 2560, N 6912; bf16): dx on sampled rows (rows are
+    independent), dW on sampled entries, db whole."""
     note(f"bitlinear_backward full size M={M} K={K} N={N}")
-    x, lat, dy, gamma = _bl_inputs(4242, M, K, N, True, True, True)
+    x, lat, dy, gamma = _bl_inputs(4242 + K, M, K, N, True, True, True)
     q, s = orc.ternarize(lat)
     w = api.TernaryLinear.from_ternary(q, s, "cuda", norm_w=gamma)
     got = api.bitlinear_backward(w, dev(x, torch.bfloat16), dev(dy, torch.bfloat16), want_dgamma=False)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 127, 128, 4095, 9000, 16382, 16383])
+    rows = np.array([0, 1, 127, 128, 4095, 9000, M - 2, M - 1])
     ref = orc.bitlinear_backward(x[rows], q, s, dy[rows].astype(np.float64), gamma=gamma)
     b = _bounds(orc, x[rows], q, s, dy[rows], gamma, True)
     _bound_check(host(got["dx"])[rows], ref["dx"], b["dx"], "dx rows")
@@ -132,7 +133,7 @@ def test_bitlinear_backward_empty(orc):
 
 
 MG_CASES = [(1, 1, 64), (1, 16, 128), (2, 37, 256), (2, 200, 1024), (1, 33, 2560), (1, 20, 4096),
-            (8, 2048, 1024)]
+            (8, 2048, 1024), (16, 2048, 2560)]
 
 
 @pytest.mark.parametrize("gate_mode", [0, 1], ids=["swish_rmsnorm", "sigmoid"])

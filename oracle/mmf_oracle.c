@@ -705,6 +705,114 @@ int orc_block(const float *x, int64_t B, int64_t T, const orc_linear *wi,
     return 0;
 }
 
+/* ------------------------------------------------- B3 block backward (reading R14)
+ * The gradients of orc_block: the forward is rerun with the same roundings (R8), then the
+ * chain of B1/B2 and the GLU's elementwise product is walked backwards:
+ *   dy1 = dy;  dm = down^T(dy) (B1 on the down input m);
+ *   dgate = dm*u*silu'(g), dup = dm*silu(g) (g, u: the gate and up pre-activations);
+ *   dy1 += gate^T(dgate) + up^T(dup) (B1 on y1);  do = o^T(dy1) (B1 on the g_norm output);
+ *   d_ifg, dh0 = B2(do, dh_last);  dx = dy1 + sum_k k^T(d_ifg_k) for k = i, f, g (B1 on x).
+ * dy [B, T, D] and dh_last [B, D] (or NULL) fp64; dx [B, T, D], dh0 [B, D]; per BitLinear
+ * (order i, f, g, o, gate, up, down) optional dw [N, K], db [N], dgamma [K]; dgnorm_w,
+ * df_bias [D] optional.  fp64.
+ */
+int orc_block_backward(const float *x, int64_t B, int64_t T, const orc_linear *const *w7,
+                       const float *f_bias, const float *f_lower, const float *gnorm_w, double eps,
+                       int gate_mode, int resid_bf16, const double *h0, const double *dy,
+                       const double *dh_last, double *dx, double *dh0, double *const *dw,
+                       double *const *db, double *const *dgamma, double *dgnorm_w,
+                       double *df_bias) {
+    if (!x || !w7 || !dy || !dx) return -1;
+    for (int k = 0; k < 7; ++k)
+        if (!w7[k]) return -1;
+    const int64_t D = w7[0]->k, F = w7[4]->n, M = B * T;
+    if (M == 0) return 0;
+    double *ifg = (double *)malloc(sizeof(double) * (size_t)(M * 3 * D));
+    double *o = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    float *o32 = (float *)malloc(sizeof(float) * (size_t)(M * D));
+    double *yo = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    float *y1 = (float *)malloc(sizeof(float) * (size_t)(M * D));
+    double *gp = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *up = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *mv = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    float *m32 = (float *)malloc(sizeof(float) * (size_t)(M * F));
+    double *dm = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *dg = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *du = (double *)malloc(sizeof(double) * (size_t)(M * F));
+    double *dy1 = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *dpart = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *dout = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    double *d_ifg = (double *)malloc(sizeof(double) * (size_t)(M * 3 * D));
+    double *dseg = (double *)malloc(sizeof(double) * (size_t)(M * D));
+    if (!ifg || !o || !o32 || !yo || !tmp || !y1 || !gp || !up || !mv || !m32 || !dm || !dg ||
+        !du || !dy1 || !dpart || !dout || !d_ifg || !dseg)
+        return -3;
+    /* forward, as orc_block computes it */
+    {
+        double *outs[3];
+        double *yi = (double *)malloc(sizeof(double) * (size_t)(M * D * 3));
+        if (!yi) return -3;
+        outs[0] = yi; outs[1] = yi + M * D; outs[2] = yi + 2 * M * D;
+        int rc = group_bitlinear(x, M, 3, w7, eps, outs, NULL);
+        if (rc) return rc;
+        for (int64_t r = 0; r < M; ++r)
+            for (int64_t c = 0; c < 3 * D; ++c) {
+                const double v = outs[c / D][r * D + c % D];
+                ifg[r * 3 * D + c] = resid_bf16 ? orc_round_bf16(v) : v;
+            }
+        free(yi);
+    }
+    int rc = orc_mlgru(ifg, B, T, D, f_bias, f_lower, h0, gnorm_w, eps, gate_mode, o, NULL);
+    if (rc) return rc;
+    to_act(o, o32, D * M, resid_bf16);
+    if ((rc = orc_bitlinear(o32, M, w7[3], eps, yo, NULL, NULL, NULL))) return rc;
+    for (int64_t i = 0; i < M * D; ++i) tmp[i] = yo[i] + (double)x[i];   /* y1 before rounding */
+    to_act(tmp, y1, M * D, resid_bf16);
+    {
+        double *outs[2] = {gp, up};
+        if ((rc = group_bitlinear(y1, M, 2, w7 + 4, eps, outs, NULL))) return rc;
+    }
+    for (int64_t i = 0; i < M * F; ++i) mv[i] = silu_d(gp[i]) * up[i];
+    to_act(mv, m32, M * F, resid_bf16);
+    /* backward */
+    if ((rc = orc_bitlinear_backward(m32, M, w7[6], eps, dy, dm, dgamma ? dgamma[6] : NULL,
+                                     dw ? dw[6] : NULL, db ? db[6] : NULL)))
+        return rc;
+    for (int64_t i = 0; i < M * F; ++i) {
+        const double sg = sigmoid_d(gp[i]);
+        dg[i] = dm[i] * up[i] * sg * (1.0 + gp[i] * (1.0 - sg));
+        du[i] = dm[i] * gp[i] * sg;
+    }
+    memcpy(dy1, dy, sizeof(double) * (size_t)(M * D));
+    for (int k = 4; k <= 5; ++k) {
+        if ((rc = orc_bitlinear_backward(y1, M, w7[k], eps, k == 4 ? dg : du, dpart,
+                                         dgamma ? dgamma[k] : NULL, dw ? dw[k] : NULL,
+                                         db ? db[k] : NULL)))
+            return rc;
+        for (int64_t i = 0; i < M * D; ++i) dy1[i] += dpart[i];
+    }
+    if ((rc = orc_bitlinear_backward(o32, M, w7[3], eps, dy1, dout, dgamma ? dgamma[3] : NULL,
+                                     dw ? dw[3] : NULL, db ? db[3] : NULL)))
+        return rc;
+    if ((rc = orc_mlgru_backward(ifg, B, T, D, f_bias, f_lower, h0, gnorm_w, eps, gate_mode, dout,
+                                 dh_last, d_ifg, dh0, dgnorm_w, df_bias)))
+        return rc;
+    memcpy(dx, dy1, sizeof(double) * (size_t)(M * D));
+    for (int k = 0; k < 3; ++k) {
+        for (int64_t r = 0; r < M; ++r)
+            for (int64_t d = 0; d < D; ++d) dseg[r * D + d] = d_ifg[r * 3 * D + k * D + d];
+        if ((rc = orc_bitlinear_backward(x, M, w7[k], eps, dseg, dpart, dgamma ? dgamma[k] : NULL,
+                                         dw ? dw[k] : NULL, db ? db[k] : NULL)))
+            return rc;
+        for (int64_t i = 0; i < M * D; ++i) dx[i] += dpart[i];
+    }
+    free(ifg); free(o); free(o32); free(yo); free(tmp); free(y1); free(gp); free(up); free(mv);
+    free(m32); free(dm); free(dg); free(du); free(dy1); free(dpart); free(dout); free(d_ifg);
+    free(dseg);
+    return 0;
+}
+
 /* ----------------------------------------- HGRN forget-gate lower bounds (R12)
  * G [L, D] per-layer logits -> lb [L, D]: for each channel, a softmax over the L layers
  * (fp64; the largest logit is subtracted first so exp cannot overflow), accumulated over

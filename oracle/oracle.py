@@ -60,6 +60,8 @@ class Oracle:
         L.orc_bitlinear_backward.argtypes = [vp, i64, C.POINTER(OrcLinear), f64, vp, vp, vp, vp, vp]
         L.orc_mlgru_backward.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, f64, i32, vp, vp, vp,
                                          vp, vp, vp]
+        L.orc_block_backward.argtypes = [vp, i64, i64, vp, vp, vp, vp, f64, i32, i32, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp]
         L.orc_trit_row_bytes.argtypes = [i64]
         L.orc_trit_row_bytes.restype = i64
         L.orc_pack_trits.argtypes = [vp, i64, i64, vp]
@@ -243,6 +245,42 @@ class Oracle:
                                          _p(out["dh0"]), _p(out["dgnorm_w"]), _p(out["df_bias"]))
         if rc:
             raise ValueError(f"orc_mlgru_backward failed ({rc})")
+        return out
+
+    def block_backward(self, x, W: dict, dy, f_bias=None, gnorm_w=None, eps: float = 1e-6,
+                       gate_mode: int = 0, resid_bf16: bool = True, h0=None, f_lower=None,
+                       dh_last=None):
+        """Block backward (reading R14).  W as for block(); x [B, T, D], dy [B, T, D].
+        Returns dict dx, dh0, dgnorm_w, df_bias and per BitLinear name (i, f, g, o, gate, up,
+        down) dw[name] [N, K], db[name] [N], dgamma[name] [K] (fp64)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        B, T, D = x.shape
+        names = ("i", "f", "g", "o", "gate", "up", "down")
+        lins = [self.linear(*W[k]) for k in names]
+        arr = (OrcLinear * 7)(*lins)
+        ptrs = (C.c_void_p * 7)(*[C.cast(C.byref(arr, i * C.sizeof(OrcLinear)), C.c_void_p) for i in range(7)])
+        dyv = np.ascontiguousarray(dy, dtype=np.float64)
+        out = {"dx": np.empty((B, T, D)), "dh0": np.empty((B, D)), "dgnorm_w": np.empty(D),
+               "df_bias": np.empty(D), "dw": {}, "db": {}, "dgamma": {}}
+        for k, ln in zip(names, lins):
+            out["dw"][k] = np.empty((ln.n, ln.k))
+            out["db"][k] = np.empty(ln.n)
+            out["dgamma"][k] = np.empty(ln.k)
+        dwp = (C.c_void_p * 7)(*[_p(out["dw"][k]) for k in names])
+        dbp = (C.c_void_p * 7)(*[_p(out["db"][k]) for k in names])
+        dgp = (C.c_void_p * 7)(*[_p(out["dgamma"][k]) for k in names])
+        fb = None if f_bias is None else np.ascontiguousarray(f_bias, dtype=np.float32)
+        lb = None if f_lower is None else np.ascontiguousarray(f_lower, dtype=np.float32)
+        gw = None if gnorm_w is None else np.ascontiguousarray(gnorm_w, dtype=np.float32)
+        h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+        dl = None if dh_last is None else np.ascontiguousarray(dh_last, dtype=np.float64)
+        self._keep.append((arr, ptrs, dwp, dbp, dgp))
+        rc = self.lib.orc_block_backward(_p(x), B, T, ptrs, _p(fb), _p(lb), _p(gw), eps, gate_mode,
+                                         int(resid_bf16), _p(h0), _p(dyv), _p(dl), _p(out["dx"]),
+                                         _p(out["dh0"]), dwp, dbp, dgp, _p(out["dgnorm_w"]),
+                                         _p(out["df_bias"]))
+        if rc:
+            raise ValueError(f"orc_block_backward failed ({rc})")
         return out
 
     # -------------------------------------------------------------------- GLU

@@ -610,10 +610,93 @@ def pin_mlgru_backward_fd(orc):
                 assert abs(got["dgnorm_w"][d] - ref) <= 1e-9 * (1 + abs(ref)), ("dgnorm_w", d)
 
 
+def pin_block_backward_ste(orc):
+    """Block gradients (R14) against central differences of the block's straight-through
+    surrogate at the base point: every BitLinear computes (u(x_in) + delta) W_hat^T + b with
+    u = x_in*gamma*r and delta = q*a - u frozen at the base point (the quantizer's error), so
+    the surrogate's value there is the quantized forward and its derivatives are the
+    straight-through ones, dW included (through q*a); the MLGRU is the pinned fp64 forward;
+    residuals and SiLU(gate)*up are written here.  fp32 activations, both gate modes, with
+    biases, gains, forget bias and bound, h0 and dh_T."""
+    rng = np.random.default_rng(21)
+    B, T, D, F, eps = 2, 5, 16, 24, 1e-6
+    M = B * T
+    shapes = {"i": (D, D), "f": (D, D), "g": (D, D), "o": (D, D), "gate": (F, D), "up": (F, D),
+              "down": (D, F)}
+    for gm in (0, 1):
+        x = rng.standard_normal((B, T, D)).astype(np.float32)
+        g_x = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+        g_gu = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+        W, What, gam, bias = {}, {}, {}, {}
+        for k, (n, kk) in shapes.items():
+            q, sc = orc.ternarize((0.3 * rng.standard_normal((n, kk))).astype(np.float32))
+            gk = g_x if k in ("i", "f", "g") else (g_gu if k in ("gate", "up") else
+                                                   (1 + 0.2 * rng.standard_normal(kk)).astype(np.float32))
+            bk = (0.1 * rng.standard_normal(n)).astype(np.float32)
+            W[k] = (q, sc, gk, bk)
+            What[k] = sc * q.astype(np.float64)
+            gam[k] = gk.astype(np.float64).copy()
+            bias[k] = bk.astype(np.float64).copy()
+        fb = (0.3 * rng.standard_normal(D)).astype(np.float32)
+        lb = (0.2 * rng.random(D)).astype(np.float32)
+        gw = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32)
+        h0 = rng.standard_normal((B, D))
+        dy = rng.standard_normal((B, T, D))
+        dl = rng.standard_normal((B, D))
+        kw = dict(f_bias=fb, gnorm_w=gw, eps=eps, gate_mode=gm, f_lower=lb)
+        base = orc.block(x, W, resid_bf16=False, h0=h0, record=True, **kw)
+        got = orc.block_backward(x, W, dy, resid_bf16=False, h0=h0, dh_last=dl, **kw)
+
+        def delta(st, k):
+            xin = st["x_in"].astype(np.float64)
+            r = 1.0 / np.sqrt((xin * xin).mean(axis=1, keepdims=True) + eps)
+            return st["q"].astype(np.float64) * st["a"][:, None] - xin * gam[k] * r
+        st = base["stages"]
+        dlt = {"ifg": delta(st["ifg"], "i"), "o": delta(st["o"], "o"), "gu": delta(st["gateup"], "gate"),
+               "down": delta(st["down"], "down")}
+        xv, h0v = x.astype(np.float64).reshape(M, D).copy(), h0.copy()
+
+        def bl(xin, k, d):
+            r = 1.0 / np.sqrt((xin * xin).mean(axis=1, keepdims=True) + eps)
+            return (xin * gam[k] * r + d) @ What[k].T + bias[k]
+
+        def forward():
+            ifg = np.concatenate([bl(xv, k, dlt["ifg"]) for k in ("i", "f", "g")], axis=1)
+            out, hl = orc.mlgru(ifg.reshape(B, T, 3 * D), h0=h0v, **kw)
+            y1 = xv + bl(out.reshape(M, D), "o", dlt["o"])
+            gg, uu = bl(y1, "gate", dlt["gu"]), bl(y1, "up", dlt["gu"])
+            y = y1 + bl(gg / (1.0 + np.exp(-gg)) * uu, "down", dlt["down"])
+            return y, hl
+
+        y0, _ = forward()
+        assert np.allclose(y0.reshape(B, T, D), base["y"], rtol=1e-5, atol=1e-5), "surrogate != forward"
+
+        def loss():
+            y, hl = forward()
+            return float(np.sum(dy.reshape(M, D) * y) + np.sum(dl * hl))
+
+        def chk(what, got_v, arr, idx):
+            fd = _fd(loss, arr, idx)
+            assert abs(got_v - fd) <= 1e-5 * (1 + abs(fd)), (gm, what, idx, got_v, fd)
+
+        for idx in [(0, 0), (3, 7), (9, 15), (5, 2)]:
+            chk("dx", got["dx"].reshape(M, D)[idx], xv, idx)
+        for idx in [(0, 1), (1, 14)]:
+            chk("dh0", got["dh0"][idx], h0v, idx)
+        for k in shapes:
+            n, kk = shapes[k]
+            for idx in [(0, 0), (n - 1, kk - 1), (n // 2, kk // 3)]:
+                chk("dw " + k, got["dw"][k][idx], What[k], idx)
+            chk("db " + k, got["db"][k][n // 2], bias[k], n // 2)
+            chk("dgamma " + k, got["dgamma"][k][kk // 2], gam[k], kk // 2)
+        # the forget bias enters as the f projection's bias does
+        assert np.allclose(got["df_bias"], got["db"]["f"], rtol=1e-12, atol=1e-12)
+
+
 PINS = [pin_act_quant_hand, pin_ternarize_hand, pin_pack_format, pin_trit_pack_hand,
         pin_trit_invariants, pin_quant_invariants,
         pin_quant_literal_rmsnorm, pin_ternary_invariants, pin_bitlinear_hand,
         pin_bitlinear_brute, pin_recurrence_hand, pin_recurrence_unrolled, pin_mlgru_roles,
         pin_mlgru_limits, pin_output_gate, pin_hgrn_lower_bound_gate, pin_hgrn_lower_bounds, pin_glu_identity, pin_block_residuals,
         pin_block_causal_and_carry, pin_block_stages, pin_embedding, pin_round_bf16,
-        pin_bitlinear_backward_fd, pin_mlgru_backward_fd]
+        pin_bitlinear_backward_fd, pin_mlgru_backward_fd, pin_block_backward_ste]

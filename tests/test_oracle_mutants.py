@@ -94,6 +94,13 @@ MUTANTS = [
      "if (dh0) dh0[b * D + d] = T > 0 ? G :"),
     ("bwd_dh_last_dropped", "G = dho[i] + (t == T - 1 ? (dh_last ? dh_last[b * D + d] : 0.0)",
      "G = dho[i] + (t == T - 1 ? 0.0"),
+    ("bwd_block_no_residual_dx", "memcpy(dx, dy1, sizeof(double) * (size_t)(M * D));",
+     "memset(dx, 0, sizeof(double) * (size_t)(M * D));"),
+    ("bwd_block_glu_gate_sigmoid", "dg[i] = dm[i] * up[i] * sg * (1.0 + gp[i] * (1.0 - sg));",
+     "dg[i] = dm[i] * up[i] * sg;"),
+    ("bwd_block_up_without_gate", "du[i] = dm[i] * gp[i] * sg;", "du[i] = dm[i] * sg;"),
+    ("bwd_block_o_grad_skips_glu", "if ((rc = orc_bitlinear_backward(o32, M, w7[3], eps, dy1, dout,",
+     "if ((rc = orc_bitlinear_backward(o32, M, w7[3], eps, dy, dout,"),
     ("embedding_no_scale", "double v = (double)qe[(int64_t)ids[t] * D + d] * (double)scale;",
      "double v = (double)qe[(int64_t)ids[t] * D + d];"),
 ]

@@ -377,6 +377,33 @@ int mlgru_backward(const mmf_mlgru_args *args, const void *dout, mmf_dtype dout_
                    const float *dh_last, float *d_ifg, float *dh0, float *dgnorm_w,
                    float *df_bias, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* block_backward: every gradient of block_forward (same arguments: x [B][T][D] of dtype dt,
+ * h0 the initial state or NULL), given dy [B][T][D] (dy_dt, gradient at the block output)
+ * and dh_last [B][D] fp32 (gradient at the final state) or NULL.  The forward is recomputed
+ * (prefill kernels; the gate and up pre-activations kept in fp32), then: down's BitLinear
+ * backward gives dm; the GLU product gives dgate = dm*up*silu'(gate), dup = dm*SiLU(gate);
+ * gate and up share one contraction for the input gradient (dy1 = dy + gate^T dgate +
+ * up^T dup), o_proj gives the gradient at the g_norm output, the MLGRU backward d_ifg, dh0,
+ * dgnorm_w, df_bias, and i, f, g one contraction for dx = dy1 + sum_k k^T d_k.  Outputs fp32:
+ * dx [B][T][D], dh0 [B][D] or NULL, and the parameter gradients in grads (any pointer NULL =
+ * not wanted; grads itself may be NULL): dw[k] [N][K] and db[k] [N] per BitLinear (order i, f,
+ * g, o, gate, up, down), dgamma[0..3] [K] for the norm gains of x (i|f|g), the g_norm output
+ * (o), y1 (gate|up) and m (down), dgnorm_w [D], df_bias [D].  Needs F % 8 == 0 and F <= 8192;
+ * same block limits as block_forward.  Workspace: block_backward_workspace_bytes (the
+ * recomputed activations, fp32 gradients between the stages, bf16 operand copies). */
+typedef struct mmf_block_grads {
+    float *dw[7];
+    float *db[7];
+    float *dgamma[4];
+    float *dgnorm_w;
+    float *df_bias;
+} mmf_block_grads;
+size_t block_backward_workspace_bytes(const mmf_block *w, int64_t B, int64_t T);
+int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
+                   const float *h0, const void *dy, mmf_dtype dy_dt, const float *dh_last, float *dx,
+                   float *dh0, const mmf_block_grads *grads, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,10 @@ class mmf_block(C.Structure):
         ("f_bias", vp), ("gnorm_w", vp), ("eps", f32), ("gate_mode", i32), ("f_lower", vp)]
 
 
+class mmf_block_grads(C.Structure):
+    _fields_ = [("dw", vp * 7), ("db", vp * 7), ("dgamma", vp * 4), ("dgnorm_w", vp), ("df_bias", vp)]
+
+
 class mmf_bitlinear_trits(C.Structure):
     _fields_ = [("packed", vp), ("scale", f32), ("norm_w", vp), ("bias", vp), ("eps", f32),
                 ("K", i32), ("N", i32)]
@@ -98,6 +102,9 @@ SIGNATURES = {
                                      vp, vp, sz, vp]),
     "mlgru_backward_workspace_bytes": (sz, [i64, i64, i64]),
     "mlgru_backward": (C.c_int, [P(mmf_mlgru_args), vp, C.c_int, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "block_backward_workspace_bytes": (sz, [P(mmf_block), i64, i64]),
+    "block_backward": (C.c_int, [P(mmf_block), vp, C.c_int, i64, i64, vp, vp, C.c_int, vp, vp, vp,
+                                 P(mmf_block_grads), vp, sz, vp]),
 }
 
 

@@ -111,7 +111,7 @@ struct NtGemmArgs {
     float scale;
     float *C;               // [R][S]
     int64_t t_per_split;    // multiple of BT (T when not split)
-    int32_t atomic;
+    int32_t atomic;         // 0: C = v; 1: C += v with fp32 atomics (split); 2: C += v
 };
 
 constexpr int BT = 64;           // contraction step (four 16-deep MFMA steps)
@@ -292,7 +292,8 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
                 const int64_t row = r0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                 if (row < p.R) {
                     float *o = p.C + row * p.S + col;
-                    if (p.atomic) atomicAdd(o, acc[i][j][e] * p.scale);
+                    if (p.atomic == 1) atomicAdd(o, acc[i][j][e] * p.scale);
+                    else if (p.atomic == 2) *o += acc[i][j][e] * p.scale;
                     else *o = acc[i][j][e] * p.scale;
                 }
             }
@@ -320,11 +321,11 @@ __global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, 
 }
 
 // dst[c][m] = bf16(src[m][c] * (scale ? scale[m] : 1)) for m < M, 0 for M <= m < ldm (the
-// padding of every destination row); src bf16, fp32 (SRC 0/1) or int8 codes (SRC 2).
+// padding of every destination row); src [M][lds] bf16, fp32 (SRC 0/1) or int8 codes (SRC 2).
 // 64 x 64 tiles through LDS: rows read and columns written as contiguous runs.
 template <int SRC>
-__global__ __launch_bounds__(256) void transpose_kernel(const void *src, const float *scale, int64_t M,
-                                                        int32_t C, int64_t ldm, uint16_t *dst) {
+__global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t lds, const float *scale,
+                                                        int64_t M, int32_t C, int64_t ldm, uint16_t *dst) {
     __shared__ float tile[64][65];
     const int tid = threadIdx.x;
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 64;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *src, const f
             const int c = c0 + cc + e;
             float v = 0.0f;
             if (m < M && c < C) {
-                const int64_t idx = m * C + c;
+                const int64_t idx = m * lds + c;
                 if constexpr (SRC == 0) v = bf16_bits_to_f32(static_cast<const uint16_t *>(src)[idx]);
                 else if constexpr (SRC == 1) v = static_cast<const float *>(src)[idx];
                 else v = static_cast<float>(static_cast<const int8_t *>(src)[idx]);
@@ -359,13 +360,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *src, const f
 }
 
 // dx and dgamma from g: workgroup per RPW rows, thread per columns c = tid + 256 j.
-//   r = (mean x^2 + eps)^(-1/2), dot = sum_c g*gamma*x, dx = r*gamma*g - x*r^3/K*dot;
+//   r = (mean x^2 + eps)^(-1/2), dot = sum_c g*gamma*x, dx = r*gamma*g - x*r^3/K*dot
+//   (+ a residual gradient res [M][K], bf16 for RES 1, fp32 for RES 2);
 //   dgamma[c] += sum over the workgroup's rows of g*x*r (fp32 atomics into a zeroed array).
 constexpr int RPW = 16;
-template <bool XBF16>
+template <bool XBF16, int RES>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const void *x, const float *gsrc, const float *gamma,
                                                        float eps, int64_t M, int32_t K, float *dx,
-                                                       float *dgamma) {
+                                                       float *dgamma, const void *res) {
     __shared__ float red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RPW;
@@ -406,7 +408,10 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const void *x, const floa
                 const float xv = load_act<XBF16>(x, m * K + c);
                 const float gv = gsrc[m * K + c];
                 const float gm = gamma ? gamma[c] : 1.0f;
-                if (dx) dx[m * K + c] = r * gm * gv - xv * c3;
+                float d = r * gm * gv - xv * c3;
+                if constexpr (RES == 1) d += bf16_bits_to_f32(static_cast<const uint16_t *>(res)[m * K + c]);
+                if constexpr (RES == 2) d += static_cast<const float *>(res)[m * K + c];
+                if (dx) dx[m * K + c] = d;
                 dg_acc[j] = fmaf(gv * xv, r, dg_acc[j]);
             }
         }
@@ -420,17 +425,17 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const void *x, const floa
     }
 }
 
-// out[c] += sum over rows [r0, r1) of src[r][c] (bf16 or fp32), thread per column, rows split
-// over blockIdx.y (fp32 atomics into a zeroed array).
+// out[c] += sum over rows [r0, r1) of src[r][c] (src [R][lds], bf16 or fp32), thread per
+// column, rows split over blockIdx.y (fp32 atomics into a zeroed array).
 template <bool BF16>
-__global__ __launch_bounds__(256) void col_sum_kernel(const void *src, int64_t R, int32_t C, int32_t rows_per,
-                                                      float *out) {
+__global__ __launch_bounds__(256) void col_sum_kernel(const void *src, int64_t lds, int64_t R, int32_t C,
+                                                      int32_t rows_per, float *out) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= C) return;
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per;
     const int64_t r1 = r0 + rows_per < R ? r0 + rows_per : R;
     float s = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) s += load_act<BF16>(src, r * C + c);
+    for (int64_t r = r0; r < r1; ++r) s += load_act<BF16>(src, r * lds + c);
     atomicAdd(&out[c], s);
 }
 
@@ -439,13 +444,36 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
-// ------------------------------------------------------------------ MLGRU backward
-constexpr int kBC = 16;           // tokens per chunk (the forward's chunk)
-
 __device__ __forceinline__ float silu_grad(float z) {
     const float s = sigmoidf_(z);
     return s * (1.0f + z * (1.0f - s));
 }
+
+// The GLU's gated product from the gate | up pre-activations gu [M][2F] fp32 (gate at column
+// f, up at F + f): m = SiLU(gate)*up in the activation dtype (the down projection's input).
+template <bool MBF16>
+__global__ __launch_bounds__(256) void glu_product_kernel(const float *gu, int64_t M, int32_t F, void *m) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M * F) return;
+    const int64_t row = i / F, f = i % F;
+    const float g = gu[row * 2 * F + f], u = gu[row * 2 * F + F + f];
+    store_act<MBF16>(m, i, siluf_(g) * u);
+}
+
+// Its backward: dgate = dm*up*silu'(gate), dup = dm*SiLU(gate), into dgu [M][2F] (gate | up).
+__global__ __launch_bounds__(256) void glu_product_bwd_kernel(const float *gu, const float *dm, int64_t M,
+                                                              int32_t F, float *dgu) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M * F) return;
+    const int64_t row = i / F, f = i % F;
+    const float g = gu[row * 2 * F + f], u = gu[row * 2 * F + F + f], d = dm[i];
+    dgu[row * 2 * F + f] = d * u * silu_grad(g);
+    dgu[row * 2 * F + F + f] = d * siluf_(g);
+}
+
+// ------------------------------------------------------------------ MLGRU backward
+constexpr int kBC = 16;           // tokens per chunk (the forward's chunk)
+
 
 // Phase 1 (gate mode 0 only): workgroup per (chunk, b); thread per channel quads
 // q = tid + 256 j (channels 4q..4q+3).  Reruns the recurrence over the chunk, keeps per token
@@ -649,7 +677,8 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_col_sum(const void *src, int bf16, int64_t R, int32_t C, float *out, hipStream_t s) {
+hipError_t launch_col_sum(const void *src, int bf16, int64_t lds, int64_t R, int32_t C, float *out,
+                          hipStream_t s) {
     if (R <= 0 || C <= 0) return hipSuccess;
     // about 64 rows per workgroup, at most 4096 row splits
     int64_t splits = (R + 63) / 64;
@@ -657,84 +686,135 @@ hipError_t launch_col_sum(const void *src, int bf16, int64_t R, int32_t C, float
     const int32_t rows_per = static_cast<int32_t>((R + splits - 1) / splits);
     splits = (R + rows_per - 1) / rows_per;
     const dim3 grid(static_cast<unsigned>((C + 255) / 256), static_cast<unsigned>(splits));
-    if (bf16) hipLaunchKernelGGL((col_sum_kernel<true>), grid, dim3(256), 0, s, src, R, C, rows_per, out);
-    else hipLaunchKernelGGL((col_sum_kernel<false>), grid, dim3(256), 0, s, src, R, C, rows_per, out);
+    if (bf16) hipLaunchKernelGGL((col_sum_kernel<true>), grid, dim3(256), 0, s, src, lds, R, C, rows_per, out);
+    else hipLaunchKernelGGL((col_sum_kernel<false>), grid, dim3(256), 0, s, src, lds, R, C, rows_per, out);
+    return hipGetLastError();
+}
+
+hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *packed, int32_t N,
+                        int32_t K, float scale, int64_t M, uint16_t *wt, float *g, int accumulate,
+                        hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int64_t n = static_cast<int64_t>(K) * (N / 8);
+    hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                       packed, N, K, wt);
+    NtGemmArgs ga{};
+    ga.A = dy;
+    ga.a_bf16 = dy_bf16;
+    ga.B = wt;
+    ga.R = M;
+    ga.S = K;
+    ga.T = N;
+    ga.lda = ldy;
+    ga.ldb = N;
+    ga.scale = scale;
+    ga.C = g;
+    ga.t_per_split = N;
+    ga.atomic = accumulate ? 2 : 0;
+    const dim3 grid(static_cast<unsigned>(((K + BS - 1) / BS) * ((M + BR - 1) / BR)), 1, 1);
+    timing_begin(FAM_BWD_G, s);
+    if (dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
+    else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, ga);
+    timing_end(FAM_BWD_G, s);
+    return hipGetLastError();
+}
+
+hipError_t bwd_launch_rows(const void *x, int x_bf16, const float *g, const float *gamma, float eps,
+                           int64_t M, int32_t K, float *dx, float *dgamma, const void *res, int res_kind,
+                           hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    hipError_t e;
+    if (dgamma && (e = launch_fill_zero(dgamma, K, s)) != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>((M + RPW - 1) / RPW));
+#define MMF_ROWS(XB, RK) hipLaunchKernelGGL((bwd_rows_kernel<XB, RK>), grid, dim3(256), 0, s, x, g, gamma, eps, M, K, dx, dgamma, res)
+    if (x_bf16) {
+        if (res_kind == 1) MMF_ROWS(true, 1);
+        else if (res_kind == 2) MMF_ROWS(true, 2);
+        else MMF_ROWS(true, 0);
+    } else {
+        if (res_kind == 1) MMF_ROWS(false, 1);
+        else if (res_kind == 2) MMF_ROWS(false, 2);
+        else MMF_ROWS(false, 0);
+    }
+#undef MMF_ROWS
+    return hipGetLastError();
+}
+
+hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uint16_t *qT, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const dim3 gt(static_cast<unsigned>((K + 63) / 64), static_cast<unsigned>(ldm / 64));
+    hipLaunchKernelGGL((transpose_kernel<2>), gt, dim3(256), 0, s, q, static_cast<int64_t>(K), nullptr, M, K, ldm, qT);
+    return hipGetLastError();
+}
+
+hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int32_t N,
+                         int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT, float *dw, hipStream_t s) {
+    if (M <= 0) return launch_fill_zero(dw, static_cast<int64_t>(N) * K, s);
+    const dim3 gt(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>(ldm / 64));
+    if (dy_bf16) hipLaunchKernelGGL((transpose_kernel<0>), gt, dim3(256), 0, s, dy, ldy, a, M, N, ldm, dyaT);
+    else hipLaunchKernelGGL((transpose_kernel<1>), gt, dim3(256), 0, s, dy, ldy, a, M, N, ldm, dyaT);
+    hipError_t e;
+    if ((e = launch_fill_zero(dw, static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
+    NtGemmArgs ga{};
+    ga.A = dyaT;
+    ga.a_bf16 = 1;
+    ga.B = qT;
+    ga.R = N;
+    ga.S = K;
+    ga.T = ldm;
+    ga.lda = ldm;
+    ga.ldb = ldm;
+    ga.scale = 1.0f;
+    ga.C = dw;
+    ga.atomic = 1;
+    const int64_t tiles = static_cast<int64_t>((K + BS - 1) / BS) * ((N + BR - 1) / BR);
+    // split the tokens so that about 1024 workgroups run, each over >= 8 steps
+    int64_t splits = (1024 + tiles - 1) / tiles;
+    const int64_t max_splits = (ldm + 8 * BT - 1) / (8 * BT);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    int64_t per = (ldm + splits - 1) / splits;
+    per = (per + BT - 1) / BT * BT;
+    splits = (ldm + per - 1) / per;
+    ga.t_per_split = per;
+    const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
+    timing_begin(FAM_BWD_DW, s);
+    hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
+    timing_end(FAM_BWD_DW, s);
+    return hipGetLastError();
+}
+
+hipError_t bwd_launch_db(const void *dy, int dy_bf16, int64_t ldy, int64_t M, int32_t N, float *db, hipStream_t s) {
+    hipError_t e;
+    if ((e = launch_fill_zero(db, N, s)) != hipSuccess) return e;
+    return launch_col_sum(dy, dy_bf16, ldy, M, N, db, s);
+}
+
+hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s) {
+    const int64_t n = M * F;
+    if (n <= 0) return hipSuccess;
+    if (m_bf16) hipLaunchKernelGGL((glu_product_kernel<true>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, M, F, m);
+    else hipLaunchKernelGGL((glu_product_kernel<false>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, M, F, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_glu_product_bwd(const float *gu, const float *dm, int64_t M, int32_t F, float *dgu, hipStream_t s) {
+    const int64_t n = M * F;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(glu_product_bwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, dm, M, F, dgu);
     return hipGetLastError();
 }
 
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    // g = s_w * dy (W^T)^T: W^T expanded to bf16 once, then the NT GEMM over n
-    {
-        const int64_t n = static_cast<int64_t>(a.K) * (a.N / 8);
-        hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                           a.packed, a.N, a.K, a.wt);
-        NtGemmArgs g{};
-        g.A = a.dy;
-        g.a_bf16 = a.dy_bf16;
-        g.B = a.wt;
-        g.R = a.M;
-        g.S = a.K;
-        g.T = a.N;
-        g.lda = a.N;
-        g.ldb = a.N;
-        g.scale = a.scale;
-        g.C = a.g;
-        g.t_per_split = a.N;
-        g.atomic = 0;
-        const dim3 grid(static_cast<unsigned>(((a.K + BS - 1) / BS) * ((a.M + BR - 1) / BR)), 1, 1);
-        timing_begin(FAM_BWD_G, s);
-        if (a.dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
-        else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, g);
-        timing_end(FAM_BWD_G, s);
-    }
-    if (a.dgamma && (e = launch_fill_zero(a.dgamma, a.K, s)) != hipSuccess) return e;
-    {
-        const dim3 grid(static_cast<unsigned>((a.M + RPW - 1) / RPW));
-        if (a.x_bf16) hipLaunchKernelGGL((bwd_rows_kernel<true>), grid, dim3(256), 0, s, a.x, a.g, a.gamma, a.eps, a.M, a.K, a.dx, a.dgamma);
-        else hipLaunchKernelGGL((bwd_rows_kernel<false>), grid, dim3(256), 0, s, a.x, a.g, a.gamma, a.eps, a.M, a.K, a.dx, a.dgamma);
-    }
+    if ((e = bwd_launch_g(a.dy, a.dy_bf16, a.N, a.packed, a.N, a.K, a.scale, a.M, a.wt, a.g, 0, s)) != hipSuccess) return e;
+    if ((e = bwd_launch_rows(a.x, a.x_bf16, a.g, a.gamma, a.eps, a.M, a.K, a.dx, a.dgamma, nullptr, 0, s)) != hipSuccess) return e;
     if (a.dw) {
-        // dW = (dy a)^T q: both operands transposed to [.][m] bf16 (m padded to ldm with
-        // zeros), then the NT GEMM over m, split over workgroups
-        const dim3 gt1(static_cast<unsigned>((a.N + 63) / 64), static_cast<unsigned>(a.ldm / 64));
-        if (a.dy_bf16) hipLaunchKernelGGL((transpose_kernel<0>), gt1, dim3(256), 0, s, a.dy, a.a, a.M, a.N, a.ldm, a.dyaT);
-        else hipLaunchKernelGGL((transpose_kernel<1>), gt1, dim3(256), 0, s, a.dy, a.a, a.M, a.N, a.ldm, a.dyaT);
-        const dim3 gt2(static_cast<unsigned>((a.K + 63) / 64), static_cast<unsigned>(a.ldm / 64));
-        hipLaunchKernelGGL((transpose_kernel<2>), gt2, dim3(256), 0, s, a.q, nullptr, a.M, a.K, a.ldm, a.qT);
-        if ((e = launch_fill_zero(a.dw, static_cast<int64_t>(a.N) * a.K, s)) != hipSuccess) return e;
-        NtGemmArgs g{};
-        g.A = a.dyaT;
-        g.a_bf16 = 1;
-        g.B = a.qT;
-        g.R = a.N;
-        g.S = a.K;
-        g.T = a.ldm;
-        g.lda = a.ldm;
-        g.ldb = a.ldm;
-        g.scale = 1.0f;
-        g.C = a.dw;
-        g.atomic = 1;
-        const int64_t tiles = static_cast<int64_t>((a.K + BS - 1) / BS) * ((a.N + BR - 1) / BR);
-        // split the tokens so that about 1024 workgroups run, each over >= 8 steps
-        int64_t splits = (1024 + tiles - 1) / tiles;
-        const int64_t max_splits = (a.ldm + 8 * BT - 1) / (8 * BT);
-        if (splits > max_splits) splits = max_splits;
-        if (splits < 1) splits = 1;
-        int64_t per = (a.ldm + splits - 1) / splits;
-        per = (per + BT - 1) / BT * BT;
-        splits = (a.ldm + per - 1) / per;
-        g.t_per_split = per;
-        const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
-        timing_begin(FAM_BWD_DW, s);
-        hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, g);
-        timing_end(FAM_BWD_DW, s);
+        if ((e = bwd_launch_qT(a.q, a.M, a.K, a.ldm, a.qT, s)) != hipSuccess) return e;
+        if ((e = bwd_launch_dw(a.dy, a.dy_bf16, a.N, a.a, a.M, a.N, a.K, a.ldm, a.qT, a.dyaT, a.dw, s)) != hipSuccess) return e;
     }
-    if (a.db) {
-        if ((e = launch_fill_zero(a.db, a.N, s)) != hipSuccess) return e;
-        if ((e = launch_col_sum(a.dy, a.dy_bf16, a.M, a.N, a.db, s)) != hipSuccess) return e;
-    }
+    if (a.db && (e = bwd_launch_db(a.dy, a.dy_bf16, a.N, a.M, a.N, a.db, s)) != hipSuccess) return e;
     return hipGetLastError();
 }
 
@@ -771,11 +851,11 @@ hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s) {
     const int64_t R = a.B * a.n_chunks;
     if (a.dgnorm_w) {
         if ((e = launch_fill_zero(a.dgnorm_w, a.D, s)) != hipSuccess) return e;
-        if ((e = launch_col_sum(a.gw_part, 0, R, a.D, a.dgnorm_w, s)) != hipSuccess) return e;
+        if ((e = launch_col_sum(a.gw_part, 0, a.D, R, a.D, a.dgnorm_w, s)) != hipSuccess) return e;
     }
     if (a.df_bias) {
         if ((e = launch_fill_zero(a.df_bias, a.D, s)) != hipSuccess) return e;
-        if ((e = launch_col_sum(a.fb_part, 0, R, a.D, a.df_bias, s)) != hipSuccess) return e;
+        if ((e = launch_col_sum(a.fb_part, 0, a.D, R, a.D, a.df_bias, s)) != hipSuccess) return e;
     }
     timing_end(FAM_BWD_SCAN, s);
     return hipGetLastError();

@@ -1196,4 +1196,178 @@ int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt,
     return MMF_OK;
 }
 
+size_t block_backward_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) {
+    if (!w || B <= 0 || T <= 0) return 0;
+    const int64_t M = B * T, D = w->i.K, F = w->gate.N, KN = std::max(D, F);
+    const int64_t ldm = (M + 63) / 64 * 64;
+    auto f4 = [](int64_t n) { return align_up(static_cast<size_t>(n) * 4); };
+    return 3 * qbuf_bytes(M, D) + qbuf_bytes(M, F) +                       // q of x, o, y1, m
+           f4(M * 3 * D) + 2 * f4(M * D) + f4(M * 2 * F) + f4(M * F) +     // ifg, o, y1, gate|up, m
+           scan_bytes(B, T, D) +                                           // forward chunk carries
+           f4(M * KN) + f4(M * F) + f4(M * 2 * F) + 2 * f4(M * D) + f4(M * 3 * D) +  // g, dm, dgu, dy1, do, d_ifg
+           align_up(static_cast<size_t>(std::max(D * D, D * F)) * 2) +    // bf16 W^T
+           2 * align_up(static_cast<size_t>(KN * ldm) * 2) +               // q^T, (dy a)^T
+           mlgru_backward_workspace_bytes(B, T, D);
+}
+
+int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
+                   const float *h0, const void *dy, mmf_dtype dy_dt, const float *dh_last, float *dx,
+                   float *dh0, const mmf_block_grads *gr, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_block(w, "block_backward");
+    if (rc) return rc;
+    if (!valid_dt(dt) || !valid_dt(dy_dt)) return set_error(MMF_EDTYPE, "block_backward: dtype %d/%d", dt, dy_dt);
+    if (B < 0 || T < 0) return set_error(MMF_ESHAPE, "block_backward: B=%lld T=%lld", (long long)B, (long long)T);
+    const int32_t D = w->i.K, F = w->gate.N;
+    if (F % 8 || F > 8192) return set_error(MMF_ESHAPE, "block_backward: F=%d must be a multiple of 8 and <= 8192", F);
+    const int64_t M = B * T;
+    static const mmf_block_grads none{};
+    const mmf_block_grads &G = gr ? *gr : none;
+    if ((h0 && !aligned16(h0)) || (dh_last && !aligned16(dh_last)) || (dh0 && !aligned16(dh0)) ||
+        (M > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(dx))))
+        return set_error(MMF_EALIGN, "block_backward: x/dy/dx/h0/dh_last/dh0 not 16-byte aligned");
+    if (M > 0 && (!x || !dy || !dx)) return set_error(MMF_EINVAL, "block_backward: NULL x, dy or dx");
+    const mmf_bitlinear *lin[7] = {&w->i, &w->f, &w->g, &w->o, &w->gate, &w->up, &w->down};
+    if (M > 0) {
+        const size_t need = block_backward_workspace_bytes(w, B, T);
+        if (!ws || ws_bytes < need) return set_error(MMF_EWORKSPACE, "block_backward: workspace %zu < %zu", ws ? ws_bytes : 0, need);
+        if (!aligned16(ws)) return set_error(MMF_EALIGN, "block_backward: workspace not 16-byte aligned");
+    }
+    if ((rc = check_device())) return rc;
+    hipError_t e = hipSuccess;
+    if (M == 0) {   // dh0 = dh_last; every parameter gradient is an empty sum
+        if (dh0 && B > 0) e = launch_copy_state(dh_last, dh0, B * D, stream);
+        for (int k = 0; k < 7 && e == hipSuccess; ++k) {
+            if (G.dw[k]) e = launch_fill_zero(G.dw[k], static_cast<int64_t>(lin[k]->N) * lin[k]->K, stream);
+            if (e == hipSuccess && G.db[k]) e = launch_fill_zero(G.db[k], lin[k]->N, stream);
+        }
+        const int32_t gk[4] = {D, D, D, F};
+        for (int k = 0; k < 4 && e == hipSuccess; ++k)
+            if (G.dgamma[k]) e = launch_fill_zero(G.dgamma[k], gk[k], stream);
+        if (e == hipSuccess && G.dgnorm_w) e = launch_fill_zero(G.dgnorm_w, D, stream);
+        if (e == hipSuccess && G.df_bias) e = launch_fill_zero(G.df_bias, D, stream);
+        return e == hipSuccess ? MMF_OK : hip_error(e, "block_backward fill");
+    }
+    const bool bf = dt == MMF_BF16, dyb = dy_dt == MMF_BF16;
+    const int64_t ldm = (M + 63) / 64 * 64, KN = std::max(D, F);
+    Carver c(ws);
+    const QBuf qx = take_qbuf(c, M, D), qo = take_qbuf(c, M, D), qy = take_qbuf(c, M, D), qm = take_qbuf(c, M, F);
+    void *ifg = c.take<char>(static_cast<size_t>(M * 3 * D) * 4);
+    void *o = c.take<char>(static_cast<size_t>(M * D) * 4);
+    void *y1 = c.take<char>(static_cast<size_t>(M * D) * 4);
+    float *gu = c.take<float>(static_cast<size_t>(M * 2 * F) * 4);
+    void *m = c.take<char>(static_cast<size_t>(M * F) * 4);
+    char *scan_ws = c.take<char>(scan_bytes(B, T, D));
+    float *g = c.take<float>(static_cast<size_t>(M * KN) * 4);
+    float *dm = c.take<float>(static_cast<size_t>(M * F) * 4);
+    float *dgu = c.take<float>(static_cast<size_t>(M * 2 * F) * 4);
+    float *dy1 = c.take<float>(static_cast<size_t>(M * D) * 4);
+    float *dO = c.take<float>(static_cast<size_t>(M * D) * 4);
+    float *d_ifg = c.take<float>(static_cast<size_t>(M * 3 * D) * 4);
+    uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(std::max(D * D, D * F)) * 2);
+    uint16_t *qT = c.take<uint16_t>(static_cast<size_t>(KN * ldm) * 2);
+    uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(KN * ldm) * 2);
+    const size_t mws_bytes = mlgru_backward_workspace_bytes(B, T, D);
+    void *mws = c.take<char>(mws_bytes);
+#define MMF_TRY(expr, what) do { if ((e = (expr)) != hipSuccess) return hip_error(e, "block_backward " what); } while (0)
+
+    // ---- forward, recomputed: i|f|g, the MLGRU with its gate (o stored), o_proj + x -> y1,
+    //      gate and up pre-activations (fp32), m = SiLU(gate)*up
+    const Seg sifg[3] = {seg_of(w->i, 0, 0), seg_of(w->f, D, D), seg_of(w->g, 2 * D, 2 * D)};
+    const Seg so = seg_of(w->o, 0, 0);
+    const Seg sgu[2] = {seg_of(w->gate, 0, 0), seg_of(w->up, F, F)};
+    MMF_TRY(quantize(x, bf, w->i.norm_w, w->i.eps, M, D, qx, nullptr, stream), "quant x");
+    MMF_TRY(gemm(qx, M, D, sifg, 3, EPI_STORE, ifg, 3 * D, bf, nullptr, 0, nullptr, 0, FAM_GEMM_IFG, stream), "ifg");
+    {
+        ScanArgs sa{};
+        sa.ifg = ifg;
+        sa.ifg_bf16 = bf;
+        sa.f_bias = w->f_bias;
+        sa.f_lower = w->f_lower;
+        sa.h0 = h0;
+        sa.gnorm_w = w->gnorm_w;
+        sa.eps = w->eps;
+        sa.gate_mode = w->gate_mode;
+        sa.B = B;
+        sa.T = T;
+        sa.D = D;
+        sa.chunk = kScanChunk;
+        sa.n_chunks = static_cast<int32_t>(scan_chunks(T));
+        if (sa.n_chunks > 1) {
+            Carver sc(scan_ws);
+            const size_t n = static_cast<size_t>(B * sa.n_chunks * D) * 4;
+            sa.hloc = sc.take<float>(n);
+            sa.pf = sc.take<float>(n);
+            sa.hin = sc.take<float>(n);
+        }
+        sa.out = o;
+        sa.out_bf16 = bf;
+        MMF_TRY(launch_scan(sa, stream), "scan");
+    }
+    MMF_TRY(quantize(o, bf, w->o.norm_w, w->o.eps, M, D, qo, nullptr, stream), "quant o");
+    MMF_TRY(gemm(qo, M, D, &so, 1, EPI_RESID, y1, D, bf, x, D, nullptr, 0, FAM_GEMM_O, stream), "o_proj");
+    MMF_TRY(quantize(y1, bf, w->gate.norm_w, w->gate.eps, M, D, qy, nullptr, stream), "quant y1");
+    MMF_TRY(gemm(qy, M, D, sgu, 2, EPI_STORE, gu, 2 * F, false, nullptr, 0, nullptr, 0, FAM_GEMM_OTHER, stream), "gate|up");
+    MMF_TRY(launch_glu_product(gu, M, F, m, bf, stream), "glu product");
+    MMF_TRY(quantize(m, bf, w->down.norm_w, w->down.eps, M, F, qm, nullptr, stream), "quant m");
+
+    // ---- down: dm = down^T(dy) through the straight-through BitLinear backward
+    MMF_TRY(bwd_launch_g(dy, dyb, D, w->down.packed, D, F, w->down.scale, M, wt, g, 0, stream), "down g");
+    MMF_TRY(bwd_launch_rows(m, bf, g, w->down.norm_w, w->down.eps, M, F, dm, G.dgamma[3], nullptr, 0, stream), "down rows");
+    if (G.dw[6]) {
+        MMF_TRY(bwd_launch_qT(qm.q, M, F, ldm, qT, stream), "down qT");
+        MMF_TRY(bwd_launch_dw(dy, dyb, D, qm.a, M, D, F, ldm, qT, dyaT, G.dw[6], stream), "down dw");
+    }
+    if (G.db[6]) MMF_TRY(bwd_launch_db(dy, dyb, D, M, D, G.db[6], stream), "down db");
+    // ---- the GLU's product, then gate and up (one g for both: they share the input y1);
+    //      dy1 = dy + gate^T(dgate) + up^T(dup)
+    MMF_TRY(launch_glu_product_bwd(gu, dm, M, F, dgu, stream), "glu product backward");
+    MMF_TRY(bwd_launch_g(dgu, 0, 2 * F, w->gate.packed, F, D, w->gate.scale, M, wt, g, 0, stream), "gate g");
+    MMF_TRY(bwd_launch_g(dgu + F, 0, 2 * F, w->up.packed, F, D, w->up.scale, M, wt, g, 1, stream), "up g");
+    MMF_TRY(bwd_launch_rows(y1, bf, g, w->gate.norm_w, w->gate.eps, M, D, dy1, G.dgamma[2], dy, dyb ? 1 : 2, stream), "gate|up rows");
+    if (G.dw[4] || G.dw[5]) MMF_TRY(bwd_launch_qT(qy.q, M, D, ldm, qT, stream), "gate|up qT");
+    if (G.dw[4]) MMF_TRY(bwd_launch_dw(dgu, 0, 2 * F, qy.a, M, F, D, ldm, qT, dyaT, G.dw[4], stream), "gate dw");
+    if (G.dw[5]) MMF_TRY(bwd_launch_dw(dgu + F, 0, 2 * F, qy.a, M, F, D, ldm, qT, dyaT, G.dw[5], stream), "up dw");
+    if (G.db[4]) MMF_TRY(bwd_launch_db(dgu, 0, 2 * F, M, F, G.db[4], stream), "gate db");
+    if (G.db[5]) MMF_TRY(bwd_launch_db(dgu + F, 0, 2 * F, M, F, G.db[5], stream), "up db");
+    // ---- o_proj: do = o^T(dy1)
+    MMF_TRY(bwd_launch_g(dy1, 0, D, w->o.packed, D, D, w->o.scale, M, wt, g, 0, stream), "o g");
+    MMF_TRY(bwd_launch_rows(o, bf, g, w->o.norm_w, w->o.eps, M, D, dO, G.dgamma[1], nullptr, 0, stream), "o rows");
+    if (G.dw[3]) {
+        MMF_TRY(bwd_launch_qT(qo.q, M, D, ldm, qT, stream), "o qT");
+        MMF_TRY(bwd_launch_dw(dy1, 0, D, qo.a, M, D, D, ldm, qT, dyaT, G.dw[3], stream), "o dw");
+    }
+    if (G.db[3]) MMF_TRY(bwd_launch_db(dy1, 0, D, M, D, G.db[3], stream), "o db");
+#undef MMF_TRY
+    // ---- the MLGRU with its output gate
+    {
+        mmf_mlgru_args ma{};
+        ma.ifg = ifg;
+        ma.ifg_dt = dt;
+        ma.f_bias = w->f_bias;
+        ma.h0 = h0;
+        ma.gnorm_w = w->gnorm_w;
+        ma.eps = w->eps;
+        ma.gate_mode = w->gate_mode;
+        ma.out_dt = dt;
+        ma.B = B;
+        ma.T = T;
+        ma.D = D;
+        ma.f_lower = w->f_lower;
+        if ((rc = mlgru_backward(&ma, dO, MMF_F32, dh_last, d_ifg, dh0, G.dgnorm_w, G.df_bias, mws, mws_bytes, stream)))
+            return rc;
+    }
+    // ---- i, f, g (one g for the three: they share the input x); dx = dy1 + sum_k k^T(d_k)
+#define MMF_TRY(expr, what) do { if ((e = (expr)) != hipSuccess) return hip_error(e, "block_backward " what); } while (0)
+    for (int k = 0; k < 3; ++k)
+        MMF_TRY(bwd_launch_g(d_ifg + k * D, 0, 3 * D, lin[k]->packed, D, D, lin[k]->scale, M, wt, g, k > 0, stream), "ifg g");
+    MMF_TRY(bwd_launch_rows(x, bf, g, w->i.norm_w, w->i.eps, M, D, dx, G.dgamma[0], dy1, 2, stream), "ifg rows");
+    if (G.dw[0] || G.dw[1] || G.dw[2]) MMF_TRY(bwd_launch_qT(qx.q, M, D, ldm, qT, stream), "ifg qT");
+    for (int k = 0; k < 3; ++k) {
+        if (G.dw[k]) MMF_TRY(bwd_launch_dw(d_ifg + k * D, 0, 3 * D, qx.a, M, D, D, ldm, qT, dyaT, G.dw[k], stream), "ifg dw");
+        if (G.db[k]) MMF_TRY(bwd_launch_db(d_ifg + k * D, 0, 3 * D, M, D, G.db[k], stream), "ifg db");
+    }
+#undef MMF_TRY
+    return MMF_OK;
+}
+
 }  // extern "C"

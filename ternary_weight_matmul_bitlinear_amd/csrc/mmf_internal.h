@@ -439,6 +439,19 @@ hipError_t launch_scan_carries(const ScanArgs &a, hipStream_t s);
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s);
 hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
+// backward pieces (backward.hip): dy [M][ldy] of which the first N columns are used
+hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *packed, int32_t N,
+                        int32_t K, float scale, int64_t M, uint16_t *wt, float *g, int accumulate,
+                        hipStream_t s);   // g (+)= scale * dy T; wt: [K][N] bf16 scratch
+hipError_t bwd_launch_rows(const void *x, int x_bf16, const float *g, const float *gamma, float eps,
+                           int64_t M, int32_t K, float *dx, float *dgamma, const void *res, int res_kind,
+                           hipStream_t s);   // res_kind 0: none, 1: bf16, 2: fp32 residual gradient
+hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uint16_t *qT, hipStream_t s);
+hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int32_t N,
+                         int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT, float *dw, hipStream_t s);
+hipError_t bwd_launch_db(const void *dy, int dy_bf16, int64_t ldy, int64_t M, int32_t N, float *db, hipStream_t s);
+hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s);
+hipError_t launch_glu_product_bwd(const float *gu, const float *dm, int64_t M, int32_t F, float *dgu, hipStream_t s);
 hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);

@@ -187,3 +187,136 @@ def test_mlgru_backward_empty(orc):
     torch.cuda.synchronize()
     assert np.array_equal(host(got["dh0"]), dl.astype(np.float32).astype(np.float64))
     assert float(got["df_bias"].abs().max()) == 0.0
+
+
+# ------------------------------------------------------------------ block backward
+
+def _block(orc, seed, D, F, with_extras):
+    """A device block (gains and biases when with_extras; i|f|g and gate|up share their gains)
+    and the oracle's weight dict (q, scale, gamma, bias) for the same ternary weights."""
+    lat = synth.layer_latents(synth.Workload("bb", D=D, F=F, B=1, T=1, seed=seed), 0)
+    gains = {}
+    if with_extras:
+        gx = (1 + 0.2 * synth.gaussian(seed + 50, (D,))).astype(np.float32)
+        ggu = (1 + 0.2 * synth.gaussian(seed + 51, (D,))).astype(np.float32)
+        gains = {"i": gx, "f": gx, "g": gx, "gate": ggu, "up": ggu,
+                 "o": (1 + 0.2 * synth.gaussian(seed + 52, (D,))).astype(np.float32),
+                 "down": (1 + 0.2 * synth.gaussian(seed + 53, (F,))).astype(np.float32)}
+    lins, W = {}, {}
+    dev_gain = {}   # one device tensor per distinct gain: the block shares them by pointer
+    for j, k in enumerate(api.BLOCK_LINEARS):
+        q, s = orc.ternarize(lat[k])
+        g = gains.get(k)
+        b = (0.05 * synth.gaussian(seed + 60 + j, (q.shape[0],))).astype(np.float32) if with_extras else None
+        gd = None
+        if g is not None:
+            gd = dev_gain.setdefault(id(g), dev(g))
+        lins[k] = api.TernaryLinear.from_ternary(q, s, "cuda", norm_w=gd, bias=b)
+        W[k] = (q, s, g, b)
+    kw = {}
+    if with_extras:
+        kw = dict(f_bias=synth.gaussian(seed + 70, (D,), 0.5),
+                  gnorm_w=(1 + 0.2 * synth.gaussian(seed + 71, (D,))).astype(np.float32),
+                  f_lower=orc.hgrn_lower_bounds(synth.gaussian(seed + 72, (3, D)))[1].astype(np.float32))
+    blk = api.Block(**lins, **{k: (dev(v) if v is not None else None) for k, v in kw.items()})
+    return blk, W, kw
+
+
+def _grad_check(got, ref, tol, what):
+    """Independent-run criterion (as for the forward's end-to-end runs): the recomputed
+    forward takes its own int8 decisions (a near-tie can flip one code against the oracle's
+    fp64 run) and every gradient passes through up to three bf16 roundings of matrix-core
+    operands, so p99.9 of the element error (relative to |ref| + the row's rms) and every
+    row's norm-wise error are held to tol, and the maximum to 5 tol."""
+    got = np.atleast_2d(np.asarray(got, np.float64))
+    ref = np.atleast_2d(np.asarray(ref, np.float64))
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+    ratio = np.abs(got - ref) / (np.abs(ref) + rms + 1e-30)
+    p999 = float(np.quantile(ratio, 0.999))
+    rowerr = float(np.max(np.linalg.norm(got - ref, axis=-1) / (np.linalg.norm(ref, axis=-1) + 1e-30)))
+    assert p999 <= tol and rowerr <= tol and ratio.max() <= 5 * tol, \
+        f"{what}: p99.9 {p999:.3e}, row {rowerr:.3e}, max {ratio.max():.3e} (tol {tol})"
+    return p999, rowerr, float(ratio.max())
+
+
+def _block_checks(got, ref, D, tol, rows=None, what=""):
+    """Every block gradient against the oracle's (rows: the dx rows compared)."""
+    dx = host(got["dx"]).reshape(-1, D)
+    worst = {"dx": _grad_check(dx if rows is None else dx[rows], ref["dx"].reshape(-1, D), tol, what + "dx"),
+             "dh0": _grad_check(host(got["dh0"]), ref["dh0"], tol, what + "dh0")}
+    for k in api.BLOCK_LINEARS:
+        worst["dw " + k] = _grad_check(host(got["dw"][k]), ref["dw"][k], tol, f"{what}dw[{k}]")
+        worst["db " + k] = _grad_check(host(got["db"][k]), ref["db"][k], tol, f"{what}db[{k}]")
+    groups = {"x": ("i", "f", "g"), "o": ("o",), "y1": ("gate", "up"), "m": ("down",)}
+    for name, ks in groups.items():
+        worst["dgamma " + name] = _grad_check(host(got["dgamma"][name]), sum(ref["dgamma"][k] for k in ks),
+                                              tol, f"{what}dgamma[{name}]")
+    worst["dgnorm_w"] = _grad_check(host(got["dgnorm_w"]), ref["dgnorm_w"], tol, what + "dgnorm_w")
+    worst["df_bias"] = _grad_check(host(got["df_bias"]), ref["df_bias"], tol, what + "df_bias")
+    note("  worst (p99.9, row, max): " + ", ".join(f"{k} {v[2]:.1e}" for k, v in worst.items() if v[2] > 2e-3))
+
+
+BB_TOL = 2e-2   # the bf16 tolerance: the backward's contractions run on bf16 matrix cores
+
+
+@pytest.mark.parametrize("gate_mode", [0, 1], ids=["swish_rmsnorm", "sigmoid"])
+@pytest.mark.parametrize("bf", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D,F,extras", [(2, 37, 256, 704, True), (1, 16, 128, 384, False),
+                                            (3, 50, 512, 1408, True)],
+                         ids=["B2T37D256", "B1T16D128-plain", "B3T50D512"])
+def test_block_backward_parity(orc, B, T, D, F, extras, bf, gate_mode):
+    note(f"block_backward B={B} T={T} D={D} F={F} extras={extras} bf16={bf} gate={gate_mode}")
+    seed = B * 100 + T + D
+    blk, W, kw = _block(orc, seed, D, F, extras)
+    blk.gate_mode = gate_mode
+    x = synth.gaussian(seed + 1, (B, T, D))
+    dy = synth.gaussian(seed + 2, (B, T, D))
+    if bf:
+        x, dy = synth.round_to_bf16(x), synth.round_to_bf16(dy)
+    h0 = synth.gaussian(seed + 3, (B, D)) if extras else None
+    dl = synth.gaussian(seed + 4, (B, D)) if extras else None
+    dt = torch.bfloat16 if bf else torch.float32
+    got = api.block_backward(blk, dev(x, dt), dev(dy, dt), h0=dev(h0) if h0 is not None else None,
+                             dh_last=dev(dl) if dl is not None else None)
+    torch.cuda.synchronize()
+    ref = orc.block_backward(x, W, dy.astype(np.float64), gate_mode=gate_mode, resid_bf16=bf,
+                             h0=h0, dh_last=dl, **kw)
+    _block_checks(got, ref, D, BB_TOL)
+
+
+def test_block_backward_full_size_prefix(orc):
+    """The 370M block at the benchmark's size (8 x 2048 tokens, bf16), with dy non-zero only
+    on the first 64 tokens of every sequence and no final-state gradient: the reverse
+    recurrence then carries nothing from the later tokens and their rows contribute nothing
+    to the parameter gradients, so every gradient equals the oracle's on the 8 x 64 prefix,
+    and dx is zero beyond it."""
+    w = synth.WORKLOADS["370M-block"]
+    B, T, D, F, P = w.B, w.T, w.D, w.F, 64
+    note(f"block_backward full size B={B} T={T} D={D} F={F}, dy on the first {P} tokens")
+    blk, W, kw = _block(orc, 4321, D, F, True)
+    x = synth.activations(w)
+    dy = np.zeros((B, T, D), np.float32)
+    dy[:, :P] = synth.round_to_bf16(synth.gaussian(4322, (B, P, D)))
+    h0 = synth.gaussian(4323, (B, D))
+    got = api.block_backward(blk, dev(x, torch.bfloat16), dev(dy, torch.bfloat16), h0=dev(h0))
+    torch.cuda.synchronize()
+    ref = orc.block_backward(x[:, :P], W, dy[:, :P].astype(np.float64), resid_bf16=True, h0=h0, **kw)
+    dx = host(got["dx"])
+    assert float(np.abs(dx[:, P:]).max()) == 0.0, "dx beyond the prefix"
+    rows = (np.arange(B)[:, None] * T + np.arange(P)[None, :]).reshape(-1)
+    got["dx"] = got["dx"].reshape(B * T, D)
+    _block_checks(got, ref, D, BB_TOL, rows=rows)
+
+
+def test_block_backward_empty(orc):
+    """T = 0: dh0 = dh_last and every parameter gradient is zero."""
+    blk, _, _ = _block(orc, 7, 128, 384, False)
+    dl = synth.gaussian(8, (2, 128))
+    got = api.block_backward(blk, torch.empty((2, 0, 128), device="cuda"),
+                             torch.empty((2, 0, 128), device="cuda"), dh_last=dev(dl))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got["dh0"]), dl.astype(np.float32).astype(np.float64))
+    for k in api.BLOCK_LINEARS:
+        assert float(got["dw"][k].abs().max()) == 0.0 and float(got["db"][k].abs().max()) == 0.0

@@ -11,9 +11,9 @@ with its launch durations from HIP events recorded on the launch stream during t
 steps; `cpu_baseline` is the CPU oracle timed on a bounded causal sample of the same
 workload.  `extra_workloads` carries the other shapes measured the same way: the 2.7B block
 (16 x 2048 tokens), the 370M block (8 x 2048 tokens) and the 24-layer 1.3B decode stack at
-batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches), then the
-backward kernels (straight-through BitLinear backward on bf16 MFMA, MLGRU backward) at the
-370M and 2.7B block sizes.
+batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches), then a
+block's backward (block_backward: forward recomputed, every gradient; straight-through
+BitLinear backwards on bf16 MFMA) at the 370M and 2.7B block sizes.
 """
 from __future__ import annotations
 
@@ -526,10 +526,11 @@ def decode_kernel_sweep(B: int, D: int, F: int, V: int) -> list:
 # ------------------------------------------------------------------ backward
 
 def bench_backward(w, args, orc) -> dict:
-    """Backward of one block-sized training step's two fused kernels at the block workload's
-    size: the straight-through BitLinear backward of the gate projection (K = D, N = F:
-    g = s_w dy T and dW = (dy a)^T q_x on bf16 MFMA, dx with the RMSNorm backward, dgamma,
-    db) and the MLGRU + output-gate backward (B x T x D).  bf16 inputs, fp32 gradients."""
+    """One block's backward at the block workload's size (block_backward): the forward
+    recomputed on the prefill kernels, then every gradient -- the seven straight-through
+    BitLinear backwards (g = s_w dy T and dW = (dy a)^T q_x on bf16 MFMA, dx with the
+    RMSNorm backward, dgamma, db), the GLU product's and the MLGRU + output gate's
+    backwards.  bf16 activations and dy, fp32 gradients, layer 0's weights."""
     import numpy as np
     import torch
 
@@ -537,73 +538,64 @@ def bench_backward(w, args, orc) -> dict:
 
     M, D, F = w.B * w.T, w.D, w.F
     lat = synth.layer_latents(w, 0)
-    lin = api.TernaryLinear.from_latent(lat["gate"], "cuda")
-    x = torch.from_numpy(synth.activations(w).reshape(M, D)).to("cuda").to(torch.bfloat16)
-    dy = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 101, (M, F)))).to("cuda").to(torch.bfloat16)
-    ifg = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 102, (w.B, w.T, 3 * D), 1.5))).to("cuda").to(torch.bfloat16)
-    dout = torch.from_numpy(synth.round_to_bf16(synth.gaussian(w.seed + 103, (w.B, w.T, D)))).to("cuda").to(torch.bfloat16)
-    fb = torch.full((D,), float(w.f_bias or 0.0), device="cuda")
-    gw = torch.ones(D, device="cuda")
-    h0 = torch.zeros((w.B, D), device="cuda")
+    fb = np.full(D, w.f_bias, np.float32) if w.f_bias else None
+    blk = api.Block.from_latents(lat, "cuda", f_bias=fb)
+    x = torch.from_numpy(synth.activations(w)).to("cuda").to(torch.bfloat16)
+    dy_np = synth.round_to_bf16(synth.gaussian(w.seed + 101, (w.B, w.T, D)))
+    dy = torch.from_numpy(dy_np).to("cuda").to(torch.bfloat16)
 
     def step(_i):
-        api.bitlinear_backward(lin, x, dy)
-        api.mlgru_backward(ifg, dout, f_bias=fb, h0=h0, gnorm_w=gw)
+        api.block_backward(blk, x, dy)
 
     spin_up(lambda: step(0), args.spin_up)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     steps = args.steps
-    wall, q = timed_events(["bwd_g", "bwd_dw", "bwd_scan"], step, steps)
-    ops = 2.0 * M * F * D
-    scan_bytes = M * D * (4 * 2 + 12.0)   # read i|f|g and dout (bf16), write d_ifg (fp32)
+    fams = ["bwd_g", "bwd_dw", "bwd_scan", "quant", "gemm_ifg", "gemm_o", "gemm", "scan"]
+    wall, q = timed_events(fams, step, steps)
+    ops = 2.0 * M * D * (4 * D + 3 * F)          # the seven contractions of g (and of dW) per step
     kern = {}
     for fam, (n, ms) in q.items():
         if not n:
             continue
-        d = {"launches_per_step": n / steps, "us_per_launch": ms / n * 1e3}
-        sec = ms / n * 1e-3
-        if fam == "bwd_scan":
-            d.update(bound="hbm", algorithmic_bytes=scan_bytes, gbs=scan_bytes / sec / 1e9,
-                     hbm_frac=scan_bytes / sec / 1e9 / PEAK_HBM_GBS)
-        else:
-            d.update(bound="mfma", algorithmic_flops=ops, tflops=ops / sec / 1e12,
+        d = {"launches_per_step": n / steps, "ms_per_step": ms / steps}
+        sec = ms / steps * 1e-3
+        if fam in ("bwd_g", "bwd_dw"):
+            d.update(bound="mfma", algorithmic_flops_per_step=ops, tflops=ops / sec / 1e12,
                      mfma_frac=ops / sec / 1e12 / PEAK_BF16_TFLOPS)
+        elif fam == "bwd_scan":
+            nb = M * D * (4 * 2 + 12.0)   # read i|f|g (bf16) and do (fp32 counted as 2 x bf16), write d_ifg
+            d.update(bound="hbm", algorithmic_bytes_per_step=nb, gbs=nb / sec / 1e9,
+                     hbm_frac=nb / sec / 1e9 / PEAK_HBM_GBS)
         kern[fam] = d
     n_g, ms_g = q["bwd_g"]
-    tf = ops / (ms_g / n_g * 1e-3) / 1e12 if n_g else None
+    tf = ops / (ms_g / steps * 1e-3) / 1e12 if n_g else None
     res = {"workload": f"{w.name} backward", "value": M / (wall * 1e-3), "unit": "tokens/s",
            "ms_per_step": wall, "steps": steps,
            "config": {"workload": f"{w.name} backward", "B": w.B, "T": w.T, "D": D, "F": F,
-                      "bitlinear": f"gate projection K={D} N={F}", "inputs": "bf16", "gradients": "fp32"},
-           "roofline": {"kernel": "bwd_g: g = s_w dy T (bf16 MFMA, ternary codes unpacked to bf16)",
+                      "step": "block_backward (forward recomputed, every gradient)",
+                      "inputs": "bf16", "gradients": "fp32"},
+           "roofline": {"kernel": "bwd_g: the seven g = s_w dy T contractions of a step (bf16 MFMA)",
                         "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / PEAK_BF16_TFLOPS if tf else None,
-                        "traffic": traffic("bwd_g", f"{w.name}-backward", ("backward.hip",)),
-                        "algorithmic_flops_per_launch": ops},
+                        "frac": tf / PEAK_BF16_TFLOPS if tf else None, "traffic": None,
+                        "algorithmic_flops_per_step": ops, "launches_per_step": n_g / steps},
            "kernels": kern}
     if orc is not None:
-        # oracle on a bounded sample: the BitLinear backward of 32 tokens (every gradient of
-        # that slice) and the MLGRU backward of one 256-token sequence
-        Ms, Ts = 32, min(256, w.T)
-        qg, sg = orc.ternarize(lat["gate"])
-        xs = x[:Ms].float().cpu().numpy()
-        dys = dy[:Ms].float().cpu().numpy().astype(np.float64)
+        # oracle on a bounded sample: the block backward of a causal prefix of one sequence
+        P = 32 if D <= 1024 else 8
+        W = {}
+        for k in ("i", "f", "g", "o", "gate", "up", "down"):
+            W[k] = orc.ternarize(lat[k])
+        xs = synth.activations(w)[:1, :P]
         t = time.perf_counter()
-        orc.bitlinear_backward(xs, qg, sg, dys)
-        t_bl = time.perf_counter() - t
-        ifs = ifg[:1, :Ts].float().cpu().numpy().astype(np.float64)
-        dos = dout[:1, :Ts].float().cpu().numpy().astype(np.float64)
-        t = time.perf_counter()
-        orc.mlgru_backward(ifs, dos, f_bias=fb.cpu().numpy(), gnorm_w=gw.cpu().numpy())
-        t_mg = time.perf_counter() - t
-        res["cpu_baseline"] = {"value": 1.0 / (t_bl / Ms + t_mg / Ts), "unit": "tokens/s",
-                               **cpu_info(orc), "kind": "oracle",
-                               "sample": f"BitLinear backward of {Ms} tokens ({t_bl:.2f} s) + "
-                                         f"MLGRU backward of 1 x {Ts} tokens ({t_mg:.3f} s), fp64"}
-    log(f"{w.name} backward: {wall:.3f} ms/step; bwd_g {kern.get('bwd_g', {}).get('mfma_frac', 0):.3f} of bf16 peak")
-    del x, dy, ifg, dout
+        orc.block_backward(xs, W, dy_np[:1, :P].astype(np.float64), f_bias=fb, resid_bf16=True)
+        dt = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": P / dt, "unit": "tokens/s", **cpu_info(orc), "kind": "oracle",
+                               "sample": f"block backward of the first {P} tokens of one sequence "
+                                         f"({dt:.2f} s), fp64"}
+    log(f"{w.name} backward: {wall:.3f} ms/step; bwd_g {tf / PEAK_BF16_TFLOPS if tf else 0:.3f} of bf16 peak")
+    del x, dy
     return res
 
 

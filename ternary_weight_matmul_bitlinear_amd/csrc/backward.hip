@@ -100,6 +100,11 @@ __device__ __forceinline__ void load16(const void *base, int64_t idx, int valid,
 // vectors, 32 elements of A and of B per thread) are issued before the current step's 8
 // MFMAs per wave and written to the other buffer after them; one barrier per step.  Rows
 // are padded to 72 elements (144 bytes), so every MFMA operand is one 16-byte LDS read.
+// The contraction may be cut into segments of seg_steps steps with a scale of their own (the
+// weight scales of linears that share an input, stacked along t): the accumulators are
+// multiplied by seg_ratio[j] = scale_j / scale_(j+1) when segment j + 1 begins, and by
+// `scale` (the last segment's) at the end.  The output rows may be cut into up to three
+// matrices of c_rows rows each (C, C1, C2; a NULL one is not written).
 struct NtGemmArgs {
     const void *A;
     int32_t a_bf16;
@@ -109,9 +114,13 @@ struct NtGemmArgs {
     int64_t T;              // contraction length
     int64_t lda, ldb;       // row strides in elements
     float scale;
-    float *C;               // [R][S]
+    float *C;               // [R][S] (or its first c_rows rows)
     int64_t t_per_split;    // multiple of BT (T when not split)
     int32_t atomic;         // 0: C = v; 1: C += v with fp32 atomics (split); 2: C += v
+    int32_t seg_steps;      // contraction steps per segment (0: one segment)
+    float seg_ratio[2];
+    int64_t c_rows;         // rows per output matrix (0: all in C)
+    float *C1, *C2;
 };
 
 constexpr int BT = 64;           // contraction step (four 16-deep MFMA steps)
@@ -268,13 +277,27 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
         store_step(0, ra0, rb0);
     }
     lds_barrier();
+    // a new contraction segment begins at step st: rescale what was accumulated so far
+    auto seg_edge = [&](int st) {
+        if (p.seg_steps && st > 0 && st % p.seg_steps == 0) {
+            const float r = p.seg_ratio[st / p.seg_steps - 1];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] *= r;
+        }
+    };
     for (int st = 0; st < nsteps; st += 2) {
         if (st + 2 < nsteps) load_step(tstep(st + 2), ra0, rb0);
+        seg_edge(st);
         compute(0);
         if (st + 1 < nsteps) store_step(1, ra1, rb1);
         lds_barrier();
         if (st + 1 < nsteps) {
             if (st + 3 < nsteps) load_step(tstep(st + 3), ra1, rb1);
+            seg_edge(st + 1);
             compute(1);
             if (st + 2 < nsteps) store_step(0, ra0, rb0);
             lds_barrier();
@@ -289,9 +312,20 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
             if (col >= p.S) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = r0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                int64_t row = r0 + wr * 64 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                 if (row < p.R) {
-                    float *o = p.C + row * p.S + col;
+                    float *cm = p.C;
+                    if (p.c_rows) {
+                        if (row >= 2 * p.c_rows) {
+                            cm = p.C2;
+                            row -= 2 * p.c_rows;
+                        } else if (row >= p.c_rows) {
+                            cm = p.C1;
+                            row -= p.c_rows;
+                        }
+                        if (!cm) continue;
+                    }
+                    float *o = cm + row * p.S + col;
                     if (p.atomic == 1) atomicAdd(o, acc[i][j][e] * p.scale);
                     else if (p.atomic == 2) *o += acc[i][j][e] * p.scale;
                     else *o = acc[i][j][e] * p.scale;
@@ -300,10 +334,15 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
         }
 }
 
-// W^T as bf16 values -1/0/1: out[k][n] for the packed [N][K/16] matrix; thread per (k, 8
-// consecutive n), one 16-byte store (N % 8 == 0).
+__device__ __forceinline__ float silu_grad(float z) {
+    const float s = sigmoidf_(z);
+    return s * (1.0f + z * (1.0f - s));
+}
+
+// W^T as bf16 values -1/0/1: out[k][n] (row stride ldo) for the packed [N][K/16] matrix;
+// thread per (k, 8 consecutive n), one 16-byte store (N % 8 == 0).
 __global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, int32_t N, int32_t K,
-                                                        uint16_t *out) {
+                                                        uint16_t *out, int64_t ldo) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int ng = N / 8;
     if (i >= static_cast<int64_t>(K) * ng) return;
@@ -315,78 +354,149 @@ __global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, 
         const int code = static_cast<int>((packed[static_cast<int64_t>(n0 + e) * KW + k / 16] >> sh) & 3u);
         v[e] = code == 2 ? 0x3F80u : (code == 0 ? 0xBF80u : 0u);
     }
-    *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(k) * N + n0) =
+    *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(k) * ldo + n0) =
         make_uint4(v[0] | (uint32_t(v[1]) << 16), v[2] | (uint32_t(v[3]) << 16),
                    v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
 }
 
+// Column sums folded into a transpose: out[j][c - j*cols] += sum_m src[m][c] for the columns
+// of segment j (up to three outputs; a NULL one is skipped), fp32 atomics into zeroed arrays.
+struct ColSums {
+    float *o[3];
+    int32_t cols;
+};
+
 // dst[c][m] = bf16(src[m][c] * (scale ? scale[m] : 1)) for m < M, 0 for M <= m < ldm (the
-// padding of every destination row); src [M][lds] bf16, fp32 (SRC 0/1) or int8 codes (SRC 2).
-// 64 x 64 tiles through LDS: rows read and columns written as contiguous runs.
+// padding of every destination row), and the column sums of the unscaled src (if any output
+// is given).  src [M][lds]: bf16, fp32 or int8 codes (SRC 0/1/2).  A workgroup takes 64
+// columns and 256 rows as four 64 x 64 tiles through LDS: rows are read as 16-byte vectors
+// (when `vec`: every row 16-byte aligned) and columns written as 32-byte runs.
 template <int SRC>
-__global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t lds, const float *scale,
-                                                        int64_t M, int32_t C, int64_t ldm, uint16_t *dst) {
+__global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t lds, int32_t vec,
+                                                        const float *scale, int64_t M, int32_t C,
+                                                        int64_t ldm, uint16_t *dst, ColSums cs) {
+    constexpr int ES = SRC == 0 ? 2 : (SRC == 1 ? 4 : 1);   // bytes per element
+    constexpr int EV = 16 / ES;                              // elements per 16-byte vector
+    constexpr int VR = 64 / EV;                              // vectors per tile row
+    constexpr int NV = 64 * VR / 256;                        // vectors per thread per tile
     __shared__ float tile[64][65];
+    __shared__ float sc[64];
     const int tid = threadIdx.x;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 64;
     const int c0 = blockIdx.x * 64;
-    {
-        const int r = tid >> 2, cc = 16 * (tid & 3);
-        const int64_t m = m0 + r;
-        const float sc = m < M ? (scale ? scale[m] : 1.0f) : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = c0 + cc + e;
-            float v = 0.0f;
-            if (m < M && c < C) {
-                const int64_t idx = m * lds + c;
-                if constexpr (SRC == 0) v = bf16_bits_to_f32(static_cast<const uint16_t *>(src)[idx]);
-                else if constexpr (SRC == 1) v = static_cast<const float *>(src)[idx];
-                else v = static_cast<float>(static_cast<const int8_t *>(src)[idx]);
-            }
-            tile[r][cc + e] = v * sc;
+    const bool sums = cs.o[0] || cs.o[1] || cs.o[2];
+    float csum = 0.0f;
+    for (int tm = 0; tm < 4; ++tm) {
+        const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 256 + 64 * tm;
+        if (m0 >= ldm) break;
+        if (tid < 64) {
+            const int64_t m = m0 + tid;
+            sc[tid] = m < M ? (scale ? scale[m] : 1.0f) : 0.0f;
         }
-    }
-    __syncthreads();
-    {
-        const int c = c0 + (tid >> 2), mm = 16 * (tid & 3);
-        if (c < C && m0 + mm < ldm) {
+        const bool full = vec && m0 + 64 <= M && c0 + 64 <= C;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int v = tid + 256 * j, r = v / VR, cc = (v % VR) * EV;
+            const int64_t m = m0 + r;
+            float f[EV];
+            if (full) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const char *>(src) +
+                                                                 (m * lds + c0 + cc) * ES);
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    if constexpr (SRC == 0) f[e] = bf16_bits_to_f32(static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2))));
+                    else if constexpr (SRC == 1) f[e] = __uint_as_float(u[e]);
+                    else f[e] = static_cast<float>(static_cast<int8_t>(u[e / 4] >> (8 * (e % 4))));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    const int c = c0 + cc + e;
+                    f[e] = 0.0f;
+                    if (m < M && c < C) {
+                        const int64_t idx = m * lds + c;
+                        if constexpr (SRC == 0) f[e] = bf16_bits_to_f32(static_cast<const uint16_t *>(src)[idx]);
+                        else if constexpr (SRC == 1) f[e] = static_cast<const float *>(src)[idx];
+                        else f[e] = static_cast<float>(static_cast<const int8_t *>(src)[idx]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EV; ++e) tile[r][cc + e] = f[e];
+        }
+        __syncthreads();
+        {
+            const int cl = tid >> 2, mm = 16 * (tid & 3);
+            const int c = c0 + cl;
             uint16_t v[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = bf16_bits(tile[mm + e][tid >> 2]);
-            store16(dst + static_cast<int64_t>(c) * ldm + m0 + mm, v);
+            for (int e = 0; e < 16; ++e) {
+                const float t = tile[mm + e][cl];
+                csum += t;
+                v[e] = bf16_bits(t * sc[mm + e]);
+            }
+            if (c < C) store16(dst + static_cast<int64_t>(c) * ldm + m0 + mm, v);
+        }
+        __syncthreads();
+    }
+    if (sums) {
+        csum += __shfl_xor(csum, 1);
+        csum += __shfl_xor(csum, 2);
+        const int c = c0 + (tid >> 2);
+        if ((tid & 3) == 0 && c < C) {
+            const int j = c / cs.cols;
+            if (j < 3 && cs.o[j]) atomicAdd(&cs.o[j][c - j * cs.cols], csum);
         }
     }
 }
 
-// dx and dgamma from g: workgroup per RPW rows, thread per columns c = tid + 256 j.
-//   r = (mean x^2 + eps)^(-1/2), dot = sum_c g*gamma*x, dx = r*gamma*g - x*r^3/K*dot
+// dx and dgamma from g, workgroup per row (rows blockIdx.x, + gridDim.x, ...), thread per
+// four consecutive columns c = 4 tid + 1024 j (K % 4 == 0, K <= 8192), the row's x and g held
+// in registers between the two passes:
+//   r = (mean x^2 + eps)^(-1/2), dot = sum_c g*gamma*x, d = r*gamma*g - x*r^3/K*dot
 //   (+ a residual gradient res [M][K], bf16 for RES 1, fp32 for RES 2);
-//   dgamma[c] += sum over the workgroup's rows of g*x*r (fp32 atomics into a zeroed array).
-constexpr int RPW = 16;
-template <bool XBF16, int RES>
-__global__ __launch_bounds__(256) void bwd_rows_kernel(const void *x, const float *gsrc, const float *gamma,
-                                                       float eps, int64_t M, int32_t K, float *dx,
-                                                       float *dgamma, const void *res) {
+//   OUT 0: dx = d (fp32); OUT 1: also a bf16 copy dx_bf16; OUT 2: d is the gradient at the
+//   GLU's gated product m = SiLU(gate)*up (K = F) and is carried through it: dgu [M][2F] bf16
+//   gets dgate = d*up*silu'(gate) at column c and dup = d*SiLU(gate) at F + c, gate | up from
+//   the pre-activations gu [M][2F] fp32;
+//   dgamma: each workgroup's sum over its rows of g*x*r into dg_part[blockIdx.x][K] (then
+//   summed over the workgroups by the column-sum kernel).
+constexpr int RV = 8;   // float4 chunks per thread (K <= 8192)
+
+template <bool XBF16>
+__device__ __forceinline__ float4 load4(const void *p, int64_t i) {
+    if constexpr (XBF16) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+    } else {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+    }
+}
+
+template <bool XBF16, int RES, int OUT>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowsArgs p) {
     __shared__ float red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RPW;
-    const int nj = (K + 255) / 256;
-    float dg_acc[32];
+    const int K = p.K;
+    float4 dg[RV];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) dg_acc[j] = 0.0f;
-    for (int rr = 0; rr < RPW; ++rr) {
-        const int64_t m = m0 + rr;
-        if (m >= M) break;
+    for (int j = 0; j < RV; ++j) dg[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t m = blockIdx.x; m < p.M; m += gridDim.x) {
+        float4 xv[RV], gv[RV];
         float ss = 0.0f, dot = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int c = tid + 256 * j;
-            if (j < nj && c < K) {
-                const float xv = load_act<XBF16>(x, m * K + c);
-                const float gv = gsrc[m * K + c];
-                ss = fmaf(xv, xv, ss);
-                dot = fmaf(gv * (gamma ? gamma[c] : 1.0f), xv, dot);
+        for (int j = 0; j < RV; ++j) {
+            const int c = 4 * tid + 1024 * j;
+            xv[j] = gv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (c < K) {
+                xv[j] = load4<XBF16>(p.x, m * K + c);
+                gv[j] = *reinterpret_cast<const float4 *>(p.g + m * K + c);
+                const float4 gm = p.gamma ? *reinterpret_cast<const float4 *>(p.gamma + c)
+                                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                ss = fmaf(xv[j].x, xv[j].x, fmaf(xv[j].y, xv[j].y, fmaf(xv[j].z, xv[j].z, fmaf(xv[j].w, xv[j].w, ss))));
+                dot = fmaf(gv[j].x * gm.x, xv[j].x, fmaf(gv[j].y * gm.y, xv[j].y,
+                      fmaf(gv[j].z * gm.z, xv[j].z, fmaf(gv[j].w * gm.w, xv[j].w, dot))));
             }
         }
         ss = wave_sum(ss);
@@ -399,28 +509,55 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const void *x, const floa
         ss = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
         dot = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
         __syncthreads();
-        const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
+        const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + p.eps);
         const float c3 = r * r * r / static_cast<float>(K) * dot;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int c = tid + 256 * j;
-            if (j < nj && c < K) {
-                const float xv = load_act<XBF16>(x, m * K + c);
-                const float gv = gsrc[m * K + c];
-                const float gm = gamma ? gamma[c] : 1.0f;
-                float d = r * gm * gv - xv * c3;
-                if constexpr (RES == 1) d += bf16_bits_to_f32(static_cast<const uint16_t *>(res)[m * K + c]);
-                if constexpr (RES == 2) d += static_cast<const float *>(res)[m * K + c];
-                if (dx) dx[m * K + c] = d;
-                dg_acc[j] = fmaf(gv * xv, r, dg_acc[j]);
+        for (int j = 0; j < RV; ++j) {
+            const int c = 4 * tid + 1024 * j;
+            if (c < K) {
+                const float4 gm = p.gamma ? *reinterpret_cast<const float4 *>(p.gamma + c)
+                                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                float d[4] = {r * gm.x * gv[j].x - xv[j].x * c3, r * gm.y * gv[j].y - xv[j].y * c3,
+                              r * gm.z * gv[j].z - xv[j].z * c3, r * gm.w * gv[j].w - xv[j].w * c3};
+                if constexpr (RES != 0) {
+                    const float4 rv = load4<RES == 1>(p.res, m * K + c);
+                    d[0] += rv.x;
+                    d[1] += rv.y;
+                    d[2] += rv.z;
+                    d[3] += rv.w;
+                }
+                if constexpr (OUT == 2) {
+                    const float4 ga = *reinterpret_cast<const float4 *>(p.gu + m * 2 * K + c);
+                    const float4 up = *reinterpret_cast<const float4 *>(p.gu + m * 2 * K + K + c);
+                    const float gg[4] = {ga.x, ga.y, ga.z, ga.w}, uu[4] = {up.x, up.y, up.z, up.w};
+                    float dga[4], dup[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dga[e] = d[e] * uu[e] * silu_grad(gg[e]);
+                        dup[e] = d[e] * siluf_(gg[e]);
+                    }
+                    *reinterpret_cast<uint2 *>(p.dgu + m * 2 * K + c) =
+                        make_uint2(pack_bf16x2(dga[0], dga[1]), pack_bf16x2(dga[2], dga[3]));
+                    *reinterpret_cast<uint2 *>(p.dgu + m * 2 * K + K + c) =
+                        make_uint2(pack_bf16x2(dup[0], dup[1]), pack_bf16x2(dup[2], dup[3]));
+                } else {
+                    if (p.dx) *reinterpret_cast<float4 *>(p.dx + m * K + c) = make_float4(d[0], d[1], d[2], d[3]);
+                    if constexpr (OUT == 1)
+                        *reinterpret_cast<uint2 *>(p.dx_bf16 + m * K + c) =
+                            make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+                }
+                dg[j].x = fmaf(gv[j].x * xv[j].x, r, dg[j].x);
+                dg[j].y = fmaf(gv[j].y * xv[j].y, r, dg[j].y);
+                dg[j].z = fmaf(gv[j].z * xv[j].z, r, dg[j].z);
+                dg[j].w = fmaf(gv[j].w * xv[j].w, r, dg[j].w);
             }
         }
     }
-    if (dgamma) {
+    if (p.dg_part) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int c = tid + 256 * j;
-            if (j < nj && c < K) atomicAdd(&dgamma[c], dg_acc[j]);
+        for (int j = 0; j < RV; ++j) {
+            const int c = 4 * tid + 1024 * j;
+            if (c < K) *reinterpret_cast<float4 *>(p.dg_part + static_cast<int64_t>(blockIdx.x) * K + c) = dg[j];
         }
     }
 }
@@ -444,31 +581,21 @@ __global__ void fill_zero_kernel(float *p, int64_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
-__device__ __forceinline__ float silu_grad(float z) {
-    const float s = sigmoidf_(z);
-    return s * (1.0f + z * (1.0f - s));
-}
-
 // The GLU's gated product from the gate | up pre-activations gu [M][2F] fp32 (gate at column
-// f, up at F + f): m = SiLU(gate)*up in the activation dtype (the down projection's input).
+// f, up at F + f): m = SiLU(gate)*up in the activation dtype (the down projection's input);
+// thread per four consecutive f (F % 4 == 0).
 template <bool MBF16>
 __global__ __launch_bounds__(256) void glu_product_kernel(const float *gu, int64_t M, int32_t F, void *m) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (i >= M * F) return;
     const int64_t row = i / F, f = i % F;
-    const float g = gu[row * 2 * F + f], u = gu[row * 2 * F + F + f];
-    store_act<MBF16>(m, i, siluf_(g) * u);
-}
-
-// Its backward: dgate = dm*up*silu'(gate), dup = dm*SiLU(gate), into dgu [M][2F] (gate | up).
-__global__ __launch_bounds__(256) void glu_product_bwd_kernel(const float *gu, const float *dm, int64_t M,
-                                                              int32_t F, float *dgu) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= M * F) return;
-    const int64_t row = i / F, f = i % F;
-    const float g = gu[row * 2 * F + f], u = gu[row * 2 * F + F + f], d = dm[i];
-    dgu[row * 2 * F + f] = d * u * silu_grad(g);
-    dgu[row * 2 * F + F + f] = d * siluf_(g);
+    const float4 g = *reinterpret_cast<const float4 *>(gu + row * 2 * F + f);
+    const float4 u = *reinterpret_cast<const float4 *>(gu + row * 2 * F + F + f);
+    const float v0 = siluf_(g.x) * u.x, v1 = siluf_(g.y) * u.y, v2 = siluf_(g.z) * u.z, v3 = siluf_(g.w) * u.w;
+    if constexpr (MBF16)
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(m) + i) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    else
+        *reinterpret_cast<float4 *>(static_cast<float *>(m) + i) = make_float4(v0, v1, v2, v3);
 }
 
 // ------------------------------------------------------------------ MLGRU backward
@@ -587,6 +714,11 @@ __global__ __launch_bounds__(256) void mlgru_bwd_carry_kernel(MlgruBwdArgs p) {
 //           product of f after the first token, f at the first token; dg and the chunk's
 //           partial sum of the g_norm weight gradient;
 //   PASS 1: from the carried G (phase 3) -> di, df_pre and the chunk's partial sum of df.
+__device__ __forceinline__ void store_grad(const MlgruBwdArgs &p, int64_t i, float v) {
+    if (p.d_ifg_bf16) store_act<true>(p.d_ifg, i, v);
+    else store_act<false>(p.d_ifg, i, v);
+}
+
 template <bool IFGBF16, bool DOBF16, int PASS>
 __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -628,7 +760,7 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
             }
             if (t0 + k == p.T - 1 && p.dh_last) dho += p.dh_last[b * D + d];
             dh[k] = dho;
-            if constexpr (PASS == 0) p.d_ifg[row * 3 * D + 2 * D + d] = dg;
+            if constexpr (PASS == 0) store_grad(p, row * 3 * D + 2 * D + d, dg);
         }
     }
     if constexpr (PASS == 0) {
@@ -658,9 +790,9 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
                 const float f = fmaf(1.0f - lb, sz, lb);
                 const float cv = siluf_(iv[k]);
                 G = dh[k] + fnext * G;
-                p.d_ifg[row * 3 * D + d] = (1.0f - f) * G * silu_grad(iv[k]);
+                store_grad(p, row * 3 * D + d, (1.0f - f) * G * silu_grad(iv[k]));
                 const float dz = (hprev[k] - cv) * G * (1.0f - lb) * sz * (1.0f - sz);
-                p.d_ifg[row * 3 * D + D + d] = dz;
+                store_grad(p, row * 3 * D + D + d, dz);
                 dfb += dz;
                 fnext = f;
             }
@@ -691,92 +823,176 @@ hipError_t launch_col_sum(const void *src, int bf16, int64_t lds, int64_t R, int
     return hipGetLastError();
 }
 
-hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *packed, int32_t N,
-                        int32_t K, float scale, int64_t M, uint16_t *wt, float *g, int accumulate,
-                        hipStream_t s) {
-    if (M <= 0) return hipSuccess;
+hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *const *packed,
+                        const float *scales, int nseg, int32_t N, int32_t K, int64_t M, uint16_t *wt,
+                        float *g, hipStream_t s) {
+    if (M <= 0 || nseg < 1 || nseg > 3) return hipSuccess;
+    const int64_t ldb = static_cast<int64_t>(nseg) * N;
     const int64_t n = static_cast<int64_t>(K) * (N / 8);
-    hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                       packed, N, K, wt);
-    NtGemmArgs ga{};
-    ga.A = dy;
-    ga.a_bf16 = dy_bf16;
-    ga.B = wt;
-    ga.R = M;
-    ga.S = K;
-    ga.T = N;
-    ga.lda = ldy;
-    ga.ldb = N;
-    ga.scale = scale;
-    ga.C = g;
-    ga.t_per_split = N;
-    ga.atomic = accumulate ? 2 : 0;
+    for (int j = 0; j < nseg; ++j)
+        hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                           packed[j], N, K, wt + static_cast<int64_t>(j) * N, ldb);
+    // one launch over the stacked contraction when every segment boundary is a step boundary
+    // and the scale ratios are finite
+    bool one = N % BT == 0;
+    for (int j = 0; j < nseg; ++j) one = one && scales[j] > 0.0f && scales[j] < 3.0e38f;
     const dim3 grid(static_cast<unsigned>(((K + BS - 1) / BS) * ((M + BR - 1) / BR)), 1, 1);
+    const int nl = nseg == 1 || one ? 1 : nseg;
     timing_begin(FAM_BWD_G, s);
-    if (dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
-    else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, ga);
+    for (int l = 0; l < nl; ++l) {
+        NtGemmArgs ga{};
+        ga.a_bf16 = dy_bf16;
+        ga.R = M;
+        ga.S = K;
+        ga.lda = ldy;
+        ga.ldb = ldb;
+        ga.C = g;
+        if (nl == 1) {
+            ga.A = dy;
+            ga.B = wt;
+            ga.T = ldb;
+            ga.scale = scales[nseg - 1];
+            ga.seg_steps = nseg > 1 ? N / BT : 0;
+            for (int j = 0; j + 1 < nseg; ++j) ga.seg_ratio[j] = scales[j] / scales[j + 1];
+        } else {   // one launch per linear, added into g
+            ga.A = static_cast<const char *>(dy) + static_cast<int64_t>(l) * N * (dy_bf16 ? 2 : 4);
+            ga.B = wt + static_cast<int64_t>(l) * N;
+            ga.T = N;
+            ga.scale = scales[l];
+            ga.atomic = l > 0 ? 2 : 0;
+        }
+        ga.t_per_split = ga.T;
+        if (dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
+        else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, ga);
+    }
     timing_end(FAM_BWD_G, s);
     return hipGetLastError();
 }
 
-hipError_t bwd_launch_rows(const void *x, int x_bf16, const float *g, const float *gamma, float eps,
-                           int64_t M, int32_t K, float *dx, float *dgamma, const void *res, int res_kind,
-                           hipStream_t s) {
-    if (M <= 0) return hipSuccess;
+// one workgroup per row up to 768 of them (each then takes every 768th row): the row kernels
+// hold 135-155 VGPRs, three 256-thread workgroups per CU, so 768 is one full wave on 256 CUs
+static int64_t rows_grid(int64_t M) { return M < 768 ? M : 768; }
+
+size_t bwd_rows_part_bytes(int64_t M, int32_t K) {
+    return M > 0 ? static_cast<size_t>(rows_grid(M)) * K * 4 : 0;
+}
+
+hipError_t bwd_launch_rows(const BwdRowsArgs &a, hipStream_t s) {
+    if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    if (dgamma && (e = launch_fill_zero(dgamma, K, s)) != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>((M + RPW - 1) / RPW));
-#define MMF_ROWS(XB, RK) hipLaunchKernelGGL((bwd_rows_kernel<XB, RK>), grid, dim3(256), 0, s, x, g, gamma, eps, M, K, dx, dgamma, res)
-    if (x_bf16) {
-        if (res_kind == 1) MMF_ROWS(true, 1);
-        else if (res_kind == 2) MMF_ROWS(true, 2);
-        else MMF_ROWS(true, 0);
+    BwdRowsArgs p = a;
+    if (!p.dgamma) p.dg_part = nullptr;
+    const int64_t nwg = rows_grid(a.M);
+    const dim3 grid(static_cast<unsigned>(nwg));
+    const int rk = a.res ? (a.res_bf16 ? 1 : 2) : 0;
+    const int ok = a.dgu ? 2 : (a.dx_bf16 ? 1 : 0);
+#define MMF_ROWS(XB, RK, OK) hipLaunchKernelGGL((bwd_rows_kernel<XB, RK, OK>), grid, dim3(256), 0, s, p)
+#define MMF_ROWS_OK(XB, RK) \
+    if (ok == 2) MMF_ROWS(XB, RK, 2); else if (ok == 1) MMF_ROWS(XB, RK, 1); else MMF_ROWS(XB, RK, 0);
+    if (a.x_bf16) {
+        if (rk == 1) { MMF_ROWS_OK(true, 1) }
+        else if (rk == 2) { MMF_ROWS_OK(true, 2) }
+        else { MMF_ROWS_OK(true, 0) }
     } else {
-        if (res_kind == 1) MMF_ROWS(false, 1);
-        else if (res_kind == 2) MMF_ROWS(false, 2);
-        else MMF_ROWS(false, 0);
+        if (rk == 1) { MMF_ROWS_OK(false, 1) }
+        else if (rk == 2) { MMF_ROWS_OK(false, 2) }
+        else { MMF_ROWS_OK(false, 0) }
     }
+#undef MMF_ROWS_OK
 #undef MMF_ROWS
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.dgamma) {
+        if ((e = launch_fill_zero(p.dgamma, a.K, s)) != hipSuccess) return e;
+        if ((e = launch_col_sum(p.dg_part, 0, a.K, nwg, a.K, p.dgamma, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int SRC>
+static void launch_transpose(const void *src, int64_t lds, const float *scale, int64_t M, int32_t C,
+                             int64_t ldm, uint16_t *dst, const ColSums &cs, hipStream_t s) {
+    constexpr int ES = SRC == 0 ? 2 : (SRC == 1 ? 4 : 1);
+    const int vec = reinterpret_cast<uintptr_t>(src) % 16 == 0 && (lds * ES) % 16 == 0;
+    const dim3 gt(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>((ldm + 255) / 256));
+    hipLaunchKernelGGL((transpose_kernel<SRC>), gt, dim3(256), 0, s, src, lds, vec, scale, M, C, ldm, dst, cs);
 }
 
 hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uint16_t *qT, hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    const dim3 gt(static_cast<unsigned>((K + 63) / 64), static_cast<unsigned>(ldm / 64));
-    hipLaunchKernelGGL((transpose_kernel<2>), gt, dim3(256), 0, s, q, static_cast<int64_t>(K), nullptr, M, K, ldm, qT);
+    launch_transpose<2>(q, static_cast<int64_t>(K), nullptr, M, K, ldm, qT, ColSums{}, s);
     return hipGetLastError();
 }
 
-hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int32_t N,
-                         int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT, float *dw, hipStream_t s) {
-    if (M <= 0) return launch_fill_zero(dw, static_cast<int64_t>(N) * K, s);
-    const dim3 gt(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>(ldm / 64));
-    if (dy_bf16) hipLaunchKernelGGL((transpose_kernel<0>), gt, dim3(256), 0, s, dy, ldy, a, M, N, ldm, dyaT);
-    else hipLaunchKernelGGL((transpose_kernel<1>), gt, dim3(256), 0, s, dy, ldy, a, M, N, ldm, dyaT);
+hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int nseg,
+                         int32_t N, int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT,
+                         float *const *dw, float *const *db, hipStream_t s) {
     hipError_t e;
-    if ((e = launch_fill_zero(dw, static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
+    bool any_dw = false;
+    for (int j = 0; j < nseg; ++j) {
+        if (db[j] && (e = launch_fill_zero(db[j], N, s)) != hipSuccess) return e;
+        any_dw = any_dw || dw[j];
+    }
+    if (M <= 0) {
+        for (int j = 0; j < nseg; ++j)
+            if (dw[j] && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
+        return hipSuccess;
+    }
+    if (!any_dw) {   // the bias gradients alone: column sums
+        for (int j = 0; j < nseg; ++j) {
+            const void *src = static_cast<const char *>(dy) + static_cast<int64_t>(j) * N * (dy_bf16 ? 2 : 4);
+            if (db[j] && (e = launch_col_sum(src, dy_bf16, ldy, M, N, db[j], s)) != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int32_t R = nseg * N;
+    ColSums cs{};
+    for (int j = 0; j < nseg; ++j) cs.o[j] = db[j];
+    cs.cols = N;
+    if (dy_bf16) launch_transpose<0>(dy, ldy, a, M, R, ldm, dyaT, cs, s);
+    else launch_transpose<1>(dy, ldy, a, M, R, ldm, dyaT, cs, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     NtGemmArgs ga{};
     ga.A = dyaT;
     ga.a_bf16 = 1;
     ga.B = qT;
-    ga.R = N;
+    ga.R = R;
     ga.S = K;
     ga.T = ldm;
     ga.lda = ldm;
     ga.ldb = ldm;
     ga.scale = 1.0f;
-    ga.C = dw;
-    ga.atomic = 1;
-    const int64_t tiles = static_cast<int64_t>((K + BS - 1) / BS) * ((N + BR - 1) / BR);
-    // split the tokens so that about 1024 workgroups run, each over >= 8 steps
-    int64_t splits = (1024 + tiles - 1) / tiles;
-    const int64_t max_splits = (ldm + 8 * BT - 1) / (8 * BT);
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
+    ga.C = dw[0];
+    if (nseg > 1) {
+        ga.c_rows = N;
+        ga.C1 = dw[1];
+        ga.C2 = nseg > 2 ? dw[2] : nullptr;
+    }
+    const int64_t tiles = static_cast<int64_t>((K + BS - 1) / BS) * ((R + BR - 1) / BR);
+    // split the tokens over workgroups (fp32 atomics) when there are too few tiles for 256
+    // CUs x 2: the smallest split count, each split >= 8 steps, whose last wave of workgroups
+    // is at least 85 % full (or the best of those tried)
+    const int64_t slots = 512;
+    const int64_t max_splits = std::min<int64_t>(64, std::max<int64_t>(1, (ldm + 8 * BT - 1) / (8 * BT)));
+    int64_t splits = 1;
+    double best = -1.0;
+    for (int64_t sp = 1; sp <= max_splits; ++sp) {
+        const int64_t wg = tiles * sp, waves = (wg + slots - 1) / slots;
+        const double fill = static_cast<double>(wg) / static_cast<double>(waves * slots);
+        if (wg < slots && sp < max_splits) continue;   // not yet one full wave
+        if (fill > best + 1e-9) {
+            best = fill;
+            splits = sp;
+        }
+        if (fill >= 0.85) break;
+    }
     int64_t per = (ldm + splits - 1) / splits;
     per = (per + BT - 1) / BT * BT;
     splits = (ldm + per - 1) / per;
     ga.t_per_split = per;
+    ga.atomic = splits > 1 ? 1 : 0;
+    if (splits > 1)
+        for (int j = 0; j < nseg; ++j)
+            if (dw[j] && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
     timing_begin(FAM_BWD_DW, s);
     hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
@@ -784,37 +1000,35 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
     return hipGetLastError();
 }
 
-hipError_t bwd_launch_db(const void *dy, int dy_bf16, int64_t ldy, int64_t M, int32_t N, float *db, hipStream_t s) {
-    hipError_t e;
-    if ((e = launch_fill_zero(db, N, s)) != hipSuccess) return e;
-    return launch_col_sum(dy, dy_bf16, ldy, M, N, db, s);
-}
-
 hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s) {
-    const int64_t n = M * F;
+    const int64_t n = M * F / 4;
     if (n <= 0) return hipSuccess;
-    if (m_bf16) hipLaunchKernelGGL((glu_product_kernel<true>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, M, F, m);
-    else hipLaunchKernelGGL((glu_product_kernel<false>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, M, F, m);
-    return hipGetLastError();
-}
-
-hipError_t launch_glu_product_bwd(const float *gu, const float *dm, int64_t M, int32_t F, float *dgu, hipStream_t s) {
-    const int64_t n = M * F;
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(glu_product_bwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, gu, dm, M, F, dgu);
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+    if (m_bf16) hipLaunchKernelGGL((glu_product_kernel<true>), grid, dim3(256), 0, s, gu, M, F, m);
+    else hipLaunchKernelGGL((glu_product_kernel<false>), grid, dim3(256), 0, s, gu, M, F, m);
     return hipGetLastError();
 }
 
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    if ((e = bwd_launch_g(a.dy, a.dy_bf16, a.N, a.packed, a.N, a.K, a.scale, a.M, a.wt, a.g, 0, s)) != hipSuccess) return e;
-    if ((e = bwd_launch_rows(a.x, a.x_bf16, a.g, a.gamma, a.eps, a.M, a.K, a.dx, a.dgamma, nullptr, 0, s)) != hipSuccess) return e;
-    if (a.dw) {
-        if ((e = bwd_launch_qT(a.q, a.M, a.K, a.ldm, a.qT, s)) != hipSuccess) return e;
-        if ((e = bwd_launch_dw(a.dy, a.dy_bf16, a.N, a.a, a.M, a.N, a.K, a.ldm, a.qT, a.dyaT, a.dw, s)) != hipSuccess) return e;
-    }
-    if (a.db && (e = bwd_launch_db(a.dy, a.dy_bf16, a.N, a.M, a.N, a.db, s)) != hipSuccess) return e;
+    if ((e = bwd_launch_g(a.dy, a.dy_bf16, a.N, &a.packed, &a.scale, 1, a.N, a.K, a.M, a.wt, a.g, s)) != hipSuccess) return e;
+    BwdRowsArgs r{};
+    r.x = a.x;
+    r.x_bf16 = a.x_bf16;
+    r.g = a.g;
+    r.gamma = a.gamma;
+    r.eps = a.eps;
+    r.M = a.M;
+    r.K = a.K;
+    r.dx = a.dx;
+    r.dgamma = a.dgamma;
+    r.dg_part = a.dg_part;
+    if ((a.dx || a.dgamma) && (e = bwd_launch_rows(r, s)) != hipSuccess) return e;
+    if (a.dw && (e = bwd_launch_qT(a.q, a.M, a.K, a.ldm, a.qT, s)) != hipSuccess) return e;
+    float *dw = a.dw, *db = a.db;
+    if (a.dw || a.db)
+        if ((e = bwd_launch_dw(a.dy, a.dy_bf16, a.N, a.a, a.M, 1, a.N, a.K, a.ldm, a.qT, a.dyaT, &dw, &db, s)) != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -1041,7 +1041,8 @@ size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m) {
     const size_t K = static_cast<size_t>(w->K), N = static_cast<size_t>(w->N), M = static_cast<size_t>(m);
     const size_t ldm = (M + 63) / 64 * 64;
     return align_up(M * K) + align_up(M * 4) + align_up(M * 4) + align_up(M * K * 4) +
-           align_up(K * N * 2) + align_up(N * ldm * 2) + align_up(K * ldm * 2);
+           align_up(K * N * 2) + align_up(N * ldm * 2) + align_up(K * ldm * 2) +
+           align_up(bwd_rows_part_bytes(m, w->K));
 }
 
 int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
@@ -1078,6 +1079,7 @@ int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, in
     uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(w->K) * w->N * 2);
     uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(w->N) * ldm * 2);
     uint16_t *qT = c.take<uint16_t>(static_cast<size_t>(w->K) * ldm * 2);
+    float *dg_part = c.take<float>(bwd_rows_part_bytes(m, w->K));
     hipError_t e = quantize(x, x_dt == MMF_BF16, w->norm_w, w->eps, m, w->K, qb, nullptr, stream);
     if (e != hipSuccess) return hip_error(e, "bitlinear_backward quant launch");
     BitlinearBwdArgs a{};
@@ -1099,6 +1101,7 @@ int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, in
     a.ldm = ldm;
     a.dyaT = dyaT;
     a.qT = qT;
+    a.dg_part = dg_part;
     a.dx = dx;
     a.dgamma = dgamma;
     a.dw = dw;
@@ -1114,9 +1117,13 @@ size_t mlgru_backward_workspace_bytes(int64_t B, int64_t T, int64_t D) {
     return scan_bytes(B, T, D) + align_up(static_cast<size_t>(B * T) * 8) + 6 * align_up(cn);
 }
 
-int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt, const float *dh_last,
-                   float *d_ifg, float *dh0, float *dgnorm_w, float *df_bias, void *ws,
-                   size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// d_ifg in bf16 (d_ifg_bf16) for the block backward's own use
+static int mlgru_backward_impl(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt,
+                               const float *dh_last, void *d_ifg, bool d_ifg_bf16, float *dh0,
+                               float *dgnorm_w, float *df_bias, void *ws, size_t ws_bytes,
+                               hipStream_t stream) {
     if (!a) return set_error(MMF_EINVAL, "mlgru_backward: NULL args");
     int rc = check_scan_shape(a->B, a->T, a->D, "mlgru_backward");
     if (rc) return rc;
@@ -1180,6 +1187,7 @@ int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt,
     b.dout_bf16 = dout_dt == MMF_BF16;
     b.dh_last = dh_last;
     b.d_ifg = d_ifg;
+    b.d_ifg_bf16 = d_ifg_bf16;
     b.dh0 = dh0;
     b.dgnorm_w = dgnorm_w;
     b.df_bias = df_bias;
@@ -1196,17 +1204,29 @@ int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt,
     return MMF_OK;
 }
 
+extern "C" {
+
+int mlgru_backward(const mmf_mlgru_args *a, const void *dout, mmf_dtype dout_dt, const float *dh_last,
+                   float *d_ifg, float *dh0, float *dgnorm_w, float *df_bias, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+    return mlgru_backward_impl(a, dout, dout_dt, dh_last, d_ifg, false, dh0, dgnorm_w, df_bias, ws,
+                               ws_bytes, stream);
+}
+
 size_t block_backward_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) {
     if (!w || B <= 0 || T <= 0) return 0;
     const int64_t M = B * T, D = w->i.K, F = w->gate.N, KN = std::max(D, F);
     const int64_t ldm = (M + 63) / 64 * 64;
     auto f4 = [](int64_t n) { return align_up(static_cast<size_t>(n) * 4); };
+    auto h2 = [](int64_t n) { return align_up(static_cast<size_t>(n) * 2); };
     return 3 * qbuf_bytes(M, D) + qbuf_bytes(M, F) +                       // q of x, o, y1, m
            f4(M * 3 * D) + 2 * f4(M * D) + f4(M * 2 * F) + f4(M * F) +     // ifg, o, y1, gate|up, m
            scan_bytes(B, T, D) +                                           // forward chunk carries
-           f4(M * KN) + f4(M * F) + f4(M * 2 * F) + 2 * f4(M * D) + f4(M * 3 * D) +  // g, dm, dgu, dy1, do, d_ifg
-           align_up(static_cast<size_t>(std::max(D * D, D * F)) * 2) +    // bf16 W^T
-           2 * align_up(static_cast<size_t>(KN * ldm) * 2) +               // q^T, (dy a)^T
+           f4(M * KN) + h2(M * 2 * F) + f4(M * D) + h2(M * D) + f4(M * D) + h2(M * 3 * D) +
+                                                              // g, dgu, dy1 (+ bf16), do, d_ifg
+           h2(std::max(3 * D * D, 2 * F * D)) +                            // bf16 W^T, stacked
+           h2(KN * ldm) + h2(std::max(3 * D, 2 * F) * ldm) +               // q^T, (dy a)^T
+           align_up(bwd_rows_part_bytes(M, static_cast<int32_t>(KN))) +   // dgamma partials
            mlgru_backward_workspace_bytes(B, T, D);
 }
 
@@ -1219,6 +1239,10 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     if (B < 0 || T < 0) return set_error(MMF_ESHAPE, "block_backward: B=%lld T=%lld", (long long)B, (long long)T);
     const int32_t D = w->i.K, F = w->gate.N;
     if (F % 8 || F > 8192) return set_error(MMF_ESHAPE, "block_backward: F=%d must be a multiple of 8 and <= 8192", F);
+    // the row kernels read the gains 16 bytes at a time
+    if ((w->i.norm_w && !aligned16(w->i.norm_w)) || (w->gate.norm_w && !aligned16(w->gate.norm_w)) ||
+        (w->down.norm_w && !aligned16(w->down.norm_w)))
+        return set_error(MMF_EALIGN, "block_backward: i/gate/down norm_w not 16-byte aligned");
     const int64_t M = B * T;
     static const mmf_block_grads none{};
     const mmf_block_grads &G = gr ? *gr : none;
@@ -1258,14 +1282,15 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     void *m = c.take<char>(static_cast<size_t>(M * F) * 4);
     char *scan_ws = c.take<char>(scan_bytes(B, T, D));
     float *g = c.take<float>(static_cast<size_t>(M * KN) * 4);
-    float *dm = c.take<float>(static_cast<size_t>(M * F) * 4);
-    float *dgu = c.take<float>(static_cast<size_t>(M * 2 * F) * 4);
+    uint16_t *dgu = c.take<uint16_t>(static_cast<size_t>(M * 2 * F) * 2);
     float *dy1 = c.take<float>(static_cast<size_t>(M * D) * 4);
+    uint16_t *dy1b = c.take<uint16_t>(static_cast<size_t>(M * D) * 2);
     float *dO = c.take<float>(static_cast<size_t>(M * D) * 4);
-    float *d_ifg = c.take<float>(static_cast<size_t>(M * 3 * D) * 4);
-    uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(std::max(D * D, D * F)) * 2);
+    uint16_t *d_ifg = c.take<uint16_t>(static_cast<size_t>(M * 3 * D) * 2);
+    uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(std::max(3 * D * D, 2 * F * D)) * 2);
     uint16_t *qT = c.take<uint16_t>(static_cast<size_t>(KN * ldm) * 2);
-    uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(KN * ldm) * 2);
+    uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(std::max(3 * D, 2 * F) * ldm) * 2);
+    float *dg_part = c.take<float>(bwd_rows_part_bytes(M, static_cast<int32_t>(KN)));
     const size_t mws_bytes = mlgru_backward_workspace_bytes(B, T, D);
     void *mws = c.take<char>(mws_bytes);
 #define MMF_TRY(expr, what) do { if ((e = (expr)) != hipSuccess) return hip_error(e, "block_backward " what); } while (0)
@@ -1310,33 +1335,63 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     MMF_TRY(launch_glu_product(gu, M, F, m, bf, stream), "glu product");
     MMF_TRY(quantize(m, bf, w->down.norm_w, w->down.eps, M, F, qm, nullptr, stream), "quant m");
 
-    // ---- down: dm = down^T(dy) through the straight-through BitLinear backward
-    MMF_TRY(bwd_launch_g(dy, dyb, D, w->down.packed, D, F, w->down.scale, M, wt, g, 0, stream), "down g");
-    MMF_TRY(bwd_launch_rows(m, bf, g, w->down.norm_w, w->down.eps, M, F, dm, G.dgamma[3], nullptr, 0, stream), "down rows");
-    if (G.dw[6]) {
-        MMF_TRY(bwd_launch_qT(qm.q, M, F, ldm, qT, stream), "down qT");
-        MMF_TRY(bwd_launch_dw(dy, dyb, D, qm.a, M, D, F, ldm, qT, dyaT, G.dw[6], stream), "down dw");
+    // Backward.  Each BitLinear: g = s_w dy T on the matrix cores, then the row kernel (dx,
+    // dgamma from g and the normalisation's input); dW and db from the transposed (dy a) and
+    // q.  Linears that share an input (gate | up; i | f | g) are one contraction over their
+    // stacked dy, with one row kernel and one dW launch.  Gradients that feed a contraction are
+    // kept in bf16 (dgate|dup, dy1's copy, d_ifg); those added as residuals stay fp32.
+    auto rows = [&](const void *xin, const mmf_bitlinear &l, int32_t K) {
+        BwdRowsArgs r{};
+        r.x = xin;
+        r.x_bf16 = bf;
+        r.g = g;
+        r.gamma = l.norm_w;
+        r.eps = l.eps;
+        r.M = M;
+        r.K = K;
+        r.dg_part = dg_part;
+        return r;
+    };
+    // ---- down (its dx, the gradient at m, is carried through m = SiLU(gate)*up in the row kernel)
+    {
+        const uint32_t *pk[1] = {w->down.packed};
+        const float sc[1] = {w->down.scale};
+        MMF_TRY(bwd_launch_g(dy, dyb, D, pk, sc, 1, D, F, M, wt, g, stream), "down g");
+        BwdRowsArgs r = rows(m, w->down, F);
+        r.gu = gu;
+        r.dgu = dgu;
+        r.dgamma = G.dgamma[3];
+        MMF_TRY(bwd_launch_rows(r, stream), "down rows");
+        if (G.dw[6]) MMF_TRY(bwd_launch_qT(qm.q, M, F, ldm, qT, stream), "down qT");
+        MMF_TRY(bwd_launch_dw(dy, dyb, D, qm.a, M, 1, D, F, ldm, qT, dyaT, &G.dw[6], &G.db[6], stream), "down dw");
     }
-    if (G.db[6]) MMF_TRY(bwd_launch_db(dy, dyb, D, M, D, G.db[6], stream), "down db");
-    // ---- the GLU's product, then gate and up (one g for both: they share the input y1);
-    //      dy1 = dy + gate^T(dgate) + up^T(dup)
-    MMF_TRY(launch_glu_product_bwd(gu, dm, M, F, dgu, stream), "glu product backward");
-    MMF_TRY(bwd_launch_g(dgu, 0, 2 * F, w->gate.packed, F, D, w->gate.scale, M, wt, g, 0, stream), "gate g");
-    MMF_TRY(bwd_launch_g(dgu + F, 0, 2 * F, w->up.packed, F, D, w->up.scale, M, wt, g, 1, stream), "up g");
-    MMF_TRY(bwd_launch_rows(y1, bf, g, w->gate.norm_w, w->gate.eps, M, D, dy1, G.dgamma[2], dy, dyb ? 1 : 2, stream), "gate|up rows");
-    if (G.dw[4] || G.dw[5]) MMF_TRY(bwd_launch_qT(qy.q, M, D, ldm, qT, stream), "gate|up qT");
-    if (G.dw[4]) MMF_TRY(bwd_launch_dw(dgu, 0, 2 * F, qy.a, M, F, D, ldm, qT, dyaT, G.dw[4], stream), "gate dw");
-    if (G.dw[5]) MMF_TRY(bwd_launch_dw(dgu + F, 0, 2 * F, qy.a, M, F, D, ldm, qT, dyaT, G.dw[5], stream), "up dw");
-    if (G.db[4]) MMF_TRY(bwd_launch_db(dgu, 0, 2 * F, M, F, G.db[4], stream), "gate db");
-    if (G.db[5]) MMF_TRY(bwd_launch_db(dgu + F, 0, 2 * F, M, F, G.db[5], stream), "up db");
+    // ---- gate | up: dy1 = dy + gate^T(dgate) + up^T(dup)
+    {
+        const uint32_t *pk[2] = {w->gate.packed, w->up.packed};
+        const float sc[2] = {w->gate.scale, w->up.scale};
+        MMF_TRY(bwd_launch_g(dgu, 1, 2 * F, pk, sc, 2, F, D, M, wt, g, stream), "gate|up g");
+        BwdRowsArgs r = rows(y1, w->gate, D);
+        r.dx = dy1;
+        r.dx_bf16 = dy1b;
+        r.res = dy;
+        r.res_bf16 = dyb;
+        r.dgamma = G.dgamma[2];
+        MMF_TRY(bwd_launch_rows(r, stream), "gate|up rows");
+        if (G.dw[4] || G.dw[5]) MMF_TRY(bwd_launch_qT(qy.q, M, D, ldm, qT, stream), "gate|up qT");
+        MMF_TRY(bwd_launch_dw(dgu, 1, 2 * F, qy.a, M, 2, F, D, ldm, qT, dyaT, &G.dw[4], &G.db[4], stream), "gate|up dw");
+    }
     // ---- o_proj: do = o^T(dy1)
-    MMF_TRY(bwd_launch_g(dy1, 0, D, w->o.packed, D, D, w->o.scale, M, wt, g, 0, stream), "o g");
-    MMF_TRY(bwd_launch_rows(o, bf, g, w->o.norm_w, w->o.eps, M, D, dO, G.dgamma[1], nullptr, 0, stream), "o rows");
-    if (G.dw[3]) {
-        MMF_TRY(bwd_launch_qT(qo.q, M, D, ldm, qT, stream), "o qT");
-        MMF_TRY(bwd_launch_dw(dy1, 0, D, qo.a, M, D, D, ldm, qT, dyaT, G.dw[3], stream), "o dw");
+    {
+        const uint32_t *pk[1] = {w->o.packed};
+        const float sc[1] = {w->o.scale};
+        MMF_TRY(bwd_launch_g(dy1b, 1, D, pk, sc, 1, D, D, M, wt, g, stream), "o g");
+        BwdRowsArgs r = rows(o, w->o, D);
+        r.dx = dO;
+        r.dgamma = G.dgamma[1];
+        MMF_TRY(bwd_launch_rows(r, stream), "o rows");
+        if (G.dw[3]) MMF_TRY(bwd_launch_qT(qo.q, M, D, ldm, qT, stream), "o qT");
+        MMF_TRY(bwd_launch_dw(dy1b, 1, D, qo.a, M, 1, D, D, ldm, qT, dyaT, &G.dw[3], &G.db[3], stream), "o dw");
     }
-    if (G.db[3]) MMF_TRY(bwd_launch_db(dy1, 0, D, M, D, G.db[3], stream), "o db");
 #undef MMF_TRY
     // ---- the MLGRU with its output gate
     {
@@ -1353,18 +1408,24 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
         ma.T = T;
         ma.D = D;
         ma.f_lower = w->f_lower;
-        if ((rc = mlgru_backward(&ma, dO, MMF_F32, dh_last, d_ifg, dh0, G.dgnorm_w, G.df_bias, mws, mws_bytes, stream)))
+        if ((rc = mlgru_backward_impl(&ma, dO, MMF_F32, dh_last, d_ifg, true, dh0, G.dgnorm_w, G.df_bias, mws,
+                                      mws_bytes, stream)))
             return rc;
     }
-    // ---- i, f, g (one g for the three: they share the input x); dx = dy1 + sum_k k^T(d_k)
+    // ---- i | f | g: dx = dy1 + i^T(d_i) + f^T(d_f) + g^T(d_g)
 #define MMF_TRY(expr, what) do { if ((e = (expr)) != hipSuccess) return hip_error(e, "block_backward " what); } while (0)
-    for (int k = 0; k < 3; ++k)
-        MMF_TRY(bwd_launch_g(d_ifg + k * D, 0, 3 * D, lin[k]->packed, D, D, lin[k]->scale, M, wt, g, k > 0, stream), "ifg g");
-    MMF_TRY(bwd_launch_rows(x, bf, g, w->i.norm_w, w->i.eps, M, D, dx, G.dgamma[0], dy1, 2, stream), "ifg rows");
-    if (G.dw[0] || G.dw[1] || G.dw[2]) MMF_TRY(bwd_launch_qT(qx.q, M, D, ldm, qT, stream), "ifg qT");
-    for (int k = 0; k < 3; ++k) {
-        if (G.dw[k]) MMF_TRY(bwd_launch_dw(d_ifg + k * D, 0, 3 * D, qx.a, M, D, D, ldm, qT, dyaT, G.dw[k], stream), "ifg dw");
-        if (G.db[k]) MMF_TRY(bwd_launch_db(d_ifg + k * D, 0, 3 * D, M, D, G.db[k], stream), "ifg db");
+    {
+        const uint32_t *pk[3] = {w->i.packed, w->f.packed, w->g.packed};
+        const float sc[3] = {w->i.scale, w->f.scale, w->g.scale};
+        MMF_TRY(bwd_launch_g(d_ifg, 1, 3 * D, pk, sc, 3, D, D, M, wt, g, stream), "ifg g");
+        BwdRowsArgs r = rows(x, w->i, D);
+        r.dx = dx;
+        r.res = dy1;
+        r.res_bf16 = 0;
+        r.dgamma = G.dgamma[0];
+        MMF_TRY(bwd_launch_rows(r, stream), "ifg rows");
+        if (G.dw[0] || G.dw[1] || G.dw[2]) MMF_TRY(bwd_launch_qT(qx.q, M, D, ldm, qT, stream), "ifg qT");
+        MMF_TRY(bwd_launch_dw(d_ifg, 1, 3 * D, qx.a, M, 3, D, D, ldm, qT, dyaT, &G.dw[0], &G.db[0], stream), "ifg dw");
     }
 #undef MMF_TRY
     return MMF_OK;

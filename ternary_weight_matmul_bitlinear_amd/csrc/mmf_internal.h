@@ -399,6 +399,7 @@ struct BitlinearBwdArgs {
     int64_t ldm;           // M rounded up to 64: row length of the two copies below
     uint16_t *dyaT;        // [N][ldm] bf16 (dy * a) transposed (workspace)
     uint16_t *qT;          // [K][ldm] bf16 q transposed (workspace)
+    float *dg_part;        // bwd_rows_part_bytes(M, K) (workspace)
     float *dx;             // [M][K] or NULL
     float *dgamma;         // [K] or NULL
     float *dw;             // [N][K] or NULL
@@ -419,7 +420,8 @@ struct MlgruBwdArgs {
     const void *dout;      // [B][T][D]
     int32_t dout_bf16;
     const float *dh_last;  // [B][D] or NULL
-    float *d_ifg;          // [B][T][3D]
+    void *d_ifg;           // [B][T][3D], fp32 (or bf16 when d_ifg_bf16)
+    int32_t d_ifg_bf16;
     float *dh0;            // [B][D] or NULL
     float *dgnorm_w;       // [D] or NULL
     float *df_bias;        // [D] or NULL
@@ -439,19 +441,40 @@ hipError_t launch_scan_carries(const ScanArgs &a, hipStream_t s);
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s);
 hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
-// backward pieces (backward.hip): dy [M][ldy] of which the first N columns are used
-hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *packed, int32_t N,
-                        int32_t K, float scale, int64_t M, uint16_t *wt, float *g, int accumulate,
-                        hipStream_t s);   // g (+)= scale * dy T; wt: [K][N] bf16 scratch
-hipError_t bwd_launch_rows(const void *x, int x_bf16, const float *g, const float *gamma, float eps,
-                           int64_t M, int32_t K, float *dx, float *dgamma, const void *res, int res_kind,
-                           hipStream_t s);   // res_kind 0: none, 1: bf16, 2: fp32 residual gradient
+// backward pieces (backward.hip).  Up to three linears that share an input are handled
+// together: their output gradients sit side by side in dy [M][ldy] (N columns each).
+// g = sum_j scale_j * dy_j T_j  [M][K] fp32 (one launch when N % 64 == 0); wt: [K][nseg*N]
+// bf16 scratch.
+hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *const *packed,
+                        const float *scales, int nseg, int32_t N, int32_t K, int64_t M, uint16_t *wt,
+                        float *g, hipStream_t s);
+// dx / dgamma from g (and the residual gradient, and the GLU product's backward)
+struct BwdRowsArgs {
+    const void *x;          // [M][K] forward input of the normalisation
+    int32_t x_bf16;
+    const float *g;         // [M][K]
+    const float *gamma;     // [K] or NULL
+    float eps;
+    int64_t M;
+    int32_t K;              // K % 4 == 0, K <= 8192
+    float *dx;              // [M][K] fp32 or NULL
+    uint16_t *dx_bf16;      // [M][K] bf16 copy or NULL
+    const void *res;        // [M][K] residual gradient added to dx, or NULL
+    int32_t res_bf16;
+    const float *gu;        // GLU mode: gate | up pre-activations [M][2K] fp32 ...
+    uint16_t *dgu;          // ... and dgate | dup [M][2K] bf16 out (dx, dx_bf16 unused)
+    float *dgamma;          // [K] or NULL
+    float *dg_part;         // workspace: bwd_rows_part_bytes(M, K)
+};
+size_t bwd_rows_part_bytes(int64_t M, int32_t K);
+hipError_t bwd_launch_rows(const BwdRowsArgs &a, hipStream_t s);
 hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uint16_t *qT, hipStream_t s);
-hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int32_t N,
-                         int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT, float *dw, hipStream_t s);
-hipError_t bwd_launch_db(const void *dy, int dy_bf16, int64_t ldy, int64_t M, int32_t N, float *db, hipStream_t s);
+// dW_j = (dy_j a)^T q  [N][K] each, into dw[j] (NULL: not wanted); db_j = sum_M dy_j into db[j]
+// (NULL: not wanted).  dyaT: [nseg*N][ldm] bf16 scratch; qT from bwd_launch_qT.
+hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int nseg,
+                         int32_t N, int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT,
+                         float *const *dw, float *const *db, hipStream_t s);
 hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s);
-hipError_t launch_glu_product_bwd(const float *gu, const float *dm, int64_t M, int32_t F, float *dgu, hipStream_t s);
 hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);

@@ -36,6 +36,8 @@
 // Per-chunk partial sums of dgnorm_w and df_bias are reduced by a column-sum kernel.
 #include "mmf_internal.h"
 
+#include <type_traits>
+
 namespace mmf {
 
 namespace {
@@ -332,6 +334,199 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
                 }
             }
         }
+}
+
+// The same product for bf16 A, fed by direct-to-LDS 16-byte loads (no register staging)
+// through a ring of DSTAGES buffers of 32-deep contraction steps: tile kt + 3 is requested
+// while tile kt is multiplied.  One workgroup of 8 waves per CU, tiles of 256 x 256 (4 x 2
+// waves, each 64 x 128 = 2 x 4 MFMA blocks: 6 operand reads per 8 MFMAs, 32 KB of operands
+// per 128 MFMAs).  An LDS tile row is 32 bf16 = 64 bytes, four 16-byte chunks, chunk c of
+// row r stored at c ^ dswz(r): any 16 consecutive rows read at one chunk hit 16 different
+// bank groups (and any 8 consecutive rows 8).  A load fills 64 consecutive 16-byte slots of
+// a stage (16 rows): lane slot s holds row s / 4, stored chunk s % 4.  Requires T and the
+// split length to be multiples of 32 and 16-byte aligned rows; rows past R or S are read
+// from row R-1 / S-1 (their outputs are not stored).
+constexpr int DGT = 512;                                 // threads (8 waves)
+constexpr int DR = 256, DS = 256, DT = 32, DSTAGES = 4;
+constexpr int DA_BYTES = DR * DT * 2;                    // 16 KB
+constexpr int DB_BYTES = DS * DT * 2;                    // 16 KB
+constexpr int DSTAGE = DA_BYTES + DB_BYTES;
+constexpr int DA_LOADS = DA_BYTES / (DGT * 16), DB_LOADS = DB_BYTES / (DGT * 16);
+constexpr int DLOADS = DA_LOADS + DB_LOADS;
+static_assert(DA_LOADS == 2 && DB_LOADS == 2, "load split");
+
+__device__ __forceinline__ int dswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ void barrier_only() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
+    __shared__ __attribute__((aligned(16))) char smem[DSTAGES * DSTAGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int r32 = lane & 31, g = lane >> 5;
+    int rt, st;
+    {   // grouped, XCD-aware tile order (as in the staged kernel above), groups of 4 row tiles
+        const int n_rt = static_cast<int>((p.R + DR - 1) / DR), n_st = (p.S + DS - 1) / DS;
+        const int nwg = gridDim.x, bid = blockIdx.x;
+        const int qx = nwg >> 3, rx = nwg & 7, xcd = bid & 7, idx = bid >> 3;
+        const int tile = (xcd < rx ? xcd * (qx + 1) : rx * (qx + 1) + (xcd - rx) * qx) + idx;
+        constexpr int GM = 4;
+        const int grp = tile / (GM * n_st), in_g = tile % (GM * n_st);
+        const int gm = n_rt - grp * GM < GM ? n_rt - grp * GM : GM;
+        rt = grp * GM + in_g % gm;
+        st = in_g / gm;
+    }
+    const int64_t r0 = static_cast<int64_t>(rt) * DR;
+    const int s0 = st * DS;
+    const int64_t t_begin = static_cast<int64_t>(blockIdx.z) * p.t_per_split;
+    const int64_t t_end = t_begin + p.t_per_split < p.T ? t_begin + p.t_per_split : p.T;
+    const int n = t_end > t_begin ? static_cast<int>((t_end - t_begin) / DT) : 0;
+
+    // per-lane byte offsets of the loads from the wave-uniform step bases
+    uint32_t a_off[DA_LOADS], b_off[DB_LOADS];
+#pragma unroll
+    for (int i = 0; i < DA_LOADS; ++i) {
+        const int sl = (wave * DA_LOADS + i) * 64 + lane, row = sl >> 2, c = (sl & 3) ^ dswz(row);
+        const int64_t rr = r0 + row < p.R ? row : p.R - 1 - r0;
+        a_off[i] = static_cast<uint32_t>((rr * p.lda + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < DB_LOADS; ++i) {
+        const int sl = (wave * DB_LOADS + i) * 64 + lane, row = sl >> 2, c = (sl & 3) ^ dswz(row);
+        const int64_t rr = s0 + row < p.S ? row : p.S - 1 - s0;
+        b_off[i] = static_cast<uint32_t>((rr * p.ldb + 8 * c) * 2);
+    }
+    const uint16_t *a_row0 = static_cast<const uint16_t *>(p.A) + r0 * p.lda;
+    const uint16_t *b_row0 = p.B + static_cast<int64_t>(s0) * p.ldb;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    auto issue = [&](int kt, int sg) {
+        const int64_t t = t_begin + static_cast<int64_t>(kt) * DT;
+        const uint32_t dst = lds0 + sg * DSTAGE;
+#pragma unroll
+        for (int i = 0; i < DA_LOADS; ++i) dma16(a_row0 + t, a_off[i], dst + (wave * DA_LOADS + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < DB_LOADS; ++i) dma16(b_row0 + t, b_off[i], dst + DA_BYTES + (wave * DB_LOADS + i) * 1024);
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    // fragment offsets in a stage: A row wr*64 + mi*32 + r32, B row wc*128 + ni*32 + r32,
+    // logical chunk 2 ks + g
+    int fa[2][2], fb[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            const int row = wr * 64 + mi * 32 + r32;
+            fa[mi][ks] = row * 64 + 16 * ((2 * ks + g) ^ dswz(row));
+        }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int row = wc * 128 + ni * 32 + r32;
+            fb[ni][ks] = DA_BYTES + row * 64 + 16 * ((2 * ks + g) ^ dswz(row));
+        }
+    }
+    auto step = [&](int kt, auto sc) {
+        constexpr int SG = decltype(sc)::value;
+        // tile kt has landed once at most the loads of the tiles after it are outstanding
+        if (kt + 2 < n) wait_vmcnt<2 * DLOADS>();
+        else if (kt + 1 < n) wait_vmcnt<DLOADS>();
+        else wait_vmcnt<0>();
+        barrier_only();   // every wave's part of tile kt is in LDS; the stage of kt - 1 is free
+        if (kt + 3 < n) issue(kt + 3, (SG + 3) % DSTAGES);
+        if (p.seg_steps && kt > 0 && (kt * DT) % (p.seg_steps * BT) == 0) {
+            const float r = p.seg_ratio[kt * DT / (p.seg_steps * BT) - 1];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] *= r;
+        }
+        const char *sb = smem + SG * DSTAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 av[2], bv[4];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) av[mi] = *reinterpret_cast<const bf16x8 *>(sb + fa[mi][ks]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) bv[ni] = *reinterpret_cast<const bf16x8 *>(sb + fb[ni][ks]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+        }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        if (i < n) issue(i, i);
+    int kt = 0;
+    for (; kt + 4 <= n; kt += 4) {
+        step(kt, S0{});
+        step(kt + 1, S1{});
+        step(kt + 2, S2{});
+        step(kt + 3, S3{});
+    }
+    if (kt < n) step(kt, S0{});
+    if (kt + 1 < n) step(kt + 1, S1{});
+    if (kt + 2 < n) step(kt + 2, S2{});
+
+    // C block (mi, ni): lane holds rows 8*(e/4) + 4*g + e%4, column r32
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int col = s0 + wc * 128 + ni * 32 + r32;
+            if (col >= p.S) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                int64_t row = r0 + wr * 64 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                if (row < p.R) {
+                    float *cm = p.C;
+                    if (p.c_rows) {
+                        if (row >= 2 * p.c_rows) {
+                            cm = p.C2;
+                            row -= 2 * p.c_rows;
+                        } else if (row >= p.c_rows) {
+                            cm = p.C1;
+                            row -= p.c_rows;
+                        }
+                        if (!cm) continue;
+                    }
+                    float *o = cm + row * p.S + col;
+                    const float v = acc[mi][ni][e] * p.scale;
+                    if (p.atomic == 1) atomicAdd(o, v);
+                    else if (p.atomic == 2) *o += v;
+                    else *o = v;
+                }
+            }
+        }
+}
+
+// The direct-load kernel takes the product when A is bf16, the contraction and the split
+// are multiples of its step, rows are 16-byte aligned and a tile's loads stay within 32-bit
+// offsets.
+static bool dma_ok(const NtGemmArgs &a) {
+    return a.a_bf16 && a.T % DT == 0 && a.t_per_split % DT == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+           reinterpret_cast<uintptr_t>(a.A) % 16 == 0 && reinterpret_cast<uintptr_t>(a.B) % 16 == 0 &&
+           static_cast<int64_t>(DS) * (a.lda > a.ldb ? a.lda : a.ldb) * 2 < (int64_t(1) << 31);
+}
+
+static dim3 dma_grid(const NtGemmArgs &a, int64_t splits) {
+    return dim3(static_cast<unsigned>(((a.R + DR - 1) / DR) * ((a.S + DS - 1) / DS)), 1, static_cast<unsigned>(splits));
 }
 
 __device__ __forceinline__ float silu_grad(float z) {
@@ -862,7 +1057,8 @@ hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t
             ga.atomic = l > 0 ? 2 : 0;
         }
         ga.t_per_split = ga.T;
-        if (dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
+        if (dma_ok(ga)) hipLaunchKernelGGL(nt_gemm_dma_kernel, dma_grid(ga, 1), dim3(DGT), 0, s, ga);
+        else if (dy_bf16) hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
         else hipLaunchKernelGGL((nt_gemm_kernel<false>), grid, dim3(GT), 0, s, ga);
     }
     timing_end(FAM_BWD_G, s);
@@ -967,11 +1163,14 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
         ga.C1 = dw[1];
         ga.C2 = nseg > 2 ? dw[2] : nullptr;
     }
-    const int64_t tiles = static_cast<int64_t>((K + BS - 1) / BS) * ((R + BR - 1) / BR);
+    ga.t_per_split = ldm;
+    const bool dma = dma_ok(ga);
+    const int64_t tiles = dma ? static_cast<int64_t>((K + DS - 1) / DS) * ((R + DR - 1) / DR)
+                              : static_cast<int64_t>((K + BS - 1) / BS) * ((R + BR - 1) / BR);
     // split the tokens over workgroups (fp32 atomics) when there are too few tiles for 256
     // CUs x 2: the smallest split count, each split >= 8 steps, whose last wave of workgroups
     // is at least 85 % full (or the best of those tried)
-    const int64_t slots = 512;
+    const int64_t slots = dma ? 256 : 512;   // co-resident workgroups on 256 CUs
     const int64_t max_splits = std::min<int64_t>(64, std::max<int64_t>(1, (ldm + 8 * BT - 1) / (8 * BT)));
     int64_t splits = 1;
     double best = -1.0;
@@ -995,7 +1194,8 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
             if (dw[j] && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
     timing_begin(FAM_BWD_DW, s);
-    hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
+    if (dma) hipLaunchKernelGGL(nt_gemm_dma_kernel, grid, dim3(DGT), 0, s, ga);
+    else hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
     timing_end(FAM_BWD_DW, s);
     return hipGetLastError();
 }

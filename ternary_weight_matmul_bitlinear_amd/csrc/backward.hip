@@ -337,25 +337,26 @@ __global__ __launch_bounds__(GT, 2) void nt_gemm_kernel(NtGemmArgs p) {
 }
 
 // The same product for bf16 A, fed by direct-to-LDS 16-byte loads (no register staging)
-// through a ring of DSTAGES buffers of 32-deep contraction steps: tile kt + 3 is requested
-// while tile kt is multiplied.  One workgroup of 8 waves per CU, tiles of 256 x 256 (4 x 2
-// waves, each 64 x 128 = 2 x 4 MFMA blocks: 6 operand reads per 8 MFMAs, 32 KB of operands
-// per 128 MFMAs).  An LDS tile row is 32 bf16 = 64 bytes, four 16-byte chunks, chunk c of
-// row r stored at c ^ dswz(r): any 16 consecutive rows read at one chunk hit 16 different
-// bank groups (and any 8 consecutive rows 8).  A load fills 64 consecutive 16-byte slots of
-// a stage (16 rows): lane slot s holds row s / 4, stored chunk s % 4.  Requires T and the
-// split length to be multiples of 32 and 16-byte aligned rows; rows past R or S are read
-// from row R-1 / S-1 (their outputs are not stored).
+// into two LDS buffers of 64-deep contraction steps: tile kt + 1 is requested while tile kt
+// is multiplied.  One workgroup of 8 waves per CU, tiles of 256 x 256 (4 x 2 waves, each
+// 64 x 128 = 2 x 4 MFMA blocks: 6 operand reads per 8 MFMAs, 64 KB of operands per 256
+// MFMAs).  The loads, not the matrix cores, set the pace (the texture data path is busy
+// most of the time), so the tile is as large as the accumulators allow and each step reads
+// whole 128-byte lines of every row (32-deep steps, half lines, took 13 % longer even with a
+// 4-buffer ring).  An LDS tile row is 64 bf16 = 128 bytes, eight 16-byte chunks, chunk c of
+// row r stored at c ^ dswz(r) (the same swizzle as the int8 GEMM's activation tile).  A load
+// fills 64 consecutive 16-byte slots of a buffer (8 rows): lane slot s holds row s / 8,
+// stored chunk s % 8.  Requires T and the split length to be multiples of 64 and 16-byte
+// aligned rows; rows past R or S are read from row R-1 / S-1 (their outputs are not stored).
 constexpr int DGT = 512;                                 // threads (8 waves)
-constexpr int DR = 256, DS = 256, DT = 32, DSTAGES = 4;
-constexpr int DA_BYTES = DR * DT * 2;                    // 16 KB
-constexpr int DB_BYTES = DS * DT * 2;                    // 16 KB
+constexpr int DR = 256, DS = 256, DT = 64, DSTAGES = 2;
+constexpr int DA_BYTES = DR * DT * 2;                    // 32 KB
+constexpr int DB_BYTES = DS * DT * 2;                    // 32 KB
 constexpr int DSTAGE = DA_BYTES + DB_BYTES;
 constexpr int DA_LOADS = DA_BYTES / (DGT * 16), DB_LOADS = DB_BYTES / (DGT * 16);
-constexpr int DLOADS = DA_LOADS + DB_LOADS;
-static_assert(DA_LOADS == 2 && DB_LOADS == 2, "load split");
+static_assert(DA_LOADS == 4 && DB_LOADS == 4, "load split");
 
-__device__ __forceinline__ int dswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int dswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 __device__ __forceinline__ void barrier_only() {
     __builtin_amdgcn_s_barrier();
@@ -389,13 +390,13 @@ __global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
     uint32_t a_off[DA_LOADS], b_off[DB_LOADS];
 #pragma unroll
     for (int i = 0; i < DA_LOADS; ++i) {
-        const int sl = (wave * DA_LOADS + i) * 64 + lane, row = sl >> 2, c = (sl & 3) ^ dswz(row);
+        const int sl = (wave * DA_LOADS + i) * 64 + lane, row = sl >> 3, c = (sl & 7) ^ dswz(row);
         const int64_t rr = r0 + row < p.R ? row : p.R - 1 - r0;
         a_off[i] = static_cast<uint32_t>((rr * p.lda + 8 * c) * 2);
     }
 #pragma unroll
     for (int i = 0; i < DB_LOADS; ++i) {
-        const int sl = (wave * DB_LOADS + i) * 64 + lane, row = sl >> 2, c = (sl & 3) ^ dswz(row);
+        const int sl = (wave * DB_LOADS + i) * 64 + lane, row = sl >> 3, c = (sl & 7) ^ dswz(row);
         const int64_t rr = s0 + row < p.S ? row : p.S - 1 - s0;
         b_off[i] = static_cast<uint32_t>((rr * p.ldb + 8 * c) * 2);
     }
@@ -420,28 +421,25 @@ __global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     // fragment offsets in a stage: A row wr*64 + mi*32 + r32, B row wc*128 + ni*32 + r32,
     // logical chunk 2 ks + g
-    int fa[2][2], fb[4][2];
+    int fa[2][4], fb[4][4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
             const int row = wr * 64 + mi * 32 + r32;
-            fa[mi][ks] = row * 64 + 16 * ((2 * ks + g) ^ dswz(row));
+            fa[mi][ks] = row * 128 + 16 * ((2 * ks + g) ^ dswz(row));
         }
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
             const int row = wc * 128 + ni * 32 + r32;
-            fb[ni][ks] = DA_BYTES + row * 64 + 16 * ((2 * ks + g) ^ dswz(row));
+            fb[ni][ks] = DA_BYTES + row * 128 + 16 * ((2 * ks + g) ^ dswz(row));
         }
     }
     auto step = [&](int kt, auto sc) {
         constexpr int SG = decltype(sc)::value;
-        // tile kt has landed once at most the loads of the tiles after it are outstanding
-        if (kt + 2 < n) wait_vmcnt<2 * DLOADS>();
-        else if (kt + 1 < n) wait_vmcnt<DLOADS>();
-        else wait_vmcnt<0>();
+        wait_vmcnt<0>();  // this wave's part of tile kt has landed (nothing later is in flight)
         barrier_only();   // every wave's part of tile kt is in LDS; the stage of kt - 1 is free
-        if (kt + 3 < n) issue(kt + 3, (SG + 3) % DSTAGES);
+        if (kt + 1 < n) issue(kt + 1, (SG + 1) % DSTAGES);
         if (p.seg_steps && kt > 0 && (kt * DT) % (p.seg_steps * BT) == 0) {
             const float r = p.seg_ratio[kt * DT / (p.seg_steps * BT) - 1];
 #pragma unroll
@@ -453,7 +451,7 @@ __global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
         }
         const char *sb = smem + SG * DSTAGE;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
             bf16x8 av[2], bv[4];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) av[mi] = *reinterpret_cast<const bf16x8 *>(sb + fa[mi][ks]);
@@ -468,21 +466,13 @@ __global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-        if (i < n) issue(i, i);
+    if (n > 0) issue(0, 0);
     int kt = 0;
-    for (; kt + 4 <= n; kt += 4) {
+    for (; kt + 2 <= n; kt += 2) {
         step(kt, S0{});
         step(kt + 1, S1{});
-        step(kt + 2, S2{});
-        step(kt + 3, S3{});
     }
     if (kt < n) step(kt, S0{});
-    if (kt + 1 < n) step(kt + 1, S1{});
-    if (kt + 2 < n) step(kt + 2, S2{});
 
     // C block (mi, ni): lane holds rows 8*(e/4) + 4*g + e%4, column r32
 #pragma unroll
@@ -517,7 +507,7 @@ __global__ __launch_bounds__(DGT, 1) void nt_gemm_dma_kernel(NtGemmArgs p) {
 }
 
 // The direct-load kernel takes the product when A is bf16, the contraction and the split
-// are multiples of its step, rows are 16-byte aligned and a tile's loads stay within 32-bit
+// are multiples of its step (64), rows are 16-byte aligned and a tile's loads stay within 32-bit
 // offsets.
 static bool dma_ok(const NtGemmArgs &a) {
     return a.a_bf16 && a.T % DT == 0 && a.t_per_split % DT == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&

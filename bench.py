@@ -578,7 +578,10 @@ def bench_backward(w, args, orc) -> dict:
                       "inputs": "bf16", "gradients": "fp32"},
            "roofline": {"kernel": "bwd_g: the seven g = s_w dy T contractions of a step (bf16 MFMA)",
                         "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / PEAK_BF16_TFLOPS if tf else None, "traffic": None,
+                        "frac": tf / PEAK_BF16_TFLOPS if tf else None,
+                        "traffic": traffic("bwd_g", f"{w.name}-backward", ("backward.hip",),
+                                           key="hbm_bytes_per_step"),
+                        "traffic_per": "step (the four g launches)",
                         "algorithmic_flops_per_step": ops, "launches_per_step": n_g / steps},
            "kernels": kern}
     if orc is not None:

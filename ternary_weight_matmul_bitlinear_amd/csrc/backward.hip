@@ -524,24 +524,53 @@ __device__ __forceinline__ float silu_grad(float z) {
     return s * (1.0f + z * (1.0f - s));
 }
 
-// W^T as bf16 values -1/0/1: out[k][n] (row stride ldo) for the packed [N][K/16] matrix;
-// thread per (k, 8 consecutive n), one 16-byte store (N % 8 == 0).
+// W^T as bf16 values -1/0/1: out[k][n] (row stride ldo) for the packed [N][K/16] matrix
+// (N % 8 == 0).  A workgroup takes 64 rows n x 32 words (512 k) of the packed matrix: the
+// words are read row by row as 16-byte vectors into LDS, then every output row k is
+// written as 64 consecutive n (eight 16-byte stores).
 __global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, int32_t N, int32_t K,
                                                         uint16_t *out, int64_t ldo) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int ng = N / 8;
-    if (i >= static_cast<int64_t>(K) * ng) return;
-    const int k = static_cast<int>(i / ng), n0 = static_cast<int>(i % ng) * 8;
-    const int KW = K / 16, sh = 8 * (k % 4) + 2 * ((k % 16) / 4);
-    uint16_t v[8];
+    __shared__ uint32_t wl[64][33];
+    const int tid = threadIdx.x;
+    const int KW = K / 16;
+    const int n0 = blockIdx.x * 64, kw0 = blockIdx.y * 32;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int code = static_cast<int>((packed[static_cast<int64_t>(n0 + e) * KW + k / 16] >> sh) & 3u);
-        v[e] = code == 2 ? 0x3F80u : (code == 0 ? 0xBF80u : 0u);
+    for (int it = 0; it < 2; ++it) {   // 64 rows x 8 vectors of 4 words
+        const int v = tid + 256 * it, r = v >> 3, c4 = 4 * (v & 7);
+        const int n = n0 + r;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (n < N) {
+            const uint32_t *src = packed + static_cast<int64_t>(n) * KW + kw0 + c4;
+            if (kw0 + c4 + 4 <= KW && (KW & 3) == 0) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(src);
+                w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (kw0 + c4 + e < KW) w[e] = src[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wl[r][c4 + e] = w[e];
     }
-    *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(k) * ldo + n0) =
-        make_uint4(v[0] | (uint32_t(v[1]) << 16), v[2] | (uint32_t(v[3]) << 16),
-                   v[4] | (uint32_t(v[5]) << 16), v[6] | (uint32_t(v[7]) << 16));
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {   // 512 rows k x 8 chunks of 8 n
+        const int v = tid + 256 * it, kl = v >> 3, nc = v & 7;
+        const int kwl = kl >> 4, j = kl & 15;
+        const int k = 16 * (kw0 + kwl) + j, n = n0 + 8 * nc;
+        if (k >= K || n >= N) continue;
+        const int sh = 8 * (j & 3) + 2 * (j >> 2);
+        uint16_t c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t code = (wl[8 * nc + e][kwl] >> sh) & 3u;
+            c[e] = code == 2 ? 0x3F80u : (code == 0 ? 0xBF80u : 0u);
+        }
+        *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(k) * ldo + n) =
+            make_uint4(c[0] | (uint32_t(c[1]) << 16), c[2] | (uint32_t(c[3]) << 16),
+                       c[4] | (uint32_t(c[5]) << 16), c[6] | (uint32_t(c[7]) << 16));
+    }
 }
 
 // Column sums folded into a transpose: out[j][c - j*cols] += sum_m src[m][c] for the columns
@@ -643,7 +672,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t
 //   OUT 0: dx = d (fp32); OUT 1: also a bf16 copy dx_bf16; OUT 2: d is the gradient at the
 //   GLU's gated product m = SiLU(gate)*up (K = F) and is carried through it: dgu [M][2F] bf16
 //   gets dgate = d*up*silu'(gate) at column c and dup = d*SiLU(gate) at F + c, gate | up from
-//   the pre-activations gu [M][2F] fp32;
+//   the pre-activations gu [M][2F] bf16;
 //   dgamma: each workgroup's sum over its rows of g*x*r into dg_part[blockIdx.x][K] (then
 //   summed over the workgroups by the column-sum kernel).
 constexpr int RV = 8;   // float4 chunks per thread (K <= 8192)
@@ -712,8 +741,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowsArgs p) {
                     d[3] += rv.w;
                 }
                 if constexpr (OUT == 2) {
-                    const float4 ga = *reinterpret_cast<const float4 *>(p.gu + m * 2 * K + c);
-                    const float4 up = *reinterpret_cast<const float4 *>(p.gu + m * 2 * K + K + c);
+                    const float4 ga = load4<true>(p.gu, m * 2 * K + c);
+                    const float4 up = load4<true>(p.gu, m * 2 * K + K + c);
                     const float gg[4] = {ga.x, ga.y, ga.z, ga.w}, uu[4] = {up.x, up.y, up.z, up.w};
                     float dga[4], dup[4];
 #pragma unroll
@@ -764,23 +793,6 @@ __global__ __launch_bounds__(256) void col_sum_kernel(const void *src, int64_t l
 __global__ void fill_zero_kernel(float *p, int64_t n) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;
-}
-
-// The GLU's gated product from the gate | up pre-activations gu [M][2F] fp32 (gate at column
-// f, up at F + f): m = SiLU(gate)*up in the activation dtype (the down projection's input);
-// thread per four consecutive f (F % 4 == 0).
-template <bool MBF16>
-__global__ __launch_bounds__(256) void glu_product_kernel(const float *gu, int64_t M, int32_t F, void *m) {
-    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (i >= M * F) return;
-    const int64_t row = i / F, f = i % F;
-    const float4 g = *reinterpret_cast<const float4 *>(gu + row * 2 * F + f);
-    const float4 u = *reinterpret_cast<const float4 *>(gu + row * 2 * F + F + f);
-    const float v0 = siluf_(g.x) * u.x, v1 = siluf_(g.y) * u.y, v2 = siluf_(g.z) * u.z, v3 = siluf_(g.w) * u.w;
-    if constexpr (MBF16)
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(m) + i) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-    else
-        *reinterpret_cast<float4 *>(static_cast<float *>(m) + i) = make_float4(v0, v1, v2, v3);
 }
 
 // ------------------------------------------------------------------ MLGRU backward
@@ -1013,10 +1025,9 @@ hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t
                         float *g, hipStream_t s) {
     if (M <= 0 || nseg < 1 || nseg > 3) return hipSuccess;
     const int64_t ldb = static_cast<int64_t>(nseg) * N;
-    const int64_t n = static_cast<int64_t>(K) * (N / 8);
+    const dim3 ge(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((K / 16 + 31) / 32));
     for (int j = 0; j < nseg; ++j)
-        hipLaunchKernelGGL(expand_wt_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                           packed[j], N, K, wt + static_cast<int64_t>(j) * N, ldb);
+        hipLaunchKernelGGL(expand_wt_kernel, ge, dim3(256), 0, s, packed[j], N, K, wt + static_cast<int64_t>(j) * N, ldb);
     // one launch over the stacked contraction when every segment boundary is a step boundary
     // and the scale ratios are finite
     bool one = N % BT == 0;
@@ -1187,15 +1198,6 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
     if (dma) hipLaunchKernelGGL(nt_gemm_dma_kernel, grid, dim3(DGT), 0, s, ga);
     else hipLaunchKernelGGL((nt_gemm_kernel<true>), grid, dim3(GT), 0, s, ga);
     timing_end(FAM_BWD_DW, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s) {
-    const int64_t n = M * F / 4;
-    if (n <= 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-    if (m_bf16) hipLaunchKernelGGL((glu_product_kernel<true>), grid, dim3(256), 0, s, gu, M, F, m);
-    else hipLaunchKernelGGL((glu_product_kernel<false>), grid, dim3(256), 0, s, gu, M, F, m);
     return hipGetLastError();
 }
 

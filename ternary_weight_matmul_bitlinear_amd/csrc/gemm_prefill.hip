@@ -72,6 +72,7 @@ __device__ __forceinline__ void unpack_codes_x2(uint32_t w0, uint32_t w1, v4i &c
 
 template <int EPI, bool OUT_BF16>
 __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
+    constexpr bool GLU = EPI == EPI_GLU || EPI == EPI_GLU_KEEP;
     __shared__ __attribute__((aligned(16))) int8_t smem[STAGES * STAGE_BYTES];
     __shared__ int32_t s_rs[BM];  // per-row activation code sum and scale of this tile
     __shared__ float s_a[BM];
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         const int s = (wave * B_LOADS + i) * 64 + lane;
         const int row = s >> 1, h = (s & 1) ^ swz_b(row);
         int r;
-        if constexpr (EPI == EPI_GLU) {
+        if constexpr (GLU) {
             // tile column c: wave wn = c / (32 NI), block ni = (c / 32) % NI, lane j = c % 32;
             // the first NI/2 blocks of a wave are gate rows, the last NI/2 the same up rows;
             // the 32 rows of one load share the block, hence the matrix (gate or up)
@@ -259,10 +260,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
     //      accesses covering whole row segments.  The staging region is private to the
     //      wave, so only wave-level ordering is needed.
     float *stg = reinterpret_cast<float *>(smem) + wave * (32 * EP_PITCH);
-    constexpr int NOB = EPI == EPI_GLU ? NI / 2 : NI;  // output blocks per 32-row slab
+    constexpr int NOB = GLU ? NI / 2 : NI;  // output blocks per 32-row slab
     // 16-byte accesses need 8-element-aligned row strides and column offsets
     const bool vec_ok = (p.ldo % 8 == 0) && (EPI != EPI_RESID || p.ldr % 8 == 0) &&
-                        (EPI == EPI_GLU || p.seg[sg].out_col0 % 8 == 0);
+                        (GLU || p.seg[sg].out_col0 % 8 == 0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         // residuals of this 32-row slab (bf16: all its blocks; fp32: loaded per block), issued
@@ -302,17 +303,17 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
         for (int ob = 0; ob < NOB; ++ob) {
             // global column of this lane's value and of the block's first column
             int col0;
-            if constexpr (EPI == EPI_GLU) {
+            if constexpr (GLU) {
                 col0 = nt * 128 + 16 * NI * wn + 32 * ob;
             } else {
                 col0 = nt * BN + wn * (32 * NI) + ob * 32;
             }
             const int col_lane = col0 + r32;
-            const Seg &S = p.seg[EPI == EPI_GLU ? 0 : sg];
+            const Seg &S = p.seg[GLU ? 0 : sg];
             const int ncols = S.n;
             if constexpr (EPI == EPI_RESID && !OUT_BF16) load_resid(ob, rvb[0]);
             float v[16];
-            if constexpr (EPI == EPI_GLU) {
+            if constexpr (GLU) {
                 const float sg0 = p.seg[0].scale, su = p.seg[1].scale;
                 const float bg = p.seg[0].bias && col_lane < ncols ? p.seg[0].bias[col_lane] : 0.0f;
                 const float bu = p.seg[1].bias && col_lane < ncols ? p.seg[1].bias[col_lane] : 0.0f;
@@ -322,6 +323,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                     const float yg = static_cast<float>(ag_) * (sg0 * a_e[e]) + bg;
                     const float yu = static_cast<float>(au) * (su * a_e[e]) + bu;
                     v[e] = siluf_(yg) * yu;
+                    if constexpr (EPI == EPI_GLU_KEEP) {
+                        const int64_t row = m0 + wm * (32 * MI) + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                        if (row < p.M && col_lane < ncols) {
+                            p.keep[row * 2 * ncols + col_lane] = f32_to_bf16_bits(yg);
+                            p.keep[row * 2 * ncols + ncols + col_lane] = f32_to_bf16_bits(yu);
+                        }
+                    }
                 }
             } else {
                 const float bb = S.bias && col_lane < ncols ? S.bias[col_lane] : 0.0f;
@@ -337,7 +345,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                     const int64_t row = m0 + wm * (32 * MI) + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
                     if (row < p.M && col_lane < ncols && p.cap.row0 <= row && row < p.cap.row1) {
                         int32_t *c = p.cap.acc + (row - p.cap.row0) * p.cap.acc_ld;
-                        if constexpr (EPI == EPI_GLU) {
+                        if constexpr (GLU) {
                             c[p.seg[0].cap_col0 + col_lane] = acc[mi][ob][e] - rs_e[e];
                             c[p.seg[1].cap_col0 + col_lane] = acc[mi][ob + NI / 2][e] - rs_e[e];
                         } else {
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_ternary_kernel(GemmArgs p) {
                 const float4 hi = *reinterpret_cast<const float4 *>(stg + rr * EP_PITCH + cc + 4);
                 float o[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 if (row >= p.M || col >= ncols) continue;
-                const int ocol = (EPI == EPI_GLU ? 0 : S.out_col0) + col;
+                const int ocol = (GLU ? 0 : S.out_col0) + col;
                 const bool full = vec_ok && col + 8 <= ncols;
                 if constexpr (EPI == EPI_RESID) {
                     const int64_t ri = row * p.ldr + ocol;
@@ -441,10 +449,11 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
     if (a_in.M <= 0) return hipSuccess;
     GemmArgs a = a_in;
     a.tiles_n_total = 0;
+    const bool glu = a.epi == EPI_GLU || a.epi == EPI_GLU_KEEP;
     for (int i = 0; i < a.nseg; ++i) {
-        const int w = a.epi == EPI_GLU ? 128 : BN;
+        const int w = glu ? 128 : BN;
         a.tiles_n[i] = (a.seg[i].n + w - 1) / w;
-        if (a.epi == EPI_GLU && i == 1) a.tiles_n[i] = 0;  // up rows ride with the gate tile
+        if (glu && i == 1) a.tiles_n[i] = 0;  // up rows ride with the gate tile
         a.tiles_n_total += a.tiles_n[i];
     }
     const int64_t tiles_m = (a.M + BM - 1) / BM;
@@ -452,6 +461,7 @@ hipError_t launch_gemm(const GemmArgs &a_in, hipStream_t s) {
     switch (a.epi) {
         case EPI_STORE: return launch_epi<EPI_STORE>(a, grid, s);
         case EPI_RESID: return launch_epi<EPI_RESID>(a, grid, s);
+        case EPI_GLU_KEEP: return launch_epi<EPI_GLU_KEEP>(a, grid, s);
         default: return launch_epi<EPI_GLU>(a, grid, s);
     }
 }

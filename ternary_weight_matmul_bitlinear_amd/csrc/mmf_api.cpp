@@ -205,7 +205,8 @@ static hipError_t quantize(const void *x, bool bf16, const float *gamma, float e
 // Prefill GEMM from quantized rows.
 static hipError_t gemm(const QBuf &qb, int64_t M, int32_t K, const Seg *segs, int nseg, int epi,
                        void *out, int32_t ldo, bool out_bf16, const void *resid, int32_t ldr,
-                       const mmf_stage_capture *cap, int32_t cap_ld, int family, hipStream_t s) {
+                       const mmf_stage_capture *cap, int32_t cap_ld, int family, hipStream_t s,
+                       uint16_t *keep = nullptr) {
     GemmArgs ga{};
     ga.A = qb.q;
     ga.rowsum = qb.rs;
@@ -225,9 +226,11 @@ static hipError_t gemm(const QBuf &qb, int64_t M, int32_t K, const Seg *segs, in
     ga.cap.q = nullptr;
     ga.cap.a = nullptr;
     ga.family = family;
+    ga.keep = keep;
     // up to kMidMaxM rows: the k-split kernel that reads the weights once (regime 3 forces
-    // the 128-row tiles at any M)
-    if (g_regime.load() != 3 && M <= kMidMaxM && mid_gemm_supported(ga)) return launch_gemm_mid(ga, s);
+    // the 128-row tiles at any M; only these keep the GLU's pre-activations)
+    if (g_regime.load() != 3 && M <= kMidMaxM && epi != EPI_GLU_KEEP && mid_gemm_supported(ga))
+        return launch_gemm_mid(ga, s);
     return launch_gemm(ga, s);
 }
 
@@ -1220,7 +1223,7 @@ size_t block_backward_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) 
     auto f4 = [](int64_t n) { return align_up(static_cast<size_t>(n) * 4); };
     auto h2 = [](int64_t n) { return align_up(static_cast<size_t>(n) * 2); };
     return 3 * qbuf_bytes(M, D) + qbuf_bytes(M, F) +                       // q of x, o, y1, m
-           f4(M * 3 * D) + 2 * f4(M * D) + f4(M * 2 * F) + f4(M * F) +     // ifg, o, y1, gate|up, m
+           f4(M * 3 * D) + 2 * f4(M * D) + h2(M * 2 * F) + f4(M * F) +     // ifg, o, y1, gate|up (bf16), m
            scan_bytes(B, T, D) +                                           // forward chunk carries
            f4(M * KN) + h2(M * 2 * F) + f4(M * D) + h2(M * D) + f4(M * D) + h2(M * 3 * D) +
                                                               // g, dgu, dy1 (+ bf16), do, d_ifg
@@ -1278,7 +1281,7 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     void *ifg = c.take<char>(static_cast<size_t>(M * 3 * D) * 4);
     void *o = c.take<char>(static_cast<size_t>(M * D) * 4);
     void *y1 = c.take<char>(static_cast<size_t>(M * D) * 4);
-    float *gu = c.take<float>(static_cast<size_t>(M * 2 * F) * 4);
+    uint16_t *gu = c.take<uint16_t>(static_cast<size_t>(M * 2 * F) * 2);
     void *m = c.take<char>(static_cast<size_t>(M * F) * 4);
     char *scan_ws = c.take<char>(scan_bytes(B, T, D));
     float *g = c.take<float>(static_cast<size_t>(M * KN) * 4);
@@ -1296,7 +1299,8 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
 #define MMF_TRY(expr, what) do { if ((e = (expr)) != hipSuccess) return hip_error(e, "block_backward " what); } while (0)
 
     // ---- forward, recomputed: i|f|g, the MLGRU with its gate (o stored), o_proj + x -> y1,
-    //      gate and up pre-activations (fp32), m = SiLU(gate)*up
+    //      m = SiLU(gate)*up from the gate|up GEMM's GLU epilogue, which also keeps the gate
+    //      and up pre-activations in bf16 for the product's backward
     const Seg sifg[3] = {seg_of(w->i, 0, 0), seg_of(w->f, D, D), seg_of(w->g, 2 * D, 2 * D)};
     const Seg so = seg_of(w->o, 0, 0);
     const Seg sgu[2] = {seg_of(w->gate, 0, 0), seg_of(w->up, F, F)};
@@ -1331,8 +1335,8 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     MMF_TRY(quantize(o, bf, w->o.norm_w, w->o.eps, M, D, qo, nullptr, stream), "quant o");
     MMF_TRY(gemm(qo, M, D, &so, 1, EPI_RESID, y1, D, bf, x, D, nullptr, 0, FAM_GEMM_O, stream), "o_proj");
     MMF_TRY(quantize(y1, bf, w->gate.norm_w, w->gate.eps, M, D, qy, nullptr, stream), "quant y1");
-    MMF_TRY(gemm(qy, M, D, sgu, 2, EPI_STORE, gu, 2 * F, false, nullptr, 0, nullptr, 0, FAM_GEMM_OTHER, stream), "gate|up");
-    MMF_TRY(launch_glu_product(gu, M, F, m, bf, stream), "glu product");
+    MMF_TRY(gemm(qy, M, D, sgu, 2, EPI_GLU_KEEP, m, F, bf, nullptr, 0, nullptr, 0, FAM_GEMM_OTHER, stream, gu),
+            "gate|up");
     MMF_TRY(quantize(m, bf, w->down.norm_w, w->down.eps, M, F, qm, nullptr, stream), "quant m");
 
     // Backward.  Each BitLinear: g = s_w dy T on the matrix cores, then the row kernel (dx,

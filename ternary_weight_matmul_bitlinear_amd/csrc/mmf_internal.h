@@ -229,7 +229,8 @@ struct Seg {
 enum Epi : int {
     EPI_STORE = 0,  // y = acc*s*a (+bias)
     EPI_RESID = 1,  // y = resid + acc*s*a (+bias)
-    EPI_GLU = 2     // segments 0,1 = gate,up: y = SiLU(gate) * up
+    EPI_GLU = 2,    // segments 0,1 = gate,up: y = SiLU(gate) * up
+    EPI_GLU_KEEP = 3  // as EPI_GLU, and gate | up also stored in bf16 to keep [M][2F]
 };
 
 // Prefill int8-MFMA GEMM with ternary weights.
@@ -250,6 +251,7 @@ struct GemmArgs {
     int32_t out_bf16;
     const void *resid;     // [M][ldr] (EPI_RESID), same dtype as out
     int32_t ldr;
+    uint16_t *keep = nullptr;  // [M][2F] bf16 gate | up pre-activations (EPI_GLU_KEEP)
     CapDev cap;            // acc capture only
     int32_t family = FAM_GEMM_OTHER;
 };
@@ -461,7 +463,7 @@ struct BwdRowsArgs {
     uint16_t *dx_bf16;      // [M][K] bf16 copy or NULL
     const void *res;        // [M][K] residual gradient added to dx, or NULL
     int32_t res_bf16;
-    const float *gu;        // GLU mode: gate | up pre-activations [M][2K] fp32 ...
+    const uint16_t *gu;     // GLU mode: gate | up pre-activations [M][2K] bf16 ...
     uint16_t *dgu;          // ... and dgate | dup [M][2K] bf16 out (dx, dx_bf16 unused)
     float *dgamma;          // [K] or NULL
     float *dg_part;         // workspace: bwd_rows_part_bytes(M, K)
@@ -474,7 +476,6 @@ hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uin
 hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int nseg,
                          int32_t N, int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT,
                          float *const *dw, float *const *db, hipStream_t s);
-hipError_t launch_glu_product(const float *gu, int64_t M, int32_t F, void *m, int m_bf16, hipStream_t s);
 hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);

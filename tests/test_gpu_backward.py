@@ -286,14 +286,15 @@ def test_block_backward_parity(orc, B, T, D, F, extras, bf, gate_mode):
     _block_checks(got, ref, D, BB_TOL)
 
 
-def test_block_backward_full_size_prefix(orc):
-    """The 370M block at the benchmark's size (8 x 2048 tokens, bf16), with dy non-zero only
-    on the first 64 tokens of every sequence and no final-state gradient: the reverse
-    recurrence then carries nothing from the later tokens and their rows contribute nothing
-    to the parameter gradients, so every gradient equals the oracle's on the 8 x 64 prefix,
-    and dx is zero beyond it."""
-    w = synth.WORKLOADS["370M-block"]
-    B, T, D, F, P = w.B, w.T, w.D, w.F, 64
+@pytest.mark.parametrize("name,P", [("370M-block", 64), ("2.7B-block", 8)])
+def test_block_backward_full_size_prefix(orc, name, P):
+    """A block at the benchmark's size (370M: 8 x 2048 tokens, 2.7B: 16 x 2048, bf16), with
+    dy non-zero only on the first P tokens of every sequence and no final-state gradient: the
+    reverse recurrence then carries nothing from the later tokens and their rows contribute
+    nothing to the parameter gradients, so every gradient equals the oracle's on the B x P
+    prefix, and dx is zero beyond it."""
+    w = synth.WORKLOADS[name]
+    B, T, D, F = w.B, w.T, w.D, w.F
     note(f"block_backward full size B={B} T={T} D={D} F={F}, dy on the first {P} tokens")
     blk, W, kw = _block(orc, 4321, D, F, True)
     x = synth.activations(w)

@@ -525,15 +525,19 @@ __device__ __forceinline__ float silu_grad(float z) {
 }
 
 // W^T as bf16 values -1/0/1: out[k][n] (row stride ldo) for the packed [N][K/16] matrix
-// (N % 8 == 0).  A workgroup takes 64 rows n x 32 words (512 k) of the packed matrix: the
+// (N % 8 == 0); up to seven matrices per launch (blockIdx.z).  A workgroup takes 64 rows n x 32 words (512 k) of the packed matrix: the
 // words are read row by row as 16-byte vectors into LDS, then every output row k is
 // written as 64 consecutive n (eight 16-byte stores).
-__global__ __launch_bounds__(256) void expand_wt_kernel(const uint32_t *packed, int32_t N, int32_t K,
-                                                        uint16_t *out, int64_t ldo) {
+__global__ __launch_bounds__(256) void expand_wt_kernel(ExpandJobs jobs) {
     __shared__ uint32_t wl[64][33];
     const int tid = threadIdx.x;
+    const uint32_t *packed = jobs.packed[blockIdx.z];
+    const int32_t N = jobs.N[blockIdx.z], K = jobs.K[blockIdx.z];
+    uint16_t *out = jobs.out[blockIdx.z];
+    const int64_t ldo = jobs.ldo[blockIdx.z];
     const int KW = K / 16;
     const int n0 = blockIdx.x * 64, kw0 = blockIdx.y * 32;
+    if (n0 >= N || kw0 >= KW) return;   // (the grid covers the largest matrix of the launch)
 #pragma unroll
     for (int it = 0; it < 2; ++it) {   // 64 rows x 8 vectors of 4 words
         const int v = tid + 256 * it, r = v >> 3, c4 = 4 * (v & 7);
@@ -673,8 +677,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t
 //   GLU's gated product m = SiLU(gate)*up (K = F) and is carried through it: dgu [M][2F] bf16
 //   gets dgate = d*up*silu'(gate) at column c and dup = d*SiLU(gate) at F + c, gate | up from
 //   the pre-activations gu [M][2F] bf16;
-//   dgamma: each workgroup's sum over its rows of g*x*r into dg_part[blockIdx.x][K] (then
-//   summed over the workgroups by the column-sum kernel).
+//   dgamma: each workgroup's sum over its rows of g*x*r into dg_part[blockIdx.x][K], then
+//   summed over the workgroups by the column-sum kernel (one fp32 atomic per column per 768
+//   workgroups contended more than the two launches cost).
 constexpr int RV = 8;   // float4 chunks per thread (K <= 8192)
 
 template <bool XBF16>
@@ -767,7 +772,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdRowsArgs p) {
             }
         }
     }
-    if (p.dg_part) {
+    if (p.dgamma) {
 #pragma unroll
         for (int j = 0; j < RV; ++j) {
             const int c = 4 * tid + 1024 * j;
@@ -788,6 +793,16 @@ __global__ __launch_bounds__(256) void col_sum_kernel(const void *src, int64_t l
     float s = 0.0f;
     for (int64_t r = r0; r < r1; ++r) s += load_act<BF16>(src, r * lds + c);
     atomicAdd(&out[c], s);
+}
+
+// Several arrays zeroed by one launch: blockIdx.y picks the array, the workgroups along x
+// stride over it.
+__global__ __launch_bounds__(256) void fill_zero_many_kernel(ZeroJobs j) {
+    float *p = j.p[blockIdx.y];
+    const int64_t n = j.n[blockIdx.y];
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = 0.0f;
 }
 
 __global__ void fill_zero_kernel(float *p, int64_t n) {
@@ -1000,6 +1015,24 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
 
 }  // namespace
 
+hipError_t launch_fill_zero_many(const ZeroJobs &j, hipStream_t s) {
+    ZeroJobs c{};
+    int nj = 0;
+    int64_t mx = 0;
+    for (int i = 0; i < j.count && i < ZeroJobs::kMax; ++i)
+        if (j.p[i] && j.n[i] > 0) {
+            c.p[nj] = j.p[i];
+            c.n[nj] = j.n[i];
+            mx = std::max(mx, j.n[i]);
+            ++nj;
+        }
+    if (!nj) return hipSuccess;
+    c.count = nj;
+    const int64_t wg = std::min<int64_t>((mx + 255) / 256, 2048);
+    hipLaunchKernelGGL(fill_zero_many_kernel, dim3(static_cast<unsigned>(wg), static_cast<unsigned>(nj)), dim3(256), 0, s, c);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
     if (n <= 0 || !p) return hipSuccess;
     hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p, n);
@@ -1009,8 +1042,8 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
 hipError_t launch_col_sum(const void *src, int bf16, int64_t lds, int64_t R, int32_t C, float *out,
                           hipStream_t s) {
     if (R <= 0 || C <= 0) return hipSuccess;
-    // about 64 rows per workgroup, at most 4096 row splits
-    int64_t splits = (R + 63) / 64;
+    // about 16 rows per workgroup, at most 4096 row splits
+    int64_t splits = (R + 15) / 16;
     if (splits > 4096) splits = 4096;
     const int32_t rows_per = static_cast<int32_t>((R + splits - 1) / splits);
     splits = (R + rows_per - 1) / rows_per;
@@ -1020,14 +1053,37 @@ hipError_t launch_col_sum(const void *src, int bf16, int64_t lds, int64_t R, int
     return hipGetLastError();
 }
 
+hipError_t launch_expand_wt(const ExpandJobs &j, hipStream_t s) {
+    if (j.count <= 0) return hipSuccess;
+    int32_t mn = 0, mk = 0;
+    for (int i = 0; i < j.count; ++i) {
+        mn = std::max(mn, j.N[i]);
+        mk = std::max(mk, j.K[i]);
+    }
+    const dim3 ge(static_cast<unsigned>((mn + 63) / 64), static_cast<unsigned>((mk / 16 + 31) / 32),
+                  static_cast<unsigned>(j.count));
+    hipLaunchKernelGGL(expand_wt_kernel, ge, dim3(256), 0, s, j);
+    return hipGetLastError();
+}
+
 hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *const *packed,
                         const float *scales, int nseg, int32_t N, int32_t K, int64_t M, uint16_t *wt,
-                        float *g, hipStream_t s) {
+                        int expanded, float *g, hipStream_t s) {
     if (M <= 0 || nseg < 1 || nseg > 3) return hipSuccess;
     const int64_t ldb = static_cast<int64_t>(nseg) * N;
-    const dim3 ge(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((K / 16 + 31) / 32));
-    for (int j = 0; j < nseg; ++j)
-        hipLaunchKernelGGL(expand_wt_kernel, ge, dim3(256), 0, s, packed[j], N, K, wt + static_cast<int64_t>(j) * N, ldb);
+    if (!expanded) {
+        ExpandJobs ej{};
+        for (int j = 0; j < nseg; ++j) {
+            ej.packed[j] = packed[j];
+            ej.N[j] = N;
+            ej.K[j] = K;
+            ej.out[j] = wt + static_cast<int64_t>(j) * N;
+            ej.ldo[j] = ldb;
+        }
+        ej.count = nseg;
+        hipError_t e = launch_expand_wt(ej, s);
+        if (e != hipSuccess) return e;
+    }
     // one launch over the stacked contraction when every segment boundary is a step boundary
     // and the scale ratios are finite
     bool one = N % BT == 0;
@@ -1077,8 +1133,8 @@ size_t bwd_rows_part_bytes(int64_t M, int32_t K) {
 hipError_t bwd_launch_rows(const BwdRowsArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    BwdRowsArgs p = a;
-    if (!p.dgamma) p.dg_part = nullptr;
+    const BwdRowsArgs &p = a;
+    if (p.dgamma && !a.dgamma_zeroed && (e = launch_fill_zero(p.dgamma, a.K, s)) != hipSuccess) return e;
     const int64_t nwg = rows_grid(a.M);
     const dim3 grid(static_cast<unsigned>(nwg));
     const int rk = a.res ? (a.res_bf16 ? 1 : 2) : 0;
@@ -1098,10 +1154,7 @@ hipError_t bwd_launch_rows(const BwdRowsArgs &a, hipStream_t s) {
 #undef MMF_ROWS_OK
 #undef MMF_ROWS
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.dgamma) {
-        if ((e = launch_fill_zero(p.dgamma, a.K, s)) != hipSuccess) return e;
-        if ((e = launch_col_sum(p.dg_part, 0, a.K, nwg, a.K, p.dgamma, s)) != hipSuccess) return e;
-    }
+    if (p.dgamma) return launch_col_sum(p.dg_part, 0, a.K, nwg, a.K, p.dgamma, s);
     return hipSuccess;
 }
 
@@ -1122,16 +1175,16 @@ hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uin
 
 hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int nseg,
                          int32_t N, int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT,
-                         float *const *dw, float *const *db, hipStream_t s) {
+                         float *const *dw, float *const *db, int zeroed, hipStream_t s) {
     hipError_t e;
     bool any_dw = false;
     for (int j = 0; j < nseg; ++j) {
-        if (db[j] && (e = launch_fill_zero(db[j], N, s)) != hipSuccess) return e;
+        if (db[j] && !zeroed && (e = launch_fill_zero(db[j], N, s)) != hipSuccess) return e;
         any_dw = any_dw || dw[j];
     }
     if (M <= 0) {
         for (int j = 0; j < nseg; ++j)
-            if (dw[j] && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
+            if (dw[j] && !zeroed && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
         return hipSuccess;
     }
     if (!any_dw) {   // the bias gradients alone: column sums
@@ -1189,8 +1242,8 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
     per = (per + BT - 1) / BT * BT;
     splits = (ldm + per - 1) / per;
     ga.t_per_split = per;
-    ga.atomic = splits > 1 ? 1 : 0;
-    if (splits > 1)
+    ga.atomic = splits > 1 || zeroed ? 1 : 0;   // onto zeros: atomics are exact adds to 0 and then sums
+    if (splits > 1 && !zeroed)
         for (int j = 0; j < nseg; ++j)
             if (dw[j] && (e = launch_fill_zero(dw[j], static_cast<int64_t>(N) * K, s)) != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(tiles), 1, static_cast<unsigned>(splits));
@@ -1204,7 +1257,7 @@ hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *
 hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
     if (a.M <= 0) return hipSuccess;
     hipError_t e;
-    if ((e = bwd_launch_g(a.dy, a.dy_bf16, a.N, &a.packed, &a.scale, 1, a.N, a.K, a.M, a.wt, a.g, s)) != hipSuccess) return e;
+    if ((e = bwd_launch_g(a.dy, a.dy_bf16, a.N, &a.packed, &a.scale, 1, a.N, a.K, a.M, a.wt, 0, a.g, s)) != hipSuccess) return e;
     BwdRowsArgs r{};
     r.x = a.x;
     r.x_bf16 = a.x_bf16;
@@ -1220,7 +1273,7 @@ hipError_t launch_bitlinear_bwd(const BitlinearBwdArgs &a, hipStream_t s) {
     if (a.dw && (e = bwd_launch_qT(a.q, a.M, a.K, a.ldm, a.qT, s)) != hipSuccess) return e;
     float *dw = a.dw, *db = a.db;
     if (a.dw || a.db)
-        if ((e = bwd_launch_dw(a.dy, a.dy_bf16, a.N, a.a, a.M, 1, a.N, a.K, a.ldm, a.qT, a.dyaT, &dw, &db, s)) != hipSuccess) return e;
+        if ((e = bwd_launch_dw(a.dy, a.dy_bf16, a.N, a.a, a.M, 1, a.N, a.K, a.ldm, a.qT, a.dyaT, &dw, &db, 0, s)) != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -1227,7 +1227,7 @@ size_t block_backward_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) 
            scan_bytes(B, T, D) +                                           // forward chunk carries
            f4(M * KN) + h2(M * 2 * F) + f4(M * D) + h2(M * D) + f4(M * D) + h2(M * 3 * D) +
                                                               // g, dgu, dy1 (+ bf16), do, d_ifg
-           h2(std::max(3 * D * D, 2 * F * D)) +                            // bf16 W^T, stacked
+           h2(F * D) + h2(2 * F * D) + h2(D * D) + h2(3 * D * D) +         // bf16 W^T of all seven
            h2(KN * ldm) + h2(std::max(3 * D, 2 * F) * ldm) +               // q^T, (dy a)^T
            align_up(bwd_rows_part_bytes(M, static_cast<int32_t>(KN))) +   // dgamma partials
            mlgru_backward_workspace_bytes(B, T, D);
@@ -1290,7 +1290,12 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     uint16_t *dy1b = c.take<uint16_t>(static_cast<size_t>(M * D) * 2);
     float *dO = c.take<float>(static_cast<size_t>(M * D) * 4);
     uint16_t *d_ifg = c.take<uint16_t>(static_cast<size_t>(M * 3 * D) * 2);
-    uint16_t *wt = c.take<uint16_t>(static_cast<size_t>(std::max(3 * D * D, 2 * F * D)) * 2);
+    // the seven W^T in bf16, stacked per contraction: down [F][D], gate|up [D][2F], o [D][D],
+    // i|f|g [D][3D]
+    uint16_t *wt_dn = c.take<uint16_t>(static_cast<size_t>(F) * D * 2);
+    uint16_t *wt_gu = c.take<uint16_t>(static_cast<size_t>(D) * 2 * F * 2);
+    uint16_t *wt_o = c.take<uint16_t>(static_cast<size_t>(D) * D * 2);
+    uint16_t *wt_ifg = c.take<uint16_t>(static_cast<size_t>(D) * 3 * D * 2);
     uint16_t *qT = c.take<uint16_t>(static_cast<size_t>(KN * ldm) * 2);
     uint16_t *dyaT = c.take<uint16_t>(static_cast<size_t>(std::max(3 * D, 2 * F) * ldm) * 2);
     float *dg_part = c.take<float>(bwd_rows_part_bytes(M, static_cast<int32_t>(KN)));
@@ -1353,27 +1358,63 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
         r.eps = l.eps;
         r.M = M;
         r.K = K;
+        r.dgamma_zeroed = 1;
         r.dg_part = dg_part;
         return r;
     };
+    // the seven ternary matrices expanded to bf16 W^T by one launch
+    {
+        ExpandJobs ej{};
+        auto job = [&](const mmf_bitlinear &l, uint16_t *out, int64_t ldo) {
+            ej.packed[ej.count] = l.packed;
+            ej.N[ej.count] = l.N;
+            ej.K[ej.count] = l.K;
+            ej.out[ej.count] = out;
+            ej.ldo[ej.count++] = ldo;
+        };
+        job(w->down, wt_dn, D);
+        job(w->gate, wt_gu, 2 * F);
+        job(w->up, wt_gu + F, 2 * F);
+        job(w->o, wt_o, D);
+        job(w->i, wt_ifg, 3 * D);
+        job(w->f, wt_ifg + D, 3 * D);
+        job(w->g, wt_ifg + 2 * D, 3 * D);
+        MMF_TRY(launch_expand_wt(ej, stream), "expand");
+    }
+    // every output that is accumulated (gains, biases, weights) zeroed by one launch
+    {
+        ZeroJobs z{};
+        const int32_t gk[4] = {D, D, D, F};
+        for (int k = 0; k < 4; ++k) {
+            z.p[z.count] = G.dgamma[k];
+            z.n[z.count++] = gk[k];
+        }
+        for (int k = 0; k < 7; ++k) {
+            z.p[z.count] = G.db[k];
+            z.n[z.count++] = lin[k]->N;
+            z.p[z.count] = G.dw[k];
+            z.n[z.count++] = static_cast<int64_t>(lin[k]->N) * lin[k]->K;
+        }
+        MMF_TRY(launch_fill_zero_many(z, stream), "zero");
+    }
     // ---- down (its dx, the gradient at m, is carried through m = SiLU(gate)*up in the row kernel)
     {
         const uint32_t *pk[1] = {w->down.packed};
         const float sc[1] = {w->down.scale};
-        MMF_TRY(bwd_launch_g(dy, dyb, D, pk, sc, 1, D, F, M, wt, g, stream), "down g");
+        MMF_TRY(bwd_launch_g(dy, dyb, D, pk, sc, 1, D, F, M, wt_dn, 1, g, stream), "down g");
         BwdRowsArgs r = rows(m, w->down, F);
         r.gu = gu;
         r.dgu = dgu;
         r.dgamma = G.dgamma[3];
         MMF_TRY(bwd_launch_rows(r, stream), "down rows");
         if (G.dw[6]) MMF_TRY(bwd_launch_qT(qm.q, M, F, ldm, qT, stream), "down qT");
-        MMF_TRY(bwd_launch_dw(dy, dyb, D, qm.a, M, 1, D, F, ldm, qT, dyaT, &G.dw[6], &G.db[6], stream), "down dw");
+        MMF_TRY(bwd_launch_dw(dy, dyb, D, qm.a, M, 1, D, F, ldm, qT, dyaT, &G.dw[6], &G.db[6], 1, stream), "down dw");
     }
     // ---- gate | up: dy1 = dy + gate^T(dgate) + up^T(dup)
     {
         const uint32_t *pk[2] = {w->gate.packed, w->up.packed};
         const float sc[2] = {w->gate.scale, w->up.scale};
-        MMF_TRY(bwd_launch_g(dgu, 1, 2 * F, pk, sc, 2, F, D, M, wt, g, stream), "gate|up g");
+        MMF_TRY(bwd_launch_g(dgu, 1, 2 * F, pk, sc, 2, F, D, M, wt_gu, 1, g, stream), "gate|up g");
         BwdRowsArgs r = rows(y1, w->gate, D);
         r.dx = dy1;
         r.dx_bf16 = dy1b;
@@ -1382,19 +1423,19 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
         r.dgamma = G.dgamma[2];
         MMF_TRY(bwd_launch_rows(r, stream), "gate|up rows");
         if (G.dw[4] || G.dw[5]) MMF_TRY(bwd_launch_qT(qy.q, M, D, ldm, qT, stream), "gate|up qT");
-        MMF_TRY(bwd_launch_dw(dgu, 1, 2 * F, qy.a, M, 2, F, D, ldm, qT, dyaT, &G.dw[4], &G.db[4], stream), "gate|up dw");
+        MMF_TRY(bwd_launch_dw(dgu, 1, 2 * F, qy.a, M, 2, F, D, ldm, qT, dyaT, &G.dw[4], &G.db[4], 1, stream), "gate|up dw");
     }
     // ---- o_proj: do = o^T(dy1)
     {
         const uint32_t *pk[1] = {w->o.packed};
         const float sc[1] = {w->o.scale};
-        MMF_TRY(bwd_launch_g(dy1b, 1, D, pk, sc, 1, D, D, M, wt, g, stream), "o g");
+        MMF_TRY(bwd_launch_g(dy1b, 1, D, pk, sc, 1, D, D, M, wt_o, 1, g, stream), "o g");
         BwdRowsArgs r = rows(o, w->o, D);
         r.dx = dO;
         r.dgamma = G.dgamma[1];
         MMF_TRY(bwd_launch_rows(r, stream), "o rows");
         if (G.dw[3]) MMF_TRY(bwd_launch_qT(qo.q, M, D, ldm, qT, stream), "o qT");
-        MMF_TRY(bwd_launch_dw(dy1b, 1, D, qo.a, M, 1, D, D, ldm, qT, dyaT, &G.dw[3], &G.db[3], stream), "o dw");
+        MMF_TRY(bwd_launch_dw(dy1b, 1, D, qo.a, M, 1, D, D, ldm, qT, dyaT, &G.dw[3], &G.db[3], 1, stream), "o dw");
     }
 #undef MMF_TRY
     // ---- the MLGRU with its output gate
@@ -1421,7 +1462,7 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
     {
         const uint32_t *pk[3] = {w->i.packed, w->f.packed, w->g.packed};
         const float sc[3] = {w->i.scale, w->f.scale, w->g.scale};
-        MMF_TRY(bwd_launch_g(d_ifg, 1, 3 * D, pk, sc, 3, D, D, M, wt, g, stream), "ifg g");
+        MMF_TRY(bwd_launch_g(d_ifg, 1, 3 * D, pk, sc, 3, D, D, M, wt_ifg, 1, g, stream), "ifg g");
         BwdRowsArgs r = rows(x, w->i, D);
         r.dx = dx;
         r.res = dy1;
@@ -1429,7 +1470,7 @@ int block_backward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, i
         r.dgamma = G.dgamma[0];
         MMF_TRY(bwd_launch_rows(r, stream), "ifg rows");
         if (G.dw[0] || G.dw[1] || G.dw[2]) MMF_TRY(bwd_launch_qT(qx.q, M, D, ldm, qT, stream), "ifg qT");
-        MMF_TRY(bwd_launch_dw(d_ifg, 1, 3 * D, qx.a, M, 3, D, D, ldm, qT, dyaT, &G.dw[0], &G.db[0], stream), "ifg dw");
+        MMF_TRY(bwd_launch_dw(d_ifg, 1, 3 * D, qx.a, M, 3, D, D, ldm, qT, dyaT, &G.dw[0], &G.db[0], 1, stream), "ifg dw");
     }
 #undef MMF_TRY
     return MMF_OK;

@@ -445,11 +445,21 @@ hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s);
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s);
 // backward pieces (backward.hip).  Up to three linears that share an input are handled
 // together: their output gradients sit side by side in dy [M][ldy] (N columns each).
+// Ternary matrices expanded to bf16 W^T: out[k][n] (row stride ldo) = T[n][k], up to seven
+// per launch.
+struct ExpandJobs {
+    const uint32_t *packed[7];
+    int32_t N[7], K[7];
+    uint16_t *out[7];
+    int64_t ldo[7];
+    int32_t count;
+};
+hipError_t launch_expand_wt(const ExpandJobs &j, hipStream_t s);
 // g = sum_j scale_j * dy_j T_j  [M][K] fp32 (one launch when N % 64 == 0); wt: [K][nseg*N]
-// bf16 scratch.
+// bf16, filled here unless `expanded` (then it already holds the stacked W^T).
 hipError_t bwd_launch_g(const void *dy, int dy_bf16, int64_t ldy, const uint32_t *const *packed,
                         const float *scales, int nseg, int32_t N, int32_t K, int64_t M, uint16_t *wt,
-                        float *g, hipStream_t s);
+                        int expanded, float *g, hipStream_t s);
 // dx / dgamma from g (and the residual gradient, and the GLU product's backward)
 struct BwdRowsArgs {
     const void *x;          // [M][K] forward input of the normalisation
@@ -466,16 +476,26 @@ struct BwdRowsArgs {
     const uint16_t *gu;     // GLU mode: gate | up pre-activations [M][2K] bf16 ...
     uint16_t *dgu;          // ... and dgate | dup [M][2K] bf16 out (dx, dx_bf16 unused)
     float *dgamma;          // [K] or NULL
+    int32_t dgamma_zeroed;  // the caller has zeroed dgamma
     float *dg_part;         // workspace: bwd_rows_part_bytes(M, K)
 };
 size_t bwd_rows_part_bytes(int64_t M, int32_t K);
 hipError_t bwd_launch_rows(const BwdRowsArgs &a, hipStream_t s);
 hipError_t bwd_launch_qT(const int8_t *q, int64_t M, int32_t K, int64_t ldm, uint16_t *qT, hipStream_t s);
 // dW_j = (dy_j a)^T q  [N][K] each, into dw[j] (NULL: not wanted); db_j = sum_M dy_j into db[j]
-// (NULL: not wanted).  dyaT: [nseg*N][ldm] bf16 scratch; qT from bwd_launch_qT.
+// (NULL: not wanted).  dyaT: [nseg*N][ldm] bf16 scratch; qT from bwd_launch_qT.  zeroed: the
+// caller has zeroed dw and db (they are then only added to).
 hipError_t bwd_launch_dw(const void *dy, int dy_bf16, int64_t ldy, const float *a, int64_t M, int nseg,
                          int32_t N, int32_t K, int64_t ldm, const uint16_t *qT, uint16_t *dyaT,
-                         float *const *dw, float *const *db, hipStream_t s);
+                         float *const *dw, float *const *db, int zeroed, hipStream_t s);
+// up to kMax arrays zeroed by one launch (NULL entries skipped)
+struct ZeroJobs {
+    static constexpr int kMax = 24;
+    float *p[kMax];
+    int64_t n[kMax];
+    int32_t count;
+};
+hipError_t launch_fill_zero_many(const ZeroJobs &j, hipStream_t s);
 hipError_t launch_embedding(const uint32_t *packed, float scale, int64_t vocab, int32_t D,
                             const int32_t *ids, int64_t m, void *x, int bf16,
                             hipStream_t s);

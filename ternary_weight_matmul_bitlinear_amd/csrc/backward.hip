@@ -603,6 +603,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const void *src, int64_t
     const int c0 = blockIdx.x * 64;
     const bool sums = cs.o[0] || cs.o[1] || cs.o[2];
     float csum = 0.0f;
+#pragma unroll 1
     for (int tm = 0; tm < 4; ++tm) {
         const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 256 + 64 * tm;
         if (m0 >= ldm) break;
@@ -943,27 +944,32 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
     const float lb = p.f_lower ? p.f_lower[d] : 0.0f;
     const float fb = p.f_bias ? p.f_bias[d] : 0.0f;
     const float gw = p.gnorm_w ? p.gnorm_w[d] : 1.0f;
-    float hprev[kBC], fz[kBC], iv[kBC], dh[kBC];
+    // per token: hprev, sigma of the forget pre-activation (taken once), i, and the gradient
+    // at h (caching sigma(i) too costs a wave of occupancy, which this latency-bound pass
+    // needs more than the sigmoids it saves)
+    float hprev[kBC], sz[kBC], iv[kBC], dh[kBC];
     float h = c == 0 ? (p.h0 ? p.h0[b * D + d] : 0.0f) : p.hin[crow * D + d];
     float gwp = 0.0f;
 #pragma unroll
     for (int k = 0; k < kBC; ++k) {
-        hprev[k] = fz[k] = iv[k] = dh[k] = 0.0f;
+        hprev[k] = sz[k] = iv[k] = dh[k] = 0.0f;
         if (k < n) {
             const int64_t row = b * p.T + t0 + k;
             iv[k] = load_act<IFGBF16>(p.ifg, row * 3 * D + d);
-            fz[k] = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d) + fb;
+            const float fzk = load_act<IFGBF16>(p.ifg, row * 3 * D + D + d) + fb;
             const float gv = load_act<IFGBF16>(p.ifg, row * 3 * D + 2 * D + d);
             const float dov = load_act<DOBF16>(p.dout, row * D + d);
-            const float f = fmaf(1.0f - lb, sigmoidf_(fz[k]), lb);
+            sz[k] = sigmoidf_(fzk);
+            const float f = fmaf(1.0f - lb, sz[k], lb);
             hprev[k] = h;
             h = f * h + (1.0f - f) * siluf_(iv[k]);
             float dho, dg;
             if (p.gate_mode == 0) {
                 const float rho = p.stats[2 * row], k3 = p.stats[2 * row + 1];
-                const float nrm = h * rho, sg = siluf_(gv);
+                const float sgg = sigmoidf_(gv);
+                const float nrm = h * rho, sg = gv * sgg;
                 dho = rho * (dov * gw * sg) - h * k3;
-                dg = dov * nrm * gw * silu_grad(gv);
+                dg = dov * nrm * gw * (sgg * (1.0f + gv * (1.0f - sgg)));
                 gwp = fmaf(dov * nrm, sg, gwp);
             } else {
                 const float s = sigmoidf_(gv);
@@ -981,7 +987,7 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
         for (int k = kBC - 1; k >= 0; --k) {
             if (k < n) {
                 G = dh[k] + fnext * G;
-                f = fmaf(1.0f - lb, sigmoidf_(fz[k]), lb);
+                f = fmaf(1.0f - lb, sz[k], lb);
                 if (k > 0) prod *= f;
                 fnext = f;
             }
@@ -998,12 +1004,12 @@ __global__ __launch_bounds__(256) void mlgru_bwd_chan_kernel(MlgruBwdArgs p) {
         for (int k = kBC - 1; k >= 0; --k) {
             if (k < n) {
                 const int64_t row = b * p.T + t0 + k;
-                const float sz = sigmoidf_(fz[k]);
-                const float f = fmaf(1.0f - lb, sz, lb);
-                const float cv = siluf_(iv[k]);
+                const float f = fmaf(1.0f - lb, sz[k], lb);
+                const float si = sigmoidf_(iv[k]);
+                const float cv = iv[k] * si;
                 G = dh[k] + fnext * G;
-                store_grad(p, row * 3 * D + d, (1.0f - f) * G * silu_grad(iv[k]));
-                const float dz = (hprev[k] - cv) * G * (1.0f - lb) * sz * (1.0f - sz);
+                store_grad(p, row * 3 * D + d, (1.0f - f) * G * (si * (1.0f + iv[k] * (1.0f - si))));
+                const float dz = (hprev[k] - cv) * G * (1.0f - lb) * sz[k] * (1.0f - sz[k]);
                 store_grad(p, row * 3 * D + D + d, dz);
                 dfb += dz;
                 fnext = f;

@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 CSRC = os.path.join(ROOT, "ternary_weight_matmul_bitlinear_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-DEFAULT_EXTRAS = "2.7B-block,370M-block,1.3B-decode@1,1.3B-decode@64"
+DEFAULT_EXTRAS = "2.7B-block,2.7B-block+hgrn,370M-block,1.3B-decode@1,1.3B-decode@64"
 DEFAULT_BACKWARD = "370M-block,2.7B-block"
 DATA = "synthetic (seeded N(0,1) activations / uniform token ids, ternary weights from N(0,0.02^2) latents)"
 
@@ -176,8 +176,12 @@ def gateup_roofline(w, M: int, n: int, ms: float, note: str) -> dict:
 
 # ------------------------------------------------------------------ prefill block
 
-def bench_block(w, args, orc) -> dict:
-    """One block over B x T tokens (the 370M and 2.7B blocks)."""
+HGRN_LAYERS, HGRN_LAYER = 32, 16
+
+
+def bench_block(w, args, orc, hgrn: bool = False) -> dict:
+    """One block over B x T tokens (the 370M and 2.7B blocks).  hgrn: with HGRN's forget-gate
+    lower bound of layer 16 of a 32-layer stack (bounds from per-layer logits ~ N(0, 1))."""
     import numpy as np
     import torch
 
@@ -186,14 +190,19 @@ def bench_block(w, args, orc) -> dict:
     dt = torch.bfloat16 if w.bf16 else torch.float32
     lat = synth.layer_latents(w, 0)
     fb = np.full(w.D, w.f_bias, np.float32) if w.f_bias else None
-    blk = api.Block.from_latents(lat, "cuda", f_bias=fb)
+    lb = None
+    if hgrn:
+        logits = synth.gaussian(w.seed + 201, (HGRN_LAYERS, w.D))
+        lb = np.ascontiguousarray(api.hgrn_lower_bounds(logits)[HGRN_LAYER])
+    blk = api.Block.from_latents(lat, "cuda", f_bias=fb, f_lower=lb)
+    name = w.name + ("+hgrn" if hgrn else "")
     x_np = synth.activations(w)
     x = torch.from_numpy(x_np).to("cuda").to(dt)
     y = torch.empty_like(x)
     h = torch.zeros((w.B, w.D), dtype=torch.float32, device="cuda")
     ws = torch.empty(api.block_workspace_bytes(blk, w.B, w.T), dtype=torch.uint8, device="cuda")
     M = w.M
-    log(f"workload {w.name}: B={w.B} T={w.T} D={w.D} F={w.F}")
+    log(f"workload {name}: B={w.B} T={w.T} D={w.D} F={w.F}")
 
     def step(i):
         api.block_forward(blk, x, h_state=h, y=y, ws=ws)
@@ -206,12 +215,15 @@ def bench_block(w, args, orc) -> dict:
     # it is launched on, so the measured stream stays close to an untimed one
     ms_step, q = timed_events(["gemm_gateup"], step, args.steps)
     n, ms = q["gemm_gateup"]
-    log(f"{w.name}: timed {args.steps} steps: {ms_step:.3f} ms/step")
+    log(f"{name}: timed {args.steps} steps: {ms_step:.3f} ms/step")
     fams = family_breakdown(step, min(args.steps, 10), gemm_families(M, w.D, w.F, 2 if w.bf16 else 4))
-    out = {"workload": w.name, "value": M / (ms_step * 1e-3), "unit": "tokens/s",
-           "ms_per_step": ms_step, "steps": args.steps,
-           "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "F": w.F, "layers": 1,
-                      "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"},
+    cfg = {"workload": name, "B": w.B, "T": w.T, "D": w.D, "F": w.F, "layers": 1,
+           "activations": "bf16" if w.bf16 else "fp32", "state": "fp32"}
+    if hgrn:
+        cfg["f_lower"] = (f"HGRN bounds of layer {HGRN_LAYER} of {HGRN_LAYERS} "
+                          f"(per-layer logits N(0, 1), mean bound {float(lb.mean()):.3f})")
+    out = {"workload": name, "value": M / (ms_step * 1e-3), "unit": "tokens/s",
+           "ms_per_step": ms_step, "steps": args.steps, "config": cfg,
            "roofline": gateup_roofline(w, M, n, ms, ""), "kernels": fams}
     if orc is not None:
         # the timed steps chained the state; the sample is checked on a fresh prefill
@@ -222,9 +234,9 @@ def bench_block(w, args, orc) -> dict:
         B0, T0 = min(w.B, args.cpu_seqs), min(ct, w.T)
         W = {k: orc.ternarize(lat[k]) for k in ("i", "f", "g", "o", "gate", "up", "down")}
         xs = np.ascontiguousarray(x_np[:B0, :T0])
-        orc.block(np.ascontiguousarray(xs[:1, :2]), W, f_bias=fb, resid_bf16=w.bf16)  # warm-up
+        orc.block(np.ascontiguousarray(xs[:1, :2]), W, f_bias=fb, resid_bf16=w.bf16, f_lower=lb)  # warm-up
         t = time.perf_counter()
-        r = orc.block(xs, W, f_bias=fb, resid_bf16=w.bf16)
+        r = orc.block(xs, W, f_bias=fb, resid_bf16=w.bf16, f_lower=lb)
         cdt = time.perf_counter() - t
         got = y.float().cpu().numpy()[:B0, :T0]
         out["cpu_baseline"] = {
@@ -605,7 +617,10 @@ def bench_backward(w, args, orc) -> dict:
 def run_workload(spec: str, args, orc):
     from ternary_weight_matmul_bitlinear_amd import synth
     name, _, b = spec.partition("@")
+    name, hgrn = (name[:-len("+hgrn")], True) if name.endswith("+hgrn") else (name, False)
     w = synth.WORKLOADS[name]
+    if hgrn:
+        return [bench_block(w, args, orc, hgrn=True)]
     if w.vocab:
         batches = [int(b)] if b else ([args.batch] if args.batch else [1, 64])
         return bench_decode(w, args, batches, orc)

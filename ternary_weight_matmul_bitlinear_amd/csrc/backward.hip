@@ -1048,9 +1048,10 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t s) {
 hipError_t launch_col_sum(const void *src, int bf16, int64_t lds, int64_t R, int32_t C, float *out,
                           hipStream_t s) {
     if (R <= 0 || C <= 0) return hipSuccess;
-    // about 16 rows per workgroup, at most 4096 row splits
+    // about 16 rows per workgroup (the partial sums of a few hundred to a few thousand
+    // workgroups), at most 256 row splits (so at most 256 atomics per column for long sums)
     int64_t splits = (R + 15) / 16;
-    if (splits > 4096) splits = 4096;
+    if (splits > 256) splits = 256;
     const int32_t rows_per = static_cast<int32_t>((R + splits - 1) / splits);
     splits = (R + rows_per - 1) / rows_per;
     const dim3 grid(static_cast<unsigned>((C + 255) / 256), static_cast<unsigned>(splits));

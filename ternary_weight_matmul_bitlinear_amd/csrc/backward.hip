@@ -30,7 +30,8 @@
 //     chunk's reverse scan of G_t = dh_t + f_{t+1} G_{t+1} from zero, keeping its value at
 //     the first token, the product of f over the chunk after the first token, and f at the
 //     first token;
-//   phase 3 (thread per channel): carry G backwards across chunks; dh0 = f_0 G_0;
+//   phase 3 (workgroup per 64 channels, runs of chunks folded and composed): carry G
+//     backwards across chunks; dh0 = f_0 G_0;
 //   phase 4 (as phase 2): walk the chunk backwards with the carried G:
 //     di = (1-f) G silu'(i), df_pre = (h_{t-1} - c) G (1-lb) sigma'(z).
 // Per-chunk partial sums of dgnorm_w and df_bias are reduced by a column-sum kernel.
@@ -905,19 +906,63 @@ __global__ __launch_bounds__(256) void mlgru_bwd_stats_kernel(MlgruBwdArgs p) {
 
 // Phase 3: thread per (b, d): G entering chunk c from the right (true G at chunk c+1's first
 // token) into cg[c]; dh0 = f_0 * G_0.
-__global__ __launch_bounds__(256) void mlgru_bwd_carry_kernel(MlgruBwdArgs p) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int D = p.D;
-    if (i >= p.B * D) return;
-    const int64_t b = i / D, d = i % D;
-    float Gn = 0.0f;   // true G at the first token of chunk c+1
-    for (int c = p.n_chunks - 1; c >= 0; --c) {
-        const int64_t crow = b * p.n_chunks + c;
-        p.cg[crow * D + d] = Gn;
-        const float fnext = c + 1 < p.n_chunks ? p.cf0[(crow + 1) * D + d] : 0.0f;
-        Gn = p.cb[crow * D + d] + p.cp[crow * D + d] * fnext * Gn;
+__global__ __launch_bounds__(512) void mlgru_bwd_carry_kernel(MlgruBwdArgs p) {
+    // G at the first token of chunk c: G_c = cb_c + m_c G_(c+1), m_c = cp_c f0_(c+1) (zero for
+    // the last chunk).  Workgroup per (b, 64 channels), wave s owns the s-th of 8 runs of
+    // consecutive chunks: it folds its run, right to left, into one affine map G -> A G + B
+    // (lane = channel), the maps are composed through LDS (from the last run backwards) to give
+    // the G entering every run from the right, and each wave walks its run again storing the
+    // G carried into each chunk (cg) -- the two-level scheme of the forward's carry pass.
+    constexpr int RUNS = 8;
+    __shared__ float sA[RUNS][64], sB[RUNS][64];
+    const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+    const int D = p.D, nc = p.n_chunks;
+    const int d = blockIdx.x * 64 + lane;
+    const bool live = d < D;
+    const int64_t b = blockIdx.y, row0 = b * nc;
+    const int L = (nc + RUNS - 1) / RUNS;
+    const int c0 = s * L < nc ? s * L : nc, c1 = c0 + L < nc ? c0 + L : nc;
+    // the run's m and cb are requested U chunks at a time ahead of the dependent chain; a run
+    // of at most U chunks (2048 tokens and fewer at 16 tokens per chunk) stays in registers
+    // for the second walk
+    constexpr int U = 16;
+    float mv[U], bv[U];
+    auto load_batch = [&](int ce) {   // chunks ce - u, u < U, clamped to the run
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = ce - u >= c0 ? ce - u : c0;
+            mv[u] = c + 1 < nc ? p.cp[(row0 + c) * D + d] * p.cf0[(row0 + c + 1) * D + d] : 0.0f;
+            bv[u] = p.cb[(row0 + c) * D + d];
+        }
+    };
+    const bool one_batch = c1 - c0 <= U;
+    float A = 1.0f, Bv = 0.0f;
+    if (live)
+        for (int ce = c1 - 1; ce >= c0; ce -= U) {
+            load_batch(ce);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ce - u >= c0) {
+                    Bv = fmaf(mv[u], Bv, bv[u]);
+                    A *= mv[u];
+                }
+        }
+    sA[s][lane] = A;
+    sB[s][lane] = Bv;
+    __syncthreads();
+    if (!live) return;
+    float G = 0.0f;   // entering the last chunk of run s from the right
+    for (int j = RUNS - 1; j > s; --j) G = fmaf(sA[j][lane], G, sB[j][lane]);
+    for (int ce = c1 - 1; ce >= c0; ce -= U) {
+        if (!one_batch) load_batch(ce);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ce - u >= c0) {
+                p.cg[(row0 + ce - u) * D + d] = G;
+                G = fmaf(mv[u], G, bv[u]);
+            }
     }
-    if (p.dh0) p.dh0[i] = p.cf0[b * p.n_chunks * D + d] * Gn;
+    if (s == 0 && p.dh0) p.dh0[b * D + d] = p.cf0[row0 * D + d] * G;
 }
 
 // Phases 2 and 4: thread per (b, chunk, d).  Rerun the chunk forward (state before each
@@ -1310,8 +1355,8 @@ hipError_t launch_mlgru_bwd(const MlgruBwdArgs &a, hipStream_t s) {
     else if (a.dout_bf16) hipLaunchKernelGGL((mlgru_bwd_chan_kernel<false, true, PASS>), g3, dim3(256), 0, s, a);        \
     else hipLaunchKernelGGL((mlgru_bwd_chan_kernel<false, false, PASS>), g3, dim3(256), 0, s, a);
     MMF_CHAN(0)
-    const int64_t nc = a.B * a.D;
-    hipLaunchKernelGGL(mlgru_bwd_carry_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mlgru_bwd_carry_kernel, dim3(static_cast<unsigned>((a.D + 63) / 64), static_cast<unsigned>(a.B)),
+                       dim3(512), 0, s, a);
     MMF_CHAN(1)
 #undef MMF_CHAN
     const int64_t R = a.B * a.n_chunks;

@@ -10,7 +10,8 @@ Prints one JSON line.  `roofline` describes the dominant kernel (the gate|up int
 with its launch durations from HIP events recorded on the launch stream during the timed
 steps; `cpu_baseline` is the CPU oracle timed on a bounded causal sample of the same
 workload.  `extra_workloads` carries the other shapes measured the same way: the 2.7B block
-(16 x 2048 tokens), the 370M block (8 x 2048 tokens) and the 24-layer 1.3B decode stack at
+(16 x 2048 tokens), the same block with HGRN's forget-gate lower bound (`+hgrn`), the 370M
+block (8 x 2048 tokens) and the 24-layer 1.3B decode stack at
 batch 1 and 64 (bound by HBM bandwidth; roofline of the decode BitLinear launches), then a
 block's backward (block_backward: forward recomputed, every gradient; straight-through
 BitLinear backwards on bf16 MFMA) at the 370M and 2.7B block sizes.
@@ -638,13 +639,13 @@ def main() -> int:
                     help="seconds of untimed steps before the warm-up steps (clock ramp)")
     ap.add_argument("--workload", default="2.7B-longctx",
                     help="headline workload (a name of synth.WORKLOADS, decode stacks as "
-                         "NAME@BATCH)")
+                         "NAME@BATCH, a block with HGRN bounds as NAME+hgrn)")
     ap.add_argument("--extras", default=DEFAULT_EXTRAS,
                     help="comma-separated workloads measured after the headline ('' for none)")
     ap.add_argument("--no-extras", dest="extras", action="store_const", const="")
     ap.add_argument("--backward", default=DEFAULT_BACKWARD,
-                    help="block workloads whose backward kernels are measured after the extras "
-                         "('' for none)")
+                    help="block workloads whose whole backward (block_backward) is measured "
+                         "after the extras ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="block workloads: tokens per sequence of the causal CPU sample "

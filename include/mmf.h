@@ -355,8 +355,8 @@ int stack_decode_status(const void *ws, hipStream_t stream);
  * for bf16 dy) and, for dw, the product dy*a is.  dgamma, dw and db are summed with fp32
  * atomics (the order of the sum varies between runs).  Needs N % 8 == 0, K <= 8192, every
  * pointer 16-byte aligned.  Workspace: bitlinear_backward_workspace_bytes (q, a, g, a bf16
- * copy of the ternary matrix transposed, and bf16 transposes of dy*a and q; about
- * m*(7K + 2N) + 2KN bytes). */
+ * copy of the ternary matrix transposed, bf16 transposes of dy*a and q, and per-workgroup
+ * partial sums of dgamma; about m*(7K + 2N) + 2KN + 3072K bytes). */
 size_t bitlinear_backward_workspace_bytes(const mmf_bitlinear *w, int64_t m);
 int bitlinear_backward(const mmf_bitlinear *w, const void *x, mmf_dtype x_dt, int64_t m,
                        const void *dy, mmf_dtype dy_dt, float *dx, float *dgamma, float *dw,
@@ -380,7 +380,8 @@ int mlgru_backward(const mmf_mlgru_args *args, const void *dout, mmf_dtype dout_
 /* block_backward: every gradient of block_forward (same arguments: x [B][T][D] of dtype dt,
  * h0 the initial state or NULL), given dy [B][T][D] (dy_dt, gradient at the block output)
  * and dh_last [B][D] fp32 (gradient at the final state) or NULL.  The forward is recomputed
- * (prefill kernels; the gate and up pre-activations kept in fp32), then: down's BitLinear
+ * (prefill kernels; the gate|up GEMM also keeps the gate and up pre-activations in bf16),
+ * then: down's BitLinear
  * backward gives dm; the GLU product gives dgate = dm*up*silu'(gate), dup = dm*SiLU(gate);
  * gate and up share one contraction for the input gradient (dy1 = dy + gate^T dgate +
  * up^T dup), o_proj gives the gradient at the g_norm output, the MLGRU backward d_ifg, dh0,
@@ -389,8 +390,11 @@ int mlgru_backward(const mmf_mlgru_args *args, const void *dout, mmf_dtype dout_
  * not wanted; grads itself may be NULL): dw[k] [N][K] and db[k] [N] per BitLinear (order i, f,
  * g, o, gate, up, down), dgamma[0..3] [K] for the norm gains of x (i|f|g), the g_norm output
  * (o), y1 (gate|up) and m (down), dgnorm_w [D], df_bias [D].  Needs F % 8 == 0 and F <= 8192;
- * same block limits as block_forward.  Workspace: block_backward_workspace_bytes (the
- * recomputed activations, fp32 gradients between the stages, bf16 operand copies). */
+ * same block limits as block_forward.  Gradients that feed a contraction pass between the
+ * stages in bf16 (dgate|dup, dy1's copy, d_ifg), those added as residuals in fp32; every
+ * accumulated output (dw, db, dgamma) is zeroed by the call and summed with fp32 atomics
+ * (the order of the sums varies between runs).  Workspace: block_backward_workspace_bytes
+ * (the recomputed activations, the gradients between the stages, bf16 operand copies). */
 typedef struct mmf_block_grads {
     float *dw[7];
     float *db[7];

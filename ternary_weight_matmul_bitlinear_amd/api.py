@@ -351,10 +351,16 @@ BLOCK_GAINS = ("x", "o", "y1", "m")   # inputs of i|f|g, o_proj, gate|up, down
 
 
 def block_backward(blk: "Block", x: torch.Tensor, dy: torch.Tensor, h0: torch.Tensor | None = None,
-                   dh_last: torch.Tensor | None = None, stream=None) -> dict:
+                   dh_last: torch.Tensor | None = None, grads=None, stream=None) -> dict:
     """Every gradient of block_forward (block_backward).  x [B, T, D], dy [B, T, D].  Returns
     dict of fp32 tensors: dx [B, T, D], dh0 [B, D], dw[name] [N, K] and db[name] [N] per
-    BitLinear, dgamma[input] [K] for the norm gains of x, o, y1 and m, dgnorm_w and df_bias."""
+    BitLinear, dgamma[input] [K] for the norm gains of x, o, y1 and m, dgnorm_w and df_bias.
+    grads: the parameter gradients wanted, as names "dw/<linear>", "db/<linear>",
+    "dgamma/<input>", "dgnorm_w", "df_bias" (None: all); the others are not computed and are
+    absent from the result."""
+    def want(key):
+        return grads is None or key in grads
+
     with _on(stream):
         lib = L.lib()
         x = x.contiguous()
@@ -364,21 +370,24 @@ def block_backward(blk: "Block", x: torch.Tensor, dy: torch.Tensor, h0: torch.Te
         f32 = dict(dtype=torch.float32, device=dev)
         lins = {k: getattr(blk, k) for k in BLOCK_LINEARS}
         out = {"dx": torch.empty((B, T, D), **f32), "dh0": torch.empty((B, D), **f32),
-               "dw": {k: torch.empty((l.N, l.K), **f32) for k, l in lins.items()},
-               "db": {k: torch.empty(l.N, **f32) for k, l in lins.items()},
-               "dgamma": {k: torch.empty(n, **f32) for k, n in zip(BLOCK_GAINS, (D, D, D, blk.F))},
-               "dgnorm_w": torch.empty(D, **f32), "df_bias": torch.empty(D, **f32)}
-        grads = L.mmf_block_grads((C.c_void_p * 7)(*[_ptr(out["dw"][k]) for k in BLOCK_LINEARS]),
-                                  (C.c_void_p * 7)(*[_ptr(out["db"][k]) for k in BLOCK_LINEARS]),
-                                  (C.c_void_p * 4)(*[_ptr(out["dgamma"][k]) for k in BLOCK_GAINS]),
-                                  _ptr(out["dgnorm_w"]), _ptr(out["df_bias"]))
+               "dw": {k: torch.empty((l.N, l.K), **f32) for k, l in lins.items() if want("dw/" + k)},
+               "db": {k: torch.empty(l.N, **f32) for k, l in lins.items() if want("db/" + k)},
+               "dgamma": {k: torch.empty(n, **f32) for k, n in zip(BLOCK_GAINS, (D, D, D, blk.F))
+                          if want("dgamma/" + k)}}
+        for k in ("dgnorm_w", "df_bias"):
+            if want(k):
+                out[k] = torch.empty(D, **f32)
+        grads_c = L.mmf_block_grads((C.c_void_p * 7)(*[_ptr(out["dw"].get(k)) for k in BLOCK_LINEARS]),
+                                    (C.c_void_p * 7)(*[_ptr(out["db"].get(k)) for k in BLOCK_LINEARS]),
+                                    (C.c_void_p * 4)(*[_ptr(out["dgamma"].get(k)) for k in BLOCK_GAINS]),
+                                    _ptr(out.get("dgnorm_w")), _ptr(out.get("df_bias")))
         d = blk.desc()
         nb = lib.block_backward_workspace_bytes(C.byref(d), B, T)
         ws = _workspace(nb, dev)
         L.check("block_backward",
                 lib.block_backward(C.byref(d), _ptr(x), _dt(x.dtype), B, T, _ptr(h0), _ptr(dy),
                                    _dt(dy.dtype), _ptr(dh_last), _ptr(out["dx"]), _ptr(out["dh0"]),
-                                   C.byref(grads), _ptr(ws), nb, _stream()))
+                                   C.byref(grads_c), _ptr(ws), nb, _stream()))
         return out
 
 

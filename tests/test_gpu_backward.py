@@ -311,6 +311,33 @@ def test_block_backward_full_size_prefix(orc, name, P):
     _block_checks(got, ref, D, BB_TOL, rows=rows)
 
 
+def test_block_backward_some_gradients(orc):
+    """Only some parameter gradients asked for (the others NULL): one row block of the stacked
+    gate|up and i|f|g dW launches, single bias and gain gradients (o's bias without its
+    weights), df_bias without dgnorm_w.
+    Each equals the same call's gradient with everything asked for (the same kernels; the
+    fp32 atomic sums may differ in order only)."""
+    B, T, D, F = 2, 40, 256, 704
+    blk, _, _ = _block(orc, 77, D, F, True)
+    x = dev(synth.round_to_bf16(synth.gaussian(78, (B, T, D))), torch.bfloat16)
+    dy = dev(synth.round_to_bf16(synth.gaussian(79, (B, T, D))), torch.bfloat16)
+    full = api.block_backward(blk, x, dy)
+    # o: its bias gradient without its weight gradient (the column-sum path)
+    want = {"dw/up", "dw/f", "dw/down", "db/g", "db/gate", "db/o", "dgamma/y1", "df_bias"}
+    part = api.block_backward(blk, x, dy, grads=want)
+    torch.cuda.synchronize()
+    assert set(part["dw"]) == {"up", "f", "down"} and set(part["db"]) == {"g", "gate", "o"}
+    assert set(part["dgamma"]) == {"y1"} and "dgnorm_w" not in part and "df_bias" in part
+    pairs = [(part["dx"], full["dx"]), (part["dh0"], full["dh0"]), (part["df_bias"], full["df_bias"])]
+    pairs += [(part["dw"][k], full["dw"][k]) for k in part["dw"]]
+    pairs += [(part["db"][k], full["db"][k]) for k in part["db"]]
+    pairs += [(part["dgamma"]["y1"], full["dgamma"]["y1"])]
+    for a, b in pairs:
+        a, b = host(a), host(b)
+        assert np.all(np.isfinite(a))
+        assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(b) + 1e-30
+
+
 def test_block_backward_empty(orc):
     """T = 0: dh0 = dh_last and every parameter gradient is zero."""
     blk, _, _ = _block(orc, 7, 128, 384, False)

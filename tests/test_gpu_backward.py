@@ -286,6 +286,22 @@ def test_block_backward_parity(orc, B, T, D, F, extras, bf, gate_mode):
     _block_checks(got, ref, D, BB_TOL)
 
 
+def test_block_backward_mixed_dtypes(orc):
+    """bf16 activations with an fp32 output gradient: down's g then runs on the fp32-operand
+    contraction, its dy*a transpose reads fp32 and the gate|up row kernel adds an fp32
+    residual."""
+    B, T, D, F = 2, 29, 256, 704
+    note(f"block_backward bf16 x, fp32 dy, B={B} T={T} D={D} F={F}")
+    blk, W, kw = _block(orc, 4040, D, F, True)
+    x = synth.round_to_bf16(synth.gaussian(4041, (B, T, D)))
+    dy = synth.gaussian(4042, (B, T, D))
+    h0 = synth.gaussian(4043, (B, D))
+    got = api.block_backward(blk, dev(x, torch.bfloat16), dev(dy, torch.float32), h0=dev(h0))
+    torch.cuda.synchronize()
+    ref = orc.block_backward(x, W, dy.astype(np.float64), resid_bf16=True, h0=h0, **kw)
+    _block_checks(got, ref, D, BB_TOL)
+
+
 @pytest.mark.parametrize("name,P", [("370M-block", 64), ("2.7B-block", 8)])
 def test_block_backward_full_size_prefix(orc, name, P):
     """A block at the benchmark's size (370M: 8 x 2048 tokens, 2.7B: 16 x 2048, bf16), with

@@ -615,6 +615,69 @@ def bench_backward(w, args, orc) -> dict:
     return res
 
 
+def library_gemm_reference() -> list:
+    """The vendor library's own GEMMs (hipBLASLt through torch: int8 x int8 -> int32 with
+    torch._int_mm, bf16 x bf16 -> bf16 with torch.matmul) next to the ternary int8 GEMM of
+    this library (bitlinear_forward, GEMM launch timed with the library's events) at the
+    shapes of the prefill and backward contractions, each as a fraction of its dense peak.
+    Context for the roofline fractions: what a general-purpose GEMM reaches on this part."""
+    import numpy as np
+    import torch
+
+    from ternary_weight_matmul_bitlinear_amd import api
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        spin_up(fn, 0.5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = []
+    shapes = [("2.7B gate|up", 32768, 2560, 13824), ("square-ish", 16384, 8192, 8192),
+              ("370M gate|up", 16384, 1024, 5632), ("2.7B down", 32768, 6912, 2560)]
+    for name, M, K, N in shapes:
+        ops = 2.0 * M * K * N
+        r = {"shape": name, "M": M, "K": K, "N": N}
+        g = torch.Generator(device="cuda").manual_seed(7)
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        bt = b.t()
+        ms = timed(lambda: torch._int_mm(a, bt))
+        r["hipblaslt_int8_ms"] = ms
+        r["hipblaslt_int8_frac"] = ops / (ms * 1e-3) / (PEAK_INT8_TOPS * 1e12)
+        del a, b, bt
+        q = np.random.default_rng(7).integers(-1, 2, (N, K)).astype(np.int8)
+        lin = api.TernaryLinear.from_ternary(q, 0.02, "cuda")
+        x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        api.timing_reset()
+        api.timing_families(["gemm"])
+        api.timing_enable(True)
+        timed(lambda: api.bitlinear_forward(lin, x))
+        api.timing_enable(False)
+        n, t = api.timing_query("gemm")
+        r["ternary_int8_ms"] = t / n
+        r["ternary_int8_frac"] = ops / (t / n * 1e-3) / (PEAK_INT8_TOPS * 1e12)
+        del x, lin
+        A = torch.randn(M, K, device="cuda", generator=g, dtype=torch.bfloat16)
+        B = torch.randn(N, K, device="cuda", generator=g, dtype=torch.bfloat16)
+        Bt = B.t()
+        ms = timed(lambda: torch.matmul(A, Bt))
+        r["hipblaslt_bf16_ms"] = ms
+        r["hipblaslt_bf16_frac"] = ops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+        del A, B, Bt
+        torch.cuda.empty_cache()
+        log(f"library GEMMs {name}: ternary int8 {r['ternary_int8_frac']:.3f}, hipBLASLt int8 "
+            f"{r['hipblaslt_int8_frac']:.3f}, hipBLASLt bf16 {r['hipblaslt_bf16_frac']:.3f}")
+        out.append(r)
+    return out
+
+
 def run_workload(spec: str, args, orc):
     from ternary_weight_matmul_bitlinear_amd import synth
     name, _, b = spec.partition("@")
@@ -667,6 +730,9 @@ def main() -> int:
                     help="decode stack at batch 1: also time the one-launch step (stack_decode_step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="decode stacks: time eager steps only (no HIP graph replay)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the vendor library's int8 and bf16 GEMMs (hipBLASLt) next "
+                         "to the ternary GEMM at the prefill and backward shapes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -703,6 +769,8 @@ def main() -> int:
         w3 = synth.WORKLOADS["1.3B-decode"]
         head["decode_bitlinear_kernels"] = {
             f"rows={b}": decode_kernel_sweep(b, w3.D, w3.F, w3.vocab) for b in (1, 64)}
+    if args.library_gemm:
+        head["library_gemm_reference"] = library_gemm_reference()
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

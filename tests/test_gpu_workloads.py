@@ -39,6 +39,7 @@ def _block_run(blk, x, B, T, D, F, row0, row1, ws):
     return y, h, _caps(cap)
 
 
+@pytest.mark.timeout(600)  # full-size launches checked against the CPU oracle
 @pytest.mark.parametrize("name,win", [("370M-block", 256), ("2.7B-block", 64)])
 def test_block_workload(orc, name, win):
     w = synth.WORKLOADS[name]
@@ -66,6 +67,7 @@ def test_block_workload(orc, name, win):
     e2e_checks(host(outs[0][[0, B - 1], :win]), r["y"], True)
 
 
+@pytest.mark.timeout(900)  # 24 oracle layers per step at five batch sizes
 def test_decode_stack_1p3b(orc):
     """24 layers + ternary embedding and head, one token per step with carried state."""
     w = synth.WORKLOADS["1.3B-decode"]
@@ -150,6 +152,7 @@ def test_decode_stack_1p3b(orc):
             assert div[0] <= 2e-2 and max(div) <= 0.25, div
 
 
+@pytest.mark.timeout(900)  # 32 oracle layers
 def test_longctx_stack_2p7b(orc):
     """32 layers over 2 x 32768 tokens with b_f = ln 9: captured windows at the start and
     deep in the second sequence for the first and last layer, a causal-prefix end-to-end

@@ -730,9 +730,11 @@ def main() -> int:
                     help="decode stack at batch 1: also time the one-launch step (stack_decode_step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="decode stacks: time eager steps only (no HIP graph replay)")
-    ap.add_argument("--library-gemm", action="store_true",
-                    help="also time the vendor library's int8 and bf16 GEMMs (hipBLASLt) next "
-                         "to the ternary GEMM at the prefill and backward shapes")
+    ap.add_argument("--library-gemm", dest="library_gemm", action="store_true", default=None,
+                    help="time the vendor library's int8 and bf16 GEMMs (hipBLASLt) next to the "
+                         "ternary GEMM at the prefill and backward shapes (default: with the "
+                         "extra workloads, so single-workload profiling runs leave it out)")
+    ap.add_argument("--no-library-gemm", dest="library_gemm", action="store_false")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -769,8 +771,14 @@ def main() -> int:
         w3 = synth.WORKLOADS["1.3B-decode"]
         head["decode_bitlinear_kernels"] = {
             f"rows={b}": decode_kernel_sweep(b, w3.D, w3.F, w3.vocab) for b in (1, 64)}
+    if args.library_gemm is None:
+        args.library_gemm = bool(args.extras)
     if args.library_gemm:
-        head["library_gemm_reference"] = library_gemm_reference()
+        try:
+            head["library_gemm_reference"] = library_gemm_reference()
+        except Exception as e:  # context only: never lose the measured line over it
+            head["library_gemm_reference"] = {"error": f"{type(e).__name__}: {e}"[:300]}
+        torch.cuda.empty_cache()
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

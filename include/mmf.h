@@ -257,9 +257,10 @@ int glu_forward(const mmf_bitlinear *gate, const mmf_bitlinear *up,
 
 /* One block [HL-hgrn]: x [B][T][D] (dt) -> y [B][T][D] (dt).  h_state: [B][D] fp32 state,
  * 16-byte aligned, read as h_0 and overwritten with h_T (NULL: h_0 = 0, h_T dropped).
- * T == 1 with h_state is one decode step; with B == 1 too the MLGRU step runs inside the
- * o_proj launch and h_T passes through the workspace before it reaches h_state (written by a
- * later launch of the same call, so h_state holds h_0 until the call's work completes).
+ * T == 1 with h_state is one decode step; with B <= 4 too (and D <= 4096) the MLGRU step runs
+ * inside the o_proj launch and h_T passes through the workspace before it reaches h_state
+ * (written by a later launch of the same call, so h_state holds h_0 until the call's work
+ * completes).
  * cap (nullable) records each BitLinear stage.  The workspace holds the quantized rows, the
  * projections, the scan's chunk summaries and (B*T == 1) one D-float state row. */
 size_t block_workspace_bytes(const mmf_block *w, int64_t B, int64_t T);

@@ -21,9 +21,9 @@
 //     holds nor requests unused chunks;
 //   - meanwhile the workgroup RMS/absmax-quantizes its token group (<= TG rows) into LDS
 //     (the same arithmetic as the standalone quantizer, so the int8 codes are identical),
-//     or copies rows that are already quantized; for o_proj of one token the prologue
-//     first runs the MLGRU step and g_norm from the i|f|g pre-activations and the carried
-//     state (XIN 3);
+//     or copies rows that are already quantized; for o_proj of a decode step (one token
+//     per sequence, one sequence per row of the grid) the prologue first runs the MLGRU
+//     step and g_norm from the i|f|g pre-activations and the carried state (XIN 3);
 //   - each packed word gives four dwords of 2-bit codes c = q + 1 ((w >> 2a) & 0x03030303),
 //     which one v_perm_b32 each maps to signed int8 weights (code 0,1,2 -> -1,0,+1),
 //     consumed by v_dot4_i32_i8 against the LDS-resident activations: the int32 result is
@@ -104,8 +104,8 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
 }
 
 // XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations, 3 = one MLGRU
-// step computed from the i|f|g pre-activations and the carried state (o_proj of one token;
-// activations in the output dtype), 4 = bf16 activations of a four-token group with K <= 8192
+// step computed from the i|f|g pre-activations and the carried state (o_proj of one token
+// per grid row, i.e. per sequence of a decode step; activations in the output dtype), 4 = bf16 activations of a four-token group with K <= 8192
 // held in registers from kernel entry.
 // TG: token rows per workgroup (1, 4, 8 or 16).  NW: waves per workgroup.
 // NI: 64-k chunks held per lane per pass (CB, or for one token the fewest of 1, 2, 4, 6, 8
@@ -861,7 +861,7 @@ void launch3(const GemvArgs &a, size_t lds, hipStream_t s) {
 template <int EPI>
 void launch2(const GemvArgs &a, size_t lds, hipStream_t s) {
     if constexpr (EPI == EPI_RESID) {
-        if (a.mlgru) {  // one token, K <= 4096 (checked by launch_gemv): 1, 2 or 4 chunks per lane
+        if (a.mlgru) {  // one token per grid row (sequence), K <= 4096 (checked by launch_gemv): 1, 2 or 4 chunks per lane
             const int groups = (a.K / 64 + LPR - 1) / LPR;
             if (groups <= 1) launch5<EPI, 3, 1, 4, 1>(a, lds, s);
             else if (groups <= 2) launch5<EPI, 3, 1, 4, 2>(a, lds, s);
@@ -884,10 +884,11 @@ hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
     if (a_in.epi != EPI_GLU)
         for (int i = 0; i + 1 < a_in.nseg; ++i)
             if (a_in.seg[i].n % RPW != 0) return hipErrorInvalidValue;  // segment not wave-aligned
-    if (a_in.mlgru && (a_in.epi != EPI_RESID || a_in.M != 1 || a_in.K > 4096 || !a_in.x ||
+    if (a_in.mlgru && (a_in.epi != EPI_RESID || a_in.M > 4 || a_in.K > 4096 || !a_in.x ||
                        a_in.x_bf16 != a_in.out_bf16))
-        return hipErrorInvalidValue;  // the fused MLGRU step covers one token, D <= 4096
-    if (a_in.copy_n % 4 != 0) return hipErrorInvalidValue;
+        return hipErrorInvalidValue;  // the fused MLGRU step: one token per grid row, <= 4 rows, D <= 4096
+    // the side copy: 4 floats per thread of grid row 0, at least 16 threads per weight row
+    if (a_in.copy_n % 4 != 0 || a_in.copy_n > 64LL * a_in.rows_total) return hipErrorInvalidValue;
     GemvArgs a = a_in;
     if (a.M == 1 && a.epi == EPI_STORE && a.nseg == 1 && a.x && a.x_bf16 && !a.mlgru &&
         a.copy_n == 0 && a.K <= 8192 && a.rows_total >= kStreamRows) {

@@ -75,6 +75,15 @@ static bool use_decode(int64_t m) {
     return m <= kDecodeMaxM;
 }
 
+// One-token decode steps of up to this many sequences run the MLGRU step, g_norm and
+// o_proj's quantization inside the o_proj launch (one token per workgroup row of its grid).
+constexpr int64_t kFusedStepMaxB = 4;
+
+static bool fused_step(int64_t B, int64_t T, int64_t D, int64_t F) {
+    // (the gate|up launch's side copy of the new state covers 64 floats per GLU row)
+    return T == 1 && B >= 1 && B <= kFusedStepMaxB && D <= 4096 && B * D <= 64 * F && use_decode(B);
+}
+
 // ------------------------------------------------------------------ timing
 struct TimingFamily {
     std::vector<hipEvent_t> ev;  // pairs (start, stop)
@@ -643,7 +652,7 @@ size_t block_workspace_bytes(const mmf_block *w, int64_t B, int64_t T) {
     const int64_t M = B * T, D = w->i.K, F = w->gate.N;
     return qbuf_bytes(M, std::max(D, F)) + align_up(static_cast<size_t>(M * std::max(3 * D, F)) * 4) +
            align_up(static_cast<size_t>(M * D) * 4) + scan_bytes(B, T, D) +
-           (M == 1 ? align_up(static_cast<size_t>(D) * 4) : 0);  // new state of a fused step
+           (T == 1 && B <= kFusedStepMaxB ? align_up(static_cast<size_t>(M * D) * 4) : 0);  // new state of a fused step
 }
 
 int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, int64_t T,
@@ -690,12 +699,13 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
     }
     if (e != hipSuccess) return hip_error(e, "block_forward ifg launch");
 
-    if (decode && M == 1) {
-        // one token: the MLGRU step, g_norm and o_proj's quantization run in the o_proj
-        // kernel's prologue (every workgroup recomputes the D-wide step; workgroup 0 writes
-        // the new state to the workspace, and the gate|up kernel, which runs after every
-        // reader of the old state has finished, copies it into h_state)
-        float *h_tmp = h_state ? c.take<float>(static_cast<size_t>(D) * 4) : nullptr;
+    if (fused_step(B, T, D, F)) {
+        // one token per sequence, up to kFusedStepMaxB sequences: the MLGRU step, g_norm and
+        // o_proj's quantization run in the o_proj kernel's prologue (the workgroups of grid row
+        // b take sequence b; each recomputes its D-wide step; workgroup (0, b) writes the new
+        // state to the workspace, and the gate|up kernel, which runs after every reader of the
+        // old state has finished, copies it into h_state)
+        float *h_tmp = h_state ? c.take<float>(static_cast<size_t>(M * D) * 4) : nullptr;
         GemvExtra eo;
         eo.mlgru = true;
         eo.h_prev = h_state;
@@ -711,7 +721,7 @@ int block_forward(const mmf_block *w, const void *x, mmf_dtype dt, int64_t B, in
         if (h_state) {
             eg.copy_src = h_tmp;
             eg.copy_dst = h_state;
-            eg.copy_n = D;
+            eg.copy_n = static_cast<int32_t>(M * D);
         }
         e = gemv(y1, bf, w->gate.norm_w, w->gate.eps, nullptr, M, D, gu, 2, EPI_GLU, act, F, bf, nullptr, 0, c_gu, 2 * F, stream, &eg);
         if (e == hipSuccess)

@@ -279,11 +279,12 @@ struct GemvArgs {
     int32_t ldr;
     int32_t tokens_per_group;  // rows of q staged in LDS per workgroup (<= kGemvTokens)
     CapDev cap;            // x_in/q/a written by column-block 0, acc by every block
-    // one MLGRU step as the input (mlgru != 0, one token, K = D <= 4096): x is the token's
-    // i|f|g pre-activations [3D] in the output dtype; gamma/eps are o_proj's
+    // one MLGRU step as the input (mlgru != 0, M <= 4 sequences of one token each, one per
+    // grid row, K = D <= 4096): x is [M][3D] i|f|g pre-activations in the output dtype;
+    // gamma/eps are o_proj's
     int32_t mlgru;
-    const float *h_prev;   // [D] carried state (NULL: zeros)
-    float *h_new;          // [D] new state, written by column-block 0 (NULL: not kept)
+    const float *h_prev;   // [M][D] carried state (NULL: zeros)
+    float *h_new;          // [M][D] new state, row m written by workgroup (0, m) (NULL: not kept)
     const float *f_bias;   // [D] or NULL
     const float *f_lower;  // [D] forget-gate lower bound or NULL (zeros)
     const float *gnorm_w;  // [D] or NULL (ones)

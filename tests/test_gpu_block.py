@@ -127,10 +127,11 @@ def test_block_decode_steps_match_prefill(orc):
 @pytest.mark.parametrize("B,D,F", [(1, 256, 704), (1, 4096, 256), (3, 256, 704), (4, 2048, 256),
                                    (16, 256, 704), (40, 512, 1088)])
 def test_block_one_token_steps(orc, dt, gate_mode, B, D, F):
-    """Decode steps of B sequences (one sequence: the MLGRU step, g_norm and o_proj
-    quantization run in the o_proj kernel; 3-4 sequences: scan kernel and four-token
-    weight streaming; 16 and 40 sequences: scan kernel and the k-split MFMA kernel with one
-    and two 32-row token blocks): each step is stage-checked from its capture against the
+    """Decode steps of B sequences (up to four sequences: the MLGRU step, g_norm and o_proj
+    quantization run in the o_proj kernel, one sequence per row of its grid, and 3-4
+    sequences use the four-token weight streaming; 16 and 40 sequences: scan kernel and the
+    k-split MFMA kernel with one and two 32-row token blocks): each step is stage-checked
+    from its capture against the
     oracle started from the carried state, and the sequence of steps matches the oracle's
     block end to end.  D = 256, 2048 and 4096 give one, two and four 64-channel chunks per
     lane."""

@@ -13,9 +13,10 @@
 //     rows of 8192 or more, so the row is quantized half as often); lane j of a row
 //     holds 16-byte chunks j, j+16, ... (64 k each) of the row in registers, and all of
 //     them are requested at kernel entry;
-//   - loads return in issue order, so for one token and for groups of up to four bf16
-//     tokens the activation rows (or the pre-quantized codes with their scale and code
-//     sum) are requested first, held in registers, and the weight and residual requests
+//   - loads return in issue order, so for one token (up to four token rows run one per row
+//     of the grid, the weight rows re-read for the next token coming from the same XCD's
+//     L2) the activation row (or the pre-quantized codes with their scale and code
+//     sum) is requested first, held in registers, and the weight and residual requests
 //     that follow are unconditional (clamped addresses) so every wait is exact; the number
 //     of chunks per lane is a template parameter (1, 2, 4, 6 or 8), so a short row neither
 //     holds nor requests unused chunks;
@@ -105,9 +106,9 @@ __device__ __forceinline__ int dot16(const v4i q[4], const v4i c[4], int acc) {
 
 // XIN: 0 = pre-quantized input, 1 = fp32 activations, 2 = bf16 activations, 3 = one MLGRU
 // step computed from the i|f|g pre-activations and the carried state (o_proj of one token
-// per grid row, i.e. per sequence of a decode step; activations in the output dtype), 4 = bf16 activations of a four-token group with K <= 8192
-// held in registers from kernel entry.
-// TG: token rows per workgroup (1, 4, 8 or 16).  NW: waves per workgroup.
+// per grid row, i.e. per sequence of a decode step; activations in the output dtype).
+// TG: token rows per workgroup (1, 4, 8 or 16; up to four rows, one per grid row).
+// NW: waves per workgroup.
 // NI: 64-k chunks held per lane per pass (CB, or for one token the fewest of 1, 2, 4, 6, 8
 // that cover the row, so short rows neither hold nor request unused chunks).
 template <int EPI, int XIN, bool OUT_BF16, int TG, int NW, int NI>
@@ -156,23 +157,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     const bool qearly = EARLY && XIN == 0 && K <= 32 * NT;  // code row held in registers
     uint4 xr[EARLY && XIN == 2 ? KEEP : 1];
     uint4 qr[2];
-    // four tokens (XIN 4): the same for every token of the group, S4 slices of 8 values per
-    // thread and token (8 * NT * S4 >= K), kept raw through both passes of the prologue
-    constexpr bool E4 = XIN == 4;
-    constexpr int S4 = E4 ? (NI + 1) / 2 : 1;
-    static_assert(!E4 || (TG == 4 && NW == 4 && NI <= 8), "four-token early path: TG 4, 4 waves, one pass");
-    uint4 xr4[E4 ? TG : 1][S4];
-    if constexpr (E4) {
-#pragma unroll
-        for (int t = 0; t < TG; ++t) {
-            const int64_t row = t0 + (t < mt ? t : mt - 1);
-#pragma unroll
-            for (int s4 = 0; s4 < S4; ++s4) {
-                const int k0 = tid * 8 + 8 * NT * s4;
-                xr4[t][s4] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + row * K + (k0 < K ? k0 : K - 8));
-            }
-        }
-    }
     // (requested whether or not the row fits the registers: clamped, in bounds, and unused
     // when it does not; a conditional load here would make the compiler park it in scratch)
     if constexpr (EARLY && XIN == 2) {
@@ -230,12 +214,12 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
         a_early = p.a[t0];
         rs_early = p.rowsum[t0];
     }
-    if constexpr (EARLY || E4) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
     uint4 wa[NI], wb[NI];
     auto load_pass = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            if constexpr (EARLY || E4) {
+            if constexpr (EARLY) {
                 // every slot is requested (slots past the row end re-read its last chunk)
                 int c = base + j + LPR * i;
                 c = c < NC ? c : NC - 1;
@@ -259,21 +243,19 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
     if constexpr (EPI == EPI_RESID) {
         if constexpr (EARLY) {
             resid_v = load_act<OUT_BF16>(p.resid, t0 * p.ldr + p.seg[sg].out_col0 + nn);
-        } else if constexpr (E4) {  // unconditional: token clamped to the group, row to a valid one
-            resid_v = load_act<OUT_BF16>(p.resid, (t0 + (tj < mt ? tj : mt - 1)) * p.ldr + p.seg[sg].out_col0 + nn);
         } else {
             if (rvalid && j % STRIDE == 0 && tj < mt)
                 resid_v = load_act<OUT_BF16>(p.resid, (t0 + tj) * p.ldr + p.seg[sg].out_col0 + n);
         }
     }
-    if constexpr (EARLY || E4) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- prologue
     if constexpr (XIN != 0) {
         // two straight-line passes over all TG token slots (slots past the group end read
         // the group's last row and are never stored), so the loads of every token are in
         // flight together
-        constexpr bool BF = XIN == 2 || XIN == 4;
+        constexpr bool BF = XIN == 2;
         float pm[TG], ps[TG];
         // one token: its row (<= KEEP x 8 values per thread) stays in registers between the
         // two passes
@@ -388,23 +370,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
                 }
                 continue;
             }
-            if constexpr (E4) {
-#pragma unroll
-                for (int s4 = 0; s4 < S4; ++s4) {
-                    const int k0 = tid * 8 + 8 * NT * s4;
-                    if (k0 < K) {
-                        float v[8];
-                        bf16x8_to_f32(xr4[t][s4], v);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float pj = p.gamma ? v[e] * p.gamma[k0 + e] : v[e];
-                            pm[t] = fmaxf(pm[t], fabsf(pj));
-                            ps[t] += v[e] * v[e];
-                        }
-                    }
-                }
-                continue;
-            }
             for (int k0 = tid * 8; k0 < K; k0 += 8 * NT) {
                 float v[8];
                 load8v<BF>(p.x, tok * K + k0, v);
@@ -465,19 +430,6 @@ __global__ __launch_bounds__(64 * NW) void gemv_dot4_kernel(GemvArgs p) {
             for (int it = 0; it < KEEP; ++it) {
                 const int k0 = tid * 8 + 8 * NT * it;
                 if (k0 < K) quant8(0, k0, xk[it]);
-            }
-        } else if constexpr (E4) {
-#pragma unroll
-            for (int s4 = 0; s4 < S4; ++s4) {
-                const int k0 = tid * 8 + 8 * NT * s4;
-                if (k0 < K) {
-#pragma unroll
-                    for (int t = 0; t < TG; ++t) {
-                        float v[8];
-                        bf16x8_to_f32(xr4[t][s4], v);
-                        quant8(t, k0, v);
-                    }
-                }
             }
         } else {
             for (int k0 = tid * 8; k0 < K; k0 += 8 * NT) {
@@ -820,17 +772,6 @@ void launch5(const GemvArgs &a, size_t lds, hipStream_t s) {
 
 template <int EPI, int XIN, int TG>
 void launch4(const GemvArgs &a, size_t lds, hipStream_t s) {
-    if constexpr (TG == 4 && XIN == 2) {
-        if (a.K <= 8192) {  // the group's rows held in registers from kernel entry
-            const int groups = (a.K / 64 + LPR - 1) / LPR;
-            if (groups <= 1) launch5<EPI, 4, TG, 4, 1>(a, lds, s);
-            else if (groups <= 2) launch5<EPI, 4, TG, 4, 2>(a, lds, s);
-            else if (groups <= 4) launch5<EPI, 4, TG, 4, 4>(a, lds, s);
-            else if (groups <= 6) launch5<EPI, 4, TG, 4, 6>(a, lds, s);
-            else launch5<EPI, 4, TG, 4, CB>(a, lds, s);
-            return;
-        }
-    }
     if constexpr (TG == 1) {
         if (a.K >= 8192) {
             launch5<EPI, XIN, TG, 8, CB>(a, lds, s);
@@ -909,8 +850,11 @@ hipError_t launch_gemv(const GemvArgs &a_in, hipStream_t s) {
         timing_end(FAM_GEMV, s);
         return hipGetLastError();
     }
-    // token rows per workgroup: as many as the batch needs, up to 16, within 64 KB of LDS
-    int tg = a.M <= 1 ? 1 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
+    // token rows per workgroup: up to 4 rows, one per row of the grid (each token takes the
+    // one-token kernel with its early activation fetch; the weight rows it re-reads for the
+    // next token come from the same XCD's L2); above, groups of 8 or 16 rows within 64 KB of
+    // LDS (reached when the decode regime is forced; by default the k-split MFMA kernel runs)
+    int tg = a.M <= 4 ? 1 : a.M <= 8 ? 8 : 16;
     while (tg > 1 && gemv_lds_bytes(a.K, tg) > 64 * 1024) tg = tg == 16 ? 8 : tg == 8 ? 4 : 1;
     a.tokens_per_group = tg;
     const size_t lds = gemv_lds_bytes(a.K, tg);
